@@ -1,0 +1,240 @@
+/*
+ * rlscan.h -- C ABI of librlscan: batched first-order linear-recurrence scans
+ * for reinforcement-learning credit assignment on AMD Instinct MI355X (gfx950).
+ *
+ * Every estimator below is one instance of the recurrence
+ *     x_t = a_t * x_{t+1} + b_t      (reverse-time estimators)
+ *     x_t = a_t * x_{t-1} + b_t      (forward-time estimators)
+ * solved per environment as an associative scan over (a, b) pairs with the
+ * composition (aL, bL) o (aE, bE) = (aL*aE, aL*bE + bL) (E applied first),
+ * the coefficients (a_t, b_t) being built on chip from the estimator's inputs
+ * inside the scan kernel ("rl-triton: High-Performance Triton GPU Kernels for
+ * Reinforcement Learning Credit Assignment", arXiv 2608.17641, abstract).
+ * The seven entry points are the seven kernels of the rl-triton README,
+ * section "Kernels" (one row each).
+ *
+ * Common conventions
+ * ------------------
+ * Layout      All per-step tensors are dense row-major [N, T] (element (n, t)
+ *             at n*T + t); Retrace's action-valued tensors are [N, T, A]
+ *             (element (n, t, a) at (n*T + t)*A + a).  N is the number of
+ *             environments, T the rollout length (README, section "Usage":
+ *             [num_envs, seq_len] tensors).
+ * Memory      Every pointer is a DEVICE pointer on the current HIP device,
+ *             allocated and owned by the caller.  The library never frees or
+ *             retains caller pointers.  Outputs must not alias inputs.
+ *             16-byte aligned pointers take the vectorised path; any other
+ *             alignment is accepted and takes a scalar-load path.
+ * Flags       terminated / truncated / dones are float32 tensors (README,
+ *             section "Usage", passes terminateds as a float tensor); a flag
+ *             is set iff its value != 0.
+ * Episodes    Reverse estimators (GAE, TD(lambda), discounted returns,
+ *             V-trace, Retrace): step t is a chain cut if terminated, or
+ *             truncated, or t = T-1.  Terminated means the successor value is
+ *             0; truncated means it is bootstrap_values[n, t]; the end of the
+ *             row means it is bootstrap_value[n] (0 if that pointer is NULL).
+ *             When both flags are set, terminated wins.  (README, section
+ *             "Performance": GAE, V-trace, TD(lambda) and discounted returns
+ *             take terminations, time-limit truncations and bootstrap values;
+ *             Retrace takes both flags, mandatory and distinct, with its
+ *             continuation value inside the next-state Q tensor; traces and
+ *             prefix sum take a single done flag and no bootstrap.)
+ *             Forward estimators: the flag at step t drops the carry from
+ *             step t-1; every row starts from 0.
+ * Parameters  gamma, lambda in [0, 1] and finite; rho_bar, c_bar > 0
+ *             (+inf allowed, NaN rejected).
+ * Streams     Work is enqueued on `stream` (NULL = the device's null stream)
+ *             and the call returns without synchronising.  Results are valid
+ *             once the stream has completed.  Faults inside kernels surface at
+ *             the caller's next synchronisation, as for any HIP kernel.
+ * Empty       N == 0 or T == 0 is a successful no-op (pointers may be NULL).
+ * Errors      A negative rlscan_status is returned, and nothing is enqueued,
+ *             for: a NULL required pointer, a negative size or an element
+ *             count above 2^48, a parameter out of range, an output pointer
+ *             equal to an input pointer (or to the other output).  A failed
+ *             HIP call (launch, allocation of the library's own scratch)
+ *             returns RLSCAN_ERR_HIP / RLSCAN_ERR_ALLOC.  No C++ exception
+ *             crosses this interface.
+ * Scratch     Sequences that span several workgroups (long rows, or rows that
+ *             do not tile evenly) use a small library-owned status buffer per
+ *             (device, stream) for the single-pass decoupled look-back,
+ *             allocated on first need and grown when a call needs more; it is
+ *             released by rlscan_release_scratch().  Calls that use it from
+ *             several host threads on one stream are serialised internally.
+ *             Calls on one stream are not safe to capture into a HIP graph.
+ * Thread      All entry points may be called concurrently from several host
+ * safety      threads.
+ */
+#ifndef RLSCAN_H_
+#define RLSCAN_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RLSCAN_OK = 0,
+    RLSCAN_ERR_NULL = -1,  /* a required pointer is NULL                        */
+    RLSCAN_ERR_SHAPE = -2, /* negative N/T, A < 1, or too many elements         */
+    RLSCAN_ERR_PARAM = -3, /* gamma/lambda/rho_bar/c_bar out of range           */
+    RLSCAN_ERR_ALIAS = -4, /* an output pointer equals an input or other output */
+    RLSCAN_ERR_HIP = -5,   /* a HIP runtime call or kernel launch failed        */
+    RLSCAN_ERR_ALLOC = -6  /* the library could not allocate its scratch        */
+} rlscan_status;
+
+/* GAE (README, Kernels table, compute_gae: a backward scan that adds each
+ * step's TD error to gamma*lambda times the next advantage; Schulman et al.
+ * 2016).
+ *   delta_t = r_t + gamma*Vhat_{t+1} - V_t
+ *   A_t     = delta_t + (cut_t ? 0 : gamma*lambda*A_{t+1})
+ * in:  rewards, values, terminated [N,T]; bootstrap_value [N] or NULL (-> 0);
+ *      truncated [N,T] or NULL (no truncation); bootstrap_values [N,T],
+ *      required iff truncated != NULL.
+ * out: advantages [N,T]. */
+int rlscan_gae(const float* rewards, const float* values, const float* bootstrap_value,
+               const float* terminated, const float* truncated,
+               const float* bootstrap_values, float* advantages,
+               int64_t N, int64_t T, float gamma, float lambda, hipStream_t stream);
+
+/* TD(lambda) returns (README, Kernels table, compute_lambda_returns: lambda
+ * returns mixing one-step TD targets with Monte-Carlo returns).
+ *   G_t = r_t + gamma*Vhat_{t+1}                                 if cut_t
+ *   G_t = r_t + gamma*((1-lambda)*V_{t+1} + lambda*G_{t+1})      otherwise
+ * Inputs as rlscan_gae.  out: returns [N,T]. */
+int rlscan_lambda_returns(const float* rewards, const float* values,
+                          const float* bootstrap_value, const float* terminated,
+                          const float* truncated, const float* bootstrap_values,
+                          float* returns, int64_t N, int64_t T, float gamma, float lambda,
+                          hipStream_t stream);
+
+/* Discounted returns (README, Kernels table, compute_discounted_returns:
+ * discounted reward-to-go).
+ *   G_t = r_t + gamma*(cut_t ? Vhat_{t+1} : G_{t+1})
+ * in:  rewards, terminated [N,T]; bootstrap_value [N] or NULL (pure
+ *      reward-to-go at the row end); truncated [N,T] or NULL;
+ *      bootstrap_values [N,T], required iff truncated != NULL.
+ * out: returns [N,T]. */
+int rlscan_discounted_returns(const float* rewards, const float* bootstrap_value,
+                              const float* terminated, const float* truncated,
+                              const float* bootstrap_values, float* returns,
+                              int64_t N, int64_t T, float gamma, hipStream_t stream);
+
+/* V-trace (README, Kernels table, compute_vtrace: importance-weighted
+ * targets and advantages; Espeholt et al. 2018, IMPALA).
+ *   rho_t = min(rho_bar, exp(log_rhos_t)),  c_t = min(c_bar, exp(log_rhos_t))
+ *   delta_t = rho_t*(r_t + gamma*Vhat_{t+1} - V_t)
+ *   vs_t  = V_t + u_t,  u_t = delta_t + (cut_t ? 0 : gamma*c_t*u_{t+1})
+ *   pg_t  = rho_t*(r_t + gamma*(cut_t ? Vhat_{t+1} : vs_{t+1}) - V_t)
+ * in:  rewards, values, log_rhos (log pi - log mu of the taken action),
+ *      terminated [N,T]; bootstrap_value, truncated, bootstrap_values as
+ *      rlscan_gae.
+ * out: vs [N,T] (targets), pg_advantages [N,T]. */
+int rlscan_vtrace(const float* rewards, const float* values, const float* bootstrap_value,
+                  const float* log_rhos, const float* terminated, const float* truncated,
+                  const float* bootstrap_values, float* vs, float* pg_advantages,
+                  int64_t N, int64_t T, float gamma, float rho_bar, float c_bar,
+                  hipStream_t stream);
+
+/* Retrace(lambda) (README, Kernels table, compute_retrace: off-policy return
+ * with truncated importance ratios; README, section "Performance": both
+ * flags mandatory, continuation value folded into next_q_values_all at every
+ * step; Munos et al. 2016).
+ *   EQ_t = sum_a next_target_probs[t,a]*next_q_values_all[t,a]
+ *   G_t  = r_t                                         if terminated_t
+ *   G_t  = r_t + gamma*EQ_t                            if truncated_t or t = T-1
+ *   G_t  = r_t + gamma*(EQ_t + c'_t*(G_{t+1} - next_q_values_all[t, a_{t+1}]))
+ *   c'_t = lambda*min(1, next_target_probs[t, a_{t+1}] / behaviour_probs[t+1])
+ * in:  rewards [N,T]; next_q_values_all, next_target_probs [N,T,A] (Q and pi
+ *      at the successor state of step t); actions [N,T] int32 (a_t);
+ *      behaviour_probs [N,T] (mu(a_t | x_t)); terminated, truncated [N,T],
+ *      both required.
+ * out: targets [N,T].
+ * Preconditions (not checked on the device): actions in [0, A) -- an
+ * out-of-range action is clamped into range and gives unspecified values,
+ * never an out-of-bounds access; behaviour_probs > 0. */
+int rlscan_retrace(const float* rewards, const float* next_q_values_all,
+                   const float* next_target_probs, const int32_t* actions,
+                   const float* behaviour_probs, const float* terminated,
+                   const float* truncated, float* targets,
+                   int64_t N, int64_t T, int64_t A, float gamma, float lambda,
+                   hipStream_t stream);
+
+/* Eligibility traces (README, Kernels table, compute_eligibility_traces:
+ * accumulating forward traces, each step adding x_t to gamma*lambda*(1-d)
+ * times the previous trace).
+ *   e_t = x_t + (d_t ? 0 : gamma*lambda*e_{t-1}),  e_{-1} = 0
+ * in:  x, dones [N,T].  out: traces [N,T]. */
+int rlscan_eligibility_traces(const float* x, const float* dones, float* traces,
+                              int64_t N, int64_t T, float gamma, float lambda,
+                              hipStream_t stream);
+
+/* Episodic prefix sum (README, Kernels table, compute_episodic_prefix_sum:
+ * cumulative sum restarted by the done mask), exact integer arithmetic.
+ *   y_t = x_t + (d_t ? 0 : y_{t-1}),  y_{-1} = 0
+ * in:  x [N,T] int32, dones [N,T] float.  out: y [N,T] int64. */
+int rlscan_episodic_prefix_sum(const int32_t* x, const float* dones, int64_t* out,
+                               int64_t N, int64_t T, hipStream_t stream);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* rlscan_status_string(int status);
+
+/* Library version string (static storage). */
+const char* rlscan_version(void);
+
+/* Frees the look-back scratch of every (device, stream) pair.  The caller
+ * must make sure no rlscan work is still running on any stream. */
+int rlscan_release_scratch(void);
+
+/* ---- launch planning (host only; no GPU work) ---------------------------
+ * The library maps the flattened N*T elements onto tiles of
+ * 1024*rounds consecutive elements, one 256-thread workgroup per tile.
+ * mapping RLSCAN_MAP_PACKED: every tile holds whole rows (1024*rounds is a
+ * multiple of T, or there is a single tile), no inter-workgroup traffic.
+ * mapping RLSCAN_MAP_LOOKBACK: rows span tiles; carries travel between
+ * workgroups through the single-pass decoupled look-back. */
+enum { RLSCAN_MAP_AUTO = 0, RLSCAN_MAP_PACKED = 1, RLSCAN_MAP_LOOKBACK = 2 };
+
+enum {
+    RLSCAN_EST_GAE = 0, RLSCAN_EST_LAMBDA_RETURNS = 1, RLSCAN_EST_DISCOUNTED = 2,
+    RLSCAN_EST_VTRACE = 3, RLSCAN_EST_RETRACE = 4, RLSCAN_EST_ELIGIBILITY = 5,
+    RLSCAN_EST_PREFIX_SUM = 6
+};
+
+typedef struct {
+    int32_t mapping;     /* RLSCAN_MAP_PACKED or RLSCAN_MAP_LOOKBACK         */
+    int32_t rounds;      /* 4-element chunks per lane per tile (1, 2 or 4)   */
+    int64_t tile_elems;  /* elements per tile = 1024 * rounds                */
+    int64_t tiles;       /* number of tiles = ceil(N*T / tile_elems)         */
+    int64_t grid;        /* workgroups launched                              */
+    int32_t threads;     /* threads per workgroup (256)                      */
+    int32_t reserved;
+} rlscan_plan_info;
+
+/* Fills *info with the launch the library would make for this estimator and
+ * shape under the current override.  Returns RLSCAN_ERR_SHAPE for invalid
+ * sizes, RLSCAN_ERR_PARAM for an unknown estimator id. */
+int rlscan_plan(int estimator, int64_t N, int64_t T, int64_t A, rlscan_plan_info* info);
+
+/* Overrides the planner for every later call in the process (tests and
+ * benchmarks).  mapping: RLSCAN_MAP_AUTO/PACKED/LOOKBACK (PACKED is only
+ * honoured where it is valid); rounds: 0 = automatic, else 1, 2 or 4;
+ * grid_cap: 0 = one workgroup per tile, else at most this many workgroups,
+ * each looping over tiles.  Returns RLSCAN_ERR_PARAM for other values. */
+int rlscan_set_launch_override(int mapping, int rounds, int64_t grid_cap);
+
+/* Diagnostics: waits in the look-back are bounded (a few seconds per
+ * predecessor); a wait that reaches the bound is counted, its tile's results
+ * are written as NaN (INT64_MIN for the prefix sum) and the kernel finishes.
+ * This call waits for every stream that has look-back scratch, then stores
+ * the total count of such timeouts since the scratch was allocated.  A
+ * correct build never reports one; the tests assert that. */
+int rlscan_lookback_timeouts(uint64_t* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLSCAN_H_ */

@@ -1,0 +1,580 @@
+// estimators.hpp -- on-chip construction of the recurrence steps (a_t, b_t)
+// for the seven credit-assignment estimators, and their epilogues.
+//
+// Each estimator type provides
+//   S, V              step type and state type (StepF/float or StepI/int64_t)
+//   kReverse          true for reverse-time estimators (x_t depends on x_{t+1})
+//   Params            device pointers and scalars of one call
+//   Chunk             registers holding one lane's 4-element chunk
+//   load<VEC>(...)    read the chunk's inputs (plus the one-element halo just
+//                     above the chunk where the step needs values at t+1)
+//   steps(...)        build the chunk's steps, in memory order
+//   store<VEC>(...)   write outputs from the states after each element (x)
+//                     and before it (before: x_{t+1} for reverse estimators)
+//
+// Shared conventions: row-major [N, T]; a flag is set iff != 0; for reverse
+// estimators step t cuts the chain if terminated, truncated or t = T-1, and
+// the successor value seen from step t is 0 (terminated, which wins), the
+// per-step bootstrap value (truncated), the per-row bootstrap value (t = T-1)
+// or V_{t+1}.  Sources are cited per estimator: the rl-triton README,
+// section "Kernels" (one row per estimator) and section "Performance"
+// (truncation/bootstrap inputs), and the estimators' published definitions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "scan_core.hpp"
+
+namespace rlscan {
+
+struct Geometry {
+    int64_t N, T, NT;       // rows, row length, N*T
+    int64_t num_tiles;      // tiles of tile_elems consecutive elements
+    int64_t grid;           // workgroups launched
+    double inv_T;           // 1.0 / T, for the row/time split of an index
+};
+
+// Position of one lane's chunk: 4 consecutive elements starting at g0.
+struct ChunkPos {
+    int64_t g0;
+    int64_t n0, t0;  // row and time of element g0
+    int valid;       // elements of the chunk below N*T (0..4)
+};
+
+__device__ __forceinline__ ChunkPos chunk_pos(int64_t g0, const Geometry& geo) {
+    ChunkPos q;
+    q.g0 = g0;
+    const int64_t rem = geo.NT - g0;
+    q.valid = rem <= 0 ? 0 : (rem >= kChunk ? kChunk : static_cast<int>(rem));
+    // g0 < 2^49, so the float64 quotient is within one of the true quotient.
+    int64_t n = static_cast<int64_t>(static_cast<double>(g0) * geo.inv_T);
+    int64_t t = g0 - n * geo.T;
+    if (t < 0) {
+        --n;
+        t += geo.T;
+    } else if (t >= geo.T) {
+        ++n;
+        t -= geo.T;
+    }
+    q.n0 = n;
+    q.t0 = t;
+    return q;
+}
+
+__device__ __forceinline__ void next_position(int64_t& n, int64_t& t, int64_t T) {
+    if (++t == T) {
+        t = 0;
+        ++n;
+    }
+}
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef long long i64x2 __attribute__((ext_vector_type(2)));
+
+// Loads of a 4-element chunk.  Elements at or past N*T read as 0 (their
+// steps are replaced by the identity before the scan).  FULL: the whole tile
+// lies below N*T, so no element needs a bounds check.
+template <bool VEC, bool FULL>
+__device__ __forceinline__ void load4(const float* __restrict__ p, const ChunkPos& q, float v[4]) {
+    if (VEC && (FULL || q.valid == kChunk)) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(p + q.g0);
+        v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) v[j] = (FULL || j < q.valid) ? p[q.g0 + j] : 0.0f;
+}
+
+template <bool VEC, bool FULL>
+__device__ __forceinline__ void load4(const int32_t* __restrict__ p, const ChunkPos& q, int32_t v[4]) {
+    if (VEC && (FULL || q.valid == kChunk)) {
+        const i32x4 w = *reinterpret_cast<const i32x4*>(p + q.g0);
+        v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) v[j] = (FULL || j < q.valid) ? p[q.g0 + j] : 0;
+}
+
+template <bool VEC, bool FULL>
+__device__ __forceinline__ void store4(float* __restrict__ p, const ChunkPos& q, const float v[4]) {
+    if (VEC && (FULL || q.valid == kChunk)) {
+        f32x4 w;
+        w.x = v[0]; w.y = v[1]; w.z = v[2]; w.w = v[3];
+        *reinterpret_cast<f32x4*>(p + q.g0) = w;
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j)
+        if (FULL || j < q.valid) p[q.g0 + j] = v[j];
+}
+
+template <bool VEC, bool FULL>
+__device__ __forceinline__ void store4(int64_t* __restrict__ p, const ChunkPos& q, const int64_t v[4]) {
+    if (VEC && (FULL || q.valid == kChunk)) {
+        i64x2 w0, w1;
+        w0.x = v[0]; w0.y = v[1]; w1.x = v[2]; w1.y = v[3];
+        reinterpret_cast<i64x2*>(p + q.g0)[0] = w0;
+        reinterpret_cast<i64x2*>(p + q.g0)[1] = w1;
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j)
+        if (FULL || j < q.valid) p[q.g0 + j] = v[j];
+}
+
+// One element past the chunk (the halo).  Past the end of the data the
+// index is clamped to the last element; the value is then never used, since
+// the chunk's last element ends its row.
+template <class T>
+__device__ __forceinline__ T load_halo(const T* __restrict__ p, const ChunkPos& q, int64_t NT) {
+    const int64_t i = q.g0 + kChunk;
+    return p[i < NT ? i : NT - 1];
+}
+
+// Shared episode logic of the reverse estimators: the flags of one chunk and
+// the bootstrap value of the row its first element lies in.
+struct EpisodeChunk {
+    float r[4], term[4], trunc[4], bv[4];
+    float boot;
+};
+
+template <bool VEC, bool FULL, bool TRUNC>
+__device__ __forceinline__ void load_episode(const float* rewards, const float* terminated,
+                                             const float* truncated,
+                                             const float* bootstrap_values,
+                                             const float* bootstrap_value, const Geometry& geo,
+                                             const ChunkPos& q, EpisodeChunk& c) {
+    // loaded with the chunk so that the row-end case costs no dependent load
+    c.boot = bootstrap_value != nullptr ? bootstrap_value[q.n0 < geo.N ? q.n0 : geo.N - 1] : 0.0f;
+    load4<VEC, FULL>(rewards, q, c.r);
+    load4<VEC, FULL>(terminated, q, c.term);
+    if constexpr (TRUNC) {
+        load4<VEC, FULL>(truncated, q, c.trunc);
+        load4<VEC, FULL>(bootstrap_values, q, c.bv);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) c.trunc[j] = c.bv[j] = 0.0f;
+    }
+}
+
+// Successor value for a chain cut (terminated > truncated > row end), and
+// whether the step is a cut.  `v_next` is V_{t+1}, used when it is not a cut.
+// A chunk holds at most one row end unless T < 4; only then can a row end
+// belong to a later row than the chunk's first element.
+__device__ __forceinline__ float successor_value(const EpisodeChunk& c, int j, bool row_end,
+                                                 bool in_range, const float* bootstrap_value,
+                                                 int64_t n, int64_t n0, float v_next, bool& cut) {
+    const bool term = c.term[j] != 0.0f;
+    const bool trunc = c.trunc[j] != 0.0f;
+    cut = term || trunc || row_end;
+    float v = v_next;
+    if (row_end) v = c.boot;
+    if (row_end && in_range && n != n0 && bootstrap_value != nullptr) v = bootstrap_value[n];
+    if (trunc) v = c.bv[j];
+    if (term) v = 0.0f;
+    return v;
+}
+
+// ------------------------------------------------------------------ GAE
+// README, Kernels table, compute_gae row (backward scan of TD errors with
+// weight gamma*lambda); Schulman et al. 2016.
+//   a_t = cut ? 0 : gamma*lambda,   b_t = r_t + gamma*Vhat_{t+1} - V_t
+struct GaeParams {
+    const float *rewards, *values, *bootstrap_value, *terminated, *truncated,
+        *bootstrap_values;
+    float* out;
+    float gamma, gamma_lambda;
+};
+
+template <bool kTrunc>
+struct Gae {
+    using S = StepF;
+    using V = float;
+    static constexpr bool kReverse = true;
+    using Params = GaeParams;
+    struct Chunk {
+        EpisodeChunk ep;
+        float v[4];
+        float v_halo;
+    };
+    template <bool VEC, bool FULL>
+    __device__ __forceinline__ static void load(const Params& p, const Geometry& geo, const ChunkPos& q, Chunk& c) {
+        load_episode<VEC, FULL, kTrunc>(p.rewards, p.terminated, p.truncated,
+                                        p.bootstrap_values, p.bootstrap_value, geo, q, c.ep);
+        load4<VEC, FULL>(p.values, q, c.v);
+        c.v_halo = load_halo(p.values, q, geo.NT);
+    }
+    __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
+                                 Chunk& c, S e[4]) {
+        int64_t n = q.n0, t = q.t0;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            bool cut;
+            const float v_next = j < kChunk - 1 ? c.v[j + 1] : c.v_halo;
+            const float vh = successor_value(c.ep, j, t == geo.T - 1, j < q.valid,
+                                             p.bootstrap_value, n, q.n0, v_next, cut);
+            e[j].a = cut ? 0.0f : p.gamma_lambda;
+            e[j].b = fmaf(p.gamma, vh, c.ep.r[j]) - c.v[j];
+            next_position(n, t, geo.T);
+        }
+    }
+    template <bool VEC, bool FULL>
+    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Chunk&, const V x[4],
+                                 const V[4]) {
+        store4<VEC, FULL>(p.out, q, x);
+    }
+};
+
+// ------------------------------------------------------------ TD(lambda)
+// README, Kernels table, compute_lambda_returns row; lambda-return.
+//   a_t = cut ? 0 : gamma*lambda
+//   b_t = cut ? r_t + gamma*Vhat_{t+1} : r_t + gamma*(1-lambda)*V_{t+1}
+struct LambdaReturnsParams {
+    const float *rewards, *values, *bootstrap_value, *terminated, *truncated,
+        *bootstrap_values;
+    float* out;
+    float gamma, gamma_lambda, gamma_one_minus_lambda;
+};
+
+template <bool kTrunc>
+struct LambdaReturns {
+    using S = StepF;
+    using V = float;
+    static constexpr bool kReverse = true;
+    using Params = LambdaReturnsParams;
+    using Chunk = typename Gae<kTrunc>::Chunk;
+    template <bool VEC, bool FULL>
+    __device__ __forceinline__ static void load(const Params& p, const Geometry& geo, const ChunkPos& q, Chunk& c) {
+        load_episode<VEC, FULL, kTrunc>(p.rewards, p.terminated, p.truncated,
+                                        p.bootstrap_values, p.bootstrap_value, geo, q, c.ep);
+        load4<VEC, FULL>(p.values, q, c.v);
+        c.v_halo = load_halo(p.values, q, geo.NT);
+    }
+    __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
+                                 Chunk& c, S e[4]) {
+        int64_t n = q.n0, t = q.t0;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            bool cut;
+            const float v_next = j < kChunk - 1 ? c.v[j + 1] : c.v_halo;
+            const float vh = successor_value(c.ep, j, t == geo.T - 1, j < q.valid,
+                                             p.bootstrap_value, n, q.n0, v_next, cut);
+            e[j].a = cut ? 0.0f : p.gamma_lambda;
+            e[j].b = cut ? fmaf(p.gamma, vh, c.ep.r[j])
+                         : fmaf(p.gamma_one_minus_lambda, v_next, c.ep.r[j]);
+            next_position(n, t, geo.T);
+        }
+    }
+    template <bool VEC, bool FULL>
+    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Chunk&, const V x[4],
+                                 const V[4]) {
+        store4<VEC, FULL>(p.out, q, x);
+    }
+};
+
+// ------------------------------------------------------ discounted returns
+// README, Kernels table, compute_discounted_returns row (reward-to-go).
+//   a_t = cut ? 0 : gamma,   b_t = cut ? r_t + gamma*Vhat_{t+1} : r_t
+struct DiscountedParams {
+    const float *rewards, *bootstrap_value, *terminated, *truncated, *bootstrap_values;
+    float* out;
+    float gamma;
+};
+
+template <bool kTrunc>
+struct Discounted {
+    using S = StepF;
+    using V = float;
+    static constexpr bool kReverse = true;
+    using Params = DiscountedParams;
+    struct Chunk {
+        EpisodeChunk ep;
+    };
+    template <bool VEC, bool FULL>
+    __device__ __forceinline__ static void load(const Params& p, const Geometry& geo, const ChunkPos& q, Chunk& c) {
+        load_episode<VEC, FULL, kTrunc>(p.rewards, p.terminated, p.truncated,
+                                        p.bootstrap_values, p.bootstrap_value, geo, q, c.ep);
+    }
+    __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
+                                 Chunk& c, S e[4]) {
+        int64_t n = q.n0, t = q.t0;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            bool cut;
+            const float vh = successor_value(c.ep, j, t == geo.T - 1, j < q.valid,
+                                             p.bootstrap_value, n, q.n0, 0.0f, cut);
+            e[j].a = cut ? 0.0f : p.gamma;
+            e[j].b = cut ? fmaf(p.gamma, vh, c.ep.r[j]) : c.ep.r[j];
+            next_position(n, t, geo.T);
+        }
+    }
+    template <bool VEC, bool FULL>
+    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Chunk&, const V x[4],
+                                 const V[4]) {
+        store4<VEC, FULL>(p.out, q, x);
+    }
+};
+
+// ------------------------------------------------------------------ V-trace
+// README, Kernels table, compute_vtrace row (importance-weighted targets and
+// advantages); Espeholt et al. 2018.  The scan computes u_t = vs_t - V_t:
+//   a_t = cut ? 0 : gamma*c_t,   b_t = delta_t = rho_t*(r_t + gamma*Vhat_{t+1} - V_t)
+// and the epilogue forms vs_t = V_t + u_t and
+//   pg_t = delta_t + (cut ? 0 : gamma*rho_t*u_{t+1})
+// which equals rho_t*(r_t + gamma*(cut ? Vhat_{t+1} : vs_{t+1}) - V_t).
+struct VtraceParams {
+    const float *rewards, *values, *bootstrap_value, *log_rhos, *terminated, *truncated,
+        *bootstrap_values;
+    float *vs, *pg;
+    float gamma, rho_bar, c_bar;
+};
+
+template <bool kTrunc>
+struct Vtrace {
+    using S = StepF;
+    using V = float;
+    static constexpr bool kReverse = true;
+    using Params = VtraceParams;
+    struct Chunk {
+        EpisodeChunk ep;
+        float v[4];
+        float lr[4];
+        float v_halo;
+        float delta[4];
+        float gamma_rho[4];  // 0 at a cut
+    };
+    template <bool VEC, bool FULL>
+    __device__ __forceinline__ static void load(const Params& p, const Geometry& geo, const ChunkPos& q, Chunk& c) {
+        load_episode<VEC, FULL, kTrunc>(p.rewards, p.terminated, p.truncated,
+                                        p.bootstrap_values, p.bootstrap_value, geo, q, c.ep);
+        load4<VEC, FULL>(p.values, q, c.v);
+        load4<VEC, FULL>(p.log_rhos, q, c.lr);
+        c.v_halo = load_halo(p.values, q, geo.NT);
+    }
+    __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
+                                 Chunk& c, S e[4]) {
+        int64_t n = q.n0, t = q.t0;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            bool cut;
+            const float v_next = j < kChunk - 1 ? c.v[j + 1] : c.v_halo;
+            const float vh = successor_value(c.ep, j, t == geo.T - 1, j < q.valid,
+                                             p.bootstrap_value, n, q.n0, v_next, cut);
+            const float ratio = expf(c.lr[j]);
+            const float rho = fminf(p.rho_bar, ratio);
+            const float cc = fminf(p.c_bar, ratio);
+            const float delta = rho * (fmaf(p.gamma, vh, c.ep.r[j]) - c.v[j]);
+            c.delta[j] = delta;
+            c.gamma_rho[j] = cut ? 0.0f : p.gamma * rho;
+            e[j].a = cut ? 0.0f : p.gamma * cc;
+            e[j].b = delta;
+            next_position(n, t, geo.T);
+        }
+    }
+    template <bool VEC, bool FULL>
+    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Chunk& c, const V x[4],
+                                 const V before[4]) {
+        float vs[4], pg[4];
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            vs[j] = c.v[j] + x[j];
+            pg[j] = fmaf(c.gamma_rho[j], before[j], c.delta[j]);
+        }
+        store4<VEC, FULL>(p.vs, q, vs);
+        store4<VEC, FULL>(p.pg, q, pg);
+    }
+};
+
+// ------------------------------------------------------------------ Retrace
+// README, Kernels table, compute_retrace row (off-policy return with
+// truncated importance ratios) and section "Performance" (both flags
+// required; continuation value inside next_q_values_all); Munos et al. 2016.
+//   EQ_t = sum_a pi'[t,a] Q'[t,a],  c'_t = lambda*min(1, pi'[t,a_{t+1}] / mu_{t+1})
+//   a_t = cut ? 0 : gamma*c'_t
+//   b_t = cut ? r_t + (terminated ? 0 : gamma*EQ_t)
+//             : r_t + gamma*(EQ_t - c'_t*Q'[t,a_{t+1}])
+// kA > 0: A known at compile time, the chunk's 4*A action values are read
+// with 16-byte loads into registers; kA == 0: any A, read element-wise.
+template <int kA>
+struct Retrace {
+    using S = StepF;
+    using V = float;
+    static constexpr bool kReverse = true;
+    struct Params {
+        const float *rewards, *next_q, *next_pi;
+        const int32_t* actions;
+        const float *behaviour_probs, *terminated, *truncated;
+        float* out;
+        int64_t A;
+        float gamma, lambda;
+    };
+    static constexpr int kRegA = kA > 0 ? kA : 1;
+    struct Chunk {
+        EpisodeChunk ep;  // bv unused
+        int32_t act[4];
+        float mu[4];
+        int32_t act_halo;
+        float mu_halo;
+        float q[4 * kRegA], pi[4 * kRegA];
+    };
+    template <bool VEC, bool FULL>
+    __device__ __forceinline__ static void load(const Params& p, const Geometry& geo, const ChunkPos& q, Chunk& c) {
+        load4<VEC, FULL>(p.rewards, q, c.ep.r);
+        load4<VEC, FULL>(p.terminated, q, c.ep.term);
+        load4<VEC, FULL>(p.truncated, q, c.ep.trunc);
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) c.ep.bv[j] = 0.0f;
+        c.ep.boot = 0.0f;
+        load4<VEC, FULL>(p.actions, q, c.act);
+        load4<VEC, FULL>(p.behaviour_probs, q, c.mu);
+        c.act_halo = load_halo(p.actions, q, geo.NT);
+        c.mu_halo = load_halo(p.behaviour_probs, q, geo.NT);
+        if constexpr (kA > 0) {
+            const int64_t base = q.g0 * kA;
+            if (VEC && (FULL || q.valid == kChunk)) {
+                // 4*kA floats = kA 16-byte vectors per tensor, 16-byte aligned
+                const f32x4* qv = reinterpret_cast<const f32x4*>(p.next_q + base);
+                const f32x4* pv = reinterpret_cast<const f32x4*>(p.next_pi + base);
+#pragma unroll
+                for (int i = 0; i < kA; ++i) {
+                    const f32x4 a = qv[i], b = pv[i];
+                    c.q[4 * i + 0] = a.x; c.q[4 * i + 1] = a.y;
+                    c.q[4 * i + 2] = a.z; c.q[4 * i + 3] = a.w;
+                    c.pi[4 * i + 0] = b.x; c.pi[4 * i + 1] = b.y;
+                    c.pi[4 * i + 2] = b.z; c.pi[4 * i + 3] = b.w;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4 * kA; ++i) {
+                    const bool ok = FULL || i / kA < q.valid;
+                    c.q[i] = ok ? p.next_q[base + i] : 0.0f;
+                    c.pi[i] = ok ? p.next_pi[base + i] : 0.0f;
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
+                                 Chunk& c, S e[4]) {
+        int64_t t = q.t0;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            const bool term = c.ep.term[j] != 0.0f;
+            const bool cut = term || c.ep.trunc[j] != 0.0f || t == geo.T - 1;
+            int32_t a_next = j < kChunk - 1 ? c.act[j + 1] : c.act_halo;
+            const float mu_next = j < kChunk - 1 ? c.mu[j + 1] : c.mu_halo;
+            float eq = 0.0f, q_sel = 0.0f, pi_sel = 0.0f;
+            if constexpr (kA > 0) {
+                a_next = a_next < 0 ? 0 : (a_next >= kA ? kA - 1 : a_next);
+#pragma unroll
+                for (int a = 0; a < kA; ++a) {
+                    const float qa = c.q[j * kA + a], pa = c.pi[j * kA + a];
+                    eq = fmaf(pa, qa, eq);
+                    q_sel = a == a_next ? qa : q_sel;
+                    pi_sel = a == a_next ? pa : pi_sel;
+                }
+            } else {
+                if (j < q.valid) {
+                    const int64_t A = p.A;
+                    const int64_t base = (q.g0 + j) * A;
+                    for (int64_t a = 0; a < A; ++a)
+                        eq = fmaf(p.next_pi[base + a], p.next_q[base + a], eq);
+                    const int64_t as = a_next < 0 ? 0 : (a_next >= A ? A - 1 : a_next);
+                    q_sel = p.next_q[base + as];
+                    pi_sel = p.next_pi[base + as];
+                }
+            }
+            const float cprime = p.lambda * fminf(1.0f, pi_sel / mu_next);
+            e[j].a = cut ? 0.0f : p.gamma * cprime;
+            e[j].b = cut ? (term ? c.ep.r[j] : fmaf(p.gamma, eq, c.ep.r[j]))
+                         : fmaf(p.gamma, fmaf(-cprime, q_sel, eq), c.ep.r[j]);
+            if (++t == geo.T) t = 0;
+        }
+    }
+    template <bool VEC, bool FULL>
+    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Chunk&, const V x[4],
+                                 const V[4]) {
+        store4<VEC, FULL>(p.out, q, x);
+    }
+};
+
+// ------------------------------------------------------- eligibility traces
+// README, Kernels table, compute_eligibility_traces row: forward traces, the
+// done flag at step t dropping the previous trace.
+//   a_t = (d_t or t = 0) ? 0 : gamma*lambda,   b_t = x_t
+struct Eligibility {
+    using S = StepF;
+    using V = float;
+    static constexpr bool kReverse = false;
+    struct Params {
+        const float *x, *dones;
+        float* out;
+        float gamma_lambda;
+    };
+    struct Chunk {
+        float x[4], d[4];
+    };
+    template <bool VEC, bool FULL>
+    __device__ __forceinline__ static void load(const Params& p, const Geometry&, const ChunkPos& q, Chunk& c) {
+        load4<VEC, FULL>(p.x, q, c.x);
+        load4<VEC, FULL>(p.dones, q, c.d);
+    }
+    __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
+                                 Chunk& c, S e[4]) {
+        int64_t t = q.t0;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            e[j].a = (c.d[j] != 0.0f || t == 0) ? 0.0f : p.gamma_lambda;
+            e[j].b = c.x[j];
+            if (++t == geo.T) t = 0;
+        }
+    }
+    template <bool VEC, bool FULL>
+    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Chunk&, const V x[4],
+                                 const V[4]) {
+        store4<VEC, FULL>(p.out, q, x);
+    }
+};
+
+// ------------------------------------------------------- episodic prefix sum
+// README, Kernels table, compute_episodic_prefix_sum row: cumulative sum
+// restarted by the done mask; exact int64 accumulation of int32 inputs.
+//   a_t = (d_t or t = 0) ? 0 : 1,   b_t = x_t
+struct PrefixSum {
+    using S = StepI;
+    using V = int64_t;
+    static constexpr bool kReverse = false;
+    struct Params {
+        const int32_t* x;
+        const float* dones;
+        int64_t* out;
+    };
+    struct Chunk {
+        int32_t x[4];
+        float d[4];
+    };
+    template <bool VEC, bool FULL>
+    __device__ __forceinline__ static void load(const Params& p, const Geometry&, const ChunkPos& q, Chunk& c) {
+        load4<VEC, FULL>(p.x, q, c.x);
+        load4<VEC, FULL>(p.dones, q, c.d);
+    }
+    __device__ __forceinline__ static void steps(const Params&, const Geometry& geo, const ChunkPos& q, Chunk& c,
+                                 S e[4]) {
+        int64_t t = q.t0;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            e[j].a = (c.d[j] != 0.0f || t == 0) ? 0u : 1u;
+            e[j].b = static_cast<int64_t>(c.x[j]);
+            if (++t == geo.T) t = 0;
+        }
+    }
+    template <bool VEC, bool FULL>
+    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Chunk&, const V x[4],
+                                 const V[4]) {
+        store4<VEC, FULL>(p.out, q, x);
+    }
+};
+
+}  // namespace rlscan

@@ -1,0 +1,650 @@
+// rlscan.hip -- scan kernels and the C ABI of librlscan (gfx950 only).
+//
+// One kernel template serves all seven estimators.  The N*T elements are
+// taken as one flattened row-major sequence and cut into tiles of
+// 1024*R consecutive elements (R "rounds"), one 256-thread workgroup per
+// tile.  Row boundaries need no special handling: the step at a row's end
+// (reverse estimators) or start (forward ones) has a == 0, which makes the
+// plain scan a segmented one.  Within a tile:
+//   1. every lane loads R chunks of 4 consecutive elements (16-byte loads;
+//      a wave's 64 chunks are 1 KiB of contiguous memory per input);
+//   2. builds the chunk's steps (a_t, b_t) in registers (estimators.hpp);
+//   3. composes its 4 steps serially, then a wave64 DPP scan combines the 64
+//      lane aggregates of each round (scan_core.hpp);
+//   4. round totals compose within the wave, wave totals go through LDS;
+//   5. the state entering the tile is 0 when the tile holds whole rows
+//      (packed mapping), else comes from the decoupled look-back
+//      (lookback.hpp);
+//   6. each lane replays its 4 steps from its entering state and stores.
+// Reverse-time estimators run the same forward scan in "scan order": lane
+// chunks are laid out from the tile's high end downwards, so a wave still
+// reads contiguous memory with every load instruction.
+//
+// Sources: "rl-triton: High-Performance Triton GPU Kernels for Reinforcement
+// Learning Credit Assignment" (arXiv 2608.17641), abstract -- seven
+// estimators as one first-order linear recurrence, one associative operator,
+// coefficients built on chip by fused per-estimator kernels; rl-triton
+// README, section "Kernels" -- the seven kernels and, in its last column,
+// that long sequences need a path beyond one fused block.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <utility>
+
+#include "estimators.hpp"
+#include "lookback.hpp"
+#include "rlscan.h"
+#include "scan_core.hpp"
+
+namespace rlscan {
+
+// ------------------------------------------------------------------ kernel
+template <class E, int R, bool LOOKBACK, bool VEC, bool FULL>
+__device__ __forceinline__ void scan_tile(const typename E::Params& p, const Geometry& geo,
+                                          const LookbackArgs& lb, uint64_t tile,
+                                          typename AggOf<typename E::S>::type* sm_wave,
+                                          typename E::V* sm_carry) {
+    using S = typename E::S;                  // one element's step
+    using A = typename AggOf<S>::type;        // a composition of steps
+    using V = typename E::V;
+    constexpr int64_t kTile = static_cast<int64_t>(kThreads) * kChunk * R;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int64_t mem_tile = E::kReverse ? geo.num_tiles - 1 - static_cast<int64_t>(tile)
+                                         : static_cast<int64_t>(tile);
+    const int64_t base = mem_tile * kTile;
+
+    // 1. loads, all rounds first so every load of the tile is in flight
+    typename E::Chunk ch[R];
+    ChunkPos pos[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int c = (wave * R + r) * kWave + lane;  // chunk index in scan order
+        const int64_t off = E::kReverse ? kTile - static_cast<int64_t>(kChunk) * (c + 1)
+                                        : static_cast<int64_t>(kChunk) * c;
+        pos[r] = chunk_pos(base + off, geo);
+        E::template load<VEC, FULL>(p, geo, pos[r], ch[r]);
+    }
+
+    // 2. steps in scan order; elements past N*T become the identity
+    S e[R][kChunk];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        S em[kChunk];
+        E::steps(p, geo, pos[r], ch[r], em);
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            const S s = (FULL || j < pos[r].valid) ? em[j] : identity_step(S{});
+            e[r][E::kReverse ? kChunk - 1 - j : j] = s;
+        }
+    }
+
+    // 3. lane aggregates and wave scans
+    A incl[R], tot[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        A agg = promote(e[r][0]);
+#pragma unroll
+        for (int k = 1; k < kChunk; ++k) agg = compose(promote(e[r][k]), agg);
+        incl[r] = wave_inclusive_scan(agg);
+        tot[r] = read_lane(incl[r], kWave - 1);
+    }
+
+    // 4. wave totals through LDS
+    A wtot = tot[0];
+#pragma unroll
+    for (int r = 1; r < R; ++r) wtot = compose(tot[r], wtot);
+    if (lane == 0) sm_wave[wave] = wtot;
+    __syncthreads();
+    A wpre = identity_step(A{});
+#pragma unroll
+    for (int w = 0; w < kWavesPerGroup; ++w)
+        if (w < wave) wpre = compose(sm_wave[w], wpre);
+
+    // 5. state entering the tile
+    if (threadIdx.x == 0) {
+        V carry = V(0);
+        if constexpr (LOOKBACK) {
+            A agg = identity_step(A{});
+#pragma unroll
+            for (int w = 0; w < kWavesPerGroup; ++w) agg = compose(sm_wave[w], agg);
+            TileStatus* st = lb.status + tile;
+            const bool known = tile == 0 || cuts_chain(agg);
+            if (known)
+                publish_inclusive(st, pack_state(apply(agg, V(0))), lb.epoch);
+            else
+                publish_aggregate(st, pack_step(agg), lb.epoch);
+            // thread 0 holds the tile's first step in scan order
+            if (tile > 0 && !cuts_chain(e[0][0])) carry = look_back<A, V>(lb, tile);
+            if (!known) publish_inclusive(st, pack_state(apply(agg, carry)), lb.epoch);
+        }
+        *sm_carry = carry;
+    }
+    __syncthreads();
+
+    // 6. replay from the entering state and store
+    V state = apply(wpre, *sm_carry);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const V after_lane = apply(incl[r], state);
+        V x = lane_before(after_lane, lane, state);
+        state = read_lane(after_lane, kWave - 1);
+        V out[kChunk], before[kChunk];
+#pragma unroll
+        for (int k = 0; k < kChunk; ++k) {
+            const int j = E::kReverse ? kChunk - 1 - k : k;
+            before[j] = x;
+            x = apply(e[r][k], x);
+            out[j] = x;
+        }
+        E::template store<VEC, FULL>(p, pos[r], ch[r], out, before);
+    }
+}
+
+template <class E, int R, bool LOOKBACK, bool VEC>
+__global__ __launch_bounds__(kThreads) void scan_kernel(const typename E::Params p,
+                                                        const Geometry geo,
+                                                        const LookbackArgs lb) {
+    using A = typename AggOf<typename E::S>::type;
+    using V = typename E::V;
+    __shared__ A sm_wave[kWavesPerGroup];
+    __shared__ V sm_carry;
+    __shared__ uint64_t sm_tile;
+    const bool one_tile_per_group = geo.grid >= geo.num_tiles;
+    uint64_t tile = blockIdx.x;
+    for (;;) {
+        if constexpr (LOOKBACK) {
+            if (threadIdx.x == 0) sm_tile = take_ticket(lb);
+            __syncthreads();
+            tile = sm_tile;
+        }
+        if (tile >= static_cast<uint64_t>(geo.num_tiles)) break;
+        // only the tile holding the end of the data needs bounds checks
+        const int64_t mem_tile = E::kReverse ? geo.num_tiles - 1 - static_cast<int64_t>(tile)
+                                             : static_cast<int64_t>(tile);
+        constexpr int64_t kTile = static_cast<int64_t>(kThreads) * kChunk * R;
+        if ((mem_tile + 1) * kTile <= geo.NT)
+            scan_tile<E, R, LOOKBACK, VEC, true>(p, geo, lb, tile, sm_wave, &sm_carry);
+        else
+            scan_tile<E, R, LOOKBACK, VEC, false>(p, geo, lb, tile, sm_wave, &sm_carry);
+        if (one_tile_per_group) break;
+        if constexpr (!LOOKBACK) tile += gridDim.x;
+        __syncthreads();  // LDS is reused by the next tile
+    }
+}
+
+// ------------------------------------------------------------------ host
+namespace {
+
+constexpr int64_t kMaxElements = int64_t(1) << 48;
+constexpr int64_t kMaxGrid = (int64_t(1) << 24) - 1;  // grid * 256 threads < 2^32
+
+struct LaunchOverride {
+    std::atomic<int> mapping{RLSCAN_MAP_AUTO};
+    std::atomic<int> rounds{0};
+    std::atomic<int64_t> grid_cap{0};
+};
+LaunchOverride g_override;
+
+struct Scratch {
+    std::mutex m;
+    TileStatus* status = nullptr;
+    unsigned long long* counter = nullptr;
+    int64_t capacity = 0;       // tiles
+    uint64_t next_ticket = 0;   // counter value at the start of the next call
+    uint64_t epoch = 0;         // last epoch used
+    bool broken = false;        // a launch failed: counter position unknown
+};
+
+std::mutex g_scratch_mutex;
+std::map<std::pair<int, uintptr_t>, std::unique_ptr<Scratch>> g_scratch;
+
+Scratch* scratch_for(int device, hipStream_t stream) {
+    std::lock_guard<std::mutex> g(g_scratch_mutex);
+    auto& slot = g_scratch[{device, reinterpret_cast<uintptr_t>(stream)}];
+    if (!slot) slot.reset(new Scratch());
+    return slot.get();
+}
+
+// Called with sc->m held.  Makes room for `tiles` status entries.
+int ensure_capacity(Scratch* sc, hipStream_t stream, int64_t tiles) {
+    if (sc->capacity >= tiles && !sc->broken) return RLSCAN_OK;
+    int64_t cap = 1024;
+    while (cap < tiles) cap *= 2;
+    // earlier work on this stream may still read the old buffers
+    if (sc->status != nullptr && hipStreamSynchronize(stream) != hipSuccess) return RLSCAN_ERR_HIP;
+    if (sc->status != nullptr) (void)hipFree(sc->status);
+    if (sc->counter != nullptr) (void)hipFree(sc->counter);
+    sc->status = nullptr;
+    sc->counter = nullptr;
+    sc->capacity = 0;
+    void* st = nullptr;
+    void* ctr = nullptr;
+    if (hipMalloc(&st, sizeof(TileStatus) * cap) != hipSuccess) return RLSCAN_ERR_ALLOC;
+    if (hipMalloc(&ctr, 256) != hipSuccess) {
+        (void)hipFree(st);
+        return RLSCAN_ERR_ALLOC;
+    }
+    // ordered before the first kernel that uses the buffers (same stream)
+    if (hipMemsetAsync(st, 0, sizeof(TileStatus) * cap, stream) != hipSuccess ||
+        hipMemsetAsync(ctr, 0, 256, stream) != hipSuccess) {
+        (void)hipFree(st);
+        (void)hipFree(ctr);
+        return RLSCAN_ERR_HIP;
+    }
+    sc->status = static_cast<TileStatus*>(st);
+    sc->counter = static_cast<unsigned long long*>(ctr);
+    sc->capacity = cap;
+    sc->next_ticket = 0;
+    sc->epoch = 0;
+    sc->broken = false;
+    return RLSCAN_OK;
+}
+
+struct Plan {
+    int mapping;
+    int rounds;
+    int64_t tile_elems, tiles, grid;
+};
+
+int auto_rounds(int est, int64_t NT) {
+    if (est == RLSCAN_EST_RETRACE) return 1;
+    if (NT <= (int64_t(1) << 20)) return 1;
+    if (NT <= (int64_t(1) << 22)) return 2;
+    return 4;
+}
+
+// `vec`: every pointer is 16-byte aligned.  Multi-round kernels exist only
+// for the vectorised path, and Retrace always runs one round.
+Plan make_plan(int est, int64_t N, int64_t T, bool vec) {
+    const int64_t NT = N * T;
+    Plan pl;
+    const int ro = g_override.rounds.load();
+    pl.rounds = ro > 0 ? ro : auto_rounds(est, NT);
+    if (!vec || est == RLSCAN_EST_RETRACE) pl.rounds = 1;
+    pl.tile_elems = int64_t(kThreads) * kChunk * pl.rounds;
+    pl.tiles = (NT + pl.tile_elems - 1) / pl.tile_elems;
+    const bool packed_ok = pl.tiles <= 1 || pl.tile_elems % T == 0;
+    const int mo = g_override.mapping.load();
+    pl.mapping = (packed_ok && mo != RLSCAN_MAP_LOOKBACK) ? RLSCAN_MAP_PACKED : RLSCAN_MAP_LOOKBACK;
+    const int64_t cap = g_override.grid_cap.load();
+    int64_t grid = pl.tiles;
+    if (cap > 0 && grid > cap) grid = cap;
+    if (grid > kMaxGrid) grid = kMaxGrid;
+    pl.grid = grid;
+    return pl;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool unit_interval(float x) { return x >= 0.0f && x <= 1.0f; }  // false for NaN
+bool positive_clip(float x) { return x > 0.0f; }                 // +inf allowed, NaN not
+
+int check_shape(int64_t N, int64_t T, int64_t A = 1) {
+    if (N < 0 || T < 0 || A < 1) return RLSCAN_ERR_SHAPE;
+    if (N == 0 || T == 0) return RLSCAN_OK;
+    if (N > kMaxElements / T) return RLSCAN_ERR_SHAPE;
+    if (N * T > kMaxElements / A) return RLSCAN_ERR_SHAPE;
+    return RLSCAN_OK;
+}
+
+int check_alias(std::initializer_list<const void*> outs, std::initializer_list<const void*> ins) {
+    for (const void* o : outs) {
+        for (const void* i : ins)
+            if (i != nullptr && i == o) return RLSCAN_ERR_ALIAS;
+        int same = 0;
+        for (const void* o2 : outs) same += (o2 == o);
+        if (same > 1) return RLSCAN_ERR_ALIAS;
+    }
+    return RLSCAN_OK;
+}
+
+template <class E, int R, bool VEC>
+hipError_t launch_r(const typename E::Params& p, const Geometry& geo, const LookbackArgs& lb,
+                    bool lookback, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(geo.grid)), block(kThreads);
+    if (lookback)
+        hipLaunchKernelGGL((scan_kernel<E, R, true, VEC>), grid, block, 0, stream, p, geo, lb);
+    else
+        hipLaunchKernelGGL((scan_kernel<E, R, false, VEC>), grid, block, 0, stream, p, geo, lb);
+    return hipGetLastError();
+}
+
+template <class E>
+hipError_t launch_kernel(const typename E::Params& p, const Geometry& geo, const LookbackArgs& lb,
+                         int rounds, bool lookback, bool vec, hipStream_t stream) {
+    if (!vec) return launch_r<E, 1, false>(p, geo, lb, lookback, stream);
+    switch (rounds) {
+        case 1: return launch_r<E, 1, true>(p, geo, lb, lookback, stream);
+        case 2: return launch_r<E, 2, true>(p, geo, lb, lookback, stream);
+        default: return launch_r<E, 4, true>(p, geo, lb, lookback, stream);
+    }
+}
+
+// Retrace keeps 2*4*A action values per round in registers: one round only.
+template <class E>
+hipError_t launch_kernel_r1(const typename E::Params& p, const Geometry& geo,
+                            const LookbackArgs& lb, bool lookback, bool vec, hipStream_t stream) {
+    if (!vec) return launch_r<E, 1, false>(p, geo, lb, lookback, stream);
+    return launch_r<E, 1, true>(p, geo, lb, lookback, stream);
+}
+
+// Plans, takes the look-back scratch if needed, and launches through `fn`.
+template <class Fn>
+int run(int est, int64_t N, int64_t T, bool vec, hipStream_t stream, Fn&& fn) {
+    const Plan pl = make_plan(est, N, T, vec);
+    if (pl.rounds != 1 && pl.rounds != 2 && pl.rounds != 4) return RLSCAN_ERR_PARAM;
+    Geometry geo;
+    geo.N = N;
+    geo.T = T;
+    geo.NT = N * T;
+    geo.num_tiles = pl.tiles;
+    geo.grid = pl.grid;
+    geo.inv_T = 1.0 / static_cast<double>(T);
+    LookbackArgs lb{};
+    if (pl.mapping == RLSCAN_MAP_PACKED) {
+        return fn(geo, lb, pl.rounds, false) == hipSuccess ? RLSCAN_OK : RLSCAN_ERR_HIP;
+    }
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return RLSCAN_ERR_HIP;
+    Scratch* sc = scratch_for(device, stream);
+    std::lock_guard<std::mutex> g(sc->m);
+    const int rc = ensure_capacity(sc, stream, pl.tiles);
+    if (rc != RLSCAN_OK) return rc;
+    lb.status = sc->status;
+    lb.ticket_counter = sc->counter;
+    lb.timeouts = reinterpret_cast<unsigned int*>(sc->counter + 1);
+    lb.ticket_base = sc->next_ticket;
+    lb.epoch = ++sc->epoch;
+    if (fn(geo, lb, pl.rounds, true) != hipSuccess) {
+        sc->broken = true;
+        return RLSCAN_ERR_HIP;
+    }
+    // every workgroup takes one ticket per tile it runs plus, when looping,
+    // one final ticket that finds no tile
+    sc->next_ticket += static_cast<uint64_t>(pl.tiles) +
+                       (pl.grid >= pl.tiles ? 0u : static_cast<uint64_t>(pl.grid));
+    return RLSCAN_OK;
+}
+
+bool all_aligned(std::initializer_list<const void*> ptrs) {
+    for (const void* p : ptrs)
+        if (p != nullptr && !aligned16(p)) return false;
+    return true;
+}
+
+}  // namespace
+}  // namespace rlscan
+
+using namespace rlscan;
+
+// ------------------------------------------------------------------ C ABI
+extern "C" {
+
+int rlscan_gae(const float* rewards, const float* values, const float* bootstrap_value,
+               const float* terminated, const float* truncated, const float* bootstrap_values,
+               float* advantages, int64_t N, int64_t T, float gamma, float lambda,
+               hipStream_t stream) {
+    int rc = check_shape(N, T);
+    if (rc != RLSCAN_OK) return rc;
+    if (!unit_interval(gamma) || !unit_interval(lambda)) return RLSCAN_ERR_PARAM;
+    if (N == 0 || T == 0) return RLSCAN_OK;
+    if (!rewards || !values || !terminated || !advantages) return RLSCAN_ERR_NULL;
+    if (truncated && !bootstrap_values) return RLSCAN_ERR_NULL;
+    rc = check_alias({advantages},
+                     {rewards, values, bootstrap_value, terminated, truncated, bootstrap_values});
+    if (rc != RLSCAN_OK) return rc;
+    const GaeParams p{rewards, values, bootstrap_value, terminated, truncated, bootstrap_values,
+                      advantages, gamma, gamma * lambda};
+    const bool vec = all_aligned({rewards, values, terminated, truncated, bootstrap_values,
+                                  advantages});
+    return run(RLSCAN_EST_GAE, N, T, vec, stream,
+               [&](const Geometry& g, const LookbackArgs& lb, int rounds, bool look) {
+                   return truncated ? launch_kernel<Gae<true>>(p, g, lb, rounds, look, vec, stream)
+                                    : launch_kernel<Gae<false>>(p, g, lb, rounds, look, vec, stream);
+               });
+}
+
+int rlscan_lambda_returns(const float* rewards, const float* values, const float* bootstrap_value,
+                          const float* terminated, const float* truncated,
+                          const float* bootstrap_values, float* returns, int64_t N, int64_t T,
+                          float gamma, float lambda, hipStream_t stream) {
+    int rc = check_shape(N, T);
+    if (rc != RLSCAN_OK) return rc;
+    if (!unit_interval(gamma) || !unit_interval(lambda)) return RLSCAN_ERR_PARAM;
+    if (N == 0 || T == 0) return RLSCAN_OK;
+    if (!rewards || !values || !terminated || !returns) return RLSCAN_ERR_NULL;
+    if (truncated && !bootstrap_values) return RLSCAN_ERR_NULL;
+    rc = check_alias({returns},
+                     {rewards, values, bootstrap_value, terminated, truncated, bootstrap_values});
+    if (rc != RLSCAN_OK) return rc;
+    const LambdaReturnsParams p{rewards,   values,  bootstrap_value, terminated,
+                                truncated, bootstrap_values, returns, gamma,
+                                gamma * lambda, gamma * (1.0f - lambda)};
+    const bool vec = all_aligned({rewards, values, terminated, truncated, bootstrap_values,
+                                  returns});
+    return run(RLSCAN_EST_LAMBDA_RETURNS, N, T, vec, stream,
+               [&](const Geometry& g, const LookbackArgs& lb, int rounds, bool look) {
+                   return truncated
+                              ? launch_kernel<LambdaReturns<true>>(p, g, lb, rounds, look, vec, stream)
+                              : launch_kernel<LambdaReturns<false>>(p, g, lb, rounds, look, vec, stream);
+               });
+}
+
+int rlscan_discounted_returns(const float* rewards, const float* bootstrap_value,
+                              const float* terminated, const float* truncated,
+                              const float* bootstrap_values, float* returns, int64_t N,
+                              int64_t T, float gamma, hipStream_t stream) {
+    int rc = check_shape(N, T);
+    if (rc != RLSCAN_OK) return rc;
+    if (!unit_interval(gamma)) return RLSCAN_ERR_PARAM;
+    if (N == 0 || T == 0) return RLSCAN_OK;
+    if (!rewards || !terminated || !returns) return RLSCAN_ERR_NULL;
+    if (truncated && !bootstrap_values) return RLSCAN_ERR_NULL;
+    rc = check_alias({returns}, {rewards, bootstrap_value, terminated, truncated, bootstrap_values});
+    if (rc != RLSCAN_OK) return rc;
+    const DiscountedParams p{rewards, bootstrap_value, terminated, truncated, bootstrap_values,
+                             returns, gamma};
+    const bool vec = all_aligned({rewards, terminated, truncated, bootstrap_values, returns});
+    return run(RLSCAN_EST_DISCOUNTED, N, T, vec, stream,
+               [&](const Geometry& g, const LookbackArgs& lb, int rounds, bool look) {
+                   return truncated
+                              ? launch_kernel<Discounted<true>>(p, g, lb, rounds, look, vec, stream)
+                              : launch_kernel<Discounted<false>>(p, g, lb, rounds, look, vec, stream);
+               });
+}
+
+int rlscan_vtrace(const float* rewards, const float* values, const float* bootstrap_value,
+                  const float* log_rhos, const float* terminated, const float* truncated,
+                  const float* bootstrap_values, float* vs, float* pg_advantages, int64_t N,
+                  int64_t T, float gamma, float rho_bar, float c_bar, hipStream_t stream) {
+    int rc = check_shape(N, T);
+    if (rc != RLSCAN_OK) return rc;
+    if (!unit_interval(gamma) || !positive_clip(rho_bar) || !positive_clip(c_bar))
+        return RLSCAN_ERR_PARAM;
+    if (N == 0 || T == 0) return RLSCAN_OK;
+    if (!rewards || !values || !log_rhos || !terminated || !vs || !pg_advantages)
+        return RLSCAN_ERR_NULL;
+    if (truncated && !bootstrap_values) return RLSCAN_ERR_NULL;
+    rc = check_alias({vs, pg_advantages}, {rewards, values, bootstrap_value, log_rhos, terminated,
+                                           truncated, bootstrap_values});
+    if (rc != RLSCAN_OK) return rc;
+    const VtraceParams p{rewards,   values, bootstrap_value, log_rhos,
+                         terminated, truncated, bootstrap_values, vs,
+                         pg_advantages, gamma, rho_bar, c_bar};
+    const bool vec = all_aligned({rewards, values, log_rhos, terminated, truncated,
+                                  bootstrap_values, vs, pg_advantages});
+    return run(RLSCAN_EST_VTRACE, N, T, vec, stream,
+               [&](const Geometry& g, const LookbackArgs& lb, int rounds, bool look) {
+                   return truncated ? launch_kernel<Vtrace<true>>(p, g, lb, rounds, look, vec, stream)
+                                    : launch_kernel<Vtrace<false>>(p, g, lb, rounds, look, vec, stream);
+               });
+}
+
+int rlscan_retrace(const float* rewards, const float* next_q_values_all,
+                   const float* next_target_probs, const int32_t* actions,
+                   const float* behaviour_probs, const float* terminated, const float* truncated,
+                   float* targets, int64_t N, int64_t T, int64_t A, float gamma, float lambda,
+                   hipStream_t stream) {
+    int rc = check_shape(N, T, A);
+    if (rc != RLSCAN_OK) return rc;
+    if (!unit_interval(gamma) || !unit_interval(lambda)) return RLSCAN_ERR_PARAM;
+    if (N == 0 || T == 0) return RLSCAN_OK;
+    if (!rewards || !next_q_values_all || !next_target_probs || !actions || !behaviour_probs ||
+        !terminated || !truncated || !targets)
+        return RLSCAN_ERR_NULL;
+    rc = check_alias({targets}, {rewards, next_q_values_all, next_target_probs, actions,
+                                 behaviour_probs, terminated, truncated});
+    if (rc != RLSCAN_OK) return rc;
+    const bool vec = all_aligned({rewards, next_q_values_all, next_target_probs, actions,
+                                  behaviour_probs, terminated, truncated, targets});
+    auto go = [&](auto tag) {
+        using E = decltype(tag);
+        typename E::Params p{rewards, next_q_values_all, next_target_probs, actions,
+                             behaviour_probs, terminated, truncated, targets, A, gamma, lambda};
+        return run(RLSCAN_EST_RETRACE, N, T, vec, stream,
+                   [&](const Geometry& g, const LookbackArgs& lb, int, bool look) {
+                       return launch_kernel_r1<E>(p, g, lb, look, vec, stream);
+                   });
+    };
+    switch (vec ? A : 0) {
+        case 4: return go(Retrace<4>{});
+        case 6: return go(Retrace<6>{});
+        case 8: return go(Retrace<8>{});
+        case 18: return go(Retrace<18>{});
+        default: return go(Retrace<0>{});
+    }
+}
+
+int rlscan_eligibility_traces(const float* x, const float* dones, float* traces, int64_t N,
+                              int64_t T, float gamma, float lambda, hipStream_t stream) {
+    int rc = check_shape(N, T);
+    if (rc != RLSCAN_OK) return rc;
+    if (!unit_interval(gamma) || !unit_interval(lambda)) return RLSCAN_ERR_PARAM;
+    if (N == 0 || T == 0) return RLSCAN_OK;
+    if (!x || !dones || !traces) return RLSCAN_ERR_NULL;
+    rc = check_alias({traces}, {x, dones});
+    if (rc != RLSCAN_OK) return rc;
+    Eligibility::Params p{x, dones, traces, gamma * lambda};
+    const bool vec = all_aligned({x, dones, traces});
+    return run(RLSCAN_EST_ELIGIBILITY, N, T, vec, stream,
+               [&](const Geometry& g, const LookbackArgs& lb, int rounds, bool look) {
+                   return launch_kernel<Eligibility>(p, g, lb, rounds, look, vec, stream);
+               });
+}
+
+int rlscan_episodic_prefix_sum(const int32_t* x, const float* dones, int64_t* out, int64_t N,
+                               int64_t T, hipStream_t stream) {
+    int rc = check_shape(N, T);
+    if (rc != RLSCAN_OK) return rc;
+    if (N == 0 || T == 0) return RLSCAN_OK;
+    if (!x || !dones || !out) return RLSCAN_ERR_NULL;
+    rc = check_alias({out}, {x, dones});
+    if (rc != RLSCAN_OK) return rc;
+    PrefixSum::Params p{x, dones, out};
+    const bool vec = all_aligned({x, dones, out});
+    return run(RLSCAN_EST_PREFIX_SUM, N, T, vec, stream,
+               [&](const Geometry& g, const LookbackArgs& lb, int rounds, bool look) {
+                   return launch_kernel<PrefixSum>(p, g, lb, rounds, look, vec, stream);
+               });
+}
+
+const char* rlscan_status_string(int status) {
+    switch (status) {
+        case RLSCAN_OK: return "ok";
+        case RLSCAN_ERR_NULL: return "a required pointer is NULL";
+        case RLSCAN_ERR_SHAPE: return "invalid shape (negative size, A < 1, or more than 2^48 elements)";
+        case RLSCAN_ERR_PARAM: return "parameter out of range";
+        case RLSCAN_ERR_ALIAS: return "an output aliases an input or the other output";
+        case RLSCAN_ERR_HIP: return "HIP runtime call or kernel launch failed";
+        case RLSCAN_ERR_ALLOC: return "could not allocate the look-back scratch";
+        default: return "unknown rlscan status";
+    }
+}
+
+const char* rlscan_version(void) { return "rlscan 0.1.0 gfx950"; }
+
+int rlscan_release_scratch(void) {
+    std::lock_guard<std::mutex> g(g_scratch_mutex);
+    int prev = 0;
+    const bool have_prev = hipGetDevice(&prev) == hipSuccess;
+    int rc = RLSCAN_OK;
+    for (auto& kv : g_scratch) {
+        Scratch* sc = kv.second.get();
+        std::lock_guard<std::mutex> gs(sc->m);
+        if (sc->status == nullptr && sc->counter == nullptr) continue;
+        if (hipSetDevice(kv.first.first) != hipSuccess) {
+            rc = RLSCAN_ERR_HIP;
+            continue;
+        }
+        if (sc->status) (void)hipFree(sc->status);
+        if (sc->counter) (void)hipFree(sc->counter);
+        sc->status = nullptr;
+        sc->counter = nullptr;
+        sc->capacity = 0;
+        sc->next_ticket = 0;
+        sc->epoch = 0;
+    }
+    g_scratch.clear();
+    if (have_prev) (void)hipSetDevice(prev);
+    return rc;
+}
+
+int rlscan_plan(int estimator, int64_t N, int64_t T, int64_t A, rlscan_plan_info* info) {
+    if (info == nullptr) return RLSCAN_ERR_NULL;
+    if (estimator < RLSCAN_EST_GAE || estimator > RLSCAN_EST_PREFIX_SUM) return RLSCAN_ERR_PARAM;
+    const int rc = check_shape(N, T, A);
+    if (rc != RLSCAN_OK) return rc;
+    std::memset(info, 0, sizeof(*info));
+    info->threads = kThreads;
+    if (N == 0 || T == 0) return RLSCAN_OK;
+    const Plan pl = make_plan(estimator, N, T, true);
+    info->mapping = pl.mapping;
+    info->rounds = pl.rounds;
+    info->tile_elems = pl.tile_elems;
+    info->tiles = pl.tiles;
+    info->grid = pl.grid;
+    return RLSCAN_OK;
+}
+
+int rlscan_lookback_timeouts(uint64_t* count) {
+    if (count == nullptr) return RLSCAN_ERR_NULL;
+    *count = 0;
+    std::lock_guard<std::mutex> g(g_scratch_mutex);
+    int prev = 0;
+    const bool have_prev = hipGetDevice(&prev) == hipSuccess;
+    int rc = RLSCAN_OK;
+    for (auto& kv : g_scratch) {
+        Scratch* sc = kv.second.get();
+        std::lock_guard<std::mutex> gs(sc->m);
+        if (sc->counter == nullptr) continue;
+        unsigned int n = 0;
+        if (hipSetDevice(kv.first.first) != hipSuccess ||
+            hipStreamSynchronize(reinterpret_cast<hipStream_t>(kv.first.second)) != hipSuccess ||
+            hipMemcpy(&n, sc->counter + 1, sizeof(n), hipMemcpyDeviceToHost) != hipSuccess) {
+            rc = RLSCAN_ERR_HIP;
+            continue;
+        }
+        *count += n;
+    }
+    if (have_prev) (void)hipSetDevice(prev);
+    return rc;
+}
+
+int rlscan_set_launch_override(int mapping, int rounds, int64_t grid_cap) {
+    if (mapping < RLSCAN_MAP_AUTO || mapping > RLSCAN_MAP_LOOKBACK) return RLSCAN_ERR_PARAM;
+    if (rounds != 0 && rounds != 1 && rounds != 2 && rounds != 4) return RLSCAN_ERR_PARAM;
+    if (grid_cap < 0) return RLSCAN_ERR_PARAM;
+    g_override.mapping.store(mapping);
+    g_override.rounds.store(rounds);
+    g_override.grid_cap.store(grid_cap);
+    return RLSCAN_OK;
+}
+
+}  // extern "C"

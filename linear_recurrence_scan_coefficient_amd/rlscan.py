@@ -1,0 +1,259 @@
+"""Thin ctypes binding of librlscan's C ABI (argument marshalling only).
+
+Each ``rlscan_*`` function here has the name and argument order of the C
+entry point declared in ``include/rlscan.h``; tensors replace raw device
+pointers and N, T (and A) are read from their shapes.  Outputs are
+caller-provided tensors, exactly as in C.  All computation runs in the HIP
+kernels of librlscan; this module has no fallback path: if the library is
+missing or fails to load, every call raises.
+
+PyTorch supplies device memory and the current stream only.  ``torch`` is
+imported before the library is loaded, so librlscan binds to the same HIP
+runtime as PyTorch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import build as _build
+
+LIB_PATH = _build.LIB_PATH
+
+RLSCAN_OK = 0
+RLSCAN_ERR_NULL = -1
+RLSCAN_ERR_SHAPE = -2
+RLSCAN_ERR_PARAM = -3
+RLSCAN_ERR_ALIAS = -4
+RLSCAN_ERR_HIP = -5
+RLSCAN_ERR_ALLOC = -6
+
+MAP_AUTO, MAP_PACKED, MAP_LOOKBACK = 0, 1, 2
+
+ESTIMATOR_IDS = {
+    "gae": 0, "lambda_returns": 1, "discounted_returns": 2, "vtrace": 3, "retrace": 4,
+    "eligibility_traces": 5, "episodic_prefix_sum": 6,
+}
+
+EXPORTED = (
+    "rlscan_gae", "rlscan_lambda_returns", "rlscan_discounted_returns", "rlscan_vtrace",
+    "rlscan_retrace", "rlscan_eligibility_traces", "rlscan_episodic_prefix_sum",
+    "rlscan_status_string", "rlscan_version", "rlscan_release_scratch", "rlscan_plan",
+    "rlscan_set_launch_override", "rlscan_lookback_timeouts",
+)
+
+
+class RlscanError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"rlscan error {status}: {message}")
+        self.status = status
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("mapping", ctypes.c_int32), ("rounds", ctypes.c_int32),
+                ("tile_elems", ctypes.c_int64), ("tiles", ctypes.c_int64),
+                ("grid", ctypes.c_int64), ("threads", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+
+
+def _declare(lib):
+    lib.rlscan_gae.argtypes = [_vp] * 7 + [_i64, _i64, _f32, _f32, _vp]
+    lib.rlscan_lambda_returns.argtypes = [_vp] * 7 + [_i64, _i64, _f32, _f32, _vp]
+    lib.rlscan_discounted_returns.argtypes = [_vp] * 6 + [_i64, _i64, _f32, _vp]
+    lib.rlscan_vtrace.argtypes = [_vp] * 9 + [_i64, _i64, _f32, _f32, _f32, _vp]
+    lib.rlscan_retrace.argtypes = [_vp] * 8 + [_i64, _i64, _i64, _f32, _f32, _vp]
+    lib.rlscan_eligibility_traces.argtypes = [_vp] * 3 + [_i64, _i64, _f32, _f32, _vp]
+    lib.rlscan_episodic_prefix_sum.argtypes = [_vp] * 3 + [_i64, _i64, _vp]
+    for name in ("rlscan_gae", "rlscan_lambda_returns", "rlscan_discounted_returns",
+                 "rlscan_vtrace", "rlscan_retrace", "rlscan_eligibility_traces",
+                 "rlscan_episodic_prefix_sum", "rlscan_release_scratch"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.rlscan_release_scratch.argtypes = []
+    lib.rlscan_status_string.argtypes = [ctypes.c_int]
+    lib.rlscan_status_string.restype = ctypes.c_char_p
+    lib.rlscan_version.argtypes = []
+    lib.rlscan_version.restype = ctypes.c_char_p
+    lib.rlscan_plan.argtypes = [ctypes.c_int, _i64, _i64, _i64, ctypes.POINTER(PlanInfo)]
+    lib.rlscan_plan.restype = ctypes.c_int
+    lib.rlscan_set_launch_override.argtypes = [ctypes.c_int, ctypes.c_int, _i64]
+    lib.rlscan_set_launch_override.restype = ctypes.c_int
+    lib.rlscan_lookback_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
+    lib.rlscan_lookback_timeouts.restype = ctypes.c_int
+
+
+def library(path: str = LIB_PATH):
+    """Loads librlscan.so (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"librlscan.so not found at {path}; build it first "
+            "(python -m linear_recurrence_scan_coefficient_amd.build)")
+    lib = ctypes.CDLL(path)
+    _declare(lib)
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return library().rlscan_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return library().rlscan_version().decode()
+
+
+def _check(status: int):
+    if status != RLSCAN_OK:
+        raise RlscanError(status, status_string(status))
+
+
+# ------------------------------------------------------------------ marshalling
+def _ptr(t, dtype=torch.float32, shape=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor or None")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() > 0 and t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _nt(t, name):
+    if t is None or t.dim() != 2:
+        raise ValueError(f"{name} must be a [N, T] tensor")
+    return t.shape
+
+
+# ------------------------------------------------------------------ entry points
+def rlscan_gae(rewards, values, bootstrap_value, terminated, truncated, bootstrap_values,
+               advantages, gamma, lam, stream=None):
+    N, T = _nt(rewards, "rewards")
+    _check(library().rlscan_gae(
+        _ptr(rewards, shape=(N, T), name="rewards"), _ptr(values, shape=(N, T), name="values"),
+        _ptr(bootstrap_value, shape=(N,), name="bootstrap_value"),
+        _ptr(terminated, shape=(N, T), name="terminated"),
+        _ptr(truncated, shape=(N, T), name="truncated"),
+        _ptr(bootstrap_values, shape=(N, T), name="bootstrap_values"),
+        _ptr(advantages, shape=(N, T), name="advantages"), N, T, gamma, lam, _stream(stream)))
+    return advantages
+
+
+def rlscan_lambda_returns(rewards, values, bootstrap_value, terminated, truncated,
+                          bootstrap_values, returns, gamma, lam, stream=None):
+    N, T = _nt(rewards, "rewards")
+    _check(library().rlscan_lambda_returns(
+        _ptr(rewards, shape=(N, T), name="rewards"), _ptr(values, shape=(N, T), name="values"),
+        _ptr(bootstrap_value, shape=(N,), name="bootstrap_value"),
+        _ptr(terminated, shape=(N, T), name="terminated"),
+        _ptr(truncated, shape=(N, T), name="truncated"),
+        _ptr(bootstrap_values, shape=(N, T), name="bootstrap_values"),
+        _ptr(returns, shape=(N, T), name="returns"), N, T, gamma, lam, _stream(stream)))
+    return returns
+
+
+def rlscan_discounted_returns(rewards, bootstrap_value, terminated, truncated, bootstrap_values,
+                              returns, gamma, stream=None):
+    N, T = _nt(rewards, "rewards")
+    _check(library().rlscan_discounted_returns(
+        _ptr(rewards, shape=(N, T), name="rewards"),
+        _ptr(bootstrap_value, shape=(N,), name="bootstrap_value"),
+        _ptr(terminated, shape=(N, T), name="terminated"),
+        _ptr(truncated, shape=(N, T), name="truncated"),
+        _ptr(bootstrap_values, shape=(N, T), name="bootstrap_values"),
+        _ptr(returns, shape=(N, T), name="returns"), N, T, gamma, _stream(stream)))
+    return returns
+
+
+def rlscan_vtrace(rewards, values, bootstrap_value, log_rhos, terminated, truncated,
+                  bootstrap_values, vs, pg_advantages, gamma, rho_bar, c_bar, stream=None):
+    N, T = _nt(rewards, "rewards")
+    _check(library().rlscan_vtrace(
+        _ptr(rewards, shape=(N, T), name="rewards"), _ptr(values, shape=(N, T), name="values"),
+        _ptr(bootstrap_value, shape=(N,), name="bootstrap_value"),
+        _ptr(log_rhos, shape=(N, T), name="log_rhos"),
+        _ptr(terminated, shape=(N, T), name="terminated"),
+        _ptr(truncated, shape=(N, T), name="truncated"),
+        _ptr(bootstrap_values, shape=(N, T), name="bootstrap_values"),
+        _ptr(vs, shape=(N, T), name="vs"), _ptr(pg_advantages, shape=(N, T), name="pg_advantages"),
+        N, T, gamma, rho_bar, c_bar, _stream(stream)))
+    return vs, pg_advantages
+
+
+def rlscan_retrace(rewards, next_q_values_all, next_target_probs, actions, behaviour_probs,
+                   terminated, truncated, targets, gamma, lam, stream=None):
+    N, T = _nt(rewards, "rewards")
+    if next_q_values_all is None or next_q_values_all.dim() != 3:
+        raise ValueError("next_q_values_all must be a [N, T, A] tensor")
+    A = next_q_values_all.shape[2]
+    _check(library().rlscan_retrace(
+        _ptr(rewards, shape=(N, T), name="rewards"),
+        _ptr(next_q_values_all, shape=(N, T, A), name="next_q_values_all"),
+        _ptr(next_target_probs, shape=(N, T, A), name="next_target_probs"),
+        _ptr(actions, dtype=torch.int32, shape=(N, T), name="actions"),
+        _ptr(behaviour_probs, shape=(N, T), name="behaviour_probs"),
+        _ptr(terminated, shape=(N, T), name="terminated"),
+        _ptr(truncated, shape=(N, T), name="truncated"),
+        _ptr(targets, shape=(N, T), name="targets"), N, T, A, gamma, lam, _stream(stream)))
+    return targets
+
+
+def rlscan_eligibility_traces(x, dones, traces, gamma, lam, stream=None):
+    N, T = _nt(x, "x")
+    _check(library().rlscan_eligibility_traces(
+        _ptr(x, shape=(N, T), name="x"), _ptr(dones, shape=(N, T), name="dones"),
+        _ptr(traces, shape=(N, T), name="traces"), N, T, gamma, lam, _stream(stream)))
+    return traces
+
+
+def rlscan_episodic_prefix_sum(x, dones, out, stream=None):
+    N, T = _nt(x, "x")
+    _check(library().rlscan_episodic_prefix_sum(
+        _ptr(x, dtype=torch.int32, shape=(N, T), name="x"),
+        _ptr(dones, shape=(N, T), name="dones"),
+        _ptr(out, dtype=torch.int64, shape=(N, T), name="out"), N, T, _stream(stream)))
+    return out
+
+
+def rlscan_release_scratch():
+    _check(library().rlscan_release_scratch())
+
+
+def rlscan_plan(estimator, N, T, A=1) -> dict:
+    info = PlanInfo()
+    est = ESTIMATOR_IDS[estimator] if isinstance(estimator, str) else int(estimator)
+    _check(library().rlscan_plan(est, N, T, A, ctypes.byref(info)))
+    return {f[0]: getattr(info, f[0]) for f in PlanInfo._fields_ if f[0] != "reserved"}
+
+
+def rlscan_set_launch_override(mapping=MAP_AUTO, rounds=0, grid_cap=0):
+    _check(library().rlscan_set_launch_override(int(mapping), int(rounds), int(grid_cap)))
+
+
+def rlscan_lookback_timeouts() -> int:
+    n = ctypes.c_uint64()
+    _check(library().rlscan_lookback_timeouts(ctypes.byref(n)))
+    return n.value

@@ -1,0 +1,149 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/rlscan.h declares, and every argument check returns its status
+before any HIP call (the fake pointers below are never dereferenced)."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rlscan.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from linear_recurrence_scan_coefficient_amd import build, rlscan
+    if build.is_stale():
+        build.build()
+    return rlscan.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rlscan_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_seven_estimators():
+    names = declared_functions()
+    for est in ("gae", "vtrace", "retrace", "lambda_returns", "discounted_returns",
+                "eligibility_traces", "episodic_prefix_sum"):
+        assert f"rlscan_{est}" in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from linear_recurrence_scan_coefficient_amd import rlscan
+    names = declared_functions()
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in rlscan.h but not exported"
+    assert sorted(rlscan.EXPORTED) == names
+
+
+def test_version_and_status_strings(lib):
+    from linear_recurrence_scan_coefficient_amd import rlscan
+    assert "gfx950" in rlscan.version()
+    for code in range(0, -7, -1):
+        s = rlscan.status_string(code)
+        assert s and s != "unknown rlscan status"
+    assert rlscan.status_string(-99) == "unknown rlscan status"
+
+
+# fake, distinct, 16-byte aligned "device pointers": only compared, never read
+P = [0x10000 * (i + 1) for i in range(12)]
+OK, NULL, SHAPE, PARAM, ALIAS = 0, -1, -2, -3, -4
+
+
+def gae(lib, *, ptrs=None, N=4, T=8, gamma=0.99, lam=0.95):
+    p = list(ptrs if ptrs is not None else P[:7])
+    return lib.rlscan_gae(*p, N, T, gamma, lam, None)
+
+
+def test_gae_argument_checks(lib):
+    assert gae(lib, N=-1) == SHAPE
+    assert gae(lib, T=-3) == SHAPE
+    assert gae(lib, N=1 << 30, T=1 << 30) == SHAPE
+    for bad in (-0.1, 1.5, math.nan, math.inf):
+        assert gae(lib, gamma=bad) == PARAM
+        assert gae(lib, lam=bad) == PARAM
+    # empty: success without touching any pointer
+    assert gae(lib, ptrs=[None] * 7, N=0) == OK
+    assert gae(lib, ptrs=[None] * 7, T=0) == OK
+    # required pointers
+    for i in (0, 1, 3, 6):
+        p = list(P[:7])
+        p[i] = None
+        assert gae(lib, ptrs=p) == NULL, i
+    p = list(P[:7])
+    p[5] = None  # truncated given without bootstrap_values
+    assert gae(lib, ptrs=p) == NULL
+    # output aliasing any input
+    for i in range(6):
+        p = list(P[:7])
+        p[6] = p[i]
+        assert gae(lib, ptrs=p) == ALIAS, i
+
+
+def test_other_entry_points_argument_checks(lib):
+    f = lib
+    # lambda returns: same shape as GAE
+    assert f.rlscan_lambda_returns(*P[:7], 4, 8, 2.0, 0.5, None) == PARAM
+    assert f.rlscan_lambda_returns(P[0], None, *P[2:7], 4, 8, 0.9, 0.5, None) == NULL
+    # discounted: values not needed, bootstrap_value optional
+    assert f.rlscan_discounted_returns(P[0], None, P[2], None, None, P[0], 4, 8, 0.9, None) == ALIAS
+    assert f.rlscan_discounted_returns(P[0], None, P[2], P[3], None, P[5], 4, 8, 0.9, None) == NULL
+    assert f.rlscan_discounted_returns(None, None, None, None, None, None, 0, 8, 0.9, None) == OK
+    # vtrace: clip levels > 0, +inf allowed (checked as far as the alias test)
+    args = P[:9]
+    assert f.rlscan_vtrace(*args, 4, 8, 0.9, 0.0, 1.0, None) == PARAM
+    assert f.rlscan_vtrace(*args, 4, 8, 0.9, 1.0, -1.0, None) == PARAM
+    assert f.rlscan_vtrace(*args, 4, 8, 0.9, math.nan, 1.0, None) == PARAM
+    same_out = list(args)
+    same_out[8] = same_out[7]
+    assert f.rlscan_vtrace(*same_out, 4, 8, 0.9, math.inf, math.inf, None) == ALIAS
+    # retrace: both flags required, A >= 1
+    assert f.rlscan_retrace(*P[:8], 4, 8, 0, 0.9, 0.9, None) == SHAPE
+    assert f.rlscan_retrace(*P[:6], None, P[7], 4, 8, 6, 0.9, 0.9, None) == NULL
+    assert f.rlscan_retrace(*P[:7], P[3], 4, 8, 6, 0.9, 0.9, None) == ALIAS
+    assert f.rlscan_retrace(*P[:8], 1 << 20, 1 << 20, 1 << 10, 0.9, 0.9, None) == SHAPE
+    # traces / prefix sum
+    assert f.rlscan_eligibility_traces(P[0], P[1], P[1], 4, 8, 0.9, 0.9, None) == ALIAS
+    assert f.rlscan_eligibility_traces(P[0], P[1], P[2], 4, 8, 0.9, -0.1, None) == PARAM
+    assert f.rlscan_episodic_prefix_sum(P[0], None, P[2], 4, 8, None) == NULL
+    assert f.rlscan_episodic_prefix_sum(P[0], P[1], P[0], 4, 8, None) == ALIAS
+    assert f.rlscan_episodic_prefix_sum(None, None, None, 3, 0, None) == OK
+
+
+def test_plan_mapping_choice(lib):
+    from linear_recurrence_scan_coefficient_amd import rlscan
+    rlscan.rlscan_set_launch_override()
+    # whole rows per tile: packed, no inter-workgroup traffic
+    p = rlscan.rlscan_plan("gae", 4096, 128)
+    assert p["mapping"] == rlscan.MAP_PACKED and p["rounds"] == 1
+    assert p["tile_elems"] == 1024 and p["tiles"] == 512 and p["grid"] == 512
+    assert p["threads"] == 256
+    assert rlscan.rlscan_plan("gae", 16384, 32)["mapping"] == rlscan.MAP_PACKED
+    assert rlscan.rlscan_plan("gae", 64, 512)["tiles"] == 32
+    # rows longer than a tile, or rows that do not divide it: look-back
+    assert rlscan.rlscan_plan("gae", 64, 8192)["mapping"] == rlscan.MAP_LOOKBACK
+    assert rlscan.rlscan_plan("gae", 5, 1000)["mapping"] == rlscan.MAP_LOOKBACK
+    big = rlscan.rlscan_plan("discounted_returns", 8, 1 << 20)
+    assert big["mapping"] == rlscan.MAP_LOOKBACK and big["rounds"] == 4
+    assert big["tiles"] == (8 << 20) // 4096
+    # a single tile never needs a carry
+    assert rlscan.rlscan_plan("gae", 3, 100)["mapping"] == rlscan.MAP_PACKED
+    # Retrace runs one round
+    assert rlscan.rlscan_plan("retrace", 8, 1 << 20, 6)["rounds"] == 1
+    # overrides
+    rlscan.rlscan_set_launch_override(rlscan.MAP_LOOKBACK, 2, 7)
+    p = rlscan.rlscan_plan("gae", 4096, 128)
+    assert p["mapping"] == rlscan.MAP_LOOKBACK and p["rounds"] == 2 and p["grid"] == 7
+    rlscan.rlscan_set_launch_override()
+    with pytest.raises(rlscan.RlscanError):
+        rlscan.rlscan_set_launch_override(rounds=3)
+    with pytest.raises(rlscan.RlscanError):
+        rlscan.rlscan_plan("gae", -1, 5)
+    assert rlscan.rlscan_plan("gae", 0, 5)["tiles"] == 0

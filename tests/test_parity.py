@@ -1,0 +1,224 @@
+"""GPU parity: every estimator through the C ABI against the float64 oracle,
+element by element, on the same seeded float32 inputs.
+
+Bar: |gpu - ref| <= 1e-4 * (1 + |ref|) for float32 outputs; identical values
+for the int64 prefix sum.  Shapes span several tiles with ragged tails, both
+launch mappings (whole rows per tile, and rows spread over tiles through the
+decoupled look-back), every round count, looping (grid-capped) launches,
+misaligned pointers, the degenerate flag patterns, empty inputs and the full
+benchmark workloads.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from reference import assert_parity, oracle_outputs
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+from linear_recurrence_scan_coefficient_amd import device, rlscan, workloads  # noqa: E402
+from linear_recurrence_scan_coefficient_amd.workloads import ESTIMATORS  # noqa: E402
+
+REVERSE_WITH_TRUNC = ("gae", "lambda_returns", "discounted_returns", "vtrace")
+
+
+@pytest.fixture(autouse=True)
+def _reset_override():
+    rlscan.rlscan_set_launch_override()
+    yield
+    rlscan.rlscan_set_launch_override()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _no_lookback_timeouts():
+    yield
+    assert rlscan.rlscan_lookback_timeouts() == 0
+
+
+def case(estimator, N, T, seed=0, **kw):
+    """A workload with many episode boundaries, truncation included where the
+    estimator takes it."""
+    opts = dict(term_p=0.05, done_p=0.05, gamma=0.97, lam=0.9)
+    if estimator in REVERSE_WITH_TRUNC or estimator == "retrace":
+        opts.update(trunc_mode="independent", trunc_p=0.05)
+    opts.update(kw)
+    w = workloads.custom(N, T, **opts)
+    return w, workloads.inputs_for(estimator, w, seed)
+
+
+def check(estimator, w, inputs, label=""):
+    print(f"[parity] {estimator} N={w.N} T={w.T} {label}", flush=True)
+    got = device.run(estimator, inputs, w)
+    assert_parity(got, oracle_outputs(estimator, inputs, w), f"{estimator} {w.N}x{w.T} {label}")
+
+
+SHAPES = [(1, 1), (1, 2), (3, 3), (2, 5), (7, 63), (5, 64), (3, 65), (4, 127), (2, 255),
+          (2, 256), (3, 257), (2, 1023), (1, 1024), (2, 1025), (1, 4097), (3, 5000), (37, 129),
+          (64, 512), (9, 1536), (2, 20000)]
+
+
+@pytest.mark.parametrize("estimator", ESTIMATORS)
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{n}x{t}" for n, t in SHAPES])
+def test_small_shapes(estimator, shape):
+    w, inputs = case(estimator, *shape, seed=shape[0] * 7919 + shape[1])
+    check(estimator, w, inputs)
+
+
+@pytest.mark.parametrize("estimator", ESTIMATORS)
+@pytest.mark.parametrize("mapping", ["lookback", "packed"])
+@pytest.mark.parametrize("rounds", [1, 2, 4])
+def test_mappings_and_rounds(estimator, mapping, rounds):
+    m = rlscan.MAP_LOOKBACK if mapping == "lookback" else rlscan.MAP_PACKED
+    rlscan.rlscan_set_launch_override(m, rounds)
+    for N, T in ((512, 128), (40, 4096), (3, 3001)):
+        w, inputs = case(estimator, N, T, seed=N + T + rounds)
+        plan = rlscan.rlscan_plan(estimator, N, T, w.A)
+        check(estimator, w, inputs, f"{mapping} R={rounds} plan={plan}")
+
+
+@pytest.mark.parametrize("estimator", ESTIMATORS)
+@pytest.mark.parametrize("mapping", ["lookback", "packed"])
+def test_grid_capped_loops(estimator, mapping):
+    m = rlscan.MAP_LOOKBACK if mapping == "lookback" else rlscan.MAP_PACKED
+    rlscan.rlscan_set_launch_override(m, 0, 13)
+    for N, T in ((256, 128), (5, 9000)):
+        w, inputs = case(estimator, N, T, seed=N * T)
+        check(estimator, w, inputs, f"{mapping} grid_cap=13")
+
+
+@pytest.mark.parametrize("estimator", ESTIMATORS)
+def test_flag_patterns(estimator):
+    N, T = 6, 700
+    w, inputs = case(estimator, N, T, seed=11)
+    flag_keys = [k for k in ("terminated", "truncated", "dones") if inputs.get(k) is not None]
+    first = np.zeros((N, T), np.float32)
+    first[:, 0] = 1
+    last = np.zeros((N, T), np.float32)
+    last[:, -1] = 1
+    alternating = np.zeros((N, T), np.float32)
+    alternating[1::2] = 1
+    patterns = {"none": np.zeros((N, T), np.float32), "all": np.ones((N, T), np.float32),
+                "first": first, "last": last, "row_alternating": alternating}
+    for name, pattern in patterns.items():
+        d = dict(inputs)
+        for k in flag_keys:
+            d[k] = pattern.copy()
+        check(estimator, w, d, f"flags={name}")
+    if estimator in REVERSE_WITH_TRUNC or estimator == "retrace":
+        d = dict(inputs)
+        d["terminated"] = np.ones((N, T), np.float32)
+        d["truncated"] = np.ones((N, T), np.float32)
+        check(estimator, w, d, "both flags everywhere (terminated wins)")
+
+
+@pytest.mark.parametrize("estimator", REVERSE_WITH_TRUNC)
+def test_optional_inputs(estimator):
+    w, inputs = case(estimator, 9, 777, seed=5, trunc_mode="none")
+    check(estimator, w, inputs, "no truncated tensor")
+    d = dict(inputs)
+    d["truncated"] = np.zeros((9, 777), np.float32)
+    d["bootstrap_values"] = np.full((9, 777), 123.0, np.float32)
+    check(estimator, w, d, "all-zero truncated tensor")
+    d = dict(inputs)
+    d["bootstrap_value"] = None
+    check(estimator, w, d, "no per-row bootstrap value")
+
+
+@pytest.mark.parametrize("estimator", ESTIMATORS)
+def test_misaligned_pointers(estimator):
+    """Inputs and outputs offset by one element: the scalar-load path."""
+    N, T = 33, 250
+    w, inputs = case(estimator, N, T, seed=3)
+    d = device.upload(inputs)
+    shifted = {}
+    for k, v in d.items():
+        if v is None:
+            shifted[k] = None
+            continue
+        buf = torch.empty(v.numel() + 1, dtype=v.dtype, device=v.device)
+        view = buf[1:].view(v.shape)
+        view.copy_(v)
+        shifted[k] = view
+    outs = {}
+    for name, dt in device.OUTPUTS[estimator]:
+        buf = torch.empty(N * T + 1, dtype=dt, device="cuda")
+        outs[name] = buf[1:].view(N, T)
+    print(f"[parity] misaligned {estimator}", flush=True)
+    device.call(estimator, shifted, outs, w)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in outs.items()}
+    assert_parity(got, oracle_outputs(estimator, inputs, w), f"misaligned {estimator}")
+
+
+@pytest.mark.parametrize("A", [1, 3, 4, 5, 6, 8, 18])
+def test_retrace_action_counts(A):
+    w, inputs = case("retrace", 17, 300, seed=A, A=A)
+    check("retrace", w, inputs, f"A={A}")
+
+
+def test_retrace_out_of_range_actions_do_not_fault():
+    w, inputs = case("retrace", 4, 200, seed=9)
+    inputs["actions"][:, ::7] = 99
+    inputs["actions"][:, 3::7] = -5
+    print("[parity] retrace out-of-range actions", flush=True)
+    got = device.run("retrace", inputs, w)
+    assert got["targets"].shape == (4, 200)
+
+
+@pytest.mark.parametrize("estimator", ESTIMATORS)
+def test_empty_inputs(estimator):
+    for N, T in ((0, 5), (5, 0), (0, 0)):
+        w, inputs = case(estimator, max(N, 1), max(T, 1), seed=1)
+        d = device.upload({k: (None if v is None else v[:N, :T] if v.ndim >= 2 else v[:N])
+                           for k, v in inputs.items()})
+        outs = device.alloc_outputs(estimator, N, T)
+        w0 = workloads.custom(N, T, gamma=w.gamma, lam=w.lam)
+        device.call(estimator, d, outs, w0)
+    torch.cuda.synchronize()
+
+
+def test_many_lookback_calls_and_scratch_growth():
+    """Consecutive look-back calls with varying tile counts (epochs, ticket
+    bases and scratch growth), on the default and on a side stream."""
+    rlscan.rlscan_set_launch_override(rlscan.MAP_LOOKBACK, 1)
+    side = torch.cuda.Stream()
+    for i, (N, T) in enumerate([(2, 3000), (50, 999), (1, 70000), (3, 5), (9, 2**17),
+                                (2, 3000)] * 3):
+        w, inputs = case("gae", N, T, seed=i)
+        d = device.upload(inputs)
+        out = device.alloc_outputs("gae", N, T)
+        stream = side if i % 2 else None
+        if stream is not None:
+            stream.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(stream):
+                device.call("gae", d, out, w)
+            torch.cuda.current_stream().wait_stream(stream)
+        else:
+            device.call("gae", d, out, w)
+        torch.cuda.synchronize()
+        print(f"[parity] look-back call {i} {N}x{T}", flush=True)
+        assert_parity({k: v.cpu().numpy() for k, v in out.items()},
+                      oracle_outputs("gae", inputs, w), f"call {i}")
+    assert rlscan.rlscan_lookback_timeouts() == 0
+
+
+def test_prefix_sum_large_magnitudes():
+    N, T = 3, 50000
+    w = workloads.custom(N, T, done_p=1e-4)
+    inputs = workloads.prefix_inputs(w, 0)
+    inputs["x"] = np.random.default_rng(0).integers(2**31 - 100, 2**31 - 1, (N, T)).astype(np.int32)
+    check("episodic_prefix_sum", w, inputs, "values near int32 max")
+
+
+# ------------------------------------------------------------ full workloads
+FULL = [(name, est) for name, wl in workloads.WORKLOADS.items() for est in wl.estimators]
+
+
+@pytest.mark.parametrize("name,estimator", FULL, ids=[f"{n}-{e}" for n, e in FULL])
+def test_benchmark_workloads(name, estimator):
+    w = workloads.get(name)
+    inputs = workloads.inputs_for(estimator, w, 0)
+    check(estimator, w, inputs, name)
