@@ -1,0 +1,380 @@
+"""Benchmark of the rlscan hot path on one MI355X.
+
+One step = one call of each of the seven estimators (GAE, V-trace, Retrace,
+TD(lambda), discounted returns, eligibility traces, episodic prefix sum) on
+the production-regime workload: 4096 environments x 128 steps, float32,
+inputs from the seeded generators (synthetic data with the distributions the
+pages benchmark).  Every estimator reads its own input arrays, and steps
+rotate over several buffer sets whose total exceeds the 256 MiB last-level
+cache, so each call reads its inputs from HBM.  Inputs are resident on the
+GPU before the timed region starts.
+
+Timing.  The timed region is K steps, each the replay of one HIP graph that
+holds the seven launches on the next buffer set (every call here takes the
+packed mapping, which launches one kernel and is graph-safe), bracketed by
+device synchronisation; `value` is estimator-elements per second over it
+(7 * N * T elements per step), `ms_per_step` its mean.  The same steps
+launched call by call from Python ("eager") and on one warm buffer set are
+reported beside it.  Each estimator's average launch duration is then
+measured live with HIP events around replays of a graph of M back-to-back
+launches over M distinct buffer sets (M * bytes >= 512 MiB, so inputs come
+from HBM); `roofline` reports the estimator with the longest launch.  The
+long-sequence workload (8 x 2^20 steps, four estimators, decoupled
+look-back, launched eagerly with events around each call) and the float64
+oracle timed on one host core are reported as well.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("elements/s and achieved HBM GB/s per estimator at N=4096,T=128 and long-T; "
+          "per-call µs")
+HBM_PEAK_GBS = 8000.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["include/rlscan.h"] + [
+    os.path.join("linear_recurrence_scan_coefficient_amd", "csrc", f)
+    for f in ("rlscan.hip", "scan_core.hpp", "lookback.hpp", "estimators.hpp")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=6, help="rotated buffer sets (cold HBM)")
+    ap.add_argument("--long-calls", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--only", default=None, help="comma list of estimators (profiling runs)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ raw calls
+def raw_call_args(est, d, out, w, stream):
+    """The C argument tuple of one call (device pointers as ints)."""
+    def p(t):
+        return None if t is None else t.data_ptr()
+    N, T = w.N, w.T
+    if est == "gae":
+        return ("rlscan_gae", (p(d["rewards"]), p(d["values"]), p(d.get("bootstrap_value")),
+                               p(d["terminated"]), p(d.get("truncated")),
+                               p(d.get("bootstrap_values")), p(out["advantages"]), N, T,
+                               w.gamma, w.lam, stream))
+    if est == "lambda_returns":
+        return ("rlscan_lambda_returns", (p(d["rewards"]), p(d["values"]),
+                                          p(d.get("bootstrap_value")), p(d["terminated"]),
+                                          p(d.get("truncated")), p(d.get("bootstrap_values")),
+                                          p(out["returns"]), N, T, w.gamma, w.lam, stream))
+    if est == "discounted_returns":
+        return ("rlscan_discounted_returns", (p(d["rewards"]), p(d.get("bootstrap_value")),
+                                              p(d["terminated"]), p(d.get("truncated")),
+                                              p(d.get("bootstrap_values")), p(out["returns"]),
+                                              N, T, w.gamma, stream))
+    if est == "vtrace":
+        return ("rlscan_vtrace", (p(d["rewards"]), p(d["values"]), p(d.get("bootstrap_value")),
+                                  p(d["log_rhos"]), p(d["terminated"]), p(d.get("truncated")),
+                                  p(d.get("bootstrap_values")), p(out["vs"]),
+                                  p(out["pg_advantages"]), N, T, w.gamma, w.rho_bar, w.c_bar,
+                                  stream))
+    if est == "retrace":
+        A = d["next_q_values_all"].shape[2]
+        return ("rlscan_retrace", (p(d["rewards"]), p(d["next_q_values_all"]),
+                                   p(d["next_target_probs"]), p(d["actions"]),
+                                   p(d["behaviour_probs"]), p(d["terminated"]), p(d["truncated"]),
+                                   p(out["targets"]), N, T, A, w.gamma, w.lam, stream))
+    if est == "eligibility_traces":
+        return ("rlscan_eligibility_traces", (p(d["x"]), p(d["dones"]), p(out["traces"]), N, T,
+                                              w.gamma, w.lam, stream))
+    if est == "episodic_prefix_sum":
+        return ("rlscan_episodic_prefix_sum", (p(d["x"]), p(d["dones"]), p(out["out"]), N, T,
+                                               stream))
+    raise ValueError(est)
+
+
+def algorithmic_bytes(inputs: dict, outputs: dict) -> int:
+    """Bytes the method must move: every input read once, every output
+    written once."""
+    return int(sum(v.nbytes for v in inputs.values() if v is not None) +
+               sum(o.numel() * o.element_size() for o in outputs.values()))
+
+
+class CallSet:
+    """Device buffers and ready-made C calls for a list of estimators."""
+
+    def __init__(self, estimators, w, seed, stream_handle, lib):
+        from linear_recurrence_scan_coefficient_amd import device, workloads
+        self.calls = []
+        self.bytes = {}
+        self.keep = []
+        for est in estimators:
+            host = workloads.inputs_for(est, w, seed)
+            d = device.upload(host)
+            out = device.alloc_outputs(est, w.N, w.T)
+            name, args = raw_call_args(est, d, out, w, stream_handle)
+            self.calls.append((est, getattr(lib, name), args))
+            self.bytes[est] = algorithmic_bytes(host, out)
+            self.keep.append((d, out))
+
+    def run(self, events=None):
+        for i, (est, fn, args) in enumerate(self.calls):
+            if events is not None:
+                events[i].record()
+            rc = fn(*args)
+            if rc != 0:
+                raise RuntimeError(f"{est}: rlscan status {rc}")
+        if events is not None:
+            events[len(self.calls)].record()
+
+
+def time_eager_calls(torch, sets, reps):
+    """Mean microseconds per call, each call bracketed by HIP events (for
+    calls long enough that launch gaps do not matter, and for the look-back
+    mapping, which is not captured into graphs)."""
+    ests = [c[0] for c in sets[0].calls]
+    sets[0].run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ests) + 1)]
+          for _ in range(reps)]
+    for i in range(reps):
+        sets[i % len(sets)].run(ev[i])
+    torch.cuda.synchronize()
+    return {e: sum(row[j].elapsed_time(row[j + 1]) for row in ev) / reps * 1000.0
+            for j, e in enumerate(ests)}
+
+
+def capture_graph(torch, calls):
+    """One HIP graph holding `calls` in order (packed launches only: each call
+    enqueues exactly one kernel and nothing else)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        h = torch.cuda.current_stream().cuda_stream
+        for est, fn, args in calls:
+            rc = fn(*args[:-1], h)
+            if rc != 0:
+                raise RuntimeError(f"{est}: rlscan status {rc} during capture")
+    return g
+
+
+def time_graph_steps(torch, graphs, steps, warmup):
+    """Wall seconds of `steps` steps, step i replaying graphs[i % len]."""
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def time_eager_steps(torch, sets, steps, warmup):
+    """Wall seconds of `steps` steps launched one C call at a time."""
+    for i in range(warmup):
+        sets[i % len(sets)].run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        sets[i % len(sets)].run()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def time_launches(torch, graph, launches, reps):
+    """Mean device time per launch of a graph of `launches` back-to-back
+    launches, from HIP events recorded around each replay on the launch
+    stream."""
+    graph.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        graph.replay()
+        b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    return sum(ms) / len(ms) / launches * 1000.0
+
+
+def per_kernel(torch, est, w, sh, lib, min_bytes=512 << 20, reps=10):
+    """Average launch duration of one estimator over M distinct buffer sets
+    (M * bytes >= min_bytes, so every launch reads cold inputs)."""
+    probe = CallSet([est], w, 0, sh, lib)
+    b = probe.bytes[est]
+    m = max(6, min(64, -(-min_bytes // b)))
+    sets = [probe] + [CallSet([est], w, seed, sh, lib) for seed in range(1, m)]
+    g = capture_graph(torch, [s.calls[0] for s in sets])
+    us = time_launches(torch, g, m, reps)
+    del g, sets
+    return us, b, m
+
+
+def launch_floor_us(torch, grid, launches=64, reps=10):
+    from linear_recurrence_scan_coefficient_amd import rlscan
+    lib = rlscan.library()
+    calls = [("empty", lib.rlscan_launch_floor, (grid, None))] * launches
+    g = capture_graph(torch, calls)
+    return time_launches(torch, g, launches, reps)
+
+
+def read_traffic(kernel_label: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if the committed
+    summary was taken on the current kernel sources."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{kernel_label}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, estimators, seconds):
+    """The float64 oracle, single-threaded, on host copies of the same
+    workload, repeated for about `seconds`."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from reference import oracle_outputs
+    from linear_recurrence_scan_coefficient_amd import workloads
+    host = {e: workloads.inputs_for(e, w, 0) for e in estimators}
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        for e in estimators:
+            oracle_outputs(e, host[e], w)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    elems = reps * len(estimators) * w.N * w.T
+    return {"value": elems / el, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": (f"all {len(estimators)} estimators on {w.name} ({w.N}x{w.T}), "
+                       f"{reps} repetitions in {el:.1f} s, float64 C loops, one thread"),
+            "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "split of this path is a design note, not a measured configuration.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_recurrence_scan_coefficient_amd import build, rlscan, workloads
+    if not os.path.exists(build.LIB_PATH):
+        build.build()
+    lib = rlscan.library()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    w = workloads.get("production_4096x128")
+    ests = list(w.estimators) if args.only is None else args.only.split(",")
+    for e in ests:
+        assert rlscan.rlscan_plan(e, w.N, w.T, w.A)["mapping"] == rlscan.MAP_PACKED
+    print(f"[bench] preparing {args.sets} buffer sets of {w.name}", file=sys.stderr, flush=True)
+    sets = [CallSet(ests, w, seed, sh, lib) for seed in range(args.sets)]
+    set_bytes = sum(sets[0].bytes.values())
+    graphs = [capture_graph(torch, s.calls) for s in sets]
+    elems_per_step = len(ests) * w.N * w.T
+
+    # timed region: K steps, each one graph replay of the seven calls on the
+    # next buffer set
+    print("[bench] timing production steps", file=sys.stderr, flush=True)
+    wall = time_graph_steps(torch, graphs, args.steps, args.warmup)
+    ms_per_step = wall * 1000.0 / args.steps
+    value = elems_per_step * args.steps / wall
+    # the same steps launched call by call from Python, and on warm buffers
+    wall_eager = time_eager_steps(torch, sets, args.steps, args.warmup)
+    wall_warm = time_graph_steps(torch, graphs[:1], args.steps, args.warmup)
+    del graphs
+
+    print("[bench] timing each estimator's launches", file=sys.stderr, flush=True)
+    per_est = {}
+    for e in ests:
+        us, b, m = per_kernel(torch, e, w, sh, lib)
+        gbs = b / (us * 1e-6) / 1e9
+        per_est[e] = {"us_per_call": round(us, 3), "elements_per_s": w.N * w.T / (us * 1e-6),
+                      "bytes": b, "GB_per_s": round(gbs, 1),
+                      "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "buffer_sets": m}
+    dom = max(ests, key=lambda e: per_est[e]["us_per_call"])
+    d = per_est[dom]
+    traffic = read_traffic(f"{dom}_{w.name}")
+    plan = rlscan.rlscan_plan(dom, w.N, w.T, w.A)
+    floor = launch_floor_us(torch, plan["grid"])
+
+    result = {
+        "metric": METRIC, "value": value, "unit": "elements/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "N": w.N, "T": w.T, "estimators": ests, "A": w.A,
+                   "gamma": w.gamma, "lambda": w.lam, "buffer_sets": args.sets,
+                   "bytes_per_step": set_bytes, "launch": "one HIP graph per step"},
+        "roofline": {"bound": "hbm", "achieved": d["GB_per_s"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": d["frac_hbm_peak"], "traffic": traffic,
+                     "kernel": dom, "algorithmic_bytes_per_launch": d["bytes"],
+                     "avg_launch_us": d["us_per_call"]},
+        "per_estimator": per_est,
+        "eager": {"value": elems_per_step * args.steps / wall_eager,
+                  "ms_per_step": wall_eager * 1000.0 / args.steps},
+        "warm": {"value": elems_per_step * args.steps / wall_warm,
+                 "ms_per_step": wall_warm * 1000.0 / args.steps},
+        "launch_floor_us": {"grid": plan["grid"], "us": round(floor, 3)},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+
+    if not args.no_long:
+        wl = workloads.get("long_8x1048576")
+        print("[bench] timing long-sequence calls", file=sys.stderr, flush=True)
+        lsets = [CallSet(wl.estimators, wl, seed, sh, lib) for seed in range(2)]
+        lper = time_eager_calls(torch, lsets, args.long_calls)
+        long_res = {}
+        for e in wl.estimators:
+            b = lsets[0].bytes[e]
+            us = lper[e]
+            long_res[e] = {"us_per_call": round(us, 2),
+                           "elements_per_s": wl.N * wl.T / (us * 1e-6), "bytes": b,
+                           "GB_per_s": round(b / (us * 1e-6) / 1e9, 1),
+                           "frac_hbm_peak": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        result["long_8x1048576"] = long_res
+        del lsets
+
+    assert rlscan.rlscan_lookback_timeouts() == 0
+
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, ests, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

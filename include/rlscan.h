@@ -61,7 +61,11 @@
  *             allocated on first need and grown when a call needs more; it is
  *             released by rlscan_release_scratch().  Calls that use it from
  *             several host threads on one stream are serialised internally.
- *             Calls on one stream are not safe to capture into a HIP graph.
+ * Graphs      Calls whose tiles hold whole rows (the packed mapping, see
+ *             rlscan_plan) launch one kernel and nothing else, and may be
+ *             captured into a HIP graph.  A call that needs the look-back
+ *             returns RLSCAN_ERR_CAPTURE on a capturing stream, since its
+ *             replay would reuse a stale ticket base.
  * Thread      All entry points may be called concurrently from several host
  * safety      threads.
  */
@@ -82,7 +86,8 @@ typedef enum {
     RLSCAN_ERR_PARAM = -3, /* gamma/lambda/rho_bar/c_bar out of range           */
     RLSCAN_ERR_ALIAS = -4, /* an output pointer equals an input or other output */
     RLSCAN_ERR_HIP = -5,   /* a HIP runtime call or kernel launch failed        */
-    RLSCAN_ERR_ALLOC = -6  /* the library could not allocate its scratch        */
+    RLSCAN_ERR_ALLOC = -6, /* the library could not allocate its scratch        */
+    RLSCAN_ERR_CAPTURE = -7 /* a look-back launch on a stream under graph capture */
 } rlscan_status;
 
 /* GAE (README, Kernels table, compute_gae: a backward scan that adds each
@@ -224,6 +229,11 @@ int rlscan_plan(int estimator, int64_t N, int64_t T, int64_t A, rlscan_plan_info
  * grid_cap: 0 = one workgroup per tile, else at most this many workgroups,
  * each looping over tiles.  Returns RLSCAN_ERR_PARAM for other values. */
 int rlscan_set_launch_override(int mapping, int rounds, int64_t grid_cap);
+
+/* Diagnostics: enqueues an empty kernel of `grid` workgroups of 256 threads
+ * on `stream` -- the launch-bound floor of a scan launch with that grid.
+ * Returns RLSCAN_ERR_SHAPE unless 1 <= grid < 2^24. */
+int rlscan_launch_floor(int64_t grid, hipStream_t stream);
 
 /* Diagnostics: waits in the look-back are bounded (a few seconds per
  * predecessor); a wait that reaches the bound is counted, its tile's results

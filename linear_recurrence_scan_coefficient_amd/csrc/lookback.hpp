@@ -1,6 +1,6 @@
 // lookback.hpp -- single-pass decoupled look-back between the workgroups that
-// share one long row (Merrill & Garland, "Single-pass Parallel Prefix Scan
-// with Decoupled Look-back", 2016), for the (a, b) recurrence steps.
+// share one long row (after Merrill & Garland, "Single-pass Parallel Prefix
+// Scan with Decoupled Look-back", 2016), for the (a, b) recurrence steps.
 //
 // Protocol, per call:
 //  * Each workgroup takes a ticket from a 64-bit counter that is never reset;
@@ -10,19 +10,22 @@
 //    tiles, so a workgroup only ever waits on tiles already claimed by
 //    running workgroups: forward progress needs no assumption about the
 //    dispatch order.
-//  * Tile s publishes its aggregate step (flag AGG) as soon as its local scan
-//    is done -- or, when it already knows its outgoing state (it is tile 0,
-//    or its aggregate cuts the chain, a == 0), that state directly (flag
-//    INCL).  After the look-back it publishes INCL.
-//  * Flags carry the call's epoch (flag = epoch << 2 | kind), so entries left
-//    by earlier calls read as "not ready" and no clearing pass is needed.
-//  * The look-back walks s-1, s-2, ... composing aggregates until it meets an
-//    INCL entry or the composed step cuts the chain.
-//
-// Values and flags live in separate 64-bit words.  Each value word is written
-// once per call before its flag is released (agent-scope release store), and
-// read only after the flag is acquired (agent-scope acquire load), so readers
-// on other XCDs never see a torn or stale value.
+//  * Tile s publishes its aggregate step (AGG) as soon as its local scan is
+//    done -- or, when it already knows its outgoing state (it is tile 0, or
+//    its aggregate cuts the chain, a == 0), that state (INCL).  After the
+//    look-back it publishes INCL.
+//  * Every status word is self-validating: 64 bits = 32-bit call tag (the
+//    call's epoch) | 32-bit payload.  A word whose tag is not the current
+//    epoch is "not ready", so entries left by earlier calls need no clearing
+//    pass, and each word is read and written with one relaxed agent-scope
+//    atomic: no release/acquire fences, hence no L2 write-back or invalidate
+//    on any XCD.  A payload wider than 32 bits spans two words, each
+//    validated by its own tag; each word is written once per call.
+//  * The look-back is wave-parallel: wave 0 reads the status of 64
+//    predecessors at once, waits until every one of them up to the nearest
+//    terminal entry (INCL, or an aggregate that cuts the chain) is ready,
+//    folds them with one wave scan, and moves the window back by 64 tiles
+//    if no terminal entry was in it.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -33,72 +36,95 @@
 namespace rlscan {
 
 struct TileStatus {
-    uint64_t flag;   // epoch << 2 | kind
-    uint64_t agg_a;  // aggregate step, a part  } written before flag = AGG
-    uint64_t agg_b;  // aggregate step, b part  }
-    uint64_t incl;   // outgoing state (written before flag = INCL)
+    uint64_t w[4];  // float: agg a, agg b, incl x, -; int: agg b lo/hi, incl x lo/hi
 };
-
-constexpr uint64_t kFlagAgg = 1;
-constexpr uint64_t kFlagIncl = 2;
 
 struct LookbackArgs {
     TileStatus* status;       // >= number of tiles entries
     unsigned long long* ticket_counter;
     unsigned int* timeouts;   // count of look-back waits that gave up
     uint64_t ticket_base;
-    uint64_t epoch;           // >= 1, distinct for every call on this scratch
+    uint32_t tag;             // the call's epoch: nonzero, distinct for every
+                              // call since the status buffer was cleared
 };
 
-// Upper bound on the polls of one predecessor's status (each poll sleeps
-// about 64 cycles plus a memory round trip: several seconds in all).  A wait
-// that long means the protocol is broken; the workgroup then records the
-// failure, writes a poisoned result and finishes, so the kernel always ends.
+// Upper bound on the polls of one look-back window (each poll sleeps about
+// 64 cycles plus a memory round trip: several seconds in all).  A wait that
+// long means the protocol is broken; the workgroup then records the failure,
+// writes a poisoned result and finishes, so the kernel always ends.
 constexpr uint32_t kMaxPolls = 1u << 22;
 
 __device__ __forceinline__ float poisoned(float) { return __builtin_nanf(""); }
 __device__ __forceinline__ int64_t poisoned(int64_t) { return INT64_MIN; }
 
-// Packing of aggregate steps and states into 64-bit words.
-struct PackedStep {
-    uint64_t a, b;
-};
-__device__ __forceinline__ PackedStep pack_step(StepD s) {
-    return {static_cast<uint64_t>(__double_as_longlong(s.a)), __float_as_uint(s.b)};
+__device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t payload) {
+    return (static_cast<uint64_t>(tag) << 32) | payload;
 }
-__device__ __forceinline__ StepD unpack_step(PackedStep u, StepD) {
-    return {__longlong_as_double(static_cast<long long>(u.a)),
-            __uint_as_float(static_cast<uint32_t>(u.b))};
+__device__ __forceinline__ void store_word(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// An integer aggregate that is published as AGG never cuts the chain (a cut
-// aggregate is published as INCL), so its a is 1 and only b is stored.
-__device__ __forceinline__ PackedStep pack_step(StepI s) {
-    return {1u, static_cast<uint64_t>(s.b)};
+__device__ __forceinline__ uint64_t load_word(uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ StepI unpack_step(PackedStep u, StepI) {
-    return {1u, static_cast<int64_t>(u.b)};
-}
-__device__ __forceinline__ uint64_t pack_state(float x) { return __float_as_uint(x); }
-__device__ __forceinline__ float unpack_state(uint64_t u, float) {
-    return __uint_as_float(static_cast<uint32_t>(u));
-}
-__device__ __forceinline__ uint64_t pack_state(int64_t x) { return static_cast<uint64_t>(x); }
-__device__ __forceinline__ int64_t unpack_state(uint64_t u, int64_t) {
-    return static_cast<int64_t>(u);
+__device__ __forceinline__ bool has_tag(uint64_t w, uint32_t tag) {
+    return static_cast<uint32_t>(w >> 32) == tag;
 }
 
-__device__ __forceinline__ void publish_aggregate(TileStatus* st, PackedStep value,
-                                                  uint64_t epoch) {
-    __hip_atomic_store(&st->agg_a, value.a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&st->agg_b, value.b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&st->flag, (epoch << 2) | kFlagAgg, __ATOMIC_RELEASE,
-                       __HIP_MEMORY_SCOPE_AGENT);
+// ---------------------------------------------------------------- publish
+// The float aggregate's a is published rounded once to float32: a single
+// rounding, unlike the many that motivated the float64 a in StepD.
+__device__ __forceinline__ void publish_aggregate(TileStatus* st, StepD s, uint32_t tag) {
+    store_word(&st->w[0], tagged(tag, __float_as_uint(static_cast<float>(s.a))));
+    store_word(&st->w[1], tagged(tag, __float_as_uint(s.b)));
+}
+__device__ __forceinline__ void publish_inclusive(TileStatus* st, float x, uint32_t tag) {
+    store_word(&st->w[2], tagged(tag, __float_as_uint(x)));
+}
+// An integer aggregate published as AGG never cuts the chain (a cut aggregate
+// is published as INCL), so its a is 1 and only b is stored.
+__device__ __forceinline__ void publish_aggregate(TileStatus* st, StepI s, uint32_t tag) {
+    const uint64_t b = static_cast<uint64_t>(s.b);
+    store_word(&st->w[0], tagged(tag, static_cast<uint32_t>(b)));
+    store_word(&st->w[1], tagged(tag, static_cast<uint32_t>(b >> 32)));
+}
+__device__ __forceinline__ void publish_inclusive(TileStatus* st, int64_t x, uint32_t tag) {
+    const uint64_t u = static_cast<uint64_t>(x);
+    store_word(&st->w[2], tagged(tag, static_cast<uint32_t>(u)));
+    store_word(&st->w[3], tagged(tag, static_cast<uint32_t>(u >> 32)));
 }
 
-__device__ __forceinline__ void publish_inclusive(TileStatus* st, uint64_t state, uint64_t epoch) {
-    __hip_atomic_store(&st->incl, state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&st->flag, (epoch << 2) | kFlagIncl, __ATOMIC_RELEASE,
-                       __HIP_MEMORY_SCOPE_AGENT);
+// ---------------------------------------------------------------- read
+// Returns 0 (not ready), 1 (aggregate) or 2 (inclusive state, given as the
+// step (0, x)), and the step in `s`.
+__device__ __forceinline__ int read_status(TileStatus* st, uint32_t tag, StepD& s) {
+    const uint64_t x = load_word(&st->w[2]);
+    const uint64_t a = load_word(&st->w[0]);
+    const uint64_t b = load_word(&st->w[1]);
+    if (has_tag(x, tag)) {
+        s = {0.0, __uint_as_float(static_cast<uint32_t>(x))};
+        return 2;
+    }
+    if (has_tag(a, tag) && has_tag(b, tag)) {
+        s = {static_cast<double>(__uint_as_float(static_cast<uint32_t>(a))),
+             __uint_as_float(static_cast<uint32_t>(b))};
+        return 1;
+    }
+    return 0;
+}
+__device__ __forceinline__ int read_status(TileStatus* st, uint32_t tag, StepI& s) {
+    const uint64_t xl = load_word(&st->w[2]);
+    const uint64_t xh = load_word(&st->w[3]);
+    const uint64_t bl = load_word(&st->w[0]);
+    const uint64_t bh = load_word(&st->w[1]);
+    if (has_tag(xl, tag) && has_tag(xh, tag)) {
+        s = {0u, static_cast<int64_t>(((xh & 0xffffffffull) << 32) | (xl & 0xffffffffull))};
+        return 2;
+    }
+    if (has_tag(bl, tag) && has_tag(bh, tag)) {
+        s = {1u, static_cast<int64_t>(((bh & 0xffffffffull) << 32) | (bl & 0xffffffffull))};
+        return 1;
+    }
+    return 0;
 }
 
 __device__ __forceinline__ uint64_t take_ticket(const LookbackArgs& lb) {
@@ -107,38 +133,45 @@ __device__ __forceinline__ uint64_t take_ticket(const LookbackArgs& lb) {
     return static_cast<uint64_t>(t) - lb.ticket_base;
 }
 
-// State entering tile `tile` (tile >= 1), by walking back over tiles
-// tile-1, tile-2, ...  Called by one thread.  Terminates: tile 0 always
+// State entering tile `tile` (tile >= 1).  Called by all 64 lanes of one
+// wave; every lane returns the same value.  Terminates: tile 0 always
 // publishes INCL, and every earlier tile has been claimed by a running
-// workgroup that publishes without waiting on later tiles; the poll bound
-// above ends the wait even if that invariant were ever broken.
-template <class S, class V>
-__device__ V look_back(const LookbackArgs& lb, uint64_t tile) {
-    S acc = identity_step(S{});
-    uint64_t p = tile - 1;
+// workgroup that publishes its aggregate without waiting on later tiles; the
+// poll bound ends the wait even if that invariant were ever broken.
+template <class A, class V>
+__device__ V look_back(const LookbackArgs& lb, uint64_t tile, int lane) {
+    A acc = identity_step(A{});  // steps between the window and `tile`
+    int64_t top = static_cast<int64_t>(tile) - 1;  // nearest tile not yet folded
     for (;;) {
-        TileStatus* st = lb.status + p;
-        uint64_t f;
+        // lane 63 reads the nearest predecessor, lane 0 the farthest; lanes
+        // before tile 0 keep the identity and count as ready
+        const int64_t q = top - (kWave - 1 - lane);
+        A s = identity_step(A{});
+        int stop = -1;
         for (uint32_t polls = 0;; ++polls) {
-            f = __hip_atomic_load(&st->flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-            if ((f >> 2) == lb.epoch) break;
+            int kind = 3;
+            if (q >= 0) kind = read_status(lb.status + q, lb.tag, s);
+            const bool terminal = kind == 2 || (kind == 1 && cuts_chain(s));
+            const uint64_t term_mask = __ballot(terminal);
+            const uint64_t ready_mask = __ballot(kind != 0);
+            stop = term_mask ? 63 - __clzll(term_mask) : -1;  // nearest terminal lane
+            const uint64_t need = stop >= 0 ? (~0ull << stop) : ~0ull;
+            if ((ready_mask & need) == need) break;
             if (polls >= kMaxPolls) {
-                __hip_atomic_fetch_add(lb.timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (lane == 0)
+                    __hip_atomic_fetch_add(lb.timeouts, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
                 return poisoned(V{});
             }
             __builtin_amdgcn_s_sleep(1);
         }
-        if ((f & 3u) == kFlagIncl) {
-            const uint64_t u = __hip_atomic_load(&st->incl, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-            return apply(acc, unpack_state(u, V{}));
-        }
-        PackedStep u;
-        u.a = __hip_atomic_load(&st->agg_a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        u.b = __hip_atomic_load(&st->agg_b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        acc = compose(acc, unpack_step(u, S{}));
-        if (cuts_chain(acc)) return acc.b;
-        --p;  // p >= 1 here: tile 0 publishes INCL only
+        // entries beyond the nearest terminal one are not needed (and may not
+        // be ready)
+        if (lane < stop) s = identity_step(A{});
+        const A total = read_lane(wave_inclusive_scan(s), kWave - 1);
+        acc = compose(acc, total);
+        if (stop >= 0) return acc.b;  // the terminal entry made acc.a zero
+        top -= kWave;
     }
 }
 

@@ -107,24 +107,31 @@ __device__ __forceinline__ void scan_tile(const typename E::Params& p, const Geo
     for (int w = 0; w < kWavesPerGroup; ++w)
         if (w < wave) wpre = compose(sm_wave[w], wpre);
 
-    // 5. state entering the tile
-    if (threadIdx.x == 0) {
-        V carry = V(0);
-        if constexpr (LOOKBACK) {
+    // 5. state entering the tile (wave 0)
+    if constexpr (LOOKBACK) {
+        if (wave == 0) {
             A agg = identity_step(A{});
 #pragma unroll
             for (int w = 0; w < kWavesPerGroup; ++w) agg = compose(sm_wave[w], agg);
             TileStatus* st = lb.status + tile;
             const bool known = tile == 0 || cuts_chain(agg);
-            if (known)
-                publish_inclusive(st, pack_state(apply(agg, V(0))), lb.epoch);
-            else
-                publish_aggregate(st, pack_step(agg), lb.epoch);
-            // thread 0 holds the tile's first step in scan order
-            if (tile > 0 && !cuts_chain(e[0][0])) carry = look_back<A, V>(lb, tile);
-            if (!known) publish_inclusive(st, pack_state(apply(agg, carry)), lb.epoch);
+            if (lane == 0) {
+                if (known)
+                    publish_inclusive(st, apply(agg, V(0)), lb.tag);
+                else
+                    publish_aggregate(st, agg, lb.tag);
+            }
+            // lane 0 of wave 0 holds the tile's first step in scan order
+            const bool first_cuts = __ballot(lane == 0 && cuts_chain(e[0][0])) != 0;
+            V carry = V(0);
+            if (tile > 0 && !first_cuts) carry = look_back<A, V>(lb, tile, lane);
+            if (lane == 0) {
+                if (!known) publish_inclusive(st, apply(agg, carry), lb.tag);
+                *sm_carry = carry;
+            }
         }
-        *sm_carry = carry;
+    } else {
+        if (threadIdx.x == 0) *sm_carry = V(0);
     }
     __syncthreads();
 
@@ -179,6 +186,10 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const typename E::Params
     }
 }
 
+// An empty kernel: the launch floor that a scan launch of the same grid
+// cannot go below.
+__global__ __launch_bounds__(kThreads) void empty_kernel() {}
+
 // ------------------------------------------------------------------ host
 namespace {
 
@@ -198,7 +209,7 @@ struct Scratch {
     unsigned long long* counter = nullptr;
     int64_t capacity = 0;       // tiles
     uint64_t next_ticket = 0;   // counter value at the start of the next call
-    uint64_t epoch = 0;         // last epoch used
+    uint64_t epoch = 0;         // tag of the last call (32-bit, 0 = none)
     bool broken = false;        // a launch failed: counter position unknown
 };
 
@@ -351,6 +362,10 @@ int run(int est, int64_t N, int64_t T, bool vec, hipStream_t stream, Fn&& fn) {
     if (pl.mapping == RLSCAN_MAP_PACKED) {
         return fn(geo, lb, pl.rounds, false) == hipSuccess ? RLSCAN_OK : RLSCAN_ERR_HIP;
     }
+    // a captured look-back launch would replay with a stale ticket base
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &capture) != hipSuccess) return RLSCAN_ERR_HIP;
+    if (capture != hipStreamCaptureStatusNone) return RLSCAN_ERR_CAPTURE;
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return RLSCAN_ERR_HIP;
     Scratch* sc = scratch_for(device, stream);
@@ -361,7 +376,13 @@ int run(int est, int64_t N, int64_t T, bool vec, hipStream_t stream, Fn&& fn) {
     lb.ticket_counter = sc->counter;
     lb.timeouts = reinterpret_cast<unsigned int*>(sc->counter + 1);
     lb.ticket_base = sc->next_ticket;
-    lb.epoch = ++sc->epoch;
+    if (sc->epoch == 0xffffffffull) {
+        // the 32-bit call tags are about to repeat: clear the status words
+        if (hipMemsetAsync(sc->status, 0, sizeof(TileStatus) * sc->capacity, stream) != hipSuccess)
+            return RLSCAN_ERR_HIP;
+        sc->epoch = 0;
+    }
+    lb.tag = static_cast<uint32_t>(++sc->epoch);
     if (fn(geo, lb, pl.rounds, true) != hipSuccess) {
         sc->broken = true;
         return RLSCAN_ERR_HIP;
@@ -564,6 +585,8 @@ const char* rlscan_status_string(int status) {
         case RLSCAN_ERR_ALIAS: return "an output aliases an input or the other output";
         case RLSCAN_ERR_HIP: return "HIP runtime call or kernel launch failed";
         case RLSCAN_ERR_ALLOC: return "could not allocate the look-back scratch";
+        case RLSCAN_ERR_CAPTURE:
+            return "this shape needs the look-back mapping, which cannot be captured into a graph";
         default: return "unknown rlscan status";
     }
 }
@@ -611,6 +634,12 @@ int rlscan_plan(int estimator, int64_t N, int64_t T, int64_t A, rlscan_plan_info
     info->tiles = pl.tiles;
     info->grid = pl.grid;
     return RLSCAN_OK;
+}
+
+int rlscan_launch_floor(int64_t grid, hipStream_t stream) {
+    if (grid < 1 || grid > kMaxGrid) return RLSCAN_ERR_SHAPE;
+    hipLaunchKernelGGL(empty_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream);
+    return hipGetLastError() == hipSuccess ? RLSCAN_OK : RLSCAN_ERR_HIP;
 }
 
 int rlscan_lookback_timeouts(uint64_t* count) {

@@ -29,6 +29,7 @@ RLSCAN_ERR_PARAM = -3
 RLSCAN_ERR_ALIAS = -4
 RLSCAN_ERR_HIP = -5
 RLSCAN_ERR_ALLOC = -6
+RLSCAN_ERR_CAPTURE = -7
 
 MAP_AUTO, MAP_PACKED, MAP_LOOKBACK = 0, 1, 2
 
@@ -41,7 +42,7 @@ EXPORTED = (
     "rlscan_gae", "rlscan_lambda_returns", "rlscan_discounted_returns", "rlscan_vtrace",
     "rlscan_retrace", "rlscan_eligibility_traces", "rlscan_episodic_prefix_sum",
     "rlscan_status_string", "rlscan_version", "rlscan_release_scratch", "rlscan_plan",
-    "rlscan_set_launch_override", "rlscan_lookback_timeouts",
+    "rlscan_set_launch_override", "rlscan_lookback_timeouts", "rlscan_launch_floor",
 )
 
 
@@ -87,6 +88,8 @@ def _declare(lib):
     lib.rlscan_set_launch_override.restype = ctypes.c_int
     lib.rlscan_lookback_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
     lib.rlscan_lookback_timeouts.restype = ctypes.c_int
+    lib.rlscan_launch_floor.argtypes = [_i64, _vp]
+    lib.rlscan_launch_floor.restype = ctypes.c_int
 
 
 def library(path: str = LIB_PATH):
@@ -257,3 +260,7 @@ def rlscan_lookback_timeouts() -> int:
     n = ctypes.c_uint64()
     _check(library().rlscan_lookback_timeouts(ctypes.byref(n)))
     return n.value
+
+
+def rlscan_launch_floor(grid, stream=None):
+    _check(library().rlscan_launch_floor(int(grid), _stream(stream)))

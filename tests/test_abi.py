@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_version_and_status_strings(lib):
     from linear_recurrence_scan_coefficient_amd import rlscan
     assert "gfx950" in rlscan.version()
-    for code in range(0, -7, -1):
+    for code in range(0, -8, -1):
         s = rlscan.status_string(code)
         assert s and s != "unknown rlscan status"
     assert rlscan.status_string(-99) == "unknown rlscan status"

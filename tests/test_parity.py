@@ -222,3 +222,51 @@ def test_benchmark_workloads(name, estimator):
     w = workloads.get(name)
     inputs = workloads.inputs_for(estimator, w, 0)
     check(estimator, w, inputs, name)
+
+
+def test_graph_capture_of_packed_calls():
+    """All seven estimators captured into one HIP graph (packed shapes) and
+    replayed several times, with eager work and synchronisations between the
+    replays; every replay must reproduce the eager outputs bit for bit."""
+    w = workloads.get("production_4096x128")
+    host = {e: workloads.inputs_for(e, w, 1) for e in ESTIMATORS}
+    dev = {e: device.upload(host[e]) for e in ESTIMATORS}
+    eager = {}
+    for e in ESTIMATORS:
+        out = device.alloc_outputs(e, w.N, w.T)
+        device.call(e, dev[e], out, w)
+        eager[e] = out
+    torch.cuda.synchronize()
+    eager = {e: {k: v.clone() for k, v in o.items()} for e, o in eager.items()}
+    outs = {e: device.alloc_outputs(e, w.N, w.T) for e in ESTIMATORS}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for e in ESTIMATORS:
+            device.call(e, dev[e], outs[e], w)
+    for rep in range(3):
+        for o in outs.values():
+            for v in o.values():
+                v.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"[parity] graph replay {rep}", flush=True)
+        for e in ESTIMATORS:
+            for k in eager[e]:
+                assert torch.equal(outs[e][k], eager[e][k]), (rep, e, k)
+        # eager work between replays
+        device.call("gae", dev["gae"], eager["gae"], w)
+        torch.cuda.synchronize()
+
+
+def test_lookback_launch_refuses_capture():
+    w, inputs = case("gae", 5, 3001, seed=2)
+    d = device.upload(inputs)
+    out = device.alloc_outputs("gae", 5, 3001)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(rlscan.RlscanError) as err:
+        with torch.cuda.graph(g):
+            device.call("gae", d, out, w)
+    assert err.value.status == rlscan.RLSCAN_ERR_CAPTURE
+    torch.cuda.synchronize()
