@@ -227,8 +227,11 @@ int rlscan_plan(int estimator, int64_t N, int64_t T, int64_t A, rlscan_plan_info
  * benchmarks).  mapping: RLSCAN_MAP_AUTO/PACKED/LOOKBACK (PACKED is only
  * honoured where it is valid); rounds: 0 = automatic, else 1, 2 or 4;
  * grid_cap: 0 = one workgroup per tile, else at most this many workgroups,
- * each looping over tiles.  Returns RLSCAN_ERR_PARAM for other values. */
-int rlscan_set_launch_override(int mapping, int rounds, int64_t grid_cap);
+ * each looping over tiles; tickets: 1 = order look-back tiles by a ticket
+ * counter even with one workgroup per tile (the default orders them by
+ * workgroup index, and falls back to tickets only when workgroups loop).
+ * Returns RLSCAN_ERR_PARAM for other values. */
+int rlscan_set_launch_override(int mapping, int rounds, int64_t grid_cap, int tickets);
 
 /* Diagnostics: enqueues an empty kernel of `grid` workgroups of 256 threads
  * on `stream` -- the launch-bound floor of a scan launch with that grid.

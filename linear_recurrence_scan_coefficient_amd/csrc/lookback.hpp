@@ -3,13 +3,17 @@
 // Scan with Decoupled Look-back", 2016), for the (a, b) recurrence steps.
 //
 // Protocol, per call:
-//  * Each workgroup takes a ticket from a 64-bit counter that is never reset;
-//    the host passes `ticket_base`, the counter value at the start of the
-//    call (it knows how many tickets every earlier call on this scratch
-//    took), so tile = ticket - ticket_base.  Tickets, not blockIdx, order the
-//    tiles, so a workgroup only ever waits on tiles already claimed by
-//    running workgroups: forward progress needs no assumption about the
-//    dispatch order.
+//  * Tile order.  By default tile = blockIdx.x with one tile per workgroup:
+//    the dispatcher hands workgroups to the XCDs round-robin and, within an
+//    XCD, in increasing index order, so every tile a workgroup waits on
+//    belongs to a workgroup that has been or will be dispatched without
+//    needing the waiter's slot.  When workgroups loop over tiles (grid
+//    capped) the order comes from tickets instead: each tile is claimed from
+//    a 64-bit counter that is never reset (the host passes `ticket_base`,
+//    the counter value at the start of the call), so a workgroup only waits
+//    on tiles claimed by running workgroups.  Tickets cost one atomic on a
+//    single address per tile -- about 12 ns each on MI355X, serialised
+//    across the XCDs -- which is why they are not the default.
 //  * Tile s publishes its aggregate step (AGG) as soon as its local scan is
 //    done -- or, when it already knows its outgoing state (it is tile 0, or
 //    its aggregate cuts the chain, a == 0), that state (INCL).  After the
@@ -46,6 +50,7 @@ struct LookbackArgs {
     uint64_t ticket_base;
     uint32_t tag;             // the call's epoch: nonzero, distinct for every
                               // call since the status buffer was cleared
+    uint32_t use_tickets;     // 1: tiles from tickets; 0: tile = blockIdx.x
 };
 
 // Upper bound on the polls of one look-back window (each poll sleeps about

@@ -167,9 +167,11 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const typename E::Params
     uint64_t tile = blockIdx.x;
     for (;;) {
         if constexpr (LOOKBACK) {
-            if (threadIdx.x == 0) sm_tile = take_ticket(lb);
-            __syncthreads();
-            tile = sm_tile;
+            if (lb.use_tickets) {
+                if (threadIdx.x == 0) sm_tile = take_ticket(lb);
+                __syncthreads();
+                tile = sm_tile;
+            }
         }
         if (tile >= static_cast<uint64_t>(geo.num_tiles)) break;
         // only the tile holding the end of the data needs bounds checks
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const typename E::Params
         else
             scan_tile<E, R, LOOKBACK, VEC, false>(p, geo, lb, tile, sm_wave, &sm_carry);
         if (one_tile_per_group) break;
-        if constexpr (!LOOKBACK) tile += gridDim.x;
+        if (!LOOKBACK || !lb.use_tickets) tile += gridDim.x;
         __syncthreads();  // LDS is reused by the next tile
     }
 }
@@ -200,6 +202,7 @@ struct LaunchOverride {
     std::atomic<int> mapping{RLSCAN_MAP_AUTO};
     std::atomic<int> rounds{0};
     std::atomic<int64_t> grid_cap{0};
+    std::atomic<int> tickets{0};  // 1: order look-back tiles by tickets always
 };
 LaunchOverride g_override;
 
@@ -372,6 +375,9 @@ int run(int est, int64_t N, int64_t T, bool vec, hipStream_t stream, Fn&& fn) {
     std::lock_guard<std::mutex> g(sc->m);
     const int rc = ensure_capacity(sc, stream, pl.tiles);
     if (rc != RLSCAN_OK) return rc;
+    // tile = blockIdx needs every tile to have its own workgroup
+    const bool tickets = pl.grid < pl.tiles || g_override.tickets.load() != 0;
+    lb.use_tickets = tickets ? 1u : 0u;
     lb.status = sc->status;
     lb.ticket_counter = sc->counter;
     lb.timeouts = reinterpret_cast<unsigned int*>(sc->counter + 1);
@@ -389,8 +395,9 @@ int run(int est, int64_t N, int64_t T, bool vec, hipStream_t stream, Fn&& fn) {
     }
     // every workgroup takes one ticket per tile it runs plus, when looping,
     // one final ticket that finds no tile
-    sc->next_ticket += static_cast<uint64_t>(pl.tiles) +
-                       (pl.grid >= pl.tiles ? 0u : static_cast<uint64_t>(pl.grid));
+    if (tickets)
+        sc->next_ticket += static_cast<uint64_t>(pl.tiles) +
+                           (pl.grid >= pl.tiles ? 0u : static_cast<uint64_t>(pl.grid));
     return RLSCAN_OK;
 }
 
@@ -666,13 +673,14 @@ int rlscan_lookback_timeouts(uint64_t* count) {
     return rc;
 }
 
-int rlscan_set_launch_override(int mapping, int rounds, int64_t grid_cap) {
+int rlscan_set_launch_override(int mapping, int rounds, int64_t grid_cap, int tickets) {
     if (mapping < RLSCAN_MAP_AUTO || mapping > RLSCAN_MAP_LOOKBACK) return RLSCAN_ERR_PARAM;
     if (rounds != 0 && rounds != 1 && rounds != 2 && rounds != 4) return RLSCAN_ERR_PARAM;
-    if (grid_cap < 0) return RLSCAN_ERR_PARAM;
+    if (grid_cap < 0 || (tickets != 0 && tickets != 1)) return RLSCAN_ERR_PARAM;
     g_override.mapping.store(mapping);
     g_override.rounds.store(rounds);
     g_override.grid_cap.store(grid_cap);
+    g_override.tickets.store(tickets);
     return RLSCAN_OK;
 }
 

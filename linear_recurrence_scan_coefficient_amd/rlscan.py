@@ -84,7 +84,7 @@ def _declare(lib):
     lib.rlscan_version.restype = ctypes.c_char_p
     lib.rlscan_plan.argtypes = [ctypes.c_int, _i64, _i64, _i64, ctypes.POINTER(PlanInfo)]
     lib.rlscan_plan.restype = ctypes.c_int
-    lib.rlscan_set_launch_override.argtypes = [ctypes.c_int, ctypes.c_int, _i64]
+    lib.rlscan_set_launch_override.argtypes = [ctypes.c_int, ctypes.c_int, _i64, ctypes.c_int]
     lib.rlscan_set_launch_override.restype = ctypes.c_int
     lib.rlscan_lookback_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
     lib.rlscan_lookback_timeouts.restype = ctypes.c_int
@@ -252,8 +252,9 @@ def rlscan_plan(estimator, N, T, A=1) -> dict:
     return {f[0]: getattr(info, f[0]) for f in PlanInfo._fields_ if f[0] != "reserved"}
 
 
-def rlscan_set_launch_override(mapping=MAP_AUTO, rounds=0, grid_cap=0):
-    _check(library().rlscan_set_launch_override(int(mapping), int(rounds), int(grid_cap)))
+def rlscan_set_launch_override(mapping=MAP_AUTO, rounds=0, grid_cap=0, tickets=0):
+    _check(library().rlscan_set_launch_override(int(mapping), int(rounds), int(grid_cap),
+                                                int(tickets)))
 
 
 def rlscan_lookback_timeouts() -> int:
