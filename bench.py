@@ -66,7 +66,45 @@ def parse_args():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--only", default=None, help="comma list of estimators (profiling runs)")
+    ap.add_argument("--pmc-run", default=None, metavar="ESTIMATOR",
+                    help="counter runs: launch ESTIMATOR ('all': each estimator in turn) once "
+                         "on each of several cold buffer sets of the production workload, "
+                         "then copy a 256 MiB buffer")
     return ap.parse_args()
+
+
+COPY_BYTES = 256 << 20
+
+
+def pmc_run(torch, est, sh, lib):
+    """Launches for `rocprofv3 --pmc`: the estimator on M distinct buffer
+    sets (cold inputs), then a plain device-to-device copy of COPY_BYTES
+    (reads and writes COPY_BYTES each), the calibration for FETCH_SIZE and
+    WRITE_SIZE."""
+    from linear_recurrence_scan_coefficient_amd import workloads
+    w = workloads.get("production_4096x128")
+    ests = list(w.estimators) if est == "all" else [est]
+    launches, per_bytes = {}, {}
+    for e in ests:
+        probe = CallSet([e], w, 0, sh, lib)
+        b = probe.bytes[e]
+        m = max(6, min(32, -(-(512 << 20) // b)))
+        sets = [probe] + [CallSet([e], w, seed, sh, lib) for seed in range(1, m)]
+        torch.cuda.synchronize()
+        for cs in sets:
+            cs.run()
+        torch.cuda.synchronize()
+        launches[e], per_bytes[e] = m, b
+        del sets, probe
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_run": est, "workload": w.name, "launches": launches,
+                      "algorithmic_bytes_per_launch": per_bytes, "copy_bytes": COPY_BYTES,
+                      "kernel_source_hash": kernel_source_hash()}), flush=True)
 
 
 # ------------------------------------------------------------------ raw calls
@@ -294,6 +332,9 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+    if args.pmc_run:
+        pmc_run(torch, args.pmc_run, sh, lib)
+        return
 
     w = workloads.get("production_4096x128")
     ests = list(w.estimators) if args.only is None else args.only.split(",")

@@ -223,15 +223,19 @@ typedef struct {
  * sizes, RLSCAN_ERR_PARAM for an unknown estimator id. */
 int rlscan_plan(int estimator, int64_t N, int64_t T, int64_t A, rlscan_plan_info* info);
 
+enum {
+    RLSCAN_FLAG_TICKETS = 1  /* order look-back tiles by a ticket counter even
+                                with one workgroup per tile                   */
+};
+
 /* Overrides the planner for every later call in the process (tests and
  * benchmarks).  mapping: RLSCAN_MAP_AUTO/PACKED/LOOKBACK (PACKED is only
  * honoured where it is valid); rounds: 0 = automatic, else 1, 2 or 4;
- * grid_cap: 0 = one workgroup per tile, else at most this many workgroups,
- * each looping over tiles; tickets: 1 = order look-back tiles by a ticket
- * counter even with one workgroup per tile (the default orders them by
- * workgroup index, and falls back to tickets only when workgroups loop).
- * Returns RLSCAN_ERR_PARAM for other values. */
-int rlscan_set_launch_override(int mapping, int rounds, int64_t grid_cap, int tickets);
+ * grid_cap: 0 = no cap, else at most this many workgroups, each looping over
+ * tiles; flags: RLSCAN_FLAG_* bits.  By default look-back tiles are ordered
+ * by workgroup index, and by tickets only when workgroups loop.  Returns
+ * RLSCAN_ERR_PARAM for other values. */
+int rlscan_set_launch_override(int mapping, int rounds, int64_t grid_cap, int flags);
 
 /* Diagnostics: enqueues an empty kernel of `grid` workgroups of 256 threads
  * on `stream` -- the launch-bound floor of a scan launch with that grid.

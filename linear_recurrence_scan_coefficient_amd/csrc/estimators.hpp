@@ -8,8 +8,11 @@
 //   Chunk             registers holding one lane's 4-element chunk
 //   load<VEC>(...)    read the chunk's inputs (plus the one-element halo just
 //                     above the chunk where the step needs values at t+1)
-//   steps(...)        build the chunk's steps, in memory order
-//   store<VEC>(...)   write outputs from the states after each element (x)
+//   Epi               values the epilogue needs besides the states (kept
+//                     apart from Chunk so the next tile can be loaded into
+//                     Chunk while the current one is still being finished)
+//   steps(...)        build the chunk's steps, in memory order, and its Epi
+//   store<VEC,FULL>   write outputs from the states after each element (x)
 //                     and before it (before: x_{t+1} for reverse estimators)
 //
 // Shared conventions: row-major [N, T]; a flag is set iff != 0; for reverse
@@ -134,6 +137,8 @@ __device__ __forceinline__ T load_halo(const T* __restrict__ p, const ChunkPos& 
     return p[i < NT ? i : NT - 1];
 }
 
+struct NoEpi {};
+
 // Shared episode logic of the reverse estimators: the flags of one chunk and
 // the bootstrap value of the row its first element lies in.
 struct EpisodeChunk {
@@ -195,6 +200,7 @@ struct Gae {
     using V = float;
     static constexpr bool kReverse = true;
     using Params = GaeParams;
+    using Epi = NoEpi;
     struct Chunk {
         EpisodeChunk ep;
         float v[4];
@@ -208,7 +214,7 @@ struct Gae {
         c.v_halo = load_halo(p.values, q, geo.NT);
     }
     __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
-                                 Chunk& c, S e[4]) {
+                                 const Chunk& c, S e[4], Epi&) {
         int64_t n = q.n0, t = q.t0;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
@@ -222,8 +228,8 @@ struct Gae {
         }
     }
     template <bool VEC, bool FULL>
-    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Chunk&, const V x[4],
-                                 const V[4]) {
+    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
+                                                 const V x[4], const V[4]) {
         store4<VEC, FULL>(p.out, q, x);
     }
 };
@@ -245,6 +251,7 @@ struct LambdaReturns {
     using V = float;
     static constexpr bool kReverse = true;
     using Params = LambdaReturnsParams;
+    using Epi = NoEpi;
     using Chunk = typename Gae<kTrunc>::Chunk;
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void load(const Params& p, const Geometry& geo, const ChunkPos& q, Chunk& c) {
@@ -254,7 +261,7 @@ struct LambdaReturns {
         c.v_halo = load_halo(p.values, q, geo.NT);
     }
     __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
-                                 Chunk& c, S e[4]) {
+                                 const Chunk& c, S e[4], Epi&) {
         int64_t n = q.n0, t = q.t0;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
@@ -269,8 +276,8 @@ struct LambdaReturns {
         }
     }
     template <bool VEC, bool FULL>
-    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Chunk&, const V x[4],
-                                 const V[4]) {
+    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
+                                                 const V x[4], const V[4]) {
         store4<VEC, FULL>(p.out, q, x);
     }
 };
@@ -290,6 +297,7 @@ struct Discounted {
     using V = float;
     static constexpr bool kReverse = true;
     using Params = DiscountedParams;
+    using Epi = NoEpi;
     struct Chunk {
         EpisodeChunk ep;
     };
@@ -299,7 +307,7 @@ struct Discounted {
                                         p.bootstrap_values, p.bootstrap_value, geo, q, c.ep);
     }
     __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
-                                 Chunk& c, S e[4]) {
+                                 const Chunk& c, S e[4], Epi&) {
         int64_t n = q.n0, t = q.t0;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
@@ -312,8 +320,8 @@ struct Discounted {
         }
     }
     template <bool VEC, bool FULL>
-    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Chunk&, const V x[4],
-                                 const V[4]) {
+    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
+                                                 const V x[4], const V[4]) {
         store4<VEC, FULL>(p.out, q, x);
     }
 };
@@ -343,6 +351,9 @@ struct Vtrace {
         float v[4];
         float lr[4];
         float v_halo;
+    };
+    struct Epi {
+        float v[4];
         float delta[4];
         float gamma_rho[4];  // 0 at a cut
     };
@@ -355,7 +366,7 @@ struct Vtrace {
         c.v_halo = load_halo(p.values, q, geo.NT);
     }
     __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
-                                 Chunk& c, S e[4]) {
+                                 const Chunk& c, S e[4], Epi& epi) {
         int64_t n = q.n0, t = q.t0;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
@@ -367,16 +378,17 @@ struct Vtrace {
             const float rho = fminf(p.rho_bar, ratio);
             const float cc = fminf(p.c_bar, ratio);
             const float delta = rho * (fmaf(p.gamma, vh, c.ep.r[j]) - c.v[j]);
-            c.delta[j] = delta;
-            c.gamma_rho[j] = cut ? 0.0f : p.gamma * rho;
+            epi.v[j] = c.v[j];
+            epi.delta[j] = delta;
+            epi.gamma_rho[j] = cut ? 0.0f : p.gamma * rho;
             e[j].a = cut ? 0.0f : p.gamma * cc;
             e[j].b = delta;
             next_position(n, t, geo.T);
         }
     }
     template <bool VEC, bool FULL>
-    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Chunk& c, const V x[4],
-                                 const V before[4]) {
+    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi& c,
+                                                 const V x[4], const V before[4]) {
         float vs[4], pg[4];
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
@@ -403,6 +415,7 @@ struct Retrace {
     using S = StepF;
     using V = float;
     static constexpr bool kReverse = true;
+    using Epi = NoEpi;
     struct Params {
         const float *rewards, *next_q, *next_pi;
         const int32_t* actions;
@@ -457,7 +470,7 @@ struct Retrace {
         }
     }
     __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
-                                 Chunk& c, S e[4]) {
+                                 const Chunk& c, S e[4], Epi&) {
         int64_t t = q.t0;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
@@ -494,8 +507,8 @@ struct Retrace {
         }
     }
     template <bool VEC, bool FULL>
-    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Chunk&, const V x[4],
-                                 const V[4]) {
+    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
+                                                 const V x[4], const V[4]) {
         store4<VEC, FULL>(p.out, q, x);
     }
 };
@@ -508,6 +521,7 @@ struct Eligibility {
     using S = StepF;
     using V = float;
     static constexpr bool kReverse = false;
+    using Epi = NoEpi;
     struct Params {
         const float *x, *dones;
         float* out;
@@ -522,7 +536,7 @@ struct Eligibility {
         load4<VEC, FULL>(p.dones, q, c.d);
     }
     __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
-                                 Chunk& c, S e[4]) {
+                                 const Chunk& c, S e[4], Epi&) {
         int64_t t = q.t0;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
@@ -532,8 +546,8 @@ struct Eligibility {
         }
     }
     template <bool VEC, bool FULL>
-    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Chunk&, const V x[4],
-                                 const V[4]) {
+    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
+                                                 const V x[4], const V[4]) {
         store4<VEC, FULL>(p.out, q, x);
     }
 };
@@ -546,6 +560,7 @@ struct PrefixSum {
     using S = StepI;
     using V = int64_t;
     static constexpr bool kReverse = false;
+    using Epi = NoEpi;
     struct Params {
         const int32_t* x;
         const float* dones;
@@ -560,8 +575,8 @@ struct PrefixSum {
         load4<VEC, FULL>(p.x, q, c.x);
         load4<VEC, FULL>(p.dones, q, c.d);
     }
-    __device__ __forceinline__ static void steps(const Params&, const Geometry& geo, const ChunkPos& q, Chunk& c,
-                                 S e[4]) {
+    __device__ __forceinline__ static void steps(const Params&, const Geometry& geo, const ChunkPos& q,
+                                                 const Chunk& c, S e[4], Epi&) {
         int64_t t = q.t0;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
@@ -571,8 +586,8 @@ struct PrefixSum {
         }
     }
     template <bool VEC, bool FULL>
-    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Chunk&, const V x[4],
-                                 const V[4]) {
+    __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
+                                                 const V x[4], const V[4]) {
         store4<VEC, FULL>(p.out, q, x);
     }
 };

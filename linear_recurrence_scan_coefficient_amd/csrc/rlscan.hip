@@ -45,69 +45,90 @@
 namespace rlscan {
 
 // ------------------------------------------------------------------ kernel
-template <class E, int R, bool LOOKBACK, bool VEC, bool FULL>
-__device__ __forceinline__ void scan_tile(const typename E::Params& p, const Geometry& geo,
-                                          const LookbackArgs& lb, uint64_t tile,
-                                          typename AggOf<typename E::S>::type* sm_wave,
-                                          typename E::V* sm_carry) {
-    using S = typename E::S;                  // one element's step
-    using A = typename AggOf<S>::type;        // a composition of steps
-    using V = typename E::V;
+// Phases of one tile, shared by the two kernels below.
+
+// Memory position of lane `lane`'s chunk in round r of wave `wave`.
+template <class E, int R>
+__device__ __forceinline__ int64_t chunk_base(const Geometry& geo, uint64_t tile, int wave, int r,
+                                              int lane) {
     constexpr int64_t kTile = static_cast<int64_t>(kThreads) * kChunk * R;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
     const int64_t mem_tile = E::kReverse ? geo.num_tiles - 1 - static_cast<int64_t>(tile)
                                          : static_cast<int64_t>(tile);
-    const int64_t base = mem_tile * kTile;
+    const int c = (wave * R + r) * kWave + lane;  // chunk index in scan order
+    const int64_t off = E::kReverse ? kTile - static_cast<int64_t>(kChunk) * (c + 1)
+                                    : static_cast<int64_t>(kChunk) * c;
+    return mem_tile * kTile + off;
+}
 
-    // 1. loads, all rounds first so every load of the tile is in flight
-    typename E::Chunk ch[R];
-    ChunkPos pos[R];
+// Whether every element of the tile lies below N*T.
+template <class E, int R>
+__device__ __forceinline__ bool tile_is_full(const Geometry& geo, uint64_t tile) {
+    constexpr int64_t kTile = static_cast<int64_t>(kThreads) * kChunk * R;
+    const int64_t mem_tile = E::kReverse ? geo.num_tiles - 1 - static_cast<int64_t>(tile)
+                                         : static_cast<int64_t>(tile);
+    return (mem_tile + 1) * kTile <= geo.NT;
+}
+
+// 1. loads, all rounds first so every load of the tile is in flight
+template <class E, int R, bool VEC, bool FULL>
+__device__ __forceinline__ void load_tile(const typename E::Params& p, const Geometry& geo,
+                                          uint64_t tile, typename E::Chunk (&ch)[R],
+                                          ChunkPos (&pos)[R]) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int c = (wave * R + r) * kWave + lane;  // chunk index in scan order
-        const int64_t off = E::kReverse ? kTile - static_cast<int64_t>(kChunk) * (c + 1)
-                                        : static_cast<int64_t>(kChunk) * c;
-        pos[r] = chunk_pos(base + off, geo);
+        pos[r] = chunk_pos(chunk_base<E, R>(geo, tile, wave, r, lane), geo);
         E::template load<VEC, FULL>(p, geo, pos[r], ch[r]);
     }
+}
 
-    // 2. steps in scan order; elements past N*T become the identity
-    S e[R][kChunk];
+// 2. steps in scan order; elements past N*T become the identity
+template <class E, int R, bool FULL>
+__device__ __forceinline__ void build_steps(const typename E::Params& p, const Geometry& geo,
+                                            const typename E::Chunk (&ch)[R],
+                                            const ChunkPos (&pos)[R],
+                                            typename E::S (&e)[R][kChunk],
+                                            typename E::Epi (&epi)[R]) {
+    using S = typename E::S;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         S em[kChunk];
-        E::steps(p, geo, pos[r], ch[r], em);
+        E::steps(p, geo, pos[r], ch[r], em, epi[r]);
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             const S s = (FULL || j < pos[r].valid) ? em[j] : identity_step(S{});
             e[r][E::kReverse ? kChunk - 1 - j : j] = s;
         }
     }
+}
 
-    // 3. lane aggregates and wave scans
-    A incl[R], tot[R];
+// 3. lane aggregates, wave scans and the wave's total
+template <int R, class S, class A>
+__device__ __forceinline__ A scan_wave(const S (&e)[R][kChunk], A (&incl)[R]) {
+    A wtot = identity_step(A{});
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         A agg = promote(e[r][0]);
 #pragma unroll
         for (int k = 1; k < kChunk; ++k) agg = compose(promote(e[r][k]), agg);
         incl[r] = wave_inclusive_scan(agg);
-        tot[r] = read_lane(incl[r], kWave - 1);
+        wtot = compose(read_lane(incl[r], kWave - 1), wtot);
     }
+    return wtot;
+}
 
-    // 4. wave totals through LDS
-    A wtot = tot[0];
-#pragma unroll
-    for (int r = 1; r < R; ++r) wtot = compose(tot[r], wtot);
-    if (lane == 0) sm_wave[wave] = wtot;
-    __syncthreads();
-    A wpre = identity_step(A{});
-#pragma unroll
-    for (int w = 0; w < kWavesPerGroup; ++w)
-        if (w < wave) wpre = compose(sm_wave[w], wpre);
-
-    // 5. state entering the tile (wave 0)
+// 5. state entering the tile, written to *sm_carry by wave 0 (call after the
+// wave totals are in sm_wave and the workgroup has synchronised)
+template <class E, bool LOOKBACK>
+__device__ __forceinline__ void tile_carry(const LookbackArgs& lb, uint64_t tile,
+                                           const typename AggOf<typename E::S>::type* sm_wave,
+                                           typename E::S first_step,
+                                           typename E::V* sm_carry) {
+    using A = typename AggOf<typename E::S>::type;
+    using V = typename E::V;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
     if constexpr (LOOKBACK) {
         if (wave == 0) {
             A agg = identity_step(A{});
@@ -122,7 +143,7 @@ __device__ __forceinline__ void scan_tile(const typename E::Params& p, const Geo
                     publish_aggregate(st, agg, lb.tag);
             }
             // lane 0 of wave 0 holds the tile's first step in scan order
-            const bool first_cuts = __ballot(lane == 0 && cuts_chain(e[0][0])) != 0;
+            const bool first_cuts = __ballot(lane == 0 && cuts_chain(first_step)) != 0;
             V carry = V(0);
             if (tile > 0 && !first_cuts) carry = look_back<A, V>(lb, tile, lane);
             if (lane == 0) {
@@ -133,10 +154,20 @@ __device__ __forceinline__ void scan_tile(const typename E::Params& p, const Geo
     } else {
         if (threadIdx.x == 0) *sm_carry = V(0);
     }
-    __syncthreads();
+}
 
-    // 6. replay from the entering state and store
-    V state = apply(wpre, *sm_carry);
+// 6. replay each lane's steps from its entering state and store
+template <class E, int R, bool VEC, bool FULL, class A>
+__device__ __forceinline__ void replay_store(const typename E::Params& p, const Geometry& geo,
+                                             uint64_t tile,
+                                             const typename E::S (&e)[R][kChunk],
+                                             const typename E::Epi (&epi)[R],
+                                             const A (&incl)[R], A wpre,
+                                             typename E::V carry) {
+    using V = typename E::V;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    V state = apply(wpre, carry);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const V after_lane = apply(incl[r], state);
@@ -150,10 +181,43 @@ __device__ __forceinline__ void scan_tile(const typename E::Params& p, const Geo
             x = apply(e[r][k], x);
             out[j] = x;
         }
-        E::template store<VEC, FULL>(p, pos[r], ch[r], out, before);
+        ChunkPos q;
+        q.g0 = chunk_base<E, R>(geo, tile, wave, r, lane);
+        const int64_t rem = geo.NT - q.g0;
+        q.valid = rem <= 0 ? 0 : (rem >= kChunk ? kChunk : static_cast<int>(rem));
+        E::template store<VEC, FULL>(p, q, epi[r], out, before);
     }
 }
 
+template <class E, int R, bool LOOKBACK, bool VEC, bool FULL>
+__device__ __forceinline__ void scan_tile(const typename E::Params& p, const Geometry& geo,
+                                          const LookbackArgs& lb, uint64_t tile,
+                                          typename AggOf<typename E::S>::type* sm_wave,
+                                          typename E::V* sm_carry) {
+    using S = typename E::S;
+    using A = typename AggOf<S>::type;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    typename E::Chunk ch[R];
+    ChunkPos pos[R];
+    load_tile<E, R, VEC, FULL>(p, geo, tile, ch, pos);
+    S e[R][kChunk];
+    typename E::Epi epi[R];
+    build_steps<E, R, FULL>(p, geo, ch, pos, e, epi);
+    A incl[R];
+    const A wtot = scan_wave<R>(e, incl);
+    if (lane == 0) sm_wave[wave] = wtot;
+    __syncthreads();
+    A wpre = identity_step(A{});
+#pragma unroll
+    for (int w = 0; w < kWavesPerGroup; ++w)
+        if (w < wave) wpre = compose(sm_wave[w], wpre);
+    tile_carry<E, LOOKBACK>(lb, tile, sm_wave, e[0][0], sm_carry);
+    __syncthreads();
+    replay_store<E, R, VEC, FULL>(p, geo, tile, e, epi, incl, wpre, *sm_carry);
+}
+
+// One tile per workgroup (or, grid-capped, a loop over tiles).
 template <class E, int R, bool LOOKBACK, bool VEC>
 __global__ __launch_bounds__(kThreads) void scan_kernel(const typename E::Params p,
                                                         const Geometry geo,
@@ -175,10 +239,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const typename E::Params
         }
         if (tile >= static_cast<uint64_t>(geo.num_tiles)) break;
         // only the tile holding the end of the data needs bounds checks
-        const int64_t mem_tile = E::kReverse ? geo.num_tiles - 1 - static_cast<int64_t>(tile)
-                                             : static_cast<int64_t>(tile);
-        constexpr int64_t kTile = static_cast<int64_t>(kThreads) * kChunk * R;
-        if ((mem_tile + 1) * kTile <= geo.NT)
+        if (tile_is_full<E, R>(geo, tile))
             scan_tile<E, R, LOOKBACK, VEC, true>(p, geo, lb, tile, sm_wave, &sm_carry);
         else
             scan_tile<E, R, LOOKBACK, VEC, false>(p, geo, lb, tile, sm_wave, &sm_carry);
@@ -202,7 +263,7 @@ struct LaunchOverride {
     std::atomic<int> mapping{RLSCAN_MAP_AUTO};
     std::atomic<int> rounds{0};
     std::atomic<int64_t> grid_cap{0};
-    std::atomic<int> tickets{0};  // 1: order look-back tiles by tickets always
+    std::atomic<int> flags{0};  // RLSCAN_FLAG_* bits
 };
 LaunchOverride g_override;
 
@@ -321,7 +382,8 @@ int check_alias(std::initializer_list<const void*> outs, std::initializer_list<c
 
 template <class E, int R, bool VEC>
 hipError_t launch_r(const typename E::Params& p, const Geometry& geo, const LookbackArgs& lb,
-                    bool lookback, hipStream_t stream) {
+                    const Plan& pl, hipStream_t stream) {
+    const bool lookback = pl.mapping == RLSCAN_MAP_LOOKBACK;
     const dim3 grid(static_cast<unsigned>(geo.grid)), block(kThreads);
     if (lookback)
         hipLaunchKernelGGL((scan_kernel<E, R, true, VEC>), grid, block, 0, stream, p, geo, lb);
@@ -332,21 +394,21 @@ hipError_t launch_r(const typename E::Params& p, const Geometry& geo, const Look
 
 template <class E>
 hipError_t launch_kernel(const typename E::Params& p, const Geometry& geo, const LookbackArgs& lb,
-                         int rounds, bool lookback, bool vec, hipStream_t stream) {
-    if (!vec) return launch_r<E, 1, false>(p, geo, lb, lookback, stream);
-    switch (rounds) {
-        case 1: return launch_r<E, 1, true>(p, geo, lb, lookback, stream);
-        case 2: return launch_r<E, 2, true>(p, geo, lb, lookback, stream);
-        default: return launch_r<E, 4, true>(p, geo, lb, lookback, stream);
+                         const Plan& pl, bool vec, hipStream_t stream) {
+    if (!vec) return launch_r<E, 1, false>(p, geo, lb, pl, stream);
+    switch (pl.rounds) {
+        case 1: return launch_r<E, 1, true>(p, geo, lb, pl, stream);
+        case 2: return launch_r<E, 2, true>(p, geo, lb, pl, stream);
+        default: return launch_r<E, 4, true>(p, geo, lb, pl, stream);
     }
 }
 
 // Retrace keeps 2*4*A action values per round in registers: one round only.
 template <class E>
 hipError_t launch_kernel_r1(const typename E::Params& p, const Geometry& geo,
-                            const LookbackArgs& lb, bool lookback, bool vec, hipStream_t stream) {
-    if (!vec) return launch_r<E, 1, false>(p, geo, lb, lookback, stream);
-    return launch_r<E, 1, true>(p, geo, lb, lookback, stream);
+                            const LookbackArgs& lb, const Plan& pl, bool vec, hipStream_t stream) {
+    if (!vec) return launch_r<E, 1, false>(p, geo, lb, pl, stream);
+    return launch_r<E, 1, true>(p, geo, lb, pl, stream);
 }
 
 // Plans, takes the look-back scratch if needed, and launches through `fn`.
@@ -363,7 +425,7 @@ int run(int est, int64_t N, int64_t T, bool vec, hipStream_t stream, Fn&& fn) {
     geo.inv_T = 1.0 / static_cast<double>(T);
     LookbackArgs lb{};
     if (pl.mapping == RLSCAN_MAP_PACKED) {
-        return fn(geo, lb, pl.rounds, false) == hipSuccess ? RLSCAN_OK : RLSCAN_ERR_HIP;
+        return fn(geo, lb, pl) == hipSuccess ? RLSCAN_OK : RLSCAN_ERR_HIP;
     }
     // a captured look-back launch would replay with a stale ticket base
     hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
@@ -376,7 +438,7 @@ int run(int est, int64_t N, int64_t T, bool vec, hipStream_t stream, Fn&& fn) {
     const int rc = ensure_capacity(sc, stream, pl.tiles);
     if (rc != RLSCAN_OK) return rc;
     // tile = blockIdx needs every tile to have its own workgroup
-    const bool tickets = pl.grid < pl.tiles || g_override.tickets.load() != 0;
+    const bool tickets = pl.grid < pl.tiles || (g_override.flags.load() & RLSCAN_FLAG_TICKETS);
     lb.use_tickets = tickets ? 1u : 0u;
     lb.status = sc->status;
     lb.ticket_counter = sc->counter;
@@ -389,7 +451,7 @@ int run(int est, int64_t N, int64_t T, bool vec, hipStream_t stream, Fn&& fn) {
         sc->epoch = 0;
     }
     lb.tag = static_cast<uint32_t>(++sc->epoch);
-    if (fn(geo, lb, pl.rounds, true) != hipSuccess) {
+    if (fn(geo, lb, pl) != hipSuccess) {
         sc->broken = true;
         return RLSCAN_ERR_HIP;
     }
@@ -433,9 +495,9 @@ int rlscan_gae(const float* rewards, const float* values, const float* bootstrap
     const bool vec = all_aligned({rewards, values, terminated, truncated, bootstrap_values,
                                   advantages});
     return run(RLSCAN_EST_GAE, N, T, vec, stream,
-               [&](const Geometry& g, const LookbackArgs& lb, int rounds, bool look) {
-                   return truncated ? launch_kernel<Gae<true>>(p, g, lb, rounds, look, vec, stream)
-                                    : launch_kernel<Gae<false>>(p, g, lb, rounds, look, vec, stream);
+               [&](const Geometry& g, const LookbackArgs& lb, const Plan& pl) {
+                   return truncated ? launch_kernel<Gae<true>>(p, g, lb, pl, vec, stream)
+                                    : launch_kernel<Gae<false>>(p, g, lb, pl, vec, stream);
                });
 }
 
@@ -458,10 +520,10 @@ int rlscan_lambda_returns(const float* rewards, const float* values, const float
     const bool vec = all_aligned({rewards, values, terminated, truncated, bootstrap_values,
                                   returns});
     return run(RLSCAN_EST_LAMBDA_RETURNS, N, T, vec, stream,
-               [&](const Geometry& g, const LookbackArgs& lb, int rounds, bool look) {
+               [&](const Geometry& g, const LookbackArgs& lb, const Plan& pl) {
                    return truncated
-                              ? launch_kernel<LambdaReturns<true>>(p, g, lb, rounds, look, vec, stream)
-                              : launch_kernel<LambdaReturns<false>>(p, g, lb, rounds, look, vec, stream);
+                              ? launch_kernel<LambdaReturns<true>>(p, g, lb, pl, vec, stream)
+                              : launch_kernel<LambdaReturns<false>>(p, g, lb, pl, vec, stream);
                });
 }
 
@@ -481,10 +543,10 @@ int rlscan_discounted_returns(const float* rewards, const float* bootstrap_value
                              returns, gamma};
     const bool vec = all_aligned({rewards, terminated, truncated, bootstrap_values, returns});
     return run(RLSCAN_EST_DISCOUNTED, N, T, vec, stream,
-               [&](const Geometry& g, const LookbackArgs& lb, int rounds, bool look) {
+               [&](const Geometry& g, const LookbackArgs& lb, const Plan& pl) {
                    return truncated
-                              ? launch_kernel<Discounted<true>>(p, g, lb, rounds, look, vec, stream)
-                              : launch_kernel<Discounted<false>>(p, g, lb, rounds, look, vec, stream);
+                              ? launch_kernel<Discounted<true>>(p, g, lb, pl, vec, stream)
+                              : launch_kernel<Discounted<false>>(p, g, lb, pl, vec, stream);
                });
 }
 
@@ -509,9 +571,9 @@ int rlscan_vtrace(const float* rewards, const float* values, const float* bootst
     const bool vec = all_aligned({rewards, values, log_rhos, terminated, truncated,
                                   bootstrap_values, vs, pg_advantages});
     return run(RLSCAN_EST_VTRACE, N, T, vec, stream,
-               [&](const Geometry& g, const LookbackArgs& lb, int rounds, bool look) {
-                   return truncated ? launch_kernel<Vtrace<true>>(p, g, lb, rounds, look, vec, stream)
-                                    : launch_kernel<Vtrace<false>>(p, g, lb, rounds, look, vec, stream);
+               [&](const Geometry& g, const LookbackArgs& lb, const Plan& pl) {
+                   return truncated ? launch_kernel<Vtrace<true>>(p, g, lb, pl, vec, stream)
+                                    : launch_kernel<Vtrace<false>>(p, g, lb, pl, vec, stream);
                });
 }
 
@@ -537,8 +599,8 @@ int rlscan_retrace(const float* rewards, const float* next_q_values_all,
         typename E::Params p{rewards, next_q_values_all, next_target_probs, actions,
                              behaviour_probs, terminated, truncated, targets, A, gamma, lambda};
         return run(RLSCAN_EST_RETRACE, N, T, vec, stream,
-                   [&](const Geometry& g, const LookbackArgs& lb, int, bool look) {
-                       return launch_kernel_r1<E>(p, g, lb, look, vec, stream);
+                   [&](const Geometry& g, const LookbackArgs& lb, const Plan& pl) {
+                       return launch_kernel_r1<E>(p, g, lb, pl, vec, stream);
                    });
     };
     switch (vec ? A : 0) {
@@ -562,8 +624,8 @@ int rlscan_eligibility_traces(const float* x, const float* dones, float* traces,
     Eligibility::Params p{x, dones, traces, gamma * lambda};
     const bool vec = all_aligned({x, dones, traces});
     return run(RLSCAN_EST_ELIGIBILITY, N, T, vec, stream,
-               [&](const Geometry& g, const LookbackArgs& lb, int rounds, bool look) {
-                   return launch_kernel<Eligibility>(p, g, lb, rounds, look, vec, stream);
+               [&](const Geometry& g, const LookbackArgs& lb, const Plan& pl) {
+                   return launch_kernel<Eligibility>(p, g, lb, pl, vec, stream);
                });
 }
 
@@ -578,8 +640,8 @@ int rlscan_episodic_prefix_sum(const int32_t* x, const float* dones, int64_t* ou
     PrefixSum::Params p{x, dones, out};
     const bool vec = all_aligned({x, dones, out});
     return run(RLSCAN_EST_PREFIX_SUM, N, T, vec, stream,
-               [&](const Geometry& g, const LookbackArgs& lb, int rounds, bool look) {
-                   return launch_kernel<PrefixSum>(p, g, lb, rounds, look, vec, stream);
+               [&](const Geometry& g, const LookbackArgs& lb, const Plan& pl) {
+                   return launch_kernel<PrefixSum>(p, g, lb, pl, vec, stream);
                });
 }
 
@@ -673,14 +735,14 @@ int rlscan_lookback_timeouts(uint64_t* count) {
     return rc;
 }
 
-int rlscan_set_launch_override(int mapping, int rounds, int64_t grid_cap, int tickets) {
+int rlscan_set_launch_override(int mapping, int rounds, int64_t grid_cap, int flags) {
     if (mapping < RLSCAN_MAP_AUTO || mapping > RLSCAN_MAP_LOOKBACK) return RLSCAN_ERR_PARAM;
     if (rounds != 0 && rounds != 1 && rounds != 2 && rounds != 4) return RLSCAN_ERR_PARAM;
-    if (grid_cap < 0 || (tickets != 0 && tickets != 1)) return RLSCAN_ERR_PARAM;
+    if (grid_cap < 0 || (flags & ~RLSCAN_FLAG_TICKETS) != 0) return RLSCAN_ERR_PARAM;
     g_override.mapping.store(mapping);
     g_override.rounds.store(rounds);
     g_override.grid_cap.store(grid_cap);
-    g_override.tickets.store(tickets);
+    g_override.flags.store(flags);
     return RLSCAN_OK;
 }
 

@@ -32,6 +32,7 @@ RLSCAN_ERR_ALLOC = -6
 RLSCAN_ERR_CAPTURE = -7
 
 MAP_AUTO, MAP_PACKED, MAP_LOOKBACK = 0, 1, 2
+FLAG_TICKETS = 1
 
 ESTIMATOR_IDS = {
     "gae": 0, "lambda_returns": 1, "discounted_returns": 2, "vtrace": 3, "retrace": 4,
@@ -252,9 +253,9 @@ def rlscan_plan(estimator, N, T, A=1) -> dict:
     return {f[0]: getattr(info, f[0]) for f in PlanInfo._fields_ if f[0] != "reserved"}
 
 
-def rlscan_set_launch_override(mapping=MAP_AUTO, rounds=0, grid_cap=0, tickets=0):
+def rlscan_set_launch_override(mapping=MAP_AUTO, rounds=0, grid_cap=0, flags=0):
     _check(library().rlscan_set_launch_override(int(mapping), int(rounds), int(grid_cap),
-                                                int(tickets)))
+                                                int(flags)))
 
 
 def rlscan_lookback_timeouts() -> int:

@@ -67,16 +67,19 @@ def test_small_shapes(estimator, shape):
     check(estimator, w, inputs)
 
 
-MAPPINGS = {"lookback": (rlscan.MAP_LOOKBACK, 0), "lookback_tickets": (rlscan.MAP_LOOKBACK, 1),
-            "packed": (rlscan.MAP_PACKED, 0)}
+MAPPINGS = {
+    "lookback": (rlscan.MAP_LOOKBACK, 0),
+    "lookback_tickets": (rlscan.MAP_LOOKBACK, rlscan.FLAG_TICKETS),
+    "packed": (rlscan.MAP_PACKED, 0),
+}
 
 
 @pytest.mark.parametrize("estimator", ESTIMATORS)
 @pytest.mark.parametrize("mapping", list(MAPPINGS))
 @pytest.mark.parametrize("rounds", [1, 2, 4])
 def test_mappings_and_rounds(estimator, mapping, rounds):
-    m, tickets = MAPPINGS[mapping]
-    rlscan.rlscan_set_launch_override(m, rounds, 0, tickets)
+    m, flags = MAPPINGS[mapping]
+    rlscan.rlscan_set_launch_override(m, rounds, 0, flags)
     for N, T in ((512, 128), (40, 4096), (3, 3001)):
         w, inputs = case(estimator, N, T, seed=N + T + rounds)
         plan = rlscan.rlscan_plan(estimator, N, T, w.A)
@@ -84,10 +87,10 @@ def test_mappings_and_rounds(estimator, mapping, rounds):
 
 
 @pytest.mark.parametrize("estimator", ESTIMATORS)
-@pytest.mark.parametrize("mapping", ["lookback", "packed"])
+@pytest.mark.parametrize("mapping", list(MAPPINGS))
 def test_grid_capped_loops(estimator, mapping):
-    m = rlscan.MAP_LOOKBACK if mapping == "lookback" else rlscan.MAP_PACKED
-    rlscan.rlscan_set_launch_override(m, 0, 13)
+    m, flags = MAPPINGS[mapping]
+    rlscan.rlscan_set_launch_override(m, 0, 13, flags)
     for N, T in ((256, 128), (5, 9000)):
         w, inputs = case(estimator, N, T, seed=N * T)
         check(estimator, w, inputs, f"{mapping} grid_cap=13")
