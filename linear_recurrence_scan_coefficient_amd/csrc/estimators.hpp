@@ -6,8 +6,10 @@
 //   kReverse          true for reverse-time estimators (x_t depends on x_{t+1})
 //   Params            device pointers and scalars of one call
 //   Chunk             registers holding one lane's 4-element chunk
-//   load<VEC>(...)    read the chunk's inputs (plus the one-element halo just
-//                     above the chunk where the step needs values at t+1)
+//   load<VEC,FULL>    read the chunk's inputs (plus the one-element halo just
+//                     above the chunk where the step needs values at t+1);
+//                     `stage` is the wave's LDS staging area, kStageFloats
+//                     floats (0 for estimators that do not stage)
 //   Epi               values the epilogue needs besides the states (kept
 //                     apart from Chunk so the next tile can be loaded into
 //                     Chunk while the current one is still being finished)
@@ -73,6 +75,8 @@ __device__ __forceinline__ void next_position(int64_t& n, int64_t& t, int64_t T)
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// A float in LDS (address space 3): loads through it are ds_read.
+typedef __attribute__((address_space(3))) float lds_float;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef long long i64x2 __attribute__((ext_vector_type(2)));
 
@@ -201,13 +205,15 @@ struct Gae {
     static constexpr bool kReverse = true;
     using Params = GaeParams;
     using Epi = NoEpi;
+    static constexpr int kStageFloats = 0;
     struct Chunk {
         EpisodeChunk ep;
         float v[4];
         float v_halo;
     };
     template <bool VEC, bool FULL>
-    __device__ __forceinline__ static void load(const Params& p, const Geometry& geo, const ChunkPos& q, Chunk& c) {
+    __device__ __forceinline__ static void load(const Params& p, const Geometry& geo,
+                                                const ChunkPos& q, Chunk& c, lds_float*) {
         load_episode<VEC, FULL, kTrunc>(p.rewards, p.terminated, p.truncated,
                                         p.bootstrap_values, p.bootstrap_value, geo, q, c.ep);
         load4<VEC, FULL>(p.values, q, c.v);
@@ -252,9 +258,11 @@ struct LambdaReturns {
     static constexpr bool kReverse = true;
     using Params = LambdaReturnsParams;
     using Epi = NoEpi;
+    static constexpr int kStageFloats = 0;
     using Chunk = typename Gae<kTrunc>::Chunk;
     template <bool VEC, bool FULL>
-    __device__ __forceinline__ static void load(const Params& p, const Geometry& geo, const ChunkPos& q, Chunk& c) {
+    __device__ __forceinline__ static void load(const Params& p, const Geometry& geo,
+                                                const ChunkPos& q, Chunk& c, lds_float*) {
         load_episode<VEC, FULL, kTrunc>(p.rewards, p.terminated, p.truncated,
                                         p.bootstrap_values, p.bootstrap_value, geo, q, c.ep);
         load4<VEC, FULL>(p.values, q, c.v);
@@ -298,11 +306,13 @@ struct Discounted {
     static constexpr bool kReverse = true;
     using Params = DiscountedParams;
     using Epi = NoEpi;
+    static constexpr int kStageFloats = 0;
     struct Chunk {
         EpisodeChunk ep;
     };
     template <bool VEC, bool FULL>
-    __device__ __forceinline__ static void load(const Params& p, const Geometry& geo, const ChunkPos& q, Chunk& c) {
+    __device__ __forceinline__ static void load(const Params& p, const Geometry& geo,
+                                                const ChunkPos& q, Chunk& c, lds_float*) {
         load_episode<VEC, FULL, kTrunc>(p.rewards, p.terminated, p.truncated,
                                         p.bootstrap_values, p.bootstrap_value, geo, q, c.ep);
     }
@@ -357,8 +367,10 @@ struct Vtrace {
         float delta[4];
         float gamma_rho[4];  // 0 at a cut
     };
+    static constexpr int kStageFloats = 0;
     template <bool VEC, bool FULL>
-    __device__ __forceinline__ static void load(const Params& p, const Geometry& geo, const ChunkPos& q, Chunk& c) {
+    __device__ __forceinline__ static void load(const Params& p, const Geometry& geo,
+                                                const ChunkPos& q, Chunk& c, lds_float*) {
         load_episode<VEC, FULL, kTrunc>(p.rewards, p.terminated, p.truncated,
                                         p.bootstrap_values, p.bootstrap_value, geo, q, c.ep);
         load4<VEC, FULL>(p.values, q, c.v);
@@ -416,6 +428,11 @@ struct Retrace {
     using V = float;
     static constexpr bool kReverse = true;
     using Epi = NoEpi;
+    // With A known and at most 8, full tiles stage the wave's 256 x A action
+    // values of each tensor through LDS: every load instruction then reads
+    // 1 KiB of contiguous memory (a lane's own 4 x A values would be a
+    // 16-byte piece every 16 x A bytes, which the L2 fetched ~14% over).
+    static constexpr int kStageFloats = (kA >= 1 && kA <= 8) ? 2 * kWave * kChunk * kA : 0;
     struct Params {
         const float *rewards, *next_q, *next_pi;
         const int32_t* actions;
@@ -432,9 +449,13 @@ struct Retrace {
         int32_t act_halo;
         float mu_halo;
         float q[4 * kRegA], pi[4 * kRegA];
+        const lds_float* lds;  // this lane's staged Q' values (pi' follow at
+                               // +kWave*kChunk*kA) when `staged`
+        bool staged;           // (LDS address 0 is valid: no null sentinel)
     };
     template <bool VEC, bool FULL>
-    __device__ __forceinline__ static void load(const Params& p, const Geometry& geo, const ChunkPos& q, Chunk& c) {
+    __device__ __forceinline__ static void load(const Params& p, const Geometry& geo,
+                                                const ChunkPos& q, Chunk& c, lds_float* stage) {
         load4<VEC, FULL>(p.rewards, q, c.ep.r);
         load4<VEC, FULL>(p.terminated, q, c.ep.term);
         load4<VEC, FULL>(p.truncated, q, c.ep.trunc);
@@ -443,9 +464,36 @@ struct Retrace {
         c.ep.boot = 0.0f;
         load4<VEC, FULL>(p.actions, q, c.act);
         load4<VEC, FULL>(p.behaviour_probs, q, c.mu);
-        c.act_halo = load_halo(p.actions, q, geo.NT);
-        c.mu_halo = load_halo(p.behaviour_probs, q, geo.NT);
-        if constexpr (kA > 0) {
+        // a_{t+1} and mu_{t+1} of the chunk's top element: element 0 of the
+        // next chunk up, held by the previous lane (lane 0 reads memory)
+        const int lane = threadIdx.x & (kWave - 1);
+        int32_t act_up = 0;
+        float mu_up = 1.0f;
+        if (lane == 0) {
+            act_up = load_halo(p.actions, q, geo.NT);
+            mu_up = load_halo(p.behaviour_probs, q, geo.NT);
+        }
+        c.act_halo = static_cast<int32_t>(lane_before_u32(static_cast<uint32_t>(c.act[0]), lane,
+                                                          static_cast<uint32_t>(act_up)));
+        c.mu_halo = lane_before(c.mu[0], lane, mu_up);
+        c.lds = stage;
+        c.staged = false;
+        if constexpr (kA > 0 && VEC && FULL && kStageFloats > 0) {
+            // the wave's chunks are contiguous; lane 63 holds the lowest one
+            constexpr int kSpan = kWave * kChunk * kA;  // floats per tensor
+            const int64_t span = q.g0 - static_cast<int64_t>(kChunk) * (kWave - 1 - lane);
+            const float* gq = p.next_q + span * kA;
+            const float* gp = p.next_pi + span * kA;
+#pragma unroll
+            for (int i = 0; i < kA; ++i) {
+                __builtin_amdgcn_global_load_lds(gq + 4 * (kWave * i + lane), stage + kWave * 4 * i,
+                                                 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(gp + 4 * (kWave * i + lane),
+                                                 stage + kSpan + kWave * 4 * i, 16, 0, 0);
+            }
+            c.lds = stage + (kWave - 1 - lane) * kChunk * kA;
+            c.staged = true;
+        } else if constexpr (kA > 0) {
             const int64_t base = q.g0 * kA;
             if (VEC && (FULL || q.valid == kChunk)) {
                 // 4*kA floats = kA 16-byte vectors per tensor, 16-byte aligned
@@ -471,6 +519,35 @@ struct Retrace {
     }
     __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
                                  const Chunk& c, S e[4], Epi&) {
+        // action values: registers, or the LDS staging area (16-byte reads)
+        float qv[4 * kRegA], pv[4 * kRegA];
+        if constexpr (kA > 0) {
+            if (c.staged) {
+                // The direct-to-LDS loads count in vmcnt, and the compiler does
+                // not order these reads after all of them (it was seen issuing
+                // reads of the last-loaded block before the wait): wait here,
+                // with a memory clobber so no LDS read moves above the wait.
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                constexpr int kSpan = kWave * kChunk * kA;
+                typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
+                lds_f32x4* lq = reinterpret_cast<lds_f32x4*>(c.lds);
+                lds_f32x4* lp = reinterpret_cast<lds_f32x4*>(c.lds + kSpan);
+#pragma unroll
+                for (int i = 0; i < kA; ++i) {
+                    const f32x4 a = lq[i], b = lp[i];
+                    qv[4 * i + 0] = a.x; qv[4 * i + 1] = a.y;
+                    qv[4 * i + 2] = a.z; qv[4 * i + 3] = a.w;
+                    pv[4 * i + 0] = b.x; pv[4 * i + 1] = b.y;
+                    pv[4 * i + 2] = b.z; pv[4 * i + 3] = b.w;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4 * kA; ++i) {
+                    qv[i] = c.q[i];
+                    pv[i] = c.pi[i];
+                }
+            }
+        }
         int64_t t = q.t0;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
@@ -483,7 +560,7 @@ struct Retrace {
                 a_next = a_next < 0 ? 0 : (a_next >= kA ? kA - 1 : a_next);
 #pragma unroll
                 for (int a = 0; a < kA; ++a) {
-                    const float qa = c.q[j * kA + a], pa = c.pi[j * kA + a];
+                    const float qa = qv[j * kA + a], pa = pv[j * kA + a];
                     eq = fmaf(pa, qa, eq);
                     q_sel = a == a_next ? qa : q_sel;
                     pi_sel = a == a_next ? pa : pi_sel;
@@ -522,6 +599,7 @@ struct Eligibility {
     using V = float;
     static constexpr bool kReverse = false;
     using Epi = NoEpi;
+    static constexpr int kStageFloats = 0;
     struct Params {
         const float *x, *dones;
         float* out;
@@ -531,7 +609,8 @@ struct Eligibility {
         float x[4], d[4];
     };
     template <bool VEC, bool FULL>
-    __device__ __forceinline__ static void load(const Params& p, const Geometry&, const ChunkPos& q, Chunk& c) {
+    __device__ __forceinline__ static void load(const Params& p, const Geometry&,
+                                                const ChunkPos& q, Chunk& c, lds_float*) {
         load4<VEC, FULL>(p.x, q, c.x);
         load4<VEC, FULL>(p.dones, q, c.d);
     }
@@ -561,6 +640,7 @@ struct PrefixSum {
     using V = int64_t;
     static constexpr bool kReverse = false;
     using Epi = NoEpi;
+    static constexpr int kStageFloats = 0;
     struct Params {
         const int32_t* x;
         const float* dones;
@@ -571,7 +651,8 @@ struct PrefixSum {
         float d[4];
     };
     template <bool VEC, bool FULL>
-    __device__ __forceinline__ static void load(const Params& p, const Geometry&, const ChunkPos& q, Chunk& c) {
+    __device__ __forceinline__ static void load(const Params& p, const Geometry&,
+                                                const ChunkPos& q, Chunk& c, lds_float*) {
         load4<VEC, FULL>(p.x, q, c.x);
         load4<VEC, FULL>(p.dones, q, c.d);
     }

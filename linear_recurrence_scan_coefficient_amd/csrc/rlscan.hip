@@ -73,13 +73,14 @@ __device__ __forceinline__ bool tile_is_full(const Geometry& geo, uint64_t tile)
 template <class E, int R, bool VEC, bool FULL>
 __device__ __forceinline__ void load_tile(const typename E::Params& p, const Geometry& geo,
                                           uint64_t tile, typename E::Chunk (&ch)[R],
-                                          ChunkPos (&pos)[R]) {
+                                          ChunkPos (&pos)[R], lds_float* stage) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         pos[r] = chunk_pos(chunk_base<E, R>(geo, tile, wave, r, lane), geo);
-        E::template load<VEC, FULL>(p, geo, pos[r], ch[r]);
+        E::template load<VEC, FULL>(p, geo, pos[r], ch[r],
+                                    stage + (wave * R + r) * E::kStageFloats);
     }
 }
 
@@ -193,14 +194,14 @@ template <class E, int R, bool LOOKBACK, bool VEC, bool FULL>
 __device__ __forceinline__ void scan_tile(const typename E::Params& p, const Geometry& geo,
                                           const LookbackArgs& lb, uint64_t tile,
                                           typename AggOf<typename E::S>::type* sm_wave,
-                                          typename E::V* sm_carry) {
+                                          typename E::V* sm_carry, lds_float* stage) {
     using S = typename E::S;
     using A = typename AggOf<S>::type;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     typename E::Chunk ch[R];
     ChunkPos pos[R];
-    load_tile<E, R, VEC, FULL>(p, geo, tile, ch, pos);
+    load_tile<E, R, VEC, FULL>(p, geo, tile, ch, pos, stage);
     S e[R][kChunk];
     typename E::Epi epi[R];
     build_steps<E, R, FULL>(p, geo, ch, pos, e, epi);
@@ -227,6 +228,10 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const typename E::Params
     __shared__ A sm_wave[kWavesPerGroup];
     __shared__ V sm_carry;
     __shared__ uint64_t sm_tile;
+    // staging area of the estimators that stage loads through LDS
+    constexpr int kStage = E::kStageFloats > 0 ? kWavesPerGroup * R * E::kStageFloats : 1;
+    __shared__ __attribute__((aligned(16))) float sm_stage[kStage];
+    lds_float* stage = (lds_float*)sm_stage;
     const bool one_tile_per_group = geo.grid >= geo.num_tiles;
     uint64_t tile = blockIdx.x;
     for (;;) {
@@ -240,9 +245,9 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const typename E::Params
         if (tile >= static_cast<uint64_t>(geo.num_tiles)) break;
         // only the tile holding the end of the data needs bounds checks
         if (tile_is_full<E, R>(geo, tile))
-            scan_tile<E, R, LOOKBACK, VEC, true>(p, geo, lb, tile, sm_wave, &sm_carry);
+            scan_tile<E, R, LOOKBACK, VEC, true>(p, geo, lb, tile, sm_wave, &sm_carry, stage);
         else
-            scan_tile<E, R, LOOKBACK, VEC, false>(p, geo, lb, tile, sm_wave, &sm_carry);
+            scan_tile<E, R, LOOKBACK, VEC, false>(p, geo, lb, tile, sm_wave, &sm_carry, stage);
         if (one_tile_per_group) break;
         if (!LOOKBACK || !lb.use_tickets) tile += gridDim.x;
         __syncthreads();  // LDS is reused by the next tile
