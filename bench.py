@@ -20,8 +20,10 @@ measured live with HIP events around replays of a graph of M back-to-back
 launches over M distinct buffer sets (M * bytes >= 512 MiB, so inputs come
 from HBM); `roofline` reports the estimator with the longest launch.  The
 long-sequence workload (8 x 2^20 steps, four estimators, decoupled
-look-back, launched eagerly with events around each call) and the float64
-oracle timed on one host core are reported as well.
+look-back, launched eagerly with events around each call), a supplementary
+large-batch workload (2^20 x 32, packed), the bandwidth of a plain streaming
+copy moving the same bytes as each call, and the float64 oracle timed on one
+host core are reported as well.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -200,6 +202,29 @@ def time_eager_calls(torch, sets, reps):
             for j, e in enumerate(ests)}
 
 
+def eager_workload(torch, w, sh, lib, reps):
+    """Per-call figures of every estimator of a large workload: calls launched
+    eagerly with events around each (two buffer sets of all its estimators,
+    far beyond the last-level cache), beside the copy ceiling for the same
+    bytes."""
+    sets = [CallSet(w.estimators, w, seed, sh, lib) for seed in range(2)]
+    per = time_eager_calls(torch, sets, reps)
+    nbytes = dict(sets[0].bytes)
+    del sets
+    torch.cuda.empty_cache()
+    res = {}
+    for e in w.estimators:
+        b, us = nbytes[e], per[e]
+        gbs = b / (us * 1e-6) / 1e9
+        copy_us, copy_gbs = copy_ceiling(torch, sh, lib, b)
+        res[e] = {"us_per_call": round(us, 2), "elements_per_s": w.N * w.T / (us * 1e-6),
+                  "bytes": b, "GB_per_s": round(gbs, 1),
+                  "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                  "copy_same_bytes_GB_per_s": round(copy_gbs, 1),
+                  "frac_of_copy": round(gbs / copy_gbs, 4)}
+    return res
+
+
 def capture_graph(torch, calls):
     """One HIP graph holding `calls` in order (packed launches only: each call
     enqueues exactly one kernel and nothing else)."""
@@ -267,6 +292,24 @@ def per_kernel(torch, est, w, sh, lib, min_bytes=512 << 20, reps=10):
     return us, b, m
 
 
+def copy_ceiling(torch, sh, lib, nbytes, min_bytes=512 << 20, reps=10):
+    """Achievable bandwidth for a launch that moves `nbytes` (read + write):
+    a plain streaming copy of nbytes/2 bytes (the library's diagnostic copy
+    kernel, same 16-byte non-temporal accesses as the scans), timed like
+    `per_kernel` over M distinct buffer pairs so every copy reads cold data.
+    Returns (microseconds per copy, GB/s counting read and write bytes)."""
+    half = (nbytes // 2) // 16 * 16
+    m = max(6, min(64, -(-min_bytes // max(1, 2 * half))))
+    pairs = [(torch.ones(half, dtype=torch.uint8, device="cuda"),
+              torch.empty(half, dtype=torch.uint8, device="cuda")) for _ in range(m)]
+    calls = [("copy", lib.rlscan_stream_copy, (dst.data_ptr(), src.data_ptr(), half, sh))
+             for src, dst in pairs]
+    g = capture_graph(torch, calls)
+    us = time_launches(torch, g, m, reps)
+    del g, pairs
+    return us, 2 * half / (us * 1e-6) / 1e9
+
+
 def launch_floor_us(torch, grid, launches=64, reps=10):
     from linear_recurrence_scan_coefficient_amd import rlscan
     lib = rlscan.library()
@@ -313,7 +356,18 @@ def cpu_baseline(w, estimators, seconds):
     return {"value": elems / el, "unit": "elements/s", "cores": 1, "kind": "oracle",
             "sample": (f"all {len(estimators)} estimators on {w.name} ({w.N}x{w.T}), "
                        f"{reps} repetitions in {el:.1f} s, float64 C loops, one thread"),
-            "cpu": platform.processor() or platform.machine()}
+            "cpu": cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def main():
@@ -368,6 +422,7 @@ def main():
     dom = max(ests, key=lambda e: per_est[e]["us_per_call"])
     d = per_est[dom]
     traffic = read_traffic(f"{dom}_{w.name}")
+    copy_us, copy_gbs = copy_ceiling(torch, sh, lib, d["bytes"])
     plan = rlscan.rlscan_plan(dom, w.N, w.T, w.A)
     floor = launch_floor_us(torch, plan["grid"])
 
@@ -382,7 +437,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": d["GB_per_s"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": d["frac_hbm_peak"], "traffic": traffic,
                      "kernel": dom, "algorithmic_bytes_per_launch": d["bytes"],
-                     "avg_launch_us": d["us_per_call"]},
+                     "avg_launch_us": d["us_per_call"],
+                     "copy_same_bytes": {"us": round(copy_us, 3),
+                                         "GB_per_s": round(copy_gbs, 1)}},
         "per_estimator": per_est,
         "eager": {"value": elems_per_step * args.steps / wall_eager,
                   "ms_per_step": wall_eager * 1000.0 / args.steps},
@@ -395,18 +452,12 @@ def main():
     if not args.no_long:
         wl = workloads.get("long_8x1048576")
         print("[bench] timing long-sequence calls", file=sys.stderr, flush=True)
-        lsets = [CallSet(wl.estimators, wl, seed, sh, lib) for seed in range(2)]
-        lper = time_eager_calls(torch, lsets, args.long_calls)
-        long_res = {}
-        for e in wl.estimators:
-            b = lsets[0].bytes[e]
-            us = lper[e]
-            long_res[e] = {"us_per_call": round(us, 2),
-                           "elements_per_s": wl.N * wl.T / (us * 1e-6), "bytes": b,
-                           "GB_per_s": round(b / (us * 1e-6) / 1e9, 1),
-                           "frac_hbm_peak": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-        result["long_8x1048576"] = long_res
-        del lsets
+        result["long_8x1048576"] = eager_workload(torch, wl, sh, lib, args.long_calls)
+        wb = workloads.get("large_batch_1048576x32")
+        print("[bench] timing the supplementary large-batch calls", file=sys.stderr, flush=True)
+        result["large_batch_1048576x32"] = eager_workload(torch, wb, sh, lib, args.long_calls)
+        result["large_batch_1048576x32"]["note"] = (
+            "supplementary shape, not one of the named configurations")
 
     assert rlscan.rlscan_lookback_timeouts() == 0
 

@@ -195,8 +195,9 @@ int rlscan_release_scratch(void);
 
 /* ---- launch planning (host only; no GPU work) ---------------------------
  * The library maps the flattened N*T elements onto tiles of
- * 1024*rounds consecutive elements, one 256-thread workgroup per tile.
- * mapping RLSCAN_MAP_PACKED: every tile holds whole rows (1024*rounds is a
+ * 256*waves*rounds consecutive elements, one workgroup of 64*waves threads
+ * (waves = 4 or 8 wave64s) per tile.
+ * mapping RLSCAN_MAP_PACKED: every tile holds whole rows (the tile size is a
  * multiple of T, or there is a single tile), no inter-workgroup traffic.
  * mapping RLSCAN_MAP_LOOKBACK: rows span tiles; carries travel between
  * workgroups through the single-pass decoupled look-back. */
@@ -211,10 +212,10 @@ enum {
 typedef struct {
     int32_t mapping;     /* RLSCAN_MAP_PACKED or RLSCAN_MAP_LOOKBACK         */
     int32_t rounds;      /* 4-element chunks per lane per tile (1, 2 or 4)   */
-    int64_t tile_elems;  /* elements per tile = 1024 * rounds                */
+    int64_t tile_elems;  /* elements per tile = 4 * rounds * threads         */
     int64_t tiles;       /* number of tiles = ceil(N*T / tile_elems)         */
     int64_t grid;        /* workgroups launched                              */
-    int32_t threads;     /* threads per workgroup (256)                      */
+    int32_t threads;     /* threads per workgroup: 256 or 512                */
     int32_t reserved;
 } rlscan_plan_info;
 
@@ -231,16 +232,27 @@ enum {
 /* Overrides the planner for every later call in the process (tests and
  * benchmarks).  mapping: RLSCAN_MAP_AUTO/PACKED/LOOKBACK (PACKED is only
  * honoured where it is valid); rounds: 0 = automatic, else 1, 2 or 4;
- * grid_cap: 0 = no cap, else at most this many workgroups, each looping over
- * tiles; flags: RLSCAN_FLAG_* bits.  By default look-back tiles are ordered
- * by workgroup index, and by tickets only when workgroups loop.  Returns
- * RLSCAN_ERR_PARAM for other values. */
-int rlscan_set_launch_override(int mapping, int rounds, int64_t grid_cap, int flags);
+ * waves: 0 = automatic, else 4 or 8 wave64s per workgroup; grid_cap: 0 = no
+ * cap, else at most this many workgroups, each looping over tiles; flags:
+ * RLSCAN_FLAG_* bits.  Retrace, and any call with an input or output that
+ * is not 16-byte aligned, always runs one round of 4 waves.  By default
+ * look-back tiles are ordered by workgroup index, and by tickets only when
+ * workgroups loop.  Returns RLSCAN_ERR_PARAM for other values. */
+int rlscan_set_launch_override(int mapping, int rounds, int waves, int64_t grid_cap, int flags);
 
 /* Diagnostics: enqueues an empty kernel of `grid` workgroups of 256 threads
  * on `stream` -- the launch-bound floor of a scan launch with that grid.
- * Returns RLSCAN_ERR_SHAPE unless 1 <= grid < 2^24. */
+ * Returns RLSCAN_ERR_SHAPE unless 1 <= grid < 2^23. */
 int rlscan_launch_floor(int64_t grid, hipStream_t stream);
+
+/* Diagnostics: enqueues a plain streaming copy of `bytes` bytes from `src`
+ * to `dst` (device pointers, 16-byte aligned, not overlapping; bytes a
+ * multiple of 16, at most about 2^37) with the same 16-byte non-temporal accesses the
+ * scan kernels use: the achievable-bandwidth reference for a kernel that
+ * reads and writes the same bytes.  Returns RLSCAN_ERR_SHAPE for a bad size,
+ * RLSCAN_ERR_NULL, RLSCAN_ERR_PARAM for a misaligned pointer, and
+ * RLSCAN_ERR_ALIAS for overlapping ranges. */
+int rlscan_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
 
 /* Diagnostics: waits in the look-back are bounded (a few seconds per
  * predecessor); a wait that reaches the bound is counted, its tile's results

@@ -2,7 +2,7 @@
 //
 // One kernel template serves all seven estimators.  The N*T elements are
 // taken as one flattened row-major sequence and cut into tiles of
-// 1024*R consecutive elements (R "rounds"), one 256-thread workgroup per
+// 256*W*R consecutive elements (R "rounds"), one workgroup of W wave64s per
 // tile.  Row boundaries need no special handling: the step at a row's end
 // (reverse estimators) or start (forward ones) has a == 0, which makes the
 // plain scan a segmented one.  Within a tile:
@@ -47,11 +47,17 @@ namespace rlscan {
 // ------------------------------------------------------------------ kernel
 // Phases of one tile, shared by the two kernels below.
 
+// Elements per tile.
+template <int R, int W>
+constexpr int64_t tile_elems() {
+    return static_cast<int64_t>(kWave) * W * kChunk * R;
+}
+
 // Memory position of lane `lane`'s chunk in round r of wave `wave`.
-template <class E, int R>
+template <class E, int R, int W>
 __device__ __forceinline__ int64_t chunk_base(const Geometry& geo, uint64_t tile, int wave, int r,
                                               int lane) {
-    constexpr int64_t kTile = static_cast<int64_t>(kThreads) * kChunk * R;
+    constexpr int64_t kTile = tile_elems<R, W>();
     const int64_t mem_tile = E::kReverse ? geo.num_tiles - 1 - static_cast<int64_t>(tile)
                                          : static_cast<int64_t>(tile);
     const int c = (wave * R + r) * kWave + lane;  // chunk index in scan order
@@ -61,16 +67,16 @@ __device__ __forceinline__ int64_t chunk_base(const Geometry& geo, uint64_t tile
 }
 
 // Whether every element of the tile lies below N*T.
-template <class E, int R>
+template <class E, int R, int W>
 __device__ __forceinline__ bool tile_is_full(const Geometry& geo, uint64_t tile) {
-    constexpr int64_t kTile = static_cast<int64_t>(kThreads) * kChunk * R;
+    constexpr int64_t kTile = tile_elems<R, W>();
     const int64_t mem_tile = E::kReverse ? geo.num_tiles - 1 - static_cast<int64_t>(tile)
                                          : static_cast<int64_t>(tile);
     return (mem_tile + 1) * kTile <= geo.NT;
 }
 
 // 1. loads, all rounds first so every load of the tile is in flight
-template <class E, int R, bool VEC, bool FULL>
+template <class E, int R, int W, bool VEC, bool FULL>
 __device__ __forceinline__ void load_tile(const typename E::Params& p, const Geometry& geo,
                                           uint64_t tile, typename E::Chunk (&ch)[R],
                                           ChunkPos (&pos)[R], lds_float* stage) {
@@ -78,7 +84,7 @@ __device__ __forceinline__ void load_tile(const typename E::Params& p, const Geo
     const int wave = threadIdx.x / kWave;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        pos[r] = chunk_pos(chunk_base<E, R>(geo, tile, wave, r, lane), geo);
+        pos[r] = chunk_pos(chunk_base<E, R, W>(geo, tile, wave, r, lane), geo);
         E::template load<VEC, FULL>(p, geo, pos[r], ch[r],
                                     stage + (wave * R + r) * E::kStageFloats);
     }
@@ -121,7 +127,7 @@ __device__ __forceinline__ A scan_wave(const S (&e)[R][kChunk], A (&incl)[R]) {
 
 // 5. state entering the tile, written to *sm_carry by wave 0 (call after the
 // wave totals are in sm_wave and the workgroup has synchronised)
-template <class E, bool LOOKBACK>
+template <class E, int W, bool LOOKBACK>
 __device__ __forceinline__ void tile_carry(const LookbackArgs& lb, uint64_t tile,
                                            const typename AggOf<typename E::S>::type* sm_wave,
                                            typename E::S first_step,
@@ -134,7 +140,7 @@ __device__ __forceinline__ void tile_carry(const LookbackArgs& lb, uint64_t tile
         if (wave == 0) {
             A agg = identity_step(A{});
 #pragma unroll
-            for (int w = 0; w < kWavesPerGroup; ++w) agg = compose(sm_wave[w], agg);
+            for (int w = 0; w < W; ++w) agg = compose(sm_wave[w], agg);
             TileStatus* st = lb.status + tile;
             const bool known = tile == 0 || cuts_chain(agg);
             if (lane == 0) {
@@ -158,7 +164,7 @@ __device__ __forceinline__ void tile_carry(const LookbackArgs& lb, uint64_t tile
 }
 
 // 6. replay each lane's steps from its entering state and store
-template <class E, int R, bool VEC, bool FULL, class A>
+template <class E, int R, int W, bool VEC, bool FULL, class A>
 __device__ __forceinline__ void replay_store(const typename E::Params& p, const Geometry& geo,
                                              uint64_t tile,
                                              const typename E::S (&e)[R][kChunk],
@@ -183,14 +189,14 @@ __device__ __forceinline__ void replay_store(const typename E::Params& p, const 
             out[j] = x;
         }
         ChunkPos q;
-        q.g0 = chunk_base<E, R>(geo, tile, wave, r, lane);
+        q.g0 = chunk_base<E, R, W>(geo, tile, wave, r, lane);
         const int64_t rem = geo.NT - q.g0;
         q.valid = rem <= 0 ? 0 : (rem >= kChunk ? kChunk : static_cast<int>(rem));
         E::template store<VEC, FULL>(p, q, epi[r], out, before);
     }
 }
 
-template <class E, int R, bool LOOKBACK, bool VEC, bool FULL>
+template <class E, int R, int W, bool LOOKBACK, bool VEC, bool FULL>
 __device__ __forceinline__ void scan_tile(const typename E::Params& p, const Geometry& geo,
                                           const LookbackArgs& lb, uint64_t tile,
                                           typename AggOf<typename E::S>::type* sm_wave,
@@ -201,7 +207,7 @@ __device__ __forceinline__ void scan_tile(const typename E::Params& p, const Geo
     const int wave = threadIdx.x / kWave;
     typename E::Chunk ch[R];
     ChunkPos pos[R];
-    load_tile<E, R, VEC, FULL>(p, geo, tile, ch, pos, stage);
+    load_tile<E, R, W, VEC, FULL>(p, geo, tile, ch, pos, stage);
     S e[R][kChunk];
     typename E::Epi epi[R];
     build_steps<E, R, FULL>(p, geo, ch, pos, e, epi);
@@ -211,25 +217,25 @@ __device__ __forceinline__ void scan_tile(const typename E::Params& p, const Geo
     __syncthreads();
     A wpre = identity_step(A{});
 #pragma unroll
-    for (int w = 0; w < kWavesPerGroup; ++w)
+    for (int w = 0; w < W; ++w)
         if (w < wave) wpre = compose(sm_wave[w], wpre);
-    tile_carry<E, LOOKBACK>(lb, tile, sm_wave, e[0][0], sm_carry);
+    tile_carry<E, W, LOOKBACK>(lb, tile, sm_wave, e[0][0], sm_carry);
     __syncthreads();
-    replay_store<E, R, VEC, FULL>(p, geo, tile, e, epi, incl, wpre, *sm_carry);
+    replay_store<E, R, W, VEC, FULL>(p, geo, tile, e, epi, incl, wpre, *sm_carry);
 }
 
 // One tile per workgroup (or, grid-capped, a loop over tiles).
-template <class E, int R, bool LOOKBACK, bool VEC>
-__global__ __launch_bounds__(kThreads) void scan_kernel(const typename E::Params p,
+template <class E, int R, int W, bool LOOKBACK, bool VEC>
+__global__ __launch_bounds__(kWave * W) void scan_kernel(const typename E::Params p,
                                                         const Geometry geo,
                                                         const LookbackArgs lb) {
     using A = typename AggOf<typename E::S>::type;
     using V = typename E::V;
-    __shared__ A sm_wave[kWavesPerGroup];
+    __shared__ A sm_wave[W];
     __shared__ V sm_carry;
     __shared__ uint64_t sm_tile;
     // staging area of the estimators that stage loads through LDS
-    constexpr int kStage = E::kStageFloats > 0 ? kWavesPerGroup * R * E::kStageFloats : 1;
+    constexpr int kStage = E::kStageFloats > 0 ? W * R * E::kStageFloats : 1;
     __shared__ __attribute__((aligned(16))) float sm_stage[kStage];
     lds_float* stage = (lds_float*)sm_stage;
     const bool one_tile_per_group = geo.grid >= geo.num_tiles;
@@ -244,10 +250,10 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const typename E::Params
         }
         if (tile >= static_cast<uint64_t>(geo.num_tiles)) break;
         // only the tile holding the end of the data needs bounds checks
-        if (tile_is_full<E, R>(geo, tile))
-            scan_tile<E, R, LOOKBACK, VEC, true>(p, geo, lb, tile, sm_wave, &sm_carry, stage);
+        if (tile_is_full<E, R, W>(geo, tile))
+            scan_tile<E, R, W, LOOKBACK, VEC, true>(p, geo, lb, tile, sm_wave, &sm_carry, stage);
         else
-            scan_tile<E, R, LOOKBACK, VEC, false>(p, geo, lb, tile, sm_wave, &sm_carry, stage);
+            scan_tile<E, R, W, LOOKBACK, VEC, false>(p, geo, lb, tile, sm_wave, &sm_carry, stage);
         if (one_tile_per_group) break;
         if (!LOOKBACK || !lb.use_tickets) tile += gridDim.x;
         __syncthreads();  // LDS is reused by the next tile
@@ -256,17 +262,40 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const typename E::Params
 
 // An empty kernel: the launch floor that a scan launch of the same grid
 // cannot go below.
-__global__ __launch_bounds__(kThreads) void empty_kernel() {}
+constexpr int kFloorThreads = 256;
+__global__ __launch_bounds__(kFloorThreads) void empty_kernel() {}
+
+// A plain streaming copy: the bandwidth a kernel that reads and writes the
+// same bytes, in the same 16-byte non-temporal accesses, can reach.  Each
+// thread moves kCopyUnroll 16-byte words, a workgroup a contiguous span.
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+__global__ __launch_bounds__(kCopyThreads) void copy_kernel(const f32x4* __restrict__ src,
+                                                            f32x4* __restrict__ dst, int64_t n) {
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kCopyThreads * kCopyUnroll + threadIdx.x;
+    f32x4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+        const int64_t i = base + static_cast<int64_t>(u) * kCopyThreads;
+        if (i < n) v[u] = __builtin_nontemporal_load(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+        const int64_t i = base + static_cast<int64_t>(u) * kCopyThreads;
+        if (i < n) __builtin_nontemporal_store(v[u], dst + i);
+    }
+}
 
 // ------------------------------------------------------------------ host
 namespace {
 
 constexpr int64_t kMaxElements = int64_t(1) << 48;
-constexpr int64_t kMaxGrid = (int64_t(1) << 24) - 1;  // grid * 256 threads < 2^32
+constexpr int64_t kMaxGrid = (int64_t(1) << 23) - 1;  // grid * 512 threads < 2^32
 
 struct LaunchOverride {
     std::atomic<int> mapping{RLSCAN_MAP_AUTO};
     std::atomic<int> rounds{0};
+    std::atomic<int> waves{0};
     std::atomic<int64_t> grid_cap{0};
     std::atomic<int> flags{0};  // RLSCAN_FLAG_* bits
 };
@@ -330,6 +359,7 @@ int ensure_capacity(Scratch* sc, hipStream_t stream, int64_t tiles) {
 struct Plan {
     int mapping;
     int rounds;
+    int waves;
     int64_t tile_elems, tiles, grid;
 };
 
@@ -340,15 +370,30 @@ int auto_rounds(int est, int64_t NT) {
     return 4;
 }
 
-// `vec`: every pointer is 16-byte aligned.  Multi-round kernels exist only
-// for the vectorised path, and Retrace always runs one round.
+// Eight waves per workgroup double the tile, which halves the look-back
+// hops per element but also the workgroups that fit on a CU.  That pays for
+// the estimators whose four-round kernels need few registers (discounted
+// returns, eligibility traces, prefix sum: at most ~96 VGPRs, five waves per
+// SIMD); GAE, TD(lambda) and V-trace hold more per lane and run four waves.
+int auto_waves(int est, int rounds) {
+    if (rounds != 4) return 4;
+    return (est == RLSCAN_EST_DISCOUNTED || est == RLSCAN_EST_ELIGIBILITY ||
+            est == RLSCAN_EST_PREFIX_SUM) ? 8 : 4;
+}
+
+// `vec`: every pointer is 16-byte aligned.  Multi-round and eight-wave
+// kernels exist only for the vectorised path, and Retrace always runs one
+// round of four waves.
 Plan make_plan(int est, int64_t N, int64_t T, bool vec) {
     const int64_t NT = N * T;
     Plan pl;
     const int ro = g_override.rounds.load();
     pl.rounds = ro > 0 ? ro : auto_rounds(est, NT);
     if (!vec || est == RLSCAN_EST_RETRACE) pl.rounds = 1;
-    pl.tile_elems = int64_t(kThreads) * kChunk * pl.rounds;
+    const int wo = g_override.waves.load();
+    pl.waves = wo > 0 ? wo : auto_waves(est, pl.rounds);
+    if (!vec || est == RLSCAN_EST_RETRACE) pl.waves = 4;
+    pl.tile_elems = int64_t(kWave) * pl.waves * kChunk * pl.rounds;
     pl.tiles = (NT + pl.tile_elems - 1) / pl.tile_elems;
     const bool packed_ok = pl.tiles <= 1 || pl.tile_elems % T == 0;
     const int mo = g_override.mapping.load();
@@ -385,35 +430,43 @@ int check_alias(std::initializer_list<const void*> outs, std::initializer_list<c
     return RLSCAN_OK;
 }
 
-template <class E, int R, bool VEC>
+template <class E, int R, int W, bool VEC>
 hipError_t launch_r(const typename E::Params& p, const Geometry& geo, const LookbackArgs& lb,
                     const Plan& pl, hipStream_t stream) {
     const bool lookback = pl.mapping == RLSCAN_MAP_LOOKBACK;
-    const dim3 grid(static_cast<unsigned>(geo.grid)), block(kThreads);
+    const dim3 grid(static_cast<unsigned>(geo.grid)), block(kWave * W);
     if (lookback)
-        hipLaunchKernelGGL((scan_kernel<E, R, true, VEC>), grid, block, 0, stream, p, geo, lb);
+        hipLaunchKernelGGL((scan_kernel<E, R, W, true, VEC>), grid, block, 0, stream, p, geo, lb);
     else
-        hipLaunchKernelGGL((scan_kernel<E, R, false, VEC>), grid, block, 0, stream, p, geo, lb);
+        hipLaunchKernelGGL((scan_kernel<E, R, W, false, VEC>), grid, block, 0, stream, p, geo, lb);
     return hipGetLastError();
+}
+
+template <class E, int W>
+hipError_t launch_w(const typename E::Params& p, const Geometry& geo, const LookbackArgs& lb,
+                    const Plan& pl, hipStream_t stream) {
+    switch (pl.rounds) {
+        case 1: return launch_r<E, 1, W, true>(p, geo, lb, pl, stream);
+        case 2: return launch_r<E, 2, W, true>(p, geo, lb, pl, stream);
+        default: return launch_r<E, 4, W, true>(p, geo, lb, pl, stream);
+    }
 }
 
 template <class E>
 hipError_t launch_kernel(const typename E::Params& p, const Geometry& geo, const LookbackArgs& lb,
                          const Plan& pl, bool vec, hipStream_t stream) {
-    if (!vec) return launch_r<E, 1, false>(p, geo, lb, pl, stream);
-    switch (pl.rounds) {
-        case 1: return launch_r<E, 1, true>(p, geo, lb, pl, stream);
-        case 2: return launch_r<E, 2, true>(p, geo, lb, pl, stream);
-        default: return launch_r<E, 4, true>(p, geo, lb, pl, stream);
-    }
+    if (!vec) return launch_r<E, 1, 4, false>(p, geo, lb, pl, stream);
+    return pl.waves == 8 ? launch_w<E, 8>(p, geo, lb, pl, stream)
+                         : launch_w<E, 4>(p, geo, lb, pl, stream);
 }
 
-// Retrace keeps 2*4*A action values per round in registers: one round only.
+// Retrace keeps 2*4*A action values per round in LDS or registers: one
+// round of four waves only.
 template <class E>
 hipError_t launch_kernel_r1(const typename E::Params& p, const Geometry& geo,
                             const LookbackArgs& lb, const Plan& pl, bool vec, hipStream_t stream) {
-    if (!vec) return launch_r<E, 1, false>(p, geo, lb, pl, stream);
-    return launch_r<E, 1, true>(p, geo, lb, pl, stream);
+    if (!vec) return launch_r<E, 1, 4, false>(p, geo, lb, pl, stream);
+    return launch_r<E, 1, 4, true>(p, geo, lb, pl, stream);
 }
 
 // Plans, takes the look-back scratch if needed, and launches through `fn`.
@@ -421,6 +474,7 @@ template <class Fn>
 int run(int est, int64_t N, int64_t T, bool vec, hipStream_t stream, Fn&& fn) {
     const Plan pl = make_plan(est, N, T, vec);
     if (pl.rounds != 1 && pl.rounds != 2 && pl.rounds != 4) return RLSCAN_ERR_PARAM;
+    if (pl.waves != 4 && pl.waves != 8) return RLSCAN_ERR_PARAM;
     Geometry geo;
     geo.N = N;
     geo.T = T;
@@ -699,9 +753,10 @@ int rlscan_plan(int estimator, int64_t N, int64_t T, int64_t A, rlscan_plan_info
     const int rc = check_shape(N, T, A);
     if (rc != RLSCAN_OK) return rc;
     std::memset(info, 0, sizeof(*info));
-    info->threads = kThreads;
+    info->threads = kWave * 4;
     if (N == 0 || T == 0) return RLSCAN_OK;
     const Plan pl = make_plan(estimator, N, T, true);
+    info->threads = kWave * pl.waves;
     info->mapping = pl.mapping;
     info->rounds = pl.rounds;
     info->tile_elems = pl.tile_elems;
@@ -712,7 +767,25 @@ int rlscan_plan(int estimator, int64_t N, int64_t T, int64_t A, rlscan_plan_info
 
 int rlscan_launch_floor(int64_t grid, hipStream_t stream) {
     if (grid < 1 || grid > kMaxGrid) return RLSCAN_ERR_SHAPE;
-    hipLaunchKernelGGL(empty_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream);
+    hipLaunchKernelGGL(empty_kernel, dim3(static_cast<unsigned>(grid)), dim3(kFloorThreads), 0,
+                       stream);
+    return hipGetLastError() == hipSuccess ? RLSCAN_OK : RLSCAN_ERR_HIP;
+}
+
+int rlscan_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
+    if (bytes < 0 || (bytes & 15) != 0) return RLSCAN_ERR_SHAPE;
+    if (bytes == 0) return RLSCAN_OK;
+    if (dst == nullptr || src == nullptr) return RLSCAN_ERR_NULL;
+    if (!aligned16(dst) || !aligned16(src)) return RLSCAN_ERR_PARAM;
+    const uintptr_t d = reinterpret_cast<uintptr_t>(dst), s = reinterpret_cast<uintptr_t>(src);
+    if (d < s + static_cast<uintptr_t>(bytes) && s < d + static_cast<uintptr_t>(bytes))
+        return RLSCAN_ERR_ALIAS;
+    const int64_t n = bytes / 16;
+    const int64_t per_group = int64_t(kCopyThreads) * kCopyUnroll;
+    const int64_t grid = (n + per_group - 1) / per_group;
+    if (grid > kMaxGrid) return RLSCAN_ERR_SHAPE;
+    hipLaunchKernelGGL(copy_kernel, dim3(static_cast<unsigned>(grid)), dim3(kCopyThreads), 0,
+                       stream, static_cast<const f32x4*>(src), static_cast<f32x4*>(dst), n);
     return hipGetLastError() == hipSuccess ? RLSCAN_OK : RLSCAN_ERR_HIP;
 }
 
@@ -740,12 +813,14 @@ int rlscan_lookback_timeouts(uint64_t* count) {
     return rc;
 }
 
-int rlscan_set_launch_override(int mapping, int rounds, int64_t grid_cap, int flags) {
+int rlscan_set_launch_override(int mapping, int rounds, int waves, int64_t grid_cap, int flags) {
     if (mapping < RLSCAN_MAP_AUTO || mapping > RLSCAN_MAP_LOOKBACK) return RLSCAN_ERR_PARAM;
     if (rounds != 0 && rounds != 1 && rounds != 2 && rounds != 4) return RLSCAN_ERR_PARAM;
+    if (waves != 0 && waves != 4 && waves != 8) return RLSCAN_ERR_PARAM;
     if (grid_cap < 0 || (flags & ~RLSCAN_FLAG_TICKETS) != 0) return RLSCAN_ERR_PARAM;
     g_override.mapping.store(mapping);
     g_override.rounds.store(rounds);
+    g_override.waves.store(waves);
     g_override.grid_cap.store(grid_cap);
     g_override.flags.store(flags);
     return RLSCAN_OK;

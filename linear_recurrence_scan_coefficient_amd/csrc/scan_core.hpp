@@ -18,9 +18,10 @@
 namespace rlscan {
 
 constexpr int kWave = 64;
-constexpr int kWavesPerGroup = 4;
-constexpr int kThreads = kWave * kWavesPerGroup;
 constexpr int kChunk = 4;  // consecutive elements per lane per round
+// A workgroup holds W wave64s (4 or 8, a template parameter of the kernels):
+// W*64 threads scanning a tile of W*64*kChunk*R elements.
+constexpr int kMaxWaves = 8;
 
 // Floating-point step of one element, as built from the inputs.
 struct StepF {

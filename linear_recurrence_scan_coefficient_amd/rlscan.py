@@ -44,6 +44,7 @@ EXPORTED = (
     "rlscan_retrace", "rlscan_eligibility_traces", "rlscan_episodic_prefix_sum",
     "rlscan_status_string", "rlscan_version", "rlscan_release_scratch", "rlscan_plan",
     "rlscan_set_launch_override", "rlscan_lookback_timeouts", "rlscan_launch_floor",
+    "rlscan_stream_copy",
 )
 
 
@@ -85,12 +86,15 @@ def _declare(lib):
     lib.rlscan_version.restype = ctypes.c_char_p
     lib.rlscan_plan.argtypes = [ctypes.c_int, _i64, _i64, _i64, ctypes.POINTER(PlanInfo)]
     lib.rlscan_plan.restype = ctypes.c_int
-    lib.rlscan_set_launch_override.argtypes = [ctypes.c_int, ctypes.c_int, _i64, ctypes.c_int]
+    lib.rlscan_set_launch_override.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64,
+                                                ctypes.c_int]
     lib.rlscan_set_launch_override.restype = ctypes.c_int
     lib.rlscan_lookback_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
     lib.rlscan_lookback_timeouts.restype = ctypes.c_int
     lib.rlscan_launch_floor.argtypes = [_i64, _vp]
     lib.rlscan_launch_floor.restype = ctypes.c_int
+    lib.rlscan_stream_copy.argtypes = [_vp, _vp, _i64, _vp]
+    lib.rlscan_stream_copy.restype = ctypes.c_int
 
 
 def library(path: str = LIB_PATH):
@@ -253,8 +257,8 @@ def rlscan_plan(estimator, N, T, A=1) -> dict:
     return {f[0]: getattr(info, f[0]) for f in PlanInfo._fields_ if f[0] != "reserved"}
 
 
-def rlscan_set_launch_override(mapping=MAP_AUTO, rounds=0, grid_cap=0, flags=0):
-    _check(library().rlscan_set_launch_override(int(mapping), int(rounds), int(grid_cap),
+def rlscan_set_launch_override(mapping=MAP_AUTO, rounds=0, waves=0, grid_cap=0, flags=0):
+    _check(library().rlscan_set_launch_override(int(mapping), int(rounds), int(waves), int(grid_cap),
                                                 int(flags)))
 
 
@@ -266,3 +270,14 @@ def rlscan_lookback_timeouts() -> int:
 
 def rlscan_launch_floor(grid, stream=None):
     _check(library().rlscan_launch_floor(int(grid), _stream(stream)))
+
+
+def rlscan_stream_copy(dst, src, nbytes=None, stream=None):
+    """Streaming copy of `nbytes` (default: all of `src`) between two
+    contiguous device tensors."""
+    if nbytes is None:
+        nbytes = src.numel() * src.element_size()
+    if nbytes > dst.numel() * dst.element_size() or nbytes > src.numel() * src.element_size():
+        raise RlscanError(RLSCAN_ERR_SHAPE, "rlscan_stream_copy: nbytes exceeds a tensor")
+    _check(library().rlscan_stream_copy(dst.data_ptr(), src.data_ptr(), int(nbytes),
+                                        _stream(stream)))

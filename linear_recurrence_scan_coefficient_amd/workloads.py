@@ -36,6 +36,11 @@ Workloads (named by what they are and their sizes):
     gamma 0.999, lambda 0.97, terminated and truncated each
     ~ Bernoulli(1e-4) drawn independently (so a step may carry both),
     bootstrap values ~ N(0, 1); prefix sum dones ~ Bernoulli(1e-4).
+``large_batch_1048576x32``
+    A supplementary large-batch case, not one of the shapes above: GAE,
+    V-trace and discounted returns at 2^20 x 32 (2^25 elements, the packed
+    mapping at a size where HBM bandwidth, not launch latency, bounds the
+    call), distributions as in the production workload.
 """
 from __future__ import annotations
 
@@ -102,6 +107,9 @@ def _presets():
             ("gae", "vtrace", "discounted_returns", "episodic_prefix_sum"),
             gamma=0.999, lam=0.97, term_p=1e-4, trunc_mode="independent", trunc_p=1e-4,
             done_p=1e-4),
+        "large_batch_1048576x32": Workload(
+            "large_batch_1048576x32", 1 << 20, 32,
+            ("gae", "vtrace", "discounted_returns")),
     }
     for n, t in SWEEP_SHAPES:
         name = f"sweep_{n}x{t}"

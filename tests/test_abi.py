@@ -130,22 +130,49 @@ def test_plan_mapping_choice(lib):
     # rows longer than a tile, or rows that do not divide it: look-back
     assert rlscan.rlscan_plan("gae", 64, 8192)["mapping"] == rlscan.MAP_LOOKBACK
     assert rlscan.rlscan_plan("gae", 5, 1000)["mapping"] == rlscan.MAP_LOOKBACK
-    big = rlscan.rlscan_plan("discounted_returns", 8, 1 << 20)
-    assert big["mapping"] == rlscan.MAP_LOOKBACK and big["rounds"] == 4
-    assert big["tiles"] == (8 << 20) // 4096
+    # long rows: four rounds; eight waves for the low-register estimators
+    for est, waves in (("discounted_returns", 8), ("episodic_prefix_sum", 8),
+                       ("eligibility_traces", 8), ("gae", 4), ("vtrace", 4),
+                       ("lambda_returns", 4)):
+        big = rlscan.rlscan_plan(est, 8, 1 << 20)
+        assert big["mapping"] == rlscan.MAP_LOOKBACK and big["rounds"] == 4, est
+        assert big["threads"] == 64 * waves, est
+        assert big["tile_elems"] == 256 * waves * 4, est
+        assert big["tiles"] == (8 << 20) // big["tile_elems"], est
+    # eight waves only with four rounds
+    assert rlscan.rlscan_plan("discounted_returns", 64, 8192)["threads"] == 256
     # a single tile never needs a carry
     assert rlscan.rlscan_plan("gae", 3, 100)["mapping"] == rlscan.MAP_PACKED
-    # Retrace runs one round
-    assert rlscan.rlscan_plan("retrace", 8, 1 << 20, 6)["rounds"] == 1
+    # Retrace runs one round of four waves
+    p = rlscan.rlscan_plan("retrace", 8, 1 << 20, 6)
+    assert p["rounds"] == 1 and p["threads"] == 256
     # overrides
-    rlscan.rlscan_set_launch_override(rlscan.MAP_LOOKBACK, 2, 7)
+    rlscan.rlscan_set_launch_override(rlscan.MAP_LOOKBACK, 2, grid_cap=7)
     p = rlscan.rlscan_plan("gae", 4096, 128)
     assert p["mapping"] == rlscan.MAP_LOOKBACK and p["rounds"] == 2 and p["grid"] == 7
+    rlscan.rlscan_set_launch_override(waves=8)
+    p = rlscan.rlscan_plan("gae", 4096, 128)
+    assert p["threads"] == 512 and p["tile_elems"] == 2048 and p["tiles"] == 256
+    assert p["mapping"] == rlscan.MAP_PACKED
+    assert rlscan.rlscan_plan("retrace", 4096, 128, 6)["threads"] == 256
     rlscan.rlscan_set_launch_override()
     with pytest.raises(rlscan.RlscanError):
         rlscan.rlscan_set_launch_override(rounds=3)
+    with pytest.raises(rlscan.RlscanError):
+        rlscan.rlscan_set_launch_override(waves=6)
     with pytest.raises(rlscan.RlscanError):
         rlscan.rlscan_set_launch_override(flags=2)
     with pytest.raises(rlscan.RlscanError):
         rlscan.rlscan_plan("gae", -1, 5)
     assert rlscan.rlscan_plan("gae", 0, 5)["tiles"] == 0
+
+
+def test_stream_copy_argument_checks(lib):
+    f = lib.rlscan_stream_copy
+    assert f(P[1], P[0], 0, None) == OK            # nothing to copy
+    assert f(P[1], P[0], 15, None) == SHAPE        # not a multiple of 16
+    assert f(P[1], P[0], -16, None) == SHAPE
+    assert f(None, P[0], 64, None) == NULL
+    assert f(P[1] + 4, P[0], 64, None) == PARAM    # misaligned
+    assert f(P[0] + 32, P[0], 64, None) == ALIAS   # overlapping ranges
+    assert f(P[0], P[0] + 32, 64, None) == ALIAS

@@ -77,23 +77,25 @@ MAPPINGS = {
 @pytest.mark.parametrize("estimator", ESTIMATORS)
 @pytest.mark.parametrize("mapping", list(MAPPINGS))
 @pytest.mark.parametrize("rounds", [1, 2, 4])
-def test_mappings_and_rounds(estimator, mapping, rounds):
+@pytest.mark.parametrize("waves", [4, 8])
+def test_mappings_and_rounds(estimator, mapping, rounds, waves):
     m, flags = MAPPINGS[mapping]
-    rlscan.rlscan_set_launch_override(m, rounds, 0, flags)
+    rlscan.rlscan_set_launch_override(m, rounds, waves, 0, flags)
     for N, T in ((512, 128), (40, 4096), (3, 3001)):
         w, inputs = case(estimator, N, T, seed=N + T + rounds)
         plan = rlscan.rlscan_plan(estimator, N, T, w.A)
-        check(estimator, w, inputs, f"{mapping} R={rounds} plan={plan}")
+        check(estimator, w, inputs, f"{mapping} R={rounds} W={waves} plan={plan}")
 
 
 @pytest.mark.parametrize("estimator", ESTIMATORS)
 @pytest.mark.parametrize("mapping", list(MAPPINGS))
-def test_grid_capped_loops(estimator, mapping):
+@pytest.mark.parametrize("waves", [4, 8])
+def test_grid_capped_loops(estimator, mapping, waves):
     m, flags = MAPPINGS[mapping]
-    rlscan.rlscan_set_launch_override(m, 0, 13, flags)
+    rlscan.rlscan_set_launch_override(m, 0, waves, 13, flags)
     for N, T in ((256, 128), (5, 9000)):
         w, inputs = case(estimator, N, T, seed=N * T)
-        check(estimator, w, inputs, f"{mapping} grid_cap=13")
+        check(estimator, w, inputs, f"{mapping} W={waves} grid_cap=13")
 
 
 @pytest.mark.parametrize("estimator", ESTIMATORS)
