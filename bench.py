@@ -20,7 +20,8 @@ measured live with HIP events around replays of a graph of M back-to-back
 launches over M distinct buffer sets (M * bytes >= 512 MiB, so inputs come
 from HBM); `roofline` reports the estimator with the longest launch.  The
 long-sequence workload (8 x 2^20 steps, four estimators, decoupled
-look-back, launched eagerly with events around each call), a supplementary
+look-back; timed over back-to-back calls, and with events around each
+call), a supplementary
 large-batch workload (2^20 x 32, packed), the bandwidth of a plain streaming
 copy moving the same bytes as each call, and the float64 oracle timed on one
 host core are reported as well.
@@ -70,21 +71,27 @@ def parse_args():
     ap.add_argument("--only", default=None, help="comma list of estimators (profiling runs)")
     ap.add_argument("--pmc-run", default=None, metavar="ESTIMATOR",
                     help="counter runs: launch ESTIMATOR ('all': each estimator in turn) once "
-                         "on each of several cold buffer sets of the production workload, "
-                         "then copy a 256 MiB buffer")
+                         "on each of several cold buffer sets of --pmc-workload, then copy a "
+                         "256 MiB buffer with the library's streaming copy")
+    ap.add_argument("--pmc-workload", default="production_4096x128")
+    ap.add_argument("--traffic-summary", nargs=4, default=None,
+                    metavar=("RUN_LOG", "FETCH_CSV", "WRITE_CSV", "HIT_CSV"),
+                    help="write profiles/traffic_<estimator>_<workload>.txt from the stdout "
+                         "of a --pmc-run and the counter_collection.csv of its three "
+                         "rocprofv3 --pmc passes (FETCH_SIZE; WRITE_SIZE; TCC_HIT_sum "
+                         "TCC_MISS_sum); no GPU needed")
     return ap.parse_args()
 
 
 COPY_BYTES = 256 << 20
 
 
-def pmc_run(torch, est, sh, lib):
+def pmc_run(torch, est, workload, sh, lib):
     """Launches for `rocprofv3 --pmc`: the estimator on M distinct buffer
-    sets (cold inputs), then a plain device-to-device copy of COPY_BYTES
-    (reads and writes COPY_BYTES each), the calibration for FETCH_SIZE and
-    WRITE_SIZE."""
-    from linear_recurrence_scan_coefficient_amd import workloads
-    w = workloads.get("production_4096x128")
+    sets (cold inputs), then a plain streaming copy of COPY_BYTES (reads and
+    writes COPY_BYTES each), the calibration for FETCH_SIZE and WRITE_SIZE."""
+    from linear_recurrence_scan_coefficient_amd import rlscan, workloads
+    w = workloads.get(workload)
     ests = list(w.estimators) if est == "all" else [est]
     launches, per_bytes = {}, {}
     for e in ests:
@@ -102,11 +109,82 @@ def pmc_run(torch, est, sh, lib):
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for _ in range(3):
-        dst.copy_(src)
+        rlscan.rlscan_stream_copy(dst, src)
     torch.cuda.synchronize()
     print(json.dumps({"pmc_run": est, "workload": w.name, "launches": launches,
                       "algorithmic_bytes_per_launch": per_bytes, "copy_bytes": COPY_BYTES,
                       "kernel_source_hash": kernel_source_hash()}), flush=True)
+
+
+def traffic_summary(run_log, fetch_csv, write_csv, hit_csv):
+    """Writes profiles/traffic_<estimator>_<workload>.txt: HBM bytes per
+    launch of the scan kernel from the FETCH_SIZE and WRITE_SIZE passes (KiB
+    per dispatch), each scaled by the factor that makes the calibration copy
+    read and write exactly COPY_BYTES, plus the TCC hit rate."""
+    import collections
+    import csv
+    meta = [json.loads(line) for line in open(run_log) if line.startswith('{"pmc_run"')][0]
+    ests = list(meta["launches"])
+    if len(ests) != 1:
+        raise SystemExit("--traffic-summary takes the log of a one-estimator --pmc-run")
+    est = ests[0]
+
+    def load(path):
+        d = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            d[(r["Kernel_Name"], r["Counter_Name"])].append(float(r["Counter_Value"]))
+        return d
+
+    def values(d, pred, counter):
+        return [v for (k, c), vs in d.items() if pred(k) and c == counter for v in vs]
+
+    def mean(xs):
+        return sum(xs) / len(xs)
+
+    is_scan = lambda k: "rlscan::scan_kernel" in k  # noqa: E731
+    is_copy = lambda k: "rlscan::copy_kernel" in k  # noqa: E731
+    F, W, H = load(fetch_csv), load(write_csv), load(hit_csv)
+    kf, kw = values(F, is_scan, "FETCH_SIZE"), values(W, is_scan, "WRITE_SIZE")
+    cf, cw = mean(values(F, is_copy, "FETCH_SIZE")), mean(values(W, is_copy, "WRITE_SIZE"))
+    hit, miss = mean(values(H, is_scan, "TCC_HIT_sum")), mean(values(H, is_scan, "TCC_MISS_sum"))
+    cb = meta["copy_bytes"]
+    f_fetch, f_write = cb / (cf * 1024), cb / (cw * 1024)
+    rd, wr = mean(kf) * 1024 * f_fetch, mean(kw) * 1024 * f_write
+    alg = meta["algorithmic_bytes_per_launch"][est]
+    kname = sorted({k for (k, c) in F if is_scan(k)})
+    wl = meta["workload"]
+    cmd = f"python3 bench.py --pmc-run {est} --pmc-workload {wl}"
+    text = f"""# HBM traffic per launch: {est}, {wl}
+#
+# Commands (repository root, one MI355X; TMPDIR=/tmp), one counter pass each:
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o {est} -- {cmd}
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o {est} -- {cmd}
+#   rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv -d gpurun_out/pmc_hit -o {est} -- {cmd}
+# then, on any machine: python3 bench.py --traffic-summary <stdout of the FETCH_SIZE pass>
+#   gpurun_out/pmc_fetch/{est}_counter_collection.csv gpurun_out/pmc_write/{est}_counter_collection.csv
+#   gpurun_out/pmc_hit/{est}_counter_collection.csv
+# `--pmc-run` launches the kernel once on each of {meta["launches"][est]} distinct buffer sets
+# (cold inputs), then copies a {cb >> 20} MiB buffer with the library's streaming copy kernel
+# (the calibration: it reads and writes exactly {cb} bytes).
+#
+# kernel: {", ".join(kname)}
+# FETCH_SIZE (KiB per dispatch, mean of {len(kf)}): {mean(kf):.1f}
+# WRITE_SIZE (KiB per dispatch, mean of {len(kw)}): {mean(kw):.1f}
+# copy of {cb} B: FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE {cw:.1f} KiB
+# calibration: bytes = KiB * 1024 * factor; fetch factor {f_fetch:.4f}, write factor {f_write:.4f}
+# TCC_HIT_sum {hit:.0f}, TCC_MISS_sum {miss:.0f} per dispatch (hit rate {hit / (hit + miss):.3f})
+# algorithmic bytes per launch: {alg}
+# measured read bytes {rd:.0f} + write bytes {wr:.0f}; ratio to algorithmic {(rd + wr) / alg:.3f}
+kernel_source_hash: {meta["kernel_source_hash"]}
+hbm_bytes_per_launch: {rd + wr:.0f}
+read_bytes_per_launch: {rd:.0f}
+write_bytes_per_launch: {wr:.0f}
+algorithmic_bytes_per_launch: {alg}
+"""
+    out = os.path.join(PROFILE_DIR, f"traffic_{est}_{wl}.txt")
+    with open(out, "w") as fh:
+        fh.write(text)
+    print(text)
 
 
 # ------------------------------------------------------------------ raw calls
@@ -202,13 +280,40 @@ def time_eager_calls(torch, sets, reps):
             for j, e in enumerate(ests)}
 
 
-def eager_workload(torch, w, sh, lib, reps):
-    """Per-call figures of every estimator of a large workload: calls launched
-    eagerly with events around each (two buffer sets of all its estimators,
-    far beyond the last-level cache), beside the copy ceiling for the same
-    bytes."""
-    sets = [CallSet(w.estimators, w, seed, sh, lib) for seed in range(2)]
-    per = time_eager_calls(torch, sets, reps)
+def time_batched_calls(torch, sets, reps):
+    """Mean microseconds per call of each estimator, from one event pair
+    around `reps` back-to-back calls that cycle through the buffer sets (the
+    launch-to-launch throughput, as the graph timing gives it for packed
+    calls; look-back calls cannot be captured into graphs)."""
+    ests = [c[0] for c in sets[0].calls]
+    out = {}
+    for j, e in enumerate(ests):
+        calls = [s.calls[j] for s in sets]
+        for est, fn, args in calls:
+            fn(*args)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            est, fn, args = calls[i % len(calls)]
+            rc = fn(*args)
+            if rc != 0:
+                raise RuntimeError(f"{est}: rlscan status {rc}")
+        b.record()
+        torch.cuda.synchronize()
+        out[e] = a.elapsed_time(b) / reps * 1000.0
+    return out
+
+
+def eager_workload(torch, w, sh, lib, reps, nsets=3):
+    """Per-call figures of every estimator of a large workload: `reps`
+    back-to-back calls per estimator cycling through `nsets` buffer sets (each
+    set alone exceeds the last-level cache, so inputs come from HBM), the
+    same calls with an event pair around each one (what one isolated call
+    costs, launch gap included), and the copy ceiling for the same bytes."""
+    sets = [CallSet(w.estimators, w, seed, sh, lib) for seed in range(nsets)]
+    per = time_batched_calls(torch, sets, reps)
+    iso = time_eager_calls(torch, sets, reps)
     nbytes = dict(sets[0].bytes)
     del sets
     torch.cuda.empty_cache()
@@ -220,6 +325,7 @@ def eager_workload(torch, w, sh, lib, reps):
         res[e] = {"us_per_call": round(us, 2), "elements_per_s": w.N * w.T / (us * 1e-6),
                   "bytes": b, "GB_per_s": round(gbs, 1),
                   "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                  "us_per_isolated_call": round(iso[e], 2),
                   "copy_same_bytes_GB_per_s": round(copy_gbs, 1),
                   "frac_of_copy": round(gbs / copy_gbs, 4)}
     return res
@@ -378,6 +484,10 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
+
     import torch
     from linear_recurrence_scan_coefficient_amd import build, rlscan, workloads
     if not os.path.exists(build.LIB_PATH):
@@ -387,7 +497,7 @@ def main():
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     if args.pmc_run:
-        pmc_run(torch, args.pmc_run, sh, lib)
+        pmc_run(torch, args.pmc_run, args.pmc_workload, sh, lib)
         return
 
     w = workloads.get("production_4096x128")
@@ -455,7 +565,8 @@ def main():
         result["long_8x1048576"] = eager_workload(torch, wl, sh, lib, args.long_calls)
         wb = workloads.get("large_batch_1048576x32")
         print("[bench] timing the supplementary large-batch calls", file=sys.stderr, flush=True)
-        result["large_batch_1048576x32"] = eager_workload(torch, wb, sh, lib, args.long_calls)
+        result["large_batch_1048576x32"] = eager_workload(torch, wb, sh, lib, args.long_calls,
+                                                          nsets=2)
         result["large_batch_1048576x32"]["note"] = (
             "supplementary shape, not one of the named configurations")
 

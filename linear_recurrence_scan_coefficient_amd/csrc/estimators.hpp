@@ -211,6 +211,7 @@ struct Gae {
     using Params = GaeParams;
     using Epi = NoEpi;
     static constexpr int kStageFloats = 0;
+    static constexpr int kOutStageFloats = 0;
     struct Chunk {
         EpisodeChunk ep;
         float v[4];
@@ -240,7 +241,7 @@ struct Gae {
     }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
-                                                 const V x[4], const V[4]) {
+                                                 const V x[4], const V[4], lds_float*) {
         store4<VEC, FULL>(p.out, q, x);
     }
 };
@@ -264,6 +265,7 @@ struct LambdaReturns {
     using Params = LambdaReturnsParams;
     using Epi = NoEpi;
     static constexpr int kStageFloats = 0;
+    static constexpr int kOutStageFloats = 0;
     using Chunk = typename Gae<kTrunc>::Chunk;
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void load(const Params& p, const Geometry& geo,
@@ -290,7 +292,7 @@ struct LambdaReturns {
     }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
-                                                 const V x[4], const V[4]) {
+                                                 const V x[4], const V[4], lds_float*) {
         store4<VEC, FULL>(p.out, q, x);
     }
 };
@@ -312,6 +314,7 @@ struct Discounted {
     using Params = DiscountedParams;
     using Epi = NoEpi;
     static constexpr int kStageFloats = 0;
+    static constexpr int kOutStageFloats = 0;
     struct Chunk {
         EpisodeChunk ep;
     };
@@ -336,7 +339,7 @@ struct Discounted {
     }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
-                                                 const V x[4], const V[4]) {
+                                                 const V x[4], const V[4], lds_float*) {
         store4<VEC, FULL>(p.out, q, x);
     }
 };
@@ -373,6 +376,7 @@ struct Vtrace {
         float gamma_rho[4];  // 0 at a cut
     };
     static constexpr int kStageFloats = 0;
+    static constexpr int kOutStageFloats = 0;
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void load(const Params& p, const Geometry& geo,
                                                 const ChunkPos& q, Chunk& c, lds_float*) {
@@ -405,7 +409,7 @@ struct Vtrace {
     }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi& c,
-                                                 const V x[4], const V before[4]) {
+                                                 const V x[4], const V before[4], lds_float*) {
         float vs[4], pg[4];
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
@@ -438,6 +442,7 @@ struct Retrace {
     // 1 KiB of contiguous memory (a lane's own 4 x A values would be a
     // 16-byte piece every 16 x A bytes, which the L2 fetched ~14% over).
     static constexpr int kStageFloats = (kA >= 1 && kA <= 8) ? 2 * kWave * kChunk * kA : 0;
+    static constexpr int kOutStageFloats = 0;
     struct Params {
         const float *rewards, *next_q, *next_pi;
         const int32_t* actions;
@@ -590,7 +595,7 @@ struct Retrace {
     }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
-                                                 const V x[4], const V[4]) {
+                                                 const V x[4], const V[4], lds_float*) {
         store4<VEC, FULL>(p.out, q, x);
     }
 };
@@ -605,6 +610,7 @@ struct Eligibility {
     static constexpr bool kReverse = false;
     using Epi = NoEpi;
     static constexpr int kStageFloats = 0;
+    static constexpr int kOutStageFloats = 0;
     struct Params {
         const float *x, *dones;
         float* out;
@@ -631,7 +637,7 @@ struct Eligibility {
     }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
-                                                 const V x[4], const V[4]) {
+                                                 const V x[4], const V[4], lds_float*) {
         store4<VEC, FULL>(p.out, q, x);
     }
 };
@@ -646,6 +652,8 @@ struct PrefixSum {
     static constexpr bool kReverse = false;
     using Epi = NoEpi;
     static constexpr int kStageFloats = 0;
+    // 32 output bytes per lane: a wave's 2 KiB of results pass through LDS
+    static constexpr int kOutStageFloats = kWave * kChunk * 2;
     struct Params {
         const int32_t* x;
         const float* dones;
@@ -671,10 +679,35 @@ struct PrefixSum {
             if (++t == geo.T) t = 0;
         }
     }
+    // A lane's four int64 results are 32 contiguous bytes.  Stored directly,
+    // each of its two 16-byte store instructions would cover only every
+    // other 16 bytes of the wave's span -- half of every cache line -- and
+    // streamed (non-temporal) partial lines reach HBM as separate writes
+    // (measured: 1.19x the output bytes).  So a full wave first transposes
+    // its 2 KiB through LDS; each store instruction then writes one
+    // contiguous KiB: lane i stores bytes [16i, 16i+16) of each half.
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
-                                                 const V x[4], const V[4]) {
-        store4<VEC, FULL>(p.out, q, x);
+                                                 const V x[4], const V[4], lds_float* ostage) {
+        static_assert(!kReverse, "the transposed store assumes lane-ascending chunks");
+        if constexpr (VEC && FULL) {
+            typedef __attribute__((address_space(3))) i64x2 lds_i64x2;
+            const int lane = threadIdx.x & (kWave - 1);
+            lds_i64x2* s = reinterpret_cast<lds_i64x2*>(ostage);
+            i64x2 w0, w1;
+            w0.x = x[0]; w0.y = x[1]; w1.x = x[2]; w1.y = x[3];
+            s[2 * lane] = w0;
+            s[2 * lane + 1] = w1;
+            __builtin_amdgcn_wave_barrier();
+            const i64x2 r0 = s[lane];
+            const i64x2 r1 = s[kWave + lane];
+            __builtin_amdgcn_wave_barrier();
+            i64x2* g = reinterpret_cast<i64x2*>(p.out + (q.g0 - static_cast<int64_t>(kChunk) * lane));
+            __builtin_nontemporal_store(r0, g + lane);
+            __builtin_nontemporal_store(r1, g + kWave + lane);
+        } else {
+            store4<VEC, FULL>(p.out, q, x);
+        }
     }
 };
 

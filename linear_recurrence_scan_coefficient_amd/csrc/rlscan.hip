@@ -170,7 +170,7 @@ __device__ __forceinline__ void replay_store(const typename E::Params& p, const 
                                              const typename E::S (&e)[R][kChunk],
                                              const typename E::Epi (&epi)[R],
                                              const A (&incl)[R], A wpre,
-                                             typename E::V carry) {
+                                             typename E::V carry, lds_float* ostage) {
     using V = typename E::V;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -192,7 +192,8 @@ __device__ __forceinline__ void replay_store(const typename E::Params& p, const 
         q.g0 = chunk_base<E, R, W>(geo, tile, wave, r, lane);
         const int64_t rem = geo.NT - q.g0;
         q.valid = rem <= 0 ? 0 : (rem >= kChunk ? kChunk : static_cast<int>(rem));
-        E::template store<VEC, FULL>(p, q, epi[r], out, before);
+        E::template store<VEC, FULL>(p, q, epi[r], out, before,
+                                     ostage + wave * E::kOutStageFloats);
     }
 }
 
@@ -200,7 +201,8 @@ template <class E, int R, int W, bool LOOKBACK, bool VEC, bool FULL>
 __device__ __forceinline__ void scan_tile(const typename E::Params& p, const Geometry& geo,
                                           const LookbackArgs& lb, uint64_t tile,
                                           typename AggOf<typename E::S>::type* sm_wave,
-                                          typename E::V* sm_carry, lds_float* stage) {
+                                          typename E::V* sm_carry, lds_float* stage,
+                                          lds_float* ostage) {
     using S = typename E::S;
     using A = typename AggOf<S>::type;
     const int lane = threadIdx.x & (kWave - 1);
@@ -221,7 +223,7 @@ __device__ __forceinline__ void scan_tile(const typename E::Params& p, const Geo
         if (w < wave) wpre = compose(sm_wave[w], wpre);
     tile_carry<E, W, LOOKBACK>(lb, tile, sm_wave, e[0][0], sm_carry);
     __syncthreads();
-    replay_store<E, R, W, VEC, FULL>(p, geo, tile, e, epi, incl, wpre, *sm_carry);
+    replay_store<E, R, W, VEC, FULL>(p, geo, tile, e, epi, incl, wpre, *sm_carry, ostage);
 }
 
 // One tile per workgroup (or, grid-capped, a loop over tiles).
@@ -238,6 +240,10 @@ __global__ __launch_bounds__(kWave * W) void scan_kernel(const typename E::Param
     constexpr int kStage = E::kStageFloats > 0 ? W * R * E::kStageFloats : 1;
     __shared__ __attribute__((aligned(16))) float sm_stage[kStage];
     lds_float* stage = (lds_float*)sm_stage;
+    // per-wave output staging of the estimators that transpose their stores
+    constexpr int kOutStage = E::kOutStageFloats > 0 ? W * E::kOutStageFloats : 1;
+    __shared__ __attribute__((aligned(16))) float sm_out[kOutStage];
+    lds_float* ostage = (lds_float*)sm_out;
     const bool one_tile_per_group = geo.grid >= geo.num_tiles;
     uint64_t tile = blockIdx.x;
     for (;;) {
@@ -251,9 +257,11 @@ __global__ __launch_bounds__(kWave * W) void scan_kernel(const typename E::Param
         if (tile >= static_cast<uint64_t>(geo.num_tiles)) break;
         // only the tile holding the end of the data needs bounds checks
         if (tile_is_full<E, R, W>(geo, tile))
-            scan_tile<E, R, W, LOOKBACK, VEC, true>(p, geo, lb, tile, sm_wave, &sm_carry, stage);
+            scan_tile<E, R, W, LOOKBACK, VEC, true>(p, geo, lb, tile, sm_wave, &sm_carry, stage,
+                                                    ostage);
         else
-            scan_tile<E, R, W, LOOKBACK, VEC, false>(p, geo, lb, tile, sm_wave, &sm_carry, stage);
+            scan_tile<E, R, W, LOOKBACK, VEC, false>(p, geo, lb, tile, sm_wave, &sm_carry, stage,
+                                                     ostage);
         if (one_tile_per_group) break;
         if (!LOOKBACK || !lb.use_tickets) tile += gridDim.x;
         __syncthreads();  // LDS is reused by the next tile
