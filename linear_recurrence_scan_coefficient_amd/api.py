@@ -1,0 +1,163 @@
+"""PyTorch-facing calls with the pages' call shape: each takes [num_envs,
+seq_len] device tensors, allocates its outputs and returns them, e.g.
+
+    advantages = compute_gae(rewards, values, terminateds, gamma=0.99, lambda_=0.95)
+
+The names and the (rewards, values, terminateds, gamma, lambda_) shape follow
+the rl-triton README, sections "Kernels" (one compute_* function per
+estimator) and "Usage" (compute_gae on [64, 512] float tensors, returning
+the advantages).  The optional truncation arguments follow its section
+"Performance" (terminations, time-limit truncations and bootstrap values for
+GAE, V-trace, TD(lambda) and discounted returns; Retrace takes both flags and
+no bootstrap tensor; traces and the prefix sum take a single dones flag).
+
+Argument marshalling only: every computation runs in librlscan's HIP kernels
+through the C ABI (`rlscan.rlscan_*`).  Inputs must already be on the GPU;
+there is no CPU path.  Flags given as bool or integer tensors are converted
+to the float32 0/1 form the ABI takes (one elementwise copy), non-contiguous
+inputs are made contiguous, and the call runs on the current stream (or
+`stream`).  gamma and lambda_ default to the values of the README's usage
+example.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import rlscan
+
+__all__ = [
+    "compute_gae", "compute_vtrace", "compute_retrace", "compute_lambda_returns",
+    "compute_discounted_returns", "compute_eligibility_traces", "compute_episodic_prefix_sum",
+]
+
+
+def _device_tensor(t, name, dtype=torch.float32, flag=False):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got device {t.device}); rlscan has no "
+                         "CPU path")
+    if t.dtype != dtype:
+        if not flag:
+            raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+        t = t.to(dtype)  # a flag: any dtype, set iff nonzero
+    return t.contiguous()
+
+
+def _flags(t, name):
+    return _device_tensor(t, name, torch.float32, flag=True)
+
+
+def _check_2d(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be a [num_envs, seq_len] tensor, got shape "
+                         f"{tuple(t.shape)}")
+    return t.shape
+
+
+def compute_gae(rewards, values, terminateds, gamma=0.99, lambda_=0.95, *,
+                bootstrap_value=None, truncateds=None, bootstrap_values=None, stream=None):
+    """Advantages A_t = delta_t + gamma*lambda*(1 - cut_t)*A_{t+1} [N, T]
+    (README, Kernels: compute_gae).  bootstrap_value [N] is V at t = T
+    (None: 0); truncateds [N, T] with bootstrap_values [N, T] handle
+    time-limit truncation."""
+    r = _device_tensor(rewards, "rewards")
+    N, T = _check_2d(r, "rewards")
+    out = torch.empty((N, T), dtype=torch.float32, device=r.device)
+    return rlscan.rlscan_gae(
+        r, _device_tensor(values, "values"), _device_tensor(bootstrap_value, "bootstrap_value"),
+        _flags(terminateds, "terminateds"), _flags(truncateds, "truncateds"),
+        _device_tensor(bootstrap_values, "bootstrap_values"), out, float(gamma),
+        float(lambda_), stream)
+
+
+def compute_lambda_returns(rewards, values, terminateds, gamma=0.99, lambda_=0.95, *,
+                           bootstrap_value=None, truncateds=None, bootstrap_values=None,
+                           stream=None):
+    """TD(lambda) returns [N, T] (README, Kernels: compute_lambda_returns)."""
+    r = _device_tensor(rewards, "rewards")
+    N, T = _check_2d(r, "rewards")
+    out = torch.empty((N, T), dtype=torch.float32, device=r.device)
+    return rlscan.rlscan_lambda_returns(
+        r, _device_tensor(values, "values"), _device_tensor(bootstrap_value, "bootstrap_value"),
+        _flags(terminateds, "terminateds"), _flags(truncateds, "truncateds"),
+        _device_tensor(bootstrap_values, "bootstrap_values"), out, float(gamma),
+        float(lambda_), stream)
+
+
+def compute_discounted_returns(rewards, terminateds, gamma=0.99, *, bootstrap_value=None,
+                               truncateds=None, bootstrap_values=None, stream=None):
+    """Discounted reward-to-go [N, T] (README, Kernels:
+    compute_discounted_returns)."""
+    r = _device_tensor(rewards, "rewards")
+    N, T = _check_2d(r, "rewards")
+    out = torch.empty((N, T), dtype=torch.float32, device=r.device)
+    return rlscan.rlscan_discounted_returns(
+        r, _device_tensor(bootstrap_value, "bootstrap_value"), _flags(terminateds, "terminateds"),
+        _flags(truncateds, "truncateds"), _device_tensor(bootstrap_values, "bootstrap_values"),
+        out, float(gamma), stream)
+
+
+def compute_vtrace(rewards, values, log_rhos, terminateds, gamma=0.99, rho_bar=1.0, c_bar=1.0,
+                   *, bootstrap_value=None, truncateds=None, bootstrap_values=None, stream=None):
+    """V-trace targets vs and policy-gradient advantages [N, T] each, as a
+    tuple (README, Kernels: compute_vtrace).  log_rhos = log pi - log mu."""
+    r = _device_tensor(rewards, "rewards")
+    N, T = _check_2d(r, "rewards")
+    vs = torch.empty((N, T), dtype=torch.float32, device=r.device)
+    pg = torch.empty((N, T), dtype=torch.float32, device=r.device)
+    return rlscan.rlscan_vtrace(
+        r, _device_tensor(values, "values"), _device_tensor(bootstrap_value, "bootstrap_value"),
+        _device_tensor(log_rhos, "log_rhos"), _flags(terminateds, "terminateds"),
+        _flags(truncateds, "truncateds"), _device_tensor(bootstrap_values, "bootstrap_values"),
+        vs, pg, float(gamma), float(rho_bar), float(c_bar), stream)
+
+
+def compute_retrace(rewards, next_q_values_all, next_target_probs, actions, behaviour_probs,
+                    terminateds, truncateds, gamma=0.99, lambda_=0.95, *, stream=None):
+    """Retrace(lambda) targets [N, T] (README, Kernels: compute_retrace).
+    next_q_values_all and next_target_probs are [N, T, A] at each step's
+    successor state; actions [N, T] are the taken actions (int32, or any
+    integer dtype, converted); behaviour_probs [N, T] is mu of the taken
+    action.  Both flags are required (README, Performance)."""
+    r = _device_tensor(rewards, "rewards")
+    N, T = _check_2d(r, "rewards")
+    if truncateds is None:
+        raise ValueError("compute_retrace takes terminateds and truncateds, both required")
+    a = actions
+    if isinstance(a, torch.Tensor) and a.dtype != torch.int32 and not a.dtype.is_floating_point:
+        a = a.to(torch.int32)
+    out = torch.empty((N, T), dtype=torch.float32, device=r.device)
+    return rlscan.rlscan_retrace(
+        r, _device_tensor(next_q_values_all, "next_q_values_all"),
+        _device_tensor(next_target_probs, "next_target_probs"),
+        _device_tensor(a, "actions", torch.int32), _device_tensor(behaviour_probs,
+                                                                  "behaviour_probs"),
+        _flags(terminateds, "terminateds"), _flags(truncateds, "truncateds"), out,
+        float(gamma), float(lambda_), stream)
+
+
+def compute_eligibility_traces(x, dones, gamma=0.99, lambda_=0.95, *, stream=None):
+    """Forward traces e_t = x_t + gamma*lambda*(1 - d_t)*e_{t-1} [N, T]
+    (README, Kernels: compute_eligibility_traces)."""
+    xx = _device_tensor(x, "x")
+    N, T = _check_2d(xx, "x")
+    out = torch.empty((N, T), dtype=torch.float32, device=xx.device)
+    return rlscan.rlscan_eligibility_traces(xx, _flags(dones, "dones"), out, float(gamma),
+                                            float(lambda_), stream)
+
+
+def compute_episodic_prefix_sum(x, dones, *, stream=None):
+    """Cumulative sum restarted where dones is set, exact in int64 [N, T]
+    (README, Kernels: compute_episodic_prefix_sum).  x is int32; narrower
+    integer dtypes are widened, int64 is refused (it would not fit)."""
+    xx = x
+    if isinstance(xx, torch.Tensor) and xx.dtype in (torch.bool, torch.uint8, torch.int8,
+                                                     torch.int16):
+        xx = xx.to(torch.int32)
+    xx = _device_tensor(xx, "x", torch.int32)
+    N, T = _check_2d(xx, "x")
+    out = torch.empty((N, T), dtype=torch.int64, device=xx.device)
+    return rlscan.rlscan_episodic_prefix_sum(xx, _flags(dones, "dones"), out, stream)

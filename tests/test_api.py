@@ -1,0 +1,131 @@
+"""GPU parity of the allocating compute_* calls (the pages' call shape)
+against the float64 oracle, plus their argument conversions: flags given as
+bool or uint8, int64 actions, and non-contiguous inputs give the same
+results as the float32 contiguous form."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from reference import assert_parity, oracle_outputs
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+from linear_recurrence_scan_coefficient_amd import api, workloads  # noqa: E402
+from linear_recurrence_scan_coefficient_amd.workloads import ESTIMATORS  # noqa: E402
+
+TRUNC = ("gae", "lambda_returns", "discounted_returns", "vtrace", "retrace")
+
+
+def case(estimator, N=37, T=300, seed=5):
+    opts = dict(term_p=0.05, done_p=0.05, gamma=0.97, lam=0.9)
+    if estimator in TRUNC:
+        opts.update(trunc_mode="independent", trunc_p=0.05)
+    w = workloads.custom(N, T, **opts)
+    return w, workloads.inputs_for(estimator, w, seed)
+
+
+def dev(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def call(estimator, d, w, flag_dtype=None):
+    f = (lambda t: t) if flag_dtype is None else (lambda t: None if t is None else t.to(flag_dtype))
+    if estimator == "gae":
+        return {"advantages": api.compute_gae(
+            d["rewards"], d["values"], f(d["terminated"]), gamma=w.gamma, lambda_=w.lam,
+            bootstrap_value=d.get("bootstrap_value"), truncateds=f(d.get("truncated")),
+            bootstrap_values=d.get("bootstrap_values"))}
+    if estimator == "lambda_returns":
+        return {"returns": api.compute_lambda_returns(
+            d["rewards"], d["values"], f(d["terminated"]), gamma=w.gamma, lambda_=w.lam,
+            bootstrap_value=d.get("bootstrap_value"), truncateds=f(d.get("truncated")),
+            bootstrap_values=d.get("bootstrap_values"))}
+    if estimator == "discounted_returns":
+        return {"returns": api.compute_discounted_returns(
+            d["rewards"], f(d["terminated"]), gamma=w.gamma,
+            bootstrap_value=d.get("bootstrap_value"), truncateds=f(d.get("truncated")),
+            bootstrap_values=d.get("bootstrap_values"))}
+    if estimator == "vtrace":
+        vs, pg = api.compute_vtrace(
+            d["rewards"], d["values"], d["log_rhos"], f(d["terminated"]), gamma=w.gamma,
+            rho_bar=w.rho_bar, c_bar=w.c_bar, bootstrap_value=d.get("bootstrap_value"),
+            truncateds=f(d.get("truncated")), bootstrap_values=d.get("bootstrap_values"))
+        return {"vs": vs, "pg_advantages": pg}
+    if estimator == "retrace":
+        return {"targets": api.compute_retrace(
+            d["rewards"], d["next_q_values_all"], d["next_target_probs"], d["actions"],
+            d["behaviour_probs"], f(d["terminated"]), f(d["truncated"]), gamma=w.gamma,
+            lambda_=w.lam)}
+    if estimator == "eligibility_traces":
+        return {"traces": api.compute_eligibility_traces(d["x"], f(d["dones"]), gamma=w.gamma,
+                                                         lambda_=w.lam)}
+    if estimator == "episodic_prefix_sum":
+        return {"out": api.compute_episodic_prefix_sum(d["x"], f(d["dones"]))}
+    raise ValueError(estimator)
+
+
+def host(out):
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+@pytest.mark.parametrize("estimator", ESTIMATORS)
+def test_compute_calls_match_the_oracle(estimator):
+    w, inputs = case(estimator)
+    d = {k: dev(v) for k, v in inputs.items()}
+    print(f"[api] {estimator} {w.N}x{w.T}", flush=True)
+    got = call(estimator, d, w)
+    torch.cuda.synchronize()
+    assert_parity(host(got), oracle_outputs(estimator, inputs, w), f"api {estimator}")
+
+
+@pytest.mark.parametrize("estimator", ESTIMATORS)
+@pytest.mark.parametrize("flag_dtype", [torch.bool, torch.uint8])
+def test_flag_dtypes_give_identical_results(estimator, flag_dtype):
+    w, inputs = case(estimator, seed=11)
+    d = {k: dev(v) for k, v in inputs.items()}
+    base = host(call(estimator, d, w))
+    conv = host(call(estimator, d, w, flag_dtype))
+    for k in base:
+        np.testing.assert_array_equal(base[k], conv[k])
+
+
+@pytest.mark.parametrize("estimator", ESTIMATORS)
+def test_non_contiguous_inputs(estimator):
+    """Each [N, T] input given as a transposed view of a [T, N] tensor."""
+    w, inputs = case(estimator, seed=13)
+    d = {}
+    for k, v in inputs.items():
+        t = dev(v)
+        if t is not None and t.dim() == 2 and k not in ("bootstrap_value",):
+            t = t.t().contiguous().t()
+            assert not t.is_contiguous()
+        d[k] = t
+    got = call(estimator, d, w)
+    torch.cuda.synchronize()
+    assert_parity(host(got), oracle_outputs(estimator, inputs, w), f"api non-contig {estimator}")
+
+
+def test_retrace_int64_actions():
+    w, inputs = case("retrace", seed=17)
+    d = {k: dev(v) for k, v in inputs.items()}
+    base = host(call("retrace", d, w))
+    d["actions"] = d["actions"].to(torch.int64)
+    np.testing.assert_array_equal(base["targets"], host(call("retrace", d, w))["targets"])
+
+
+def test_usage_example_shape():
+    """The README's usage call: [64, 512] float tensors, zero terminateds."""
+    g = torch.Generator(device="cpu").manual_seed(0)
+    rewards = torch.randn(64, 512, generator=g)
+    values = torch.randn(64, 512, generator=g)
+    terminateds = torch.zeros(64, 512)
+    adv = api.compute_gae(rewards.cuda(), values.cuda(), terminateds.cuda(), gamma=0.99,
+                          lambda_=0.95)
+    assert adv.shape == (64, 512) and adv.dtype == torch.float32 and adv.is_cuda
+    import oracle
+    ref = oracle.gae(rewards.numpy(), values.numpy(), terminateds.numpy(), gamma=0.99, lam=0.95)
+    err = np.abs(adv.cpu().numpy().astype(np.float64) - ref) / (1 + np.abs(ref))
+    assert err.max() <= 1e-4
