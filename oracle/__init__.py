@@ -54,20 +54,23 @@ def load_library(path: str = _LIB_PATH, rebuild: bool = False):
     lib.oracle_op_compose_i64.restype = None
     lib.oracle_linear_recurrence.argtypes = [_i64, _i64, ctypes.c_int, _f64p, _f64p, _f64p]
     lib.oracle_linear_recurrence.restype = None
-    lib.oracle_gae.argtypes = [_i64, _i64, _f32, _f32] + [_f32p] * 6 + [_f64p]
+    # every estimator: ..., carry_in (or NULL), outputs..., carry_out (or NULL)
+    lib.oracle_gae.argtypes = [_i64, _i64, _f32, _f32] + [_f32p] * 7 + [_f64p, _f64p]
     lib.oracle_gae.restype = None
-    lib.oracle_lambda_returns.argtypes = [_i64, _i64, _f32, _f32] + [_f32p] * 6 + [_f64p]
+    lib.oracle_lambda_returns.argtypes = [_i64, _i64, _f32, _f32] + [_f32p] * 7 + [_f64p, _f64p]
     lib.oracle_lambda_returns.restype = None
-    lib.oracle_discounted_returns.argtypes = [_i64, _i64, _f32] + [_f32p] * 5 + [_f64p]
+    lib.oracle_discounted_returns.argtypes = [_i64, _i64, _f32] + [_f32p] * 6 + [_f64p, _f64p]
     lib.oracle_discounted_returns.restype = None
-    lib.oracle_vtrace.argtypes = [_i64, _i64, _f32, _f32, _f32] + [_f32p] * 7 + [_f64p, _f64p]
+    lib.oracle_vtrace.argtypes = ([_i64, _i64, _f32, _f32, _f32] + [_f32p] * 8
+                                  + [_f64p, _f64p, _f64p])
     lib.oracle_vtrace.restype = None
     lib.oracle_retrace.argtypes = ([_i64, _i64, _i64, _f32, _f32, _f32p, _f32p, _f32p, _i32p]
-                                   + [_f32p] * 3 + [_f64p])
+                                   + [_f32p] * 4 + [_i32p, _f32p, _f64p, _f64p])
     lib.oracle_retrace.restype = ctypes.c_int
-    lib.oracle_eligibility_traces.argtypes = [_i64, _i64, _f32, _f32, _f32p, _f32p, _f64p]
+    lib.oracle_eligibility_traces.argtypes = [_i64, _i64, _f32, _f32, _f32p, _f32p, _f32p,
+                                              _f64p, _f64p]
     lib.oracle_eligibility_traces.restype = None
-    lib.oracle_episodic_prefix_sum.argtypes = [_i64, _i64, _i32p, _f32p, _i64p]
+    lib.oracle_episodic_prefix_sum.argtypes = [_i64, _i64, _i32p, _f32p, _i64p, _i64p, _i64p]
     lib.oracle_episodic_prefix_sum.restype = None
     if path == _LIB_PATH:
         _lib = lib
@@ -145,56 +148,85 @@ def _reverse_inputs(rewards, values, bootstrap_value, terminated, truncated,
     return N, T, r, v, bv, term, trunc, bvals
 
 
+# Carry (streaming one rollout through several calls; see oracle.c):
+# `carry_in` [N] is the output just past the chunk (t = T reverse, t = -1
+# forward), or None for whole rollouts; with return_carry=True the call also
+# returns carry_out [N], the output at the chunk's other edge.
+def _carry_in(carry_in, N):
+    return _f32_in(carry_in, (N,))
+
+
+def _with_carry(result, carry_out, return_carry):
+    if not return_carry:
+        return result
+    return (*result, carry_out) if isinstance(result, tuple) else (result, carry_out)
+
+
 def gae(rewards, values, terminated, *, gamma, lam, bootstrap_value=None,
-        truncated=None, bootstrap_values=None, lib=None):
+        truncated=None, bootstrap_values=None, carry_in=None, return_carry=False, lib=None):
     lib = lib or load_library()
     N, T, r, v, bv, term, trunc, bvals = _reverse_inputs(
         rewards, values, bootstrap_value, terminated, truncated, bootstrap_values)
     out = np.empty((N, T), np.float64)
+    co = np.empty(N, np.float64)
     lib.oracle_gae(N, T, _param(gamma), _param(lam), _ptr(r), _ptr(v), _ptr(bv), _ptr(term),
-                   _ptr(trunc), _ptr(bvals), out.ctypes.data_as(_f64p))
-    return out
+                   _ptr(trunc), _ptr(bvals), _ptr(_carry_in(carry_in, N)),
+                   out.ctypes.data_as(_f64p), co.ctypes.data_as(_f64p))
+    return _with_carry(out, co, return_carry)
 
 
 def lambda_returns(rewards, values, terminated, *, gamma, lam, bootstrap_value=None,
-                   truncated=None, bootstrap_values=None, lib=None):
+                   truncated=None, bootstrap_values=None, carry_in=None, return_carry=False,
+                   lib=None):
     lib = lib or load_library()
     N, T, r, v, bv, term, trunc, bvals = _reverse_inputs(
         rewards, values, bootstrap_value, terminated, truncated, bootstrap_values)
     out = np.empty((N, T), np.float64)
+    co = np.empty(N, np.float64)
     lib.oracle_lambda_returns(N, T, _param(gamma), _param(lam), _ptr(r), _ptr(v), _ptr(bv),
-                              _ptr(term), _ptr(trunc), _ptr(bvals), out.ctypes.data_as(_f64p))
-    return out
+                              _ptr(term), _ptr(trunc), _ptr(bvals),
+                              _ptr(_carry_in(carry_in, N)), out.ctypes.data_as(_f64p),
+                              co.ctypes.data_as(_f64p))
+    return _with_carry(out, co, return_carry)
 
 
 def discounted_returns(rewards, terminated, *, gamma, bootstrap_value=None, truncated=None,
-                       bootstrap_values=None, lib=None):
+                       bootstrap_values=None, carry_in=None, return_carry=False, lib=None):
     lib = lib or load_library()
     N, T, r, _, bv, term, trunc, bvals = _reverse_inputs(
         rewards, None, bootstrap_value, terminated, truncated, bootstrap_values)
     out = np.empty((N, T), np.float64)
+    co = np.empty(N, np.float64)
     lib.oracle_discounted_returns(N, T, _param(gamma), _ptr(r), _ptr(bv), _ptr(term),
-                                  _ptr(trunc), _ptr(bvals), out.ctypes.data_as(_f64p))
-    return out
+                                  _ptr(trunc), _ptr(bvals), _ptr(_carry_in(carry_in, N)),
+                                  out.ctypes.data_as(_f64p), co.ctypes.data_as(_f64p))
+    return _with_carry(out, co, return_carry)
 
 
 def vtrace(rewards, values, log_rhos, terminated, *, gamma, rho_bar=1.0, c_bar=1.0,
-           bootstrap_value=None, truncated=None, bootstrap_values=None, lib=None):
-    """Returns (vs, pg_advantages), both float64 [N, T]."""
+           bootstrap_value=None, truncated=None, bootstrap_values=None, carry_in=None,
+           return_carry=False, lib=None):
+    """Returns (vs, pg_advantages), both float64 [N, T] (and carry_out, the
+    vs at t = 0, with return_carry); carry_in is vs at t = T."""
     lib = lib or load_library()
     N, T, r, v, bv, term, trunc, bvals = _reverse_inputs(
         rewards, values, bootstrap_value, terminated, truncated, bootstrap_values)
     lr = _f32_in(log_rhos, (N, T))
     vs = np.empty((N, T), np.float64)
     pg = np.empty((N, T), np.float64)
+    co = np.empty(N, np.float64)
     lib.oracle_vtrace(N, T, _param(gamma), _param(rho_bar), _param(c_bar), _ptr(r), _ptr(v),
                       _ptr(bv), _ptr(lr), _ptr(term), _ptr(trunc), _ptr(bvals),
-                      vs.ctypes.data_as(_f64p), pg.ctypes.data_as(_f64p))
-    return vs, pg
+                      _ptr(_carry_in(carry_in, N)), vs.ctypes.data_as(_f64p),
+                      pg.ctypes.data_as(_f64p), co.ctypes.data_as(_f64p))
+    return _with_carry((vs, pg), co, return_carry)
 
 
 def retrace(rewards, next_q_values_all, next_target_probs, actions, behaviour_probs,
-            terminated, truncated, *, gamma, lam, lib=None):
+            terminated, truncated, *, gamma, lam, carry_in=None, next_actions=None,
+            next_behaviour_probs=None, return_carry=False, lib=None):
+    """With carry_in (G at t = T), next_actions [N] and next_behaviour_probs
+    [N] are a_T and mu(a_T | x_T) of the chunk that follows."""
     lib = lib or load_library()
     N, T = _shape2(rewards)
     q = np.ascontiguousarray(next_q_values_all, dtype=np.float32)
@@ -211,32 +243,50 @@ def retrace(rewards, next_q_values_all, next_target_probs, actions, behaviour_pr
     trunc = _f32_in(truncated, (N, T))
     if term[0] is None or trunc[0] is None:
         raise ValueError("retrace takes both terminated and truncated")
+    ci = _carry_in(carry_in, N)
+    na = nmu = None
+    if ci[0] is not None:
+        if next_actions is None or next_behaviour_probs is None:
+            raise ValueError("carry_in needs next_actions and next_behaviour_probs")
+        na = np.ascontiguousarray(next_actions, dtype=np.int32).reshape(N)
+        nmu = _f32_in(next_behaviour_probs, (N,))
     out = np.empty((N, T), np.float64)
+    co = np.empty(N, np.float64)
     rc = lib.oracle_retrace(N, T, A, _param(gamma), _param(lam), _ptr(r),
                             q.ctypes.data_as(_f32p), _ptr(p), acts.ctypes.data_as(_i32p),
-                            _ptr(mu), _ptr(term), _ptr(trunc), out.ctypes.data_as(_f64p))
+                            _ptr(mu), _ptr(term), _ptr(trunc), _ptr(ci),
+                            na.ctypes.data_as(_i32p) if na is not None else None,
+                            _ptr(nmu) if nmu is not None else None,
+                            out.ctypes.data_as(_f64p), co.ctypes.data_as(_f64p))
     if rc != 0:
         raise ValueError("an action lies outside [0, A)")
-    return out
+    return _with_carry(out, co, return_carry)
 
 
-def eligibility_traces(x, dones, *, gamma, lam, lib=None):
+def eligibility_traces(x, dones, *, gamma, lam, carry_in=None, return_carry=False, lib=None):
     lib = lib or load_library()
     N, T = _shape2(x)
     xs = _f32_in(x, (N, T))
     d = _f32_in(dones, (N, T))
     out = np.empty((N, T), np.float64)
+    co = np.empty(N, np.float64)
     lib.oracle_eligibility_traces(N, T, _param(gamma), _param(lam), _ptr(xs), _ptr(d),
-                                  out.ctypes.data_as(_f64p))
-    return out
+                                  _ptr(_carry_in(carry_in, N)), out.ctypes.data_as(_f64p),
+                                  co.ctypes.data_as(_f64p))
+    return _with_carry(out, co, return_carry)
 
 
-def episodic_prefix_sum(x, dones, *, lib=None):
+def episodic_prefix_sum(x, dones, *, carry_in=None, return_carry=False, lib=None):
     lib = lib or load_library()
     N, T = _shape2(x)
     xs = np.ascontiguousarray(x, dtype=np.int32)
     d = _f32_in(dones, (N, T))
+    ci = None
+    if carry_in is not None:
+        ci = np.ascontiguousarray(carry_in, dtype=np.int64).reshape(N)
     out = np.empty((N, T), np.int64)
+    co = np.empty(N, np.int64)
     lib.oracle_episodic_prefix_sum(N, T, xs.ctypes.data_as(_i32p), _ptr(d),
-                                   out.ctypes.data_as(_i64p))
-    return out
+                                   ci.ctypes.data_as(_i64p) if ci is not None else None,
+                                   out.ctypes.data_as(_i64p), co.ctypes.data_as(_i64p))
+    return _with_carry(out, co, return_carry)

@@ -44,6 +44,19 @@
  *         values[n, t+1]           otherwise;
  *   - forward estimators (traces, prefix sum): the flag at step t drops the
  *     carry coming from step t-1, and every row starts from 0.
+ *   - streaming one rollout through several calls (the "carry" arguments;
+ *     the pages' chunked fallback for long sequences, README, Kernels table,
+ *     last column): carry_in[n], when given, is the estimator's output at the
+ *     step just past this chunk -- t = T for the reverse estimators (the
+ *     first step of the chunk that follows), t = -1 for the forward ones.
+ *     The chunk's edge step (t = T-1, resp. t = 0) then continues into it
+ *     instead of ending the episode; it still ends there when terminated,
+ *     truncated (reverse) or done (forward).  V at t = T is
+ *     bootstrap_value[n], and Retrace takes a_T and mu_T as next_actions[n]
+ *     and next_behaviour_probs[n].  carry_out[n], when given, receives the
+ *     output at the opposite edge (t = 0 reverse, t = T-1 forward; V-trace:
+ *     vs), which is the carry_in of the call for the neighbouring chunk.
+ *     NULL carry_in: every row is a whole rollout, as above.
  *
  * Build: gcc -O2 -ffp-contract=off -shared -fPIC oracle.c -o liboracle.so -lm
  * Parity of the semantic readings themselves is unpinned by the pages (they
@@ -75,10 +88,16 @@ static double next_state_value(const float* values, const float* bootstrap_value
     return (double)values[i + 1];
 }
 
+/* `continues`: the row carries on past t = T-1 (a carry_in was given). */
 static int is_cut(const float* terminated, const float* truncated,
-                  int64_t i, int64_t t, int64_t T)
+                  int64_t i, int64_t t, int64_t T, int continues)
 {
-    return is_set(terminated, i) || is_set(truncated, i) || t == T - 1;
+    return is_set(terminated, i) || is_set(truncated, i) || (t == T - 1 && !continues);
+}
+
+static double carry_of(const float* carry_in, int64_t n)
+{
+    return carry_in ? (double)carry_in[n] : 0.0;
 }
 
 /* ------------------------------------------------------------------------ *
@@ -139,21 +158,24 @@ void oracle_gae(int64_t N, int64_t T, float gamma_f, float lambda_f,
                 const float* rewards, const float* values,
                 const float* bootstrap_value, const float* terminated,
                 const float* truncated, const float* bootstrap_values,
-                double* advantages)
+                const float* carry_in, double* advantages, double* carry_out)
 {
     const double gamma = gamma_f, lambda = lambda_f;
+    const int continues = carry_in != NULL;
     for (int64_t n = 0; n < N; ++n) {
-        double next_adv = 0.0;
+        double next_adv = carry_of(carry_in, n);  /* A_T */
         for (int64_t t = T - 1; t >= 0; --t) {
             const int64_t i = n * T + t;
             const double v_next = next_state_value(values, bootstrap_value, terminated,
                                                    truncated, bootstrap_values, n, t, T);
             const double delta = (double)rewards[i] + gamma * v_next - (double)values[i];
-            const double carry = is_cut(terminated, truncated, i, t, T) ? 0.0 : next_adv;
+            const double carry =
+                is_cut(terminated, truncated, i, t, T, continues) ? 0.0 : next_adv;
             const double adv = delta + gamma * lambda * carry;
             advantages[i] = adv;
             next_adv = adv;
         }
+        if (carry_out) carry_out[n] = advantages[n * T];
     }
 }
 
@@ -167,25 +189,25 @@ void oracle_lambda_returns(int64_t N, int64_t T, float gamma_f, float lambda_f,
                            const float* rewards, const float* values,
                            const float* bootstrap_value, const float* terminated,
                            const float* truncated, const float* bootstrap_values,
-                           double* returns)
+                           const float* carry_in, double* returns, double* carry_out)
 {
     const double gamma = gamma_f, lambda = lambda_f;
+    const int continues = carry_in != NULL;
     for (int64_t n = 0; n < N; ++n) {
-        double next_ret = 0.0;
+        double next_ret = carry_of(carry_in, n);  /* G_T */
         for (int64_t t = T - 1; t >= 0; --t) {
             const int64_t i = n * T + t;
+            const double v_next = next_state_value(values, bootstrap_value, terminated,
+                                                   truncated, bootstrap_values, n, t, T);
             double g;
-            if (is_cut(terminated, truncated, i, t, T)) {
-                const double v_next = next_state_value(values, bootstrap_value, terminated,
-                                                       truncated, bootstrap_values, n, t, T);
+            if (is_cut(terminated, truncated, i, t, T, continues))
                 g = (double)rewards[i] + gamma * v_next;
-            } else {
-                g = (double)rewards[i] +
-                    gamma * ((1.0 - lambda) * (double)values[i + 1] + lambda * next_ret);
-            }
+            else  /* here v_next is V_{t+1} (bootstrap_value[n] at t = T-1) */
+                g = (double)rewards[i] + gamma * ((1.0 - lambda) * v_next + lambda * next_ret);
             returns[i] = g;
             next_ret = g;
         }
+        if (carry_out) carry_out[n] = returns[n * T];
     }
 }
 
@@ -200,15 +222,17 @@ void oracle_lambda_returns(int64_t N, int64_t T, float gamma_f, float lambda_f,
 void oracle_discounted_returns(int64_t N, int64_t T, float gamma_f,
                                const float* rewards, const float* bootstrap_value,
                                const float* terminated, const float* truncated,
-                               const float* bootstrap_values, double* returns)
+                               const float* bootstrap_values, const float* carry_in,
+                               double* returns, double* carry_out)
 {
     const double gamma = gamma_f;
+    const int continues = carry_in != NULL;
     for (int64_t n = 0; n < N; ++n) {
-        double next_ret = 0.0;
+        double next_ret = carry_of(carry_in, n);  /* G_T */
         for (int64_t t = T - 1; t >= 0; --t) {
             const int64_t i = n * T + t;
             double follow;
-            if (is_cut(terminated, truncated, i, t, T))
+            if (is_cut(terminated, truncated, i, t, T, continues))
                 follow = next_state_value(NULL, bootstrap_value, terminated, truncated,
                                           bootstrap_values, n, t, T);
             else
@@ -217,6 +241,7 @@ void oracle_discounted_returns(int64_t N, int64_t T, float gamma_f,
             returns[i] = g;
             next_ret = g;
         }
+        if (carry_out) carry_out[n] = returns[n * T];
     }
 }
 
@@ -234,12 +259,16 @@ void oracle_vtrace(int64_t N, int64_t T, float gamma_f, float rho_bar_f, float c
                    const float* rewards, const float* values,
                    const float* bootstrap_value, const float* log_rhos,
                    const float* terminated, const float* truncated,
-                   const float* bootstrap_values, double* vs, double* pg_advantages)
+                   const float* bootstrap_values, const float* carry_in, double* vs,
+                   double* pg_advantages, double* carry_out)
 {
     const double gamma = gamma_f, rho_bar = rho_bar_f, c_bar = c_bar_f;
+    const int continues = carry_in != NULL;
     for (int64_t n = 0; n < N; ++n) {
-        double next_u = 0.0;   /* vs_{t+1} - V_{t+1} */
-        double next_vs = 0.0;  /* vs_{t+1} */
+        /* carry_in is vs_T; V_T is bootstrap_value[n] (or 0) */
+        const double v_T = bootstrap_value ? (double)bootstrap_value[n] : 0.0;
+        double next_vs = carry_of(carry_in, n);           /* vs_{t+1} */
+        double next_u = continues ? next_vs - v_T : 0.0;  /* vs_{t+1} - V_{t+1} */
         for (int64_t t = T - 1; t >= 0; --t) {
             const int64_t i = n * T + t;
             const double ratio = exp((double)log_rhos[i]);
@@ -247,7 +276,7 @@ void oracle_vtrace(int64_t N, int64_t T, float gamma_f, float rho_bar_f, float c
             const double c = ratio < c_bar ? ratio : c_bar;
             const double v_next = next_state_value(values, bootstrap_value, terminated,
                                                    truncated, bootstrap_values, n, t, T);
-            const int cut = is_cut(terminated, truncated, i, t, T);
+            const int cut = is_cut(terminated, truncated, i, t, T, continues);
             const double delta = rho * ((double)rewards[i] + gamma * v_next - (double)values[i]);
             const double u = delta + (cut ? 0.0 : gamma * c * next_u);
             const double vs_t = (double)values[i] + u;
@@ -257,6 +286,7 @@ void oracle_vtrace(int64_t N, int64_t T, float gamma_f, float rho_bar_f, float c
             next_u = u;
             next_vs = vs_t;
         }
+        if (carry_out) carry_out[n] = vs[n * T];
     }
 }
 
@@ -281,11 +311,14 @@ void oracle_vtrace(int64_t N, int64_t T, float gamma_f, float rho_bar_f, float c
 int oracle_retrace(int64_t N, int64_t T, int64_t A, float gamma_f, float lambda_f,
                    const float* rewards, const float* next_q, const float* next_pi,
                    const int32_t* actions, const float* behaviour_probs,
-                   const float* terminated, const float* truncated, double* targets)
+                   const float* terminated, const float* truncated,
+                   const float* carry_in, const int32_t* next_actions,
+                   const float* next_behaviour_probs, double* targets, double* carry_out)
 {
     const double gamma = gamma_f, lambda = lambda_f;
+    const int continues = carry_in != NULL;
     for (int64_t n = 0; n < N; ++n) {
-        double next_g = 0.0;
+        double next_g = carry_of(carry_in, n);  /* G_T */
         for (int64_t t = T - 1; t >= 0; --t) {
             const int64_t i = n * T + t;
             const float* q = next_q + i * A;
@@ -295,18 +328,22 @@ int oracle_retrace(int64_t N, int64_t T, int64_t A, float gamma_f, float lambda_
             double g;
             if (is_set(terminated, i)) {
                 g = (double)rewards[i];
-            } else if (is_set(truncated, i) || t == T - 1) {
+            } else if (is_set(truncated, i) || (t == T - 1 && !continues)) {
                 g = (double)rewards[i] + gamma * eq;
             } else {
-                const int32_t a_next = actions[i + 1];
+                /* a_{t+1} and mu_{t+1}: the next chunk's first step at t = T-1 */
+                const int32_t a_next = t == T - 1 ? next_actions[n] : actions[i + 1];
+                const double mu_next = t == T - 1 ? (double)next_behaviour_probs[n]
+                                                  : (double)behaviour_probs[i + 1];
                 if (a_next < 0 || (int64_t)a_next >= A) return -1;
-                const double ratio = (double)p[a_next] / (double)behaviour_probs[i + 1];
+                const double ratio = (double)p[a_next] / mu_next;
                 const double c = lambda * (ratio < 1.0 ? ratio : 1.0);
                 g = (double)rewards[i] + gamma * (eq + c * (next_g - (double)q[a_next]));
             }
             targets[i] = g;
             next_g = g;
         }
+        if (carry_out) carry_out[n] = targets[n * T];
     }
     return 0;
 }
@@ -318,17 +355,19 @@ int oracle_retrace(int64_t N, int64_t T, int64_t A, float gamma_f, float lambda_
  *     e_t = x_t + (d_t ? 0 : gamma * lambda * e_{t-1}),   e_{-1} = 0
  * ------------------------------------------------------------------------ */
 void oracle_eligibility_traces(int64_t N, int64_t T, float gamma_f, float lambda_f,
-                               const float* x, const float* dones, double* traces)
+                               const float* x, const float* dones, const float* carry_in,
+                               double* traces, double* carry_out)
 {
     const double gamma = gamma_f, lambda = lambda_f;
     for (int64_t n = 0; n < N; ++n) {
-        double prev = 0.0;
+        double prev = carry_of(carry_in, n);  /* e_{-1} */
         for (int64_t t = 0; t < T; ++t) {
             const int64_t i = n * T + t;
             const double e = (double)x[i] + (is_set(dones, i) ? 0.0 : gamma * lambda * prev);
             traces[i] = e;
             prev = e;
         }
+        if (carry_out) carry_out[n] = traces[n * T + T - 1];
     }
 }
 
@@ -339,15 +378,17 @@ void oracle_eligibility_traces(int64_t N, int64_t T, float gamma_f, float lambda
  *     y_t = x_t + (d_t ? 0 : y_{t-1}),   y_{-1} = 0
  * ------------------------------------------------------------------------ */
 void oracle_episodic_prefix_sum(int64_t N, int64_t T, const int32_t* x,
-                                const float* dones, int64_t* out)
+                                const float* dones, const int64_t* carry_in, int64_t* out,
+                                int64_t* carry_out)
 {
     for (int64_t n = 0; n < N; ++n) {
-        int64_t prev = 0;
+        int64_t prev = carry_in ? carry_in[n] : 0;  /* y_{-1} */
         for (int64_t t = 0; t < T; ++t) {
             const int64_t i = n * T + t;
             const int64_t y = (int64_t)x[i] + (is_set(dones, i) ? 0 : prev);
             out[i] = y;
             prev = y;
         }
+        if (carry_out) carry_out[n] = out[n * T + T - 1];
     }
 }

@@ -555,18 +555,192 @@ def pin_prefix_sum(lib):
         == 4 * (2**31 - 1)
 
 
+# ------------------------------------------------------------ carry (chunking)
+# Streaming one rollout through several calls must give the whole-rollout
+# result: the chunk after a split point is computed first (reverse
+# estimators) and hands its edge output to the chunk before it as carry_in;
+# forward estimators hand it the other way.  The whole-rollout oracle is
+# pinned by the brute-force and closed-form pins above, so these pin the
+# carry arguments to it.  The carry crosses the call in float32 (as on the
+# GPU), hence the tolerance; a dropped or misplaced carry errs by O(1).
+CARRY_TOL = 1e-6
+
+
+def split_points(T):
+    return (1, 2, T // 2, T - 1)
+
+
+def _force_edge_flags(d, T1):
+    """Make the step just before the split terminated in row 0 and
+    truncated in row 1, so the carry must be ignored there."""
+    if d.get("terminated") is not None:
+        d["terminated"][0, T1 - 1] = 1.0
+    if d.get("truncated") is not None:
+        d["truncated"][1, T1 - 1] = 1.0
+
+
+def _cols(d, lo, hi):
+    out = {}
+    for k, v in d.items():
+        if v is None or k == "bootstrap_value":
+            out[k] = v
+        elif isinstance(v, np.ndarray) and v.ndim >= 2:
+            out[k] = np.ascontiguousarray(v[:, lo:hi])
+        else:
+            out[k] = v
+    return out
+
+
+def _reverse_chunk_pin(lib, fn, keys, d, gamma_kw, two_outputs=False):
+    T = d["rewards"].shape[1]
+    whole = fn(**{k: d[k] for k in keys}, **gamma_kw, lib=lib)
+    for T1 in split_points(T):
+        late = _cols(d, T1, T)
+        early = _cols(d, 0, T1)
+        res_late = fn(**{k: late[k] for k in keys}, **gamma_kw, return_carry=True, lib=lib)
+        carry = res_late[-1].astype(np.float32)
+        if "values" in d:  # V at the split point is the early chunk's bootstrap
+            early["bootstrap_value"] = np.ascontiguousarray(d["values"][:, T1])
+        res_early = fn(**{k: early[k] for k in keys}, **gamma_kw, carry_in=carry,
+                       return_carry=True, lib=lib)
+        outs_whole = whole if two_outputs else (whole,)
+        for i, w in enumerate(outs_whole):
+            got = np.concatenate([res_early[i], res_late[i]], axis=1)
+            close(got, w, CARRY_TOL)
+        close(res_early[-1], res_early[0][:, 0], 0.0)  # carry_out is the t = 0 output
+
+
+def _reverse_data(seed, with_values=True):
+    d = small_value_inputs(seed, N=3, T=12)
+    if not with_values:
+        d.pop("values")
+    return d
+
+
+def pin_gae_chunked(lib):
+    for T1 in (5,):
+        d = _reverse_data(41)
+        _force_edge_flags(d, T1)
+        _reverse_chunk_pin(lib, oracle.gae, ("rewards", "values", "terminated",
+                                             "bootstrap_value", "truncated",
+                                             "bootstrap_values"), d,
+                           dict(gamma=0.97, lam=0.9))
+    _reverse_chunk_pin(lib, oracle.gae, ("rewards", "values", "terminated", "bootstrap_value",
+                                         "truncated", "bootstrap_values"), _reverse_data(42),
+                       dict(gamma=0.97, lam=0.9))
+
+
+def pin_lambda_returns_chunked(lib):
+    d = _reverse_data(43)
+    _force_edge_flags(d, 6)
+    _reverse_chunk_pin(lib, oracle.lambda_returns, ("rewards", "values", "terminated",
+                                                    "bootstrap_value", "truncated",
+                                                    "bootstrap_values"), d,
+                       dict(gamma=0.95, lam=0.8))
+
+
+def pin_discounted_chunked(lib):
+    d = _reverse_data(44)
+    _force_edge_flags(d, 6)
+    # the split point's V_T is not an input of discounted returns: the early
+    # chunk continues straight into the carried return
+    _reverse_chunk_pin(lib, oracle.discounted_returns,
+                       ("rewards", "terminated", "bootstrap_value", "truncated",
+                        "bootstrap_values"), {k: v for k, v in d.items() if k != "values"},
+                       dict(gamma=0.93))
+
+
+def pin_vtrace_chunked(lib):
+    d = _reverse_data(45)
+    _force_edge_flags(d, 6)
+    rng = np.random.default_rng(46)
+    d["log_rhos"] = (0.5 * rng.standard_normal(d["rewards"].shape)).astype(np.float32)
+    _reverse_chunk_pin(lib, oracle.vtrace, ("rewards", "values", "log_rhos", "terminated",
+                                            "bootstrap_value", "truncated",
+                                            "bootstrap_values"), d,
+                       dict(gamma=0.96, rho_bar=1.0, c_bar=0.9), two_outputs=True)
+
+
+def pin_retrace_chunked(lib):
+    d = small_retrace_inputs(47, N=3, T=12)
+    T = 12
+    whole = call_retrace(d, 0.95, 0.85, lib)
+    for T1 in split_points(T):
+        e = {k: np.ascontiguousarray(v[:, :T1]) for k, v in d.items()}
+        l = {k: np.ascontiguousarray(v[:, T1:]) for k, v in d.items()}
+        if T1 == T // 2:
+            e["terminated"][0, -1] = 1.0
+            e["truncated"][1, -1] = 1.0
+            dd = {k: v.copy() for k, v in d.items()}
+            dd["terminated"][0, T1 - 1] = dd["truncated"][1, T1 - 1] = 1.0
+            ref = call_retrace(dd, 0.95, 0.85, lib)
+        else:
+            ref = whole
+        tl, carry = oracle.retrace(l["rewards"], l["next_q"], l["next_pi"], l["actions"],
+                                   l["mu"], l["terminated"], l["truncated"], gamma=0.95,
+                                   lam=0.85, return_carry=True, lib=lib)
+        te, co = oracle.retrace(e["rewards"], e["next_q"], e["next_pi"], e["actions"], e["mu"],
+                                e["terminated"], e["truncated"], gamma=0.95, lam=0.85,
+                                carry_in=carry.astype(np.float32),
+                                next_actions=d["actions"][:, T1],
+                                next_behaviour_probs=d["mu"][:, T1], return_carry=True,
+                                lib=lib)
+        close(np.concatenate([te, tl], axis=1), ref, CARRY_TOL)
+        close(co, te[:, 0], 0.0)
+
+
+def pin_eligibility_chunked(lib):
+    rng = np.random.default_rng(48)
+    x = rng.standard_normal((3, 12)).astype(np.float32)
+    dones = (rng.random((3, 12)) < 0.2).astype(np.float32)
+    whole = oracle.eligibility_traces(x, dones, gamma=0.9, lam=0.8, lib=lib)
+    for T1 in split_points(12):
+        dd = dones.copy()
+        if T1 == 6:
+            dd[0, T1] = 1.0  # the later chunk's first step drops the carry
+        ref = oracle.eligibility_traces(x, dd, gamma=0.9, lam=0.8, lib=lib)
+        e, co = oracle.eligibility_traces(x[:, :T1], dd[:, :T1], gamma=0.9, lam=0.8,
+                                          return_carry=True, lib=lib)
+        l = oracle.eligibility_traces(np.ascontiguousarray(x[:, T1:]),
+                                      np.ascontiguousarray(dd[:, T1:]), gamma=0.9, lam=0.8,
+                                      carry_in=co.astype(np.float32), lib=lib)
+        close(np.concatenate([e, l], axis=1), ref, CARRY_TOL)
+        close(co, e[:, -1], 0.0)
+    assert np.array_equal(whole, oracle.eligibility_traces(x, dones, gamma=0.9, lam=0.8,
+                                                           lib=lib))
+
+
+def pin_prefix_sum_chunked(lib):
+    rng = np.random.default_rng(49)
+    x = rng.integers(-8, 9, (3, 12)).astype(np.int32)
+    dones = (rng.random((3, 12)) < 0.2).astype(np.float32)
+    for T1 in split_points(12):
+        dd = dones.copy()
+        if T1 == 6:
+            dd[1, T1] = 1.0
+        ref = segment_cumsum(x, dd)
+        e, co = oracle.episodic_prefix_sum(x[:, :T1], dd[:, :T1], return_carry=True, lib=lib)
+        l = oracle.episodic_prefix_sum(np.ascontiguousarray(x[:, T1:]),
+                                       np.ascontiguousarray(dd[:, T1:]), carry_in=co, lib=lib)
+        assert np.array_equal(np.concatenate([e, l], axis=1), ref)
+        assert np.array_equal(co, e[:, -1])
+
+
 PINS = {
     "operator": [pin_operator_associative, pin_operator_identity_and_meaning,
                  pin_linear_recurrence_brute],
     "gae": [pin_gae_brute, pin_gae_lambda0_is_td_error,
-            pin_gae_lambda1_is_mc_return_minus_value, pin_gae_terminated_wins],
+            pin_gae_lambda1_is_mc_return_minus_value, pin_gae_terminated_wins,
+            pin_gae_chunked],
     "lambda_returns": [pin_lambda_returns_brute, pin_lambda_returns_is_gae_plus_values,
-                       pin_lambda_returns_limits],
+                       pin_lambda_returns_limits, pin_lambda_returns_chunked],
     "discounted_returns": [pin_discounted_brute, pin_discounted_constant_reward,
-                           pin_discounted_lfilter],
+                           pin_discounted_lfilter, pin_discounted_chunked],
     "vtrace": [pin_vtrace_brute, pin_vtrace_on_policy_is_discounted_return,
-               pin_vtrace_no_trace_is_one_step],
-    "retrace": [pin_retrace_brute, pin_retrace_lambda0, pin_retrace_onehot_on_policy],
-    "eligibility_traces": [pin_eligibility_brute, pin_eligibility_limits],
-    "episodic_prefix_sum": [pin_prefix_sum],
+               pin_vtrace_no_trace_is_one_step, pin_vtrace_chunked],
+    "retrace": [pin_retrace_brute, pin_retrace_lambda0, pin_retrace_onehot_on_policy,
+                pin_retrace_chunked],
+    "eligibility_traces": [pin_eligibility_brute, pin_eligibility_limits,
+                           pin_eligibility_chunked],
+    "episodic_prefix_sum": [pin_prefix_sum, pin_prefix_sum_chunked],
 }

@@ -131,15 +131,15 @@ MUTATIONS = [
      "const double delta = (double)rewards[i] + v_next - (double)values[i];"),
     ("gae", "const double adv = delta + gamma * lambda * carry;",
      "const double adv = delta + gamma * carry;"),
-    ("gae", "const double carry = is_cut(terminated, truncated, i, t, T) ? 0.0 : next_adv;",
-     "const double carry = is_cut(terminated, NULL, i, t, T) ? 0.0 : next_adv;"),
+    ("gae", "is_cut(terminated, truncated, i, t, T, continues) ? 0.0 : next_adv;",
+     "is_cut(terminated, NULL, i, t, T, continues) ? 0.0 : next_adv;"),
     ("gae", "if (is_set(terminated, i)) return 0.0;\n    if (is_set(truncated, i)) return "
             "(double)bootstrap_values[i];",
      "if (is_set(truncated, i)) return (double)bootstrap_values[i];\n    "
      "if (is_set(terminated, i)) return 0.0;"),
     ("gae", "if (t == T - 1) return bootstrap_value ? (double)bootstrap_value[n] : 0.0;",
      "if (t == T - 1) return 0.0;"),
-    ("lambda_returns", "(1.0 - lambda) * (double)values[i + 1]", "lambda * (double)values[i + 1]"),
+    ("lambda_returns", "(1.0 - lambda) * v_next", "lambda * v_next"),
     ("lambda_returns", "g = (double)rewards[i] + gamma * v_next;", "g = (double)rewards[i] + v_next;"),
     ("discounted_returns", "follow = next_ret;", "follow = gamma * next_ret;"),
     ("discounted_returns", "follow = next_state_value(NULL,", "follow = 0.0 * next_state_value(NULL,"),
@@ -148,7 +148,7 @@ MUTATIONS = [
      "const double follow = cut ? v_next : next_u;"),
     ("vtrace", "const double c = ratio < c_bar ? ratio : c_bar;",
      "const double c = ratio < c_bar ? ratio : 1.0;"),
-    ("retrace", "const int32_t a_next = actions[i + 1];", "const int32_t a_next = actions[i];"),
+    ("retrace", "next_actions[n] : actions[i + 1];", "next_actions[n] : actions[i];"),
     ("retrace", "(double)behaviour_probs[i + 1]", "(double)behaviour_probs[i]"),
     ("retrace", "g = (double)rewards[i];\n", "g = (double)rewards[i] + gamma * eq;\n"),
     ("retrace", "const double c = lambda * (ratio < 1.0 ? ratio : 1.0);",
@@ -156,6 +156,24 @@ MUTATIONS = [
     ("eligibility_traces", "(is_set(dones, i) ? 0.0 : gamma * lambda * prev)",
      "((t > 0 && is_set(dones, i - 1)) ? 0.0 : gamma * lambda * prev)"),
     ("episodic_prefix_sum", "(is_set(dones, i) ? 0 : prev)", "prev"),
+    # the carry arguments (streaming one rollout through several calls)
+    ("gae", "(t == T - 1 && !continues)", "(t == T - 1)"),
+    ("gae", "double next_adv = carry_of(carry_in, n);", "double next_adv = 0.0;"),
+    ("gae", "if (carry_out) carry_out[n] = advantages[n * T];",
+     "if (carry_out) carry_out[n] = advantages[n * T + 1];"),
+    ("lambda_returns", "double next_ret = carry_of(carry_in, n);  /* G_T */\n        for "
+                       "(int64_t t = T - 1; t >= 0; --t) {\n            const int64_t i = n * T "
+                       "+ t;\n            const double v_next",
+     "double next_ret = 0.0;\n        for (int64_t t = T - 1; t >= 0; --t) {\n            "
+     "const int64_t i = n * T + t;\n            const double v_next"),
+    ("discounted_returns", "carry_out[n] = returns[n * T];\n    }\n}\n\n/* ----------------"
+                           "-------------------------------------------------------- *\n * V-trace",
+     "carry_out[n] = returns[n * T + T - 1];\n    }\n}\n\n/* ----------------"
+     "-------------------------------------------------------- *\n * V-trace"),
+    ("vtrace", "next_vs - v_T", "next_vs"),
+    ("retrace", "(double)next_behaviour_probs[n]", "(double)behaviour_probs[i]"),
+    ("eligibility_traces", "double prev = carry_of(carry_in, n);", "double prev = 0.0;"),
+    ("episodic_prefix_sum", "int64_t prev = carry_in ? carry_in[n] : 0;", "int64_t prev = 0;"),
 ]
 
 
