@@ -183,6 +183,68 @@ int rlscan_eligibility_traces(const float* x, const float* dones, float* traces,
 int rlscan_episodic_prefix_sum(const int32_t* x, const float* dones, int64_t* out,
                                int64_t N, int64_t T, hipStream_t stream);
 
+/* ---- streaming one rollout through several calls (carry) -----------------
+ * The rl-triton README, Kernels table, last column, serves long sequences
+ * by a chunked fallback: a rollout is processed in pieces.  Each *_carry
+ * entry point is the call above plus two per-row arrays:
+ *   carry_in [N] or NULL  the estimator's output just past this chunk: at
+ *                         t = T for the reverse estimators (GAE, TD(lambda),
+ *                         discounted returns, V-trace, Retrace -- the first
+ *                         step of the chunk that follows, which is therefore
+ *                         processed first), at t = -1 for the forward ones
+ *                         (traces, prefix sum -- the last step of the chunk
+ *                         before).  V-trace takes vs_T.
+ *                         With carry_in, the chunk's edge step (t = T-1,
+ *                         resp. t = 0) is not an episode end: it continues
+ *                         into the carry unless it is terminated, truncated
+ *                         or done.  V at t = T is bootstrap_value[n] (NULL:
+ *                         0).  NULL carry_in: each row is a whole rollout,
+ *                         exactly as the plain call.
+ *   carry_out [N] or NULL the output at the opposite edge (t = 0 reverse,
+ *                         t = T-1 forward; V-trace: vs), i.e. the carry_in of
+ *                         the call for the neighbouring chunk.
+ * Retrace with carry_in also needs next_actions [N] (a_T, int32) and
+ * next_behaviour_probs [N] (mu(a_T | x_T)) of the chunk that follows
+ * (RLSCAN_ERR_NULL if missing).  Layout, ownership, streams and errors are as
+ * for the plain calls; carry_out must not alias any other argument.  Calls
+ * with carry arguments run kernels built for them (four waves per
+ * workgroup); the plain calls are unaffected. */
+int rlscan_gae_carry(const float* rewards, const float* values, const float* bootstrap_value,
+                     const float* terminated, const float* truncated,
+                     const float* bootstrap_values, const float* carry_in, float* advantages,
+                     float* carry_out, int64_t N, int64_t T, float gamma, float lambda,
+                     hipStream_t stream);
+int rlscan_lambda_returns_carry(const float* rewards, const float* values,
+                                const float* bootstrap_value, const float* terminated,
+                                const float* truncated, const float* bootstrap_values,
+                                const float* carry_in, float* returns, float* carry_out,
+                                int64_t N, int64_t T, float gamma, float lambda,
+                                hipStream_t stream);
+int rlscan_discounted_returns_carry(const float* rewards, const float* bootstrap_value,
+                                    const float* terminated, const float* truncated,
+                                    const float* bootstrap_values, const float* carry_in,
+                                    float* returns, float* carry_out, int64_t N, int64_t T,
+                                    float gamma, hipStream_t stream);
+int rlscan_vtrace_carry(const float* rewards, const float* values, const float* bootstrap_value,
+                        const float* log_rhos, const float* terminated, const float* truncated,
+                        const float* bootstrap_values, const float* carry_in, float* vs,
+                        float* pg_advantages, float* carry_out, int64_t N, int64_t T,
+                        float gamma, float rho_bar, float c_bar, hipStream_t stream);
+int rlscan_retrace_carry(const float* rewards, const float* next_q_values_all,
+                         const float* next_target_probs, const int32_t* actions,
+                         const float* behaviour_probs, const float* terminated,
+                         const float* truncated, const float* carry_in,
+                         const int32_t* next_actions, const float* next_behaviour_probs,
+                         float* targets, float* carry_out, int64_t N, int64_t T, int64_t A,
+                         float gamma, float lambda, hipStream_t stream);
+int rlscan_eligibility_traces_carry(const float* x, const float* dones, const float* carry_in,
+                                    float* traces, float* carry_out, int64_t N, int64_t T,
+                                    float gamma, float lambda, hipStream_t stream);
+int rlscan_episodic_prefix_sum_carry(const int32_t* x, const float* dones,
+                                     const int64_t* carry_in, int64_t* out,
+                                     int64_t* carry_out, int64_t N, int64_t T,
+                                     hipStream_t stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* rlscan_status_string(int status);
 

@@ -6,22 +6,38 @@
 //   kReverse          true for reverse-time estimators (x_t depends on x_{t+1})
 //   Params            device pointers and scalars of one call
 //   Chunk             registers holding one lane's 4-element chunk
-//   load<VEC,FULL>    read the chunk's inputs (plus the one-element halo just
+//   load<VEC,FULL,CARRY>  read the chunk's inputs (plus the one-element halo just
 //                     above the chunk where the step needs values at t+1);
 //                     `stage` is the wave's LDS staging area, kStageFloats
 //                     floats (0 for estimators that do not stage)
 //   Epi               values the epilogue needs besides the states (kept
 //                     apart from Chunk: the raw inputs are dead once the
 //                     steps are built, only these stay live until the store)
-//   steps(...)        build the chunk's steps, in memory order, and its Epi
+//   steps<CARRY>(...)  build the chunk's steps, in memory order, and its Epi
+//                     (CARRY: kernels built for the carry arguments; without
+//                     it every carry branch is compiled out)
 //   store<VEC,FULL>   write outputs from the states after each element (x)
 //                     and before it (before: x_{t+1} for reverse estimators)
+//   edge_value        the output written to carry_out for element j
 //
 // Shared conventions: row-major [N, T]; a flag is set iff != 0; for reverse
 // estimators step t cuts the chain if terminated, truncated or t = T-1, and
 // the successor value seen from step t is 0 (terminated, which wins), the
 // per-step bootstrap value (truncated), the per-row bootstrap value (t = T-1)
-// or V_{t+1}.  Sources are cited per estimator: the rl-triton README,
+// or V_{t+1}.
+//
+// Carry (streaming one rollout through several calls; the chunked fallback
+// of the rl-triton README, Kernels table, last column): every Params has
+// carry_in [N] (NULL: each row is a whole rollout) and carry_out [N] (NULL:
+// not written).  carry_in[n] is the output just past the chunk -- t = T for
+// reverse estimators, t = -1 for forward ones -- and the chunk's edge step
+// (t = T-1, resp. t = 0) continues into it unless terminated, truncated or
+// done there.  The carry is a known value, so the edge step (a, b) applied
+// to it is folded into the cut step (0, b + a*carry): the scan keeps its
+// row-edge cuts and nothing else changes.  carry_out[n] is the output at
+// the opposite edge (t = 0 reverse, t = T-1 forward).
+//
+// Sources are cited per estimator: the rl-triton README,
 // section "Kernels" (one row per estimator) and section "Performance"
 // (truncation/bootstrap inputs), and the estimators' published definitions.
 #pragma once
@@ -152,17 +168,21 @@ struct NoEpi {};
 // the bootstrap value of the row its first element lies in.
 struct EpisodeChunk {
     float r[4], term[4], trunc[4], bv[4];
-    float boot;
+    float boot;   // V at t = T of the chunk's first row
+    float carry;  // carry_in of the chunk's first row
 };
 
-template <bool VEC, bool FULL, bool TRUNC>
+template <bool VEC, bool FULL, bool TRUNC, bool CARRY>
 __device__ __forceinline__ void load_episode(const float* rewards, const float* terminated,
                                              const float* truncated,
                                              const float* bootstrap_values,
-                                             const float* bootstrap_value, const Geometry& geo,
+                                             const float* bootstrap_value,
+                                             const float* carry_in, const Geometry& geo,
                                              const ChunkPos& q, EpisodeChunk& c) {
     // loaded with the chunk so that the row-end case costs no dependent load
-    c.boot = bootstrap_value != nullptr ? bootstrap_value[q.n0 < geo.N ? q.n0 : geo.N - 1] : 0.0f;
+    const int64_t nr = q.n0 < geo.N ? q.n0 : geo.N - 1;
+    c.boot = bootstrap_value != nullptr ? bootstrap_value[nr] : 0.0f;
+    c.carry = (CARRY && carry_in != nullptr) ? carry_in[nr] : 0.0f;
     load4<VEC, FULL>(rewards, q, c.r);
     load4<VEC, FULL>(terminated, q, c.term);
     if constexpr (TRUNC) {
@@ -177,13 +197,16 @@ __device__ __forceinline__ void load_episode(const float* rewards, const float* 
 // Successor value for a chain cut (terminated > truncated > row end), and
 // whether the step is a cut.  `v_next` is V_{t+1}, used when it is not a cut.
 // A chunk holds at most one row end unless T < 4; only then can a row end
-// belong to a later row than the chunk's first element.
+// belong to a later row than the chunk's first element.  `continues`: a
+// carry_in was given, so a row end is not a cut by itself (its successor
+// value is still V at t = T).
 __device__ __forceinline__ float successor_value(const EpisodeChunk& c, int j, bool row_end,
                                                  bool in_range, const float* bootstrap_value,
-                                                 int64_t n, int64_t n0, float v_next, bool& cut) {
+                                                 int64_t n, int64_t n0, float v_next,
+                                                 bool continues, bool& cut) {
     const bool term = c.term[j] != 0.0f;
     const bool trunc = c.trunc[j] != 0.0f;
-    cut = term || trunc || row_end;
+    cut = term || trunc || (row_end && !continues);
     float v = v_next;
     if (row_end) v = c.boot;
     if (row_end && in_range && n != n0 && bootstrap_value != nullptr) v = bootstrap_value[n];
@@ -192,14 +215,27 @@ __device__ __forceinline__ float successor_value(const EpisodeChunk& c, int j, b
     return v;
 }
 
+// carry_in of row n, for an element of a chunk whose first row is n0 (the
+// first row's value is preloaded with the chunk).
+__device__ __forceinline__ float row_carry(const EpisodeChunk& c, const float* carry_in,
+                                           int64_t n, int64_t n0) {
+    return n == n0 ? c.carry : carry_in[n];
+}
+
+// The edge step (a, b) applied to the known carry, as a cut step.
+__device__ __forceinline__ void fold_carry(StepF& e, float carry) {
+    e.b = fmaf(e.a, carry, e.b);
+    e.a = 0.0f;
+}
+
 // ------------------------------------------------------------------ GAE
 // README, Kernels table, compute_gae row (backward scan of TD errors with
 // weight gamma*lambda); Schulman et al. 2016.
 //   a_t = cut ? 0 : gamma*lambda,   b_t = r_t + gamma*Vhat_{t+1} - V_t
 struct GaeParams {
     const float *rewards, *values, *bootstrap_value, *terminated, *truncated,
-        *bootstrap_values;
-    float* out;
+        *bootstrap_values, *carry_in;
+    float *out, *carry_out;
     float gamma, gamma_lambda;
 };
 
@@ -217,27 +253,36 @@ struct Gae {
         float v[4];
         float v_halo;
     };
-    template <bool VEC, bool FULL>
+    template <bool VEC, bool FULL, bool CARRY>
     __device__ __forceinline__ static void load(const Params& p, const Geometry& geo,
                                                 const ChunkPos& q, Chunk& c, lds_float*) {
-        load_episode<VEC, FULL, kTrunc>(p.rewards, p.terminated, p.truncated,
-                                        p.bootstrap_values, p.bootstrap_value, geo, q, c.ep);
+        load_episode<VEC, FULL, kTrunc, CARRY>(p.rewards, p.terminated, p.truncated,
+                                        p.bootstrap_values, p.bootstrap_value, p.carry_in, geo,
+                                        q, c.ep);
         load4<VEC, FULL>(p.values, q, c.v);
         c.v_halo = load_halo(p.values, q, geo.NT);
     }
+    template <bool CARRY>
     __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
                                  const Chunk& c, S e[4], Epi&) {
         int64_t n = q.n0, t = q.t0;
+const bool continues = CARRY && p.carry_in != nullptr;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             bool cut;
+            const bool row_end = t == geo.T - 1;
             const float v_next = j < kChunk - 1 ? c.v[j + 1] : c.v_halo;
-            const float vh = successor_value(c.ep, j, t == geo.T - 1, j < q.valid,
-                                             p.bootstrap_value, n, q.n0, v_next, cut);
+            const float vh = successor_value(c.ep, j, row_end, j < q.valid,
+                                             p.bootstrap_value, n, q.n0, v_next, continues, cut);
             e[j].a = cut ? 0.0f : p.gamma_lambda;
             e[j].b = fmaf(p.gamma, vh, c.ep.r[j]) - c.v[j];
+            if (row_end && continues && !cut && j < q.valid)
+                fold_carry(e[j], row_carry(c.ep, p.carry_in, n, q.n0));  // A_T
             next_position(n, t, geo.T);
         }
+    }
+    __device__ __forceinline__ static V edge_value(const Epi&, const V x[4], int j) {
+        return x[j];
     }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
@@ -252,8 +297,8 @@ struct Gae {
 //   b_t = cut ? r_t + gamma*Vhat_{t+1} : r_t + gamma*(1-lambda)*V_{t+1}
 struct LambdaReturnsParams {
     const float *rewards, *values, *bootstrap_value, *terminated, *truncated,
-        *bootstrap_values;
-    float* out;
+        *bootstrap_values, *carry_in;
+    float *out, *carry_out;
     float gamma, gamma_lambda, gamma_one_minus_lambda;
 };
 
@@ -267,28 +312,39 @@ struct LambdaReturns {
     static constexpr int kStageFloats = 0;
     static constexpr int kOutStageFloats = 0;
     using Chunk = typename Gae<kTrunc>::Chunk;
-    template <bool VEC, bool FULL>
+    template <bool VEC, bool FULL, bool CARRY>
     __device__ __forceinline__ static void load(const Params& p, const Geometry& geo,
                                                 const ChunkPos& q, Chunk& c, lds_float*) {
-        load_episode<VEC, FULL, kTrunc>(p.rewards, p.terminated, p.truncated,
-                                        p.bootstrap_values, p.bootstrap_value, geo, q, c.ep);
+        load_episode<VEC, FULL, kTrunc, CARRY>(p.rewards, p.terminated, p.truncated,
+                                        p.bootstrap_values, p.bootstrap_value, p.carry_in, geo,
+                                        q, c.ep);
         load4<VEC, FULL>(p.values, q, c.v);
         c.v_halo = load_halo(p.values, q, geo.NT);
     }
+    template <bool CARRY>
     __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
                                  const Chunk& c, S e[4], Epi&) {
         int64_t n = q.n0, t = q.t0;
+const bool continues = CARRY && p.carry_in != nullptr;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             bool cut;
+            const bool row_end = t == geo.T - 1;
             const float v_next = j < kChunk - 1 ? c.v[j + 1] : c.v_halo;
-            const float vh = successor_value(c.ep, j, t == geo.T - 1, j < q.valid,
-                                             p.bootstrap_value, n, q.n0, v_next, cut);
+            // vh is V_{t+1} on a step that is not a cut (V at t = T at a
+            // continued row end)
+            const float vh = successor_value(c.ep, j, row_end, j < q.valid,
+                                             p.bootstrap_value, n, q.n0, v_next, continues, cut);
             e[j].a = cut ? 0.0f : p.gamma_lambda;
             e[j].b = cut ? fmaf(p.gamma, vh, c.ep.r[j])
-                         : fmaf(p.gamma_one_minus_lambda, v_next, c.ep.r[j]);
+                         : fmaf(p.gamma_one_minus_lambda, vh, c.ep.r[j]);
+            if (row_end && continues && !cut && j < q.valid)
+                fold_carry(e[j], row_carry(c.ep, p.carry_in, n, q.n0));  // G_T
             next_position(n, t, geo.T);
         }
+    }
+    __device__ __forceinline__ static V edge_value(const Epi&, const V x[4], int j) {
+        return x[j];
     }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
@@ -301,8 +357,9 @@ struct LambdaReturns {
 // README, Kernels table, compute_discounted_returns row (reward-to-go).
 //   a_t = cut ? 0 : gamma,   b_t = cut ? r_t + gamma*Vhat_{t+1} : r_t
 struct DiscountedParams {
-    const float *rewards, *bootstrap_value, *terminated, *truncated, *bootstrap_values;
-    float* out;
+    const float *rewards, *bootstrap_value, *terminated, *truncated, *bootstrap_values,
+        *carry_in;
+    float *out, *carry_out;
     float gamma;
 };
 
@@ -318,24 +375,33 @@ struct Discounted {
     struct Chunk {
         EpisodeChunk ep;
     };
-    template <bool VEC, bool FULL>
+    template <bool VEC, bool FULL, bool CARRY>
     __device__ __forceinline__ static void load(const Params& p, const Geometry& geo,
                                                 const ChunkPos& q, Chunk& c, lds_float*) {
-        load_episode<VEC, FULL, kTrunc>(p.rewards, p.terminated, p.truncated,
-                                        p.bootstrap_values, p.bootstrap_value, geo, q, c.ep);
+        load_episode<VEC, FULL, kTrunc, CARRY>(p.rewards, p.terminated, p.truncated,
+                                        p.bootstrap_values, p.bootstrap_value, p.carry_in, geo,
+                                        q, c.ep);
     }
+    template <bool CARRY>
     __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
                                  const Chunk& c, S e[4], Epi&) {
         int64_t n = q.n0, t = q.t0;
+const bool continues = CARRY && p.carry_in != nullptr;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             bool cut;
-            const float vh = successor_value(c.ep, j, t == geo.T - 1, j < q.valid,
-                                             p.bootstrap_value, n, q.n0, 0.0f, cut);
+            const bool row_end = t == geo.T - 1;
+            const float vh = successor_value(c.ep, j, row_end, j < q.valid,
+                                             p.bootstrap_value, n, q.n0, 0.0f, continues, cut);
             e[j].a = cut ? 0.0f : p.gamma;
             e[j].b = cut ? fmaf(p.gamma, vh, c.ep.r[j]) : c.ep.r[j];
+            if (row_end && continues && !cut && j < q.valid)
+                fold_carry(e[j], row_carry(c.ep, p.carry_in, n, q.n0));  // G_T
             next_position(n, t, geo.T);
         }
+    }
+    __device__ __forceinline__ static V edge_value(const Epi&, const V x[4], int j) {
+        return x[j];
     }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
@@ -353,8 +419,8 @@ struct Discounted {
 // which equals rho_t*(r_t + gamma*(cut ? Vhat_{t+1} : vs_{t+1}) - V_t).
 struct VtraceParams {
     const float *rewards, *values, *bootstrap_value, *log_rhos, *terminated, *truncated,
-        *bootstrap_values;
-    float *vs, *pg;
+        *bootstrap_values, *carry_in;  // carry_in: vs at t = T
+    float *vs, *pg, *carry_out;       // carry_out: vs at t = 0
     float gamma, rho_bar, c_bar;
 };
 
@@ -377,24 +443,28 @@ struct Vtrace {
     };
     static constexpr int kStageFloats = 0;
     static constexpr int kOutStageFloats = 0;
-    template <bool VEC, bool FULL>
+    template <bool VEC, bool FULL, bool CARRY>
     __device__ __forceinline__ static void load(const Params& p, const Geometry& geo,
                                                 const ChunkPos& q, Chunk& c, lds_float*) {
-        load_episode<VEC, FULL, kTrunc>(p.rewards, p.terminated, p.truncated,
-                                        p.bootstrap_values, p.bootstrap_value, geo, q, c.ep);
+        load_episode<VEC, FULL, kTrunc, CARRY>(p.rewards, p.terminated, p.truncated,
+                                        p.bootstrap_values, p.bootstrap_value, p.carry_in, geo,
+                                        q, c.ep);
         load4<VEC, FULL>(p.values, q, c.v);
         load4<VEC, FULL>(p.log_rhos, q, c.lr);
         c.v_halo = load_halo(p.values, q, geo.NT);
     }
+    template <bool CARRY>
     __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
                                  const Chunk& c, S e[4], Epi& epi) {
         int64_t n = q.n0, t = q.t0;
+const bool continues = CARRY && p.carry_in != nullptr;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             bool cut;
+            const bool row_end = t == geo.T - 1;
             const float v_next = j < kChunk - 1 ? c.v[j + 1] : c.v_halo;
-            const float vh = successor_value(c.ep, j, t == geo.T - 1, j < q.valid,
-                                             p.bootstrap_value, n, q.n0, v_next, cut);
+            const float vh = successor_value(c.ep, j, row_end, j < q.valid,
+                                             p.bootstrap_value, n, q.n0, v_next, continues, cut);
             const float ratio = expf(c.lr[j]);
             const float rho = fminf(p.rho_bar, ratio);
             const float cc = fminf(p.c_bar, ratio);
@@ -404,8 +474,20 @@ struct Vtrace {
             epi.gamma_rho[j] = cut ? 0.0f : p.gamma * rho;
             e[j].a = cut ? 0.0f : p.gamma * cc;
             e[j].b = delta;
+            if (row_end && continues && !cut && j < q.valid) {
+                // u at t = T is vs_T - V_T; the state before this element is
+                // not in the scan, so pg takes it here
+                const float u_T = row_carry(c.ep, p.carry_in, n, q.n0) - vh;
+                fold_carry(e[j], u_T);
+                epi.delta[j] = fmaf(epi.gamma_rho[j], u_T, delta);
+                epi.gamma_rho[j] = 0.0f;
+            }
             next_position(n, t, geo.T);
         }
+    }
+    // carry_out of V-trace is vs, like its carry_in
+    __device__ __forceinline__ static V edge_value(const Epi& c, const V x[4], int j) {
+        return c.v[j] + x[j];
     }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi& c,
@@ -450,6 +532,11 @@ struct Retrace {
         float* out;
         int64_t A;
         float gamma, lambda;
+        // carry: G at t = T, and a_T, mu(a_T | x_T) of the chunk that follows
+        const float* carry_in;
+        const int32_t* next_actions;
+        const float* next_mu;
+        float* carry_out;
     };
     static constexpr int kRegA = kA > 0 ? kA : 1;
     struct Chunk {
@@ -463,7 +550,7 @@ struct Retrace {
                                // +kWave*kChunk*kA) when `staged`
         bool staged;           // (LDS address 0 is valid: no null sentinel)
     };
-    template <bool VEC, bool FULL>
+    template <bool VEC, bool FULL, bool CARRY>
     __device__ __forceinline__ static void load(const Params& p, const Geometry& geo,
                                                 const ChunkPos& q, Chunk& c, lds_float* stage) {
         load4<VEC, FULL>(p.rewards, q, c.ep.r);
@@ -472,6 +559,7 @@ struct Retrace {
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) c.ep.bv[j] = 0.0f;
         c.ep.boot = 0.0f;
+        c.ep.carry = 0.0f;
         load4<VEC, FULL>(p.actions, q, c.act);
         load4<VEC, FULL>(p.behaviour_probs, q, c.mu);
         // a_{t+1} and mu_{t+1} of the chunk's top element: element 0 of the
@@ -527,6 +615,7 @@ struct Retrace {
             }
         }
     }
+    template <bool CARRY>
     __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
                                  const Chunk& c, S e[4], Epi&) {
         // action values: registers, or the LDS staging area (16-byte reads)
@@ -558,13 +647,20 @@ struct Retrace {
                 }
             }
         }
-        int64_t t = q.t0;
+        const bool continues = CARRY && p.carry_in != nullptr;
+        int64_t n = q.n0, t = q.t0;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             const bool term = c.ep.term[j] != 0.0f;
-            const bool cut = term || c.ep.trunc[j] != 0.0f || t == geo.T - 1;
+            const bool row_end = t == geo.T - 1;
+            const bool cut = term || c.ep.trunc[j] != 0.0f || (row_end && !continues);
+            const bool edge = row_end && continues && !cut && j < q.valid;
             int32_t a_next = j < kChunk - 1 ? c.act[j + 1] : c.act_halo;
-            const float mu_next = j < kChunk - 1 ? c.mu[j + 1] : c.mu_halo;
+            float mu_next = j < kChunk - 1 ? c.mu[j + 1] : c.mu_halo;
+            if (edge) {  // the next step lies in the chunk that follows
+                a_next = p.next_actions[n];
+                mu_next = p.next_mu[n];
+            }
             float eq = 0.0f, q_sel = 0.0f, pi_sel = 0.0f;
             if constexpr (kA > 0) {
                 a_next = a_next < 0 ? 0 : (a_next >= kA ? kA - 1 : a_next);
@@ -590,8 +686,12 @@ struct Retrace {
             e[j].a = cut ? 0.0f : p.gamma * cprime;
             e[j].b = cut ? (term ? c.ep.r[j] : fmaf(p.gamma, eq, c.ep.r[j]))
                          : fmaf(p.gamma, fmaf(-cprime, q_sel, eq), c.ep.r[j]);
-            if (++t == geo.T) t = 0;
+            if (edge) fold_carry(e[j], p.carry_in[n]);  // G_T
+            next_position(n, t, geo.T);
         }
+    }
+    __device__ __forceinline__ static V edge_value(const Epi&, const V x[4], int j) {
+        return x[j];
     }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
@@ -599,6 +699,13 @@ struct Retrace {
         store4<VEC, FULL>(p.out, q, x);
     }
 };
+
+// Row of the first row start (t = 0) at or after a forward chunk's first
+// element, clamped to a valid row (its carry is then simply unused).
+__device__ __forceinline__ int64_t first_start_row(const ChunkPos& q, const Geometry& geo) {
+    const int64_t n = q.t0 == 0 ? q.n0 : q.n0 + 1;
+    return n < geo.N ? n : geo.N - 1;
+}
 
 // ------------------------------------------------------- eligibility traces
 // README, Kernels table, compute_eligibility_traces row: forward traces, the
@@ -615,25 +722,38 @@ struct Eligibility {
         const float *x, *dones;
         float* out;
         float gamma_lambda;
+        const float* carry_in;  // e at t = -1
+        float* carry_out;       // e at t = T-1
     };
     struct Chunk {
         float x[4], d[4];
+        float carry;  // carry_in of the first row that starts in the chunk
     };
-    template <bool VEC, bool FULL>
-    __device__ __forceinline__ static void load(const Params& p, const Geometry&,
+    template <bool VEC, bool FULL, bool CARRY>
+    __device__ __forceinline__ static void load(const Params& p, const Geometry& geo,
                                                 const ChunkPos& q, Chunk& c, lds_float*) {
         load4<VEC, FULL>(p.x, q, c.x);
         load4<VEC, FULL>(p.dones, q, c.d);
+        c.carry = (CARRY && p.carry_in != nullptr) ? p.carry_in[first_start_row(q, geo)] : 0.0f;
     }
+    template <bool CARRY>
     __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
                                  const Chunk& c, S e[4], Epi&) {
-        int64_t t = q.t0;
+        const bool continues = CARRY && p.carry_in != nullptr;
+        const int64_t n_first = first_start_row(q, geo);
+        int64_t n = q.n0, t = q.t0;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
-            e[j].a = (c.d[j] != 0.0f || t == 0) ? 0.0f : p.gamma_lambda;
+            const float a_live = c.d[j] != 0.0f ? 0.0f : p.gamma_lambda;
+            e[j].a = t == 0 ? 0.0f : a_live;
             e[j].b = c.x[j];
-            if (++t == geo.T) t = 0;
+            if (t == 0 && continues && j < q.valid)  // e_{-1} from the previous chunk
+                e[j].b = fmaf(a_live, n == n_first ? c.carry : p.carry_in[n], c.x[j]);
+            next_position(n, t, geo.T);
         }
+    }
+    __device__ __forceinline__ static V edge_value(const Epi&, const V x[4], int j) {
+        return x[j];
     }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
@@ -658,25 +778,35 @@ struct PrefixSum {
         const int32_t* x;
         const float* dones;
         int64_t* out;
+        const int64_t* carry_in;  // y at t = -1
+        int64_t* carry_out;       // y at t = T-1
     };
     struct Chunk {
         int32_t x[4];
         float d[4];
+        int64_t carry;  // carry_in of the first row that starts in the chunk
     };
-    template <bool VEC, bool FULL>
-    __device__ __forceinline__ static void load(const Params& p, const Geometry&,
+    template <bool VEC, bool FULL, bool CARRY>
+    __device__ __forceinline__ static void load(const Params& p, const Geometry& geo,
                                                 const ChunkPos& q, Chunk& c, lds_float*) {
         load4<VEC, FULL>(p.x, q, c.x);
         load4<VEC, FULL>(p.dones, q, c.d);
+        c.carry = (CARRY && p.carry_in != nullptr) ? p.carry_in[first_start_row(q, geo)] : 0;
     }
-    __device__ __forceinline__ static void steps(const Params&, const Geometry& geo, const ChunkPos& q,
-                                                 const Chunk& c, S e[4], Epi&) {
-        int64_t t = q.t0;
+    template <bool CARRY>
+    __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo,
+                                                 const ChunkPos& q, const Chunk& c, S e[4], Epi&) {
+        const bool continues = CARRY && p.carry_in != nullptr;
+        const int64_t n_first = first_start_row(q, geo);
+        int64_t n = q.n0, t = q.t0;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
-            e[j].a = (c.d[j] != 0.0f || t == 0) ? 0u : 1u;
+            const bool done = c.d[j] != 0.0f;
+            e[j].a = (done || t == 0) ? 0u : 1u;
             e[j].b = static_cast<int64_t>(c.x[j]);
-            if (++t == geo.T) t = 0;
+            if (t == 0 && continues && !done && j < q.valid)  // y_{-1} from the previous chunk
+                e[j].b += n == n_first ? c.carry : p.carry_in[n];
+            next_position(n, t, geo.T);
         }
     }
     // A lane's four int64 results are 32 contiguous bytes.  Stored directly,
@@ -686,6 +816,9 @@ struct PrefixSum {
     // (measured: 1.19x the output bytes).  So a full wave first transposes
     // its 2 KiB through LDS; each store instruction then writes one
     // contiguous KiB: lane i stores bytes [16i, 16i+16) of each half.
+    __device__ __forceinline__ static V edge_value(const Epi&, const V x[4], int j) {
+        return x[j];
+    }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
                                                  const V x[4], const V[4], lds_float* ostage) {

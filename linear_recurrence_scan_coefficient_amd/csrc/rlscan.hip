@@ -76,7 +76,7 @@ __device__ __forceinline__ bool tile_is_full(const Geometry& geo, uint64_t tile)
 }
 
 // 1. loads, all rounds first so every load of the tile is in flight
-template <class E, int R, int W, bool VEC, bool FULL>
+template <class E, int R, int W, bool VEC, bool FULL, bool CARRY>
 __device__ __forceinline__ void load_tile(const typename E::Params& p, const Geometry& geo,
                                           uint64_t tile, typename E::Chunk (&ch)[R],
                                           ChunkPos (&pos)[R], lds_float* stage) {
@@ -85,13 +85,13 @@ __device__ __forceinline__ void load_tile(const typename E::Params& p, const Geo
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         pos[r] = chunk_pos(chunk_base<E, R, W>(geo, tile, wave, r, lane), geo);
-        E::template load<VEC, FULL>(p, geo, pos[r], ch[r],
+        E::template load<VEC, FULL, CARRY>(p, geo, pos[r], ch[r],
                                     stage + (wave * R + r) * E::kStageFloats);
     }
 }
 
 // 2. steps in scan order; elements past N*T become the identity
-template <class E, int R, bool FULL>
+template <class E, int R, bool FULL, bool CARRY>
 __device__ __forceinline__ void build_steps(const typename E::Params& p, const Geometry& geo,
                                             const typename E::Chunk (&ch)[R],
                                             const ChunkPos (&pos)[R],
@@ -101,7 +101,7 @@ __device__ __forceinline__ void build_steps(const typename E::Params& p, const G
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         S em[kChunk];
-        E::steps(p, geo, pos[r], ch[r], em, epi[r]);
+        E::template steps<CARRY>(p, geo, pos[r], ch[r], em, epi[r]);
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             const S s = (FULL || j < pos[r].valid) ? em[j] : identity_step(S{});
@@ -164,7 +164,7 @@ __device__ __forceinline__ void tile_carry(const LookbackArgs& lb, uint64_t tile
 }
 
 // 6. replay each lane's steps from its entering state and store
-template <class E, int R, int W, bool VEC, bool FULL, class A>
+template <class E, int R, int W, bool VEC, bool FULL, bool CARRY, class A>
 __device__ __forceinline__ void replay_store(const typename E::Params& p, const Geometry& geo,
                                              uint64_t tile,
                                              const typename E::S (&e)[R][kChunk],
@@ -194,10 +194,22 @@ __device__ __forceinline__ void replay_store(const typename E::Params& p, const 
         q.valid = rem <= 0 ? 0 : (rem >= kChunk ? kChunk : static_cast<int>(rem));
         E::template store<VEC, FULL>(p, q, epi[r], out, before,
                                      ostage + wave * E::kOutStageFloats);
+        if (CARRY && p.carry_out != nullptr) {
+            // the output at the row edge the next call continues from:
+            // t = 0 (reverse estimators) or t = T-1 (forward ones)
+            const ChunkPos qp = chunk_pos(q.g0, geo);
+            int64_t n = qp.n0, t = qp.t0;
+#pragma unroll
+            for (int j = 0; j < kChunk; ++j) {
+                if (j < q.valid && t == (E::kReverse ? 0 : geo.T - 1))
+                    p.carry_out[n] = E::edge_value(epi[r], out, j);
+                next_position(n, t, geo.T);
+            }
+        }
     }
 }
 
-template <class E, int R, int W, bool LOOKBACK, bool VEC, bool FULL>
+template <class E, int R, int W, bool LOOKBACK, bool VEC, bool FULL, bool CARRY>
 __device__ __forceinline__ void scan_tile(const typename E::Params& p, const Geometry& geo,
                                           const LookbackArgs& lb, uint64_t tile,
                                           typename AggOf<typename E::S>::type* sm_wave,
@@ -209,10 +221,10 @@ __device__ __forceinline__ void scan_tile(const typename E::Params& p, const Geo
     const int wave = threadIdx.x / kWave;
     typename E::Chunk ch[R];
     ChunkPos pos[R];
-    load_tile<E, R, W, VEC, FULL>(p, geo, tile, ch, pos, stage);
+    load_tile<E, R, W, VEC, FULL, CARRY>(p, geo, tile, ch, pos, stage);
     S e[R][kChunk];
     typename E::Epi epi[R];
-    build_steps<E, R, FULL>(p, geo, ch, pos, e, epi);
+    build_steps<E, R, FULL, CARRY>(p, geo, ch, pos, e, epi);
     A incl[R];
     const A wtot = scan_wave<R>(e, incl);
     if (lane == 0) sm_wave[wave] = wtot;
@@ -223,11 +235,12 @@ __device__ __forceinline__ void scan_tile(const typename E::Params& p, const Geo
         if (w < wave) wpre = compose(sm_wave[w], wpre);
     tile_carry<E, W, LOOKBACK>(lb, tile, sm_wave, e[0][0], sm_carry);
     __syncthreads();
-    replay_store<E, R, W, VEC, FULL>(p, geo, tile, e, epi, incl, wpre, *sm_carry, ostage);
+    replay_store<E, R, W, VEC, FULL, CARRY>(p, geo, tile, e, epi, incl, wpre, *sm_carry,
+                                             ostage);
 }
 
 // One tile per workgroup (or, grid-capped, a loop over tiles).
-template <class E, int R, int W, bool LOOKBACK, bool VEC>
+template <class E, int R, int W, bool LOOKBACK, bool VEC, bool CARRY>
 __global__ __launch_bounds__(kWave * W) void scan_kernel(const typename E::Params p,
                                                         const Geometry geo,
                                                         const LookbackArgs lb) {
@@ -257,11 +270,11 @@ __global__ __launch_bounds__(kWave * W) void scan_kernel(const typename E::Param
         if (tile >= static_cast<uint64_t>(geo.num_tiles)) break;
         // only the tile holding the end of the data needs bounds checks
         if (tile_is_full<E, R, W>(geo, tile))
-            scan_tile<E, R, W, LOOKBACK, VEC, true>(p, geo, lb, tile, sm_wave, &sm_carry, stage,
-                                                    ostage);
+            scan_tile<E, R, W, LOOKBACK, VEC, true, CARRY>(p, geo, lb, tile, sm_wave, &sm_carry,
+                                                           stage, ostage);
         else
-            scan_tile<E, R, W, LOOKBACK, VEC, false>(p, geo, lb, tile, sm_wave, &sm_carry, stage,
-                                                     ostage);
+            scan_tile<E, R, W, LOOKBACK, VEC, false, CARRY>(p, geo, lb, tile, sm_wave, &sm_carry,
+                                                            stage, ostage);
         if (one_tile_per_group) break;
         if (!LOOKBACK || !lb.use_tickets) tile += gridDim.x;
         __syncthreads();  // LDS is reused by the next tile
@@ -390,9 +403,9 @@ int auto_waves(int est, int rounds) {
 }
 
 // `vec`: every pointer is 16-byte aligned.  Multi-round and eight-wave
-// kernels exist only for the vectorised path, and Retrace always runs one
-// round of four waves.
-Plan make_plan(int est, int64_t N, int64_t T, bool vec) {
+// kernels exist only for the vectorised path, Retrace always runs one round
+// of four waves, and calls with carry arguments (`carry`) four waves.
+Plan make_plan(int est, int64_t N, int64_t T, bool vec, bool carry = false) {
     const int64_t NT = N * T;
     Plan pl;
     const int ro = g_override.rounds.load();
@@ -400,7 +413,7 @@ Plan make_plan(int est, int64_t N, int64_t T, bool vec) {
     if (!vec || est == RLSCAN_EST_RETRACE) pl.rounds = 1;
     const int wo = g_override.waves.load();
     pl.waves = wo > 0 ? wo : auto_waves(est, pl.rounds);
-    if (!vec || est == RLSCAN_EST_RETRACE) pl.waves = 4;
+    if (!vec || carry || est == RLSCAN_EST_RETRACE) pl.waves = 4;
     pl.tile_elems = int64_t(kWave) * pl.waves * kChunk * pl.rounds;
     pl.tiles = (NT + pl.tile_elems - 1) / pl.tile_elems;
     const bool packed_ok = pl.tiles <= 1 || pl.tile_elems % T == 0;
@@ -427,8 +440,11 @@ int check_shape(int64_t N, int64_t T, int64_t A = 1) {
     return RLSCAN_OK;
 }
 
+// Outputs must not equal an input or each other; NULL (an optional output
+// not asked for) is skipped.
 int check_alias(std::initializer_list<const void*> outs, std::initializer_list<const void*> ins) {
     for (const void* o : outs) {
+        if (o == nullptr) continue;
         for (const void* i : ins)
             if (i != nullptr && i == o) return RLSCAN_ERR_ALIAS;
         int same = 0;
@@ -438,49 +454,61 @@ int check_alias(std::initializer_list<const void*> outs, std::initializer_list<c
     return RLSCAN_OK;
 }
 
-template <class E, int R, int W, bool VEC>
+template <class E, int R, int W, bool VEC, bool CARRY>
 hipError_t launch_r(const typename E::Params& p, const Geometry& geo, const LookbackArgs& lb,
                     const Plan& pl, hipStream_t stream) {
     const bool lookback = pl.mapping == RLSCAN_MAP_LOOKBACK;
     const dim3 grid(static_cast<unsigned>(geo.grid)), block(kWave * W);
     if (lookback)
-        hipLaunchKernelGGL((scan_kernel<E, R, W, true, VEC>), grid, block, 0, stream, p, geo, lb);
+        hipLaunchKernelGGL((scan_kernel<E, R, W, true, VEC, CARRY>), grid, block, 0, stream, p,
+                           geo, lb);
     else
-        hipLaunchKernelGGL((scan_kernel<E, R, W, false, VEC>), grid, block, 0, stream, p, geo, lb);
+        hipLaunchKernelGGL((scan_kernel<E, R, W, false, VEC, CARRY>), grid, block, 0, stream, p,
+                           geo, lb);
     return hipGetLastError();
 }
 
-template <class E, int W>
+template <class E, int W, bool CARRY>
 hipError_t launch_w(const typename E::Params& p, const Geometry& geo, const LookbackArgs& lb,
                     const Plan& pl, hipStream_t stream) {
     switch (pl.rounds) {
-        case 1: return launch_r<E, 1, W, true>(p, geo, lb, pl, stream);
-        case 2: return launch_r<E, 2, W, true>(p, geo, lb, pl, stream);
-        default: return launch_r<E, 4, W, true>(p, geo, lb, pl, stream);
+        case 1: return launch_r<E, 1, W, true, CARRY>(p, geo, lb, pl, stream);
+        case 2: return launch_r<E, 2, W, true, CARRY>(p, geo, lb, pl, stream);
+        default: return launch_r<E, 4, W, true, CARRY>(p, geo, lb, pl, stream);
     }
 }
 
+// Kernels built for the carry arguments exist with four waves only (the
+// plan forces it); all others come with four or eight.
 template <class E>
 hipError_t launch_kernel(const typename E::Params& p, const Geometry& geo, const LookbackArgs& lb,
-                         const Plan& pl, bool vec, hipStream_t stream) {
-    if (!vec) return launch_r<E, 1, 4, false>(p, geo, lb, pl, stream);
-    return pl.waves == 8 ? launch_w<E, 8>(p, geo, lb, pl, stream)
-                         : launch_w<E, 4>(p, geo, lb, pl, stream);
+                         const Plan& pl, bool vec, bool carry, hipStream_t stream) {
+    if (carry) {
+        if (!vec) return launch_r<E, 1, 4, false, true>(p, geo, lb, pl, stream);
+        return launch_w<E, 4, true>(p, geo, lb, pl, stream);
+    }
+    if (!vec) return launch_r<E, 1, 4, false, false>(p, geo, lb, pl, stream);
+    return pl.waves == 8 ? launch_w<E, 8, false>(p, geo, lb, pl, stream)
+                         : launch_w<E, 4, false>(p, geo, lb, pl, stream);
 }
 
 // Retrace keeps 2*4*A action values per round in LDS or registers: one
 // round of four waves only.
 template <class E>
 hipError_t launch_kernel_r1(const typename E::Params& p, const Geometry& geo,
-                            const LookbackArgs& lb, const Plan& pl, bool vec, hipStream_t stream) {
-    if (!vec) return launch_r<E, 1, 4, false>(p, geo, lb, pl, stream);
-    return launch_r<E, 1, 4, true>(p, geo, lb, pl, stream);
+                            const LookbackArgs& lb, const Plan& pl, bool vec, bool carry,
+                            hipStream_t stream) {
+    if (carry)
+        return vec ? launch_r<E, 1, 4, true, true>(p, geo, lb, pl, stream)
+                   : launch_r<E, 1, 4, false, true>(p, geo, lb, pl, stream);
+    return vec ? launch_r<E, 1, 4, true, false>(p, geo, lb, pl, stream)
+               : launch_r<E, 1, 4, false, false>(p, geo, lb, pl, stream);
 }
 
 // Plans, takes the look-back scratch if needed, and launches through `fn`.
 template <class Fn>
-int run(int est, int64_t N, int64_t T, bool vec, hipStream_t stream, Fn&& fn) {
-    const Plan pl = make_plan(est, N, T, vec);
+int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream, Fn&& fn) {
+    const Plan pl = make_plan(est, N, T, vec, carry);
     if (pl.rounds != 1 && pl.rounds != 2 && pl.rounds != 4) return RLSCAN_ERR_PARAM;
     if (pl.waves != 4 && pl.waves != 8) return RLSCAN_ERR_PARAM;
     Geometry geo;
@@ -544,27 +572,69 @@ using namespace rlscan;
 // ------------------------------------------------------------------ C ABI
 extern "C" {
 
-int rlscan_gae(const float* rewards, const float* values, const float* bootstrap_value,
-               const float* terminated, const float* truncated, const float* bootstrap_values,
-               float* advantages, int64_t N, int64_t T, float gamma, float lambda,
-               hipStream_t stream) {
+int rlscan_gae_carry(const float* rewards, const float* values, const float* bootstrap_value,
+                     const float* terminated, const float* truncated,
+                     const float* bootstrap_values, const float* carry_in, float* advantages,
+                     float* carry_out, int64_t N, int64_t T, float gamma, float lambda,
+                     hipStream_t stream) {
     int rc = check_shape(N, T);
     if (rc != RLSCAN_OK) return rc;
     if (!unit_interval(gamma) || !unit_interval(lambda)) return RLSCAN_ERR_PARAM;
     if (N == 0 || T == 0) return RLSCAN_OK;
     if (!rewards || !values || !terminated || !advantages) return RLSCAN_ERR_NULL;
     if (truncated && !bootstrap_values) return RLSCAN_ERR_NULL;
-    rc = check_alias({advantages},
-                     {rewards, values, bootstrap_value, terminated, truncated, bootstrap_values});
+    rc = check_alias({advantages, carry_out}, {rewards, values, bootstrap_value, terminated,
+                                               truncated, bootstrap_values, carry_in});
     if (rc != RLSCAN_OK) return rc;
-    const GaeParams p{rewards, values, bootstrap_value, terminated, truncated, bootstrap_values,
-                      advantages, gamma, gamma * lambda};
+    const GaeParams p{rewards,  values,     bootstrap_value, terminated, truncated,
+                      bootstrap_values, carry_in, advantages, carry_out, gamma,
+                      gamma * lambda};
     const bool vec = all_aligned({rewards, values, terminated, truncated, bootstrap_values,
                                   advantages});
-    return run(RLSCAN_EST_GAE, N, T, vec, stream,
+    const bool carry = carry_in != nullptr || carry_out != nullptr;
+    return run(RLSCAN_EST_GAE, N, T, vec, carry, stream,
                [&](const Geometry& g, const LookbackArgs& lb, const Plan& pl) {
-                   return truncated ? launch_kernel<Gae<true>>(p, g, lb, pl, vec, stream)
-                                    : launch_kernel<Gae<false>>(p, g, lb, pl, vec, stream);
+                   return truncated ? launch_kernel<Gae<true>>(p, g, lb, pl, vec, carry, stream)
+                                    : launch_kernel<Gae<false>>(p, g, lb, pl, vec, carry, stream);
+               });
+}
+
+int rlscan_gae(const float* rewards, const float* values, const float* bootstrap_value,
+               const float* terminated, const float* truncated, const float* bootstrap_values,
+               float* advantages, int64_t N, int64_t T, float gamma, float lambda,
+               hipStream_t stream) {
+    return rlscan_gae_carry(rewards, values, bootstrap_value, terminated, truncated,
+                            bootstrap_values, nullptr, advantages, nullptr, N, T, gamma, lambda,
+                            stream);
+}
+
+int rlscan_lambda_returns_carry(const float* rewards, const float* values,
+                                const float* bootstrap_value, const float* terminated,
+                                const float* truncated, const float* bootstrap_values,
+                                const float* carry_in, float* returns, float* carry_out,
+                                int64_t N, int64_t T, float gamma, float lambda,
+                                hipStream_t stream) {
+    int rc = check_shape(N, T);
+    if (rc != RLSCAN_OK) return rc;
+    if (!unit_interval(gamma) || !unit_interval(lambda)) return RLSCAN_ERR_PARAM;
+    if (N == 0 || T == 0) return RLSCAN_OK;
+    if (!rewards || !values || !terminated || !returns) return RLSCAN_ERR_NULL;
+    if (truncated && !bootstrap_values) return RLSCAN_ERR_NULL;
+    rc = check_alias({returns, carry_out}, {rewards, values, bootstrap_value, terminated,
+                                            truncated, bootstrap_values, carry_in});
+    if (rc != RLSCAN_OK) return rc;
+    const LambdaReturnsParams p{rewards,   values,   bootstrap_value, terminated,
+                                truncated, bootstrap_values, carry_in, returns,
+                                carry_out, gamma,    gamma * lambda,
+                                gamma * (1.0f - lambda)};
+    const bool vec = all_aligned({rewards, values, terminated, truncated, bootstrap_values,
+                                  returns});
+    const bool carry = carry_in != nullptr || carry_out != nullptr;
+    return run(RLSCAN_EST_LAMBDA_RETURNS, N, T, vec, carry, stream,
+               [&](const Geometry& g, const LookbackArgs& lb, const Plan& pl) {
+                   return truncated
+                              ? launch_kernel<LambdaReturns<true>>(p, g, lb, pl, vec, carry, stream)
+                              : launch_kernel<LambdaReturns<false>>(p, g, lb, pl, vec, carry, stream);
                });
 }
 
@@ -572,25 +642,34 @@ int rlscan_lambda_returns(const float* rewards, const float* values, const float
                           const float* terminated, const float* truncated,
                           const float* bootstrap_values, float* returns, int64_t N, int64_t T,
                           float gamma, float lambda, hipStream_t stream) {
+    return rlscan_lambda_returns_carry(rewards, values, bootstrap_value, terminated, truncated,
+                                       bootstrap_values, nullptr, returns, nullptr, N, T, gamma,
+                                       lambda, stream);
+}
+
+int rlscan_discounted_returns_carry(const float* rewards, const float* bootstrap_value,
+                                    const float* terminated, const float* truncated,
+                                    const float* bootstrap_values, const float* carry_in,
+                                    float* returns, float* carry_out, int64_t N, int64_t T,
+                                    float gamma, hipStream_t stream) {
     int rc = check_shape(N, T);
     if (rc != RLSCAN_OK) return rc;
-    if (!unit_interval(gamma) || !unit_interval(lambda)) return RLSCAN_ERR_PARAM;
+    if (!unit_interval(gamma)) return RLSCAN_ERR_PARAM;
     if (N == 0 || T == 0) return RLSCAN_OK;
-    if (!rewards || !values || !terminated || !returns) return RLSCAN_ERR_NULL;
+    if (!rewards || !terminated || !returns) return RLSCAN_ERR_NULL;
     if (truncated && !bootstrap_values) return RLSCAN_ERR_NULL;
-    rc = check_alias({returns},
-                     {rewards, values, bootstrap_value, terminated, truncated, bootstrap_values});
+    rc = check_alias({returns, carry_out}, {rewards, bootstrap_value, terminated, truncated,
+                                            bootstrap_values, carry_in});
     if (rc != RLSCAN_OK) return rc;
-    const LambdaReturnsParams p{rewards,   values,  bootstrap_value, terminated,
-                                truncated, bootstrap_values, returns, gamma,
-                                gamma * lambda, gamma * (1.0f - lambda)};
-    const bool vec = all_aligned({rewards, values, terminated, truncated, bootstrap_values,
-                                  returns});
-    return run(RLSCAN_EST_LAMBDA_RETURNS, N, T, vec, stream,
+    const DiscountedParams p{rewards, bootstrap_value, terminated, truncated, bootstrap_values,
+                             carry_in, returns, carry_out, gamma};
+    const bool vec = all_aligned({rewards, terminated, truncated, bootstrap_values, returns});
+    const bool carry = carry_in != nullptr || carry_out != nullptr;
+    return run(RLSCAN_EST_DISCOUNTED, N, T, vec, carry, stream,
                [&](const Geometry& g, const LookbackArgs& lb, const Plan& pl) {
                    return truncated
-                              ? launch_kernel<LambdaReturns<true>>(p, g, lb, pl, vec, stream)
-                              : launch_kernel<LambdaReturns<false>>(p, g, lb, pl, vec, stream);
+                              ? launch_kernel<Discounted<true>>(p, g, lb, pl, vec, carry, stream)
+                              : launch_kernel<Discounted<false>>(p, g, lb, pl, vec, carry, stream);
                });
 }
 
@@ -598,29 +677,16 @@ int rlscan_discounted_returns(const float* rewards, const float* bootstrap_value
                               const float* terminated, const float* truncated,
                               const float* bootstrap_values, float* returns, int64_t N,
                               int64_t T, float gamma, hipStream_t stream) {
-    int rc = check_shape(N, T);
-    if (rc != RLSCAN_OK) return rc;
-    if (!unit_interval(gamma)) return RLSCAN_ERR_PARAM;
-    if (N == 0 || T == 0) return RLSCAN_OK;
-    if (!rewards || !terminated || !returns) return RLSCAN_ERR_NULL;
-    if (truncated && !bootstrap_values) return RLSCAN_ERR_NULL;
-    rc = check_alias({returns}, {rewards, bootstrap_value, terminated, truncated, bootstrap_values});
-    if (rc != RLSCAN_OK) return rc;
-    const DiscountedParams p{rewards, bootstrap_value, terminated, truncated, bootstrap_values,
-                             returns, gamma};
-    const bool vec = all_aligned({rewards, terminated, truncated, bootstrap_values, returns});
-    return run(RLSCAN_EST_DISCOUNTED, N, T, vec, stream,
-               [&](const Geometry& g, const LookbackArgs& lb, const Plan& pl) {
-                   return truncated
-                              ? launch_kernel<Discounted<true>>(p, g, lb, pl, vec, stream)
-                              : launch_kernel<Discounted<false>>(p, g, lb, pl, vec, stream);
-               });
+    return rlscan_discounted_returns_carry(rewards, bootstrap_value, terminated, truncated,
+                                           bootstrap_values, nullptr, returns, nullptr, N, T,
+                                           gamma, stream);
 }
 
-int rlscan_vtrace(const float* rewards, const float* values, const float* bootstrap_value,
-                  const float* log_rhos, const float* terminated, const float* truncated,
-                  const float* bootstrap_values, float* vs, float* pg_advantages, int64_t N,
-                  int64_t T, float gamma, float rho_bar, float c_bar, hipStream_t stream) {
+int rlscan_vtrace_carry(const float* rewards, const float* values, const float* bootstrap_value,
+                        const float* log_rhos, const float* terminated, const float* truncated,
+                        const float* bootstrap_values, const float* carry_in, float* vs,
+                        float* pg_advantages, float* carry_out, int64_t N, int64_t T,
+                        float gamma, float rho_bar, float c_bar, hipStream_t stream) {
     int rc = check_shape(N, T);
     if (rc != RLSCAN_OK) return rc;
     if (!unit_interval(gamma) || !positive_clip(rho_bar) || !positive_clip(c_bar))
@@ -629,26 +695,40 @@ int rlscan_vtrace(const float* rewards, const float* values, const float* bootst
     if (!rewards || !values || !log_rhos || !terminated || !vs || !pg_advantages)
         return RLSCAN_ERR_NULL;
     if (truncated && !bootstrap_values) return RLSCAN_ERR_NULL;
-    rc = check_alias({vs, pg_advantages}, {rewards, values, bootstrap_value, log_rhos, terminated,
-                                           truncated, bootstrap_values});
+    rc = check_alias({vs, pg_advantages, carry_out},
+                     {rewards, values, bootstrap_value, log_rhos, terminated, truncated,
+                      bootstrap_values, carry_in});
     if (rc != RLSCAN_OK) return rc;
-    const VtraceParams p{rewards,   values, bootstrap_value, log_rhos,
-                         terminated, truncated, bootstrap_values, vs,
-                         pg_advantages, gamma, rho_bar, c_bar};
+    const VtraceParams p{rewards,   values,        bootstrap_value, log_rhos,
+                         terminated, truncated,    bootstrap_values, carry_in,
+                         vs,        pg_advantages, carry_out,        gamma,
+                         rho_bar,   c_bar};
     const bool vec = all_aligned({rewards, values, log_rhos, terminated, truncated,
                                   bootstrap_values, vs, pg_advantages});
-    return run(RLSCAN_EST_VTRACE, N, T, vec, stream,
+    const bool carry = carry_in != nullptr || carry_out != nullptr;
+    return run(RLSCAN_EST_VTRACE, N, T, vec, carry, stream,
                [&](const Geometry& g, const LookbackArgs& lb, const Plan& pl) {
-                   return truncated ? launch_kernel<Vtrace<true>>(p, g, lb, pl, vec, stream)
-                                    : launch_kernel<Vtrace<false>>(p, g, lb, pl, vec, stream);
+                   return truncated ? launch_kernel<Vtrace<true>>(p, g, lb, pl, vec, carry, stream)
+                                    : launch_kernel<Vtrace<false>>(p, g, lb, pl, vec, carry, stream);
                });
 }
 
-int rlscan_retrace(const float* rewards, const float* next_q_values_all,
-                   const float* next_target_probs, const int32_t* actions,
-                   const float* behaviour_probs, const float* terminated, const float* truncated,
-                   float* targets, int64_t N, int64_t T, int64_t A, float gamma, float lambda,
-                   hipStream_t stream) {
+int rlscan_vtrace(const float* rewards, const float* values, const float* bootstrap_value,
+                  const float* log_rhos, const float* terminated, const float* truncated,
+                  const float* bootstrap_values, float* vs, float* pg_advantages, int64_t N,
+                  int64_t T, float gamma, float rho_bar, float c_bar, hipStream_t stream) {
+    return rlscan_vtrace_carry(rewards, values, bootstrap_value, log_rhos, terminated, truncated,
+                               bootstrap_values, nullptr, vs, pg_advantages, nullptr, N, T,
+                               gamma, rho_bar, c_bar, stream);
+}
+
+int rlscan_retrace_carry(const float* rewards, const float* next_q_values_all,
+                         const float* next_target_probs, const int32_t* actions,
+                         const float* behaviour_probs, const float* terminated,
+                         const float* truncated, const float* carry_in,
+                         const int32_t* next_actions, const float* next_behaviour_probs,
+                         float* targets, float* carry_out, int64_t N, int64_t T, int64_t A,
+                         float gamma, float lambda, hipStream_t stream) {
     int rc = check_shape(N, T, A);
     if (rc != RLSCAN_OK) return rc;
     if (!unit_interval(gamma) || !unit_interval(lambda)) return RLSCAN_ERR_PARAM;
@@ -656,18 +736,23 @@ int rlscan_retrace(const float* rewards, const float* next_q_values_all,
     if (!rewards || !next_q_values_all || !next_target_probs || !actions || !behaviour_probs ||
         !terminated || !truncated || !targets)
         return RLSCAN_ERR_NULL;
-    rc = check_alias({targets}, {rewards, next_q_values_all, next_target_probs, actions,
-                                 behaviour_probs, terminated, truncated});
+    if (carry_in && (!next_actions || !next_behaviour_probs)) return RLSCAN_ERR_NULL;
+    rc = check_alias({targets, carry_out},
+                     {rewards, next_q_values_all, next_target_probs, actions, behaviour_probs,
+                      terminated, truncated, carry_in, next_actions, next_behaviour_probs});
     if (rc != RLSCAN_OK) return rc;
     const bool vec = all_aligned({rewards, next_q_values_all, next_target_probs, actions,
                                   behaviour_probs, terminated, truncated, targets});
+    const bool carry = carry_in != nullptr || carry_out != nullptr;
     auto go = [&](auto tag) {
         using E = decltype(tag);
-        typename E::Params p{rewards, next_q_values_all, next_target_probs, actions,
-                             behaviour_probs, terminated, truncated, targets, A, gamma, lambda};
-        return run(RLSCAN_EST_RETRACE, N, T, vec, stream,
+        typename E::Params p{rewards,  next_q_values_all, next_target_probs, actions,
+                             behaviour_probs, terminated, truncated, targets,
+                             A,        gamma,             lambda,            carry_in,
+                             next_actions, next_behaviour_probs, carry_out};
+        return run(RLSCAN_EST_RETRACE, N, T, vec, carry, stream,
                    [&](const Geometry& g, const LookbackArgs& lb, const Plan& pl) {
-                       return launch_kernel_r1<E>(p, g, lb, pl, vec, stream);
+                       return launch_kernel_r1<E>(p, g, lb, pl, vec, carry, stream);
                    });
     };
     switch (vec ? A : 0) {
@@ -679,37 +764,62 @@ int rlscan_retrace(const float* rewards, const float* next_q_values_all,
     }
 }
 
-int rlscan_eligibility_traces(const float* x, const float* dones, float* traces, int64_t N,
-                              int64_t T, float gamma, float lambda, hipStream_t stream) {
+int rlscan_retrace(const float* rewards, const float* next_q_values_all,
+                   const float* next_target_probs, const int32_t* actions,
+                   const float* behaviour_probs, const float* terminated, const float* truncated,
+                   float* targets, int64_t N, int64_t T, int64_t A, float gamma, float lambda,
+                   hipStream_t stream) {
+    return rlscan_retrace_carry(rewards, next_q_values_all, next_target_probs, actions,
+                                behaviour_probs, terminated, truncated, nullptr, nullptr, nullptr,
+                                targets, nullptr, N, T, A, gamma, lambda, stream);
+}
+
+int rlscan_eligibility_traces_carry(const float* x, const float* dones, const float* carry_in,
+                                    float* traces, float* carry_out, int64_t N, int64_t T,
+                                    float gamma, float lambda, hipStream_t stream) {
     int rc = check_shape(N, T);
     if (rc != RLSCAN_OK) return rc;
     if (!unit_interval(gamma) || !unit_interval(lambda)) return RLSCAN_ERR_PARAM;
     if (N == 0 || T == 0) return RLSCAN_OK;
     if (!x || !dones || !traces) return RLSCAN_ERR_NULL;
-    rc = check_alias({traces}, {x, dones});
+    rc = check_alias({traces, carry_out}, {x, dones, carry_in});
     if (rc != RLSCAN_OK) return rc;
-    Eligibility::Params p{x, dones, traces, gamma * lambda};
+    Eligibility::Params p{x, dones, traces, gamma * lambda, carry_in, carry_out};
     const bool vec = all_aligned({x, dones, traces});
-    return run(RLSCAN_EST_ELIGIBILITY, N, T, vec, stream,
+    const bool carry = carry_in != nullptr || carry_out != nullptr;
+    return run(RLSCAN_EST_ELIGIBILITY, N, T, vec, carry, stream,
                [&](const Geometry& g, const LookbackArgs& lb, const Plan& pl) {
-                   return launch_kernel<Eligibility>(p, g, lb, pl, vec, stream);
+                   return launch_kernel<Eligibility>(p, g, lb, pl, vec, carry, stream);
+               });
+}
+
+int rlscan_eligibility_traces(const float* x, const float* dones, float* traces, int64_t N,
+                              int64_t T, float gamma, float lambda, hipStream_t stream) {
+    return rlscan_eligibility_traces_carry(x, dones, nullptr, traces, nullptr, N, T, gamma,
+                                           lambda, stream);
+}
+
+int rlscan_episodic_prefix_sum_carry(const int32_t* x, const float* dones,
+                                     const int64_t* carry_in, int64_t* out, int64_t* carry_out,
+                                     int64_t N, int64_t T, hipStream_t stream) {
+    int rc = check_shape(N, T);
+    if (rc != RLSCAN_OK) return rc;
+    if (N == 0 || T == 0) return RLSCAN_OK;
+    if (!x || !dones || !out) return RLSCAN_ERR_NULL;
+    rc = check_alias({out, carry_out}, {x, dones, carry_in});
+    if (rc != RLSCAN_OK) return rc;
+    PrefixSum::Params p{x, dones, out, carry_in, carry_out};
+    const bool vec = all_aligned({x, dones, out});
+    const bool carry = carry_in != nullptr || carry_out != nullptr;
+    return run(RLSCAN_EST_PREFIX_SUM, N, T, vec, carry, stream,
+               [&](const Geometry& g, const LookbackArgs& lb, const Plan& pl) {
+                   return launch_kernel<PrefixSum>(p, g, lb, pl, vec, carry, stream);
                });
 }
 
 int rlscan_episodic_prefix_sum(const int32_t* x, const float* dones, int64_t* out, int64_t N,
                                int64_t T, hipStream_t stream) {
-    int rc = check_shape(N, T);
-    if (rc != RLSCAN_OK) return rc;
-    if (N == 0 || T == 0) return RLSCAN_OK;
-    if (!x || !dones || !out) return RLSCAN_ERR_NULL;
-    rc = check_alias({out}, {x, dones});
-    if (rc != RLSCAN_OK) return rc;
-    PrefixSum::Params p{x, dones, out};
-    const bool vec = all_aligned({x, dones, out});
-    return run(RLSCAN_EST_PREFIX_SUM, N, T, vec, stream,
-               [&](const Geometry& g, const LookbackArgs& lb, const Plan& pl) {
-                   return launch_kernel<PrefixSum>(p, g, lb, pl, vec, stream);
-               });
+    return rlscan_episodic_prefix_sum_carry(x, dones, nullptr, out, nullptr, N, T, stream);
 }
 
 const char* rlscan_status_string(int status) {

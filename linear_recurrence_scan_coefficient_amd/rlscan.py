@@ -45,6 +45,9 @@ EXPORTED = (
     "rlscan_status_string", "rlscan_version", "rlscan_release_scratch", "rlscan_plan",
     "rlscan_set_launch_override", "rlscan_lookback_timeouts", "rlscan_launch_floor",
     "rlscan_stream_copy",
+    "rlscan_gae_carry", "rlscan_lambda_returns_carry", "rlscan_discounted_returns_carry",
+    "rlscan_vtrace_carry", "rlscan_retrace_carry", "rlscan_eligibility_traces_carry",
+    "rlscan_episodic_prefix_sum_carry",
 )
 
 
@@ -75,10 +78,19 @@ def _declare(lib):
     lib.rlscan_retrace.argtypes = [_vp] * 8 + [_i64, _i64, _i64, _f32, _f32, _vp]
     lib.rlscan_eligibility_traces.argtypes = [_vp] * 3 + [_i64, _i64, _f32, _f32, _vp]
     lib.rlscan_episodic_prefix_sum.argtypes = [_vp] * 3 + [_i64, _i64, _vp]
+    lib.rlscan_gae_carry.argtypes = [_vp] * 9 + [_i64, _i64, _f32, _f32, _vp]
+    lib.rlscan_lambda_returns_carry.argtypes = [_vp] * 9 + [_i64, _i64, _f32, _f32, _vp]
+    lib.rlscan_discounted_returns_carry.argtypes = [_vp] * 8 + [_i64, _i64, _f32, _vp]
+    lib.rlscan_vtrace_carry.argtypes = [_vp] * 11 + [_i64, _i64, _f32, _f32, _f32, _vp]
+    lib.rlscan_retrace_carry.argtypes = [_vp] * 12 + [_i64, _i64, _i64, _f32, _f32, _vp]
+    lib.rlscan_eligibility_traces_carry.argtypes = [_vp] * 5 + [_i64, _i64, _f32, _f32, _vp]
+    lib.rlscan_episodic_prefix_sum_carry.argtypes = [_vp] * 5 + [_i64, _i64, _vp]
     for name in ("rlscan_gae", "rlscan_lambda_returns", "rlscan_discounted_returns",
                  "rlscan_vtrace", "rlscan_retrace", "rlscan_eligibility_traces",
                  "rlscan_episodic_prefix_sum", "rlscan_release_scratch"):
         getattr(lib, name).restype = ctypes.c_int
+        if name != "rlscan_release_scratch":
+            getattr(lib, name + "_carry").restype = ctypes.c_int
     lib.rlscan_release_scratch.argtypes = []
     lib.rlscan_status_string.argtypes = [ctypes.c_int]
     lib.rlscan_status_string.restype = ctypes.c_char_p
@@ -157,92 +169,147 @@ def _nt(t, name):
 
 
 # ------------------------------------------------------------------ entry points
+# Every entry point below takes optional carry_in / carry_out [N] tensors
+# (streaming one rollout through several calls); with either given it calls
+# the *_carry C function, else the plain one.
+def _carry(carry_in, carry_out, N, dtype=torch.float32):
+    return (carry_in is not None or carry_out is not None,
+            _ptr(carry_in, dtype=dtype, shape=(N,), name="carry_in"),
+            _ptr(carry_out, dtype=dtype, shape=(N,), name="carry_out"))
+
+
 def rlscan_gae(rewards, values, bootstrap_value, terminated, truncated, bootstrap_values,
-               advantages, gamma, lam, stream=None):
+               advantages, gamma, lam, stream=None, carry_in=None, carry_out=None):
     N, T = _nt(rewards, "rewards")
-    _check(library().rlscan_gae(
-        _ptr(rewards, shape=(N, T), name="rewards"), _ptr(values, shape=(N, T), name="values"),
-        _ptr(bootstrap_value, shape=(N,), name="bootstrap_value"),
-        _ptr(terminated, shape=(N, T), name="terminated"),
-        _ptr(truncated, shape=(N, T), name="truncated"),
-        _ptr(bootstrap_values, shape=(N, T), name="bootstrap_values"),
-        _ptr(advantages, shape=(N, T), name="advantages"), N, T, gamma, lam, _stream(stream)))
+    use, ci, co = _carry(carry_in, carry_out, N)
+    ins = (_ptr(rewards, shape=(N, T), name="rewards"), _ptr(values, shape=(N, T), name="values"),
+           _ptr(bootstrap_value, shape=(N,), name="bootstrap_value"),
+           _ptr(terminated, shape=(N, T), name="terminated"),
+           _ptr(truncated, shape=(N, T), name="truncated"),
+           _ptr(bootstrap_values, shape=(N, T), name="bootstrap_values"))
+    out = _ptr(advantages, shape=(N, T), name="advantages")
+    lib = library()
+    if use:
+        _check(lib.rlscan_gae_carry(*ins, ci, out, co, N, T, gamma, lam, _stream(stream)))
+    else:
+        _check(lib.rlscan_gae(*ins, out, N, T, gamma, lam, _stream(stream)))
     return advantages
 
 
 def rlscan_lambda_returns(rewards, values, bootstrap_value, terminated, truncated,
-                          bootstrap_values, returns, gamma, lam, stream=None):
+                          bootstrap_values, returns, gamma, lam, stream=None, carry_in=None,
+                          carry_out=None):
     N, T = _nt(rewards, "rewards")
-    _check(library().rlscan_lambda_returns(
-        _ptr(rewards, shape=(N, T), name="rewards"), _ptr(values, shape=(N, T), name="values"),
-        _ptr(bootstrap_value, shape=(N,), name="bootstrap_value"),
-        _ptr(terminated, shape=(N, T), name="terminated"),
-        _ptr(truncated, shape=(N, T), name="truncated"),
-        _ptr(bootstrap_values, shape=(N, T), name="bootstrap_values"),
-        _ptr(returns, shape=(N, T), name="returns"), N, T, gamma, lam, _stream(stream)))
+    use, ci, co = _carry(carry_in, carry_out, N)
+    ins = (_ptr(rewards, shape=(N, T), name="rewards"), _ptr(values, shape=(N, T), name="values"),
+           _ptr(bootstrap_value, shape=(N,), name="bootstrap_value"),
+           _ptr(terminated, shape=(N, T), name="terminated"),
+           _ptr(truncated, shape=(N, T), name="truncated"),
+           _ptr(bootstrap_values, shape=(N, T), name="bootstrap_values"))
+    out = _ptr(returns, shape=(N, T), name="returns")
+    lib = library()
+    if use:
+        _check(lib.rlscan_lambda_returns_carry(*ins, ci, out, co, N, T, gamma, lam,
+                                               _stream(stream)))
+    else:
+        _check(lib.rlscan_lambda_returns(*ins, out, N, T, gamma, lam, _stream(stream)))
     return returns
 
 
 def rlscan_discounted_returns(rewards, bootstrap_value, terminated, truncated, bootstrap_values,
-                              returns, gamma, stream=None):
+                              returns, gamma, stream=None, carry_in=None, carry_out=None):
     N, T = _nt(rewards, "rewards")
-    _check(library().rlscan_discounted_returns(
-        _ptr(rewards, shape=(N, T), name="rewards"),
-        _ptr(bootstrap_value, shape=(N,), name="bootstrap_value"),
-        _ptr(terminated, shape=(N, T), name="terminated"),
-        _ptr(truncated, shape=(N, T), name="truncated"),
-        _ptr(bootstrap_values, shape=(N, T), name="bootstrap_values"),
-        _ptr(returns, shape=(N, T), name="returns"), N, T, gamma, _stream(stream)))
+    use, ci, co = _carry(carry_in, carry_out, N)
+    ins = (_ptr(rewards, shape=(N, T), name="rewards"),
+           _ptr(bootstrap_value, shape=(N,), name="bootstrap_value"),
+           _ptr(terminated, shape=(N, T), name="terminated"),
+           _ptr(truncated, shape=(N, T), name="truncated"),
+           _ptr(bootstrap_values, shape=(N, T), name="bootstrap_values"))
+    out = _ptr(returns, shape=(N, T), name="returns")
+    lib = library()
+    if use:
+        _check(lib.rlscan_discounted_returns_carry(*ins, ci, out, co, N, T, gamma,
+                                                   _stream(stream)))
+    else:
+        _check(lib.rlscan_discounted_returns(*ins, out, N, T, gamma, _stream(stream)))
     return returns
 
 
 def rlscan_vtrace(rewards, values, bootstrap_value, log_rhos, terminated, truncated,
-                  bootstrap_values, vs, pg_advantages, gamma, rho_bar, c_bar, stream=None):
+                  bootstrap_values, vs, pg_advantages, gamma, rho_bar, c_bar, stream=None,
+                  carry_in=None, carry_out=None):
     N, T = _nt(rewards, "rewards")
-    _check(library().rlscan_vtrace(
-        _ptr(rewards, shape=(N, T), name="rewards"), _ptr(values, shape=(N, T), name="values"),
-        _ptr(bootstrap_value, shape=(N,), name="bootstrap_value"),
-        _ptr(log_rhos, shape=(N, T), name="log_rhos"),
-        _ptr(terminated, shape=(N, T), name="terminated"),
-        _ptr(truncated, shape=(N, T), name="truncated"),
-        _ptr(bootstrap_values, shape=(N, T), name="bootstrap_values"),
-        _ptr(vs, shape=(N, T), name="vs"), _ptr(pg_advantages, shape=(N, T), name="pg_advantages"),
-        N, T, gamma, rho_bar, c_bar, _stream(stream)))
+    use, ci, co = _carry(carry_in, carry_out, N)
+    ins = (_ptr(rewards, shape=(N, T), name="rewards"), _ptr(values, shape=(N, T), name="values"),
+           _ptr(bootstrap_value, shape=(N,), name="bootstrap_value"),
+           _ptr(log_rhos, shape=(N, T), name="log_rhos"),
+           _ptr(terminated, shape=(N, T), name="terminated"),
+           _ptr(truncated, shape=(N, T), name="truncated"),
+           _ptr(bootstrap_values, shape=(N, T), name="bootstrap_values"))
+    outs = (_ptr(vs, shape=(N, T), name="vs"),
+            _ptr(pg_advantages, shape=(N, T), name="pg_advantages"))
+    lib = library()
+    if use:
+        _check(lib.rlscan_vtrace_carry(*ins, ci, *outs, co, N, T, gamma, rho_bar, c_bar,
+                                       _stream(stream)))
+    else:
+        _check(lib.rlscan_vtrace(*ins, *outs, N, T, gamma, rho_bar, c_bar, _stream(stream)))
     return vs, pg_advantages
 
 
 def rlscan_retrace(rewards, next_q_values_all, next_target_probs, actions, behaviour_probs,
-                   terminated, truncated, targets, gamma, lam, stream=None):
+                   terminated, truncated, targets, gamma, lam, stream=None, carry_in=None,
+                   carry_out=None, next_actions=None, next_behaviour_probs=None):
     N, T = _nt(rewards, "rewards")
     if next_q_values_all is None or next_q_values_all.dim() != 3:
         raise ValueError("next_q_values_all must be a [N, T, A] tensor")
     A = next_q_values_all.shape[2]
-    _check(library().rlscan_retrace(
-        _ptr(rewards, shape=(N, T), name="rewards"),
-        _ptr(next_q_values_all, shape=(N, T, A), name="next_q_values_all"),
-        _ptr(next_target_probs, shape=(N, T, A), name="next_target_probs"),
-        _ptr(actions, dtype=torch.int32, shape=(N, T), name="actions"),
-        _ptr(behaviour_probs, shape=(N, T), name="behaviour_probs"),
-        _ptr(terminated, shape=(N, T), name="terminated"),
-        _ptr(truncated, shape=(N, T), name="truncated"),
-        _ptr(targets, shape=(N, T), name="targets"), N, T, A, gamma, lam, _stream(stream)))
+    use, ci, co = _carry(carry_in, carry_out, N)
+    ins = (_ptr(rewards, shape=(N, T), name="rewards"),
+           _ptr(next_q_values_all, shape=(N, T, A), name="next_q_values_all"),
+           _ptr(next_target_probs, shape=(N, T, A), name="next_target_probs"),
+           _ptr(actions, dtype=torch.int32, shape=(N, T), name="actions"),
+           _ptr(behaviour_probs, shape=(N, T), name="behaviour_probs"),
+           _ptr(terminated, shape=(N, T), name="terminated"),
+           _ptr(truncated, shape=(N, T), name="truncated"))
+    out = _ptr(targets, shape=(N, T), name="targets")
+    lib = library()
+    if use:
+        _check(lib.rlscan_retrace_carry(
+            *ins, ci, _ptr(next_actions, dtype=torch.int32, shape=(N,), name="next_actions"),
+            _ptr(next_behaviour_probs, shape=(N,), name="next_behaviour_probs"), out, co,
+            N, T, A, gamma, lam, _stream(stream)))
+    else:
+        _check(lib.rlscan_retrace(*ins, out, N, T, A, gamma, lam, _stream(stream)))
     return targets
 
 
-def rlscan_eligibility_traces(x, dones, traces, gamma, lam, stream=None):
+def rlscan_eligibility_traces(x, dones, traces, gamma, lam, stream=None, carry_in=None,
+                              carry_out=None):
     N, T = _nt(x, "x")
-    _check(library().rlscan_eligibility_traces(
-        _ptr(x, shape=(N, T), name="x"), _ptr(dones, shape=(N, T), name="dones"),
-        _ptr(traces, shape=(N, T), name="traces"), N, T, gamma, lam, _stream(stream)))
+    use, ci, co = _carry(carry_in, carry_out, N)
+    ins = (_ptr(x, shape=(N, T), name="x"), _ptr(dones, shape=(N, T), name="dones"))
+    out = _ptr(traces, shape=(N, T), name="traces")
+    lib = library()
+    if use:
+        _check(lib.rlscan_eligibility_traces_carry(*ins, ci, out, co, N, T, gamma, lam,
+                                                   _stream(stream)))
+    else:
+        _check(lib.rlscan_eligibility_traces(*ins, out, N, T, gamma, lam, _stream(stream)))
     return traces
 
 
-def rlscan_episodic_prefix_sum(x, dones, out, stream=None):
+def rlscan_episodic_prefix_sum(x, dones, out, stream=None, carry_in=None, carry_out=None):
     N, T = _nt(x, "x")
-    _check(library().rlscan_episodic_prefix_sum(
-        _ptr(x, dtype=torch.int32, shape=(N, T), name="x"),
-        _ptr(dones, shape=(N, T), name="dones"),
-        _ptr(out, dtype=torch.int64, shape=(N, T), name="out"), N, T, _stream(stream)))
+    use, ci, co = _carry(carry_in, carry_out, N, dtype=torch.int64)
+    ins = (_ptr(x, dtype=torch.int32, shape=(N, T), name="x"),
+           _ptr(dones, shape=(N, T), name="dones"))
+    o = _ptr(out, dtype=torch.int64, shape=(N, T), name="out")
+    lib = library()
+    if use:
+        _check(lib.rlscan_episodic_prefix_sum_carry(*ins, ci, o, co, N, T, _stream(stream)))
+    else:
+        _check(lib.rlscan_episodic_prefix_sum(*ins, o, N, T, _stream(stream)))
     return out
 
 

@@ -176,3 +176,33 @@ def test_stream_copy_argument_checks(lib):
     assert f(P[1] + 4, P[0], 64, None) == PARAM    # misaligned
     assert f(P[0] + 32, P[0], 64, None) == ALIAS   # overlapping ranges
     assert f(P[0], P[0] + 32, 64, None) == ALIAS
+
+
+def test_carry_entry_points_argument_checks(lib):
+    f = lib
+    # GAE with carry: carry_out may not alias an input or the output
+    args = list(P[:9])  # 6 inputs, carry_in, advantages, carry_out
+    bad = list(args)
+    bad[8] = bad[7]
+    assert f.rlscan_gae_carry(*bad, 4, 8, 0.9, 0.9, None) == ALIAS
+    bad = list(args)
+    bad[8] = bad[6]
+    assert f.rlscan_gae_carry(*bad, 4, 8, 0.9, 0.9, None) == ALIAS
+    # carry_out alone is allowed to be the only optional pointer given
+    assert f.rlscan_gae_carry(*P[:6], None, P[7], P[7], 4, 8, 0.9, 0.9, None) == ALIAS
+    # Retrace: a carry_in needs next_actions and next_behaviour_probs
+    r = list(P[:7]) + [P[7], None, P[9], P[10], P[11]]
+    assert f.rlscan_retrace_carry(*r, 4, 8, 6, 0.9, 0.9, None) == NULL
+    r = list(P[:7]) + [P[7], P[8], None, P[10], P[11]]
+    assert f.rlscan_retrace_carry(*r, 4, 8, 6, 0.9, 0.9, None) == NULL
+    r = list(P[:7]) + [P[7], P[8], P[9], P[10], P[10]]
+    assert f.rlscan_retrace_carry(*r, 4, 8, 6, 0.9, 0.9, None) == ALIAS
+    # forward estimators
+    assert f.rlscan_eligibility_traces_carry(P[0], P[1], P[2], P[3], P[2], 4, 8, 0.9, 0.9,
+                                             None) == ALIAS
+    assert f.rlscan_episodic_prefix_sum_carry(P[0], P[1], P[2], P[3], P[0], 4, 8, None) == ALIAS
+    assert f.rlscan_episodic_prefix_sum_carry(None, None, None, None, None, 0, 8, None) == OK
+    # the same parameter checks as the plain calls
+    assert f.rlscan_discounted_returns_carry(*P[:8], 4, 8, 1.5, None) == PARAM
+    assert f.rlscan_vtrace_carry(*P[:11], 4, 8, 0.9, 0.0, 1.0, None) == PARAM
+    assert f.rlscan_lambda_returns_carry(*P[:9], -1, 8, 0.9, 0.9, None) == SHAPE

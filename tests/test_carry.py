@@ -1,0 +1,253 @@
+"""GPU parity of the carry arguments (streaming one rollout through several
+calls) against the float64 oracle, element by element, and chained GPU
+calls against the whole-rollout oracle.
+
+Cases: random carry_in with carry_out, carry_out alone, edge steps that are
+terminated / truncated / done (the carry must then be ignored), short rows
+(several row edges per chunk), long rows that take the look-back mapping,
+every round count, and chunks chained across calls.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from reference import assert_parity
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+from linear_recurrence_scan_coefficient_amd import rlscan, workloads  # noqa: E402
+from linear_recurrence_scan_coefficient_amd.workloads import ESTIMATORS  # noqa: E402
+
+TRUNC = ("gae", "lambda_returns", "discounted_returns", "vtrace", "retrace")
+
+
+@pytest.fixture(autouse=True)
+def _reset_override():
+    rlscan.rlscan_set_launch_override()
+    yield
+    rlscan.rlscan_set_launch_override()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _no_lookback_timeouts():
+    yield
+    assert rlscan.rlscan_lookback_timeouts() == 0
+
+
+def case(estimator, N, T, seed):
+    opts = dict(term_p=0.05, done_p=0.05, gamma=0.97, lam=0.9)
+    if estimator in TRUNC:
+        opts.update(trunc_mode="independent", trunc_p=0.05)
+    w = workloads.custom(N, T, **opts)
+    d = workloads.inputs_for(estimator, w, seed)
+    rng = np.random.default_rng(seed + 1)
+    # every row gets a V at t = T (the carry's partner) unless the estimator
+    # has no values
+    if estimator in ("gae", "lambda_returns", "vtrace", "discounted_returns"):
+        d["bootstrap_value"] = rng.standard_normal(N).astype(np.float32)
+    return w, d, rng
+
+
+def dev(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def carry_inputs(estimator, d, N, rng):
+    if estimator == "episodic_prefix_sum":
+        return {"carry_in": rng.integers(-1000, 1000, N).astype(np.int64)}
+    c = {"carry_in": rng.standard_normal(N).astype(np.float32)}
+    if estimator == "retrace":
+        A = d["next_q_values_all"].shape[2]
+        c["next_actions"] = rng.integers(0, A, N).astype(np.int32)
+        c["next_behaviour_probs"] = rng.uniform(0.05, 1.0, N).astype(np.float32)
+    return c
+
+
+def oracle_call(estimator, d, w, carry):
+    kw = dict(return_carry=True)
+    kw.update({k: v for k, v in carry.items() if v is not None})
+    g, lam = w.gamma, w.lam
+    if estimator == "gae":
+        a, co = oracle.gae(d["rewards"], d["values"], d["terminated"], gamma=g, lam=lam,
+                           bootstrap_value=d.get("bootstrap_value"), truncated=d.get("truncated"),
+                           bootstrap_values=d.get("bootstrap_values"), **kw)
+        return {"advantages": a, "carry_out": co}
+    if estimator == "lambda_returns":
+        a, co = oracle.lambda_returns(d["rewards"], d["values"], d["terminated"], gamma=g,
+                                      lam=lam, bootstrap_value=d.get("bootstrap_value"),
+                                      truncated=d.get("truncated"),
+                                      bootstrap_values=d.get("bootstrap_values"), **kw)
+        return {"returns": a, "carry_out": co}
+    if estimator == "discounted_returns":
+        a, co = oracle.discounted_returns(d["rewards"], d["terminated"], gamma=g,
+                                          bootstrap_value=d.get("bootstrap_value"),
+                                          truncated=d.get("truncated"),
+                                          bootstrap_values=d.get("bootstrap_values"), **kw)
+        return {"returns": a, "carry_out": co}
+    if estimator == "vtrace":
+        vs, pg, co = oracle.vtrace(d["rewards"], d["values"], d["log_rhos"], d["terminated"],
+                                   gamma=g, rho_bar=w.rho_bar, c_bar=w.c_bar,
+                                   bootstrap_value=d.get("bootstrap_value"),
+                                   truncated=d.get("truncated"),
+                                   bootstrap_values=d.get("bootstrap_values"), **kw)
+        return {"vs": vs, "pg_advantages": pg, "carry_out": co}
+    if estimator == "retrace":
+        a, co = oracle.retrace(d["rewards"], d["next_q_values_all"], d["next_target_probs"],
+                               d["actions"], d["behaviour_probs"], d["terminated"],
+                               d["truncated"], gamma=g, lam=lam, **kw)
+        return {"targets": a, "carry_out": co}
+    if estimator == "eligibility_traces":
+        a, co = oracle.eligibility_traces(d["x"], d["dones"], gamma=g, lam=lam, **kw)
+        return {"traces": a, "carry_out": co}
+    if estimator == "episodic_prefix_sum":
+        a, co = oracle.episodic_prefix_sum(d["x"], d["dones"], **kw)
+        return {"out": a, "carry_out": co}
+    raise ValueError(estimator)
+
+
+def gpu_call(estimator, d, w, carry):
+    N, T = w.N, w.T
+    t = {k: dev(v) for k, v in d.items()}
+    c = {k: dev(v) for k, v in carry.items()}
+    f32 = dict(dtype=torch.float32, device="cuda")
+    if estimator == "episodic_prefix_sum":
+        co = torch.full((N,), -7, dtype=torch.int64, device="cuda")
+    else:
+        co = torch.full((N,), float("nan"), **f32)
+    ci = c.get("carry_in")
+    if estimator in ("gae", "lambda_returns"):
+        out = torch.empty((N, T), **f32)
+        fn = rlscan.rlscan_gae if estimator == "gae" else rlscan.rlscan_lambda_returns
+        fn(t["rewards"], t["values"], t.get("bootstrap_value"), t["terminated"],
+           t.get("truncated"), t.get("bootstrap_values"), out, w.gamma, w.lam, carry_in=ci,
+           carry_out=co)
+        res = {"advantages" if estimator == "gae" else "returns": out}
+    elif estimator == "discounted_returns":
+        out = torch.empty((N, T), **f32)
+        rlscan.rlscan_discounted_returns(t["rewards"], t.get("bootstrap_value"), t["terminated"],
+                                         t.get("truncated"), t.get("bootstrap_values"), out,
+                                         w.gamma, carry_in=ci, carry_out=co)
+        res = {"returns": out}
+    elif estimator == "vtrace":
+        vs = torch.empty((N, T), **f32)
+        pg = torch.empty((N, T), **f32)
+        rlscan.rlscan_vtrace(t["rewards"], t["values"], t.get("bootstrap_value"), t["log_rhos"],
+                             t["terminated"], t.get("truncated"), t.get("bootstrap_values"), vs,
+                             pg, w.gamma, w.rho_bar, w.c_bar, carry_in=ci, carry_out=co)
+        res = {"vs": vs, "pg_advantages": pg}
+    elif estimator == "retrace":
+        out = torch.empty((N, T), **f32)
+        rlscan.rlscan_retrace(t["rewards"], t["next_q_values_all"], t["next_target_probs"],
+                              t["actions"], t["behaviour_probs"], t["terminated"],
+                              t["truncated"], out, w.gamma, w.lam, carry_in=ci, carry_out=co,
+                              next_actions=c.get("next_actions"),
+                              next_behaviour_probs=c.get("next_behaviour_probs"))
+        res = {"targets": out}
+    elif estimator == "eligibility_traces":
+        out = torch.empty((N, T), **f32)
+        rlscan.rlscan_eligibility_traces(t["x"], t["dones"], out, w.gamma, w.lam, carry_in=ci,
+                                         carry_out=co)
+        res = {"traces": out}
+    else:
+        out = torch.empty((N, T), dtype=torch.int64, device="cuda")
+        rlscan.rlscan_episodic_prefix_sum(t["x"], t["dones"], out, carry_in=ci, carry_out=co)
+        res = {"out": out}
+    res["carry_out"] = co
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in res.items()}
+
+
+def force_edge_flags(estimator, d, T):
+    """Row 0: the edge step ends its episode (terminated, or done for the
+    forward estimators); row 1: truncated there (reverse estimators)."""
+    if estimator in ("eligibility_traces", "episodic_prefix_sum"):
+        d["dones"][0, 0] = 1.0
+        d["dones"][1, 0] = 0.0
+        return
+    d["terminated"][0, T - 1] = 1.0
+    if d.get("truncated") is not None:
+        d["terminated"][1, T - 1] = 0.0
+        d["truncated"][1, T - 1] = 1.0
+
+
+SHAPES = [(37, 300), (5, 3), (64, 128), (3, 5000), (2, 70001)]
+
+
+@pytest.mark.parametrize("estimator", ESTIMATORS)
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{n}x{t}" for n, t in SHAPES])
+def test_carry_in_and_out(estimator, shape):
+    N, T = shape
+    w, d, rng = case(estimator, N, T, seed=N * 31 + T)
+    if N >= 2 and T >= 1:
+        force_edge_flags(estimator, d, T)
+    carry = carry_inputs(estimator, d, N, rng)
+    print(f"[carry] {estimator} {N}x{T}", flush=True)
+    assert_parity(gpu_call(estimator, d, w, carry), oracle_call(estimator, d, w, carry),
+                  f"carry {estimator} {N}x{T}")
+
+
+@pytest.mark.parametrize("estimator", ESTIMATORS)
+def test_carry_out_alone(estimator):
+    w, d, rng = case(estimator, 9, 1000, seed=3)
+    print(f"[carry] {estimator} carry_out only", flush=True)
+    assert_parity(gpu_call(estimator, d, w, {}), oracle_call(estimator, d, w, {}),
+                  f"carry_out only {estimator}")
+
+
+@pytest.mark.parametrize("estimator", ESTIMATORS)
+@pytest.mark.parametrize("rounds", [1, 2, 4])
+@pytest.mark.parametrize("mapping", ["lookback", "packed"])
+def test_carry_across_mappings(estimator, rounds, mapping):
+    m = rlscan.MAP_LOOKBACK if mapping == "lookback" else rlscan.MAP_PACKED
+    rlscan.rlscan_set_launch_override(m, rounds)
+    w, d, rng = case(estimator, 40, 4096, seed=rounds + 10 * (m + 1))
+    force_edge_flags(estimator, d, 4096)
+    carry = carry_inputs(estimator, d, 40, rng)
+    print(f"[carry] {estimator} {mapping} R={rounds}", flush=True)
+    assert_parity(gpu_call(estimator, d, w, carry), oracle_call(estimator, d, w, carry),
+                  f"carry {estimator} {mapping} R={rounds}")
+
+
+def _cols(d, lo, hi):
+    return {k: (np.ascontiguousarray(v[:, lo:hi]) if isinstance(v, np.ndarray) and v.ndim >= 2
+                else v) for k, v in d.items()}
+
+
+@pytest.mark.parametrize("estimator", ESTIMATORS)
+def test_chained_chunks_match_the_whole_rollout(estimator):
+    """Three GPU calls over consecutive pieces of each row, chained through
+    carry_in / carry_out, against the oracle on the whole rows."""
+    N, T = 6, 30000
+    w, d, rng = case(estimator, N, T, seed=77)
+    whole = oracle_call(estimator, d, w, {})
+    cuts = [0, 9000, 21001, T]
+    pieces = [(cuts[i], cuts[i + 1]) for i in range(3)]
+    outs = {}
+    forward = estimator in ("eligibility_traces", "episodic_prefix_sum")
+    order = pieces if forward else pieces[::-1]
+    carry = {}
+    for lo, hi in order:
+        sub = _cols(d, lo, hi)
+        if not forward and hi < T and "values" in d:
+            sub["bootstrap_value"] = np.ascontiguousarray(d["values"][:, hi])
+        elif not forward and hi < T:
+            sub["bootstrap_value"] = None
+        if estimator == "retrace" and hi < T:
+            carry["next_actions"] = np.ascontiguousarray(d["actions"][:, hi])
+            carry["next_behaviour_probs"] = np.ascontiguousarray(d["behaviour_probs"][:, hi])
+        wsub = workloads.custom(N, hi - lo, gamma=w.gamma, lam=w.lam, rho_bar=w.rho_bar,
+                                c_bar=w.c_bar)
+        print(f"[carry] {estimator} chunk [{lo}, {hi})", flush=True)
+        got = gpu_call(estimator, sub, wsub, carry)
+        for k, v in got.items():
+            if k != "carry_out":
+                outs.setdefault(k, {})[lo] = v
+        carry = {"carry_in": got["carry_out"]}
+    result = {k: np.concatenate([parts[lo] for lo, _ in pieces], axis=1)
+              for k, parts in outs.items()}
+    want = {k: v for k, v in whole.items() if k != "carry_out"}
+    assert_parity(result, want, f"chained {estimator}")
