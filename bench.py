@@ -229,6 +229,104 @@ def raw_call_args(est, d, out, w, stream):
     raise ValueError(est)
 
 
+def raw_carry_call_args(est, d, out, N, T, w, carry_in, carry_out, stream):
+    """The C argument tuple of one *_carry call (device pointers as ints;
+    carry_in / carry_out are [N] device tensors or None)."""
+    def p(t):
+        return None if t is None else t.data_ptr()
+    ci, co = p(carry_in), p(carry_out)
+    if est == "gae":
+        return ("rlscan_gae_carry", (p(d["rewards"]), p(d["values"]), p(d.get("bootstrap_value")),
+                                     p(d["terminated"]), p(d.get("truncated")),
+                                     p(d.get("bootstrap_values")), ci, p(out["advantages"]), co,
+                                     N, T, w.gamma, w.lam, stream))
+    if est == "discounted_returns":
+        return ("rlscan_discounted_returns_carry",
+                (p(d["rewards"]), p(d.get("bootstrap_value")), p(d["terminated"]),
+                 p(d.get("truncated")), p(d.get("bootstrap_values")), ci, p(out["returns"]), co,
+                 N, T, w.gamma, stream))
+    if est == "vtrace":
+        return ("rlscan_vtrace_carry", (p(d["rewards"]), p(d["values"]),
+                                        p(d.get("bootstrap_value")), p(d["log_rhos"]),
+                                        p(d["terminated"]), p(d.get("truncated")),
+                                        p(d.get("bootstrap_values")), ci, p(out["vs"]),
+                                        p(out["pg_advantages"]), co, N, T, w.gamma, w.rho_bar,
+                                        w.c_bar, stream))
+    if est == "episodic_prefix_sum":
+        return ("rlscan_episodic_prefix_sum_carry", (p(d["x"]), p(d["dones"]), ci, p(out["out"]),
+                                                     co, N, T, stream))
+    raise ValueError(f"no streamed timing for {est}")
+
+
+class StreamedSet:
+    """One rollout per row split into `chunks` pieces along T, as device
+    copies, with the C calls that process it piece by piece through the
+    carry arguments: later pieces first for the reverse estimators, earlier
+    first for the forward ones.  V at an inner piece's end is the next
+    piece's first value."""
+
+    def __init__(self, est, w, seed, chunks, stream_handle, lib):
+        import torch
+        from linear_recurrence_scan_coefficient_amd import device, workloads
+        host = workloads.inputs_for(est, w, seed)
+        self.bytes = algorithmic_bytes(host, device.alloc_outputs(est, w.N, w.T))
+        full = device.upload(host)
+        N, T = w.N, w.T
+        bounds = [T * i // chunks for i in range(chunks + 1)]
+        forward = est == "episodic_prefix_sum"
+        self.keep, self.calls = [], []
+        dtype = torch.int64 if forward else torch.float32
+        carries = [torch.zeros(N, dtype=dtype, device="cuda") for _ in range(chunks + 1)]
+        self.keep.append(carries)
+        order = range(chunks) if forward else range(chunks - 1, -1, -1)
+        for i in order:
+            lo, hi = bounds[i], bounds[i + 1]
+            d = {k: (v[:, lo:hi].contiguous() if v is not None and v.dim() >= 2 else v)
+                 for k, v in full.items()}
+            if not forward and hi < T:
+                d["bootstrap_value"] = (full["values"][:, hi].contiguous() if "values" in full
+                                        else None)
+            out = device.alloc_outputs(est, N, hi - lo)
+            self.keep.append((d, out))
+            if forward:
+                ci, co = (carries[i] if i > 0 else None), carries[i + 1]
+            else:
+                ci, co = (carries[i + 1] if hi < T else None), carries[i]
+            name, args = raw_carry_call_args(est, d, out, N, hi - lo, w, ci, co, stream_handle)
+            self.calls.append((est, getattr(lib, name), args))
+        del full
+
+    def run(self):
+        for est, fn, args in self.calls:
+            rc = fn(*args)
+            if rc != 0:
+                raise RuntimeError(f"{est}: rlscan status {rc}")
+
+
+def time_streamed(torch, w, sh, lib, chunks, reps):
+    """Microseconds per whole rollout streamed in `chunks` calls per row
+    (back-to-back, alternating two buffer sets), per estimator."""
+    res = {}
+    for est in w.estimators:
+        sets = [StreamedSet(est, w, seed, chunks, sh, lib) for seed in range(2)]
+        sets[0].run()
+        sets[1].run()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            sets[i % 2].run()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / reps * 1000.0
+        gbs = sets[0].bytes / (us * 1e-6) / 1e9
+        res[est] = {"us_per_rollout": round(us, 2), "calls": chunks, "bytes": sets[0].bytes,
+                    "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        del sets
+        torch.cuda.empty_cache()
+    return res
+
+
 def algorithmic_bytes(inputs: dict, outputs: dict) -> int:
     """Bytes the method must move: every input read once, every output
     written once."""
@@ -563,6 +661,13 @@ def main():
         wl = workloads.get("long_8x1048576")
         print("[bench] timing long-sequence calls", file=sys.stderr, flush=True)
         result["long_8x1048576"] = eager_workload(torch, wl, sh, lib, args.long_calls)
+        print("[bench] timing the long rollout streamed in 8 calls per row",
+              file=sys.stderr, flush=True)
+        result["long_8x1048576_streamed"] = time_streamed(torch, wl, sh, lib, chunks=8,
+                                                          reps=max(4, args.long_calls // 2))
+        result["long_8x1048576_streamed"]["note"] = (
+            "each row processed as 8 pieces of 2^17 steps chained through carry_in/carry_out "
+            "(the *_carry entry points); bytes are those of the whole rollout")
         wb = workloads.get("large_batch_1048576x32")
         print("[bench] timing the supplementary large-batch calls", file=sys.stderr, flush=True)
         result["large_batch_1048576x32"] = eager_workload(torch, wb, sh, lib, args.long_calls,

@@ -18,6 +18,15 @@ to the float32 0/1 form the ABI takes (one elementwise copy), non-contiguous
 inputs are made contiguous, and the call runs on the current stream (or
 `stream`).  gamma and lambda_ default to the values of the README's usage
 example.
+
+Streaming one rollout through several calls (the README's chunked fallback
+for long sequences, Kernels table, last column): every call takes
+`carry_in` [num_envs], the output just past this chunk (t = T for the
+reverse estimators, whose later chunks go first; t = -1 for traces and the
+prefix sum), and with `return_carry=True` also returns carry_out [num_envs],
+the output at the chunk's other edge -- the next call's carry_in.  V at
+t = T is `bootstrap_value`; compute_retrace also needs `next_actions` and
+`next_behaviour_probs` [num_envs] of the chunk that follows.
 """
 from __future__ import annotations
 
@@ -50,6 +59,10 @@ def _flags(t, name):
     return _device_tensor(t, name, torch.float32, flag=True)
 
 
+def _carry_out(wanted, N, device, dtype=torch.float32):
+    return torch.empty((N,), dtype=dtype, device=device) if wanted else None
+
+
 def _check_2d(t, name):
     if t.dim() != 2:
         raise ValueError(f"{name} must be a [num_envs, seq_len] tensor, got shape "
@@ -58,7 +71,8 @@ def _check_2d(t, name):
 
 
 def compute_gae(rewards, values, terminateds, gamma=0.99, lambda_=0.95, *,
-                bootstrap_value=None, truncateds=None, bootstrap_values=None, stream=None):
+                bootstrap_value=None, truncateds=None, bootstrap_values=None, carry_in=None,
+                return_carry=False, stream=None):
     """Advantages A_t = delta_t + gamma*lambda*(1 - cut_t)*A_{t+1} [N, T]
     (README, Kernels: compute_gae).  bootstrap_value [N] is V at t = T
     (None: 0); truncateds [N, T] with bootstrap_values [N, T] handle
@@ -66,57 +80,71 @@ def compute_gae(rewards, values, terminateds, gamma=0.99, lambda_=0.95, *,
     r = _device_tensor(rewards, "rewards")
     N, T = _check_2d(r, "rewards")
     out = torch.empty((N, T), dtype=torch.float32, device=r.device)
-    return rlscan.rlscan_gae(
+    co = _carry_out(return_carry, N, r.device)
+    rlscan.rlscan_gae(
         r, _device_tensor(values, "values"), _device_tensor(bootstrap_value, "bootstrap_value"),
         _flags(terminateds, "terminateds"), _flags(truncateds, "truncateds"),
         _device_tensor(bootstrap_values, "bootstrap_values"), out, float(gamma),
-        float(lambda_), stream)
+        float(lambda_), stream, carry_in=_device_tensor(carry_in, "carry_in"), carry_out=co)
+    return (out, co) if return_carry else out
 
 
 def compute_lambda_returns(rewards, values, terminateds, gamma=0.99, lambda_=0.95, *,
                            bootstrap_value=None, truncateds=None, bootstrap_values=None,
-                           stream=None):
+                           carry_in=None, return_carry=False, stream=None):
     """TD(lambda) returns [N, T] (README, Kernels: compute_lambda_returns)."""
     r = _device_tensor(rewards, "rewards")
     N, T = _check_2d(r, "rewards")
     out = torch.empty((N, T), dtype=torch.float32, device=r.device)
-    return rlscan.rlscan_lambda_returns(
+    co = _carry_out(return_carry, N, r.device)
+    rlscan.rlscan_lambda_returns(
         r, _device_tensor(values, "values"), _device_tensor(bootstrap_value, "bootstrap_value"),
         _flags(terminateds, "terminateds"), _flags(truncateds, "truncateds"),
         _device_tensor(bootstrap_values, "bootstrap_values"), out, float(gamma),
-        float(lambda_), stream)
+        float(lambda_), stream, carry_in=_device_tensor(carry_in, "carry_in"), carry_out=co)
+    return (out, co) if return_carry else out
 
 
 def compute_discounted_returns(rewards, terminateds, gamma=0.99, *, bootstrap_value=None,
-                               truncateds=None, bootstrap_values=None, stream=None):
+                               truncateds=None, bootstrap_values=None, carry_in=None,
+                               return_carry=False, stream=None):
     """Discounted reward-to-go [N, T] (README, Kernels:
     compute_discounted_returns)."""
     r = _device_tensor(rewards, "rewards")
     N, T = _check_2d(r, "rewards")
     out = torch.empty((N, T), dtype=torch.float32, device=r.device)
-    return rlscan.rlscan_discounted_returns(
+    co = _carry_out(return_carry, N, r.device)
+    rlscan.rlscan_discounted_returns(
         r, _device_tensor(bootstrap_value, "bootstrap_value"), _flags(terminateds, "terminateds"),
         _flags(truncateds, "truncateds"), _device_tensor(bootstrap_values, "bootstrap_values"),
-        out, float(gamma), stream)
+        out, float(gamma), stream, carry_in=_device_tensor(carry_in, "carry_in"), carry_out=co)
+    return (out, co) if return_carry else out
 
 
 def compute_vtrace(rewards, values, log_rhos, terminateds, gamma=0.99, rho_bar=1.0, c_bar=1.0,
-                   *, bootstrap_value=None, truncateds=None, bootstrap_values=None, stream=None):
+                   *, bootstrap_value=None, truncateds=None, bootstrap_values=None,
+                   carry_in=None, return_carry=False, stream=None):
     """V-trace targets vs and policy-gradient advantages [N, T] each, as a
-    tuple (README, Kernels: compute_vtrace).  log_rhos = log pi - log mu."""
+    tuple (README, Kernels: compute_vtrace).  log_rhos = log pi - log mu.
+    carry_in / carry_out are vs values."""
     r = _device_tensor(rewards, "rewards")
     N, T = _check_2d(r, "rewards")
     vs = torch.empty((N, T), dtype=torch.float32, device=r.device)
     pg = torch.empty((N, T), dtype=torch.float32, device=r.device)
-    return rlscan.rlscan_vtrace(
+    co = _carry_out(return_carry, N, r.device)
+    rlscan.rlscan_vtrace(
         r, _device_tensor(values, "values"), _device_tensor(bootstrap_value, "bootstrap_value"),
         _device_tensor(log_rhos, "log_rhos"), _flags(terminateds, "terminateds"),
         _flags(truncateds, "truncateds"), _device_tensor(bootstrap_values, "bootstrap_values"),
-        vs, pg, float(gamma), float(rho_bar), float(c_bar), stream)
+        vs, pg, float(gamma), float(rho_bar), float(c_bar), stream,
+        carry_in=_device_tensor(carry_in, "carry_in"), carry_out=co)
+    return (vs, pg, co) if return_carry else (vs, pg)
 
 
 def compute_retrace(rewards, next_q_values_all, next_target_probs, actions, behaviour_probs,
-                    terminateds, truncateds, gamma=0.99, lambda_=0.95, *, stream=None):
+                    terminateds, truncateds, gamma=0.99, lambda_=0.95, *, carry_in=None,
+                    next_actions=None, next_behaviour_probs=None, return_carry=False,
+                    stream=None):
     """Retrace(lambda) targets [N, T] (README, Kernels: compute_retrace).
     next_q_values_all and next_target_probs are [N, T, A] at each step's
     successor state; actions [N, T] are the taken actions (int32, or any
@@ -129,27 +157,38 @@ def compute_retrace(rewards, next_q_values_all, next_target_probs, actions, beha
     a = actions
     if isinstance(a, torch.Tensor) and a.dtype != torch.int32 and not a.dtype.is_floating_point:
         a = a.to(torch.int32)
+    na = next_actions
+    if isinstance(na, torch.Tensor) and na.dtype != torch.int32 and not na.dtype.is_floating_point:
+        na = na.to(torch.int32)
     out = torch.empty((N, T), dtype=torch.float32, device=r.device)
-    return rlscan.rlscan_retrace(
+    co = _carry_out(return_carry, N, r.device)
+    rlscan.rlscan_retrace(
         r, _device_tensor(next_q_values_all, "next_q_values_all"),
         _device_tensor(next_target_probs, "next_target_probs"),
         _device_tensor(a, "actions", torch.int32), _device_tensor(behaviour_probs,
                                                                   "behaviour_probs"),
         _flags(terminateds, "terminateds"), _flags(truncateds, "truncateds"), out,
-        float(gamma), float(lambda_), stream)
+        float(gamma), float(lambda_), stream, carry_in=_device_tensor(carry_in, "carry_in"),
+        carry_out=co, next_actions=_device_tensor(na, "next_actions", torch.int32),
+        next_behaviour_probs=_device_tensor(next_behaviour_probs, "next_behaviour_probs"))
+    return (out, co) if return_carry else out
 
 
-def compute_eligibility_traces(x, dones, gamma=0.99, lambda_=0.95, *, stream=None):
+def compute_eligibility_traces(x, dones, gamma=0.99, lambda_=0.95, *, carry_in=None,
+                               return_carry=False, stream=None):
     """Forward traces e_t = x_t + gamma*lambda*(1 - d_t)*e_{t-1} [N, T]
     (README, Kernels: compute_eligibility_traces)."""
     xx = _device_tensor(x, "x")
     N, T = _check_2d(xx, "x")
     out = torch.empty((N, T), dtype=torch.float32, device=xx.device)
-    return rlscan.rlscan_eligibility_traces(xx, _flags(dones, "dones"), out, float(gamma),
-                                            float(lambda_), stream)
+    co = _carry_out(return_carry, N, xx.device)
+    rlscan.rlscan_eligibility_traces(xx, _flags(dones, "dones"), out, float(gamma),
+                                     float(lambda_), stream,
+                                     carry_in=_device_tensor(carry_in, "carry_in"), carry_out=co)
+    return (out, co) if return_carry else out
 
 
-def compute_episodic_prefix_sum(x, dones, *, stream=None):
+def compute_episodic_prefix_sum(x, dones, *, carry_in=None, return_carry=False, stream=None):
     """Cumulative sum restarted where dones is set, exact in int64 [N, T]
     (README, Kernels: compute_episodic_prefix_sum).  x is int32; narrower
     integer dtypes are widened, int64 is refused (it would not fit)."""
@@ -160,4 +199,8 @@ def compute_episodic_prefix_sum(x, dones, *, stream=None):
     xx = _device_tensor(xx, "x", torch.int32)
     N, T = _check_2d(xx, "x")
     out = torch.empty((N, T), dtype=torch.int64, device=xx.device)
-    return rlscan.rlscan_episodic_prefix_sum(xx, _flags(dones, "dones"), out, stream)
+    co = _carry_out(return_carry, N, xx.device, torch.int64)
+    rlscan.rlscan_episodic_prefix_sum(xx, _flags(dones, "dones"), out, stream,
+                                      carry_in=_device_tensor(carry_in, "carry_in", torch.int64),
+                                      carry_out=co)
+    return (out, co) if return_carry else out

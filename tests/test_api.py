@@ -129,3 +129,94 @@ def test_usage_example_shape():
     ref = oracle.gae(rewards.numpy(), values.numpy(), terminateds.numpy(), gamma=0.99, lam=0.95)
     err = np.abs(adv.cpu().numpy().astype(np.float64) - ref) / (1 + np.abs(ref))
     assert err.max() <= 1e-4
+
+
+@pytest.mark.parametrize("estimator", ESTIMATORS)
+def test_streamed_compute_calls_match_one_call(estimator):
+    """The compute_* calls over two pieces of each row, chained through
+    carry_in / return_carry, against one call over the whole rows."""
+    w, inputs = case(estimator, N=5, T=3000, seed=23)
+    d = {k: dev(v) for k, v in inputs.items()}
+    whole = host(call(estimator, d, w))
+    T1 = 1234
+    fwd = estimator in ("eligibility_traces", "episodic_prefix_sum")
+    part = lambda lo, hi: {k: (v[:, lo:hi].contiguous() if v is not None and v.dim() >= 2
+                               else v) for k, v in d.items()}  # noqa: E731
+    g, lam = w.gamma, w.lam
+    if fwd:
+        a, b = part(0, T1), part(T1, w.T)
+        if estimator == "eligibility_traces":
+            first, c = api.compute_eligibility_traces(a["x"], a["dones"], g, lam,
+                                                      return_carry=True)
+            second = api.compute_eligibility_traces(b["x"], b["dones"], g, lam, carry_in=c)
+            got = {"traces": torch.cat([first, second], 1)}
+        else:
+            first, c = api.compute_episodic_prefix_sum(a["x"], a["dones"], return_carry=True)
+            second = api.compute_episodic_prefix_sum(b["x"], b["dones"], carry_in=c)
+            got = {"out": torch.cat([first, second], 1)}
+    else:
+        early, late = part(0, T1), part(T1, w.T)
+        vb = d["values"][:, T1].contiguous() if "values" in d else None
+        if estimator == "gae":
+            l, c = api.compute_gae(late["rewards"], late["values"], late["terminated"], g, lam,
+                                   bootstrap_value=d.get("bootstrap_value"),
+                                   truncateds=late.get("truncated"),
+                                   bootstrap_values=late.get("bootstrap_values"),
+                                   return_carry=True)
+            e = api.compute_gae(early["rewards"], early["values"], early["terminated"], g, lam,
+                                bootstrap_value=vb, truncateds=early.get("truncated"),
+                                bootstrap_values=early.get("bootstrap_values"), carry_in=c)
+            got = {"advantages": torch.cat([e, l], 1)}
+        elif estimator == "lambda_returns":
+            l, c = api.compute_lambda_returns(late["rewards"], late["values"], late["terminated"],
+                                              g, lam, bootstrap_value=d.get("bootstrap_value"),
+                                              truncateds=late.get("truncated"),
+                                              bootstrap_values=late.get("bootstrap_values"),
+                                              return_carry=True)
+            e = api.compute_lambda_returns(early["rewards"], early["values"],
+                                           early["terminated"], g, lam, bootstrap_value=vb,
+                                           truncateds=early.get("truncated"),
+                                           bootstrap_values=early.get("bootstrap_values"),
+                                           carry_in=c)
+            got = {"returns": torch.cat([e, l], 1)}
+        elif estimator == "discounted_returns":
+            l, c = api.compute_discounted_returns(late["rewards"], late["terminated"], g,
+                                                  bootstrap_value=d.get("bootstrap_value"),
+                                                  truncateds=late.get("truncated"),
+                                                  bootstrap_values=late.get("bootstrap_values"),
+                                                  return_carry=True)
+            e = api.compute_discounted_returns(early["rewards"], early["terminated"], g,
+                                               truncateds=early.get("truncated"),
+                                               bootstrap_values=early.get("bootstrap_values"),
+                                               carry_in=c)
+            got = {"returns": torch.cat([e, l], 1)}
+        elif estimator == "vtrace":
+            lv, lp, c = api.compute_vtrace(late["rewards"], late["values"], late["log_rhos"],
+                                           late["terminated"], g, w.rho_bar, w.c_bar,
+                                           bootstrap_value=d.get("bootstrap_value"),
+                                           truncateds=late.get("truncated"),
+                                           bootstrap_values=late.get("bootstrap_values"),
+                                           return_carry=True)
+            ev, ep = api.compute_vtrace(early["rewards"], early["values"], early["log_rhos"],
+                                        early["terminated"], g, w.rho_bar, w.c_bar,
+                                        bootstrap_value=vb, truncateds=early.get("truncated"),
+                                        bootstrap_values=early.get("bootstrap_values"),
+                                        carry_in=c)
+            got = {"vs": torch.cat([ev, lv], 1), "pg_advantages": torch.cat([ep, lp], 1)}
+        else:
+            l, c = api.compute_retrace(late["rewards"], late["next_q_values_all"],
+                                       late["next_target_probs"], late["actions"],
+                                       late["behaviour_probs"], late["terminated"],
+                                       late["truncated"], g, lam, return_carry=True)
+            e = api.compute_retrace(early["rewards"], early["next_q_values_all"],
+                                    early["next_target_probs"], early["actions"],
+                                    early["behaviour_probs"], early["terminated"],
+                                    early["truncated"], g, lam, carry_in=c,
+                                    next_actions=d["actions"][:, T1].contiguous(),
+                                    next_behaviour_probs=d["behaviour_probs"][:, T1].contiguous())
+            got = {"targets": torch.cat([e, l], 1)}
+    got = host(got)
+    for k in whole:
+        ref = whole[k].astype(np.float64)
+        err = np.abs(got[k].astype(np.float64) - ref) / (1 + np.abs(ref))
+        assert err.max() <= 1e-4, (k, float(err.max()))
