@@ -45,9 +45,10 @@ METRIC = ("elements/s and achieved HBM GB/s per estimator at N=4096,T=128 and lo
           "per-call µs")
 HBM_PEAK_GBS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["include/rlscan.h"] + [
-    os.path.join("linear_recurrence_scan_coefficient_amd", "csrc", f)
-    for f in ("rlscan.hip", "scan_core.hpp", "lookback.hpp", "estimators.hpp")]
+_CSRC = os.path.join("linear_recurrence_scan_coefficient_amd", "csrc")
+KERNEL_SOURCES = ["include/rlscan.h"] + sorted(
+    os.path.join(_CSRC, f) for f in os.listdir(os.path.join(ROOT, _CSRC))
+    if f.endswith((".hip", ".hpp")))
 
 
 def kernel_source_hash() -> str:

@@ -1,0 +1,262 @@
+// host.hip -- librlscan's launch planner, look-back scratch and the entry
+// points that are not estimators (status text, version, planning, launch
+// override, diagnostics), plus the two diagnostic kernels (gfx950 only).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <utility>
+
+#include "host.hpp"
+
+namespace rlscan {
+
+LaunchOverride g_override;
+
+namespace {
+std::mutex g_scratch_mutex;
+std::map<std::pair<int, uintptr_t>, std::unique_ptr<Scratch>> g_scratch;
+}  // namespace
+
+Scratch* scratch_for(int device, hipStream_t stream) {
+    std::lock_guard<std::mutex> g(g_scratch_mutex);
+    auto& slot = g_scratch[{device, reinterpret_cast<uintptr_t>(stream)}];
+    if (!slot) slot.reset(new Scratch());
+    return slot.get();
+}
+
+int ensure_capacity(Scratch* sc, hipStream_t stream, int64_t tiles) {
+    if (sc->capacity >= tiles && !sc->broken) return RLSCAN_OK;
+    int64_t cap = 1024;
+    while (cap < tiles) cap *= 2;
+    // earlier work on this stream may still read the old buffers
+    if (sc->status != nullptr && hipStreamSynchronize(stream) != hipSuccess) return RLSCAN_ERR_HIP;
+    if (sc->status != nullptr) (void)hipFree(sc->status);
+    if (sc->counter != nullptr) (void)hipFree(sc->counter);
+    sc->status = nullptr;
+    sc->counter = nullptr;
+    sc->capacity = 0;
+    void* st = nullptr;
+    void* ctr = nullptr;
+    if (hipMalloc(&st, sizeof(TileStatus) * cap) != hipSuccess) return RLSCAN_ERR_ALLOC;
+    if (hipMalloc(&ctr, 256) != hipSuccess) {
+        (void)hipFree(st);
+        return RLSCAN_ERR_ALLOC;
+    }
+    // ordered before the first kernel that uses the buffers (same stream)
+    if (hipMemsetAsync(st, 0, sizeof(TileStatus) * cap, stream) != hipSuccess ||
+        hipMemsetAsync(ctr, 0, 256, stream) != hipSuccess) {
+        (void)hipFree(st);
+        (void)hipFree(ctr);
+        return RLSCAN_ERR_HIP;
+    }
+    sc->status = static_cast<TileStatus*>(st);
+    sc->counter = static_cast<unsigned long long*>(ctr);
+    sc->capacity = cap;
+    sc->next_ticket = 0;
+    sc->epoch = 0;
+    sc->broken = false;
+    return RLSCAN_OK;
+}
+
+int auto_rounds(int est, int64_t NT) {
+    if (est == RLSCAN_EST_RETRACE) return 1;
+    if (NT <= (int64_t(1) << 20)) return 1;
+    if (NT <= (int64_t(1) << 22)) return 2;
+    return 4;
+}
+
+// Eight waves per workgroup double the tile, which halves the look-back
+// hops per element but also the workgroups that fit on a CU.  That pays for
+// the estimators whose four-round kernels need few registers (discounted
+// returns, eligibility traces, prefix sum: at most ~96 VGPRs, five waves per
+// SIMD); GAE, TD(lambda) and V-trace hold more per lane and run four waves.
+int auto_waves(int est, int rounds) {
+    if (rounds != 4) return 4;
+    return (est == RLSCAN_EST_DISCOUNTED || est == RLSCAN_EST_ELIGIBILITY ||
+            est == RLSCAN_EST_PREFIX_SUM) ? 8 : 4;
+}
+
+// `vec`: every pointer is 16-byte aligned.  Multi-round and eight-wave
+// kernels exist only for the vectorised path, Retrace always runs one round
+// of four waves, and calls with carry arguments (`carry`) four waves.
+Plan make_plan(int est, int64_t N, int64_t T, bool vec, bool carry) {
+    const int64_t NT = N * T;
+    Plan pl;
+    const int ro = g_override.rounds.load();
+    pl.rounds = ro > 0 ? ro : auto_rounds(est, NT);
+    if (!vec || est == RLSCAN_EST_RETRACE) pl.rounds = 1;
+    const int wo = g_override.waves.load();
+    pl.waves = wo > 0 ? wo : auto_waves(est, pl.rounds);
+    if (!vec || carry || est == RLSCAN_EST_RETRACE) pl.waves = 4;
+    pl.tile_elems = int64_t(kWave) * pl.waves * kChunk * pl.rounds;
+    pl.tiles = (NT + pl.tile_elems - 1) / pl.tile_elems;
+    const bool packed_ok = pl.tiles <= 1 || pl.tile_elems % T == 0;
+    const int mo = g_override.mapping.load();
+    pl.mapping = (packed_ok && mo != RLSCAN_MAP_LOOKBACK) ? RLSCAN_MAP_PACKED : RLSCAN_MAP_LOOKBACK;
+    const int64_t cap = g_override.grid_cap.load();
+    int64_t grid = pl.tiles;
+    if (cap > 0 && grid > cap) grid = cap;
+    if (grid > kMaxGrid) grid = kMaxGrid;
+    pl.grid = grid;
+    return pl;
+}
+
+// An empty kernel: the launch floor that a scan launch of the same grid
+// cannot go below.
+constexpr int kFloorThreads = 256;
+__global__ __launch_bounds__(kFloorThreads) void empty_kernel() {}
+
+// A plain streaming copy: the bandwidth a kernel that reads and writes the
+// same bytes, in the same 16-byte non-temporal accesses, can reach.  Each
+// thread moves kCopyUnroll 16-byte words, a workgroup a contiguous span.
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+__global__ __launch_bounds__(kCopyThreads) void copy_kernel(const f32x4* __restrict__ src,
+                                                            f32x4* __restrict__ dst, int64_t n) {
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kCopyThreads * kCopyUnroll + threadIdx.x;
+    f32x4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+        const int64_t i = base + static_cast<int64_t>(u) * kCopyThreads;
+        if (i < n) v[u] = __builtin_nontemporal_load(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+        const int64_t i = base + static_cast<int64_t>(u) * kCopyThreads;
+        if (i < n) __builtin_nontemporal_store(v[u], dst + i);
+    }
+}
+
+}  // namespace rlscan
+
+using namespace rlscan;
+
+extern "C" {
+
+const char* rlscan_status_string(int status) {
+    switch (status) {
+        case RLSCAN_OK: return "ok";
+        case RLSCAN_ERR_NULL: return "a required pointer is NULL";
+        case RLSCAN_ERR_SHAPE: return "invalid shape (negative size, A < 1, or more than 2^48 elements)";
+        case RLSCAN_ERR_PARAM: return "parameter out of range";
+        case RLSCAN_ERR_ALIAS: return "an output aliases an input or the other output";
+        case RLSCAN_ERR_HIP: return "HIP runtime call or kernel launch failed";
+        case RLSCAN_ERR_ALLOC: return "could not allocate the look-back scratch";
+        case RLSCAN_ERR_CAPTURE:
+            return "this shape needs the look-back mapping, which cannot be captured into a graph";
+        default: return "unknown rlscan status";
+    }
+}
+
+const char* rlscan_version(void) { return "rlscan 0.1.0 gfx950"; }
+
+int rlscan_release_scratch(void) {
+    std::lock_guard<std::mutex> g(g_scratch_mutex);
+    int prev = 0;
+    const bool have_prev = hipGetDevice(&prev) == hipSuccess;
+    int rc = RLSCAN_OK;
+    for (auto& kv : g_scratch) {
+        Scratch* sc = kv.second.get();
+        std::lock_guard<std::mutex> gs(sc->m);
+        if (sc->status == nullptr && sc->counter == nullptr) continue;
+        if (hipSetDevice(kv.first.first) != hipSuccess) {
+            rc = RLSCAN_ERR_HIP;
+            continue;
+        }
+        if (sc->status) (void)hipFree(sc->status);
+        if (sc->counter) (void)hipFree(sc->counter);
+        sc->status = nullptr;
+        sc->counter = nullptr;
+        sc->capacity = 0;
+        sc->next_ticket = 0;
+        sc->epoch = 0;
+    }
+    g_scratch.clear();
+    if (have_prev) (void)hipSetDevice(prev);
+    return rc;
+}
+
+int rlscan_plan(int estimator, int64_t N, int64_t T, int64_t A, rlscan_plan_info* info) {
+    if (info == nullptr) return RLSCAN_ERR_NULL;
+    if (estimator < RLSCAN_EST_GAE || estimator > RLSCAN_EST_PREFIX_SUM) return RLSCAN_ERR_PARAM;
+    const int rc = check_shape(N, T, A);
+    if (rc != RLSCAN_OK) return rc;
+    std::memset(info, 0, sizeof(*info));
+    info->threads = kWave * 4;
+    if (N == 0 || T == 0) return RLSCAN_OK;
+    const Plan pl = make_plan(estimator, N, T, true);
+    info->threads = kWave * pl.waves;
+    info->mapping = pl.mapping;
+    info->rounds = pl.rounds;
+    info->tile_elems = pl.tile_elems;
+    info->tiles = pl.tiles;
+    info->grid = pl.grid;
+    return RLSCAN_OK;
+}
+
+int rlscan_launch_floor(int64_t grid, hipStream_t stream) {
+    if (grid < 1 || grid > kMaxGrid) return RLSCAN_ERR_SHAPE;
+    hipLaunchKernelGGL(empty_kernel, dim3(static_cast<unsigned>(grid)), dim3(kFloorThreads), 0,
+                       stream);
+    return hipGetLastError() == hipSuccess ? RLSCAN_OK : RLSCAN_ERR_HIP;
+}
+
+int rlscan_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
+    if (bytes < 0 || (bytes & 15) != 0) return RLSCAN_ERR_SHAPE;
+    if (bytes == 0) return RLSCAN_OK;
+    if (dst == nullptr || src == nullptr) return RLSCAN_ERR_NULL;
+    if (!aligned16(dst) || !aligned16(src)) return RLSCAN_ERR_PARAM;
+    const uintptr_t d = reinterpret_cast<uintptr_t>(dst), s = reinterpret_cast<uintptr_t>(src);
+    if (d < s + static_cast<uintptr_t>(bytes) && s < d + static_cast<uintptr_t>(bytes))
+        return RLSCAN_ERR_ALIAS;
+    const int64_t n = bytes / 16;
+    const int64_t per_group = int64_t(kCopyThreads) * kCopyUnroll;
+    const int64_t grid = (n + per_group - 1) / per_group;
+    if (grid > kMaxGrid) return RLSCAN_ERR_SHAPE;
+    hipLaunchKernelGGL(copy_kernel, dim3(static_cast<unsigned>(grid)), dim3(kCopyThreads), 0,
+                       stream, static_cast<const f32x4*>(src), static_cast<f32x4*>(dst), n);
+    return hipGetLastError() == hipSuccess ? RLSCAN_OK : RLSCAN_ERR_HIP;
+}
+
+int rlscan_lookback_timeouts(uint64_t* count) {
+    if (count == nullptr) return RLSCAN_ERR_NULL;
+    *count = 0;
+    std::lock_guard<std::mutex> g(g_scratch_mutex);
+    int prev = 0;
+    const bool have_prev = hipGetDevice(&prev) == hipSuccess;
+    int rc = RLSCAN_OK;
+    for (auto& kv : g_scratch) {
+        Scratch* sc = kv.second.get();
+        std::lock_guard<std::mutex> gs(sc->m);
+        if (sc->counter == nullptr) continue;
+        unsigned int n = 0;
+        if (hipSetDevice(kv.first.first) != hipSuccess ||
+            hipStreamSynchronize(reinterpret_cast<hipStream_t>(kv.first.second)) != hipSuccess ||
+            hipMemcpy(&n, sc->counter + 1, sizeof(n), hipMemcpyDeviceToHost) != hipSuccess) {
+            rc = RLSCAN_ERR_HIP;
+            continue;
+        }
+        *count += n;
+    }
+    if (have_prev) (void)hipSetDevice(prev);
+    return rc;
+}
+
+int rlscan_set_launch_override(int mapping, int rounds, int waves, int64_t grid_cap, int flags) {
+    if (mapping < RLSCAN_MAP_AUTO || mapping > RLSCAN_MAP_LOOKBACK) return RLSCAN_ERR_PARAM;
+    if (rounds != 0 && rounds != 1 && rounds != 2 && rounds != 4) return RLSCAN_ERR_PARAM;
+    if (waves != 0 && waves != 4 && waves != 8) return RLSCAN_ERR_PARAM;
+    if (grid_cap < 0 || (flags & ~RLSCAN_FLAG_TICKETS) != 0) return RLSCAN_ERR_PARAM;
+    g_override.mapping.store(mapping);
+    g_override.rounds.store(rounds);
+    g_override.waves.store(waves);
+    g_override.grid_cap.store(grid_cap);
+    g_override.flags.store(flags);
+    return RLSCAN_OK;
+}
+
+}  // extern "C"

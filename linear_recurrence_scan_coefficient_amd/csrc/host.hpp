@@ -1,0 +1,195 @@
+// host.hpp -- host side of librlscan shared by its translation units: the
+// launch planner, the look-back scratch, argument checks, and the launch
+// path every estimator entry point takes (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <initializer_list>
+#include <mutex>
+
+#include "estimators.hpp"
+#include "lookback.hpp"
+#include "rlscan.h"
+#include "tile_kernel.hpp"
+
+namespace rlscan {
+
+
+constexpr int64_t kMaxElements = int64_t(1) << 48;
+constexpr int64_t kMaxGrid = (int64_t(1) << 23) - 1;  // grid * 512 threads < 2^32
+
+struct LaunchOverride {
+    std::atomic<int> mapping{RLSCAN_MAP_AUTO};
+    std::atomic<int> rounds{0};
+    std::atomic<int> waves{0};
+    std::atomic<int64_t> grid_cap{0};
+    std::atomic<int> flags{0};  // RLSCAN_FLAG_* bits
+};
+extern LaunchOverride g_override;
+
+struct Scratch {
+    std::mutex m;
+    TileStatus* status = nullptr;
+    unsigned long long* counter = nullptr;
+    int64_t capacity = 0;       // tiles
+    uint64_t next_ticket = 0;   // counter value at the start of the next call
+    uint64_t epoch = 0;         // tag of the last call (32-bit, 0 = none)
+    bool broken = false;        // a launch failed: counter position unknown
+};
+
+// Look-back scratch of (device, stream); created on first use.
+Scratch* scratch_for(int device, hipStream_t stream);
+// Called with sc->m held.  Makes room for `tiles` status entries.
+int ensure_capacity(Scratch* sc, hipStream_t stream, int64_t tiles);
+
+struct Plan {
+    int mapping;
+    int rounds;
+    int waves;
+    int64_t tile_elems, tiles, grid;
+};
+
+// `vec`: every pointer is 16-byte aligned; `carry`: a carry argument is given.
+Plan make_plan(int est, int64_t N, int64_t T, bool vec, bool carry = false);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool unit_interval(float x) { return x >= 0.0f && x <= 1.0f; }  // false for NaN
+inline bool positive_clip(float x) { return x > 0.0f; }                 // +inf allowed, NaN not
+
+inline int check_shape(int64_t N, int64_t T, int64_t A = 1) {
+    if (N < 0 || T < 0 || A < 1) return RLSCAN_ERR_SHAPE;
+    if (N == 0 || T == 0) return RLSCAN_OK;
+    if (N > kMaxElements / T) return RLSCAN_ERR_SHAPE;
+    if (N * T > kMaxElements / A) return RLSCAN_ERR_SHAPE;
+    return RLSCAN_OK;
+}
+
+// Outputs must not equal an input or each other; NULL (an optional output
+// not asked for) is skipped.
+inline int check_alias(std::initializer_list<const void*> outs, std::initializer_list<const void*> ins) {
+    for (const void* o : outs) {
+        if (o == nullptr) continue;
+        for (const void* i : ins)
+            if (i != nullptr && i == o) return RLSCAN_ERR_ALIAS;
+        int same = 0;
+        for (const void* o2 : outs) same += (o2 == o);
+        if (same > 1) return RLSCAN_ERR_ALIAS;
+    }
+    return RLSCAN_OK;
+}
+
+inline bool all_aligned(std::initializer_list<const void*> ptrs) {
+    for (const void* p : ptrs)
+        if (p != nullptr && !aligned16(p)) return false;
+    return true;
+}
+
+template <class E, int R, int W, bool VEC, bool CARRY>
+hipError_t launch_r(const typename E::Params& p, const Geometry& geo, const LookbackArgs& lb,
+                    const Plan& pl, hipStream_t stream) {
+    const bool lookback = pl.mapping == RLSCAN_MAP_LOOKBACK;
+    const dim3 grid(static_cast<unsigned>(geo.grid)), block(kWave * W);
+    if (lookback)
+        hipLaunchKernelGGL((scan_kernel<E, R, W, true, VEC, CARRY>), grid, block, 0, stream, p,
+                           geo, lb);
+    else
+        hipLaunchKernelGGL((scan_kernel<E, R, W, false, VEC, CARRY>), grid, block, 0, stream, p,
+                           geo, lb);
+    return hipGetLastError();
+}
+
+template <class E, int W, bool CARRY>
+hipError_t launch_w(const typename E::Params& p, const Geometry& geo, const LookbackArgs& lb,
+                    const Plan& pl, hipStream_t stream) {
+    switch (pl.rounds) {
+        case 1: return launch_r<E, 1, W, true, CARRY>(p, geo, lb, pl, stream);
+        case 2: return launch_r<E, 2, W, true, CARRY>(p, geo, lb, pl, stream);
+        default: return launch_r<E, 4, W, true, CARRY>(p, geo, lb, pl, stream);
+    }
+}
+
+// Kernels built for the carry arguments exist with four waves only (the
+// plan forces it); all others come with four or eight.
+template <class E>
+hipError_t launch_kernel(const typename E::Params& p, const Geometry& geo, const LookbackArgs& lb,
+                         const Plan& pl, bool vec, bool carry, hipStream_t stream) {
+    if (carry) {
+        if (!vec) return launch_r<E, 1, 4, false, true>(p, geo, lb, pl, stream);
+        return launch_w<E, 4, true>(p, geo, lb, pl, stream);
+    }
+    if (!vec) return launch_r<E, 1, 4, false, false>(p, geo, lb, pl, stream);
+    return pl.waves == 8 ? launch_w<E, 8, false>(p, geo, lb, pl, stream)
+                         : launch_w<E, 4, false>(p, geo, lb, pl, stream);
+}
+
+// Retrace keeps 2*4*A action values per round in LDS or registers: one
+// round of four waves only.
+template <class E>
+hipError_t launch_kernel_r1(const typename E::Params& p, const Geometry& geo,
+                            const LookbackArgs& lb, const Plan& pl, bool vec, bool carry,
+                            hipStream_t stream) {
+    if (carry)
+        return vec ? launch_r<E, 1, 4, true, true>(p, geo, lb, pl, stream)
+                   : launch_r<E, 1, 4, false, true>(p, geo, lb, pl, stream);
+    return vec ? launch_r<E, 1, 4, true, false>(p, geo, lb, pl, stream)
+               : launch_r<E, 1, 4, false, false>(p, geo, lb, pl, stream);
+}
+
+// Plans, takes the look-back scratch if needed, and launches through `fn`.
+template <class Fn>
+int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream, Fn&& fn) {
+    const Plan pl = make_plan(est, N, T, vec, carry);
+    if (pl.rounds != 1 && pl.rounds != 2 && pl.rounds != 4) return RLSCAN_ERR_PARAM;
+    if (pl.waves != 4 && pl.waves != 8) return RLSCAN_ERR_PARAM;
+    Geometry geo;
+    geo.N = N;
+    geo.T = T;
+    geo.NT = N * T;
+    geo.num_tiles = pl.tiles;
+    geo.grid = pl.grid;
+    geo.inv_T = 1.0 / static_cast<double>(T);
+    LookbackArgs lb{};
+    if (pl.mapping == RLSCAN_MAP_PACKED) {
+        return fn(geo, lb, pl) == hipSuccess ? RLSCAN_OK : RLSCAN_ERR_HIP;
+    }
+    // a captured look-back launch would replay with a stale ticket base
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &capture) != hipSuccess) return RLSCAN_ERR_HIP;
+    if (capture != hipStreamCaptureStatusNone) return RLSCAN_ERR_CAPTURE;
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return RLSCAN_ERR_HIP;
+    Scratch* sc = scratch_for(device, stream);
+    std::lock_guard<std::mutex> g(sc->m);
+    const int rc = ensure_capacity(sc, stream, pl.tiles);
+    if (rc != RLSCAN_OK) return rc;
+    // tile = blockIdx needs every tile to have its own workgroup
+    const bool tickets = pl.grid < pl.tiles || (g_override.flags.load() & RLSCAN_FLAG_TICKETS);
+    lb.use_tickets = tickets ? 1u : 0u;
+    lb.status = sc->status;
+    lb.ticket_counter = sc->counter;
+    lb.timeouts = reinterpret_cast<unsigned int*>(sc->counter + 1);
+    lb.ticket_base = sc->next_ticket;
+    if (sc->epoch == 0xffffffffull) {
+        // the 32-bit call tags are about to repeat: clear the status words
+        if (hipMemsetAsync(sc->status, 0, sizeof(TileStatus) * sc->capacity, stream) != hipSuccess)
+            return RLSCAN_ERR_HIP;
+        sc->epoch = 0;
+    }
+    lb.tag = static_cast<uint32_t>(++sc->epoch);
+    if (fn(geo, lb, pl) != hipSuccess) {
+        sc->broken = true;
+        return RLSCAN_ERR_HIP;
+    }
+    // every workgroup takes one ticket per tile it runs plus, when looping,
+    // one final ticket that finds no tile
+    if (tickets)
+        sc->next_ticket += static_cast<uint64_t>(pl.tiles) +
+                           (pl.grid >= pl.tiles ? 0u : static_cast<uint64_t>(pl.grid));
+    return RLSCAN_OK;
+}
+
+}  // namespace rlscan
