@@ -258,7 +258,7 @@ int rlscan_release_scratch(void);
 /* ---- launch planning (host only; no GPU work) ---------------------------
  * The library maps the flattened N*T elements onto tiles of
  * 256*waves*rounds consecutive elements, one workgroup of 64*waves threads
- * (waves = 4 or 8 wave64s) per tile.
+ * (waves = 1, 2, 4 or 8 wave64s; 1 and 2 with one round only) per tile.
  * mapping RLSCAN_MAP_PACKED: every tile holds whole rows (the tile size is a
  * multiple of T, or there is a single tile), no inter-workgroup traffic.
  * mapping RLSCAN_MAP_LOOKBACK: rows span tiles; carries travel between
@@ -277,7 +277,7 @@ typedef struct {
     int64_t tile_elems;  /* elements per tile = 4 * rounds * threads         */
     int64_t tiles;       /* number of tiles = ceil(N*T / tile_elems)         */
     int64_t grid;        /* workgroups launched                              */
-    int32_t threads;     /* threads per workgroup: 256 or 512                */
+    int32_t threads;     /* threads per workgroup: 64, 128, 256 or 512       */
     int32_t reserved;
 } rlscan_plan_info;
 
@@ -294,10 +294,12 @@ enum {
 /* Overrides the planner for every later call in the process (tests and
  * benchmarks).  mapping: RLSCAN_MAP_AUTO/PACKED/LOOKBACK (PACKED is only
  * honoured where it is valid); rounds: 0 = automatic, else 1, 2 or 4;
- * waves: 0 = automatic, else 4 or 8 wave64s per workgroup; grid_cap: 0 = no
- * cap, else at most this many workgroups, each looping over tiles; flags:
- * RLSCAN_FLAG_* bits.  Retrace, and any call with an input or output that
- * is not 16-byte aligned, always runs one round of 4 waves.  By default
+ * waves: 0 = automatic, else 1, 2, 4 or 8 wave64s per workgroup (1 and 2
+ * apply with one round; with more rounds 4 is used); grid_cap: 0 = no cap,
+ * else at most this many workgroups, each looping over tiles; flags:
+ * RLSCAN_FLAG_* bits.  Retrace runs one round of at most 4 waves; a call
+ * with an input or output that is not 16-byte aligned, or with carry
+ * arguments, runs 4 waves (the former one round).  By default
  * look-back tiles are ordered by workgroup index, and by tickets only when
  * workgroups loop.  Returns RLSCAN_ERR_PARAM for other values. */
 int rlscan_set_launch_override(int mapping, int rounds, int waves, int64_t grid_cap, int flags);

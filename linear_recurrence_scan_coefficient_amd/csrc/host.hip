@@ -69,20 +69,29 @@ int auto_rounds(int est, int64_t NT) {
     return 4;
 }
 
-// Eight waves per workgroup double the tile, which halves the look-back
-// hops per element but also the workgroups that fit on a CU.  That pays for
-// the estimators whose four-round kernels need few registers (discounted
-// returns, eligibility traces, prefix sum: at most ~96 VGPRs, five waves per
-// SIMD); GAE, TD(lambda) and V-trace hold more per lane and run four waves.
-int auto_waves(int est, int rounds) {
-    if (rounds != 4) return 4;
-    return (est == RLSCAN_EST_DISCOUNTED || est == RLSCAN_EST_ELIGIBILITY ||
-            est == RLSCAN_EST_PREFIX_SUM) ? 8 : 4;
+// Waves per workgroup (the tile is 256*W*R elements).
+//  - Four rounds (long inputs): eight waves double the tile, which halves
+//    the look-back hops per element but also the workgroups that fit on a
+//    CU.  That pays for the estimators whose four-round kernels need few
+//    registers (discounted returns, eligibility traces, prefix sum: at most
+//    ~96 VGPRs, five waves per SIMD); GAE, TD(lambda) and V-trace hold more
+//    per lane and run four waves.
+//  - One round (at most 2^20 elements, bound by launch and one memory round
+//    trip): the smallest tile that still holds whole rows -- more, smaller
+//    workgroups in flight.  Measured at 4096 x 128: one wave beat four by
+//    2-8 %, two waves by as much for GAE and V-trace.
+int auto_waves(int est, int rounds, int64_t T) {
+    if (rounds == 4)
+        return (est == RLSCAN_EST_DISCOUNTED || est == RLSCAN_EST_ELIGIBILITY ||
+                est == RLSCAN_EST_PREFIX_SUM) ? 8 : 4;
+    if (rounds == 1) {
+        const int first = (est == RLSCAN_EST_GAE || est == RLSCAN_EST_VTRACE) ? 2 : 1;
+        for (int w = first; w <= 2; w *= 2)
+            if ((int64_t(kWave) * w * kChunk) % T == 0) return w;
+    }
+    return 4;
 }
 
-// `vec`: every pointer is 16-byte aligned.  Multi-round and eight-wave
-// kernels exist only for the vectorised path, Retrace always runs one round
-// of four waves, and calls with carry arguments (`carry`) four waves.
 Plan make_plan(int est, int64_t N, int64_t T, bool vec, bool carry) {
     const int64_t NT = N * T;
     Plan pl;
@@ -90,8 +99,12 @@ Plan make_plan(int est, int64_t N, int64_t T, bool vec, bool carry) {
     pl.rounds = ro > 0 ? ro : auto_rounds(est, NT);
     if (!vec || est == RLSCAN_EST_RETRACE) pl.rounds = 1;
     const int wo = g_override.waves.load();
-    pl.waves = wo > 0 ? wo : auto_waves(est, pl.rounds);
-    if (!vec || carry || est == RLSCAN_EST_RETRACE) pl.waves = 4;
+    pl.waves = wo > 0 ? wo : auto_waves(est, pl.rounds, T);
+    // kernels exist for 1 and 2 waves with one round only, for 8 waves not
+    // for Retrace, and for the unaligned and carry paths with 4 waves only
+    if (pl.waves < 4 && pl.rounds != 1) pl.waves = 4;
+    if (pl.waves == 8 && est == RLSCAN_EST_RETRACE) pl.waves = 4;
+    if (!vec || carry) pl.waves = 4;
     pl.tile_elems = int64_t(kWave) * pl.waves * kChunk * pl.rounds;
     pl.tiles = (NT + pl.tile_elems - 1) / pl.tile_elems;
     const bool packed_ok = pl.tiles <= 1 || pl.tile_elems % T == 0;
@@ -249,7 +262,8 @@ int rlscan_lookback_timeouts(uint64_t* count) {
 int rlscan_set_launch_override(int mapping, int rounds, int waves, int64_t grid_cap, int flags) {
     if (mapping < RLSCAN_MAP_AUTO || mapping > RLSCAN_MAP_LOOKBACK) return RLSCAN_ERR_PARAM;
     if (rounds != 0 && rounds != 1 && rounds != 2 && rounds != 4) return RLSCAN_ERR_PARAM;
-    if (waves != 0 && waves != 4 && waves != 8) return RLSCAN_ERR_PARAM;
+    if (waves != 0 && waves != 1 && waves != 2 && waves != 4 && waves != 8)
+        return RLSCAN_ERR_PARAM;
     if (grid_cap < 0 || (flags & ~RLSCAN_FLAG_TICKETS) != 0) return RLSCAN_ERR_PARAM;
     g_override.mapping.store(mapping);
     g_override.rounds.store(rounds);

@@ -113,7 +113,7 @@ hipError_t launch_w(const typename E::Params& p, const Geometry& geo, const Look
 }
 
 // Kernels built for the carry arguments exist with four waves only (the
-// plan forces it); all others come with four or eight.
+// plan forces it); all others with 1 or 2 waves (one round), 4 or 8.
 template <class E>
 hipError_t launch_kernel(const typename E::Params& p, const Geometry& geo, const LookbackArgs& lb,
                          const Plan& pl, bool vec, bool carry, hipStream_t stream) {
@@ -122,12 +122,16 @@ hipError_t launch_kernel(const typename E::Params& p, const Geometry& geo, const
         return launch_w<E, 4, true>(p, geo, lb, pl, stream);
     }
     if (!vec) return launch_r<E, 1, 4, false, false>(p, geo, lb, pl, stream);
-    return pl.waves == 8 ? launch_w<E, 8, false>(p, geo, lb, pl, stream)
-                         : launch_w<E, 4, false>(p, geo, lb, pl, stream);
+    switch (pl.waves) {
+        case 1: return launch_r<E, 1, 1, true, false>(p, geo, lb, pl, stream);
+        case 2: return launch_r<E, 1, 2, true, false>(p, geo, lb, pl, stream);
+        case 8: return launch_w<E, 8, false>(p, geo, lb, pl, stream);
+        default: return launch_w<E, 4, false>(p, geo, lb, pl, stream);
+    }
 }
 
 // Retrace keeps 2*4*A action values per round in LDS or registers: one
-// round of four waves only.
+// round of at most four waves.
 template <class E>
 hipError_t launch_kernel_r1(const typename E::Params& p, const Geometry& geo,
                             const LookbackArgs& lb, const Plan& pl, bool vec, bool carry,
@@ -135,8 +139,12 @@ hipError_t launch_kernel_r1(const typename E::Params& p, const Geometry& geo,
     if (carry)
         return vec ? launch_r<E, 1, 4, true, true>(p, geo, lb, pl, stream)
                    : launch_r<E, 1, 4, false, true>(p, geo, lb, pl, stream);
-    return vec ? launch_r<E, 1, 4, true, false>(p, geo, lb, pl, stream)
-               : launch_r<E, 1, 4, false, false>(p, geo, lb, pl, stream);
+    if (!vec) return launch_r<E, 1, 4, false, false>(p, geo, lb, pl, stream);
+    switch (pl.waves) {
+        case 1: return launch_r<E, 1, 1, true, false>(p, geo, lb, pl, stream);
+        case 2: return launch_r<E, 1, 2, true, false>(p, geo, lb, pl, stream);
+        default: return launch_r<E, 1, 4, true, false>(p, geo, lb, pl, stream);
+    }
 }
 
 // Plans, takes the look-back scratch if needed, and launches through `fn`.
@@ -144,7 +152,8 @@ template <class Fn>
 int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream, Fn&& fn) {
     const Plan pl = make_plan(est, N, T, vec, carry);
     if (pl.rounds != 1 && pl.rounds != 2 && pl.rounds != 4) return RLSCAN_ERR_PARAM;
-    if (pl.waves != 4 && pl.waves != 8) return RLSCAN_ERR_PARAM;
+    if (pl.waves != 1 && pl.waves != 2 && pl.waves != 4 && pl.waves != 8)
+        return RLSCAN_ERR_PARAM;
     Geometry geo;
     geo.N = N;
     geo.T = T;

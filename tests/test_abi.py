@@ -120,13 +120,22 @@ def test_other_entry_points_argument_checks(lib):
 def test_plan_mapping_choice(lib):
     from linear_recurrence_scan_coefficient_amd import rlscan
     rlscan.rlscan_set_launch_override()
-    # whole rows per tile: packed, no inter-workgroup traffic
+    # whole rows per tile: packed, no inter-workgroup traffic; one round
+    # takes the smallest tile that holds whole rows (two waves for GAE and
+    # V-trace, one for the others)
     p = rlscan.rlscan_plan("gae", 4096, 128)
     assert p["mapping"] == rlscan.MAP_PACKED and p["rounds"] == 1
-    assert p["tile_elems"] == 1024 and p["tiles"] == 512 and p["grid"] == 512
-    assert p["threads"] == 256
+    assert p["tile_elems"] == 512 and p["tiles"] == 1024 and p["grid"] == 1024
+    assert p["threads"] == 128
+    p = rlscan.rlscan_plan("episodic_prefix_sum", 4096, 128)
+    assert p["threads"] == 64 and p["tile_elems"] == 256 and p["tiles"] == 2048
+    assert rlscan.rlscan_plan("retrace", 4096, 128, 6)["threads"] == 64
     assert rlscan.rlscan_plan("gae", 16384, 32)["mapping"] == rlscan.MAP_PACKED
-    assert rlscan.rlscan_plan("gae", 64, 512)["tiles"] == 32
+    p = rlscan.rlscan_plan("gae", 64, 512)
+    assert p["tiles"] == 64 and p["threads"] == 128
+    assert rlscan.rlscan_plan("eligibility_traces", 64, 512)["threads"] == 128
+    # rows that no small tile holds whole keep four waves
+    assert rlscan.rlscan_plan("gae", 1024, 1024)["threads"] == 256
     # rows longer than a tile, or rows that do not divide it: look-back
     assert rlscan.rlscan_plan("gae", 64, 8192)["mapping"] == rlscan.MAP_LOOKBACK
     assert rlscan.rlscan_plan("gae", 5, 1000)["mapping"] == rlscan.MAP_LOOKBACK
@@ -155,6 +164,12 @@ def test_plan_mapping_choice(lib):
     assert p["threads"] == 512 and p["tile_elems"] == 2048 and p["tiles"] == 256
     assert p["mapping"] == rlscan.MAP_PACKED
     assert rlscan.rlscan_plan("retrace", 4096, 128, 6)["threads"] == 256
+    # one or two waves exist with one round only
+    rlscan.rlscan_set_launch_override(rounds=2, waves=1)
+    assert rlscan.rlscan_plan("gae", 4096, 128)["threads"] == 256
+    rlscan.rlscan_set_launch_override(rounds=1, waves=1)
+    p = rlscan.rlscan_plan("vtrace", 4096, 128)
+    assert p["threads"] == 64 and p["tiles"] == 2048
     rlscan.rlscan_set_launch_override()
     with pytest.raises(rlscan.RlscanError):
         rlscan.rlscan_set_launch_override(rounds=3)

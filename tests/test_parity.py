@@ -74,10 +74,13 @@ MAPPINGS = {
 }
 
 
+# (rounds, waves) pairs that have kernels: 1 and 2 waves with one round
+SHAPES_RW = [(1, 1), (1, 2), (1, 4), (1, 8), (2, 4), (2, 8), (4, 4), (4, 8)]
+
+
 @pytest.mark.parametrize("estimator", ESTIMATORS)
 @pytest.mark.parametrize("mapping", list(MAPPINGS))
-@pytest.mark.parametrize("rounds", [1, 2, 4])
-@pytest.mark.parametrize("waves", [4, 8])
+@pytest.mark.parametrize("rounds,waves", SHAPES_RW, ids=[f"R{r}W{w}" for r, w in SHAPES_RW])
 def test_mappings_and_rounds(estimator, mapping, rounds, waves):
     m, flags = MAPPINGS[mapping]
     rlscan.rlscan_set_launch_override(m, rounds, waves, 0, flags)
@@ -89,7 +92,7 @@ def test_mappings_and_rounds(estimator, mapping, rounds, waves):
 
 @pytest.mark.parametrize("estimator", ESTIMATORS)
 @pytest.mark.parametrize("mapping", list(MAPPINGS))
-@pytest.mark.parametrize("waves", [4, 8])
+@pytest.mark.parametrize("waves", [1, 4, 8])
 def test_grid_capped_loops(estimator, mapping, waves):
     m, flags = MAPPINGS[mapping]
     rlscan.rlscan_set_launch_override(m, 0, waves, 13, flags)
