@@ -61,6 +61,12 @@
  *             allocated on first need and grown when a call needs more; it is
  *             released by rlscan_release_scratch().  Calls that use it from
  *             several host threads on one stream are serialised internally.
+ *             Look-back launches of one device are also ordered across
+ *             streams: such a launch on a stream other than the previous
+ *             one's waits (on the GPU, through an event) for the previous
+ *             look-back launch, so two of them never run at once and hold
+ *             slots the other's tiles need.  Packed launches are not
+ *             ordered.
  * Graphs      Calls whose tiles hold whole rows (the packed mapping, see
  *             rlscan_plan) launch one kernel and nothing else, and may be
  *             captured into a HIP graph.  A call that needs the look-back

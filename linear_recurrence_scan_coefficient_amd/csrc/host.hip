@@ -19,7 +19,22 @@ LaunchOverride g_override;
 namespace {
 std::mutex g_scratch_mutex;
 std::map<std::pair<int, uintptr_t>, std::unique_ptr<Scratch>> g_scratch;
+std::mutex g_order_mutex;
+std::map<int, std::unique_ptr<LaunchOrder>> g_order;
 }  // namespace
+
+// Created with its event on first use (the event records no timing).
+LaunchOrder* launch_order(int device) {
+    std::lock_guard<std::mutex> g(g_order_mutex);
+    auto& slot = g_order[device];
+    if (!slot) {
+        std::unique_ptr<LaunchOrder> o(new LaunchOrder());
+        if (hipEventCreateWithFlags(&o->last, hipEventDisableTiming) != hipSuccess)
+            return nullptr;
+        slot = std::move(o);
+    }
+    return slot.get();
+}
 
 Scratch* scratch_for(int device, hipStream_t stream) {
     std::lock_guard<std::mutex> g(g_scratch_mutex);

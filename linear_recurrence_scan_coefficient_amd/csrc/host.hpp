@@ -42,6 +42,21 @@ struct Scratch {
 
 // Look-back scratch of (device, stream); created on first use.
 Scratch* scratch_for(int device, hipStream_t stream);
+
+// Order of the look-back launches of one device across streams.  A look-back
+// workgroup waits on lower tiles of its own launch; one launch always makes
+// progress because each XCD dispatches its workgroups in index order.  Two
+// look-back launches running at once on different streams could each hold
+// slots that the other's undispatched tiles need, so a look-back launch on a
+// stream other than the previous one's first waits for that launch (an event
+// recorded after every look-back launch).  Packed launches are not ordered.
+struct LaunchOrder {
+    std::mutex m;
+    hipEvent_t last = nullptr;          // recorded after the latest launch
+    hipStream_t last_stream = nullptr;
+    bool any = false;
+};
+LaunchOrder* launch_order(int device);
 // Called with sc->m held.  Makes room for `tiles` status entries.
 int ensure_capacity(Scratch* sc, hipStream_t stream, int64_t tiles);
 
@@ -189,10 +204,19 @@ int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream,
         sc->epoch = 0;
     }
     lb.tag = static_cast<uint32_t>(++sc->epoch);
+    LaunchOrder* order = launch_order(device);
+    if (order == nullptr) return RLSCAN_ERR_HIP;
+    std::lock_guard<std::mutex> go(order->m);
+    if (order->any && order->last_stream != stream &&
+        hipStreamWaitEvent(stream, order->last, 0) != hipSuccess)
+        return RLSCAN_ERR_HIP;
     if (fn(geo, lb, pl) != hipSuccess) {
         sc->broken = true;
         return RLSCAN_ERR_HIP;
     }
+    if (hipEventRecord(order->last, stream) != hipSuccess) return RLSCAN_ERR_HIP;
+    order->last_stream = stream;
+    order->any = true;
     // every workgroup takes one ticket per tile it runs plus, when looping,
     // one final ticket that finds no tile
     if (tickets)

@@ -282,3 +282,28 @@ def test_lookback_launch_refuses_capture():
             device.call("gae", d, out, w)
     assert err.value.status == rlscan.RLSCAN_ERR_CAPTURE
     torch.cuda.synchronize()
+
+
+def test_lookback_calls_on_two_streams_without_host_synchronisation():
+    """Look-back calls alternating between two streams with no
+    synchronisation between them: the library orders look-back launches
+    across streams, so every call is correct and no wait times out."""
+    rlscan.rlscan_set_launch_override(rlscan.MAP_LOOKBACK)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    jobs = []
+    for i in range(12):
+        est = ("gae", "episodic_prefix_sum", "vtrace")[i % 3]
+        w, inputs = case(est, 4, 200000 + 1000 * i, seed=300 + i)
+        d = device.upload(inputs)
+        out = device.alloc_outputs(est, w.N, w.T)
+        jobs.append((est, w, inputs, d, out))
+    torch.cuda.synchronize()
+    for i, (est, w, inputs, d, out) in enumerate(jobs):
+        with torch.cuda.stream(streams[i % 2]):
+            device.call(est, d, out, w)
+    torch.cuda.synchronize()
+    for i, (est, w, inputs, d, out) in enumerate(jobs):
+        print(f"[parity] two streams, call {i}: {est} {w.N}x{w.T}", flush=True)
+        assert_parity({k: v.cpu().numpy() for k, v in out.items()},
+                      oracle_outputs(est, inputs, w), f"two streams call {i}")
+    assert rlscan.rlscan_lookback_timeouts() == 0
