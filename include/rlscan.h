@@ -65,8 +65,10 @@
  *             streams: such a launch on a stream other than the previous
  *             one's waits (on the GPU, through an event) for the previous
  *             look-back launch, so two of them never run at once and hold
- *             slots the other's tiles need.  Packed launches are not
- *             ordered.
+ *             slots the other's tiles need.  The event is recorded only once
+ *             look-back launches have come from more than one stream of the
+ *             device (a stream used for them must then stay alive while
+ *             later calls are enqueued).  Packed launches are not ordered.
  * Graphs      Calls whose tiles hold whole rows (the packed mapping, see
  *             rlscan_plan) launch one kernel and nothing else, and may be
  *             captured into a HIP graph.  A call that needs the look-back

@@ -48,13 +48,17 @@ Scratch* scratch_for(int device, hipStream_t stream);
 // progress because each XCD dispatches its workgroups in index order.  Two
 // look-back launches running at once on different streams could each hold
 // slots that the other's undispatched tiles need, so a look-back launch on a
-// stream other than the previous one's first waits for that launch (an event
-// recorded after every look-back launch).  Packed launches are not ordered.
+// stream other than the previous one's first waits for that launch.  While
+// one stream does all the look-back launches of a device nothing is recorded
+// (an event per launch costs ~3 us of GPU time between back-to-back long
+// calls); from the first launch on another stream on, an event is recorded
+// after every look-back launch.  Packed launches are not ordered.
 struct LaunchOrder {
     std::mutex m;
     hipEvent_t last = nullptr;          // recorded after the latest launch
     hipStream_t last_stream = nullptr;
-    bool any = false;
+    bool any = false;                   // a look-back launch has happened
+    bool multi = false;                 // launches came from several streams
 };
 LaunchOrder* launch_order(int device);
 // Called with sc->m held.  Makes room for `tiles` status entries.
@@ -207,14 +211,22 @@ int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream,
     LaunchOrder* order = launch_order(device);
     if (order == nullptr) return RLSCAN_ERR_HIP;
     std::lock_guard<std::mutex> go(order->m);
-    if (order->any && order->last_stream != stream &&
-        hipStreamWaitEvent(stream, order->last, 0) != hipSuccess)
-        return RLSCAN_ERR_HIP;
+    if (order->any && order->last_stream != stream) {
+        if (!order->multi) {
+            // first switch: the event covers everything enqueued so far on
+            // the previous stream, its latest look-back launch included
+            if (hipEventRecord(order->last, order->last_stream) != hipSuccess)
+                return RLSCAN_ERR_HIP;
+            order->multi = true;
+        }
+        if (hipStreamWaitEvent(stream, order->last, 0) != hipSuccess) return RLSCAN_ERR_HIP;
+    }
     if (fn(geo, lb, pl) != hipSuccess) {
         sc->broken = true;
         return RLSCAN_ERR_HIP;
     }
-    if (hipEventRecord(order->last, stream) != hipSuccess) return RLSCAN_ERR_HIP;
+    if (order->multi && hipEventRecord(order->last, stream) != hipSuccess)
+        return RLSCAN_ERR_HIP;
     order->last_stream = stream;
     order->any = true;
     // every workgroup takes one ticket per tile it runs plus, when looping,
