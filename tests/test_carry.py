@@ -251,3 +251,75 @@ def test_chained_chunks_match_the_whole_rollout(estimator):
               for k, parts in outs.items()}
     want = {k: v for k, v in whole.items() if k != "carry_out"}
     assert_parity(result, want, f"chained {estimator}")
+
+
+@pytest.mark.parametrize("estimator", ESTIMATORS)
+def test_carry_with_misaligned_pointers(estimator):
+    """Every [N, T] input and output offset by one element (the scalar-load
+    path, which has its own carry kernels)."""
+    N, T = 21, 700
+    w, d, rng = case(estimator, N, T, seed=91)
+    force_edge_flags(estimator, d, T)
+    carry = carry_inputs(estimator, d, N, rng)
+    want = oracle_call(estimator, d, w, carry)
+
+    def shifted(a):
+        if a is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
+        view = buf[1:].view(t.shape)
+        view.copy_(t.cuda())
+        return view
+
+    t = {k: (shifted(v) if isinstance(v, np.ndarray) and v.ndim >= 2 else dev(v))
+         for k, v in d.items()}
+    c = {k: dev(v) for k, v in carry.items()}
+
+    def out2(dtype=torch.float32):
+        return torch.empty(N * T + 1, dtype=dtype, device="cuda")[1:].view(N, T)
+
+    co = torch.empty(N, dtype=torch.int64 if estimator == "episodic_prefix_sum" else torch.float32,
+                     device="cuda")
+    ci = c.get("carry_in")
+    if estimator in ("gae", "lambda_returns"):
+        out = out2()
+        fn = rlscan.rlscan_gae if estimator == "gae" else rlscan.rlscan_lambda_returns
+        fn(t["rewards"], t["values"], t.get("bootstrap_value"), t["terminated"],
+           t.get("truncated"), t.get("bootstrap_values"), out, w.gamma, w.lam, carry_in=ci,
+           carry_out=co)
+        got = {"advantages" if estimator == "gae" else "returns": out}
+    elif estimator == "discounted_returns":
+        out = out2()
+        rlscan.rlscan_discounted_returns(t["rewards"], t.get("bootstrap_value"), t["terminated"],
+                                         t.get("truncated"), t.get("bootstrap_values"), out,
+                                         w.gamma, carry_in=ci, carry_out=co)
+        got = {"returns": out}
+    elif estimator == "vtrace":
+        vs, pg = out2(), out2()
+        rlscan.rlscan_vtrace(t["rewards"], t["values"], t.get("bootstrap_value"), t["log_rhos"],
+                             t["terminated"], t.get("truncated"), t.get("bootstrap_values"), vs,
+                             pg, w.gamma, w.rho_bar, w.c_bar, carry_in=ci, carry_out=co)
+        got = {"vs": vs, "pg_advantages": pg}
+    elif estimator == "retrace":
+        out = out2()
+        rlscan.rlscan_retrace(t["rewards"], t["next_q_values_all"], t["next_target_probs"],
+                              t["actions"], t["behaviour_probs"], t["terminated"],
+                              t["truncated"], out, w.gamma, w.lam, carry_in=ci, carry_out=co,
+                              next_actions=c.get("next_actions"),
+                              next_behaviour_probs=c.get("next_behaviour_probs"))
+        got = {"targets": out}
+    elif estimator == "eligibility_traces":
+        out = out2()
+        rlscan.rlscan_eligibility_traces(t["x"], t["dones"], out, w.gamma, w.lam, carry_in=ci,
+                                         carry_out=co)
+        got = {"traces": out}
+    else:
+        out = out2(torch.int64)
+        rlscan.rlscan_episodic_prefix_sum(t["x"], t["dones"], out, carry_in=ci, carry_out=co)
+        got = {"out": out}
+    got["carry_out"] = co
+    torch.cuda.synchronize()
+    print(f"[carry] misaligned {estimator}", flush=True)
+    assert_parity({k: v.cpu().numpy() for k, v in got.items()}, want,
+                  f"carry misaligned {estimator}")
