@@ -61,7 +61,7 @@ def load_library(path: str = _LIB_PATH, rebuild: bool = False):
     lib.oracle_lambda_returns.restype = None
     lib.oracle_discounted_returns.argtypes = [_i64, _i64, _f32] + [_f32p] * 6 + [_f64p, _f64p]
     lib.oracle_discounted_returns.restype = None
-    lib.oracle_vtrace.argtypes = ([_i64, _i64, _f32, _f32, _f32] + [_f32p] * 8
+    lib.oracle_vtrace.argtypes = ([_i64, _i64, _f32, _f32, _f32, _f32, _f32] + [_f32p] * 8
                                   + [_f64p, _f64p, _f64p])
     lib.oracle_vtrace.restype = None
     lib.oracle_retrace.argtypes = ([_i64, _i64, _i64, _f32, _f32, _f32p, _f32p, _f32p, _i32p]
@@ -72,6 +72,9 @@ def load_library(path: str = _LIB_PATH, rebuild: bool = False):
     lib.oracle_eligibility_traces.restype = None
     lib.oracle_episodic_prefix_sum.argtypes = [_i64, _i64, _i32p, _f32p, _i64p, _i64p, _i64p]
     lib.oracle_episodic_prefix_sum.restype = None
+    lib.oracle_episodic_prefix_sum_float.argtypes = [_i64, _i64, _f32p, _f32p, _f32p, _f64p,
+                                                     _f64p]
+    lib.oracle_episodic_prefix_sum_float.restype = None
     if path == _LIB_PATH:
         _lib = lib
     return lib
@@ -205,9 +208,11 @@ def discounted_returns(rewards, terminated, *, gamma, bootstrap_value=None, trun
 
 def vtrace(rewards, values, log_rhos, terminated, *, gamma, rho_bar=1.0, c_bar=1.0,
            bootstrap_value=None, truncated=None, bootstrap_values=None, carry_in=None,
-           return_carry=False, lib=None):
+           return_carry=False, lam=1.0, rho_bar_pg=None, lib=None):
     """Returns (vs, pg_advantages), both float64 [N, T] (and carry_out, the
-    vs at t = 0, with return_carry); carry_in is vs at t = T."""
+    vs at t = 0, with return_carry); carry_in is vs at t = T.  lam scales
+    every trace coefficient c_t; rho_bar_pg (None: rho_bar) truncates the
+    policy-gradient weight."""
     lib = lib or load_library()
     N, T, r, v, bv, term, trunc, bvals = _reverse_inputs(
         rewards, values, bootstrap_value, terminated, truncated, bootstrap_values)
@@ -215,7 +220,9 @@ def vtrace(rewards, values, log_rhos, terminated, *, gamma, rho_bar=1.0, c_bar=1
     vs = np.empty((N, T), np.float64)
     pg = np.empty((N, T), np.float64)
     co = np.empty(N, np.float64)
-    lib.oracle_vtrace(N, T, _param(gamma), _param(rho_bar), _param(c_bar), _ptr(r), _ptr(v),
+    pg_clip = rho_bar if rho_bar_pg is None else rho_bar_pg
+    lib.oracle_vtrace(N, T, _param(gamma), _param(lam), _param(rho_bar), _param(c_bar),
+                      _param(pg_clip), _ptr(r), _ptr(v),
                       _ptr(bv), _ptr(lr), _ptr(term), _ptr(trunc), _ptr(bvals),
                       _ptr(_carry_in(carry_in, N)), vs.ctypes.data_as(_f64p),
                       pg.ctypes.data_as(_f64p), co.ctypes.data_as(_f64p))
@@ -289,4 +296,18 @@ def episodic_prefix_sum(x, dones, *, carry_in=None, return_carry=False, lib=None
     lib.oracle_episodic_prefix_sum(N, T, xs.ctypes.data_as(_i32p), _ptr(d),
                                    ci.ctypes.data_as(_i64p) if ci is not None else None,
                                    out.ctypes.data_as(_i64p), co.ctypes.data_as(_i64p))
+    return _with_carry(out, co, return_carry)
+
+
+def episodic_prefix_sum_float(x, dones, *, carry_in=None, return_carry=False, lib=None):
+    """Float-valued episodic prefix sum, float64 [N, T]; carry_in is y at
+    t = -1, carry_out y at t = T - 1."""
+    lib = lib or load_library()
+    N, T = _shape2(x)
+    xs = _f32_in(x, (N, T))
+    d = _f32_in(dones, (N, T))
+    out = np.empty((N, T), np.float64)
+    co = np.empty(N, np.float64)
+    lib.oracle_episodic_prefix_sum_float(N, T, _ptr(xs), _ptr(d), _ptr(_carry_in(carry_in, N)),
+                                         out.ctypes.data_as(_f64p), co.ctypes.data_as(_f64p))
     return _with_carry(out, co, return_carry)

@@ -248,21 +248,29 @@ void oracle_discounted_returns(int64_t N, int64_t T, float gamma_f,
 /* ------------------------------------------------------------------------ *
  * V-trace   [README, Kernels table, compute_vtrace row: importance-weighted
  * targets and advantages; Espeholt et al. 2018, IMPALA, the recursive form
- * of the v-trace target and the policy-gradient advantage]
- *     rho_t = min(rho_bar, exp(log_rho_t)),  c_t = min(c_bar, exp(log_rho_t))
+ * of the v-trace target and the policy-gradient advantage, and the same
+ * paper's variant that multiplies every trace coefficient c_i by a factor
+ * lambda in [0, 1]]
+ *     ratio_t = exp(log_rho_t)
+ *     rho_t = min(rho_bar, ratio_t),  c_t = lambda * min(c_bar, ratio_t)
  *     delta_t = rho_t * (r_t + gamma * Vhat_{t+1} - V_t)
  *     u_t  = delta_t + (cut_t ? 0 : gamma * c_t * u_{t+1}),   vs_t = V_t + u_t
- *     pg_t = rho_t * (r_t + gamma * (cut_t ? Vhat_{t+1} : vs_{t+1}) - V_t)
- * log_rho_t is log pi(a_t|x_t) - log mu(a_t|x_t).
+ *     pg_t = min(rho_bar_pg, ratio_t)
+ *            * (r_t + gamma * (cut_t ? Vhat_{t+1} : vs_{t+1}) - V_t)
+ * log_rho_t is log pi(a_t|x_t) - log mu(a_t|x_t).  The plain form of the
+ * paper is lambda = 1 and rho_bar_pg = rho_bar (one truncation level for
+ * the target and the policy-gradient weight); a separate rho_bar_pg is the
+ * option implementations commonly give the policy-gradient weight.
  * ------------------------------------------------------------------------ */
-void oracle_vtrace(int64_t N, int64_t T, float gamma_f, float rho_bar_f, float c_bar_f,
-                   const float* rewards, const float* values,
+void oracle_vtrace(int64_t N, int64_t T, float gamma_f, float lambda_f, float rho_bar_f,
+                   float c_bar_f, float rho_bar_pg_f, const float* rewards, const float* values,
                    const float* bootstrap_value, const float* log_rhos,
                    const float* terminated, const float* truncated,
                    const float* bootstrap_values, const float* carry_in, double* vs,
                    double* pg_advantages, double* carry_out)
 {
-    const double gamma = gamma_f, rho_bar = rho_bar_f, c_bar = c_bar_f;
+    const double gamma = gamma_f, lambda = lambda_f, rho_bar = rho_bar_f, c_bar = c_bar_f;
+    const double rho_bar_pg = rho_bar_pg_f;
     const int continues = carry_in != NULL;
     for (int64_t n = 0; n < N; ++n) {
         /* carry_in is vs_T; V_T is bootstrap_value[n] (or 0) */
@@ -273,7 +281,8 @@ void oracle_vtrace(int64_t N, int64_t T, float gamma_f, float rho_bar_f, float c
             const int64_t i = n * T + t;
             const double ratio = exp((double)log_rhos[i]);
             const double rho = ratio < rho_bar ? ratio : rho_bar;
-            const double c = ratio < c_bar ? ratio : c_bar;
+            const double c = lambda * (ratio < c_bar ? ratio : c_bar);
+            const double rho_pg = ratio < rho_bar_pg ? ratio : rho_bar_pg;
             const double v_next = next_state_value(values, bootstrap_value, terminated,
                                                    truncated, bootstrap_values, n, t, T);
             const int cut = is_cut(terminated, truncated, i, t, T, continues);
@@ -282,7 +291,7 @@ void oracle_vtrace(int64_t N, int64_t T, float gamma_f, float rho_bar_f, float c
             const double vs_t = (double)values[i] + u;
             const double follow = cut ? v_next : next_vs;
             vs[i] = vs_t;
-            pg_advantages[i] = rho * ((double)rewards[i] + gamma * follow - (double)values[i]);
+            pg_advantages[i] = rho_pg * ((double)rewards[i] + gamma * follow - (double)values[i]);
             next_u = u;
             next_vs = vs_t;
         }
@@ -386,6 +395,28 @@ void oracle_episodic_prefix_sum(int64_t N, int64_t T, const int32_t* x,
         for (int64_t t = 0; t < T; ++t) {
             const int64_t i = n * T + t;
             const int64_t y = (int64_t)x[i] + (is_set(dones, i) ? 0 : prev);
+            out[i] = y;
+            prev = y;
+        }
+        if (carry_out) carry_out[n] = out[n * T + T - 1];
+    }
+}
+
+/* ------------------------------------------------------------------------ *
+ * Episodic prefix sum of float values   [README, Kernels table,
+ * compute_episodic_prefix_sum row: cumulative sum that restarts where the
+ * done mask is set], for float inputs; float64 accumulator
+ *     y_t = x_t + (d_t ? 0 : y_{t-1}),   y_{-1} = 0
+ * ------------------------------------------------------------------------ */
+void oracle_episodic_prefix_sum_float(int64_t N, int64_t T, const float* x,
+                                      const float* dones, const float* carry_in, double* out,
+                                      double* carry_out)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        double prev = carry_of(carry_in, n);  /* y_{-1} */
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t i = n * T + t;
+            const double y = (double)x[i] + (is_set(dones, i) ? 0.0 : prev);
             out[i] = y;
             prev = y;
         }

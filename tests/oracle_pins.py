@@ -339,7 +339,9 @@ def pin_discounted_lfilter(lib):
 
 
 # ------------------------------------------------------------ V-trace
-def vtrace_brute(d, gamma, rho_bar, c_bar):
+def vtrace_brute(d, gamma, rho_bar, c_bar, lam=1.0, rho_bar_pg=None):
+    """IMPALA's explicit sum for vs (trace coefficients lambda*min(c_bar, ratio))
+    and the policy-gradient advantage with weight min(rho_bar_pg, ratio)."""
     g = fr(f32(gamma))
     N, T = d["rewards"].shape
     def clip(level, n, t):
@@ -347,7 +349,9 @@ def vtrace_brute(d, gamma, rho_bar, c_bar):
         return ratio if math.isinf(level) else min(fr(f32(level)), ratio)
 
     rho = [[clip(rho_bar, n, t) for t in range(T)] for n in range(N)]
-    c = [[clip(c_bar, n, t) for t in range(T)] for n in range(N)]
+    c = [[fr(f32(lam)) * clip(c_bar, n, t) for t in range(T)] for n in range(N)]
+    pg_level = rho_bar if rho_bar_pg is None else rho_bar_pg
+    rho_pg = [[clip(pg_level, n, t) for t in range(T)] for n in range(N)]
     vs = [[None] * T for _ in range(N)]
     for n in range(N):
         for s in range(T):
@@ -363,8 +367,8 @@ def vtrace_brute(d, gamma, rho_bar, c_bar):
     for n in range(N):
         for s in range(T):
             follow = vhat(d, n, s) if cut(d, n, s) else vs[n][s + 1]
-            pg[n, s] = float(rho[n][s] * (fr(d["rewards"][n, s]) + g * follow
-                                          - fr(d["values"][n, s])))
+            pg[n, s] = float(rho_pg[n][s] * (fr(d["rewards"][n, s]) + g * follow
+                                             - fr(d["values"][n, s])))
     return np.array([[float(v) for v in row] for row in vs]), pg
 
 
@@ -410,6 +414,72 @@ def pin_vtrace_no_trace_is_one_step(lib):
     vnext[:, :-1] = d["values"][:, 1:]
     vnext = np.where(cut_array(d), vhat_array(d), vnext)
     close(vs, d["values"] + rho * (d["rewards"] + g * vnext - d["values"]))
+
+
+def _vtrace_inputs(seed, scale=0.7, **kw):
+    d = small_value_inputs(seed, **kw)
+    d["log_rhos"] = (scale * np.random.default_rng(seed).standard_normal(
+        d["rewards"].shape)).astype(np.float32)
+    return d
+
+
+def pin_vtrace_lambda_and_pg_clip_brute(lib):
+    """IMPALA's lambda variant and a separate policy-gradient truncation
+    level, against the explicit sum in exact rationals."""
+    for seed, trunc, (rho_bar, c_bar, lam, rho_bar_pg) in (
+            (45, True, (1.0, 1.0, 0.8, 0.5)),
+            (46, False, (1.5, 0.9, 0.3, math.inf)),
+            (47, True, (math.inf, 1.2, 0.95, 2.0))):
+        d = _vtrace_inputs(seed, with_trunc=trunc)
+        vs, pg = oracle.vtrace(d["rewards"], d["values"], d["log_rhos"], d["terminated"],
+                               gamma=0.9, rho_bar=rho_bar, c_bar=c_bar, lam=lam,
+                               rho_bar_pg=rho_bar_pg, lib=lib, **oracle_kw(d))
+        want_vs, want_pg = vtrace_brute(d, 0.9, rho_bar, c_bar, lam, rho_bar_pg)
+        close(vs, want_vs)
+        close(pg, want_pg)
+
+
+def pin_vtrace_lambda_zero_is_one_step(lib):
+    """lambda = 0 switches the traces off: vs_t = V_t + rho_t*(r_t + gamma*Vhat_{t+1} - V_t)."""
+    d = _vtrace_inputs(48, 0.5, N=3, T=30)
+    g = f32(0.9)
+    vs, _ = oracle.vtrace(d["rewards"], d["values"], d["log_rhos"], d["terminated"],
+                          gamma=0.9, rho_bar=1.0, c_bar=1.0, lam=0.0, lib=lib, **oracle_kw(d))
+    rho = np.minimum(1.0, np.exp(d["log_rhos"].astype(np.float64)))
+    vnext = np.zeros_like(vs)
+    vnext[:, :-1] = d["values"][:, 1:]
+    vnext = np.where(cut_array(d), vhat_array(d), vnext)
+    close(vs, d["values"] + rho * (d["rewards"] + g * vnext - d["values"]))
+
+
+def pin_vtrace_lambda_scales_c_bar(lib):
+    """Where every ratio is at least c_bar, c_t = lambda*c_bar for every t, which
+    is the plain form with truncation level lambda*c_bar (lambda = 0.5, so the
+    product is exact in float32)."""
+    d = _vtrace_inputs(49, 0.5, N=3, T=60)
+    d["log_rhos"] = (np.abs(d["log_rhos"]) + np.float32(math.log(0.8) + 1e-3)).astype(
+        np.float32)
+    kw = dict(gamma=0.95, rho_bar=1.0, lib=lib, **oracle_kw(d))
+    args = (d["rewards"], d["values"], d["log_rhos"], d["terminated"])
+    vs_l, pg_l = oracle.vtrace(*args, c_bar=0.8, lam=0.5, **kw)
+    vs_c, pg_c = oracle.vtrace(*args, c_bar=0.4, **kw)
+    close(vs_l, vs_c, 1e-14)
+    close(pg_l, pg_c, 1e-14)
+    vs_1, _ = oracle.vtrace(*args, c_bar=0.8, **kw)
+    assert np.abs(vs_1 - vs_l).max() > 1e-3  # lambda does act
+
+
+def pin_vtrace_pg_clip_only_rescales_pg(lib):
+    """rho_bar_pg leaves vs unchanged and multiplies each pg_t by
+    min(rho_bar_pg, ratio_t) / min(rho_bar, ratio_t)."""
+    d = _vtrace_inputs(50, 1.0, N=3, T=40)
+    args = (d["rewards"], d["values"], d["log_rhos"], d["terminated"])
+    kw = dict(gamma=0.97, rho_bar=1.0, c_bar=1.0, lam=0.9, lib=lib, **oracle_kw(d))
+    vs_a, pg_a = oracle.vtrace(*args, **kw)
+    vs_b, pg_b = oracle.vtrace(*args, rho_bar_pg=0.6, **kw)
+    assert np.array_equal(vs_a, vs_b)
+    ratio = np.exp(d["log_rhos"].astype(np.float64))
+    close(pg_b, pg_a * np.minimum(f32(0.6), ratio) / np.minimum(1.0, ratio), 1e-13)
 
 
 # ------------------------------------------------------------ Retrace
@@ -553,6 +623,39 @@ def pin_prefix_sum(lib):
     big = np.full((1, 4), 2**31 - 1, np.int32)
     assert oracle.episodic_prefix_sum(big, np.zeros((1, 4), np.float32), lib=lib)[0, -1] \
         == 4 * (2**31 - 1)
+
+
+def segment_cumsum_float(x, dones):
+    out = np.empty(x.shape, np.float64)
+    for n in range(x.shape[0]):
+        starts = sorted(set([0] + list(np.flatnonzero(dones[n] != 0))))
+        ends = starts[1:] + [x.shape[1]]
+        for s, e in zip(starts, ends):
+            out[n, s:e] = np.cumsum(x[n, s:e].astype(np.float64))
+    return out
+
+
+def pin_prefix_sum_float(lib):
+    """Float values: per-episode numpy.cumsum in float64; all-done is x; no
+    done is the whole-row cumsum; a carry enters only the first episode."""
+    rng = np.random.default_rng(71)
+    x = rng.standard_normal((5, 300)).astype(np.float32)
+    d = (rng.random((5, 300)) < 0.03).astype(np.float32)
+    close(oracle.episodic_prefix_sum_float(x, d, lib=lib), segment_cumsum_float(x, d), 1e-14)
+    none = np.zeros_like(d)
+    close(oracle.episodic_prefix_sum_float(x, none, lib=lib),
+          np.cumsum(x.astype(np.float64), axis=1), 1e-14)
+    assert np.array_equal(oracle.episodic_prefix_sum_float(x, np.ones_like(d), lib=lib),
+                          x.astype(np.float64))
+    ci = rng.standard_normal(5).astype(np.float32)
+    got, co = oracle.episodic_prefix_sum_float(x, d, carry_in=ci, return_carry=True, lib=lib)
+    want = segment_cumsum_float(x, d)
+    for n in range(5):
+        first = np.flatnonzero(d[n] != 0)
+        stop = first[0] if first.size else 300
+        want[n, :stop] += np.float64(ci[n])
+    close(got, want, 1e-13)
+    assert np.array_equal(co, got[:, -1])
 
 
 # ------------------------------------------------------------ carry (chunking)
@@ -737,10 +840,13 @@ PINS = {
     "discounted_returns": [pin_discounted_brute, pin_discounted_constant_reward,
                            pin_discounted_lfilter, pin_discounted_chunked],
     "vtrace": [pin_vtrace_brute, pin_vtrace_on_policy_is_discounted_return,
-               pin_vtrace_no_trace_is_one_step, pin_vtrace_chunked],
+               pin_vtrace_no_trace_is_one_step, pin_vtrace_chunked,
+               pin_vtrace_lambda_and_pg_clip_brute, pin_vtrace_lambda_zero_is_one_step,
+               pin_vtrace_lambda_scales_c_bar, pin_vtrace_pg_clip_only_rescales_pg],
     "retrace": [pin_retrace_brute, pin_retrace_lambda0, pin_retrace_onehot_on_policy,
                 pin_retrace_chunked],
     "eligibility_traces": [pin_eligibility_brute, pin_eligibility_limits,
                            pin_eligibility_chunked],
     "episodic_prefix_sum": [pin_prefix_sum, pin_prefix_sum_chunked],
+    "episodic_prefix_sum_float": [pin_prefix_sum_float],
 }

@@ -146,8 +146,11 @@ MUTATIONS = [
     ("vtrace", "gamma * c * next_u", "gamma * rho * next_u"),
     ("vtrace", "const double follow = cut ? v_next : next_vs;",
      "const double follow = cut ? v_next : next_u;"),
-    ("vtrace", "const double c = ratio < c_bar ? ratio : c_bar;",
-     "const double c = ratio < c_bar ? ratio : 1.0;"),
+    ("vtrace", "(ratio < c_bar ? ratio : c_bar)", "(ratio < c_bar ? ratio : 1.0)"),
+    ("vtrace", "const double c = lambda * (", "const double c = ("),
+    ("vtrace", "const double rho_pg = ratio < rho_bar_pg ? ratio : rho_bar_pg;",
+     "const double rho_pg = ratio < rho_bar ? ratio : rho_bar;"),
+    ("vtrace", "pg_advantages[i] = rho_pg *", "pg_advantages[i] = rho *"),
     ("retrace", "next_actions[n] : actions[i + 1];", "next_actions[n] : actions[i];"),
     ("retrace", "(double)behaviour_probs[i + 1]", "(double)behaviour_probs[i]"),
     ("retrace", "g = (double)rewards[i];\n", "g = (double)rewards[i] + gamma * eq;\n"),
@@ -174,6 +177,15 @@ MUTATIONS = [
     ("retrace", "(double)next_behaviour_probs[n]", "(double)behaviour_probs[i]"),
     ("eligibility_traces", "double prev = carry_of(carry_in, n);", "double prev = 0.0;"),
     ("episodic_prefix_sum", "int64_t prev = carry_in ? carry_in[n] : 0;", "int64_t prev = 0;"),
+    ("episodic_prefix_sum_float", "(double)x[i] + (is_set(dones, i) ? 0.0 : prev)",
+     "(double)x[i] + prev"),
+    ("episodic_prefix_sum_float", "double prev = carry_of(carry_in, n);  /* y_{-1} */",
+     "double prev = 0.0;  /* y_{-1} */"),
+    ("episodic_prefix_sum_float",
+     "? 0.0 : prev);\n            out[i] = y;\n            prev = y;\n        }\n        if "
+     "(carry_out) carry_out[n] = out[n * T + T - 1];",
+     "? 0.0 : prev);\n            out[i] = y;\n            prev = y;\n        }\n        if "
+     "(carry_out) carry_out[n] = out[n * T];"),
 ]
 
 
