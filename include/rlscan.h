@@ -23,11 +23,13 @@
  * Memory      Every pointer is a DEVICE pointer on the current HIP device,
  *             allocated and owned by the caller.  The library never frees or
  *             retains caller pointers.  Outputs must not alias inputs.
- *             16-byte aligned pointers take the vectorised path; any other
- *             alignment is accepted and takes a scalar-load path.
+ *             16-byte aligned pointers take the vectorised path (one-byte
+ *             flag tensors: 4-byte aligned); any other alignment is accepted
+ *             and takes a scalar-load path.
  * Flags       terminated / truncated / dones are float32 tensors (README,
- *             section "Usage", passes terminateds as a float tensor); a flag
- *             is set iff its value != 0.
+ *             section "Usage", passes terminateds as a float tensor), or
+ *             uint8 tensors for the *_u8 entry points; a flag is set iff its
+ *             value != 0.
  * Episodes    Reverse estimators (GAE, TD(lambda), discounted returns,
  *             V-trace, Retrace): step t is a chain cut if terminated, or
  *             truncated, or t = T-1.  Terminated means the successor value is
@@ -41,8 +43,8 @@
  *             prefix sum take a single done flag and no bootstrap.)
  *             Forward estimators: the flag at step t drops the carry from
  *             step t-1; every row starts from 0.
- * Parameters  gamma, lambda in [0, 1] and finite; rho_bar, c_bar > 0
- *             (+inf allowed, NaN rejected).
+ * Parameters  gamma, lambda in [0, 1] and finite; rho_bar, c_bar, rho_bar_pg
+ *             > 0 (+inf allowed, NaN rejected).
  * Streams     Work is enqueued on `stream` (NULL = the device's null stream)
  *             and the call returns without synchronising.  Results are valid
  *             once the stream has completed.  Faults inside kernels surface at
@@ -69,6 +71,12 @@
  *             look-back launches have come from more than one stream of the
  *             device (a stream used for them must then stay alive while
  *             later calls are enqueued).  Packed launches are not ordered.
+ * Rounding    float32 results of a call that uses the look-back (see
+ *             rlscan_plan) can differ in the last bits between two runs on
+ *             the same inputs: a tile composes whichever of its
+ *             predecessors' published values are ready, in an order that
+ *             depends on timing.  Packed calls and the int64 prefix sum are
+ *             deterministic.
  * Graphs      Calls whose tiles hold whole rows (the packed mapping, see
  *             rlscan_plan) launch one kernel and nothing else, and may be
  *             captured into a HIP graph.  A call that needs the look-back
@@ -253,6 +261,79 @@ int rlscan_episodic_prefix_sum_carry(const int32_t* x, const float* dones,
                                      int64_t* carry_out, int64_t N, int64_t T,
                                      hipStream_t stream);
 
+/* ---- V-trace options ------------------------------------------------------
+ * IMPALA (Espeholt et al. 2018) lets the trace coefficients carry a factor
+ * lambda in [0, 1], and implementations commonly truncate the weight of the
+ * policy-gradient advantage at a level rho_bar_pg of its own:
+ *   c_t  = lambda*min(c_bar, exp(log_rhos_t))
+ *   pg_t = min(rho_bar_pg, exp(log_rhos_t))
+ *          * (r_t + gamma*(cut_t ? Vhat_{t+1} : vs_{t+1}) - V_t)
+ * with rho_t, delta_t and vs_t as in rlscan_vtrace.  Every other argument is
+ * as for rlscan_vtrace_carry, which is this call with lambda = 1 and
+ * rho_bar_pg = rho_bar (bit for bit). */
+int rlscan_vtrace_ex(const float* rewards, const float* values, const float* bootstrap_value,
+                     const float* log_rhos, const float* terminated, const float* truncated,
+                     const float* bootstrap_values, const float* carry_in, float* vs,
+                     float* pg_advantages, float* carry_out, int64_t N, int64_t T, float gamma,
+                     float lambda, float rho_bar, float c_bar, float rho_bar_pg,
+                     hipStream_t stream);
+
+/* ---- float-valued episodic prefix sum -------------------------------------
+ * The episodic prefix sum (README, Kernels table,
+ * compute_episodic_prefix_sum) of float32 values:
+ *   y_t = x_t + (d_t ? 0 : y_{t-1}),  y_{-1} = carry_in[n] (NULL: 0)
+ * in float32 arithmetic, summed in the scan's order (not the sequential one).
+ * in:  x, dones [N,T] float32; carry_in [N] or NULL.
+ * out: y [N,T] float32; carry_out [N] or NULL (y at t = T-1).
+ * It is the eligibility-trace recurrence with gamma*lambda = 1. */
+int rlscan_episodic_prefix_sum_f32(const float* x, const float* dones, const float* carry_in,
+                                   float* out, float* carry_out, int64_t N, int64_t T,
+                                   hipStream_t stream);
+
+/* ---- one-byte flags --------------------------------------------------------
+ * Each *_u8 entry point is its estimator's most general call above (the
+ * *_carry call; for V-trace rlscan_vtrace_ex) with terminated, truncated or
+ * dones given as uint8 [N,T]: set iff != 0, so a bool tensor qualifies as
+ * is.  A flag then moves 1 byte per step instead of 4 (GAE without
+ * truncation reads 9 bytes per step instead of 12).  The arithmetic is that
+ * of the float-flag call with every set flag read as 1, so the results are
+ * identical.  Flag tensors 4-byte aligned (and the others 16-byte aligned)
+ * take the vectorised path. */
+int rlscan_gae_u8(const float* rewards, const float* values, const float* bootstrap_value,
+                  const uint8_t* terminated, const uint8_t* truncated,
+                  const float* bootstrap_values, const float* carry_in, float* advantages,
+                  float* carry_out, int64_t N, int64_t T, float gamma, float lambda,
+                  hipStream_t stream);
+int rlscan_lambda_returns_u8(const float* rewards, const float* values,
+                             const float* bootstrap_value, const uint8_t* terminated,
+                             const uint8_t* truncated, const float* bootstrap_values,
+                             const float* carry_in, float* returns, float* carry_out, int64_t N,
+                             int64_t T, float gamma, float lambda, hipStream_t stream);
+int rlscan_discounted_returns_u8(const float* rewards, const float* bootstrap_value,
+                                 const uint8_t* terminated, const uint8_t* truncated,
+                                 const float* bootstrap_values, const float* carry_in,
+                                 float* returns, float* carry_out, int64_t N, int64_t T,
+                                 float gamma, hipStream_t stream);
+int rlscan_vtrace_u8(const float* rewards, const float* values, const float* bootstrap_value,
+                     const float* log_rhos, const uint8_t* terminated, const uint8_t* truncated,
+                     const float* bootstrap_values, const float* carry_in, float* vs,
+                     float* pg_advantages, float* carry_out, int64_t N, int64_t T, float gamma,
+                     float lambda, float rho_bar, float c_bar, float rho_bar_pg,
+                     hipStream_t stream);
+int rlscan_retrace_u8(const float* rewards, const float* next_q_values_all,
+                      const float* next_target_probs, const int32_t* actions,
+                      const float* behaviour_probs, const uint8_t* terminated,
+                      const uint8_t* truncated, const float* carry_in,
+                      const int32_t* next_actions, const float* next_behaviour_probs,
+                      float* targets, float* carry_out, int64_t N, int64_t T, int64_t A,
+                      float gamma, float lambda, hipStream_t stream);
+int rlscan_eligibility_traces_u8(const float* x, const uint8_t* dones, const float* carry_in,
+                                 float* traces, float* carry_out, int64_t N, int64_t T,
+                                 float gamma, float lambda, hipStream_t stream);
+int rlscan_episodic_prefix_sum_u8(const int32_t* x, const uint8_t* dones,
+                                  const int64_t* carry_in, int64_t* out, int64_t* carry_out,
+                                  int64_t N, int64_t T, hipStream_t stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* rlscan_status_string(int status);
 
@@ -306,7 +387,7 @@ enum {
  * apply with one round; with more rounds 4 is used); grid_cap: 0 = no cap,
  * else at most this many workgroups, each looping over tiles; flags:
  * RLSCAN_FLAG_* bits.  Retrace runs one round of at most 4 waves; a call
- * with an input or output that is not 16-byte aligned, or with carry
+ * with an input or output that is not aligned for the vector path, or with carry
  * arguments, runs 4 waves (the former one round).  By default
  * look-back tiles are ordered by workgroup index, and by tickets only when
  * workgroups loop.  Returns RLSCAN_ERR_PARAM for other values. */

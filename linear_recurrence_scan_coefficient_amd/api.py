@@ -13,11 +13,13 @@ no bootstrap tensor; traces and the prefix sum take a single dones flag).
 
 Argument marshalling only: every computation runs in librlscan's HIP kernels
 through the C ABI (`rlscan.rlscan_*`).  Inputs must already be on the GPU;
-there is no CPU path.  Flags given as bool or integer tensors are converted
-to the float32 0/1 form the ABI takes (one elementwise copy), non-contiguous
-inputs are made contiguous, and the call runs on the current stream (or
-`stream`).  gamma and lambda_ default to the values of the README's usage
-example.
+there is no CPU path.  Flags (set iff != 0) given as float32 take the
+float-flag kernels and bool / uint8 flags the one-byte-flag kernels, both
+without any conversion; flags of other dtypes, or a mix of float32 and
+one-byte flags in one call, are first turned into bool (one elementwise
+pass).  Non-contiguous inputs are made contiguous, and the call runs on the
+current stream (or `stream`).  gamma and lambda_ default to the values of
+the README's usage example.
 
 Streaming one rollout through several calls (the README's chunked fallback
 for long sequences, Kernels table, last column): every call takes
@@ -55,8 +57,27 @@ def _device_tensor(t, name, dtype=torch.float32, flag=False):
     return t.contiguous()
 
 
-def _flags(t, name):
-    return _device_tensor(t, name, torch.float32, flag=True)
+_BYTE = (torch.bool, torch.uint8)
+
+
+def _flags(**flags):
+    """The call's flag tensors, all float32 or all one-byte (bool / uint8)."""
+    given = {k: t for k, t in flags.items() if t is not None}
+    for k, t in given.items():
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{k} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{k} must be on the GPU (got device {t.device}); rlscan has no "
+                             "CPU path")
+    def kind(t):
+        return "float32" if t.dtype == torch.float32 else ("byte" if t.dtype in _BYTE else "other")
+
+    kinds = {kind(t) for t in given.values()}
+    if kinds in ({"float32"}, {"byte"}):
+        out = {k: t.contiguous() for k, t in given.items()}
+    else:  # any other dtype, or a mix: one byte per flag
+        out = {k: (t if t.dtype in _BYTE else t != 0).contiguous() for k, t in given.items()}
+    return [out.get(k) for k in flags]
 
 
 def _carry_out(wanted, N, device, dtype=torch.float32):
@@ -81,10 +102,10 @@ def compute_gae(rewards, values, terminateds, gamma=0.99, lambda_=0.95, *,
     N, T = _check_2d(r, "rewards")
     out = torch.empty((N, T), dtype=torch.float32, device=r.device)
     co = _carry_out(return_carry, N, r.device)
+    term, trunc = _flags(terminateds=terminateds, truncateds=truncateds)
     rlscan.rlscan_gae(
         r, _device_tensor(values, "values"), _device_tensor(bootstrap_value, "bootstrap_value"),
-        _flags(terminateds, "terminateds"), _flags(truncateds, "truncateds"),
-        _device_tensor(bootstrap_values, "bootstrap_values"), out, float(gamma),
+        term, trunc, _device_tensor(bootstrap_values, "bootstrap_values"), out, float(gamma),
         float(lambda_), stream, carry_in=_device_tensor(carry_in, "carry_in"), carry_out=co)
     return (out, co) if return_carry else out
 
@@ -97,10 +118,10 @@ def compute_lambda_returns(rewards, values, terminateds, gamma=0.99, lambda_=0.9
     N, T = _check_2d(r, "rewards")
     out = torch.empty((N, T), dtype=torch.float32, device=r.device)
     co = _carry_out(return_carry, N, r.device)
+    term, trunc = _flags(terminateds=terminateds, truncateds=truncateds)
     rlscan.rlscan_lambda_returns(
         r, _device_tensor(values, "values"), _device_tensor(bootstrap_value, "bootstrap_value"),
-        _flags(terminateds, "terminateds"), _flags(truncateds, "truncateds"),
-        _device_tensor(bootstrap_values, "bootstrap_values"), out, float(gamma),
+        term, trunc, _device_tensor(bootstrap_values, "bootstrap_values"), out, float(gamma),
         float(lambda_), stream, carry_in=_device_tensor(carry_in, "carry_in"), carry_out=co)
     return (out, co) if return_carry else out
 
@@ -114,30 +135,36 @@ def compute_discounted_returns(rewards, terminateds, gamma=0.99, *, bootstrap_va
     N, T = _check_2d(r, "rewards")
     out = torch.empty((N, T), dtype=torch.float32, device=r.device)
     co = _carry_out(return_carry, N, r.device)
+    term, trunc = _flags(terminateds=terminateds, truncateds=truncateds)
     rlscan.rlscan_discounted_returns(
-        r, _device_tensor(bootstrap_value, "bootstrap_value"), _flags(terminateds, "terminateds"),
-        _flags(truncateds, "truncateds"), _device_tensor(bootstrap_values, "bootstrap_values"),
-        out, float(gamma), stream, carry_in=_device_tensor(carry_in, "carry_in"), carry_out=co)
+        r, _device_tensor(bootstrap_value, "bootstrap_value"), term, trunc,
+        _device_tensor(bootstrap_values, "bootstrap_values"), out, float(gamma), stream,
+        carry_in=_device_tensor(carry_in, "carry_in"), carry_out=co)
     return (out, co) if return_carry else out
 
 
 def compute_vtrace(rewards, values, log_rhos, terminateds, gamma=0.99, rho_bar=1.0, c_bar=1.0,
                    *, bootstrap_value=None, truncateds=None, bootstrap_values=None,
-                   carry_in=None, return_carry=False, stream=None):
+                   carry_in=None, return_carry=False, lambda_=None, rho_bar_pg=None,
+                   stream=None):
     """V-trace targets vs and policy-gradient advantages [N, T] each, as a
     tuple (README, Kernels: compute_vtrace).  log_rhos = log pi - log mu.
-    carry_in / carry_out are vs values."""
+    carry_in / carry_out are vs values.  IMPALA's options: lambda_ scales
+    every trace coefficient c_t (None: 1) and rho_bar_pg truncates the
+    policy-gradient weight (None: rho_bar)."""
     r = _device_tensor(rewards, "rewards")
     N, T = _check_2d(r, "rewards")
     vs = torch.empty((N, T), dtype=torch.float32, device=r.device)
     pg = torch.empty((N, T), dtype=torch.float32, device=r.device)
     co = _carry_out(return_carry, N, r.device)
+    term, trunc = _flags(terminateds=terminateds, truncateds=truncateds)
     rlscan.rlscan_vtrace(
         r, _device_tensor(values, "values"), _device_tensor(bootstrap_value, "bootstrap_value"),
-        _device_tensor(log_rhos, "log_rhos"), _flags(terminateds, "terminateds"),
-        _flags(truncateds, "truncateds"), _device_tensor(bootstrap_values, "bootstrap_values"),
-        vs, pg, float(gamma), float(rho_bar), float(c_bar), stream,
-        carry_in=_device_tensor(carry_in, "carry_in"), carry_out=co)
+        _device_tensor(log_rhos, "log_rhos"), term, trunc,
+        _device_tensor(bootstrap_values, "bootstrap_values"), vs, pg, float(gamma),
+        float(rho_bar), float(c_bar), stream, carry_in=_device_tensor(carry_in, "carry_in"),
+        carry_out=co, lam=None if lambda_ is None else float(lambda_),
+        rho_bar_pg=None if rho_bar_pg is None else float(rho_bar_pg))
     return (vs, pg, co) if return_carry else (vs, pg)
 
 
@@ -162,13 +189,13 @@ def compute_retrace(rewards, next_q_values_all, next_target_probs, actions, beha
         na = na.to(torch.int32)
     out = torch.empty((N, T), dtype=torch.float32, device=r.device)
     co = _carry_out(return_carry, N, r.device)
+    term, trunc = _flags(terminateds=terminateds, truncateds=truncateds)
     rlscan.rlscan_retrace(
         r, _device_tensor(next_q_values_all, "next_q_values_all"),
         _device_tensor(next_target_probs, "next_target_probs"),
         _device_tensor(a, "actions", torch.int32), _device_tensor(behaviour_probs,
                                                                   "behaviour_probs"),
-        _flags(terminateds, "terminateds"), _flags(truncateds, "truncateds"), out,
-        float(gamma), float(lambda_), stream, carry_in=_device_tensor(carry_in, "carry_in"),
+        term, trunc, out, float(gamma), float(lambda_), stream, carry_in=_device_tensor(carry_in, "carry_in"),
         carry_out=co, next_actions=_device_tensor(na, "next_actions", torch.int32),
         next_behaviour_probs=_device_tensor(next_behaviour_probs, "next_behaviour_probs"))
     return (out, co) if return_carry else out
@@ -182,16 +209,28 @@ def compute_eligibility_traces(x, dones, gamma=0.99, lambda_=0.95, *, carry_in=N
     N, T = _check_2d(xx, "x")
     out = torch.empty((N, T), dtype=torch.float32, device=xx.device)
     co = _carry_out(return_carry, N, xx.device)
-    rlscan.rlscan_eligibility_traces(xx, _flags(dones, "dones"), out, float(gamma),
+    rlscan.rlscan_eligibility_traces(xx, _flags(dones=dones)[0], out, float(gamma),
                                      float(lambda_), stream,
                                      carry_in=_device_tensor(carry_in, "carry_in"), carry_out=co)
     return (out, co) if return_carry else out
 
 
 def compute_episodic_prefix_sum(x, dones, *, carry_in=None, return_carry=False, stream=None):
-    """Cumulative sum restarted where dones is set, exact in int64 [N, T]
-    (README, Kernels: compute_episodic_prefix_sum).  x is int32; narrower
-    integer dtypes are widened, int64 is refused (it would not fit)."""
+    """Cumulative sum restarted where dones is set (README, Kernels:
+    compute_episodic_prefix_sum).  Integer x: exact int64 output [N, T]; x is
+    int32, narrower integer dtypes are widened, int64 is refused (it would
+    not fit).  float32 x: float32 output, summed in float32 in the scan's
+    order (float dones only)."""
+    if isinstance(x, torch.Tensor) and x.dtype == torch.float32:
+        xx = _device_tensor(x, "x")
+        N, T = _check_2d(xx, "x")
+        out = torch.empty((N, T), dtype=torch.float32, device=xx.device)
+        co = _carry_out(return_carry, N, xx.device)
+        d = _device_tensor(dones, "dones", torch.float32, flag=True)
+        rlscan.rlscan_episodic_prefix_sum_f32(xx, d, out, stream,
+                                              carry_in=_device_tensor(carry_in, "carry_in"),
+                                              carry_out=co)
+        return (out, co) if return_carry else out
     xx = x
     if isinstance(xx, torch.Tensor) and xx.dtype in (torch.bool, torch.uint8, torch.int8,
                                                      torch.int16):
@@ -200,7 +239,7 @@ def compute_episodic_prefix_sum(x, dones, *, carry_in=None, return_carry=False, 
     N, T = _check_2d(xx, "x")
     out = torch.empty((N, T), dtype=torch.int64, device=xx.device)
     co = _carry_out(return_carry, N, xx.device, torch.int64)
-    rlscan.rlscan_episodic_prefix_sum(xx, _flags(dones, "dones"), out, stream,
+    rlscan.rlscan_episodic_prefix_sum(xx, _flags(dones=dones)[0], out, stream,
                                       carry_in=_device_tensor(carry_in, "carry_in", torch.int64),
                                       carry_out=co)
     return (out, co) if return_carry else out

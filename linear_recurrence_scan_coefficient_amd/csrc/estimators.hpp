@@ -19,6 +19,14 @@
 //   store<VEC,FULL>   write outputs from the states after each element (x)
 //                     and before it (before: x_{t+1} for reverse estimators)
 //   edge_value        the output written to carry_out for element j
+//   reads_before      whether the output of element j reads the state before
+//                     it (x_{t+1} for reverse estimators) even though its
+//                     step has a == 0 -- the tile's entering state is then
+//                     needed although nothing else depends on it
+//
+// Flags (terminated, truncated, dones) are float (set iff != 0.0f) or uint8_t
+// (set iff != 0): every estimator takes the flag element type F as a template
+// parameter, and the loads turn either into 0/1 floats in registers.
 //
 // Shared conventions: row-major [N, T]; a flag is set iff != 0; for reverse
 // estimators step t cuts the chain if terminated, truncated or t = T-1, and
@@ -126,6 +134,21 @@ __device__ __forceinline__ void load4(const int32_t* __restrict__ p, const Chunk
     for (int j = 0; j < kChunk; ++j) v[j] = (FULL || j < q.valid) ? p[q.g0 + j] : 0;
 }
 
+// One-byte flags: a chunk's four flags are one 4-byte word (a wave reads
+// 256 contiguous bytes per instruction), unpacked to 0/1 floats.
+template <bool VEC, bool FULL>
+__device__ __forceinline__ void load4(const uint8_t* __restrict__ p, const ChunkPos& q, float v[4]) {
+    if (VEC && (FULL || q.valid == kChunk)) {
+        const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p + q.g0));
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) v[j] = ((w >> (8 * j)) & 0xffu) != 0u ? 1.0f : 0.0f;
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j)
+        v[j] = ((FULL || j < q.valid) && p[q.g0 + j] != 0) ? 1.0f : 0.0f;
+}
+
 template <bool VEC, bool FULL>
 __device__ __forceinline__ void store4(float* __restrict__ p, const ChunkPos& q, const float v[4]) {
     if (VEC && (FULL || q.valid == kChunk)) {
@@ -172,9 +195,9 @@ struct EpisodeChunk {
     float carry;  // carry_in of the chunk's first row
 };
 
-template <bool VEC, bool FULL, bool TRUNC, bool CARRY>
-__device__ __forceinline__ void load_episode(const float* rewards, const float* terminated,
-                                             const float* truncated,
+template <bool VEC, bool FULL, bool TRUNC, bool CARRY, class F>
+__device__ __forceinline__ void load_episode(const float* rewards, const F* terminated,
+                                             const F* truncated,
                                              const float* bootstrap_values,
                                              const float* bootstrap_value,
                                              const float* carry_in, const Geometry& geo,
@@ -232,19 +255,21 @@ __device__ __forceinline__ void fold_carry(StepF& e, float carry) {
 // README, Kernels table, compute_gae row (backward scan of TD errors with
 // weight gamma*lambda); Schulman et al. 2016.
 //   a_t = cut ? 0 : gamma*lambda,   b_t = r_t + gamma*Vhat_{t+1} - V_t
+template <class F>
 struct GaeParams {
-    const float *rewards, *values, *bootstrap_value, *terminated, *truncated,
-        *bootstrap_values, *carry_in;
+    const float *rewards, *values, *bootstrap_value;
+    const F *terminated, *truncated;
+    const float *bootstrap_values, *carry_in;
     float *out, *carry_out;
     float gamma, gamma_lambda;
 };
 
-template <bool kTrunc>
+template <bool kTrunc, class F = float>
 struct Gae {
     using S = StepF;
     using V = float;
     static constexpr bool kReverse = true;
-    using Params = GaeParams;
+    using Params = GaeParams<F>;
     using Epi = NoEpi;
     static constexpr int kStageFloats = 0;
     static constexpr int kOutStageFloats = 0;
@@ -266,7 +291,7 @@ struct Gae {
     __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
                                  const Chunk& c, S e[4], Epi&) {
         int64_t n = q.n0, t = q.t0;
-const bool continues = CARRY && p.carry_in != nullptr;
+        const bool continues = CARRY && p.carry_in != nullptr;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             bool cut;
@@ -284,6 +309,7 @@ const bool continues = CARRY && p.carry_in != nullptr;
     __device__ __forceinline__ static V edge_value(const Epi&, const V x[4], int j) {
         return x[j];
     }
+    __device__ __forceinline__ static bool reads_before(const Epi&, int) { return false; }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
                                                  const V x[4], const V[4], lds_float*) {
@@ -295,23 +321,25 @@ const bool continues = CARRY && p.carry_in != nullptr;
 // README, Kernels table, compute_lambda_returns row; lambda-return.
 //   a_t = cut ? 0 : gamma*lambda
 //   b_t = cut ? r_t + gamma*Vhat_{t+1} : r_t + gamma*(1-lambda)*V_{t+1}
+template <class F>
 struct LambdaReturnsParams {
-    const float *rewards, *values, *bootstrap_value, *terminated, *truncated,
-        *bootstrap_values, *carry_in;
+    const float *rewards, *values, *bootstrap_value;
+    const F *terminated, *truncated;
+    const float *bootstrap_values, *carry_in;
     float *out, *carry_out;
     float gamma, gamma_lambda, gamma_one_minus_lambda;
 };
 
-template <bool kTrunc>
+template <bool kTrunc, class F = float>
 struct LambdaReturns {
     using S = StepF;
     using V = float;
     static constexpr bool kReverse = true;
-    using Params = LambdaReturnsParams;
+    using Params = LambdaReturnsParams<F>;
     using Epi = NoEpi;
     static constexpr int kStageFloats = 0;
     static constexpr int kOutStageFloats = 0;
-    using Chunk = typename Gae<kTrunc>::Chunk;
+    using Chunk = typename Gae<kTrunc, F>::Chunk;
     template <bool VEC, bool FULL, bool CARRY>
     __device__ __forceinline__ static void load(const Params& p, const Geometry& geo,
                                                 const ChunkPos& q, Chunk& c, lds_float*) {
@@ -325,7 +353,7 @@ struct LambdaReturns {
     __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
                                  const Chunk& c, S e[4], Epi&) {
         int64_t n = q.n0, t = q.t0;
-const bool continues = CARRY && p.carry_in != nullptr;
+        const bool continues = CARRY && p.carry_in != nullptr;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             bool cut;
@@ -346,6 +374,7 @@ const bool continues = CARRY && p.carry_in != nullptr;
     __device__ __forceinline__ static V edge_value(const Epi&, const V x[4], int j) {
         return x[j];
     }
+    __device__ __forceinline__ static bool reads_before(const Epi&, int) { return false; }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
                                                  const V x[4], const V[4], lds_float*) {
@@ -356,19 +385,21 @@ const bool continues = CARRY && p.carry_in != nullptr;
 // ------------------------------------------------------ discounted returns
 // README, Kernels table, compute_discounted_returns row (reward-to-go).
 //   a_t = cut ? 0 : gamma,   b_t = cut ? r_t + gamma*Vhat_{t+1} : r_t
+template <class F>
 struct DiscountedParams {
-    const float *rewards, *bootstrap_value, *terminated, *truncated, *bootstrap_values,
-        *carry_in;
+    const float *rewards, *bootstrap_value;
+    const F *terminated, *truncated;
+    const float *bootstrap_values, *carry_in;
     float *out, *carry_out;
     float gamma;
 };
 
-template <bool kTrunc>
+template <bool kTrunc, class F = float>
 struct Discounted {
     using S = StepF;
     using V = float;
     static constexpr bool kReverse = true;
-    using Params = DiscountedParams;
+    using Params = DiscountedParams<F>;
     using Epi = NoEpi;
     static constexpr int kStageFloats = 0;
     static constexpr int kOutStageFloats = 0;
@@ -386,7 +417,7 @@ struct Discounted {
     __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
                                  const Chunk& c, S e[4], Epi&) {
         int64_t n = q.n0, t = q.t0;
-const bool continues = CARRY && p.carry_in != nullptr;
+        const bool continues = CARRY && p.carry_in != nullptr;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             bool cut;
@@ -403,6 +434,7 @@ const bool continues = CARRY && p.carry_in != nullptr;
     __device__ __forceinline__ static V edge_value(const Epi&, const V x[4], int j) {
         return x[j];
     }
+    __device__ __forceinline__ static bool reads_before(const Epi&, int) { return false; }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
                                                  const V x[4], const V[4], lds_float*) {
@@ -412,24 +444,32 @@ const bool continues = CARRY && p.carry_in != nullptr;
 
 // ------------------------------------------------------------------ V-trace
 // README, Kernels table, compute_vtrace row (importance-weighted targets and
-// advantages); Espeholt et al. 2018.  The scan computes u_t = vs_t - V_t:
-//   a_t = cut ? 0 : gamma*c_t,   b_t = delta_t = rho_t*(r_t + gamma*Vhat_{t+1} - V_t)
+// advantages); Espeholt et al. 2018, with that paper's optional factor
+// lambda on the trace coefficients and a truncation level rho_bar_pg of its
+// own for the policy-gradient weight (lambda = 1, rho_bar_pg = rho_bar is
+// the plain form).  With ratio_t = exp(log_rho_t), rho_t = min(rho_bar,
+// ratio_t), c_t = lambda*min(c_bar, ratio_t), rho'_t = min(rho_bar_pg,
+// ratio_t) and td_t = r_t + gamma*Vhat_{t+1} - V_t, the scan computes
+// u_t = vs_t - V_t:
+//   a_t = cut ? 0 : gamma*c_t,   b_t = delta_t = rho_t*td_t
 // and the epilogue forms vs_t = V_t + u_t and
-//   pg_t = delta_t + (cut ? 0 : gamma*rho_t*u_{t+1})
-// which equals rho_t*(r_t + gamma*(cut ? Vhat_{t+1} : vs_{t+1}) - V_t).
+//   pg_t = rho'_t*td_t + (cut ? 0 : gamma*rho'_t*u_{t+1})
+// which equals rho'_t*(r_t + gamma*(cut ? Vhat_{t+1} : vs_{t+1}) - V_t).
+template <class F>
 struct VtraceParams {
-    const float *rewards, *values, *bootstrap_value, *log_rhos, *terminated, *truncated,
-        *bootstrap_values, *carry_in;  // carry_in: vs at t = T
-    float *vs, *pg, *carry_out;       // carry_out: vs at t = 0
-    float gamma, rho_bar, c_bar;
+    const float *rewards, *values, *bootstrap_value, *log_rhos;
+    const F *terminated, *truncated;
+    const float *bootstrap_values, *carry_in;  // carry_in: vs at t = T
+    float *vs, *pg, *carry_out;               // carry_out: vs at t = 0
+    float gamma, lambda, rho_bar, c_bar, rho_bar_pg;
 };
 
-template <bool kTrunc>
+template <bool kTrunc, class F = float>
 struct Vtrace {
     using S = StepF;
     using V = float;
     static constexpr bool kReverse = true;
-    using Params = VtraceParams;
+    using Params = VtraceParams<F>;
     struct Chunk {
         EpisodeChunk ep;
         float v[4];
@@ -438,8 +478,8 @@ struct Vtrace {
     };
     struct Epi {
         float v[4];
-        float delta[4];
-        float gamma_rho[4];  // 0 at a cut
+        float pg_base[4];    // rho'_t * td_t
+        float gamma_rho[4];  // gamma * rho'_t, 0 at a cut
     };
     static constexpr int kStageFloats = 0;
     static constexpr int kOutStageFloats = 0;
@@ -457,7 +497,7 @@ struct Vtrace {
     __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
                                  const Chunk& c, S e[4], Epi& epi) {
         int64_t n = q.n0, t = q.t0;
-const bool continues = CARRY && p.carry_in != nullptr;
+        const bool continues = CARRY && p.carry_in != nullptr;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             bool cut;
@@ -467,19 +507,20 @@ const bool continues = CARRY && p.carry_in != nullptr;
                                              p.bootstrap_value, n, q.n0, v_next, continues, cut);
             const float ratio = expf(c.lr[j]);
             const float rho = fminf(p.rho_bar, ratio);
-            const float cc = fminf(p.c_bar, ratio);
-            const float delta = rho * (fmaf(p.gamma, vh, c.ep.r[j]) - c.v[j]);
+            const float cc = p.lambda * fminf(p.c_bar, ratio);
+            const float rho_pg = fminf(p.rho_bar_pg, ratio);
+            const float td = fmaf(p.gamma, vh, c.ep.r[j]) - c.v[j];
             epi.v[j] = c.v[j];
-            epi.delta[j] = delta;
-            epi.gamma_rho[j] = cut ? 0.0f : p.gamma * rho;
+            epi.pg_base[j] = rho_pg * td;
+            epi.gamma_rho[j] = cut ? 0.0f : p.gamma * rho_pg;
             e[j].a = cut ? 0.0f : p.gamma * cc;
-            e[j].b = delta;
+            e[j].b = rho * td;
             if (row_end && continues && !cut && j < q.valid) {
                 // u at t = T is vs_T - V_T; the state before this element is
                 // not in the scan, so pg takes it here
                 const float u_T = row_carry(c.ep, p.carry_in, n, q.n0) - vh;
                 fold_carry(e[j], u_T);
-                epi.delta[j] = fmaf(epi.gamma_rho[j], u_T, delta);
+                epi.pg_base[j] = fmaf(epi.gamma_rho[j], u_T, epi.pg_base[j]);
                 epi.gamma_rho[j] = 0.0f;
             }
             next_position(n, t, geo.T);
@@ -489,6 +530,11 @@ const bool continues = CARRY && p.carry_in != nullptr;
     __device__ __forceinline__ static V edge_value(const Epi& c, const V x[4], int j) {
         return c.v[j] + x[j];
     }
+    // pg_t reads u_{t+1} unless t is a cut, also where c_t = 0 makes a_t = 0
+    // (lambda = 0, or lambda * c underflowing)
+    __device__ __forceinline__ static bool reads_before(const Epi& c, int j) {
+        return c.gamma_rho[j] != 0.0f;
+    }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi& c,
                                                  const V x[4], const V before[4], lds_float*) {
@@ -496,7 +542,7 @@ const bool continues = CARRY && p.carry_in != nullptr;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             vs[j] = c.v[j] + x[j];
-            pg[j] = fmaf(c.gamma_rho[j], before[j], c.delta[j]);
+            pg[j] = fmaf(c.gamma_rho[j], before[j], c.pg_base[j]);
         }
         store4<VEC, FULL>(p.vs, q, vs);
         store4<VEC, FULL>(p.pg, q, pg);
@@ -513,7 +559,7 @@ const bool continues = CARRY && p.carry_in != nullptr;
 //             : r_t + gamma*(EQ_t - c'_t*Q'[t,a_{t+1}])
 // kA > 0: A known at compile time, the chunk's 4*A action values are read
 // with 16-byte loads into registers; kA == 0: any A, read element-wise.
-template <int kA>
+template <int kA, class F = float>
 struct Retrace {
     using S = StepF;
     using V = float;
@@ -528,7 +574,8 @@ struct Retrace {
     struct Params {
         const float *rewards, *next_q, *next_pi;
         const int32_t* actions;
-        const float *behaviour_probs, *terminated, *truncated;
+        const float* behaviour_probs;
+        const F *terminated, *truncated;
         float* out;
         int64_t A;
         float gamma, lambda;
@@ -693,6 +740,7 @@ struct Retrace {
     __device__ __forceinline__ static V edge_value(const Epi&, const V x[4], int j) {
         return x[j];
     }
+    __device__ __forceinline__ static bool reads_before(const Epi&, int) { return false; }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
                                                  const V x[4], const V[4], lds_float*) {
@@ -711,6 +759,9 @@ __device__ __forceinline__ int64_t first_start_row(const ChunkPos& q, const Geom
 // README, Kernels table, compute_eligibility_traces row: forward traces, the
 // done flag at step t dropping the previous trace.
 //   a_t = (d_t or t = 0) ? 0 : gamma*lambda,   b_t = x_t
+// With gamma*lambda = 1 this is also the episodic prefix sum of float
+// values (README, Kernels table, compute_episodic_prefix_sum row).
+template <class F = float>
 struct Eligibility {
     using S = StepF;
     using V = float;
@@ -719,7 +770,8 @@ struct Eligibility {
     static constexpr int kStageFloats = 0;
     static constexpr int kOutStageFloats = 0;
     struct Params {
-        const float *x, *dones;
+        const float* x;
+        const F* dones;
         float* out;
         float gamma_lambda;
         const float* carry_in;  // e at t = -1
@@ -755,6 +807,7 @@ struct Eligibility {
     __device__ __forceinline__ static V edge_value(const Epi&, const V x[4], int j) {
         return x[j];
     }
+    __device__ __forceinline__ static bool reads_before(const Epi&, int) { return false; }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
                                                  const V x[4], const V[4], lds_float*) {
@@ -766,6 +819,7 @@ struct Eligibility {
 // README, Kernels table, compute_episodic_prefix_sum row: cumulative sum
 // restarted by the done mask; exact int64 accumulation of int32 inputs.
 //   a_t = (d_t or t = 0) ? 0 : 1,   b_t = x_t
+template <class F = float>
 struct PrefixSum {
     using S = StepI;
     using V = int64_t;
@@ -776,7 +830,7 @@ struct PrefixSum {
     static constexpr int kOutStageFloats = kWave * kChunk * 2;
     struct Params {
         const int32_t* x;
-        const float* dones;
+        const F* dones;
         int64_t* out;
         const int64_t* carry_in;  // y at t = -1
         int64_t* carry_out;       // y at t = T-1
@@ -819,6 +873,7 @@ struct PrefixSum {
     __device__ __forceinline__ static V edge_value(const Epi&, const V x[4], int j) {
         return x[j];
     }
+    __device__ __forceinline__ static bool reads_before(const Epi&, int) { return false; }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi&,
                                                  const V x[4], const V[4], lds_float* ostage) {

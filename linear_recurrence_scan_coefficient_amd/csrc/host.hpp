@@ -107,6 +107,13 @@ inline bool all_aligned(std::initializer_list<const void*> ptrs) {
     return true;
 }
 
+// A flag tensor's 4-element chunks are 16 bytes (float) or 4 bytes
+// (uint8_t): what the vector path needs of its base address.
+template <class F>
+inline bool flags_aligned(const F* p) {
+    return (reinterpret_cast<uintptr_t>(p) % (sizeof(F) * 4)) == 0;  // NULL is aligned
+}
+
 template <class E, int R, int W, bool VEC, bool CARRY>
 hipError_t launch_r(const typename E::Params& p, const Geometry& geo, const LookbackArgs& lb,
                     const Plan& pl, hipStream_t stream) {

@@ -122,12 +122,14 @@ __device__ __forceinline__ A scan_wave(const S (&e)[R][kChunk], A (&incl)[R]) {
 }
 
 // 5. state entering the tile, written to *sm_carry by wave 0 (call after the
-// wave totals are in sm_wave and the workgroup has synchronised)
+// wave totals are in sm_wave and the workgroup has synchronised).
+// `first_free` (lane 0 of wave 0): the tile's first step in scan order has
+// a == 0 and its output does not read the state before it, so no output of
+// the tile depends on the entering state and the look-back is skipped.
 template <class E, int W, bool LOOKBACK>
 __device__ __forceinline__ void tile_carry(const LookbackArgs& lb, uint64_t tile,
                                            const typename AggOf<typename E::S>::type* sm_wave,
-                                           typename E::S first_step,
-                                           typename E::V* sm_carry) {
+                                           bool first_free, typename E::V* sm_carry) {
     using A = typename AggOf<typename E::S>::type;
     using V = typename E::V;
     const int lane = threadIdx.x & (kWave - 1);
@@ -145,8 +147,7 @@ __device__ __forceinline__ void tile_carry(const LookbackArgs& lb, uint64_t tile
                 else
                     publish_aggregate(st, agg, lb.tag);
             }
-            // lane 0 of wave 0 holds the tile's first step in scan order
-            const bool first_cuts = __ballot(lane == 0 && cuts_chain(first_step)) != 0;
+            const bool first_cuts = __ballot(lane == 0 && first_free) != 0;
             V carry = V(0);
             if (tile > 0 && !first_cuts) carry = look_back<A, V>(lb, tile, lane);
             if (lane == 0) {
@@ -229,7 +230,11 @@ __device__ __forceinline__ void scan_tile(const typename E::Params& p, const Geo
 #pragma unroll
     for (int w = 0; w < W; ++w)
         if (w < wave) wpre = compose(sm_wave[w], wpre);
-    tile_carry<E, W, LOOKBACK>(lb, tile, sm_wave, e[0][0], sm_carry);
+    // lane 0 of wave 0 holds the tile's first step in scan order: element
+    // kChunk-1 of its first chunk for reverse estimators, element 0 otherwise
+    const bool first_free =
+        cuts_chain(e[0][0]) && !E::reads_before(epi[0], E::kReverse ? kChunk - 1 : 0);
+    tile_carry<E, W, LOOKBACK>(lb, tile, sm_wave, first_free, sm_carry);
     __syncthreads();
     replay_store<E, R, W, VEC, FULL, CARRY>(p, geo, tile, e, epi, incl, wpre, *sm_carry,
                                              ostage);

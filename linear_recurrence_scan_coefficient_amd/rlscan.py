@@ -48,6 +48,10 @@ EXPORTED = (
     "rlscan_gae_carry", "rlscan_lambda_returns_carry", "rlscan_discounted_returns_carry",
     "rlscan_vtrace_carry", "rlscan_retrace_carry", "rlscan_eligibility_traces_carry",
     "rlscan_episodic_prefix_sum_carry",
+    "rlscan_vtrace_ex", "rlscan_episodic_prefix_sum_f32",
+    "rlscan_gae_u8", "rlscan_lambda_returns_u8", "rlscan_discounted_returns_u8",
+    "rlscan_vtrace_u8", "rlscan_retrace_u8", "rlscan_eligibility_traces_u8",
+    "rlscan_episodic_prefix_sum_u8",
 )
 
 
@@ -85,6 +89,20 @@ def _declare(lib):
     lib.rlscan_retrace_carry.argtypes = [_vp] * 12 + [_i64, _i64, _i64, _f32, _f32, _vp]
     lib.rlscan_eligibility_traces_carry.argtypes = [_vp] * 5 + [_i64, _i64, _f32, _f32, _vp]
     lib.rlscan_episodic_prefix_sum_carry.argtypes = [_vp] * 5 + [_i64, _i64, _vp]
+    lib.rlscan_vtrace_ex.argtypes = [_vp] * 11 + [_i64, _i64] + [_f32] * 5 + [_vp]
+    lib.rlscan_episodic_prefix_sum_f32.argtypes = [_vp] * 5 + [_i64, _i64, _vp]
+    # the *_u8 calls take the argument list of the *_carry calls (V-trace: of
+    # rlscan_vtrace_ex) with one-byte flags
+    lib.rlscan_gae_u8.argtypes = lib.rlscan_gae_carry.argtypes
+    lib.rlscan_lambda_returns_u8.argtypes = lib.rlscan_lambda_returns_carry.argtypes
+    lib.rlscan_discounted_returns_u8.argtypes = lib.rlscan_discounted_returns_carry.argtypes
+    lib.rlscan_vtrace_u8.argtypes = lib.rlscan_vtrace_ex.argtypes
+    lib.rlscan_retrace_u8.argtypes = lib.rlscan_retrace_carry.argtypes
+    lib.rlscan_eligibility_traces_u8.argtypes = lib.rlscan_eligibility_traces_carry.argtypes
+    lib.rlscan_episodic_prefix_sum_u8.argtypes = lib.rlscan_episodic_prefix_sum_carry.argtypes
+    for name in EXPORTED:
+        if name.endswith(("_u8", "_ex", "_f32")):
+            getattr(lib, name).restype = ctypes.c_int
     for name in ("rlscan_gae", "rlscan_lambda_returns", "rlscan_discounted_returns",
                  "rlscan_vtrace", "rlscan_retrace", "rlscan_eligibility_traces",
                  "rlscan_episodic_prefix_sum", "rlscan_release_scratch"):
@@ -171,25 +189,51 @@ def _nt(t, name):
 # ------------------------------------------------------------------ entry points
 # Every entry point below takes optional carry_in / carry_out [N] tensors
 # (streaming one rollout through several calls); with either given it calls
-# the *_carry C function, else the plain one.
+# the *_carry C function, else the plain one.  Flags are float32, or uint8 /
+# bool (one byte, set iff != 0) for every flag of the call, which calls the
+# *_u8 C function.
 def _carry(carry_in, carry_out, N, dtype=torch.float32):
     return (carry_in is not None or carry_out is not None,
             _ptr(carry_in, dtype=dtype, shape=(N,), name="carry_in"),
             _ptr(carry_out, dtype=dtype, shape=(N,), name="carry_out"))
 
 
+_BYTE_FLAGS = (torch.uint8, torch.bool)
+
+
+def _byte_flags(flags: dict) -> bool:
+    """True if the given flag tensors are one-byte (uint8 or bool), False if
+    float32; a mix of the two is refused."""
+    kinds = {t.dtype in _BYTE_FLAGS for t in flags.values() if t is not None}
+    if len(kinds) > 1:
+        raise TypeError(f"flags {sorted(flags)} must all be float32 or all uint8/bool")
+    return kinds == {True}
+
+
+def _flag(t, N, T, name, byte):
+    if t is None:
+        return None
+    if byte:
+        if t.dtype not in _BYTE_FLAGS:
+            raise TypeError(f"{name} must be uint8 or bool, got {t.dtype}")
+        return _ptr(t, dtype=t.dtype, shape=(N, T), name=name)
+    return _ptr(t, shape=(N, T), name=name)
+
+
 def rlscan_gae(rewards, values, bootstrap_value, terminated, truncated, bootstrap_values,
                advantages, gamma, lam, stream=None, carry_in=None, carry_out=None):
     N, T = _nt(rewards, "rewards")
     use, ci, co = _carry(carry_in, carry_out, N)
+    byte = _byte_flags({"terminated": terminated, "truncated": truncated})
     ins = (_ptr(rewards, shape=(N, T), name="rewards"), _ptr(values, shape=(N, T), name="values"),
            _ptr(bootstrap_value, shape=(N,), name="bootstrap_value"),
-           _ptr(terminated, shape=(N, T), name="terminated"),
-           _ptr(truncated, shape=(N, T), name="truncated"),
+           _flag(terminated, N, T, "terminated", byte), _flag(truncated, N, T, "truncated", byte),
            _ptr(bootstrap_values, shape=(N, T), name="bootstrap_values"))
     out = _ptr(advantages, shape=(N, T), name="advantages")
     lib = library()
-    if use:
+    if byte:
+        _check(lib.rlscan_gae_u8(*ins, ci, out, co, N, T, gamma, lam, _stream(stream)))
+    elif use:
         _check(lib.rlscan_gae_carry(*ins, ci, out, co, N, T, gamma, lam, _stream(stream)))
     else:
         _check(lib.rlscan_gae(*ins, out, N, T, gamma, lam, _stream(stream)))
@@ -201,14 +245,17 @@ def rlscan_lambda_returns(rewards, values, bootstrap_value, terminated, truncate
                           carry_out=None):
     N, T = _nt(rewards, "rewards")
     use, ci, co = _carry(carry_in, carry_out, N)
+    byte = _byte_flags({"terminated": terminated, "truncated": truncated})
     ins = (_ptr(rewards, shape=(N, T), name="rewards"), _ptr(values, shape=(N, T), name="values"),
            _ptr(bootstrap_value, shape=(N,), name="bootstrap_value"),
-           _ptr(terminated, shape=(N, T), name="terminated"),
-           _ptr(truncated, shape=(N, T), name="truncated"),
+           _flag(terminated, N, T, "terminated", byte), _flag(truncated, N, T, "truncated", byte),
            _ptr(bootstrap_values, shape=(N, T), name="bootstrap_values"))
     out = _ptr(returns, shape=(N, T), name="returns")
     lib = library()
-    if use:
+    if byte:
+        _check(lib.rlscan_lambda_returns_u8(*ins, ci, out, co, N, T, gamma, lam,
+                                            _stream(stream)))
+    elif use:
         _check(lib.rlscan_lambda_returns_carry(*ins, ci, out, co, N, T, gamma, lam,
                                                _stream(stream)))
     else:
@@ -220,14 +267,17 @@ def rlscan_discounted_returns(rewards, bootstrap_value, terminated, truncated, b
                               returns, gamma, stream=None, carry_in=None, carry_out=None):
     N, T = _nt(rewards, "rewards")
     use, ci, co = _carry(carry_in, carry_out, N)
+    byte = _byte_flags({"terminated": terminated, "truncated": truncated})
     ins = (_ptr(rewards, shape=(N, T), name="rewards"),
            _ptr(bootstrap_value, shape=(N,), name="bootstrap_value"),
-           _ptr(terminated, shape=(N, T), name="terminated"),
-           _ptr(truncated, shape=(N, T), name="truncated"),
+           _flag(terminated, N, T, "terminated", byte), _flag(truncated, N, T, "truncated", byte),
            _ptr(bootstrap_values, shape=(N, T), name="bootstrap_values"))
     out = _ptr(returns, shape=(N, T), name="returns")
     lib = library()
-    if use:
+    if byte:
+        _check(lib.rlscan_discounted_returns_u8(*ins, ci, out, co, N, T, gamma,
+                                                _stream(stream)))
+    elif use:
         _check(lib.rlscan_discounted_returns_carry(*ins, ci, out, co, N, T, gamma,
                                                    _stream(stream)))
     else:
@@ -237,19 +287,30 @@ def rlscan_discounted_returns(rewards, bootstrap_value, terminated, truncated, b
 
 def rlscan_vtrace(rewards, values, bootstrap_value, log_rhos, terminated, truncated,
                   bootstrap_values, vs, pg_advantages, gamma, rho_bar, c_bar, stream=None,
-                  carry_in=None, carry_out=None):
+                  carry_in=None, carry_out=None, lam=None, rho_bar_pg=None):
+    """lam (trace factor) and rho_bar_pg (policy-gradient clip), when either is
+    given, call rlscan_vtrace_ex (None: 1 and rho_bar)."""
     N, T = _nt(rewards, "rewards")
     use, ci, co = _carry(carry_in, carry_out, N)
+    byte = _byte_flags({"terminated": terminated, "truncated": truncated})
     ins = (_ptr(rewards, shape=(N, T), name="rewards"), _ptr(values, shape=(N, T), name="values"),
            _ptr(bootstrap_value, shape=(N,), name="bootstrap_value"),
            _ptr(log_rhos, shape=(N, T), name="log_rhos"),
-           _ptr(terminated, shape=(N, T), name="terminated"),
-           _ptr(truncated, shape=(N, T), name="truncated"),
+           _flag(terminated, N, T, "terminated", byte), _flag(truncated, N, T, "truncated", byte),
            _ptr(bootstrap_values, shape=(N, T), name="bootstrap_values"))
     outs = (_ptr(vs, shape=(N, T), name="vs"),
             _ptr(pg_advantages, shape=(N, T), name="pg_advantages"))
     lib = library()
-    if use:
+    ex = lam is not None or rho_bar_pg is not None
+    lam = 1.0 if lam is None else lam
+    rho_bar_pg = rho_bar if rho_bar_pg is None else rho_bar_pg
+    if byte:
+        _check(lib.rlscan_vtrace_u8(*ins, ci, *outs, co, N, T, gamma, lam, rho_bar, c_bar,
+                                    rho_bar_pg, _stream(stream)))
+    elif ex:
+        _check(lib.rlscan_vtrace_ex(*ins, ci, *outs, co, N, T, gamma, lam, rho_bar, c_bar,
+                                    rho_bar_pg, _stream(stream)))
+    elif use:
         _check(lib.rlscan_vtrace_carry(*ins, ci, *outs, co, N, T, gamma, rho_bar, c_bar,
                                        _stream(stream)))
     else:
@@ -265,20 +326,20 @@ def rlscan_retrace(rewards, next_q_values_all, next_target_probs, actions, behav
         raise ValueError("next_q_values_all must be a [N, T, A] tensor")
     A = next_q_values_all.shape[2]
     use, ci, co = _carry(carry_in, carry_out, N)
+    byte = _byte_flags({"terminated": terminated, "truncated": truncated})
     ins = (_ptr(rewards, shape=(N, T), name="rewards"),
            _ptr(next_q_values_all, shape=(N, T, A), name="next_q_values_all"),
            _ptr(next_target_probs, shape=(N, T, A), name="next_target_probs"),
            _ptr(actions, dtype=torch.int32, shape=(N, T), name="actions"),
            _ptr(behaviour_probs, shape=(N, T), name="behaviour_probs"),
-           _ptr(terminated, shape=(N, T), name="terminated"),
-           _ptr(truncated, shape=(N, T), name="truncated"))
+           _flag(terminated, N, T, "terminated", byte), _flag(truncated, N, T, "truncated", byte))
     out = _ptr(targets, shape=(N, T), name="targets")
     lib = library()
-    if use:
-        _check(lib.rlscan_retrace_carry(
-            *ins, ci, _ptr(next_actions, dtype=torch.int32, shape=(N,), name="next_actions"),
-            _ptr(next_behaviour_probs, shape=(N,), name="next_behaviour_probs"), out, co,
-            N, T, A, gamma, lam, _stream(stream)))
+    if use or byte:
+        fn = lib.rlscan_retrace_u8 if byte else lib.rlscan_retrace_carry
+        _check(fn(*ins, ci, _ptr(next_actions, dtype=torch.int32, shape=(N,), name="next_actions"),
+                  _ptr(next_behaviour_probs, shape=(N,), name="next_behaviour_probs"), out, co,
+                  N, T, A, gamma, lam, _stream(stream)))
     else:
         _check(lib.rlscan_retrace(*ins, out, N, T, A, gamma, lam, _stream(stream)))
     return targets
@@ -288,10 +349,14 @@ def rlscan_eligibility_traces(x, dones, traces, gamma, lam, stream=None, carry_i
                               carry_out=None):
     N, T = _nt(x, "x")
     use, ci, co = _carry(carry_in, carry_out, N)
-    ins = (_ptr(x, shape=(N, T), name="x"), _ptr(dones, shape=(N, T), name="dones"))
+    byte = _byte_flags({"dones": dones})
+    ins = (_ptr(x, shape=(N, T), name="x"), _flag(dones, N, T, "dones", byte))
     out = _ptr(traces, shape=(N, T), name="traces")
     lib = library()
-    if use:
+    if byte:
+        _check(lib.rlscan_eligibility_traces_u8(*ins, ci, out, co, N, T, gamma, lam,
+                                                _stream(stream)))
+    elif use:
         _check(lib.rlscan_eligibility_traces_carry(*ins, ci, out, co, N, T, gamma, lam,
                                                    _stream(stream)))
     else:
@@ -302,15 +367,95 @@ def rlscan_eligibility_traces(x, dones, traces, gamma, lam, stream=None, carry_i
 def rlscan_episodic_prefix_sum(x, dones, out, stream=None, carry_in=None, carry_out=None):
     N, T = _nt(x, "x")
     use, ci, co = _carry(carry_in, carry_out, N, dtype=torch.int64)
-    ins = (_ptr(x, dtype=torch.int32, shape=(N, T), name="x"),
-           _ptr(dones, shape=(N, T), name="dones"))
+    byte = _byte_flags({"dones": dones})
+    ins = (_ptr(x, dtype=torch.int32, shape=(N, T), name="x"), _flag(dones, N, T, "dones", byte))
     o = _ptr(out, dtype=torch.int64, shape=(N, T), name="out")
     lib = library()
-    if use:
+    if byte:
+        _check(lib.rlscan_episodic_prefix_sum_u8(*ins, ci, o, co, N, T, _stream(stream)))
+    elif use:
         _check(lib.rlscan_episodic_prefix_sum_carry(*ins, ci, o, co, N, T, _stream(stream)))
     else:
         _check(lib.rlscan_episodic_prefix_sum(*ins, o, N, T, _stream(stream)))
     return out
+
+
+def rlscan_episodic_prefix_sum_f32(x, dones, out, stream=None, carry_in=None, carry_out=None):
+    """Episodic prefix sum of float32 values x [N, T] into float32 out."""
+    N, T = _nt(x, "x")
+    _, ci, co = _carry(carry_in, carry_out, N)
+    _check(library().rlscan_episodic_prefix_sum_f32(
+        _ptr(x, shape=(N, T), name="x"), _ptr(dones, shape=(N, T), name="dones"), ci,
+        _ptr(out, shape=(N, T), name="out"), co, N, T, _stream(stream)))
+    return out
+
+
+def _require_byte_flags(**flags):
+    if not _byte_flags(flags) or any(t is None for k, t in flags.items() if k != "truncated"):
+        raise TypeError(f"{', '.join(flags)} must be uint8 or bool tensors")
+
+
+# The *_u8 names of the C ABI: the calls above with one-byte flags required.
+def rlscan_gae_u8(rewards, values, bootstrap_value, terminated, truncated, bootstrap_values,
+                  advantages, gamma, lam, stream=None, carry_in=None, carry_out=None):
+    _require_byte_flags(terminated=terminated, truncated=truncated)
+    return rlscan_gae(rewards, values, bootstrap_value, terminated, truncated, bootstrap_values,
+                      advantages, gamma, lam, stream, carry_in, carry_out)
+
+
+def rlscan_lambda_returns_u8(rewards, values, bootstrap_value, terminated, truncated,
+                             bootstrap_values, returns, gamma, lam, stream=None, carry_in=None,
+                             carry_out=None):
+    _require_byte_flags(terminated=terminated, truncated=truncated)
+    return rlscan_lambda_returns(rewards, values, bootstrap_value, terminated, truncated,
+                                 bootstrap_values, returns, gamma, lam, stream, carry_in,
+                                 carry_out)
+
+
+def rlscan_discounted_returns_u8(rewards, bootstrap_value, terminated, truncated,
+                                 bootstrap_values, returns, gamma, stream=None, carry_in=None,
+                                 carry_out=None):
+    _require_byte_flags(terminated=terminated, truncated=truncated)
+    return rlscan_discounted_returns(rewards, bootstrap_value, terminated, truncated,
+                                     bootstrap_values, returns, gamma, stream, carry_in,
+                                     carry_out)
+
+
+def rlscan_vtrace_ex(rewards, values, bootstrap_value, log_rhos, terminated, truncated,
+                     bootstrap_values, vs, pg_advantages, gamma, lam, rho_bar, c_bar,
+                     rho_bar_pg, stream=None, carry_in=None, carry_out=None):
+    return rlscan_vtrace(rewards, values, bootstrap_value, log_rhos, terminated, truncated,
+                         bootstrap_values, vs, pg_advantages, gamma, rho_bar, c_bar, stream,
+                         carry_in, carry_out, lam=lam, rho_bar_pg=rho_bar_pg)
+
+
+def rlscan_vtrace_u8(rewards, values, bootstrap_value, log_rhos, terminated, truncated,
+                     bootstrap_values, vs, pg_advantages, gamma, lam, rho_bar, c_bar,
+                     rho_bar_pg, stream=None, carry_in=None, carry_out=None):
+    _require_byte_flags(terminated=terminated, truncated=truncated)
+    return rlscan_vtrace_ex(rewards, values, bootstrap_value, log_rhos, terminated, truncated,
+                            bootstrap_values, vs, pg_advantages, gamma, lam, rho_bar, c_bar,
+                            rho_bar_pg, stream, carry_in, carry_out)
+
+
+def rlscan_retrace_u8(rewards, next_q_values_all, next_target_probs, actions, behaviour_probs,
+                      terminated, truncated, targets, gamma, lam, stream=None, carry_in=None,
+                      carry_out=None, next_actions=None, next_behaviour_probs=None):
+    _require_byte_flags(terminated=terminated, truncated=truncated)
+    return rlscan_retrace(rewards, next_q_values_all, next_target_probs, actions,
+                          behaviour_probs, terminated, truncated, targets, gamma, lam, stream,
+                          carry_in, carry_out, next_actions, next_behaviour_probs)
+
+
+def rlscan_eligibility_traces_u8(x, dones, traces, gamma, lam, stream=None, carry_in=None,
+                                 carry_out=None):
+    _require_byte_flags(dones=dones)
+    return rlscan_eligibility_traces(x, dones, traces, gamma, lam, stream, carry_in, carry_out)
+
+
+def rlscan_episodic_prefix_sum_u8(x, dones, out, stream=None, carry_in=None, carry_out=None):
+    _require_byte_flags(dones=dones)
+    return rlscan_episodic_prefix_sum(x, dones, out, stream, carry_in, carry_out)
 
 
 def rlscan_release_scratch():

@@ -221,3 +221,38 @@ def test_carry_entry_points_argument_checks(lib):
     assert f.rlscan_discounted_returns_carry(*P[:8], 4, 8, 1.5, None) == PARAM
     assert f.rlscan_vtrace_carry(*P[:11], 4, 8, 0.9, 0.0, 1.0, None) == PARAM
     assert f.rlscan_lambda_returns_carry(*P[:9], -1, 8, 0.9, 0.9, None) == SHAPE
+
+
+def test_variant_entry_points_argument_checks(lib):
+    """V-trace options, the float prefix sum and the one-byte-flag calls:
+    their own parameter checks, and the shared ones (nothing is launched:
+    every case below returns before any HIP call)."""
+    f = lib
+    vt = list(P[:11])  # 7 inputs, carry_in, vs, pg, carry_out
+    for lam, pg in ((1.5, 1.0), (-0.5, 1.0), (math.nan, 1.0), (0.9, 0.0), (0.9, -2.0),
+                    (0.9, math.nan)):
+        assert f.rlscan_vtrace_ex(*vt, 4, 8, 0.9, lam, 1.0, 1.0, pg, None) == PARAM
+        assert f.rlscan_vtrace_u8(*vt, 4, 8, 0.9, lam, 1.0, 1.0, pg, None) == PARAM
+    bad = list(vt)
+    bad[9] = bad[8]
+    assert f.rlscan_vtrace_ex(*bad, 4, 8, 0.9, 0.9, 1.0, 1.0, math.inf, None) == ALIAS
+    assert f.rlscan_vtrace_ex(*[None] * 11, 0, 8, 0.9, 0.9, 1.0, 1.0, 1.0, None) == OK
+    # float prefix sum: x, dones, carry_in, out, carry_out
+    assert f.rlscan_episodic_prefix_sum_f32(P[0], None, None, P[3], None, 4, 8, None) == NULL
+    assert f.rlscan_episodic_prefix_sum_f32(P[0], P[1], None, P[0], None, 4, 8, None) == ALIAS
+    assert f.rlscan_episodic_prefix_sum_f32(P[0], P[1], None, P[3], None, -1, 8, None) == SHAPE
+    assert f.rlscan_episodic_prefix_sum_f32(None, None, None, None, None, 4, 0, None) == OK
+    # one-byte flags: the checks of the *_carry calls
+    assert f.rlscan_gae_u8(*P[:9], 4, 8, 1.5, 0.9, None) == PARAM
+    assert f.rlscan_gae_u8(P[0], P[1], P[2], None, *P[4:9], 4, 8, 0.9, 0.9, None) == NULL
+    assert f.rlscan_lambda_returns_u8(*P[:6], None, P[7], P[7], 4, 8, 0.9, 0.9, None) == ALIAS
+    assert f.rlscan_discounted_returns_u8(P[0], None, P[2], P[3], None, None, P[6], None, 4, 8,
+                                          0.9, None) == NULL
+    r = list(P[:7]) + [P[7], None, P[9], P[10], P[11]]
+    assert f.rlscan_retrace_u8(*r, 4, 8, 6, 0.9, 0.9, None) == NULL
+    r = list(P[:5]) + [P[5], None] + [None, None, None, P[10], None]
+    assert f.rlscan_retrace_u8(*r, 4, 8, 6, 0.9, 0.9, None) == NULL
+    assert f.rlscan_eligibility_traces_u8(P[0], P[1], None, P[1], None, 4, 8, 0.9, 0.9,
+                                          None) == ALIAS
+    assert f.rlscan_episodic_prefix_sum_u8(P[0], None, None, P[3], None, 4, 8, None) == NULL
+    assert f.rlscan_episodic_prefix_sum_u8(None, None, None, None, None, 0, 0, None) == OK
