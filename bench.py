@@ -9,22 +9,23 @@ rotate over several buffer sets whose total exceeds the 256 MiB last-level
 cache, so each call reads its inputs from HBM.  Inputs are resident on the
 GPU before the timed region starts.
 
-Timing.  The timed region is K steps, each the seven C calls on the next
-buffer set launched one after another on one stream, bracketed by device
-synchronisation; `value` is estimator-elements per second over it (7 * N * T
-elements per step), `ms_per_step` its mean.  The same steps as one HIP graph
-replay each (every call here takes the packed mapping, which launches one
-kernel and is graph-safe; a replay carries a fixed cost of a few
-microseconds, so these are slower) and the calls on one warm buffer set are
-reported beside it.  Each estimator's average launch duration is then
-measured live with HIP events around replays of a graph of M back-to-back
-launches over M distinct buffer sets (M * bytes >= 512 MiB, so inputs come
-from HBM); `roofline` reports the estimator with the longest launch.  The
+Timing.  The timed region is K steps, each one rlscan_group call that runs
+the seven estimator calls of the next buffer set in one kernel launch,
+bracketed by device synchronisation; `value` is estimator-elements per
+second over it (7 * N * T elements per step), `ms_per_step` its mean, and
+`roofline` the grouped kernel: the step's algorithmic bytes over its average
+launch duration (HIP events on the launch stream around the timed region).
+Beside it: the same seven calls made one by one on one stream (eager, as one
+HIP graph replay per step, and on one warm buffer set), the grouped step at
+each wave count, and each estimator's own average launch duration, measured
+with HIP events around replays of a graph of M back-to-back launches over M
+distinct buffer sets (M * bytes >= 512 MiB, so inputs come from HBM).  The
 long-sequence workload (8 x 2^20 steps, four estimators, decoupled
 look-back; timed over back-to-back calls, and with events around each
-call), a supplementary
-large-batch workload (2^20 x 32, packed), the bandwidth of a plain streaming
-copy moving the same bytes as each call, and the float64 oracle timed on one
+call), the same rollout streamed through the carry calls, a supplementary
+large-batch workload (2^20 x 32, packed), the estimator variants (one-byte
+flags, V-trace options, float prefix sum), the bandwidth of a plain
+streaming copy moving the same bytes, and the float64 oracle timed on one
 host core are reported as well.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -70,12 +71,17 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the one-byte-flag, V-trace-option and float-prefix figures")
     ap.add_argument("--only", default=None, help="comma list of estimators (profiling runs)")
     ap.add_argument("--pmc-run", default=None, metavar="ESTIMATOR",
-                    help="counter runs: launch ESTIMATOR ('all': each estimator in turn) once "
+                    help="counter runs: launch ESTIMATOR ('all': each estimator in turn; "
+                         "'group': the workload's estimators as one rlscan_group launch) once "
                          "on each of several cold buffer sets of --pmc-workload, then copy a "
                          "256 MiB buffer with the library's streaming copy")
     ap.add_argument("--pmc-workload", default="production_4096x128")
+    ap.add_argument("--pmc-byte-flags", action="store_true",
+                    help="counter runs with uint8 flags (the *_u8 entry points)")
     ap.add_argument("--traffic-summary", nargs=4, default=None,
                     metavar=("RUN_LOG", "FETCH_CSV", "WRITE_CSV", "HIT_CSV"),
                     help="write profiles/traffic_<estimator>_<workload>.txt from the stdout "
@@ -88,7 +94,7 @@ def parse_args():
 COPY_BYTES = 256 << 20
 
 
-def pmc_run(torch, est, workload, sh, lib):
+def pmc_run(torch, est, workload, sh, lib, byte_flags=False):
     """Launches for `rocprofv3 --pmc`: the estimator on M distinct buffer
     sets (cold inputs), then a plain streaming copy of COPY_BYTES (reads and
     writes COPY_BYTES each), the calibration for FETCH_SIZE and WRITE_SIZE."""
@@ -96,11 +102,25 @@ def pmc_run(torch, est, workload, sh, lib):
     w = workloads.get(workload)
     ests = list(w.estimators) if est == "all" else [est]
     launches, per_bytes = {}, {}
+    if est == "group":  # the workload's estimators in one rlscan_group launch per set
+        ests = []
+        probe = CallSet(list(w.estimators), w, 0, sh, lib, byte_flags)
+        b = sum(probe.bytes.values())
+        m = max(6, min(32, -(-(512 << 20) // b)))
+        sets = [probe] + [CallSet(list(w.estimators), w, seed, sh, lib, byte_flags)
+                          for seed in range(1, m)]
+        groups = [cs.group_array() for cs in sets]
+        torch.cuda.synchronize()
+        for arr, n, _ in groups:
+            assert lib.rlscan_group(arr, n, sh) == 0
+        torch.cuda.synchronize()
+        launches["group"], per_bytes["group"] = m, b
+        del sets, groups, probe
     for e in ests:
-        probe = CallSet([e], w, 0, sh, lib)
+        probe = CallSet([e], w, 0, sh, lib, byte_flags)
         b = probe.bytes[e]
         m = max(6, min(32, -(-(512 << 20) // b)))
-        sets = [probe] + [CallSet([e], w, seed, sh, lib) for seed in range(1, m)]
+        sets = [probe] + [CallSet([e], w, seed, sh, lib, byte_flags) for seed in range(1, m)]
         torch.cuda.synchronize()
         for cs in sets:
             cs.run()
@@ -113,7 +133,8 @@ def pmc_run(torch, est, workload, sh, lib):
     for _ in range(3):
         rlscan.rlscan_stream_copy(dst, src)
     torch.cuda.synchronize()
-    print(json.dumps({"pmc_run": est, "workload": w.name, "launches": launches,
+    print(json.dumps({"pmc_run": est, "workload": w.name, "byte_flags": byte_flags,
+                      "launches": launches,
                       "algorithmic_bytes_per_launch": per_bytes, "copy_bytes": COPY_BYTES,
                       "kernel_source_hash": kernel_source_hash()}), flush=True)
 
@@ -143,7 +164,7 @@ def traffic_summary(run_log, fetch_csv, write_csv, hit_csv):
     def mean(xs):
         return sum(xs) / len(xs)
 
-    is_scan = lambda k: "rlscan::scan_kernel" in k  # noqa: E731
+    is_scan = lambda k: "rlscan::scan_kernel" in k or "rlscan::group_kernel" in k  # noqa: E731
     is_copy = lambda k: "rlscan::copy_kernel" in k  # noqa: E731
     F, W, H = load(fetch_csv), load(write_csv), load(hit_csv)
     kf, kw = values(F, is_scan, "FETCH_SIZE"), values(W, is_scan, "WRITE_SIZE")
@@ -156,15 +177,20 @@ def traffic_summary(run_log, fetch_csv, write_csv, hit_csv):
     kname = sorted({k for (k, c) in F if is_scan(k)})
     wl = meta["workload"]
     cmd = f"python3 bench.py --pmc-run {est} --pmc-workload {wl}"
+    tag = est
+    if meta.get("byte_flags"):
+        cmd += " --pmc-byte-flags"
+        wl += "_u8_flags"
+        tag += "_u8"
     text = f"""# HBM traffic per launch: {est}, {wl}
 #
 # Commands (repository root, one MI355X; TMPDIR=/tmp), one counter pass each:
-#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o {est} -- {cmd}
-#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o {est} -- {cmd}
-#   rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv -d gpurun_out/pmc_hit -o {est} -- {cmd}
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o {tag} -- {cmd}
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o {tag} -- {cmd}
+#   rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv -d gpurun_out/pmc_hit -o {tag} -- {cmd}
 # then, on any machine: python3 bench.py --traffic-summary <stdout of the FETCH_SIZE pass>
-#   gpurun_out/pmc_fetch/{est}_counter_collection.csv gpurun_out/pmc_write/{est}_counter_collection.csv
-#   gpurun_out/pmc_hit/{est}_counter_collection.csv
+#   gpurun_out/pmc_fetch/{tag}_counter_collection.csv gpurun_out/pmc_write/{tag}_counter_collection.csv
+#   gpurun_out/pmc_hit/{tag}_counter_collection.csv
 # `--pmc-run` launches the kernel once on each of {meta["launches"][est]} distinct buffer sets
 # (cold inputs), then copies a {cb >> 20} MiB buffer with the library's streaming copy kernel
 # (the calibration: it reads and writes exactly {cb} bytes).
@@ -329,6 +355,63 @@ def time_streamed(torch, w, sh, lib, chunks, reps):
     return res
 
 
+def raw_u8_call_args(est, d, out, w, stream):
+    """The C argument tuple of one *_u8 call (one-byte flags in `d`; no
+    carry; V-trace with lambda = 1 and rho_bar_pg = rho_bar)."""
+    def p(t):
+        return None if t is None else t.data_ptr()
+    N, T = w.N, w.T
+    if est in ("gae", "lambda_returns"):
+        return (f"rlscan_{est}_u8", (p(d["rewards"]), p(d["values"]), p(d.get("bootstrap_value")),
+                                     p(d["terminated"]), p(d.get("truncated")),
+                                     p(d.get("bootstrap_values")), None,
+                                     p(out["advantages" if est == "gae" else "returns"]), None,
+                                     N, T, w.gamma, w.lam, stream))
+    if est == "discounted_returns":
+        return ("rlscan_discounted_returns_u8", (p(d["rewards"]), p(d.get("bootstrap_value")),
+                                                 p(d["terminated"]), p(d.get("truncated")),
+                                                 p(d.get("bootstrap_values")), None,
+                                                 p(out["returns"]), None, N, T, w.gamma, stream))
+    if est == "vtrace":
+        return ("rlscan_vtrace_u8", (p(d["rewards"]), p(d["values"]), p(d.get("bootstrap_value")),
+                                     p(d["log_rhos"]), p(d["terminated"]), p(d.get("truncated")),
+                                     p(d.get("bootstrap_values")), None, p(out["vs"]),
+                                     p(out["pg_advantages"]), None, N, T, w.gamma, 1.0,
+                                     w.rho_bar, w.c_bar, w.rho_bar, stream))
+    if est == "retrace":
+        A = d["next_q_values_all"].shape[2]
+        return ("rlscan_retrace_u8", (p(d["rewards"]), p(d["next_q_values_all"]),
+                                      p(d["next_target_probs"]), p(d["actions"]),
+                                      p(d["behaviour_probs"]), p(d["terminated"]),
+                                      p(d["truncated"]), None, None, None, p(out["targets"]),
+                                      None, N, T, A, w.gamma, w.lam, stream))
+    if est == "eligibility_traces":
+        return ("rlscan_eligibility_traces_u8", (p(d["x"]), p(d["dones"]), None, p(out["traces"]),
+                                                 None, N, T, w.gamma, w.lam, stream))
+    if est == "episodic_prefix_sum":
+        return ("rlscan_episodic_prefix_sum_u8", (p(d["x"]), p(d["dones"]), None, p(out["out"]),
+                                                  None, N, T, stream))
+    raise ValueError(est)
+
+
+FLAG_KEYS = ("terminated", "truncated", "dones")
+
+# each estimator's inputs in the order of its plain entry point
+GROUP_INPUTS = {
+    "gae": ("rewards", "values", "bootstrap_value", "terminated", "truncated", "bootstrap_values"),
+    "lambda_returns": ("rewards", "values", "bootstrap_value", "terminated", "truncated",
+                       "bootstrap_values"),
+    "discounted_returns": ("rewards", "bootstrap_value", "terminated", "truncated",
+                           "bootstrap_values"),
+    "vtrace": ("rewards", "values", "bootstrap_value", "log_rhos", "terminated", "truncated",
+               "bootstrap_values"),
+    "retrace": ("rewards", "next_q_values_all", "next_target_probs", "actions",
+                "behaviour_probs", "terminated", "truncated"),
+    "eligibility_traces": ("x", "dones"),
+    "episodic_prefix_sum": ("x", "dones"),
+}
+
+
 def algorithmic_bytes(inputs: dict, outputs: dict) -> int:
     """Bytes the method must move: every input read once, every output
     written once."""
@@ -337,21 +420,42 @@ def algorithmic_bytes(inputs: dict, outputs: dict) -> int:
 
 
 class CallSet:
-    """Device buffers and ready-made C calls for a list of estimators."""
+    """Device buffers and ready-made C calls for a list of estimators
+    (byte_flags: flags as uint8, through the *_u8 entry points)."""
 
-    def __init__(self, estimators, w, seed, stream_handle, lib):
+    def __init__(self, estimators, w, seed, stream_handle, lib, byte_flags=False):
+        import numpy as np
         from linear_recurrence_scan_coefficient_amd import device, workloads
         self.calls = []
         self.bytes = {}
         self.keep = []
         for est in estimators:
             host = workloads.inputs_for(est, w, seed)
+            if byte_flags:
+                host = {k: ((v != 0).astype(np.uint8) if k in FLAG_KEYS and v is not None else v)
+                        for k, v in host.items()}
             d = device.upload(host)
             out = device.alloc_outputs(est, w.N, w.T)
-            name, args = raw_call_args(est, d, out, w, stream_handle)
+            make = raw_u8_call_args if byte_flags else raw_call_args
+            name, args = make(est, d, out, w, stream_handle)
             self.calls.append((est, getattr(lib, name), args))
             self.bytes[est] = algorithmic_bytes(host, out)
             self.keep.append((d, out))
+        self.w = w
+
+    def group_array(self):
+        """The set's calls as one rlscan_group argument array."""
+        from linear_recurrence_scan_coefficient_amd import device, rlscan
+        calls = []
+        for (est, _, _), (d, out) in zip(self.calls, self.keep):
+            ins = tuple(d.get(k) for k in GROUP_INPUTS[est])
+            outs = tuple(out[name] for name, _ in device.OUTPUTS[est])
+            w = self.w
+            calls.append(rlscan.GroupCall(est, ins, outs, gamma=w.gamma,
+                                          lam=1.0 if est == "vtrace" else w.lam,
+                                          rho_bar=w.rho_bar, c_bar=w.c_bar))
+        arr = (rlscan.Call * len(calls))(*[c.call for c in calls])
+        return arr, len(calls), calls
 
     def run(self, events=None):
         for i, (est, fn, args) in enumerate(self.calls):
@@ -405,13 +509,13 @@ def time_batched_calls(torch, sets, reps):
     return out
 
 
-def eager_workload(torch, w, sh, lib, reps, nsets=3):
+def eager_workload(torch, w, sh, lib, reps, nsets=3, byte_flags=False):
     """Per-call figures of every estimator of a large workload: `reps`
     back-to-back calls per estimator cycling through `nsets` buffer sets (each
     set alone exceeds the last-level cache, so inputs come from HBM), the
     same calls with an event pair around each one (what one isolated call
     costs, launch gap included), and the copy ceiling for the same bytes."""
-    sets = [CallSet(w.estimators, w, seed, sh, lib) for seed in range(nsets)]
+    sets = [CallSet(w.estimators, w, seed, sh, lib, byte_flags) for seed in range(nsets)]
     per = time_batched_calls(torch, sets, reps)
     iso = time_eager_calls(torch, sets, reps)
     nbytes = dict(sets[0].bytes)
@@ -456,6 +560,28 @@ def time_graph_steps(torch, graphs, steps, warmup):
     return time.perf_counter() - t0
 
 
+def time_group_steps(torch, lib, groups, sh, steps, warmup):
+    """Wall seconds of `steps` steps, each one rlscan_group call of the next
+    set's calls, and the device milliseconds between HIP events recorded on
+    the launch stream around them."""
+    def step(i):
+        arr, n, _ = groups[i % len(groups)]
+        rc = lib.rlscan_group(arr, n, sh)
+        if rc != 0:
+            raise RuntimeError(f"rlscan_group status {rc}")
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for i in range(steps):
+        step(i)
+    b.record()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, a.elapsed_time(b)
+
+
 def time_eager_steps(torch, sets, steps, warmup):
     """Wall seconds of `steps` steps launched one C call at a time."""
     for i in range(warmup):
@@ -485,13 +611,13 @@ def time_launches(torch, graph, launches, reps):
     return sum(ms) / len(ms) / launches * 1000.0
 
 
-def per_kernel(torch, est, w, sh, lib, min_bytes=512 << 20, reps=10):
+def per_kernel(torch, est, w, sh, lib, min_bytes=512 << 20, reps=10, byte_flags=False):
     """Average launch duration of one estimator over M distinct buffer sets
     (M * bytes >= min_bytes, so every launch reads cold inputs)."""
-    probe = CallSet([est], w, 0, sh, lib)
+    probe = CallSet([est], w, 0, sh, lib, byte_flags)
     b = probe.bytes[est]
     m = max(6, min(64, -(-min_bytes // b)))
-    sets = [probe] + [CallSet([est], w, seed, sh, lib) for seed in range(1, m)]
+    sets = [probe] + [CallSet([est], w, seed, sh, lib, byte_flags) for seed in range(1, m)]
     g = capture_graph(torch, [s.calls[0] for s in sets])
     us = time_launches(torch, g, m, reps)
     del g, sets
@@ -576,6 +702,99 @@ def cpu_model() -> str:
     return platform.processor() or platform.machine()
 
 
+def time_variants(torch, w, ests, sh, lib, args):
+    """The estimator variants: the production step and the long-rollout calls
+    with one-byte flags (their algorithmic bytes count 1 byte per flag), and
+    V-trace with lambda and a policy-gradient clip and the float-valued
+    prefix sum as single-call figures."""
+    from linear_recurrence_scan_coefficient_amd import workloads
+    res = {}
+    sets = [CallSet(ests, w, seed, sh, lib, byte_flags=True) for seed in range(args.sets)]
+    wall = time_eager_steps(torch, sets, args.steps, args.warmup)
+    step_bytes = sum(sets[0].bytes.values())
+    del sets
+    torch.cuda.empty_cache()
+    per = {}
+    for e in ests:
+        us, b, _ = per_kernel(torch, e, w, sh, lib, byte_flags=True)
+        per[e] = {"us_per_call": round(us, 3), "bytes": b,
+                  "GB_per_s": round(b / (us * 1e-6) / 1e9, 1)}
+    res["production_u8_flags"] = {
+        "value": len(ests) * w.N * w.T * args.steps / wall, "unit": "elements/s",
+        "ms_per_step": wall * 1000.0 / args.steps, "bytes_per_step": step_bytes,
+        "per_estimator": per,
+        "note": "the same seven-call step with uint8 flags (the *_u8 entry points)"}
+    if not args.no_long:
+        wl = workloads.get("long_8x1048576")
+        res["long_8x1048576_u8_flags"] = eager_workload(torch, wl, sh, lib, args.long_calls,
+                                                        byte_flags=True)
+    res["vtrace_lambda_pg_clip"] = time_vtrace_ex(torch, w, sh, lib)
+    if not args.no_long:
+        res["prefix_sum_f32_long_8x1048576"] = time_prefix_f32(torch, sh, lib, args.long_calls)
+    return res
+
+
+def time_vtrace_ex(torch, w, sh, lib, reps=200, nsets=4):
+    """rlscan_vtrace_ex (lambda 0.95, rho_bar_pg 0.5) against rlscan_vtrace on
+    the same production buffers: mean us per call from one event pair around
+    `reps` back-to-back calls."""
+    from linear_recurrence_scan_coefficient_amd import device, workloads
+    keep, plain, ex = [], [], []
+    for seed in range(nsets):
+        d = device.upload(workloads.inputs_for("vtrace", w, seed))
+        out = device.alloc_outputs("vtrace", w.N, w.T)
+        keep.append((d, out))
+        name, a = raw_call_args("vtrace", d, out, w, sh)
+        plain.append((getattr(lib, name), a))
+        ex_args = a[:7] + (None,) + a[7:9] + (None, w.N, w.T, w.gamma, 0.95, w.rho_bar, w.c_bar,
+                                               0.5, sh)
+        ex.append((lib.rlscan_vtrace_ex, ex_args))
+    res = {}
+    for label, calls in (("plain_us_per_call", plain), ("ex_us_per_call", ex)):
+        for fn, a in calls:
+            assert fn(*a) == 0
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            fn, a = calls[i % len(calls)]
+            fn(*a)
+        e1.record()
+        torch.cuda.synchronize()
+        res[label] = round(e0.elapsed_time(e1) / reps * 1000.0, 3)
+    res["workload"] = w.name
+    return res
+
+
+def time_prefix_f32(torch, sh, lib, reps, nsets=3):
+    """rlscan_episodic_prefix_sum_f32 on the long-rollout shape (8 x 2^20,
+    float32 x ~ N(0,1), dones ~ Bernoulli(1e-4)): back-to-back calls over
+    buffer sets larger than the last-level cache."""
+    import numpy as np
+    N, T = 8, 1 << 20
+    bufs = []
+    for seed in range(nsets):
+        rng = np.random.default_rng(1000 + seed)
+        x = torch.from_numpy(rng.standard_normal((N, T)).astype(np.float32)).cuda()
+        dn = torch.from_numpy((rng.random((N, T)) < 1e-4).astype(np.float32)).cuda()
+        bufs.append((x, dn, torch.empty((N, T), device="cuda")))
+    calls = [(x.data_ptr(), dn.data_ptr(), None, o.data_ptr(), None, N, T, sh) for x, dn, o in bufs]
+    for a in calls:
+        assert lib.rlscan_episodic_prefix_sum_f32(*a) == 0
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        lib.rlscan_episodic_prefix_sum_f32(*calls[i % len(calls)])
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1000.0
+    nbytes = 12 * N * T
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us_per_call": round(us, 2), "bytes": nbytes, "GB_per_s": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -597,7 +816,7 @@ def main():
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     if args.pmc_run:
-        pmc_run(torch, args.pmc_run, args.pmc_workload, sh, lib)
+        pmc_run(torch, args.pmc_run, args.pmc_workload, sh, lib, args.pmc_byte_flags)
         return
 
     w = workloads.get("production_4096x128")
@@ -607,19 +826,33 @@ def main():
     print(f"[bench] preparing {args.sets} buffer sets of {w.name}", file=sys.stderr, flush=True)
     sets = [CallSet(ests, w, seed, sh, lib) for seed in range(args.sets)]
     set_bytes = sum(sets[0].bytes.values())
-    graphs = [capture_graph(torch, s.calls) for s in sets]
+    groups = [s.group_array() for s in sets]
     elems_per_step = len(ests) * w.N * w.T
 
-    # timed region: K steps, each the seven C calls on the next buffer set,
-    # launched one after another on one stream
+    # timed region: K steps, each one rlscan_group call that runs the seven
+    # estimator calls of the next buffer set in one kernel launch
     print("[bench] timing production steps", file=sys.stderr, flush=True)
-    wall = time_eager_steps(torch, sets, args.steps, args.warmup)
+    wall, dev_ms = time_group_steps(torch, lib, groups, sh, args.steps, args.warmup)
     ms_per_step = wall * 1000.0 / args.steps
     value = elems_per_step * args.steps / wall
-    # the same steps as one HIP graph replay each, and on one warm set
+    launch_us = dev_ms * 1000.0 / args.steps
+    group_gbs = set_bytes / (launch_us * 1e-6) / 1e9
+
+    # the same seven calls made one by one on one stream: eager, as one HIP
+    # graph replay per step, and on one warm set
+    print("[bench] timing the seven calls made one by one", file=sys.stderr, flush=True)
+    graphs = [capture_graph(torch, s.calls) for s in sets]
+    wall_sep = time_eager_steps(torch, sets, args.steps, args.warmup)
     wall_graph = time_graph_steps(torch, graphs, args.steps, args.warmup)
     wall_warm = time_eager_steps(torch, sets[:1], args.steps, args.warmup)
     del graphs
+    waves_sweep = {}
+    for wv in (1, 2, 4):
+        rlscan.rlscan_set_launch_override(waves=wv)
+        wall_g, _ = time_group_steps(torch, lib, groups, sh, args.steps, args.warmup)
+        waves_sweep[str(wv)] = {"value": elems_per_step * args.steps / wall_g,
+                                "ms_per_step": wall_g * 1000.0 / args.steps}
+    rlscan.rlscan_set_launch_override()
 
     print("[bench] timing each estimator's launches", file=sys.stderr, flush=True)
     per_est = {}
@@ -631,8 +864,8 @@ def main():
                       "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "buffer_sets": m}
     dom = max(ests, key=lambda e: per_est[e]["us_per_call"])
     d = per_est[dom]
-    traffic = read_traffic(f"{dom}_{w.name}")
-    copy_us, copy_gbs = copy_ceiling(torch, sh, lib, d["bytes"])
+    copy_us, copy_gbs = copy_ceiling(torch, sh, lib, set_bytes)
+    dom_copy_us, dom_copy_gbs = copy_ceiling(torch, sh, lib, d["bytes"])
     plan = rlscan.rlscan_plan(dom, w.N, w.T, w.A)
     floor = launch_floor_us(torch, plan["grid"])
 
@@ -644,18 +877,33 @@ def main():
         "config": {"workload": w.name, "N": w.N, "T": w.T, "estimators": ests, "A": w.A,
                    "gamma": w.gamma, "lambda": w.lam, "buffer_sets": args.sets,
                    "bytes_per_step": set_bytes,
-                   "launch": "seven C calls per step on one stream"},
-        "roofline": {"bound": "hbm", "achieved": d["GB_per_s"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": d["frac_hbm_peak"], "traffic": traffic,
-                     "kernel": dom, "algorithmic_bytes_per_launch": d["bytes"],
-                     "avg_launch_us": d["us_per_call"],
+                   "launch": "one rlscan_group call per step: the seven estimator calls "
+                             "in one kernel launch"},
+        "roofline": {"bound": "hbm", "achieved": round(group_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(group_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": read_traffic(f"group_{w.name}"),
+                     "kernel": "group_kernel (the seven calls of a step)",
+                     "algorithmic_bytes_per_launch": set_bytes,
+                     "avg_launch_us": round(launch_us, 3),
                      "copy_same_bytes": {"us": round(copy_us, 3),
                                          "GB_per_s": round(copy_gbs, 1)}},
         "per_estimator": per_est,
-        "graph": {"value": elems_per_step * args.steps / wall_graph,
-                  "ms_per_step": wall_graph * 1000.0 / args.steps},
-        "warm": {"value": elems_per_step * args.steps / wall_warm,
-                 "ms_per_step": wall_warm * 1000.0 / args.steps},
+        "separate_calls": {
+            "value": elems_per_step * args.steps / wall_sep,
+            "ms_per_step": wall_sep * 1000.0 / args.steps,
+            "graph": {"value": elems_per_step * args.steps / wall_graph,
+                      "ms_per_step": wall_graph * 1000.0 / args.steps},
+            "warm": {"value": elems_per_step * args.steps / wall_warm,
+                     "ms_per_step": wall_warm * 1000.0 / args.steps},
+            "dominant_kernel": {"kernel": dom, "achieved": d["GB_per_s"],
+                                "frac": d["frac_hbm_peak"],
+                                "traffic": read_traffic(f"{dom}_{w.name}"),
+                                "algorithmic_bytes_per_launch": d["bytes"],
+                                "avg_launch_us": d["us_per_call"],
+                                "copy_same_bytes": {"us": round(dom_copy_us, 3),
+                                                    "GB_per_s": round(dom_copy_gbs, 1)}},
+            "note": "the seven C calls one after another on one stream"},
+        "group_waves": waves_sweep,
         "launch_floor_us": {"grid": plan["grid"], "us": round(floor, 3)},
         "kernel_source_hash": kernel_source_hash(),
     }
@@ -677,6 +925,10 @@ def main():
                                                           nsets=2)
         result["large_batch_1048576x32"]["note"] = (
             "supplementary shape, not one of the named configurations")
+
+    if not args.no_variants:
+        print("[bench] timing the variants", file=sys.stderr, flush=True)
+        result["variants"] = time_variants(torch, w, ests, sh, lib, args)
 
     assert rlscan.rlscan_lookback_timeouts() == 0
 

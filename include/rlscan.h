@@ -334,6 +334,54 @@ int rlscan_episodic_prefix_sum_u8(const int32_t* x, const uint8_t* dones,
                                   const int64_t* carry_in, int64_t* out, int64_t* carry_out,
                                   int64_t N, int64_t T, hipStream_t stream);
 
+/* ---- several calls in one launch -------------------------------------------
+ * A call of a few million elements (4096 x 128: 6-38 MB) is bound by its
+ * launch and one memory round trip, not by bandwidth; a step of several such
+ * calls on one stream pays that once per call.  rlscan_group runs `count`
+ * independent calls in one kernel launch (up to 8 calls per launch; more are
+ * split into several launches, in order): every call computes exactly what
+ * its own entry point computes, with its own tiles running side by side with
+ * the others'.
+ *
+ * Each call is described by an rlscan_call: `in` holds its inputs and `out`
+ * its outputs, in the order of the estimator's plain entry point above
+ * (GAE: rewards, values, bootstrap_value, terminated, truncated,
+ * bootstrap_values -> advantages; V-trace: ... -> vs, pg_advantages;
+ * Retrace: rewards, next_q_values_all, next_target_probs, actions,
+ * behaviour_probs, terminated, truncated -> targets; traces and prefix sum:
+ * x, dones -> out).  Unused entries are NULL.  V-trace reads lambda as its
+ * trace factor and rho_bar_pg as its policy-gradient clip (the plain form:
+ * lambda = 1, rho_bar_pg = rho_bar); the other estimators ignore rho_bar,
+ * c_bar and rho_bar_pg.  With RLSCAN_CALL_BYTE_FLAGS the flags are uint8
+ * (as for the *_u8 entry points).
+ *
+ * Every call must be one that runs as a single packed launch: rows that fit
+ * whole in the group's tile (N*T <= 1024, or T dividing 256, 512 or 1024),
+ * every pointer 16-byte aligned (one-byte flags: 4-byte aligned), and, for
+ * Retrace, A in {4, 6, 8}.  The calls must be independent: no call may
+ * write a buffer another call of the group reads or writes.
+ *
+ * Returns the first failing call's status (its argument checks are those of
+ * its entry point), RLSCAN_ERR_PARAM if a call cannot be grouped or names an
+ * unknown estimator, RLSCAN_ERR_ALIAS for calls that are not independent;
+ * nothing is enqueued then.  Streams, graphs and errors otherwise as for the
+ * single calls (a grouped launch may be captured). */
+enum { RLSCAN_CALL_BYTE_FLAGS = 1 };
+
+typedef struct rlscan_call {
+    int32_t estimator;       /* RLSCAN_EST_*                                   */
+    int32_t flags;           /* RLSCAN_CALL_* bits                             */
+    int64_t N, T;            /* rows, steps per row                            */
+    int64_t A;               /* Retrace: actions per step; otherwise ignored   */
+    float gamma, lambda;
+    float rho_bar, c_bar, rho_bar_pg;  /* V-trace                             */
+    float reserved;          /* set to 0                                       */
+    const void* in[8];
+    void* out[2];
+} rlscan_call;
+
+int rlscan_group(const rlscan_call* calls, int32_t count, hipStream_t stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* rlscan_status_string(int status);
 

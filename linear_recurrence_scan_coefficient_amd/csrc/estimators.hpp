@@ -559,7 +559,10 @@ struct Vtrace {
 //             : r_t + gamma*(EQ_t - c'_t*Q'[t,a_{t+1}])
 // kA > 0: A known at compile time, the chunk's 4*A action values are read
 // with 16-byte loads into registers; kA == 0: any A, read element-wise.
-template <int kA, class F = float>
+// kStaged: full tiles stage the action values through LDS (below); without
+// it they are read straight into registers, which needs no LDS -- the form
+// grouped launches use, where the LDS of one workgroup limits every call.
+template <int kA, class F = float, bool kStaged = true>
 struct Retrace {
     using S = StepF;
     using V = float;
@@ -569,7 +572,8 @@ struct Retrace {
     // values of each tensor through LDS: every load instruction then reads
     // 1 KiB of contiguous memory (a lane's own 4 x A values would be a
     // 16-byte piece every 16 x A bytes, which the L2 fetched ~14% over).
-    static constexpr int kStageFloats = (kA >= 1 && kA <= 8) ? 2 * kWave * kChunk * kA : 0;
+    static constexpr int kStageFloats =
+        (kStaged && kA >= 1 && kA <= 8) ? 2 * kWave * kChunk * kA : 0;
     static constexpr int kOutStageFloats = 0;
     struct Params {
         const float *rewards, *next_q, *next_pi;

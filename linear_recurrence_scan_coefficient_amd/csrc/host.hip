@@ -14,6 +14,8 @@
 
 namespace rlscan {
 
+thread_local GroupCollector* t_group = nullptr;
+
 LaunchOverride g_override;
 
 namespace {

@@ -11,6 +11,7 @@
 #include <mutex>
 
 #include "estimators.hpp"
+#include "group.hpp"
 #include "lookback.hpp"
 #include "rlscan.h"
 #include "tile_kernel.hpp"
@@ -143,6 +144,10 @@ hipError_t launch_w(const typename E::Params& p, const Geometry& geo, const Look
 template <class E>
 hipError_t launch_kernel(const typename E::Params& p, const Geometry& geo, const LookbackArgs& lb,
                          const Plan& pl, bool vec, bool carry, hipStream_t stream) {
+    if (t_group != nullptr) {  // collected for a grouped launch instead
+        t_group->add<E>(p, geo, pl.mapping, vec, carry);
+        return hipSuccess;
+    }
     if (carry) {
         if (!vec) return launch_r<E, 1, 4, false, true>(p, geo, lb, pl, stream);
         return launch_w<E, 4, true>(p, geo, lb, pl, stream);
@@ -162,6 +167,10 @@ template <class E>
 hipError_t launch_kernel_r1(const typename E::Params& p, const Geometry& geo,
                             const LookbackArgs& lb, const Plan& pl, bool vec, bool carry,
                             hipStream_t stream) {
+    if (t_group != nullptr) {
+        t_group->add<E>(p, geo, pl.mapping, vec, carry);
+        return hipSuccess;
+    }
     if (carry)
         return vec ? launch_r<E, 1, 4, true, true>(p, geo, lb, pl, stream)
                    : launch_r<E, 1, 4, false, true>(p, geo, lb, pl, stream);
@@ -188,6 +197,13 @@ int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream,
     geo.grid = pl.grid;
     geo.inv_T = 1.0 / static_cast<double>(T);
     LookbackArgs lb{};
+    if (t_group != nullptr) {  // collecting for a grouped launch: no side effects
+        if (pl.mapping == RLSCAN_MAP_PACKED)
+            fn(geo, lb, pl);
+        else
+            t_group->reject = true;
+        return RLSCAN_OK;
+    }
     if (pl.mapping == RLSCAN_MAP_PACKED) {
         return fn(geo, lb, pl) == hipSuccess ? RLSCAN_OK : RLSCAN_ERR_HIP;
     }

@@ -51,7 +51,7 @@ EXPORTED = (
     "rlscan_vtrace_ex", "rlscan_episodic_prefix_sum_f32",
     "rlscan_gae_u8", "rlscan_lambda_returns_u8", "rlscan_discounted_returns_u8",
     "rlscan_vtrace_u8", "rlscan_retrace_u8", "rlscan_eligibility_traces_u8",
-    "rlscan_episodic_prefix_sum_u8",
+    "rlscan_episodic_prefix_sum_u8", "rlscan_group",
 )
 
 
@@ -59,6 +59,23 @@ class RlscanError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"rlscan error {status}: {message}")
         self.status = status
+
+
+class Call(ctypes.Structure):
+    """rlscan_call: one estimator call of a grouped launch."""
+    _fields_ = [("estimator", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("N", ctypes.c_int64), ("T", ctypes.c_int64), ("A", ctypes.c_int64),
+                ("gamma", ctypes.c_float), ("lam", ctypes.c_float),
+                ("rho_bar", ctypes.c_float), ("c_bar", ctypes.c_float),
+                ("rho_bar_pg", ctypes.c_float), ("reserved", ctypes.c_float),
+                ("inp", ctypes.c_void_p * 8), ("out", ctypes.c_void_p * 2)]
+
+
+CALL_BYTE_FLAGS = 1
+# positions of the flag tensors among each estimator's inputs
+_FLAG_SLOTS = {"gae": (3, 4), "lambda_returns": (3, 4), "discounted_returns": (2, 3),
+               "vtrace": (4, 5), "retrace": (5, 6), "eligibility_traces": (1,),
+               "episodic_prefix_sum": (1,)}
 
 
 class PlanInfo(ctypes.Structure):
@@ -109,6 +126,8 @@ def _declare(lib):
         getattr(lib, name).restype = ctypes.c_int
         if name != "rlscan_release_scratch":
             getattr(lib, name + "_carry").restype = ctypes.c_int
+    lib.rlscan_group.argtypes = [ctypes.POINTER(Call), ctypes.c_int32, _vp]
+    lib.rlscan_group.restype = ctypes.c_int
     lib.rlscan_release_scratch.argtypes = []
     lib.rlscan_status_string.argtypes = [ctypes.c_int]
     lib.rlscan_status_string.restype = ctypes.c_char_p
@@ -456,6 +475,45 @@ def rlscan_eligibility_traces_u8(x, dones, traces, gamma, lam, stream=None, carr
 def rlscan_episodic_prefix_sum_u8(x, dones, out, stream=None, carry_in=None, carry_out=None):
     _require_byte_flags(dones=dones)
     return rlscan_episodic_prefix_sum(x, dones, out, stream, carry_in, carry_out)
+
+
+class GroupCall:
+    """One call of a grouped launch: the estimator's inputs and outputs as
+    tensors in the order of its plain entry point (None for an absent
+    optional input).  One-byte flags (uint8 / bool) set the byte-flag bit."""
+
+    def __init__(self, estimator, inputs, outputs, gamma=0.99, lam=0.95, rho_bar=1.0,
+                 c_bar=1.0, rho_bar_pg=None):
+        if estimator not in ESTIMATOR_IDS:
+            raise ValueError(f"unknown estimator {estimator!r}")
+        if len(inputs) > 8 or len(outputs) > 2:
+            raise ValueError("at most 8 inputs and 2 outputs")
+        first = inputs[0]
+        if first is None or first.dim() != 2:
+            raise ValueError("the first input must be a [N, T] tensor")
+        N, T = first.shape
+        flags = {f"input {i}": inputs[i] for i in _FLAG_SLOTS[estimator] if i < len(inputs)}
+        byte = _byte_flags(flags)
+        self.keep = (tuple(inputs), tuple(outputs))  # the tensors outlive the launch
+        c = Call()
+        c.estimator = ESTIMATOR_IDS[estimator]
+        c.flags = CALL_BYTE_FLAGS if byte else 0
+        c.N, c.T = N, T
+        c.A = inputs[1].shape[2] if estimator == "retrace" and inputs[1] is not None else 1
+        c.gamma, c.lam = gamma, lam
+        c.rho_bar, c.c_bar = rho_bar, c_bar
+        c.rho_bar_pg = rho_bar if rho_bar_pg is None else rho_bar_pg
+        for i, t in enumerate(inputs):
+            c.inp[i] = None if t is None else _ptr(t, dtype=t.dtype, name=f"input {i}")
+        for i, t in enumerate(outputs):
+            c.out[i] = None if t is None else _ptr(t, dtype=t.dtype, name=f"output {i}")
+        self.call = c
+
+
+def rlscan_group(calls, stream=None):
+    """Runs the GroupCall list `calls` in one kernel launch (rlscan_group)."""
+    arr = (Call * len(calls))(*[c.call for c in calls])
+    _check(library().rlscan_group(arr, len(calls), _stream(stream)))
 
 
 def rlscan_release_scratch():

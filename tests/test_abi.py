@@ -256,3 +256,36 @@ def test_variant_entry_points_argument_checks(lib):
                                           None) == ALIAS
     assert f.rlscan_episodic_prefix_sum_u8(P[0], None, None, P[3], None, 4, 8, None) == NULL
     assert f.rlscan_episodic_prefix_sum_u8(None, None, None, None, None, 0, 0, None) == OK
+
+
+def test_group_argument_checks(lib):
+    """rlscan_group refusals that return before anything is launched."""
+    from linear_recurrence_scan_coefficient_amd.rlscan import Call
+    assert lib.rlscan_group(None, 0, None) == OK
+    assert lib.rlscan_group(None, -1, None) == SHAPE
+    assert lib.rlscan_group(None, 2, None) == NULL
+
+    def call(est, N=4, T=8, ins=P[:6], outs=P[6:7], gamma=0.9):
+        c = Call()
+        c.estimator, c.N, c.T, c.A = est, N, T, 6
+        c.gamma, c.lam, c.rho_bar, c.c_bar, c.rho_bar_pg = gamma, 0.9, 1.0, 1.0, 1.0
+        for i, p in enumerate(ins):
+            c.inp[i] = p
+        for i, p in enumerate(outs):
+            c.out[i] = p
+        return c
+
+    def group(*calls):
+        arr = (Call * len(calls))(*calls)
+        return lib.rlscan_group(arr, len(calls), None)
+
+    # one call writes what another reads
+    assert group(call(0), call(0, ins=[P[6]] + P[1:6], outs=[P[7]])) == ALIAS
+    # rows of 3000 steps fit no grouped tile
+    assert group(call(0, N=2, T=3000)) == PARAM
+    # unknown estimator
+    assert group(call(9)) == PARAM
+    # a call's own checks: gamma out of range
+    assert group(call(0, gamma=1.5)) == PARAM
+    # misaligned pointer: refused while collecting, before any launch
+    assert group(call(0, ins=[P[0] + 4] + P[1:6])) == PARAM
