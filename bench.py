@@ -396,20 +396,6 @@ def raw_u8_call_args(est, d, out, w, stream):
 
 FLAG_KEYS = ("terminated", "truncated", "dones")
 
-# each estimator's inputs in the order of its plain entry point
-GROUP_INPUTS = {
-    "gae": ("rewards", "values", "bootstrap_value", "terminated", "truncated", "bootstrap_values"),
-    "lambda_returns": ("rewards", "values", "bootstrap_value", "terminated", "truncated",
-                       "bootstrap_values"),
-    "discounted_returns": ("rewards", "bootstrap_value", "terminated", "truncated",
-                           "bootstrap_values"),
-    "vtrace": ("rewards", "values", "bootstrap_value", "log_rhos", "terminated", "truncated",
-               "bootstrap_values"),
-    "retrace": ("rewards", "next_q_values_all", "next_target_probs", "actions",
-                "behaviour_probs", "terminated", "truncated"),
-    "eligibility_traces": ("x", "dones"),
-    "episodic_prefix_sum": ("x", "dones"),
-}
 
 
 def algorithmic_bytes(inputs: dict, outputs: dict) -> int:
@@ -448,7 +434,7 @@ class CallSet:
         from linear_recurrence_scan_coefficient_amd import device, rlscan
         calls = []
         for (est, _, _), (d, out) in zip(self.calls, self.keep):
-            ins = tuple(d.get(k) for k in GROUP_INPUTS[est])
+            ins = tuple(d.get(k) for k in device.INPUT_ORDER[est])
             outs = tuple(out[name] for name, _ in device.OUTPUTS[est])
             w = self.w
             calls.append(rlscan.GroupCall(est, ins, outs, gamma=w.gamma,

@@ -22,6 +22,23 @@ OUTPUTS = {
 }
 
 
+# each estimator's inputs in the order of its plain C entry point (the order
+# of an rlscan_call's `in` array)
+INPUT_ORDER = {
+    "gae": ("rewards", "values", "bootstrap_value", "terminated", "truncated", "bootstrap_values"),
+    "lambda_returns": ("rewards", "values", "bootstrap_value", "terminated", "truncated",
+                       "bootstrap_values"),
+    "discounted_returns": ("rewards", "bootstrap_value", "terminated", "truncated",
+                           "bootstrap_values"),
+    "vtrace": ("rewards", "values", "bootstrap_value", "log_rhos", "terminated", "truncated",
+               "bootstrap_values"),
+    "retrace": ("rewards", "next_q_values_all", "next_target_probs", "actions",
+                "behaviour_probs", "terminated", "truncated"),
+    "eligibility_traces": ("x", "dones"),
+    "episodic_prefix_sum": ("x", "dones"),
+}
+
+
 def upload(inputs: dict, device="cuda") -> dict:
     return {k: (None if v is None else torch.from_numpy(np.ascontiguousarray(v)).to(device))
             for k, v in inputs.items()}

@@ -39,24 +39,11 @@ def case(estimator, N, T, seed, **kw):
     return w, workloads.inputs_for(estimator, w, seed)
 
 
-INPUT_ORDER = {
-    "gae": ("rewards", "values", "bootstrap_value", "terminated", "truncated", "bootstrap_values"),
-    "lambda_returns": ("rewards", "values", "bootstrap_value", "terminated", "truncated",
-                       "bootstrap_values"),
-    "discounted_returns": ("rewards", "bootstrap_value", "terminated", "truncated",
-                           "bootstrap_values"),
-    "vtrace": ("rewards", "values", "bootstrap_value", "log_rhos", "terminated", "truncated",
-               "bootstrap_values"),
-    "retrace": ("rewards", "next_q_values_all", "next_target_probs", "actions",
-                "behaviour_probs", "terminated", "truncated"),
-    "eligibility_traces": ("x", "dones"),
-    "episodic_prefix_sum": ("x", "dones"),
-}
 FLAG_KEYS = ("terminated", "truncated", "dones")
 
 
 def group_call(estimator, d, out, w, **kw):
-    ins = tuple(d.get(k) for k in INPUT_ORDER[estimator])
+    ins = tuple(d.get(k) for k in device.INPUT_ORDER[estimator])
     outs = tuple(out[name] for name, _ in device.OUTPUTS[estimator])
     opts = dict(gamma=w.gamma, lam=w.lam, rho_bar=w.rho_bar, c_bar=w.c_bar)
     if estimator == "vtrace":
