@@ -29,8 +29,18 @@ prefix sum), and with `return_carry=True` also returns carry_out [num_envs],
 the output at the chunk's other edge -- the next call's carry_in.  V at
 t = T is `bootstrap_value`; compute_retrace also needs `next_actions` and
 `next_behaviour_probs` [num_envs] of the chunk that follows.
+
+Several calls in one launch: inside `with grouped():` the compute_* calls
+return their (not yet written) outputs at once and are run together as one
+`rlscan_group` launch when the block ends, on the stream current then.
+Calls that take or return a carry, or name a stream of their own, and the
+float-valued prefix sum run at once as usual.  If the collected calls cannot share a launch (rows longer
+than a grouped tile, unaligned tensors, Retrace with an action count other
+than 4, 6 or 8), they run one by one instead.
 """
 from __future__ import annotations
+
+import threading
 
 import torch
 
@@ -39,7 +49,54 @@ from . import rlscan
 __all__ = [
     "compute_gae", "compute_vtrace", "compute_retrace", "compute_lambda_returns",
     "compute_discounted_returns", "compute_eligibility_traces", "compute_episodic_prefix_sum",
+    "grouped",
 ]
+
+_local = threading.local()
+
+
+class grouped:
+    """Collects the compute_* calls made in its block (on this thread) and
+    runs them as one grouped launch when the block ends."""
+
+    def __init__(self, stream=None):
+        self.stream = stream
+        self.calls = []  # (GroupCall, the same call made alone)
+
+    def __enter__(self):
+        stack = getattr(_local, "groups", None)
+        if stack is None:
+            stack = _local.groups = []
+        stack.append(self)
+        return self
+
+    def __exit__(self, exc_type, exc, tb):
+        _local.groups.pop()
+        if exc_type is None:
+            self.launch()
+        return False
+
+    def launch(self):
+        calls, self.calls = self.calls, []
+        if not calls:
+            return
+        try:
+            rlscan.rlscan_group([g for g, _ in calls], self.stream)
+        except rlscan.RlscanError as e:
+            if e.status != rlscan.RLSCAN_ERR_PARAM:
+                raise
+            for _, alone in calls:  # not groupable: the same calls one by one
+                alone(self.stream)
+
+
+def _submit(estimator, ins, outs, params, alone, stream, carry):
+    """Runs `alone(stream)` now, or defers the call to the innermost active
+    `grouped` block (plain calls on the default stream only)."""
+    stack = getattr(_local, "groups", None)
+    if stack and not carry and stream is None:
+        stack[-1].calls.append((rlscan.GroupCall(estimator, ins, outs, **params), alone))
+    else:
+        alone(stream)
 
 
 def _device_tensor(t, name, dtype=torch.float32, flag=False):
@@ -103,10 +160,13 @@ def compute_gae(rewards, values, terminateds, gamma=0.99, lambda_=0.95, *,
     out = torch.empty((N, T), dtype=torch.float32, device=r.device)
     co = _carry_out(return_carry, N, r.device)
     term, trunc = _flags(terminateds=terminateds, truncateds=truncateds)
-    rlscan.rlscan_gae(
-        r, _device_tensor(values, "values"), _device_tensor(bootstrap_value, "bootstrap_value"),
-        term, trunc, _device_tensor(bootstrap_values, "bootstrap_values"), out, float(gamma),
-        float(lambda_), stream, carry_in=_device_tensor(carry_in, "carry_in"), carry_out=co)
+    ins = (r, _device_tensor(values, "values"), _device_tensor(bootstrap_value, "bootstrap_value"),
+           term, trunc, _device_tensor(bootstrap_values, "bootstrap_values"))
+    ci = _device_tensor(carry_in, "carry_in")
+    _submit("gae", ins, (out,), dict(gamma=float(gamma), lam=float(lambda_)),
+            lambda st: rlscan.rlscan_gae(*ins, out, float(gamma), float(lambda_), st,
+                                         carry_in=ci, carry_out=co),
+            stream, ci is not None or co is not None)
     return (out, co) if return_carry else out
 
 
@@ -119,10 +179,13 @@ def compute_lambda_returns(rewards, values, terminateds, gamma=0.99, lambda_=0.9
     out = torch.empty((N, T), dtype=torch.float32, device=r.device)
     co = _carry_out(return_carry, N, r.device)
     term, trunc = _flags(terminateds=terminateds, truncateds=truncateds)
-    rlscan.rlscan_lambda_returns(
-        r, _device_tensor(values, "values"), _device_tensor(bootstrap_value, "bootstrap_value"),
-        term, trunc, _device_tensor(bootstrap_values, "bootstrap_values"), out, float(gamma),
-        float(lambda_), stream, carry_in=_device_tensor(carry_in, "carry_in"), carry_out=co)
+    ins = (r, _device_tensor(values, "values"), _device_tensor(bootstrap_value, "bootstrap_value"),
+           term, trunc, _device_tensor(bootstrap_values, "bootstrap_values"))
+    ci = _device_tensor(carry_in, "carry_in")
+    _submit("lambda_returns", ins, (out,), dict(gamma=float(gamma), lam=float(lambda_)),
+            lambda st: rlscan.rlscan_lambda_returns(*ins, out, float(gamma), float(lambda_), st,
+                                                    carry_in=ci, carry_out=co),
+            stream, ci is not None or co is not None)
     return (out, co) if return_carry else out
 
 
@@ -136,10 +199,13 @@ def compute_discounted_returns(rewards, terminateds, gamma=0.99, *, bootstrap_va
     out = torch.empty((N, T), dtype=torch.float32, device=r.device)
     co = _carry_out(return_carry, N, r.device)
     term, trunc = _flags(terminateds=terminateds, truncateds=truncateds)
-    rlscan.rlscan_discounted_returns(
-        r, _device_tensor(bootstrap_value, "bootstrap_value"), term, trunc,
-        _device_tensor(bootstrap_values, "bootstrap_values"), out, float(gamma), stream,
-        carry_in=_device_tensor(carry_in, "carry_in"), carry_out=co)
+    ins = (r, _device_tensor(bootstrap_value, "bootstrap_value"), term, trunc,
+           _device_tensor(bootstrap_values, "bootstrap_values"))
+    ci = _device_tensor(carry_in, "carry_in")
+    _submit("discounted_returns", ins, (out,), dict(gamma=float(gamma)),
+            lambda st: rlscan.rlscan_discounted_returns(*ins, out, float(gamma), st, carry_in=ci,
+                                                        carry_out=co),
+            stream, ci is not None or co is not None)
     return (out, co) if return_carry else out
 
 
@@ -158,13 +224,19 @@ def compute_vtrace(rewards, values, log_rhos, terminateds, gamma=0.99, rho_bar=1
     pg = torch.empty((N, T), dtype=torch.float32, device=r.device)
     co = _carry_out(return_carry, N, r.device)
     term, trunc = _flags(terminateds=terminateds, truncateds=truncateds)
-    rlscan.rlscan_vtrace(
-        r, _device_tensor(values, "values"), _device_tensor(bootstrap_value, "bootstrap_value"),
-        _device_tensor(log_rhos, "log_rhos"), term, trunc,
-        _device_tensor(bootstrap_values, "bootstrap_values"), vs, pg, float(gamma),
-        float(rho_bar), float(c_bar), stream, carry_in=_device_tensor(carry_in, "carry_in"),
-        carry_out=co, lam=None if lambda_ is None else float(lambda_),
-        rho_bar_pg=None if rho_bar_pg is None else float(rho_bar_pg))
+    ins = (r, _device_tensor(values, "values"), _device_tensor(bootstrap_value, "bootstrap_value"),
+           _device_tensor(log_rhos, "log_rhos"), term, trunc,
+           _device_tensor(bootstrap_values, "bootstrap_values"))
+    ci = _device_tensor(carry_in, "carry_in")
+    lam = None if lambda_ is None else float(lambda_)
+    pgc = None if rho_bar_pg is None else float(rho_bar_pg)
+    _submit("vtrace", ins, (vs, pg),
+            dict(gamma=float(gamma), lam=1.0 if lam is None else lam, rho_bar=float(rho_bar),
+                 c_bar=float(c_bar), rho_bar_pg=pgc),
+            lambda st: rlscan.rlscan_vtrace(*ins, vs, pg, float(gamma), float(rho_bar),
+                                            float(c_bar), st, carry_in=ci, carry_out=co,
+                                            lam=lam, rho_bar_pg=pgc),
+            stream, ci is not None or co is not None)
     return (vs, pg, co) if return_carry else (vs, pg)
 
 
@@ -190,14 +262,18 @@ def compute_retrace(rewards, next_q_values_all, next_target_probs, actions, beha
     out = torch.empty((N, T), dtype=torch.float32, device=r.device)
     co = _carry_out(return_carry, N, r.device)
     term, trunc = _flags(terminateds=terminateds, truncateds=truncateds)
-    rlscan.rlscan_retrace(
-        r, _device_tensor(next_q_values_all, "next_q_values_all"),
-        _device_tensor(next_target_probs, "next_target_probs"),
-        _device_tensor(a, "actions", torch.int32), _device_tensor(behaviour_probs,
-                                                                  "behaviour_probs"),
-        term, trunc, out, float(gamma), float(lambda_), stream, carry_in=_device_tensor(carry_in, "carry_in"),
-        carry_out=co, next_actions=_device_tensor(na, "next_actions", torch.int32),
-        next_behaviour_probs=_device_tensor(next_behaviour_probs, "next_behaviour_probs"))
+    ins = (r, _device_tensor(next_q_values_all, "next_q_values_all"),
+           _device_tensor(next_target_probs, "next_target_probs"),
+           _device_tensor(a, "actions", torch.int32),
+           _device_tensor(behaviour_probs, "behaviour_probs"), term, trunc)
+    ci = _device_tensor(carry_in, "carry_in")
+    nat = _device_tensor(na, "next_actions", torch.int32)
+    nbp = _device_tensor(next_behaviour_probs, "next_behaviour_probs")
+    _submit("retrace", ins, (out,), dict(gamma=float(gamma), lam=float(lambda_)),
+            lambda st: rlscan.rlscan_retrace(*ins, out, float(gamma), float(lambda_), st,
+                                             carry_in=ci, carry_out=co, next_actions=nat,
+                                             next_behaviour_probs=nbp),
+            stream, ci is not None or co is not None)
     return (out, co) if return_carry else out
 
 
@@ -209,9 +285,12 @@ def compute_eligibility_traces(x, dones, gamma=0.99, lambda_=0.95, *, carry_in=N
     N, T = _check_2d(xx, "x")
     out = torch.empty((N, T), dtype=torch.float32, device=xx.device)
     co = _carry_out(return_carry, N, xx.device)
-    rlscan.rlscan_eligibility_traces(xx, _flags(dones=dones)[0], out, float(gamma),
-                                     float(lambda_), stream,
-                                     carry_in=_device_tensor(carry_in, "carry_in"), carry_out=co)
+    ins = (xx, _flags(dones=dones)[0])
+    ci = _device_tensor(carry_in, "carry_in")
+    _submit("eligibility_traces", ins, (out,), dict(gamma=float(gamma), lam=float(lambda_)),
+            lambda st: rlscan.rlscan_eligibility_traces(*ins, out, float(gamma), float(lambda_),
+                                                        st, carry_in=ci, carry_out=co),
+            stream, ci is not None or co is not None)
     return (out, co) if return_carry else out
 
 
@@ -239,7 +318,10 @@ def compute_episodic_prefix_sum(x, dones, *, carry_in=None, return_carry=False, 
     N, T = _check_2d(xx, "x")
     out = torch.empty((N, T), dtype=torch.int64, device=xx.device)
     co = _carry_out(return_carry, N, xx.device, torch.int64)
-    rlscan.rlscan_episodic_prefix_sum(xx, _flags(dones=dones)[0], out, stream,
-                                      carry_in=_device_tensor(carry_in, "carry_in", torch.int64),
-                                      carry_out=co)
+    ins = (xx, _flags(dones=dones)[0])
+    ci = _device_tensor(carry_in, "carry_in", torch.int64)
+    _submit("episodic_prefix_sum", ins, (out,), {},
+            lambda st: rlscan.rlscan_episodic_prefix_sum(*ins, out, st, carry_in=ci,
+                                                         carry_out=co),
+            stream, ci is not None or co is not None)
     return (out, co) if return_carry else out

@@ -220,3 +220,47 @@ def test_streamed_compute_calls_match_one_call(estimator):
         ref = whole[k].astype(np.float64)
         err = np.abs(got[k].astype(np.float64) - ref) / (1 + np.abs(ref))
         assert err.max() <= 1e-4, (k, float(err.max()))
+
+
+def _all_seven(d, w, flag_dtype=None):
+    return {e: call(e, d[e], w, flag_dtype) for e in ESTIMATORS}
+
+
+@pytest.mark.parametrize("flag_dtype", [None, torch.bool])
+def test_grouped_block_matches_single_calls(flag_dtype):
+    """The seven compute_* calls inside `with api.grouped():` (one grouped
+    launch at the end of the block) against the same calls made alone."""
+    w = workloads.get("production_4096x128")
+    data = {e: {k: dev(v) for k, v in workloads.inputs_for(e, w, 21).items()}
+            for e in ESTIMATORS}
+    alone = _all_seven(data, w, flag_dtype)
+    with api.grouped():
+        pending = _all_seven(data, w, flag_dtype)
+    torch.cuda.synchronize()
+    for e in ESTIMATORS:
+        a, g = host(alone[e]), host(pending[e])
+        for k in a:
+            ref = a[k].astype(np.float64)
+            err = np.abs(g[k].astype(np.float64) - ref) / (1 + np.abs(ref))
+            assert err.max() <= 1e-6, (e, k, float(err.max()))
+        assert_parity(g, oracle_outputs(e, workloads.inputs_for(e, w, 21), w), f"grouped {e}")
+
+
+def test_grouped_block_with_calls_that_cannot_share_a_launch():
+    """Rows of 5000 steps take the look-back, which a grouped launch does not
+    run: the block then runs its calls one by one; a carry call inside the
+    block runs at once."""
+    w, inputs = case("gae", N=3, T=5000, seed=31)
+    d = {k: dev(v) for k, v in inputs.items()}
+    w2, inputs2 = case("vtrace", N=64, T=128, seed=32)
+    d2 = {k: dev(v) for k, v in inputs2.items()}
+    with api.grouped():
+        got = call("gae", d, w)
+        got2 = call("vtrace", d2, w2)
+        _, c = api.compute_gae(d["rewards"], d["values"], d["terminated"], w.gamma, w.lam,
+                               truncateds=d.get("truncated"),
+                               bootstrap_values=d.get("bootstrap_values"), return_carry=True)
+    torch.cuda.synchronize()
+    assert_parity(host(got), oracle_outputs("gae", inputs, w), "grouped long gae")
+    assert_parity(host(got2), oracle_outputs("vtrace", inputs2, w2), "grouped vtrace")
+    assert c.shape == (3,)

@@ -7,10 +7,20 @@ from linear_recurrence_scan_coefficient_amd import api
 
 
 def test_names_follow_the_pages():
+    """The seven compute_* names of the README's Kernels table, plus the
+    grouped-launch block."""
     assert sorted(api.__all__) == sorted([
         "compute_gae", "compute_vtrace", "compute_retrace", "compute_lambda_returns",
         "compute_discounted_returns", "compute_eligibility_traces",
-        "compute_episodic_prefix_sum"])
+        "compute_episodic_prefix_sum", "grouped"])
+
+
+def test_empty_grouped_block_launches_nothing():
+    with api.grouped() as g:
+        assert g.calls == []
+    with pytest.raises(RuntimeError):  # an exception inside the block skips the launch
+        with api.grouped() as g:
+            raise RuntimeError("inside")
 
 
 @pytest.mark.parametrize("fn,args", [
