@@ -223,7 +223,7 @@ int rlscan_episodic_prefix_sum(const int32_t* x, const float* dones, int64_t* ou
  * next_behaviour_probs [N] (mu(a_T | x_T)) of the chunk that follows
  * (RLSCAN_ERR_NULL if missing).  Layout, ownership, streams and errors are as
  * for the plain calls; carry_out must not alias any other argument.  Calls
- * with carry arguments run kernels built for them (four waves per
+ * with carry arguments run kernels built for them (four or eight waves per
  * workgroup); the plain calls are unaffected. */
 int rlscan_gae_carry(const float* rewards, const float* values, const float* bootstrap_value,
                      const float* terminated, const float* truncated,
@@ -435,8 +435,8 @@ enum {
  * apply with one round; with more rounds 4 is used); grid_cap: 0 = no cap,
  * else at most this many workgroups, each looping over tiles; flags:
  * RLSCAN_FLAG_* bits.  Retrace runs one round of at most 4 waves; a call
- * with an input or output that is not aligned for the vector path, or with carry
- * arguments, runs 4 waves (the former one round).  By default
+ * with an input or output that is not aligned for the vector path runs one
+ * round of 4 waves, and one with carry arguments 4 or 8 waves.  By default
  * look-back tiles are ordered by workgroup index, and by tickets only when
  * workgroups loop.  Returns RLSCAN_ERR_PARAM for other values. */
 int rlscan_set_launch_override(int mapping, int rounds, int waves, int64_t grid_cap, int flags);

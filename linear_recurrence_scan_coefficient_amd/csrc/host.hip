@@ -96,15 +96,20 @@ int auto_rounds(int est, int64_t NT) {
 //  - One round (at most 2^20 elements, bound by launch and one memory round
 //    trip): the smallest tile that still holds whole rows -- more, smaller
 //    workgroups in flight.  Measured at 4096 x 128: one wave beat four by
-//    2-8 %, two waves by as much for GAE and V-trace.
+//    2-8 %, two waves by as much for GAE and V-trace.  Where no tile of up
+//    to eight waves holds whole rows (the look-back mapping), eight waves:
+//    half the tiles, so half the look-back waits.  Measured on GAE, V-trace
+//    and discounted returns against four waves: 64 x 8192 and 16 x 32768
+//    5-7 % faster, 8 x 131072 12-18 % faster (Retrace stays at four).
 int auto_waves(int est, int rounds, int64_t T) {
     if (rounds == 4)
         return (est == RLSCAN_EST_DISCOUNTED || est == RLSCAN_EST_ELIGIBILITY ||
                 est == RLSCAN_EST_PREFIX_SUM) ? 8 : 4;
     if (rounds == 1) {
         const int first = (est == RLSCAN_EST_GAE || est == RLSCAN_EST_VTRACE) ? 2 : 1;
-        for (int w = first; w <= 2; w *= 2)
+        for (int w = first; w <= 8; w *= 2)
             if ((int64_t(kWave) * w * kChunk) % T == 0) return w;
+        return est == RLSCAN_EST_RETRACE ? 4 : 8;
     }
     return 4;
 }
@@ -118,10 +123,11 @@ Plan make_plan(int est, int64_t N, int64_t T, bool vec, bool carry) {
     const int wo = g_override.waves.load();
     pl.waves = wo > 0 ? wo : auto_waves(est, pl.rounds, T);
     // kernels exist for 1 and 2 waves with one round only, for 8 waves not
-    // for Retrace, and for the unaligned and carry paths with 4 waves only
+    // for Retrace, for the unaligned path with 4 waves only and for the
+    // carry path with 4 or 8
     if (pl.waves < 4 && pl.rounds != 1) pl.waves = 4;
     if (pl.waves == 8 && est == RLSCAN_EST_RETRACE) pl.waves = 4;
-    if (!vec || carry) pl.waves = 4;
+    if (!vec || (carry && pl.waves != 8)) pl.waves = 4;
     pl.tile_elems = int64_t(kWave) * pl.waves * kChunk * pl.rounds;
     pl.tiles = (NT + pl.tile_elems - 1) / pl.tile_elems;
     const bool packed_ok = pl.tiles <= 1 || pl.tile_elems % T == 0;

@@ -139,8 +139,8 @@ hipError_t launch_w(const typename E::Params& p, const Geometry& geo, const Look
     }
 }
 
-// Kernels built for the carry arguments exist with four waves only (the
-// plan forces it); all others with 1 or 2 waves (one round), 4 or 8.
+// Kernels built for the carry arguments exist with four or eight waves (the
+// plan sees to it); all others with 1 or 2 waves (one round), 4 or 8.
 template <class E>
 hipError_t launch_kernel(const typename E::Params& p, const Geometry& geo, const LookbackArgs& lb,
                          const Plan& pl, bool vec, bool carry, hipStream_t stream) {
@@ -150,7 +150,8 @@ hipError_t launch_kernel(const typename E::Params& p, const Geometry& geo, const
     }
     if (carry) {
         if (!vec) return launch_r<E, 1, 4, false, true>(p, geo, lb, pl, stream);
-        return launch_w<E, 4, true>(p, geo, lb, pl, stream);
+        return pl.waves == 8 ? launch_w<E, 8, true>(p, geo, lb, pl, stream)
+                             : launch_w<E, 4, true>(p, geo, lb, pl, stream);
     }
     if (!vec) return launch_r<E, 1, 4, false, false>(p, geo, lb, pl, stream);
     switch (pl.waves) {

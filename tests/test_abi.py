@@ -134,10 +134,14 @@ def test_plan_mapping_choice(lib):
     p = rlscan.rlscan_plan("gae", 64, 512)
     assert p["tiles"] == 64 and p["threads"] == 128
     assert rlscan.rlscan_plan("eligibility_traces", 64, 512)["threads"] == 128
-    # rows that no small tile holds whole keep four waves
+    # the smallest tile of up to eight waves that holds whole rows
     assert rlscan.rlscan_plan("gae", 1024, 1024)["threads"] == 256
-    # rows longer than a tile, or rows that do not divide it: look-back
-    assert rlscan.rlscan_plan("gae", 64, 8192)["mapping"] == rlscan.MAP_LOOKBACK
+    p = rlscan.rlscan_plan("discounted_returns", 256, 2048)
+    assert p["threads"] == 512 and p["mapping"] == rlscan.MAP_PACKED
+    # rows longer than a tile, or rows that do not divide it: look-back,
+    # with eight waves (one round)
+    p = rlscan.rlscan_plan("gae", 64, 8192)
+    assert p["mapping"] == rlscan.MAP_LOOKBACK and p["threads"] == 512 and p["rounds"] == 1
     assert rlscan.rlscan_plan("gae", 5, 1000)["mapping"] == rlscan.MAP_LOOKBACK
     # long rows: four rounds; eight waves for the low-register estimators
     for est, waves in (("discounted_returns", 8), ("episodic_prefix_sum", 8),
@@ -148,8 +152,8 @@ def test_plan_mapping_choice(lib):
         assert big["threads"] == 64 * waves, est
         assert big["tile_elems"] == 256 * waves * 4, est
         assert big["tiles"] == (8 << 20) // big["tile_elems"], est
-    # eight waves only with four rounds
-    assert rlscan.rlscan_plan("discounted_returns", 64, 8192)["threads"] == 256
+    # two rounds keep four waves
+    assert rlscan.rlscan_plan("discounted_returns", 8, 1 << 19)["threads"] == 256
     # a single tile never needs a carry
     assert rlscan.rlscan_plan("gae", 3, 100)["mapping"] == rlscan.MAP_PACKED
     # Retrace runs one round of four waves

@@ -201,15 +201,17 @@ def test_carry_out_alone(estimator):
 @pytest.mark.parametrize("estimator", ESTIMATORS)
 @pytest.mark.parametrize("rounds", [1, 2, 4])
 @pytest.mark.parametrize("mapping", ["lookback", "packed"])
-def test_carry_across_mappings(estimator, rounds, mapping):
+@pytest.mark.parametrize("waves", [4, 8])
+def test_carry_across_mappings(estimator, rounds, mapping, waves):
+    """Carry kernels exist with four and eight waves (Retrace: four)."""
     m = rlscan.MAP_LOOKBACK if mapping == "lookback" else rlscan.MAP_PACKED
-    rlscan.rlscan_set_launch_override(m, rounds)
-    w, d, rng = case(estimator, 40, 4096, seed=rounds + 10 * (m + 1))
+    rlscan.rlscan_set_launch_override(m, rounds, waves)
+    w, d, rng = case(estimator, 40, 4096, seed=rounds + 10 * (m + 1) + waves)
     force_edge_flags(estimator, d, 4096)
     carry = carry_inputs(estimator, d, 40, rng)
-    print(f"[carry] {estimator} {mapping} R={rounds}", flush=True)
+    print(f"[carry] {estimator} {mapping} R={rounds} W={waves}", flush=True)
     assert_parity(gpu_call(estimator, d, w, carry), oracle_call(estimator, d, w, carry),
-                  f"carry {estimator} {mapping} R={rounds}")
+                  f"carry {estimator} {mapping} R={rounds} W={waves}")
 
 
 def _cols(d, lo, hi):
