@@ -79,10 +79,14 @@ int ensure_capacity(Scratch* sc, hipStream_t stream, int64_t tiles) {
     return RLSCAN_OK;
 }
 
+// Rounds per tile: one up to 2^20 elements (the production shapes: more,
+// smaller workgroups in flight), two below 2^22, four from there (measured
+// at 8 x 2^19: four rounds 8-30 % faster than two).  Retrace keeps its
+// action values per round in registers: always one.
 int auto_rounds(int est, int64_t NT) {
     if (est == RLSCAN_EST_RETRACE) return 1;
     if (NT <= (int64_t(1) << 20)) return 1;
-    if (NT <= (int64_t(1) << 22)) return 2;
+    if (NT < (int64_t(1) << 22)) return 2;
     return 4;
 }
 
@@ -101,6 +105,9 @@ int auto_rounds(int est, int64_t NT) {
 //    half the tiles, so half the look-back waits.  Measured on GAE, V-trace
 //    and discounted returns against four waves: 64 x 8192 and 16 x 32768
 //    5-7 % faster, 8 x 131072 12-18 % faster (Retrace stays at four).
+//  - Two rounds: eight waves.  Measured against four: 32 x 65536 (look-back)
+//    10-18 % faster; 4096 x 512 and 16384 x 128 (packed) up to 12 % for GAE
+//    and V-trace, the same within 4 % for the others.
 int auto_waves(int est, int rounds, int64_t T) {
     if (rounds == 4)
         return (est == RLSCAN_EST_DISCOUNTED || est == RLSCAN_EST_ELIGIBILITY ||
@@ -111,7 +118,7 @@ int auto_waves(int est, int rounds, int64_t T) {
             if ((int64_t(kWave) * w * kChunk) % T == 0) return w;
         return est == RLSCAN_EST_RETRACE ? 4 : 8;
     }
-    return 4;
+    return 8;  // two rounds
 }
 
 Plan make_plan(int est, int64_t N, int64_t T, bool vec, bool carry) {

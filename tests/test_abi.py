@@ -152,8 +152,10 @@ def test_plan_mapping_choice(lib):
         assert big["threads"] == 64 * waves, est
         assert big["tile_elems"] == 256 * waves * 4, est
         assert big["tiles"] == (8 << 20) // big["tile_elems"], est
-    # two rounds keep four waves
-    assert rlscan.rlscan_plan("discounted_returns", 8, 1 << 19)["threads"] == 256
+    # two rounds below 2^22 elements, with eight waves; four from 2^22
+    p = rlscan.rlscan_plan("gae", 8, 1 << 18)
+    assert p["rounds"] == 2 and p["threads"] == 512
+    assert rlscan.rlscan_plan("gae", 8, 1 << 19)["rounds"] == 4
     # a single tile never needs a carry
     assert rlscan.rlscan_plan("gae", 3, 100)["mapping"] == rlscan.MAP_PACKED
     # Retrace runs one round of four waves
