@@ -499,7 +499,12 @@ class GroupCall:
         c.estimator = ESTIMATOR_IDS[estimator]
         c.flags = CALL_BYTE_FLAGS if byte else 0
         c.N, c.T = N, T
-        c.A = inputs[1].shape[2] if estimator == "retrace" and inputs[1] is not None else 1
+        c.A = 1
+        if estimator == "retrace":
+            q = inputs[1] if len(inputs) > 1 else None
+            if q is None or q.dim() != 3:
+                raise ValueError("Retrace's next_q_values_all must be a [N, T, A] tensor")
+            c.A = q.shape[2]
         c.gamma, c.lam = gamma, lam
         c.rho_bar, c.c_bar = rho_bar, c_bar
         c.rho_bar_pg = rho_bar if rho_bar_pg is None else rho_bar_pg
