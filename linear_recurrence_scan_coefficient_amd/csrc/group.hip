@@ -143,11 +143,7 @@ struct CollectorScope {
     ~CollectorScope() { t_group = nullptr; }
 };
 
-}  // namespace
-
-extern "C" {
-
-int rlscan_group(const rlscan_call* calls, int32_t count, hipStream_t stream) {
+int group(const rlscan_call* calls, int32_t count, hipStream_t stream) {
     if (count < 0) return RLSCAN_ERR_SHAPE;
     if (count == 0) return RLSCAN_OK;
     if (calls == nullptr) return RLSCAN_ERR_NULL;
@@ -188,6 +184,21 @@ int rlscan_group(const rlscan_call* calls, int32_t count, hipStream_t stream) {
         start += k;
     }
     return RLSCAN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+// The collector's table lives on the host heap: an allocation failure is
+// returned as RLSCAN_ERR_ALLOC, never thrown across the C interface.
+int rlscan_group(const rlscan_call* calls, int32_t count, hipStream_t stream) {
+    try {
+        return group(calls, count, stream);
+    } catch (...) {
+        t_group = nullptr;
+        return RLSCAN_ERR_ALLOC;
+    }
 }
 
 }  // extern "C"

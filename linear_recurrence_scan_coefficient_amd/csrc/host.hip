@@ -26,23 +26,34 @@ std::map<int, std::unique_ptr<LaunchOrder>> g_order;
 }  // namespace
 
 // Created with its event on first use (the event records no timing).
+// nullptr if the host is out of memory or the event cannot be created: no
+// exception leaves the library.
 LaunchOrder* launch_order(int device) {
     std::lock_guard<std::mutex> g(g_order_mutex);
-    auto& slot = g_order[device];
-    if (!slot) {
-        std::unique_ptr<LaunchOrder> o(new LaunchOrder());
-        if (hipEventCreateWithFlags(&o->last, hipEventDisableTiming) != hipSuccess)
-            return nullptr;
-        slot = std::move(o);
+    try {
+        auto& slot = g_order[device];
+        if (!slot) {
+            std::unique_ptr<LaunchOrder> o(new LaunchOrder());
+            if (hipEventCreateWithFlags(&o->last, hipEventDisableTiming) != hipSuccess)
+                return nullptr;
+            slot = std::move(o);
+        }
+        return slot.get();
+    } catch (...) {
+        return nullptr;
     }
-    return slot.get();
 }
 
+// nullptr if the host is out of memory.
 Scratch* scratch_for(int device, hipStream_t stream) {
     std::lock_guard<std::mutex> g(g_scratch_mutex);
-    auto& slot = g_scratch[{device, reinterpret_cast<uintptr_t>(stream)}];
-    if (!slot) slot.reset(new Scratch());
-    return slot.get();
+    try {
+        auto& slot = g_scratch[{device, reinterpret_cast<uintptr_t>(stream)}];
+        if (!slot) slot.reset(new Scratch());
+        return slot.get();
+    } catch (...) {
+        return nullptr;
+    }
 }
 
 int ensure_capacity(Scratch* sc, hipStream_t stream, int64_t tiles) {

@@ -215,6 +215,7 @@ int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream,
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return RLSCAN_ERR_HIP;
     Scratch* sc = scratch_for(device, stream);
+    if (sc == nullptr) return RLSCAN_ERR_ALLOC;
     std::lock_guard<std::mutex> g(sc->m);
     const int rc = ensure_capacity(sc, stream, pl.tiles);
     if (rc != RLSCAN_OK) return rc;
