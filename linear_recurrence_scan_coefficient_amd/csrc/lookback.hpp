@@ -59,6 +59,9 @@ struct LookbackArgs {
 // writes a poisoned result and finishes, so the kernel always ends.
 constexpr uint32_t kMaxPolls = 1u << 22;
 
+// Predecessors read by a look-back poll before it widens to the whole window.
+constexpr int kNarrow = 4;
+
 __device__ __forceinline__ float poisoned(float) { return __builtin_nanf(""); }
 __device__ __forceinline__ int64_t poisoned(int64_t) { return INT64_MIN; }
 
@@ -153,15 +156,27 @@ __device__ V look_back(const LookbackArgs& lb, uint64_t tile, int lane) {
         const int64_t q = top - (kWave - 1 - lane);
         A s = identity_step(A{});
         int stop = -1;
+        // Polls read the kNarrow nearest predecessors first (most walks end
+        // there: about half the tiles of a long row hold a chain cut) and
+        // the whole window only once those are ready and hold no terminal
+        // entry -- the status reads are uncached round trips that compete
+        // with the streaming loads.
+        int width = kNarrow;
         for (uint32_t polls = 0;; ++polls) {
-            int kind = 3;
-            if (q >= 0) kind = read_status(lb.status + q, lb.tag, s);
+            const bool in_window = kWave - 1 - lane < width;
+            int kind = q < 0 ? 3 : 0;
+            if (q >= 0 && in_window) kind = read_status(lb.status + q, lb.tag, s);
             const bool terminal = kind == 2 || (kind == 1 && cuts_chain(s));
             const uint64_t term_mask = __ballot(terminal);
             const uint64_t ready_mask = __ballot(kind != 0);
             stop = term_mask ? 63 - __clzll(term_mask) : -1;  // nearest terminal lane
             const uint64_t need = stop >= 0 ? (~0ull << stop) : ~0ull;
             if ((ready_mask & need) == need) break;
+            const uint64_t narrow = ~0ull << (kWave - kNarrow);
+            if (stop < 0 && width < kWave && (ready_mask & narrow) == narrow) {
+                width = kWave;  // no terminal entry near: read the whole window now
+                continue;
+            }
             if (polls >= kMaxPolls) {
                 if (lane == 0)
                     __hip_atomic_fetch_add(lb.timeouts, 1u, __ATOMIC_RELAXED,
