@@ -102,12 +102,12 @@ int auto_rounds(int est, int64_t NT) {
 }
 
 // Waves per workgroup (the tile is 256*W*R elements).
-//  - Four rounds (long inputs): eight waves double the tile, which halves
-//    the look-back hops per element but also the workgroups that fit on a
-//    CU.  That pays for the estimators whose four-round kernels need few
-//    registers (discounted returns, eligibility traces, prefix sum: at most
-//    ~96 VGPRs, five waves per SIMD); GAE, TD(lambda) and V-trace hold more
-//    per lane and run four waves.
+//  - Four rounds (long inputs): four waves.  Eight double the tile, which
+//    halves the look-back waits per element but also the workgroups that fit
+//    on a CU; with the narrow first poll of the look-back the waits are
+//    cheap, and four waves measured as fast or faster for every estimator
+//    (8 x 2^20: discounted 32.9 -> 31.4 us, eligibility 20.9 -> 20.0, prefix
+//    28.0 -> 27.6; GAE 47.5 -> 36.6).
 //  - One round (at most 2^20 elements, bound by launch and one memory round
 //    trip): the smallest tile that still holds whole rows -- more, smaller
 //    workgroups in flight.  Measured at 4096 x 128: one wave beat four by
@@ -120,9 +120,7 @@ int auto_rounds(int est, int64_t NT) {
 //    10-18 % faster; 4096 x 512 and 16384 x 128 (packed) up to 12 % for GAE
 //    and V-trace, the same within 4 % for the others.
 int auto_waves(int est, int rounds, int64_t T) {
-    if (rounds == 4)
-        return (est == RLSCAN_EST_DISCOUNTED || est == RLSCAN_EST_ELIGIBILITY ||
-                est == RLSCAN_EST_PREFIX_SUM) ? 8 : 4;
+    if (rounds == 4) return 4;
     if (rounds == 1) {
         const int first = (est == RLSCAN_EST_GAE || est == RLSCAN_EST_VTRACE) ? 2 : 1;
         for (int w = first; w <= 8; w *= 2)

@@ -143,9 +143,9 @@ def test_plan_mapping_choice(lib):
     p = rlscan.rlscan_plan("gae", 64, 8192)
     assert p["mapping"] == rlscan.MAP_LOOKBACK and p["threads"] == 512 and p["rounds"] == 1
     assert rlscan.rlscan_plan("gae", 5, 1000)["mapping"] == rlscan.MAP_LOOKBACK
-    # long rows: four rounds; eight waves for the low-register estimators
-    for est, waves in (("discounted_returns", 8), ("episodic_prefix_sum", 8),
-                       ("eligibility_traces", 8), ("gae", 4), ("vtrace", 4),
+    # long rows: four rounds of four waves
+    for est, waves in (("discounted_returns", 4), ("episodic_prefix_sum", 4),
+                       ("eligibility_traces", 4), ("gae", 4), ("vtrace", 4),
                        ("lambda_returns", 4)):
         big = rlscan.rlscan_plan(est, 8, 1 << 20)
         assert big["mapping"] == rlscan.MAP_LOOKBACK and big["rounds"] == 4, est
