@@ -698,7 +698,16 @@ def time_variants(torch, w, ests, sh, lib, args):
     sets = [CallSet(ests, w, seed, sh, lib, byte_flags=True) for seed in range(args.sets)]
     wall = time_eager_steps(torch, sets, args.steps, args.warmup)
     step_bytes = sum(sets[0].bytes.values())
-    del sets
+    groups = [s.group_array() for s in sets]
+    wall_g, dev_ms = time_group_steps(torch, lib, groups, sh, args.steps, args.warmup)
+    launch_us = dev_ms * 1000.0 / args.steps
+    res["production_u8_flags_grouped"] = {
+        "value": len(ests) * w.N * w.T * args.steps / wall_g, "unit": "elements/s",
+        "ms_per_step": wall_g * 1000.0 / args.steps, "bytes_per_step": step_bytes,
+        "avg_launch_us": round(launch_us, 3),
+        "GB_per_s": round(step_bytes / (launch_us * 1e-6) / 1e9, 1),
+        "note": "the seven calls with uint8 flags as one rlscan_group launch per step"}
+    del sets, groups
     torch.cuda.empty_cache()
     per = {}
     for e in ests:

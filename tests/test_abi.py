@@ -295,3 +295,5 @@ def test_group_argument_checks(lib):
     assert group(call(0, gamma=1.5)) == PARAM
     # misaligned pointer: refused while collecting, before any launch
     assert group(call(0, ins=[P[0] + 4] + P[1:6])) == PARAM
+    # empty calls are no-ops: a group of them launches nothing
+    assert group(call(0, N=0), call(5, T=0, ins=P[8:10], outs=P[10:11])) == OK
