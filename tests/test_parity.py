@@ -307,3 +307,49 @@ def test_lookback_calls_on_two_streams_without_host_synchronisation():
         assert_parity({k: v.cpu().numpy() for k, v in out.items()},
                       oracle_outputs(est, inputs, w), f"two streams call {i}")
     assert rlscan.rlscan_lookback_timeouts() == 0
+
+
+def test_calls_from_several_host_threads():
+    """Four host threads, each with its own stream, making look-back and
+    packed calls at once (the binding releases the interpreter lock during
+    each C call): every result is correct and no look-back wait times out."""
+    import threading
+
+    jobs = []
+    for t in range(4):
+        mine = []
+        for i, (est, N, T) in enumerate((("gae", 3, 70000), ("vtrace", 64, 128),
+                                        ("episodic_prefix_sum", 2, 90000),
+                                        ("discounted_returns", 512, 256))):
+            w, inputs = case(est, N, T, seed=400 + 10 * t + i)
+            mine.append((est, w, inputs, device.upload(inputs),
+                         device.alloc_outputs(est, w.N, w.T)))
+        jobs.append(mine)
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(mine):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for rep in range(3):
+                    for est, w, inputs, d, out in mine:
+                        device.call(est, d, out, w)
+            s.synchronize()
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(m,)) for m in jobs]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=60)
+    assert not any(th.is_alive() for th in threads)
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for t, mine in enumerate(jobs):
+        for est, w, inputs, d, out in mine:
+            print(f"[parity] thread {t}: {est} {w.N}x{w.T}", flush=True)
+            assert_parity({k: v.cpu().numpy() for k, v in out.items()},
+                          oracle_outputs(est, inputs, w), f"thread {t} {est}")
+    assert rlscan.rlscan_lookback_timeouts() == 0
