@@ -863,6 +863,9 @@ def main():
     dom_copy_us, dom_copy_gbs = copy_ceiling(torch, sh, lib, d["bytes"])
     plan = rlscan.rlscan_plan(dom, w.N, w.T, w.A)
     floor = launch_floor_us(torch, plan["grid"])
+    # the grouped launch's grid: every call's tiles at the group's wave count
+    group_grid = sum(-(-w.N * w.T // (256 * 2)) for _ in ests)
+    group_floor = launch_floor_us(torch, group_grid)
 
     result = {
         "metric": METRIC, "value": value, "unit": "elements/s", "n_gpus": 1,
@@ -899,7 +902,9 @@ def main():
                                                     "GB_per_s": round(dom_copy_gbs, 1)}},
             "note": "the seven C calls one after another on one stream"},
         "group_waves": waves_sweep,
-        "launch_floor_us": {"grid": plan["grid"], "us": round(floor, 3)},
+        "launch_floor_us": {"grid": plan["grid"], "us": round(floor, 3),
+                            "grouped_grid": group_grid, "grouped_us": round(group_floor, 3),
+                            "note": "an empty kernel of that many 256-thread workgroups"},
         "kernel_source_hash": kernel_source_hash(),
     }
 
