@@ -37,7 +37,7 @@ struct Scratch {
     unsigned long long* counter = nullptr;
     int64_t capacity = 0;       // tiles
     uint64_t next_ticket = 0;   // counter value at the start of the next call
-    uint64_t epoch = 0;         // tag of the last call (32-bit, 0 = none)
+    uint64_t epoch = 0;         // tag of the last call (below 2^31, 0 = none)
     bool broken = false;        // a launch failed: counter position unknown
 };
 
@@ -226,8 +226,9 @@ int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream,
     lb.ticket_counter = sc->counter;
     lb.timeouts = reinterpret_cast<unsigned int*>(sc->counter + 1);
     lb.ticket_base = sc->next_ticket;
-    if (sc->epoch == 0xffffffffull) {
-        // the 32-bit call tags are about to repeat: clear the status words
+    if (sc->epoch >= 0x7fffffffull) {
+        // the call tags (below 2^31: their top bit marks a one-word integer
+        // value) are about to repeat: clear the status words
         if (hipMemsetAsync(sc->status, 0, sizeof(TileStatus) * sc->capacity, stream) != hipSuccess)
             return RLSCAN_ERR_HIP;
         sc->epoch = 0;

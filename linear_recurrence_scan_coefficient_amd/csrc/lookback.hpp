@@ -25,6 +25,10 @@
 //    atomic: no release/acquire fences, hence no L2 write-back or invalidate
 //    on any XCD.  A payload wider than 32 bits spans two words, each
 //    validated by its own tag; each word is written once per call.
+//  * Integer states take two words only when they need them: a value that
+//    fits in 32 bits (signed) is published as one word whose tag has its top
+//    bit set (call tags stay below 2^31), so the common case costs a poll
+//    two status reads instead of four.
 //  * The look-back is wave-parallel: wave 0 reads the status of 64
 //    predecessors at once, waits until every one of them up to the nearest
 //    terminal entry (INCL, or an aggregate that cuts the chain) is ready,
@@ -48,8 +52,9 @@ struct LookbackArgs {
     unsigned long long* ticket_counter;
     unsigned int* timeouts;   // count of look-back waits that gave up
     uint64_t ticket_base;
-    uint32_t tag;             // the call's epoch: nonzero, distinct for every
-                              // call since the status buffer was cleared
+    uint32_t tag;             // the call's epoch: nonzero, below 2^31, distinct
+                              // for every call since the status buffer was
+                              // cleared
     uint32_t use_tickets;     // 1: tiles from tickets; 0: tile = blockIdx.x
 };
 
@@ -78,6 +83,20 @@ __device__ __forceinline__ bool has_tag(uint64_t w, uint32_t tag) {
     return static_cast<uint32_t>(w >> 32) == tag;
 }
 
+// Tag bit of an integer word that holds a whole value (sign-extended from its
+// 32-bit payload).
+constexpr uint32_t kShortForm = 0x80000000u;
+
+__device__ __forceinline__ bool fits_short(int64_t v) {
+    return v == static_cast<int64_t>(static_cast<int32_t>(v));
+}
+__device__ __forceinline__ int64_t short_value(uint64_t w) {
+    return static_cast<int64_t>(static_cast<int32_t>(static_cast<uint32_t>(w)));
+}
+__device__ __forceinline__ int64_t long_value(uint64_t lo, uint64_t hi) {
+    return static_cast<int64_t>(((hi & 0xffffffffull) << 32) | (lo & 0xffffffffull));
+}
+
 // ---------------------------------------------------------------- publish
 // The float aggregate's a is published rounded once to float32: a single
 // rounding, unlike the many that motivated the float64 a in StepD.
@@ -88,17 +107,23 @@ __device__ __forceinline__ void publish_aggregate(TileStatus* st, StepD s, uint3
 __device__ __forceinline__ void publish_inclusive(TileStatus* st, float x, uint32_t tag) {
     store_word(&st->w[2], tagged(tag, __float_as_uint(x)));
 }
+// Integer value v into words w[k] (and w[k+1] if it needs 64 bits).
+__device__ __forceinline__ void publish_int(uint64_t* w, int64_t v, uint32_t tag) {
+    const uint64_t u = static_cast<uint64_t>(v);
+    if (fits_short(v)) {
+        store_word(w, tagged(tag | kShortForm, static_cast<uint32_t>(u)));
+    } else {
+        store_word(w, tagged(tag, static_cast<uint32_t>(u)));
+        store_word(w + 1, tagged(tag, static_cast<uint32_t>(u >> 32)));
+    }
+}
 // An integer aggregate published as AGG never cuts the chain (a cut aggregate
 // is published as INCL), so its a is 1 and only b is stored.
 __device__ __forceinline__ void publish_aggregate(TileStatus* st, StepI s, uint32_t tag) {
-    const uint64_t b = static_cast<uint64_t>(s.b);
-    store_word(&st->w[0], tagged(tag, static_cast<uint32_t>(b)));
-    store_word(&st->w[1], tagged(tag, static_cast<uint32_t>(b >> 32)));
+    publish_int(&st->w[0], s.b, tag);
 }
 __device__ __forceinline__ void publish_inclusive(TileStatus* st, int64_t x, uint32_t tag) {
-    const uint64_t u = static_cast<uint64_t>(x);
-    store_word(&st->w[2], tagged(tag, static_cast<uint32_t>(u)));
-    store_word(&st->w[3], tagged(tag, static_cast<uint32_t>(u >> 32)));
+    publish_int(&st->w[2], x, tag);
 }
 
 // ---------------------------------------------------------------- read
@@ -119,18 +144,26 @@ __device__ __forceinline__ int read_status(TileStatus* st, uint32_t tag, StepD& 
     }
     return 0;
 }
+// The high word of a two-word value is read only once its low word is seen
+// (one dependent read, the inclusive value's if its low word is there).
 __device__ __forceinline__ int read_status(TileStatus* st, uint32_t tag, StepI& s) {
-    const uint64_t xl = load_word(&st->w[2]);
-    const uint64_t xh = load_word(&st->w[3]);
-    const uint64_t bl = load_word(&st->w[0]);
-    const uint64_t bh = load_word(&st->w[1]);
-    if (has_tag(xl, tag) && has_tag(xh, tag)) {
-        s = {0u, static_cast<int64_t>(((xh & 0xffffffffull) << 32) | (xl & 0xffffffffull))};
+    const uint64_t x = load_word(&st->w[2]);
+    const uint64_t b = load_word(&st->w[0]);
+    if (has_tag(x, tag | kShortForm)) {
+        s = {0u, short_value(x)};
         return 2;
     }
-    if (has_tag(bl, tag) && has_tag(bh, tag)) {
-        s = {1u, static_cast<int64_t>(((bh & 0xffffffffull) << 32) | (bl & 0xffffffffull))};
+    const bool x_long = has_tag(x, tag);
+    if (!x_long && has_tag(b, tag | kShortForm)) {
+        s = {1u, short_value(b)};
         return 1;
+    }
+    if (x_long || has_tag(b, tag)) {
+        const uint64_t hi = load_word(&st->w[x_long ? 3 : 1]);
+        if (has_tag(hi, tag)) {
+            s = {x_long ? 0u : 1u, long_value(x_long ? x : b, hi)};
+            return x_long ? 2 : 1;
+        }
     }
     return 0;
 }

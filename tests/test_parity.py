@@ -225,6 +225,24 @@ def test_prefix_sum_large_magnitudes():
     check("episodic_prefix_sum", w, inputs, "values near int32 max")
 
 
+@pytest.mark.parametrize("rounds,waves", [(0, 0), (1, 4), (4, 8)])
+def test_prefix_sum_mixed_magnitudes(rounds, waves):
+    """Blocks of small values between blocks of +-2^30: tile aggregates and
+    running sums that fit 32 bits and others that need 64, side by side in
+    one look-back window."""
+    N, T = 3, (1 << 20) + 123
+    w = workloads.custom(N, T, done_p=2e-4)
+    inputs = workloads.prefix_inputs(w, 5)
+    g = np.random.default_rng(5)
+    flat = inputs["x"].reshape(-1)
+    kinds = g.integers(0, 3, flat.size // 4096 + 1)
+    for k, sign in ((1, 1), (2, -1)):
+        idx = np.flatnonzero(np.repeat(kinds == k, 4096)[:flat.size])
+        flat[idx] = sign * ((1 << 30) + g.integers(0, 9, idx.size))
+    rlscan.rlscan_set_launch_override(rlscan.MAP_LOOKBACK, rounds, waves)
+    check("episodic_prefix_sum", w, inputs, f"mixed magnitudes R{rounds}W{waves}")
+
+
 # ------------------------------------------------------------ full workloads
 FULL = [(name, est) for name, wl in workloads.WORKLOADS.items() for est in wl.estimators]
 
