@@ -429,8 +429,9 @@ class CallSet:
             self.keep.append((d, out))
         self.w = w
 
-    def group_array(self):
-        """The set's calls as one rlscan_group argument array."""
+    def group_array(self, reverse=False):
+        """The set's calls as one rlscan_group argument array (reverse: in
+        the opposite order)."""
         from linear_recurrence_scan_coefficient_amd import device, rlscan
         calls = []
         for (est, _, _), (d, out) in zip(self.calls, self.keep):
@@ -440,6 +441,8 @@ class CallSet:
             calls.append(rlscan.GroupCall(est, ins, outs, gamma=w.gamma,
                                           lam=1.0 if est == "vtrace" else w.lam,
                                           rho_bar=w.rho_bar, c_bar=w.c_bar))
+        if reverse:
+            calls = calls[::-1]
         arr = (rlscan.Call * len(calls))(*[c.call for c in calls])
         return arr, len(calls), calls
 
@@ -848,6 +851,18 @@ def main():
         waves_sweep[str(wv)] = {"value": elems_per_step * args.steps / wall_g,
                                 "ms_per_step": wall_g * 1000.0 / args.steps}
     rlscan.rlscan_set_launch_override()
+    # grid layouts: the calls' tiles call after call (the default) or dealt
+    # in turn, with the calls in the given order and reversed (Retrace, the
+    # most bytes per tile, then sits near the end of the grid)
+    layouts = {}
+    rev_groups = [s.group_array(reverse=True) for s in sets]
+    for lay, flag in (("contiguous", 0), ("interleaved", rlscan.FLAG_GROUP_INTERLEAVED)):
+        rlscan.rlscan_set_launch_override(flags=flag)
+        for order, gs in (("given_order", groups), ("reversed_order", rev_groups)):
+            _, ms = time_group_steps(torch, lib, gs, sh, args.steps, args.warmup)
+            layouts[f"{lay}_{order}_us"] = round(ms * 1000.0 / args.steps, 3)
+    rlscan.rlscan_set_launch_override()
+    del rev_groups
 
     print("[bench] timing each estimator's launches", file=sys.stderr, flush=True)
     per_est = {}
@@ -902,6 +917,7 @@ def main():
                                                     "GB_per_s": round(dom_copy_gbs, 1)}},
             "note": "the seven C calls one after another on one stream"},
         "group_waves": waves_sweep,
+        "group_layouts": layouts,
         "launch_floor_us": {"grid": plan["grid"], "us": round(floor, 3),
                             "grouped_grid": group_grid, "grouped_us": round(group_floor, 3),
                             "note": "an empty kernel of that many 256-thread workgroups"},

@@ -424,8 +424,15 @@ typedef struct {
 int rlscan_plan(int estimator, int64_t N, int64_t T, int64_t A, rlscan_plan_info* info);
 
 enum {
-    RLSCAN_FLAG_TICKETS = 1  /* order look-back tiles by a ticket counter even
-                                with one workgroup per tile                   */
+    RLSCAN_FLAG_TICKETS = 1,          /* order look-back tiles by a ticket counter
+                                         even with one workgroup per tile     */
+    RLSCAN_FLAG_GROUP_INTERLEAVED = 2 /* rlscan_group: deal the workgroups to the
+                                         calls' tiles in turn instead of one
+                                         stretch of the grid per call: the
+                                         time no longer depends on the calls'
+                                         order (the contiguous default is
+                                         slowest when the call moving the
+                                         most bytes per tile comes last)    */
 };
 
 /* Overrides the planner for every later call in the process (tests and

@@ -179,6 +179,26 @@ int group(const rlscan_call* calls, int32_t count, hipStream_t stream) {
         }
         a.count = k;
         for (int32_t j = k; j <= kGroupMax; ++j) a.first_block[j] = blocks;
+        a.interleaved = (g_override.flags.load() & RLSCAN_FLAG_GROUP_INTERLEAVED) ? 1 : 0;
+        // interleaved schedule: calls by ascending tile count; segment s runs
+        // the calls order[s..k-1] for the tiles the shorter ones do not have
+        for (int32_t j = 0; j < k; ++j) a.order[j] = j;
+        for (int32_t j = 1; j < k; ++j)  // insertion sort: stable, k <= 8
+            for (int32_t q = j; q > 0 && a.e[a.order[q]].geo.num_tiles <
+                                             a.e[a.order[q - 1]].geo.num_tiles; --q) {
+                const int32_t t = a.order[q];
+                a.order[q] = a.order[q - 1];
+                a.order[q - 1] = t;
+            }
+        int64_t seg_block = 0, done_tiles = 0;
+        for (int32_t sg = 0; sg < k; ++sg) {
+            const int64_t tiles = a.e[a.order[sg]].geo.num_tiles;
+            a.seg_first[sg] = static_cast<int32_t>(seg_block);
+            a.seg_tile0[sg] = static_cast<int32_t>(done_tiles);
+            seg_block += (tiles - done_tiles) * (k - sg);  // sums to `blocks`
+            done_tiles = tiles;
+        }
+        for (int32_t sg = k; sg <= kGroupMax; ++sg) a.seg_first[sg] = static_cast<int32_t>(blocks);
         if (launch_group(a, col.waves, wide, col.lds, stream) != hipSuccess)
             return RLSCAN_ERR_HIP;
         start += k;

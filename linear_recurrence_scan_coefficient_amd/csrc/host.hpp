@@ -200,7 +200,7 @@ int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream,
     LookbackArgs lb{};
     if (t_group != nullptr) {  // collecting for a grouped launch: no side effects
         if (pl.mapping == RLSCAN_MAP_PACKED)
-            fn(geo, lb, pl);
+            (void)fn(geo, lb, pl);  // records the call; launches nothing
         else
             t_group->reject = true;
         return RLSCAN_OK;

@@ -4,7 +4,9 @@ against the float64 oracle and against the same calls made one by one.
 Cases: the seven estimators at the 4096 x 128 production shape, mixed shapes
 that need wider tiles, one-byte flags and V-trace's options inside a group,
 more calls than one launch takes, graph capture and replay, and the calls a
-group refuses (nothing may be written then)."""
+group refuses (nothing may be written then).  The shape cases run with the
+calls' tiles laid out call after call (the default) and interleaved over the
+grid."""
 from __future__ import annotations
 
 import numpy as np
@@ -40,6 +42,7 @@ def case(estimator, N, T, seed, **kw):
 
 
 FLAG_KEYS = ("terminated", "truncated", "dones")
+LAYOUTS = {"contiguous": 0, "interleaved": rlscan.FLAG_GROUP_INTERLEAVED}
 
 
 def group_call(estimator, d, out, w, **kw):
@@ -66,8 +69,9 @@ def close_to(got, ref, label):
             assert err.max() <= 1e-6, (label, k, float(err.max()))
 
 
+@pytest.mark.parametrize("layout", list(LAYOUTS))
 @pytest.mark.parametrize("waves", [0, 1, 2, 4])
-def test_group_of_the_seven_production_calls(waves):
+def test_group_of_the_seven_production_calls(waves, layout):
     """All seven estimators at 4096 x 128 in one launch: the oracle, and the
     same calls made one by one."""
     w = workloads.get("production_4096x128")
@@ -78,8 +82,8 @@ def test_group_of_the_seven_production_calls(waves):
         device.call(e, data[e], singles[e], w)
         grouped[e] = device.alloc_outputs(e, w.N, w.T)
         calls.append(group_call(e, data[e], grouped[e], w))
-    rlscan.rlscan_set_launch_override(waves=waves)
-    print(f"[group] production seven, waves={waves}", flush=True)
+    rlscan.rlscan_set_launch_override(waves=waves, flags=LAYOUTS[layout])
+    print(f"[group] production seven, waves={waves}, {layout}", flush=True)
     rlscan.rlscan_group(calls)
     torch.cuda.synchronize()
     for e in ESTIMATORS:
@@ -88,7 +92,8 @@ def test_group_of_the_seven_production_calls(waves):
         assert_parity(got, oracle_outputs(e, workloads.inputs_for(e, w, 3), w), f"group {e}")
 
 
-def test_group_of_mixed_shapes_flags_and_options():
+@pytest.mark.parametrize("layout", list(LAYOUTS))
+def test_group_of_mixed_shapes_flags_and_options(layout):
     """Different shapes in one group (the tile grows to hold 512-step rows),
     one-byte flags, Retrace with 4 and 8 actions, V-trace with lambda and a
     policy-gradient clip, a ragged last tile, and three 300-step rows that
@@ -120,14 +125,16 @@ def test_group_of_mixed_shapes_flags_and_options():
             want.append(oracle_outputs(e, inputs, w))
         calls.append(group_call(e, d, out, w, **opts))
         outs.append(out)
-    print("[group] mixed shapes", flush=True)
+    rlscan.rlscan_set_launch_override(flags=LAYOUTS[layout])
+    print(f"[group] mixed shapes, {layout}", flush=True)
     rlscan.rlscan_group(calls)
     torch.cuda.synchronize()
     for (e, N, T, _), out, ref in zip(specs, outs, want):
         assert_parity(host(out), ref, f"group mixed {e} {N}x{T}")
 
 
-def test_group_of_more_calls_than_one_launch_takes():
+@pytest.mark.parametrize("layout", list(LAYOUTS))
+def test_group_of_more_calls_than_one_launch_takes(layout):
     calls, outs, want = [], [], []
     for i in range(19):
         e = ESTIMATORS[i % len(ESTIMATORS)]
@@ -137,7 +144,8 @@ def test_group_of_more_calls_than_one_launch_takes():
         calls.append(group_call(e, d, out, w))
         outs.append(out)
         want.append((e, oracle_outputs(e, inputs, w)))
-    print("[group] 19 calls", flush=True)
+    rlscan.rlscan_set_launch_override(flags=LAYOUTS[layout])
+    print(f"[group] 19 calls, {layout}", flush=True)
     rlscan.rlscan_group(calls)
     torch.cuda.synchronize()
     for out, (e, ref) in zip(outs, want):
