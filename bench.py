@@ -5,9 +5,10 @@ TD(lambda), discounted returns, eligibility traces, episodic prefix sum) on
 the production-regime workload: 4096 environments x 128 steps, float32,
 inputs from the seeded generators (synthetic data with the distributions the
 pages benchmark).  Every estimator reads its own input arrays, and steps
-rotate over several buffer sets whose total exceeds the 256 MiB last-level
-cache, so each call reads its inputs from HBM.  Inputs are resident on the
-GPU before the timed region starts.
+rotate over buffer sets totalling at least COLD_BYTES (2 GiB, 8x the 256 MiB
+last-level cache; seeded sets plus device-side clones), so each call reads
+its inputs from HBM.  Inputs are resident on the GPU before the timed region
+starts.
 
 Timing.  The timed region is K steps, each one rlscan_group call that runs
 the seven estimator calls of the next buffer set in one kernel launch,
@@ -19,7 +20,7 @@ Beside it: the same seven calls made one by one on one stream (eager, as one
 HIP graph replay per step, and on one warm buffer set), the grouped step at
 each wave count, and each estimator's own average launch duration, measured
 with HIP events around replays of a graph of M back-to-back launches over M
-distinct buffer sets (M * bytes >= 512 MiB, so inputs come from HBM).  The
+buffer sets in distinct memory (M * bytes >= COLD_BYTES).  The
 long-sequence workload (8 x 2^20 steps, four estimators, decoupled
 look-back; timed over back-to-back calls, and with events around each
 call), the same rollout streamed through the carry calls, a supplementary
@@ -46,6 +47,20 @@ sys.path.insert(0, ROOT)
 METRIC = ("elements/s and achieved HBM GB/s per estimator at N=4096,T=128 and long-T; "
           "per-call µs")
 HBM_PEAK_GBS = 8000.0
+# Every timed rotation over buffer sets touches at least this many bytes per
+# pass, 8x the 256 MiB last-level cache.  Measured on MI355X: the grouped
+# production step takes 16.9 us when rotating over 0.53 GB, 18.1 us over
+# 1.06 GB and 18.4 us from 2.1 GB on (the long calls 2-4 % less between 0.6
+# and 2 GB); below a few GB part of the inputs still come from the cache.
+COLD_BYTES = 2 << 30
+
+
+def cold_rotation(sets, per_set_bytes, stream_handle, lib, cap=512):
+    """`sets` extended with device-side clones (same values, new buffers)
+    until one pass over them moves at least COLD_BYTES."""
+    n = max(len(sets), min(cap, -(-COLD_BYTES // max(1, per_set_bytes))))
+    return sets + [sets[i % len(sets)].clone(stream_handle, lib) for i in range(n - len(sets))]
+
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 _CSRC = os.path.join("linear_recurrence_scan_coefficient_amd", "csrc")
 KERNEL_SOURCES = ["include/rlscan.h"] + sorted(
@@ -66,13 +81,16 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--sets", type=int, default=6, help="rotated buffer sets (cold HBM)")
+    ap.add_argument("--sets", type=int, default=6,
+                    help="seeded buffer sets; device-side clones extend the rotation to "
+                         "COLD_BYTES")
     ap.add_argument("--long-calls", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the one-byte-flag, V-trace-option and float-prefix figures")
+                    help="skip the one-byte-flag, V-trace-option, float-prefix, "
+                         "grouped-layout and small-rotation figures")
     ap.add_argument("--only", default=None, help="comma list of estimators (profiling runs)")
     ap.add_argument("--pmc-run", default=None, metavar="ESTIMATOR",
                     help="counter runs: launch ESTIMATOR ('all': each estimator in turn; "
@@ -293,10 +311,12 @@ class StreamedSet:
     first for the forward ones.  V at an inner piece's end is the next
     piece's first value."""
 
-    def __init__(self, est, w, seed, chunks, stream_handle, lib):
+    def __init__(self, est, w, seed, chunks, stream_handle, lib, host=None):
         import torch
         from linear_recurrence_scan_coefficient_amd import device, workloads
-        host = workloads.inputs_for(est, w, seed)
+        if host is None:
+            host = workloads.inputs_for(est, w, seed)
+        self.host = host
         self.bytes = algorithmic_bytes(host, device.alloc_outputs(est, w.N, w.T))
         full = device.upload(host)
         N, T = w.N, w.T
@@ -333,17 +353,23 @@ class StreamedSet:
 
 def time_streamed(torch, w, sh, lib, chunks, reps):
     """Microseconds per whole rollout streamed in `chunks` calls per row
-    (back-to-back, alternating two buffer sets), per estimator."""
+    (back-to-back over two seeded buffer sets and further uploads of the same
+    values, at least COLD_BYTES per pass), per estimator."""
     res = {}
     for est in w.estimators:
         sets = [StreamedSet(est, w, seed, chunks, sh, lib) for seed in range(2)]
-        sets[0].run()
-        sets[1].run()
+        n = max(2, -(-COLD_BYTES // sets[0].bytes))
+        sets += [StreamedSet(est, w, 0, chunks, sh, lib, host=sets[i % 2].host)
+                 for i in range(n - 2)]
+        for st in sets:
+            st.host = None
+            st.run()
         torch.cuda.synchronize()
+        reps = max(reps, n)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for i in range(reps):
-            sets[i % 2].run()
+            sets[i % len(sets)].run()
         b.record()
         torch.cuda.synchronize()
         us = a.elapsed_time(b) / reps * 1000.0
@@ -429,6 +455,23 @@ class CallSet:
             self.keep.append((d, out))
         self.w = w
 
+    def clone(self, stream_handle, lib):
+        """A set with the same input values in new device buffers (and its own
+        outputs): more distinct addresses for a cold rotation without more
+        host-side input generation."""
+        from linear_recurrence_scan_coefficient_amd import device
+        c = CallSet.__new__(CallSet)
+        c.calls, c.bytes, c.keep, c.w = [], dict(self.bytes), [], self.w
+        for (est, fn, _), (d, out) in zip(self.calls, self.keep):
+            d2 = {k: (None if v is None else v.clone()) for k, v in d.items()}
+            out2 = device.alloc_outputs(est, self.w.N, self.w.T)
+            byte_flags = fn.__name__.endswith("_u8")
+            make = raw_u8_call_args if byte_flags else raw_call_args
+            name, args = make(est, d2, out2, self.w, stream_handle)
+            c.calls.append((est, getattr(lib, name), args))
+            c.keep.append((d2, out2))
+        return c
+
     def group_array(self, reverse=False):
         """The set's calls as one rlscan_group argument array (reverse: in
         the opposite order)."""
@@ -500,11 +543,14 @@ def time_batched_calls(torch, sets, reps):
 
 def eager_workload(torch, w, sh, lib, reps, nsets=3, byte_flags=False):
     """Per-call figures of every estimator of a large workload: `reps`
-    back-to-back calls per estimator cycling through `nsets` buffer sets (each
-    set alone exceeds the last-level cache, so inputs come from HBM), the
+    back-to-back calls per estimator cycling through `nsets` seeded buffer
+    sets and their device-side clones (at least COLD_BYTES per pass), the
     same calls with an event pair around each one (what one isolated call
     costs, launch gap included), and the copy ceiling for the same bytes."""
     sets = [CallSet(w.estimators, w, seed, sh, lib, byte_flags) for seed in range(nsets)]
+    # clones until one pass of the smallest estimator's calls moves COLD_BYTES
+    sets = cold_rotation(sets, min(sets[0].bytes.values()), sh, lib)
+    reps = max(reps, len(sets))
     per = time_batched_calls(torch, sets, reps)
     iso = time_eager_calls(torch, sets, reps)
     nbytes = dict(sets[0].bytes)
@@ -600,27 +646,29 @@ def time_launches(torch, graph, launches, reps):
     return sum(ms) / len(ms) / launches * 1000.0
 
 
-def per_kernel(torch, est, w, sh, lib, min_bytes=512 << 20, reps=10, byte_flags=False):
-    """Average launch duration of one estimator over M distinct buffer sets
-    (M * bytes >= min_bytes, so every launch reads cold inputs)."""
+def per_kernel(torch, est, w, sh, lib, reps=10, byte_flags=False):
+    """Average launch duration of one estimator over M buffer sets in distinct
+    memory (6 seeds, then device-side clones; M * bytes >= COLD_BYTES, so
+    every launch reads cold inputs)."""
     probe = CallSet([est], w, 0, sh, lib, byte_flags)
     b = probe.bytes[est]
-    m = max(6, min(64, -(-min_bytes // b)))
-    sets = [probe] + [CallSet([est], w, seed, sh, lib, byte_flags) for seed in range(1, m)]
+    sets = [probe] + [CallSet([est], w, seed, sh, lib, byte_flags) for seed in range(1, 6)]
+    sets = cold_rotation(sets, b, sh, lib)
+    m = len(sets)
     g = capture_graph(torch, [s.calls[0] for s in sets])
     us = time_launches(torch, g, m, reps)
     del g, sets
     return us, b, m
 
 
-def copy_ceiling(torch, sh, lib, nbytes, min_bytes=512 << 20, reps=10):
+def copy_ceiling(torch, sh, lib, nbytes, min_bytes=COLD_BYTES, reps=10):
     """Achievable bandwidth for a launch that moves `nbytes` (read + write):
     a plain streaming copy of nbytes/2 bytes (the library's diagnostic copy
     kernel, same 16-byte non-temporal accesses as the scans), timed like
     `per_kernel` over M distinct buffer pairs so every copy reads cold data.
     Returns (microseconds per copy, GB/s counting read and write bytes)."""
     half = (nbytes // 2) // 16 * 16
-    m = max(6, min(64, -(-min_bytes // max(1, 2 * half))))
+    m = max(6, min(512, -(-min_bytes // max(1, 2 * half))))
     pairs = [(torch.ones(half, dtype=torch.uint8, device="cuda"),
               torch.empty(half, dtype=torch.uint8, device="cuda")) for _ in range(m)]
     calls = [("copy", lib.rlscan_stream_copy, (dst.data_ptr(), src.data_ptr(), half, sh))
@@ -699,8 +747,9 @@ def time_variants(torch, w, ests, sh, lib, args):
     from linear_recurrence_scan_coefficient_amd import workloads
     res = {}
     sets = [CallSet(ests, w, seed, sh, lib, byte_flags=True) for seed in range(args.sets)]
-    wall = time_eager_steps(torch, sets, args.steps, args.warmup)
     step_bytes = sum(sets[0].bytes.values())
+    sets = cold_rotation(sets, step_bytes, sh, lib)
+    wall = time_eager_steps(torch, sets, args.steps, args.warmup)
     groups = [s.group_array() for s in sets]
     wall_g, dev_ms = time_group_steps(torch, lib, groups, sh, args.steps, args.warmup)
     launch_us = dev_ms * 1000.0 / args.steps
@@ -732,34 +781,31 @@ def time_variants(torch, w, ests, sh, lib, args):
     return res
 
 
-def time_vtrace_ex(torch, w, sh, lib, reps=200, nsets=4):
+def time_vtrace_ex(torch, w, sh, lib, reps=10, nsets=4):
     """rlscan_vtrace_ex (lambda 0.95, rho_bar_pg 0.5) against rlscan_vtrace on
-    the same production buffers: mean us per call from one event pair around
-    `reps` back-to-back calls."""
+    the same production buffers (a rotation of at least COLD_BYTES): average
+    launch duration from HIP events around replays of a graph of one launch
+    per buffer set, as for the per-estimator figures."""
     from linear_recurrence_scan_coefficient_amd import device, workloads
     keep, plain, ex = [], [], []
-    for seed in range(nsets):
-        d = device.upload(workloads.inputs_for("vtrace", w, seed))
+    seeded = [device.upload(workloads.inputs_for("vtrace", w, seed)) for seed in range(nsets)]
+    set_bytes = sum(v.nbytes for v in seeded[0].values() if v is not None) + 2 * 4 * w.N * w.T
+    n = max(nsets, min(512, -(-COLD_BYTES // set_bytes)))
+    for i in range(n):  # seeded sets, then device-side clones of them
+        d = seeded[i] if i < nsets else {k: (None if v is None else v.clone())
+                                         for k, v in seeded[i % nsets].items()}
         out = device.alloc_outputs("vtrace", w.N, w.T)
         keep.append((d, out))
         name, a = raw_call_args("vtrace", d, out, w, sh)
-        plain.append((getattr(lib, name), a))
+        plain.append(("vtrace", getattr(lib, name), a))
         ex_args = a[:7] + (None,) + a[7:9] + (None, w.N, w.T, w.gamma, 0.95, w.rho_bar, w.c_bar,
                                                0.5, sh)
-        ex.append((lib.rlscan_vtrace_ex, ex_args))
+        ex.append(("vtrace_ex", lib.rlscan_vtrace_ex, ex_args))
     res = {}
     for label, calls in (("plain_us_per_call", plain), ("ex_us_per_call", ex)):
-        for fn, a in calls:
-            assert fn(*a) == 0
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(reps):
-            fn, a = calls[i % len(calls)]
-            fn(*a)
-        e1.record()
-        torch.cuda.synchronize()
-        res[label] = round(e0.elapsed_time(e1) / reps * 1000.0, 3)
+        g = capture_graph(torch, calls)
+        res[label] = round(time_launches(torch, g, len(calls), reps), 3)
+        del g
     res["workload"] = w.name
     return res
 
@@ -767,7 +813,7 @@ def time_vtrace_ex(torch, w, sh, lib, reps=200, nsets=4):
 def time_prefix_f32(torch, sh, lib, reps, nsets=3):
     """rlscan_episodic_prefix_sum_f32 on the long-rollout shape (8 x 2^20,
     float32 x ~ N(0,1), dones ~ Bernoulli(1e-4)): back-to-back calls over
-    buffer sets larger than the last-level cache."""
+    buffer sets of at least COLD_BYTES per pass."""
     import numpy as np
     N, T = 8, 1 << 20
     bufs = []
@@ -776,6 +822,11 @@ def time_prefix_f32(torch, sh, lib, reps, nsets=3):
         x = torch.from_numpy(rng.standard_normal((N, T)).astype(np.float32)).cuda()
         dn = torch.from_numpy((rng.random((N, T)) < 1e-4).astype(np.float32)).cuda()
         bufs.append((x, dn, torch.empty((N, T), device="cuda")))
+    set_bytes = 3 * 4 * N * T
+    for i in range(nsets, max(nsets, -(-COLD_BYTES // set_bytes))):  # device-side clones
+        x, dn, _ = bufs[i % nsets]
+        bufs.append((x.clone(), dn.clone(), torch.empty((N, T), device="cuda")))
+    reps = max(reps, len(bufs))
     calls = [(x.data_ptr(), dn.data_ptr(), None, o.data_ptr(), None, N, T, sh) for x, dn, o in bufs]
     for a in calls:
         assert lib.rlscan_episodic_prefix_sum_f32(*a) == 0
@@ -822,8 +873,10 @@ def main():
     for e in ests:
         assert rlscan.rlscan_plan(e, w.N, w.T, w.A)["mapping"] == rlscan.MAP_PACKED
     print(f"[bench] preparing {args.sets} buffer sets of {w.name}", file=sys.stderr, flush=True)
-    sets = [CallSet(ests, w, seed, sh, lib) for seed in range(args.sets)]
-    set_bytes = sum(sets[0].bytes.values())
+    seeded = [CallSet(ests, w, seed, sh, lib) for seed in range(args.sets)]
+    set_bytes = sum(seeded[0].bytes.values())
+    # the timed rotation: the seeded sets and device-side clones of them
+    sets = cold_rotation(seeded, set_bytes, sh, lib)
     groups = [s.group_array() for s in sets]
     elems_per_step = len(ests) * w.N * w.T
 
@@ -835,6 +888,20 @@ def main():
     value = elems_per_step * args.steps / wall
     launch_us = dev_ms * 1000.0 / args.steps
     group_gbs = set_bytes / (launch_us * 1e-6) / 1e9
+    # context (with the variants: the same kernel symbol, so left out of
+    # profiling runs of the production step alone): the same step rotating
+    # over the seeded sets only, a pass smaller than COLD_BYTES, part of it
+    # served from the last-level cache
+    small_rotation = None
+    if not args.no_variants:
+        wall_small, dev_small = time_group_steps(torch, lib, groups[:len(seeded)], sh,
+                                                 args.steps, args.warmup)
+        small_rotation = {
+            "buffer_sets": len(seeded), "rotation_bytes": set_bytes * len(seeded),
+            "ms_per_step": wall_small * 1000.0 / args.steps,
+            "avg_launch_us": round(dev_small * 1000.0 / args.steps, 3),
+            "note": "the timed step rotating over the seeded sets only: part of each pass "
+                    "is still served from the last-level cache"}
 
     # the same seven calls made one by one on one stream: eager, as one HIP
     # graph replay per step, and on one warm set
@@ -854,15 +921,19 @@ def main():
     # grid layouts: the calls' tiles call after call (the default) or dealt
     # in turn, with the calls in the given order and reversed (Retrace, the
     # most bytes per tile, then sits near the end of the grid)
-    layouts = {}
-    rev_groups = [s.group_array(reverse=True) for s in sets]
-    for lay, flag in (("contiguous", 0), ("interleaved", rlscan.FLAG_GROUP_INTERLEAVED)):
-        rlscan.rlscan_set_launch_override(flags=flag)
-        for order, gs in (("given_order", groups), ("reversed_order", rev_groups)):
-            _, ms = time_group_steps(torch, lib, gs, sh, args.steps, args.warmup)
-            layouts[f"{lay}_{order}_us"] = round(ms * 1000.0 / args.steps, 3)
-    rlscan.rlscan_set_launch_override()
-    del rev_groups
+    # (a variant: the same kernel symbol, so left out of profiling runs of the
+    # production step alone)
+    layouts = None
+    if not args.no_variants:
+        layouts = {}
+        rev_groups = [s.group_array(reverse=True) for s in sets]
+        for lay, flag in (("contiguous", 0), ("interleaved", rlscan.FLAG_GROUP_INTERLEAVED)):
+            rlscan.rlscan_set_launch_override(flags=flag)
+            for order, gs in (("given_order", groups), ("reversed_order", rev_groups)):
+                _, ms = time_group_steps(torch, lib, gs, sh, args.steps, args.warmup)
+                layouts[f"{lay}_{order}_us"] = round(ms * 1000.0 / args.steps, 3)
+        rlscan.rlscan_set_launch_override()
+        del rev_groups
 
     print("[bench] timing each estimator's launches", file=sys.stderr, flush=True)
     per_est = {}
@@ -888,7 +959,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "N": w.N, "T": w.T, "estimators": ests, "A": w.A,
-                   "gamma": w.gamma, "lambda": w.lam, "buffer_sets": args.sets,
+                   "gamma": w.gamma, "lambda": w.lam, "buffer_sets": len(sets),
+                   "seeded_buffer_sets": args.sets, "rotation_bytes": set_bytes * len(sets),
                    "bytes_per_step": set_bytes,
                    "launch": "one rlscan_group call per step: the seven estimator calls "
                              "in one kernel launch"},
@@ -916,6 +988,7 @@ def main():
                                 "copy_same_bytes": {"us": round(dom_copy_us, 3),
                                                     "GB_per_s": round(dom_copy_gbs, 1)}},
             "note": "the seven C calls one after another on one stream"},
+        "small_rotation": small_rotation,
         "group_waves": waves_sweep,
         "group_layouts": layouts,
         "launch_floor_us": {"grid": plan["grid"], "us": round(floor, 3),

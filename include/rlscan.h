@@ -430,9 +430,10 @@ enum {
                                          calls' tiles in turn instead of one
                                          stretch of the grid per call: the
                                          time no longer depends on the calls'
-                                         order (the contiguous default is
-                                         slowest when the call moving the
-                                         most bytes per tile comes last)    */
+                                         order.  The contiguous default is
+                                         faster when the call moving the most
+                                         bytes per tile is not last, slower
+                                         when it is                         */
 };
 
 /* Overrides the planner for every later call in the process (tests and

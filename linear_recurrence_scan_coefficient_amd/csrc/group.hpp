@@ -9,20 +9,20 @@
 // overlap.
 //
 // Layout of the grid.  By default each call's tiles form one contiguous
-// stretch of workgroups, call after call, in the order given.  Measured on
-// the seven 4096 x 128 production calls (two waves): 16.8 us in the order
-// GAE, V-trace, Retrace, TD(lambda), discounted, traces, prefix sum, but
-// 17.7 us with Retrace (72 B per element, 4.5x the bytes of a GAE tile)
-// first and 20.3 us with it last, where its tiles form the kernel's tail.
-// RLSCAN_FLAG_GROUP_INTERLEAVED deals the workgroups to the calls' tiles in
-// turn instead: with the calls sorted by tile count, the grid is cut into
-// segments; segment s runs the calls that still have tiles after the s
-// shortest ones are done, one tile of each in turn, the turn order rotating
-// by one call every row (workgroups go to the XCDs round-robin, so a fixed
-// turn order of 8 calls would put each call on one XCD).  Every stretch of
-// the grid then holds the same mix of heavy and light tiles: 17.1 us in any
-// of the three orders above.  Runs of 4 to 256 consecutive tiles per turn
-// measured 17.3-18.7 us.
+// stretch of workgroups, call after call, in the order given.  The order
+// matters: on the seven 4096 x 128 production calls (two waves, inputs
+// rotating over 2 GB of buffers) the order GAE, V-trace, Retrace, TD(lambda),
+// discounted, traces, prefix sum takes 18.4 us and the reverse order 21.5 us,
+// where Retrace's tiles (72 B per element, 4.5x the bytes of a GAE tile)
+// form the kernel's tail.  RLSCAN_FLAG_GROUP_INTERLEAVED deals the
+// workgroups to the calls' tiles in turn instead: with the calls sorted by
+// tile count, the grid is cut into segments; segment s runs the calls that
+// still have tiles after the s shortest ones are done, one tile of each in
+// turn, the turn order rotating by one call every row (workgroups go to the
+// XCDs round-robin, so a fixed turn order of 8 calls would put each call on
+// one XCD).  Every stretch of the grid then holds the same mix of heavy and
+// light tiles and the time no longer depends on the order: 20.0 us in
+// either order.  Runs of 4 to 256 consecutive tiles per turn were no faster.
 //
 // Calls join a group when their own plan is packed, every pointer takes the
 // vector path, no carry is given, and their tile at the group's wave count
