@@ -361,6 +361,12 @@ int rlscan_episodic_prefix_sum_u8(const int32_t* x, const uint8_t* dones,
  * Retrace, A in {4, 6, 8}.  The calls must be independent: no call may
  * write a buffer another call of the group reads or writes.
  *
+ * Each call's tiles run as one contiguous stretch of the launch's workgroups,
+ * in the order given (or dealt in turn with RLSCAN_FLAG_GROUP_INTERLEAVED,
+ * see rlscan_set_launch_override).  The order changes the time, not the
+ * results: a call that moves many bytes per tile (Retrace) is best placed
+ * early, since placed last its tiles form the launch's tail.
+ *
  * Returns the first failing call's status (its argument checks are those of
  * its entry point), RLSCAN_ERR_PARAM if a call cannot be grouped or names an
  * unknown estimator, RLSCAN_ERR_ALIAS for calls that are not independent;
