@@ -501,9 +501,10 @@ class CallSet:
 
 
 def time_eager_calls(torch, sets, reps):
-    """Mean microseconds per call, each call bracketed by HIP events (for
-    calls long enough that launch gaps do not matter, and for the look-back
-    mapping, which is not captured into graphs)."""
+    """Microseconds of each call, every call bracketed by HIP events (what one
+    isolated call costs, launch gap included; also for the look-back
+    mapping, which is not captured into graphs): a list of `reps` samples
+    per estimator."""
     ests = [c[0] for c in sets[0].calls]
     sets[0].run()
     torch.cuda.synchronize()
@@ -512,8 +513,17 @@ def time_eager_calls(torch, sets, reps):
     for i in range(reps):
         sets[i % len(sets)].run(ev[i])
     torch.cuda.synchronize()
-    return {e: sum(row[j].elapsed_time(row[j + 1]) for row in ev) / reps * 1000.0
+    return {e: [row[j].elapsed_time(row[j + 1]) * 1000.0 for row in ev]
             for j, e in enumerate(ests)}
+
+
+def spread(samples):
+    """Median, p10 and p90 of a list of microsecond samples."""
+    xs = sorted(samples)
+
+    def q(f):
+        return round(xs[min(len(xs) - 1, int(f * (len(xs) - 1) + 0.5))], 3)
+    return {"median": q(0.5), "p10": q(0.1), "p90": q(0.9), "samples": len(xs)}
 
 
 def time_batched_calls(torch, sets, reps):
@@ -552,7 +562,7 @@ def eager_workload(torch, w, sh, lib, reps, nsets=3, byte_flags=False):
     sets = cold_rotation(sets, min(sets[0].bytes.values()), sh, lib)
     reps = max(reps, len(sets))
     per = time_batched_calls(torch, sets, reps)
-    iso = time_eager_calls(torch, sets, reps)
+    iso = time_eager_calls(torch, sets, max(reps, 50))
     nbytes = dict(sets[0].bytes)
     del sets
     torch.cuda.empty_cache()
@@ -564,7 +574,8 @@ def eager_workload(torch, w, sh, lib, reps, nsets=3, byte_flags=False):
         res[e] = {"us_per_call": round(us, 2), "elements_per_s": w.N * w.T / (us * 1e-6),
                   "bytes": b, "GB_per_s": round(gbs, 1),
                   "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-                  "us_per_isolated_call": round(iso[e], 2),
+                  "us_per_isolated_call": round(sum(iso[e]) / len(iso[e]), 2),
+                  "isolated_call_us": spread(iso[e]),
                   "copy_same_bytes_GB_per_s": round(copy_gbs, 1),
                   "frac_of_copy": round(gbs / copy_gbs, 4)}
     return res
@@ -943,6 +954,11 @@ def main():
         per_est[e] = {"us_per_call": round(us, 3), "elements_per_s": w.N * w.T / (us * 1e-6),
                       "bytes": b, "GB_per_s": round(gbs, 1),
                       "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "buffer_sets": m}
+    # each call alone: an event pair around every call of 100 steps made one
+    # call at a time over the cold rotation
+    iso = time_eager_calls(torch, sets, 100)
+    for e in ests:
+        per_est[e]["isolated_call_us"] = spread(iso[e])
     dom = max(ests, key=lambda e: per_est[e]["us_per_call"])
     d = per_est[dom]
     copy_us, copy_gbs = copy_ceiling(torch, sh, lib, set_bytes)
