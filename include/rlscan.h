@@ -432,7 +432,7 @@ int rlscan_plan(int estimator, int64_t N, int64_t T, int64_t A, rlscan_plan_info
 enum {
     RLSCAN_FLAG_TICKETS = 1,          /* order look-back tiles by a ticket counter
                                          even with one workgroup per tile     */
-    RLSCAN_FLAG_GROUP_INTERLEAVED = 2 /* rlscan_group: deal the workgroups to the
+    RLSCAN_FLAG_GROUP_INTERLEAVED = 2, /* rlscan_group: deal the workgroups to the
                                          calls' tiles in turn instead of one
                                          stretch of the grid per call: the
                                          time no longer depends on the calls'
@@ -440,6 +440,11 @@ enum {
                                          faster when the call moving the most
                                          bytes per tile is not last, slower
                                          when it is                         */
+    RLSCAN_FLAG_LOOKBACK_GIVE_UP = 4  /* tests of the failure path: every
+                                         look-back wait gives up after a few
+                                         polls, as if no predecessor had
+                                         published; see
+                                         rlscan_lookback_timeouts            */
 };
 
 /* Overrides the planner for every later call in the process (tests and
@@ -470,11 +475,14 @@ int rlscan_launch_floor(int64_t grid, hipStream_t stream);
 int rlscan_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
 
 /* Diagnostics: waits in the look-back are bounded (a few seconds per
- * predecessor); a wait that reaches the bound is counted, its tile's results
- * are written as NaN (INT64_MIN for the prefix sum) and the kernel finishes.
- * This call waits for every stream that has look-back scratch, then stores
- * the total count of such timeouts since the scratch was allocated.  A
- * correct build never reports one; the tests assert that. */
+ * predecessor); a wait that reaches the bound is counted, its tile takes NaN
+ * as its entering state, so every float result of the tile is NaN (the
+ * prefix sum takes INT64_MIN: the tile's results up to its first reset are
+ * INT64_MIN plus their partial sums, in wrapping int64 arithmetic), and the
+ * kernel finishes.  This call waits for every stream that has look-back
+ * scratch, then stores the total count of such timeouts since the scratch
+ * was allocated.  A correct build never reports one; the tests assert that
+ * (and force the path with RLSCAN_FLAG_LOOKBACK_GIVE_UP). */
 int rlscan_lookback_timeouts(uint64_t* count);
 
 #ifdef __cplusplus

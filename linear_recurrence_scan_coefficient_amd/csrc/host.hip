@@ -303,7 +303,8 @@ int rlscan_set_launch_override(int mapping, int rounds, int waves, int64_t grid_
     if (rounds != 0 && rounds != 1 && rounds != 2 && rounds != 4) return RLSCAN_ERR_PARAM;
     if (waves != 0 && waves != 1 && waves != 2 && waves != 4 && waves != 8)
         return RLSCAN_ERR_PARAM;
-    if (grid_cap < 0 || (flags & ~(RLSCAN_FLAG_TICKETS | RLSCAN_FLAG_GROUP_INTERLEAVED)) != 0)
+    if (grid_cap < 0 || (flags & ~(RLSCAN_FLAG_TICKETS | RLSCAN_FLAG_GROUP_INTERLEAVED |
+                                    RLSCAN_FLAG_LOOKBACK_GIVE_UP)) != 0)
         return RLSCAN_ERR_PARAM;
     g_override.mapping.store(mapping);
     g_override.rounds.store(rounds);

@@ -226,14 +226,17 @@ int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream,
     lb.ticket_counter = sc->counter;
     lb.timeouts = reinterpret_cast<unsigned int*>(sc->counter + 1);
     lb.ticket_base = sc->next_ticket;
-    if (sc->epoch >= 0x7fffffffull) {
-        // the call tags (below 2^31: their top bit marks a one-word integer
-        // value) are about to repeat: clear the status words
+    if (sc->epoch >= kLastTag) {
+        // the call tags (at most kLastTag: their top bit marks a one-word
+        // integer value) are about to repeat: clear the status words
         if (hipMemsetAsync(sc->status, 0, sizeof(TileStatus) * sc->capacity, stream) != hipSuccess)
             return RLSCAN_ERR_HIP;
         sc->epoch = 0;
     }
     lb.tag = static_cast<uint32_t>(++sc->epoch);
+    const bool give_up = (g_override.flags.load() & RLSCAN_FLAG_LOOKBACK_GIVE_UP) != 0;
+    lb.read_tag = give_up ? kNeverTag : lb.tag;
+    lb.max_polls = give_up ? 8u : kMaxPolls;
     LaunchOrder* order = launch_order(device);
     if (order == nullptr) return RLSCAN_ERR_HIP;
     std::lock_guard<std::mutex> go(order->m);

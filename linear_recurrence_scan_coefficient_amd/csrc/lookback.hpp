@@ -52,16 +52,27 @@ struct LookbackArgs {
     unsigned long long* ticket_counter;
     unsigned int* timeouts;   // count of look-back waits that gave up
     uint64_t ticket_base;
-    uint32_t tag;             // the call's epoch: nonzero, below 2^31, distinct
-                              // for every call since the status buffer was
-                              // cleared
+    uint32_t tag;             // the call's epoch: nonzero, at most
+                              // kLastTag, distinct for every call since the
+                              // status buffer was cleared
     uint32_t use_tickets;     // 1: tiles from tickets; 0: tile = blockIdx.x
+    uint32_t read_tag;        // tag the look-back accepts: `tag`, or kNeverTag
+                              // to make every wait give up (tests)
+    uint32_t max_polls;       // polls of one window before a wait gives up
 };
+
+// Call tags run from 1 to kLastTag; kNeverTag is never written, in either
+// form (a float or two-word integer word carries the tag, a one-word integer
+// the tag with its top bit set), so a look-back reading with it never sees a
+// ready predecessor.
+constexpr uint32_t kLastTag = 0x7ffffffeu;
+constexpr uint32_t kNeverTag = 0x7fffffffu;
 
 // Upper bound on the polls of one look-back window (each poll sleeps about
 // 64 cycles plus a memory round trip: several seconds in all).  A wait that
 // long means the protocol is broken; the workgroup then records the failure,
-// writes a poisoned result and finishes, so the kernel always ends.
+// writes a poisoned result and finishes, so the kernel always ends.  (Tests
+// force this path with a few polls and kNeverTag.)
 constexpr uint32_t kMaxPolls = 1u << 22;
 
 // Predecessors read by a look-back poll before it widens to the whole window.
@@ -198,7 +209,7 @@ __device__ V look_back(const LookbackArgs& lb, uint64_t tile, int lane) {
         for (uint32_t polls = 0;; ++polls) {
             const bool in_window = kWave - 1 - lane < width;
             int kind = q < 0 ? 3 : 0;
-            if (q >= 0 && in_window) kind = read_status(lb.status + q, lb.tag, s);
+            if (q >= 0 && in_window) kind = read_status(lb.status + q, lb.read_tag, s);
             const bool terminal = kind == 2 || (kind == 1 && cuts_chain(s));
             const uint64_t term_mask = __ballot(terminal);
             const uint64_t ready_mask = __ballot(kind != 0);
@@ -210,7 +221,7 @@ __device__ V look_back(const LookbackArgs& lb, uint64_t tile, int lane) {
                 width = kWave;  // no terminal entry near: read the whole window now
                 continue;
             }
-            if (polls >= kMaxPolls) {
+            if (polls >= lb.max_polls) {
                 if (lane == 0)
                     __hip_atomic_fetch_add(lb.timeouts, 1u, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);

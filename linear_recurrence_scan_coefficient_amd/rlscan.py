@@ -34,6 +34,7 @@ RLSCAN_ERR_CAPTURE = -7
 MAP_AUTO, MAP_PACKED, MAP_LOOKBACK = 0, 1, 2
 FLAG_TICKETS = 1
 FLAG_GROUP_INTERLEAVED = 2  # rlscan_group: deal workgroups to the calls' tiles in turn
+FLAG_LOOKBACK_GIVE_UP = 4  # tests: every look-back wait gives up (poisoned outputs)
 
 ESTIMATOR_IDS = {
     "gae": 0, "lambda_returns": 1, "discounted_returns": 2, "vtrace": 3, "retrace": 4,

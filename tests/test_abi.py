@@ -182,7 +182,7 @@ def test_plan_mapping_choice(lib):
     with pytest.raises(rlscan.RlscanError):
         rlscan.rlscan_set_launch_override(waves=6)
     with pytest.raises(rlscan.RlscanError):
-        rlscan.rlscan_set_launch_override(flags=4)
+        rlscan.rlscan_set_launch_override(flags=8)
     with pytest.raises(rlscan.RlscanError):
         rlscan.rlscan_plan("gae", -1, 5)
     assert rlscan.rlscan_plan("gae", 0, 5)["tiles"] == 0
