@@ -106,6 +106,14 @@ def parse_args():
                          "of a --pmc-run and the counter_collection.csv of its three "
                          "rocprofv3 --pmc passes (FETCH_SIZE; WRITE_SIZE; TCC_HIT_sum "
                          "TCC_MISS_sum); no GPU needed")
+    ap.add_argument("--trace-summary", nargs=5, default=None,
+                    metavar=("RUN_LOG", "STATS_CSV", "TRACE_CSV", "OUT_MD", "COMMAND"),
+                    help="write a kernel-duration summary (markdown) of a rocprofv3 "
+                         "--kernel-trace --stats run of this script: the kernel_stats.csv "
+                         "table, and the grouped kernel's average over the timed production "
+                         "steps (its first warmup + steps dispatches in the kernel_trace.csv) "
+                         "beside the bench line of the run (RUN_LOG, its stdout); no GPU "
+                         "needed")
     return ap.parse_args()
 
 
@@ -229,6 +237,75 @@ algorithmic_bytes_per_launch: {alg}
 """
     out = os.path.join(PROFILE_DIR, f"traffic_{est}_{wl}.txt")
     with open(out, "w") as fh:
+        fh.write(text)
+    print(text)
+
+
+def short_kernel_name(name: str) -> str:
+    """A kernel's demangled name without its return type, parameter list and
+    namespace, cut to 80 characters."""
+    n = name[5:] if name.startswith("void ") else name
+    if n.startswith("rlscan::"):
+        depth = 0
+        for i, ch in enumerate(n):
+            depth += (ch == "<") - (ch == ">")
+            if ch == "(" and depth == 0:
+                n = n[:i]
+                break
+    return n.replace("rlscan::", "")[:80]
+
+
+def trace_summary(run_log, stats_csv, trace_csv, out_md, command):
+    """Writes the kernel durations of a rocprofv3 --kernel-trace --stats run
+    of this script: every kernel's statistics over all its launches, and the
+    grouped kernel's average over the timed production steps.  The timed
+    steps are the run's first group launches (warmup, then steps), so their
+    dispatches are the first warmup + steps of that kernel in the trace; the
+    same kernel symbol also runs later comparisons (other layouts, one-byte
+    flags, a smaller rotation) that the all-launch average mixes in."""
+    import collections
+    import csv
+    bench = [json.loads(line) for line in open(run_log) if line.startswith('{"metric"')][-1]
+    rows = list(csv.DictReader(open(stats_csv)))
+    disp = collections.defaultdict(list)
+    order = []
+    with open(trace_csv) as fh:
+        for r in csv.DictReader(fh):
+            name = r["Kernel_Name"]
+            if "rlscan::group_kernel" in name:
+                start, end = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+                disp[name].append((start, end))
+                order.append((start, name))
+    first = min(order)[1]  # the kernel of the first grouped launch: the timed step's
+    launches = sorted(disp[first])
+    w, k = bench["warmup"], bench["steps"]
+    timed = [(e - s) / 1e3 for s, e in launches[w:w + k]]
+    timed_avg = sum(timed) / len(timed)
+    lines = [
+        "# Kernel durations of the default bench run", "",
+        "Command (run from the repository root on one MI355X):", "", "```", command, "```", "",
+        "Source: `kernel_stats.csv` of that run (all launches of each kernel in the run), and "
+        "its `kernel_trace.csv` for the timed production steps; made with "
+        "`python3 bench.py --trace-summary <stdout of the run> <kernel_stats.csv> "
+        "<kernel_trace.csv> <this file> <command>`.", "",
+        "## The timed production steps", "",
+        f"- kernel: `{short_kernel_name(first)}`, dispatches {w + 1}–{w + k} of "
+        f"{len(launches)} in the run (the first {w} are the warmup steps)",
+        f"- average duration over the {len(timed)} timed steps: {timed_avg:.2f} µs "
+        f"(min {min(timed):.2f}, max {max(timed):.2f})",
+        f"- the same run's bench line: `roofline.avg_launch_us` {bench['roofline']['avg_launch_us']}"
+        f" µs (HIP events around the timed steps on the launch stream: the kernels and the gaps "
+        f"between them), `ms_per_step` {bench['ms_per_step'] * 1000:.2f} µs",
+        f"- kernel sources: `{bench['kernel_source_hash']}`", "",
+        "## Every kernel of the run", "",
+        "| kernel | calls | avg µs | min µs | max µs | % of GPU time |",
+        "|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        lines.append(f"| `{short_kernel_name(r['Name'])}` | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    text = "\n".join(lines) + "\n"
+    with open(out_md, "w") as fh:
         fh.write(text)
     print(text)
 
@@ -865,6 +942,9 @@ def main():
 
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
+        return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
         return
 
     import torch
