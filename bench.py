@@ -767,10 +767,12 @@ def copy_ceiling(torch, sh, lib, nbytes, min_bytes=COLD_BYTES, reps=10):
     return us, 2 * half / (us * 1e-6) / 1e9
 
 
-def launch_floor_us(torch, grid, launches=64, reps=10):
+def launch_floor_us(torch, grid, threads, launches=64, reps=10):
+    """Mean device time per launch of an empty kernel of `grid` workgroups of
+    `threads` threads, back-to-back in one graph."""
     from linear_recurrence_scan_coefficient_amd import rlscan
     lib = rlscan.library()
-    calls = [("empty", lib.rlscan_launch_floor, (grid, None))] * launches
+    calls = [("empty", lib.rlscan_launch_floor, (grid, threads, None))] * launches
     g = capture_graph(torch, calls)
     return time_launches(torch, g, launches, reps)
 
@@ -1039,15 +1041,18 @@ def main():
     iso = time_eager_calls(torch, sets, 100)
     for e in ests:
         per_est[e]["isolated_call_us"] = spread(iso[e])
+        p = rlscan.rlscan_plan(e, w.N, w.T, w.A)
+        per_est[e]["launch_floor_us"] = round(launch_floor_us(torch, p["grid"], p["threads"]), 3)
     dom = max(ests, key=lambda e: per_est[e]["us_per_call"])
     d = per_est[dom]
     copy_us, copy_gbs = copy_ceiling(torch, sh, lib, set_bytes)
     dom_copy_us, dom_copy_gbs = copy_ceiling(torch, sh, lib, d["bytes"])
     plan = rlscan.rlscan_plan(dom, w.N, w.T, w.A)
-    floor = launch_floor_us(torch, plan["grid"])
-    # the grouped launch's grid: every call's tiles at the group's wave count
-    group_grid = sum(-(-w.N * w.T // (256 * 2)) for _ in ests)
-    group_floor = launch_floor_us(torch, group_grid)
+    floor = per_est[dom]["launch_floor_us"]
+    # the grouped launch's grid: every call's tiles at the group's two waves
+    group_waves_used = 2
+    group_grid = sum(-(-w.N * w.T // (256 * group_waves_used)) for _ in ests)
+    group_floor = launch_floor_us(torch, group_grid, 64 * group_waves_used)
 
     result = {
         "metric": METRIC, "value": value, "unit": "elements/s", "n_gpus": 1,
@@ -1087,9 +1092,12 @@ def main():
         "small_rotation": small_rotation,
         "group_waves": waves_sweep,
         "group_layouts": layouts,
-        "launch_floor_us": {"grid": plan["grid"], "us": round(floor, 3),
-                            "grouped_grid": group_grid, "grouped_us": round(group_floor, 3),
-                            "note": "an empty kernel of that many 256-thread workgroups"},
+        "launch_floor_us": {"kernel": dom, "grid": plan["grid"], "threads": plan["threads"],
+                            "us": round(floor, 3), "grouped_grid": group_grid,
+                            "grouped_threads": 64 * group_waves_used,
+                            "grouped_us": round(group_floor, 3),
+                            "note": "an empty kernel of the same grid and workgroup size; "
+                                    "per_estimator holds each call's own"},
         "kernel_source_hash": kernel_source_hash(),
     }
 

@@ -460,10 +460,12 @@ enum {
  * workgroups loop.  Returns RLSCAN_ERR_PARAM for other values. */
 int rlscan_set_launch_override(int mapping, int rounds, int waves, int64_t grid_cap, int flags);
 
-/* Diagnostics: enqueues an empty kernel of `grid` workgroups of 256 threads
- * on `stream` -- the launch-bound floor of a scan launch with that grid.
- * Returns RLSCAN_ERR_SHAPE unless 1 <= grid < 2^23. */
-int rlscan_launch_floor(int64_t grid, hipStream_t stream);
+/* Diagnostics: enqueues an empty kernel of `grid` workgroups of `threads`
+ * threads on `stream` -- the launch-bound floor of a scan launch with that
+ * grid and workgroup size (rlscan_plan gives both).  Returns
+ * RLSCAN_ERR_SHAPE unless 1 <= grid < 2^23 and threads is a multiple of 64
+ * from 64 to 1024. */
+int rlscan_launch_floor(int64_t grid, int32_t threads, hipStream_t stream);
 
 /* Diagnostics: enqueues a plain streaming copy of `bytes` bytes from `src`
  * to `dst` (device pointers, 16-byte aligned, not overlapping; bytes a

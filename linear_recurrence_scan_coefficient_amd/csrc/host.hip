@@ -157,10 +157,9 @@ Plan make_plan(int est, int64_t N, int64_t T, bool vec, bool carry) {
     return pl;
 }
 
-// An empty kernel: the launch floor that a scan launch of the same grid
-// cannot go below.
-constexpr int kFloorThreads = 256;
-__global__ __launch_bounds__(kFloorThreads) void empty_kernel() {}
+// An empty kernel: the launch floor that a scan launch of the same grid and
+// workgroup size cannot go below.
+__global__ __launch_bounds__(1024) void empty_kernel() {}
 
 // A plain streaming copy: the bandwidth a kernel that reads and writes the
 // same bytes, in the same 16-byte non-temporal accesses, can reach.  Each
@@ -250,10 +249,11 @@ int rlscan_plan(int estimator, int64_t N, int64_t T, int64_t A, rlscan_plan_info
     return RLSCAN_OK;
 }
 
-int rlscan_launch_floor(int64_t grid, hipStream_t stream) {
+int rlscan_launch_floor(int64_t grid, int32_t threads, hipStream_t stream) {
     if (grid < 1 || grid > kMaxGrid) return RLSCAN_ERR_SHAPE;
-    hipLaunchKernelGGL(empty_kernel, dim3(static_cast<unsigned>(grid)), dim3(kFloorThreads), 0,
-                       stream);
+    if (threads < kWave || threads > 1024 || threads % kWave != 0) return RLSCAN_ERR_SHAPE;
+    hipLaunchKernelGGL(empty_kernel, dim3(static_cast<unsigned>(grid)),
+                       dim3(static_cast<unsigned>(threads)), 0, stream);
     return hipGetLastError() == hipSuccess ? RLSCAN_OK : RLSCAN_ERR_HIP;
 }
 

@@ -142,7 +142,7 @@ def _declare(lib):
     lib.rlscan_set_launch_override.restype = ctypes.c_int
     lib.rlscan_lookback_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
     lib.rlscan_lookback_timeouts.restype = ctypes.c_int
-    lib.rlscan_launch_floor.argtypes = [_i64, _vp]
+    lib.rlscan_launch_floor.argtypes = [_i64, ctypes.c_int32, _vp]
     lib.rlscan_launch_floor.restype = ctypes.c_int
     lib.rlscan_stream_copy.argtypes = [_vp, _vp, _i64, _vp]
     lib.rlscan_stream_copy.restype = ctypes.c_int
@@ -545,8 +545,8 @@ def rlscan_lookback_timeouts() -> int:
     return n.value
 
 
-def rlscan_launch_floor(grid, stream=None):
-    _check(library().rlscan_launch_floor(int(grid), _stream(stream)))
+def rlscan_launch_floor(grid, threads=256, stream=None):
+    _check(library().rlscan_launch_floor(int(grid), int(threads), _stream(stream)))
 
 
 def rlscan_stream_copy(dst, src, nbytes=None, stream=None):

@@ -199,6 +199,16 @@ def test_stream_copy_argument_checks(lib):
     assert f(P[0], P[0] + 32, 64, None) == ALIAS
 
 
+def test_launch_floor_argument_checks(lib):
+    """Refused on the host before any launch: a grid outside [1, 2^23) or a
+    workgroup size that is not a multiple of 64 from 64 to 1024."""
+    f = lib.rlscan_launch_floor
+    assert f(0, 256, None) == SHAPE
+    assert f(1 << 23, 256, None) == SHAPE
+    for threads in (0, 32, 100, 1088, -64):
+        assert f(16, threads, None) == SHAPE, threads
+
+
 def test_carry_entry_points_argument_checks(lib):
     f = lib
     # GAE with carry: carry_out may not alias an input or the output
