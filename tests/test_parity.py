@@ -180,6 +180,32 @@ def test_retrace_out_of_range_actions_do_not_fault():
     assert got["targets"].shape == (4, 200)
 
 
+# Degenerate parameters of the method: gamma = 0 or lambda = 0 make every
+# step a chain cut (a = 0: no state crosses any step); gamma = lambda = 1
+# leaves the recurrence undamped (a = 1: plain episodic sums, the longest
+# chains and the largest magnitudes); V-trace with both clips at +inf (plain
+# importance weights) or at 1e-3 (traces all but cut).
+DEGENERATE = [
+    dict(gamma=0.0, lam=0.9), dict(gamma=0.97, lam=0.0), dict(gamma=1.0, lam=1.0),
+    dict(gamma=0.97, lam=1.0), dict(gamma=1.0, lam=0.5),
+    dict(gamma=0.97, lam=0.9, rho_bar=float("inf"), c_bar=float("inf")),
+    dict(gamma=0.97, lam=0.9, rho_bar=1e-3, c_bar=1e-3),
+]
+
+
+@pytest.mark.parametrize("estimator", [e for e in ESTIMATORS if e != "episodic_prefix_sum"])
+@pytest.mark.parametrize("params", DEGENERATE,
+                         ids=["-".join(f"{k}{v:g}" for k, v in p.items()) for p in DEGENERATE])
+@pytest.mark.parametrize("shape", [(64, 128), (2, 5000)], ids=["packed", "lookback"])
+def test_degenerate_parameters(estimator, params, shape):
+    if "rho_bar" in params and estimator != "vtrace":
+        pytest.skip("clip parameters are V-trace's")
+    w, inputs = case(estimator, *shape, seed=shape[1] + 17, **params)
+    mapping = rlscan.rlscan_plan(estimator, w.N, w.T, w.A)["mapping"]
+    assert mapping == (rlscan.MAP_PACKED if shape[1] == 128 else rlscan.MAP_LOOKBACK)
+    check(estimator, w, inputs, f"degenerate {params}")
+
+
 @pytest.mark.parametrize("estimator", ESTIMATORS)
 def test_empty_inputs(estimator):
     for N, T in ((0, 5), (5, 0), (0, 0)):
