@@ -397,3 +397,54 @@ def test_calls_from_several_host_threads():
             assert_parity({k: v.cpu().numpy() for k, v in out.items()},
                           oracle_outputs(est, inputs, w), f"thread {t} {est}")
     assert rlscan.rlscan_lookback_timeouts() == 0
+
+
+def random_case(seed):
+    """A seeded random call: estimator, shape (log-uniform, up to ~2e5
+    elements), flag rates, truncation mode, gamma and lambda (including the
+    exact ends 0 and 1), V-trace clips, Retrace's action count, and a launch
+    override (mapping, rounds, waves, grid cap, ticket order)."""
+    rng = np.random.default_rng(90_000 + seed)
+    est = ESTIMATORS[rng.integers(len(ESTIMATORS))]
+    N = int(np.exp(rng.uniform(0, np.log(400))))
+    T = int(np.exp(rng.uniform(0, np.log(20000))))
+    while N * T > 200_000:
+        T = max(1, T // 2)
+
+    def unit():
+        return float(rng.choice([0.0, 1.0, rng.uniform(0.5, 1.0), rng.uniform(0.0, 1.0)],
+                                p=[0.1, 0.1, 0.5, 0.3]))
+    opts = dict(gamma=unit(), lam=unit(), term_p=float(rng.choice([0.0, 1e-3, 0.02, 0.3])),
+                done_p=float(rng.choice([0.0, 1e-3, 0.02, 0.3])),
+                A=int(rng.choice([1, 3, 4, 6, 8])))
+    if est in REVERSE_WITH_TRUNC or est == "retrace":
+        opts["trunc_mode"] = str(rng.choice(["none", "independent", "exclusive"]))
+        opts["trunc_p"] = float(rng.choice([1e-3, 0.05]))
+        if est == "retrace" and opts["trunc_mode"] == "none":
+            opts["trunc_mode"] = "independent"
+    if est == "vtrace":
+        # traces stay clipped at c_bar <= 1: above 1 the recurrence expands
+        # (a = gamma*c > 1 where the ratio exceeds 1) and float32 rounding
+        # grows with the trace product along an episode, beyond the parity
+        # bar for any float32 evaluation (a sequential float32 loop misses it
+        # too); test_degenerate_parameters covers c_bar = +inf on short
+        # episodes
+        opts["rho_bar"] = float(rng.choice([1.0, 0.5, 2.0, np.inf]))
+        opts["c_bar"] = float(rng.choice([1.0, 0.9, 1e-3]))
+    rounds, waves = SHAPES_RW[rng.integers(len(SHAPES_RW))]
+    mapping = int(rng.choice([rlscan.MAP_AUTO, rlscan.MAP_LOOKBACK]))
+    grid_cap = int(rng.choice([0, 0, 0, 7, 64]))
+    flags = int(rng.choice([0, 0, rlscan.FLAG_TICKETS]))
+    if rng.random() < 0.3:  # the planner's own choice
+        mapping, rounds, waves, grid_cap, flags = rlscan.MAP_AUTO, 0, 0, 0, 0
+    return est, N, T, opts, (mapping, rounds, waves, grid_cap, flags)
+
+
+@pytest.mark.parametrize("seed", range(256))
+def test_random_cases(seed):
+    est, N, T, opts, override = random_case(seed)
+    w = workloads.custom(N, T, **opts)
+    inputs = workloads.inputs_for(est, w, seed)
+    rlscan.rlscan_set_launch_override(*override)
+    plan = rlscan.rlscan_plan(est, N, T, w.A)
+    check(est, w, inputs, f"random seed={seed} {opts} override={override} plan={plan}")
