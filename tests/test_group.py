@@ -225,3 +225,42 @@ def test_group_refusals_write_nothing():
     assert e.value.status == rlscan.RLSCAN_ERR_PARAM
     torch.cuda.synchronize()
     assert bool((out["advantages"] == 5.0).all())
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_groups(seed):
+    """Seeded random groups: 1-11 calls of random estimators and shapes whose
+    rows fit the group's tile (T a power of two up to 1024, or a single tile),
+    float or one-byte flags per call, either grid layout; every output is
+    checked against the oracle."""
+    rng = np.random.default_rng(70_000 + seed)
+    count = int(rng.integers(1, 12))
+    calls, outs, want = [], [], []
+    for i in range(count):
+        e = ESTIMATORS[rng.integers(len(ESTIMATORS))]
+        if rng.random() < 0.2:
+            N, T = int(rng.integers(1, 4)), int(rng.integers(1, 300))  # one tile
+            if N * T > 512:
+                N = 1
+        else:
+            T = int(2 ** rng.integers(0, 11))
+            N = int(rng.integers(1, max(2, 40_000 // T)))
+        kw = {"A": int(rng.choice([4, 6, 8]))} if e == "retrace" else {}
+        w, inputs = case(e, N, T, seed=seed * 100 + i, **kw)
+        d = device.upload(inputs)
+        if rng.random() < 0.5:
+            for k in FLAG_KEYS:
+                if d.get(k) is not None:
+                    d[k] = (d[k] != 0).to(torch.uint8)
+        out = device.alloc_outputs(e, N, T)
+        calls.append(group_call(e, d, out, w))
+        outs.append((e, N, T, out))
+        want.append(oracle_outputs(e, inputs, w))
+    layout = list(LAYOUTS)[rng.integers(len(LAYOUTS))]
+    rlscan.rlscan_set_launch_override(flags=LAYOUTS[layout])
+    print(f"[group] random seed={seed}: {count} calls, {layout}: "
+          f"{[(e, N, T) for e, N, T, _ in outs]}", flush=True)
+    rlscan.rlscan_group(calls)
+    torch.cuda.synchronize()
+    for (e, N, T, out), ref in zip(outs, want):
+        assert_parity(host(out), ref, f"random group seed={seed} {e} {N}x{T}")
