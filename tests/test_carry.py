@@ -325,3 +325,51 @@ def test_carry_with_misaligned_pointers(estimator):
     print(f"[carry] misaligned {estimator}", flush=True)
     assert_parity({k: v.cpu().numpy() for k, v in got.items()}, want,
                   f"carry misaligned {estimator}")
+
+
+# (rounds, waves) pairs that have carry kernels (four or eight waves)
+CARRY_RW = [(1, 4), (1, 8), (2, 4), (2, 8), (4, 4), (4, 8)]
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_chained_chunks(seed):
+    """Seeded random rollouts split at random points into 2-6 pieces, the
+    pieces chained through carry_in / carry_out under a random launch
+    override, against the oracle on the whole rows."""
+    rng = np.random.default_rng(50_000 + seed)
+    estimator = ESTIMATORS[rng.integers(len(ESTIMATORS))]
+    N = int(rng.integers(1, 40))
+    T = int(np.exp(rng.uniform(np.log(8), np.log(60_000 // N + 8))))
+    w, d, _ = case(estimator, N, T, seed=seed)
+    whole = oracle_call(estimator, d, w, {})
+    k = int(rng.integers(2, min(6, T) + 1))
+    cuts = [0] + sorted(rng.choice(np.arange(1, T), size=k - 1, replace=False).tolist()) + [T]
+    pieces = [(cuts[i], cuts[i + 1]) for i in range(k)]
+    rounds, waves = CARRY_RW[rng.integers(len(CARRY_RW))]
+    mapping = int(rng.choice([rlscan.MAP_AUTO, rlscan.MAP_LOOKBACK]))
+    if rng.random() < 0.3:
+        mapping, rounds, waves = rlscan.MAP_AUTO, 0, 0
+    rlscan.rlscan_set_launch_override(mapping, rounds, waves, 0, 0)
+    forward = estimator in ("eligibility_traces", "episodic_prefix_sum")
+    print(f"[carry] random seed={seed} {estimator} {N}x{T} pieces={pieces} "
+          f"override={(mapping, rounds, waves)}", flush=True)
+    outs, carry = {}, {}
+    for lo, hi in (pieces if forward else pieces[::-1]):
+        sub = _cols(d, lo, hi)
+        if not forward and hi < T:
+            sub["bootstrap_value"] = (np.ascontiguousarray(d["values"][:, hi])
+                                      if "values" in d else None)
+        if estimator == "retrace" and hi < T:
+            carry["next_actions"] = np.ascontiguousarray(d["actions"][:, hi])
+            carry["next_behaviour_probs"] = np.ascontiguousarray(d["behaviour_probs"][:, hi])
+        wsub = workloads.custom(N, hi - lo, gamma=w.gamma, lam=w.lam, rho_bar=w.rho_bar,
+                                c_bar=w.c_bar)
+        got = gpu_call(estimator, sub, wsub, carry)
+        for name, v in got.items():
+            if name != "carry_out":
+                outs.setdefault(name, {})[lo] = v
+        carry = {"carry_in": got["carry_out"]}
+    result = {name: np.concatenate([parts[lo] for lo, _ in pieces], axis=1)
+              for name, parts in outs.items()}
+    assert_parity(result, {name: v for name, v in whole.items() if name != "carry_out"},
+                  f"random chained seed={seed} {estimator} {N}x{T} {pieces}")
