@@ -437,14 +437,26 @@ def random_case(seed):
     flags = int(rng.choice([0, 0, rlscan.FLAG_TICKETS]))
     if rng.random() < 0.3:  # the planner's own choice
         mapping, rounds, waves, grid_cap, flags = rlscan.MAP_AUTO, 0, 0, 0, 0
-    return est, N, T, opts, (mapping, rounds, waves, grid_cap, flags)
+    byte_flags = bool(rng.random() < 0.5)  # uint8 flags: the *_u8 entry points
+    return est, N, T, opts, (mapping, rounds, waves, grid_cap, flags), byte_flags
 
 
 @pytest.mark.parametrize("seed", range(256))
 def test_random_cases(seed):
-    est, N, T, opts, override = random_case(seed)
+    est, N, T, opts, override, byte_flags = random_case(seed)
     w = workloads.custom(N, T, **opts)
     inputs = workloads.inputs_for(est, w, seed)
     rlscan.rlscan_set_launch_override(*override)
     plan = rlscan.rlscan_plan(est, N, T, w.A)
-    check(est, w, inputs, f"random seed={seed} {opts} override={override} plan={plan}")
+    label = f"random seed={seed} {opts} override={override} u8={byte_flags} plan={plan}"
+    print(f"[parity] {est} N={N} T={T} {label}", flush=True)
+    d = device.upload(inputs)
+    if byte_flags:
+        for k in ("terminated", "truncated", "dones"):
+            if d.get(k) is not None:
+                d[k] = (d[k] != 0).to(torch.uint8)
+    out = device.alloc_outputs(est, N, T)
+    device.call(est, d, out, w)
+    torch.cuda.synchronize()
+    assert_parity({k: v.cpu().numpy() for k, v in out.items()}, oracle_outputs(est, inputs, w),
+                  f"{est} {N}x{T} {label}")
