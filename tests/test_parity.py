@@ -315,6 +315,8 @@ def test_graph_capture_of_packed_calls():
         torch.cuda.synchronize()
 
 
+# the refused call enqueues nothing, so the captured graph is empty by design
+@pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")
 def test_lookback_launch_refuses_capture():
     w, inputs = case("gae", 5, 3001, seed=2)
     d = device.upload(inputs)
