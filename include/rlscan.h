@@ -71,6 +71,10 @@
  *             look-back launches have come from more than one stream of the
  *             device (a stream used for them must then stay alive while
  *             later calls are enqueued).  Packed launches are not ordered.
+ *             The scratch of a stream handle stays until
+ *             rlscan_release_scratch() and is reused by a later stream that
+ *             gets the same handle: destroy a stream only after its rlscan
+ *             work has completed.
  * Rounding    float32 results of a call that uses the look-back (see
  *             rlscan_plan) can differ in the last bits between two runs on
  *             the same inputs: a tile composes whichever of its
@@ -394,8 +398,9 @@ const char* rlscan_status_string(int status);
 /* Library version string (static storage). */
 const char* rlscan_version(void);
 
-/* Frees the look-back scratch of every (device, stream) pair.  The caller
- * must make sure no rlscan work is still running on any stream. */
+/* Frees the look-back scratch of every (device, stream) pair; a later call
+ * that needs scratch allocates it again.  The caller must make sure no
+ * rlscan work is still running on any stream. */
 int rlscan_release_scratch(void);
 
 /* ---- launch planning (host only; no GPU work) ---------------------------
@@ -481,7 +486,7 @@ int rlscan_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t st
  * as its entering state, so every float result of the tile is NaN (the
  * prefix sum takes INT64_MIN: the tile's results up to its first reset are
  * INT64_MIN plus their partial sums, in wrapping int64 arithmetic), and the
- * kernel finishes.  This call waits for every stream that has look-back
+ * kernel finishes.  This call waits for every device that has look-back
  * scratch, then stores the total count of such timeouts since the scratch
  * was allocated.  A correct build never reports one; the tests assert that
  * (and force the path with RLSCAN_FLAG_LOOKBACK_GIVE_UP). */

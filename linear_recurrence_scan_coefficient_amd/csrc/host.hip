@@ -56,6 +56,23 @@ Scratch* scratch_for(int device, hipStream_t stream) {
     }
 }
 
+// A grid-stride loop of plain vector stores.
+__global__ __launch_bounds__(256) void clear_kernel(uint64_t* p, int64_t words) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < words;
+         i += stride)
+        p[i] = 0;
+}
+
+hipError_t clear_words(uint64_t* p, int64_t words, hipStream_t stream) {
+    if (words <= 0) return hipSuccess;
+    int64_t grid = (words + 255) / 256;
+    if (grid > 1024) grid = 1024;
+    hipLaunchKernelGGL(clear_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, p,
+                       words);
+    return hipGetLastError();
+}
+
 int ensure_capacity(Scratch* sc, hipStream_t stream, int64_t tiles) {
     if (sc->capacity >= tiles && !sc->broken) return RLSCAN_OK;
     int64_t cap = 1024;
@@ -75,8 +92,9 @@ int ensure_capacity(Scratch* sc, hipStream_t stream, int64_t tiles) {
         return RLSCAN_ERR_ALLOC;
     }
     // ordered before the first kernel that uses the buffers (same stream)
-    if (hipMemsetAsync(st, 0, sizeof(TileStatus) * cap, stream) != hipSuccess ||
-        hipMemsetAsync(ctr, 0, 256, stream) != hipSuccess) {
+    if (clear_words(static_cast<uint64_t*>(st), static_cast<int64_t>(sizeof(TileStatus) / 8) * cap,
+                    stream) != hipSuccess ||
+        clear_words(static_cast<uint64_t*>(ctr), 256 / 8, stream) != hipSuccess) {
         (void)hipFree(st);
         (void)hipFree(ctr);
         return RLSCAN_ERR_HIP;
@@ -205,6 +223,9 @@ const char* rlscan_status_string(int status) {
 
 const char* rlscan_version(void) { return "rlscan 0.1.0 gfx950"; }
 
+// The Scratch objects themselves stay (a call on another thread may hold a
+// pointer to one): only their device buffers are freed, under each object's
+// own lock, and the next call that needs one allocates it afresh.
 int rlscan_release_scratch(void) {
     std::lock_guard<std::mutex> g(g_scratch_mutex);
     int prev = 0;
@@ -225,8 +246,8 @@ int rlscan_release_scratch(void) {
         sc->capacity = 0;
         sc->next_ticket = 0;
         sc->epoch = 0;
+        sc->broken = false;
     }
-    g_scratch.clear();
     if (have_prev) (void)hipSetDevice(prev);
     return rc;
 }
@@ -274,27 +295,34 @@ int rlscan_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t st
     return hipGetLastError() == hipSuccess ? RLSCAN_OK : RLSCAN_ERR_HIP;
 }
 
+// Waits for each device that holds look-back scratch (not for the streams
+// the scratch was keyed by: the caller may have destroyed them since).
 int rlscan_lookback_timeouts(uint64_t* count) {
     if (count == nullptr) return RLSCAN_ERR_NULL;
     *count = 0;
-    std::lock_guard<std::mutex> g(g_scratch_mutex);
-    int prev = 0;
-    const bool have_prev = hipGetDevice(&prev) == hipSuccess;
     int rc = RLSCAN_OK;
-    for (auto& kv : g_scratch) {
-        Scratch* sc = kv.second.get();
-        std::lock_guard<std::mutex> gs(sc->m);
-        if (sc->counter == nullptr) continue;
-        unsigned int n = 0;
-        if (hipSetDevice(kv.first.first) != hipSuccess ||
-            hipStreamSynchronize(reinterpret_cast<hipStream_t>(kv.first.second)) != hipSuccess ||
-            hipMemcpy(&n, sc->counter + 1, sizeof(n), hipMemcpyDeviceToHost) != hipSuccess) {
-            rc = RLSCAN_ERR_HIP;
-            continue;
+    {
+        std::lock_guard<std::mutex> g(g_scratch_mutex);
+        int prev = 0;
+        const bool have_prev = hipGetDevice(&prev) == hipSuccess;
+        int synced = -1;
+        for (auto& kv : g_scratch) {  // ordered by device
+            Scratch* sc = kv.second.get();
+            std::lock_guard<std::mutex> gs(sc->m);
+            if (sc->counter == nullptr) continue;
+            unsigned int n = 0;
+            const int dev = kv.first.first;
+            if (hipSetDevice(dev) != hipSuccess ||
+                (synced != dev && hipDeviceSynchronize() != hipSuccess) ||
+                hipMemcpy(&n, sc->counter + 1, sizeof(n), hipMemcpyDeviceToHost) != hipSuccess) {
+                rc = RLSCAN_ERR_HIP;
+                continue;
+            }
+            synced = dev;
+            *count += n;
         }
-        *count += n;
+        if (have_prev) (void)hipSetDevice(prev);
     }
-    if (have_prev) (void)hipSetDevice(prev);
     return rc;
 }
 

@@ -34,15 +34,21 @@ extern LaunchOverride g_override;
 struct Scratch {
     std::mutex m;
     TileStatus* status = nullptr;
-    unsigned long long* counter = nullptr;
+    unsigned long long* counter = nullptr;  // [0]: tickets; low half of [1]: timeouts
     int64_t capacity = 0;       // tiles
     uint64_t next_ticket = 0;   // counter value at the start of the next call
     uint64_t epoch = 0;         // tag of the last call (below 2^31, 0 = none)
     bool broken = false;        // a launch failed: counter position unknown
 };
 
-// Look-back scratch of (device, stream); created on first use.
+// Look-back scratch of (device, stream); created on first use and kept until
+// the process ends (rlscan_release_scratch frees its device buffers only, so
+// a pointer returned here stays valid).  nullptr if the host is out of memory.
 Scratch* scratch_for(int device, hipStream_t stream);
+
+// Enqueues a kernel that zeroes `words` 64-bit words at `p` (the status
+// words and counters are cleared this way, never by a memset node).
+hipError_t clear_words(uint64_t* p, int64_t words, hipStream_t stream);
 
 // Order of the look-back launches of one device across streams.  A look-back
 // workgroup waits on lower tiles of its own launch; one launch always makes
@@ -229,7 +235,9 @@ int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream,
     if (sc->epoch >= kLastTag) {
         // the call tags (at most kLastTag: their top bit marks a one-word
         // integer value) are about to repeat: clear the status words
-        if (hipMemsetAsync(sc->status, 0, sizeof(TileStatus) * sc->capacity, stream) != hipSuccess)
+        if (clear_words(reinterpret_cast<uint64_t*>(sc->status),
+                        static_cast<int64_t>(sizeof(TileStatus) / 8) * sc->capacity,
+                        stream) != hipSuccess)
             return RLSCAN_ERR_HIP;
         sc->epoch = 0;
     }
