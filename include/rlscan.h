@@ -107,7 +107,9 @@ typedef enum {
     RLSCAN_ERR_ALIAS = -4, /* an output pointer equals an input or other output */
     RLSCAN_ERR_HIP = -5,   /* a HIP runtime call or kernel launch failed        */
     RLSCAN_ERR_ALLOC = -6, /* the library could not allocate its scratch        */
-    RLSCAN_ERR_CAPTURE = -7 /* a look-back launch on a stream under graph capture */
+    RLSCAN_ERR_CAPTURE = -7, /* a look-back launch on a stream under graph capture */
+    RLSCAN_ERR_SCRATCH = -8  /* rlscan_gae_noalloc: more look-back tiles than its
+                                fixed array holds                                */
 } rlscan_status;
 
 /* GAE (README, Kernels table, compute_gae: a backward scan that adds each
@@ -338,6 +340,33 @@ int rlscan_episodic_prefix_sum_u8(const int32_t* x, const uint8_t* dones,
                                   const int64_t* carry_in, int64_t* out, int64_t* carry_out,
                                   int64_t N, int64_t T, hipStream_t stream);
 
+/* ---- GAE without allocation ------------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * rlscan_gae_noalloc is rlscan_gae_carry (same arguments, same results) but
+ * never allocates: it calls no hipMalloc, hipFree or allocating library
+ * routine and creates no event.  The look-back scratch it needs for rows
+ * that span several workgroups is one fixed library array of 2 MiB + 256 B
+ * per GPU (65536 tiles of 32 bytes plus two counters), held by every GPU
+ * the library runs on until the process ends.
+ *   Limit    A call whose plan (rlscan_plan) is RLSCAN_MAP_LOOKBACK with more
+ *            than 65536 tiles (beyond 2^28 elements at 4096-element tiles)
+ *            returns RLSCAN_ERR_SCRATCH, before any HIP call, with nothing
+ *            enqueued.  Packed calls use no scratch and have no such limit.
+ *   Sharing  Every call on one GPU uses that GPU's array, which keeps the
+ *            last call's contents (the status words are tagged per call, so
+ *            none needs clearing between calls).  Calls that overlap on one
+ *            GPU race on it: issue them on one stream, and do not let them
+ *            overlap with the library's other look-back launches on that GPU
+ *            (unlike those, they are not ordered across streams).
+ *   Graphs   As for rlscan_gae: a look-back call returns RLSCAN_ERR_CAPTURE on
+ *            a capturing stream; packed calls may be captured. */
+int rlscan_gae_noalloc(const float* rewards, const float* values, const float* bootstrap_value,
+                       const float* terminated, const float* truncated,
+                       const float* bootstrap_values, const float* carry_in, float* advantages,
+                       float* carry_out, int64_t N, int64_t T, float gamma, float lambda,
+                       hipStream_t stream);
+
 /* ---- several calls in one launch -------------------------------------------
  * A call of a few million elements (4096 x 128: 6-38 MB) is bound by its
  * launch and one memory round trip, not by bandwidth; a step of several such
@@ -400,7 +429,8 @@ const char* rlscan_version(void);
 
 /* Frees the look-back scratch of every (device, stream) pair; a later call
  * that needs scratch allocates it again.  The caller must make sure no
- * rlscan work is still running on any stream. */
+ * rlscan work is still running on any stream.  (The fixed array of
+ * rlscan_gae_noalloc is not affected.) */
 int rlscan_release_scratch(void);
 
 /* ---- launch planning (host only; no GPU work) ---------------------------
@@ -488,7 +518,7 @@ int rlscan_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t st
  * INT64_MIN plus their partial sums, in wrapping int64 arithmetic), and the
  * kernel finishes.  This call waits for every device that has look-back
  * scratch, then stores the total count of such timeouts since the scratch
- * was allocated.  A correct build never reports one; the tests assert that
+ * was allocated (rlscan_gae_noalloc's fixed arrays included).  A correct build never reports one; the tests assert that
  * (and force the path with RLSCAN_FLAG_LOOKBACK_GIVE_UP). */
 int rlscan_lookback_timeouts(uint64_t* count);
 

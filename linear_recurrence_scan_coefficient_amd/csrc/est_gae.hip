@@ -17,7 +17,7 @@ template <class F>
 int gae(const float* rewards, const float* values, const float* bootstrap_value,
         const F* terminated, const F* truncated, const float* bootstrap_values,
         const float* carry_in, float* advantages, float* carry_out, int64_t N, int64_t T,
-        float gamma, float lambda, hipStream_t stream) {
+        float gamma, float lambda, hipStream_t stream, const ScratchSource* src = nullptr) {
     int rc = check_shape(N, T);
     if (rc != RLSCAN_OK) return rc;
     if (!unit_interval(gamma) || !unit_interval(lambda)) return RLSCAN_ERR_PARAM;
@@ -38,10 +38,24 @@ int gae(const float* rewards, const float* values, const float* bootstrap_value,
                    return truncated
                               ? launch_kernel<Gae<true, F>>(p, g, lb, pl, vec, carry, stream)
                               : launch_kernel<Gae<false, F>>(p, g, lb, pl, vec, carry, stream);
-               });
+               },
+               src);
 }
 
 }  // namespace
+
+namespace rlscan {
+
+int gae_with_scratch(const float* rewards, const float* values, const float* bootstrap_value,
+                     const float* terminated, const float* truncated,
+                     const float* bootstrap_values, const float* carry_in, float* advantages,
+                     float* carry_out, int64_t N, int64_t T, float gamma, float lambda,
+                     hipStream_t stream, const ScratchSource* src) {
+    return gae(rewards, values, bootstrap_value, terminated, truncated, bootstrap_values,
+               carry_in, advantages, carry_out, N, T, gamma, lambda, stream, src);
+}
+
+}  // namespace rlscan
 
 extern "C" {
 

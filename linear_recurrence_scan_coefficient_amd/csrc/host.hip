@@ -74,6 +74,20 @@ hipError_t clear_words(uint64_t* p, int64_t words, hipStream_t stream) {
 }
 
 int ensure_capacity(Scratch* sc, hipStream_t stream, int64_t tiles) {
+    if (sc->fixed) {
+        if (tiles > sc->capacity) return RLSCAN_ERR_SCRATCH;
+        if (!sc->broken) return RLSCAN_OK;
+        // a failed launch left the ticket counter at an unknown value: start
+        // the array afresh (status words and counters)
+        const int64_t words = static_cast<int64_t>(sizeof(TileStatus) / 8) * sc->capacity;
+        if (clear_words(reinterpret_cast<uint64_t*>(sc->status), words, stream) != hipSuccess ||
+            clear_words(reinterpret_cast<uint64_t*>(sc->counter), 256 / 8, stream) != hipSuccess)
+            return RLSCAN_ERR_HIP;
+        sc->next_ticket = 0;
+        sc->epoch = 0;
+        sc->broken = false;
+        return RLSCAN_OK;
+    }
     if (sc->capacity >= tiles && !sc->broken) return RLSCAN_OK;
     int64_t cap = 1024;
     while (cap < tiles) cap *= 2;
@@ -217,6 +231,8 @@ const char* rlscan_status_string(int status) {
         case RLSCAN_ERR_ALLOC: return "could not allocate the look-back scratch";
         case RLSCAN_ERR_CAPTURE:
             return "this shape needs the look-back mapping, which cannot be captured into a graph";
+        case RLSCAN_ERR_SCRATCH:
+            return "the call needs more look-back tiles than the fixed scratch array holds";
         default: return "unknown rlscan status";
     }
 }
@@ -323,7 +339,10 @@ int rlscan_lookback_timeouts(uint64_t* count) {
         }
         if (have_prev) (void)hipSetDevice(prev);
     }
-    return rc;
+    uint64_t fixed = 0;
+    const int rs = static_scratch_timeouts(&fixed);
+    *count += fixed;
+    return rc != RLSCAN_OK ? rc : rs;
 }
 
 int rlscan_set_launch_override(int mapping, int rounds, int waves, int64_t grid_cap, int flags) {

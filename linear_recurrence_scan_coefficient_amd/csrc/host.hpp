@@ -39,6 +39,7 @@ struct Scratch {
     uint64_t next_ticket = 0;   // counter value at the start of the next call
     uint64_t epoch = 0;         // tag of the last call (below 2^31, 0 = none)
     bool broken = false;        // a launch failed: counter position unknown
+    bool fixed = false;         // a static device array: never allocated, grown or freed
 };
 
 // Look-back scratch of (device, stream); created on first use and kept until
@@ -46,9 +47,30 @@ struct Scratch {
 // a pointer returned here stays valid).  nullptr if the host is out of memory.
 Scratch* scratch_for(int device, hipStream_t stream);
 
+// Where a call takes its look-back scratch from.  The default (nullptr)
+// allocates per (device, stream) with scratch_for; a source with `get` set
+// hands out a fixed array of at most `max_tiles` tiles per device, and the
+// call then allocates nothing: it is refused with RLSCAN_ERR_SCRATCH, before
+// any HIP call, when its plan needs more tiles.
+struct ScratchSource {
+    Scratch* (*get)(int device);
+    int64_t max_tiles;
+};
+
 // Enqueues a kernel that zeroes `words` 64-bit words at `p` (the status
 // words and counters are cleared this way, never by a memset node).
 hipError_t clear_words(uint64_t* p, int64_t words, hipStream_t stream);
+
+// rlscan_gae_carry with its look-back scratch taken from `src`.
+int gae_with_scratch(const float* rewards, const float* values, const float* bootstrap_value,
+                     const float* terminated, const float* truncated,
+                     const float* bootstrap_values, const float* carry_in, float* advantages,
+                     float* carry_out, int64_t N, int64_t T, float gamma, float lambda,
+                     hipStream_t stream, const ScratchSource* src);
+
+// Timeouts recorded in the fixed scratch arrays of the no-allocation entry
+// point (waits for each device that has one).
+int static_scratch_timeouts(uint64_t* count);
 
 // Order of the look-back launches of one device across streams.  A look-back
 // workgroup waits on lower tiles of its own launch; one launch always makes
@@ -190,12 +212,17 @@ hipError_t launch_kernel_r1(const typename E::Params& p, const Geometry& geo,
 }
 
 // Plans, takes the look-back scratch if needed, and launches through `fn`.
+// `src`: where the scratch comes from (nullptr: allocated per stream).
 template <class Fn>
-int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream, Fn&& fn) {
+int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream, Fn&& fn,
+        const ScratchSource* src = nullptr) {
     const Plan pl = make_plan(est, N, T, vec, carry);
     if (pl.rounds != 1 && pl.rounds != 2 && pl.rounds != 4) return RLSCAN_ERR_PARAM;
     if (pl.waves != 1 && pl.waves != 2 && pl.waves != 4 && pl.waves != 8)
         return RLSCAN_ERR_PARAM;
+    if (src != nullptr && t_group == nullptr && pl.mapping == RLSCAN_MAP_LOOKBACK &&
+        pl.tiles > src->max_tiles)
+        return RLSCAN_ERR_SCRATCH;
     Geometry geo;
     geo.N = N;
     geo.T = T;
@@ -220,8 +247,8 @@ int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream,
     if (capture != hipStreamCaptureStatusNone) return RLSCAN_ERR_CAPTURE;
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return RLSCAN_ERR_HIP;
-    Scratch* sc = scratch_for(device, stream);
-    if (sc == nullptr) return RLSCAN_ERR_ALLOC;
+    Scratch* sc = src != nullptr ? src->get(device) : scratch_for(device, stream);
+    if (sc == nullptr) return src != nullptr ? RLSCAN_ERR_HIP : RLSCAN_ERR_ALLOC;
     std::lock_guard<std::mutex> g(sc->m);
     const int rc = ensure_capacity(sc, stream, pl.tiles);
     if (rc != RLSCAN_OK) return rc;
@@ -245,6 +272,19 @@ int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream,
     const bool give_up = (g_override.flags.load() & RLSCAN_FLAG_LOOKBACK_GIVE_UP) != 0;
     lb.read_tag = give_up ? kNeverTag : lb.tag;
     lb.max_polls = give_up ? 8u : kMaxPolls;
+    if (sc->fixed) {
+        // the fixed array's calls are not ordered across streams (ordering
+        // them would need an event, i.e. an allocation): the caller keeps
+        // them from overlapping with other look-back launches of the device
+        if (fn(geo, lb, pl) != hipSuccess) {
+            sc->broken = true;
+            return RLSCAN_ERR_HIP;
+        }
+        if (tickets)
+            sc->next_ticket += static_cast<uint64_t>(pl.tiles) +
+                               (pl.grid >= pl.tiles ? 0u : static_cast<uint64_t>(pl.grid));
+        return RLSCAN_OK;
+    }
     LaunchOrder* order = launch_order(device);
     if (order == nullptr) return RLSCAN_ERR_HIP;
     std::lock_guard<std::mutex> go(order->m);

@@ -30,6 +30,7 @@ RLSCAN_ERR_ALIAS = -4
 RLSCAN_ERR_HIP = -5
 RLSCAN_ERR_ALLOC = -6
 RLSCAN_ERR_CAPTURE = -7
+RLSCAN_ERR_SCRATCH = -8
 
 MAP_AUTO, MAP_PACKED, MAP_LOOKBACK = 0, 1, 2
 FLAG_TICKETS = 1
@@ -53,7 +54,7 @@ EXPORTED = (
     "rlscan_vtrace_ex", "rlscan_episodic_prefix_sum_f32",
     "rlscan_gae_u8", "rlscan_lambda_returns_u8", "rlscan_discounted_returns_u8",
     "rlscan_vtrace_u8", "rlscan_retrace_u8", "rlscan_eligibility_traces_u8",
-    "rlscan_episodic_prefix_sum_u8", "rlscan_group",
+    "rlscan_episodic_prefix_sum_u8", "rlscan_group", "rlscan_gae_noalloc",
 )
 
 
@@ -128,6 +129,8 @@ def _declare(lib):
         getattr(lib, name).restype = ctypes.c_int
         if name != "rlscan_release_scratch":
             getattr(lib, name + "_carry").restype = ctypes.c_int
+    lib.rlscan_gae_noalloc.argtypes = lib.rlscan_gae_carry.argtypes
+    lib.rlscan_gae_noalloc.restype = ctypes.c_int
     lib.rlscan_group.argtypes = [ctypes.POINTER(Call), ctypes.c_int32, _vp]
     lib.rlscan_group.restype = ctypes.c_int
     lib.rlscan_release_scratch.argtypes = []
@@ -258,6 +261,24 @@ def rlscan_gae(rewards, values, bootstrap_value, terminated, truncated, bootstra
         _check(lib.rlscan_gae_carry(*ins, ci, out, co, N, T, gamma, lam, _stream(stream)))
     else:
         _check(lib.rlscan_gae(*ins, out, N, T, gamma, lam, _stream(stream)))
+    return advantages
+
+
+def rlscan_gae_noalloc(rewards, values, bootstrap_value, terminated, truncated,
+                       bootstrap_values, advantages, gamma, lam, stream=None, carry_in=None,
+                       carry_out=None):
+    """rlscan_gae_carry without any allocation (float32 flags): the look-back
+    scratch is the library's fixed per-GPU array."""
+    N, T = _nt(rewards, "rewards")
+    _, ci, co = _carry(carry_in, carry_out, N)
+    _check(library().rlscan_gae_noalloc(
+        _ptr(rewards, shape=(N, T), name="rewards"), _ptr(values, shape=(N, T), name="values"),
+        _ptr(bootstrap_value, shape=(N,), name="bootstrap_value"),
+        _ptr(terminated, shape=(N, T), name="terminated"),
+        _ptr(truncated, shape=(N, T), name="truncated"),
+        _ptr(bootstrap_values, shape=(N, T), name="bootstrap_values"), ci,
+        _ptr(advantages, shape=(N, T), name="advantages"), co, N, T, gamma, lam,
+        _stream(stream)))
     return advantages
 
 

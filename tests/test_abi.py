@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_version_and_status_strings(lib):
     from linear_recurrence_scan_coefficient_amd import rlscan
     assert "gfx950" in rlscan.version()
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         s = rlscan.status_string(code)
         assert s and s != "unknown rlscan status"
     assert rlscan.status_string(-99) == "unknown rlscan status"
@@ -237,6 +237,31 @@ def test_carry_entry_points_argument_checks(lib):
     assert f.rlscan_discounted_returns_carry(*P[:8], 4, 8, 1.5, None) == PARAM
     assert f.rlscan_vtrace_carry(*P[:11], 4, 8, 0.9, 0.0, 1.0, None) == PARAM
     assert f.rlscan_lambda_returns_carry(*P[:9], -1, 8, 0.9, 0.9, None) == SHAPE
+
+
+def test_noalloc_argument_checks(lib):
+    """rlscan_gae_noalloc checks its arguments as rlscan_gae_carry does, and
+    refuses a look-back plan beyond its fixed array before any HIP call."""
+    f = lib.rlscan_gae_noalloc
+    SCRATCH = -8
+    bad = list(P[:9])
+    bad[8] = bad[7]
+    assert f(*bad, 4, 8, 0.9, 0.9, None) == ALIAS
+    assert f(*P[:9], 4, 8, 1.5, 0.9, None) == PARAM
+    assert f(*P[:9], -1, 8, 0.9, 0.9, None) == SHAPE
+    assert f(*[None] * 9, 0, 8, 0.9, 0.9, None) == OK
+    p = list(P[:9])
+    p[0] = None
+    assert f(*p, 4, 8, 0.9, 0.9, None) == NULL
+    # 2 rows of 2^28 + 4096 steps: 4096-element tiles, 131074 > 65536 of them
+    plan = lib.rlscan_plan
+    from linear_recurrence_scan_coefficient_amd import rlscan
+    info = rlscan.PlanInfo()
+    N, T = 2, (1 << 28) + 4096
+    assert plan(0, N, T, 1, ctypes.byref(info)) == OK
+    assert info.mapping == 2 and info.tiles > 65536
+    assert f(*P[:9], N, T, 0.9, 0.9, None) == SCRATCH
+    assert rlscan.status_string(SCRATCH) != "unknown rlscan status"
 
 
 def test_variant_entry_points_argument_checks(lib):
