@@ -18,7 +18,10 @@ float-flag kernels and bool / uint8 flags the one-byte-flag kernels, both
 without any conversion; flags of other dtypes, or a mix of float32 and
 one-byte flags in one call, are first turned into bool (one elementwise
 pass).  Non-contiguous inputs are made contiguous, and the call runs on the
-current stream (or `stream`).  gamma and lambda_ default to the values of
+current stream, or on `stream`: such a call first waits for the current
+stream (where its temporaries and outputs are made) and marks every tensor
+it uses as used by `stream`; the caller waits for `stream` before reading
+the outputs elsewhere.  gamma and lambda_ default to the values of
 the README's usage example.
 
 Streaming one rollout through several calls (the README's chunked fallback
@@ -80,23 +83,56 @@ class grouped:
         calls, self.calls = self.calls, []
         if not calls:
             return
-        try:
-            rlscan.rlscan_group([g for g, _ in calls], self.stream)
-        except rlscan.RlscanError as e:
-            if e.status != rlscan.RLSCAN_ERR_PARAM:
-                raise
-            for _, alone in calls:  # not groupable: the same calls one by one
-                alone(self.stream)
+        tensors = [t for g, _ in calls for part in g.keep for t in part]
+
+        def run(stream):
+            try:
+                rlscan.rlscan_group([g for g, _ in calls], stream)
+            except rlscan.RlscanError as e:
+                if e.status != rlscan.RLSCAN_ERR_PARAM:
+                    raise
+                for _, alone in calls:  # not groupable: the same calls one by one
+                    alone(stream)
+
+        _on_stream(run, self.stream, tensors)
 
 
-def _submit(estimator, ins, outs, params, alone, stream, carry):
+def _as_stream(stream):
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
+def _on_stream(fn, stream, tensors):
+    """Runs `fn(stream)`.  Inputs, temporaries and outputs were made on the
+    current stream; a launch on another stream first waits for the current
+    one, and every tensor is marked as used by that stream so that the
+    caching allocator does not hand its memory out again before that
+    stream's work is done."""
+    if stream is None:
+        fn(None)
+        return
+    s = _as_stream(stream)
+    cur = torch.cuda.current_stream(s.device)
+    if s == cur:
+        fn(s)
+        return
+    s.wait_stream(cur)
+    fn(s)
+    for t in tensors:
+        if isinstance(t, torch.Tensor) and t.is_cuda:
+            t.record_stream(s)
+
+
+def _submit(estimator, ins, outs, params, alone, stream, carry, extra=()):
     """Runs `alone(stream)` now, or defers the call to the innermost active
-    `grouped` block (plain calls on the default stream only)."""
+    `grouped` block (plain calls on the current stream only).  `extra`: the
+    call's other tensors (carries, Retrace's next-chunk arrays)."""
     stack = getattr(_local, "groups", None)
     if stack and not carry and stream is None:
         stack[-1].calls.append((rlscan.GroupCall(estimator, ins, outs, **params), alone))
     else:
-        alone(stream)
+        _on_stream(alone, stream, (*ins, *outs, *extra))
 
 
 def _device_tensor(t, name, dtype=torch.float32, flag=False):
@@ -166,7 +202,7 @@ def compute_gae(rewards, values, terminateds, gamma=0.99, lambda_=0.95, *,
     _submit("gae", ins, (out,), dict(gamma=float(gamma), lam=float(lambda_)),
             lambda st: rlscan.rlscan_gae(*ins, out, float(gamma), float(lambda_), st,
                                          carry_in=ci, carry_out=co),
-            stream, ci is not None or co is not None)
+            stream, ci is not None or co is not None, (ci, co))
     return (out, co) if return_carry else out
 
 
@@ -185,7 +221,7 @@ def compute_lambda_returns(rewards, values, terminateds, gamma=0.99, lambda_=0.9
     _submit("lambda_returns", ins, (out,), dict(gamma=float(gamma), lam=float(lambda_)),
             lambda st: rlscan.rlscan_lambda_returns(*ins, out, float(gamma), float(lambda_), st,
                                                     carry_in=ci, carry_out=co),
-            stream, ci is not None or co is not None)
+            stream, ci is not None or co is not None, (ci, co))
     return (out, co) if return_carry else out
 
 
@@ -205,7 +241,7 @@ def compute_discounted_returns(rewards, terminateds, gamma=0.99, *, bootstrap_va
     _submit("discounted_returns", ins, (out,), dict(gamma=float(gamma)),
             lambda st: rlscan.rlscan_discounted_returns(*ins, out, float(gamma), st, carry_in=ci,
                                                         carry_out=co),
-            stream, ci is not None or co is not None)
+            stream, ci is not None or co is not None, (ci, co))
     return (out, co) if return_carry else out
 
 
@@ -236,7 +272,7 @@ def compute_vtrace(rewards, values, log_rhos, terminateds, gamma=0.99, rho_bar=1
             lambda st: rlscan.rlscan_vtrace(*ins, vs, pg, float(gamma), float(rho_bar),
                                             float(c_bar), st, carry_in=ci, carry_out=co,
                                             lam=lam, rho_bar_pg=pgc),
-            stream, ci is not None or co is not None)
+            stream, ci is not None or co is not None, (ci, co))
     return (vs, pg, co) if return_carry else (vs, pg)
 
 
@@ -273,7 +309,7 @@ def compute_retrace(rewards, next_q_values_all, next_target_probs, actions, beha
             lambda st: rlscan.rlscan_retrace(*ins, out, float(gamma), float(lambda_), st,
                                              carry_in=ci, carry_out=co, next_actions=nat,
                                              next_behaviour_probs=nbp),
-            stream, ci is not None or co is not None)
+            stream, ci is not None or co is not None, (ci, co, nat, nbp))
     return (out, co) if return_carry else out
 
 
@@ -290,7 +326,7 @@ def compute_eligibility_traces(x, dones, gamma=0.99, lambda_=0.95, *, carry_in=N
     _submit("eligibility_traces", ins, (out,), dict(gamma=float(gamma), lam=float(lambda_)),
             lambda st: rlscan.rlscan_eligibility_traces(*ins, out, float(gamma), float(lambda_),
                                                         st, carry_in=ci, carry_out=co),
-            stream, ci is not None or co is not None)
+            stream, ci is not None or co is not None, (ci, co))
     return (out, co) if return_carry else out
 
 
@@ -306,9 +342,10 @@ def compute_episodic_prefix_sum(x, dones, *, carry_in=None, return_carry=False, 
         out = torch.empty((N, T), dtype=torch.float32, device=xx.device)
         co = _carry_out(return_carry, N, xx.device)
         d = _device_tensor(dones, "dones", torch.float32, flag=True)
-        rlscan.rlscan_episodic_prefix_sum_f32(xx, d, out, stream,
-                                              carry_in=_device_tensor(carry_in, "carry_in"),
-                                              carry_out=co)
+        ci = _device_tensor(carry_in, "carry_in")
+        _on_stream(lambda st: rlscan.rlscan_episodic_prefix_sum_f32(xx, d, out, st, carry_in=ci,
+                                                                     carry_out=co),
+                   stream, (xx, d, out, ci, co))
         return (out, co) if return_carry else out
     xx = x
     if isinstance(xx, torch.Tensor) and xx.dtype in (torch.bool, torch.uint8, torch.int8,
@@ -323,5 +360,5 @@ def compute_episodic_prefix_sum(x, dones, *, carry_in=None, return_carry=False, 
     _submit("episodic_prefix_sum", ins, (out,), {},
             lambda st: rlscan.rlscan_episodic_prefix_sum(*ins, out, st, carry_in=ci,
                                                          carry_out=co),
-            stream, ci is not None or co is not None)
+            stream, ci is not None or co is not None, (ci, co))
     return (out, co) if return_carry else out

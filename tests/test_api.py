@@ -264,3 +264,35 @@ def test_grouped_block_with_calls_that_cannot_share_a_launch():
     assert_parity(host(got), oracle_outputs("gae", inputs, w), "grouped long gae")
     assert_parity(host(got2), oracle_outputs("vtrace", inputs2, w2), "grouped vtrace")
     assert c.shape == (3,)
+
+
+def test_calls_on_a_stream_that_is_not_current():
+    """A call given stream=S runs on S only after the current stream's work.
+    The current stream is kept busy (a sleep kernel) while the call converts
+    int64 actions and a mix of float and bool flags on it, so a launch on S
+    that did not wait would read the converted buffers before they are
+    written.  Also a grouped block on S."""
+    w, inputs = case("retrace", seed=41)
+    d = {k: dev(v) for k, v in inputs.items()}
+    actions64 = d["actions"].to(torch.int64)
+    trunc_bool = d["truncated"].to(torch.bool)  # float terminated + bool truncated: a mix
+    wg, inputs_g = case("gae", N=64, T=128, seed=42)
+    dg = {k: dev(v) for k, v in inputs_g.items()}
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(20_000_000)
+    out = api.compute_retrace(d["rewards"], d["next_q_values_all"], d["next_target_probs"],
+                              actions64, d["behaviour_probs"], d["terminated"], trunc_bool,
+                              gamma=w.gamma, lambda_=w.lam, stream=s)
+    torch.cuda._sleep(20_000_000)
+    with api.grouped(stream=s):
+        adv = api.compute_gae(dg["rewards"], dg["values"], dg["terminated"], wg.gamma, wg.lam,
+                              bootstrap_value=dg["bootstrap_value"],
+                              truncateds=dg["truncated"].to(torch.uint8),
+                              bootstrap_values=dg["bootstrap_values"])
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert_parity({"targets": out.cpu().numpy()}, oracle_outputs("retrace", inputs, w),
+                  "retrace on another stream")
+    assert_parity({"advantages": adv.cpu().numpy()}, oracle_outputs("gae", inputs_g, wg),
+                  "grouped gae on another stream")
