@@ -82,10 +82,14 @@
  *             depends on timing.  Packed calls and the int64 prefix sum are
  *             deterministic.
  * Graphs      Calls whose tiles hold whole rows (the packed mapping, see
- *             rlscan_plan) launch one kernel and nothing else, and may be
- *             captured into a HIP graph.  A call that needs the look-back
- *             returns RLSCAN_ERR_CAPTURE on a capturing stream, since its
- *             replay would reuse a stale ticket base.
+ *             rlscan_plan: all rows in one tile, or whole rows filling at
+ *             least 3/4 of a tile -- every T that divides the tile, and
+ *             most other rollout lengths up to it, e.g. 20, 96, 100, 200
+ *             or 1000) launch one kernel and nothing else, and may be
+ *             captured into a HIP graph.  A call that needs the
+ *             look-back (rlscan_plan: RLSCAN_MAP_LOOKBACK) returns
+ *             RLSCAN_ERR_CAPTURE on a capturing stream, since its replay
+ *             would reuse a stale ticket base.
  * Thread      All entry points may be called concurrently from several host
  * safety      threads.
  */
@@ -158,7 +162,22 @@ int rlscan_discounted_returns(const float* rewards, const float* bootstrap_value
  * in:  rewards, values, log_rhos (log pi - log mu of the taken action),
  *      terminated [N,T]; bootstrap_value, truncated, bootstrap_values as
  *      rlscan_gae.
- * out: vs [N,T] (targets), pg_advantages [N,T]. */
+ * out: vs [N,T] (targets), pg_advantages [N,T].
+ * Precision: with gamma*c_bar > 1 (for rlscan_vtrace_ex: gamma*lambda*c_bar
+ * > 1; c_bar = +inf included) a trace coefficient gamma*c_t can exceed 1,
+ * and the recurrence expands: the products of the coefficients along an
+ * episode grow, and so does the weight of every rounding made before them
+ * (over episodes of about 100 steps, one float32 rounding of a coefficient
+ * can move a result by 1e-4 of its size).  Such calls run a float64 form of
+ * the kernels -- ratio (exp), clips, TD error, scan state and epilogue in
+ * float64, only vs and pg rounded to float32 -- and stay within
+ * 1e-4*(1 + |exact|) of the exact result for the given float32 inputs,
+ * like every other call.  That form runs at most two rounds per tile (see
+ * rlscan_plan, which reports the float32 form's plan) and takes two
+ * look-back status entries per tile.  A chunked rollout (the *_carry calls)
+ * hands vs across chunk edges in float32: expanding traces amplify that
+ * rounding too, so chunked and whole-rollout results then agree only up to
+ * it. */
 int rlscan_vtrace(const float* rewards, const float* values, const float* bootstrap_value,
                   const float* log_rhos, const float* terminated, const float* truncated,
                   const float* bootstrap_values, float* vs, float* pg_advantages,
@@ -388,10 +407,10 @@ int rlscan_gae_noalloc(const float* rewards, const float* values, const float* b
  * c_bar and rho_bar_pg.  With RLSCAN_CALL_BYTE_FLAGS the flags are uint8
  * (as for the *_u8 entry points).
  *
- * Every call must be one that runs as a single packed launch: rows that fit
- * whole in the group's tile (N*T <= 1024, or T dividing 256, 512 or 1024),
- * every pointer 16-byte aligned (one-byte flags: 4-byte aligned), and, for
- * Retrace, A in {4, 6, 8}.  The calls must be independent: no call may
+ * Every call must be one that runs as a single packed launch (rlscan_plan:
+ * RLSCAN_MAP_PACKED) whose rows fit whole in the group's tile of 512 or
+ * 1024 elements (T <= 1024, or N*T <= 1024), every pointer 16-byte aligned
+ * (one-byte flags: 4-byte aligned), and, for Retrace, A in {4, 6, 8}.  The calls must be independent: no call may
  * write a buffer another call of the group reads or writes.
  *
  * Each call's tiles run as one contiguous stretch of the launch's workgroups,
@@ -437,10 +456,19 @@ int rlscan_release_scratch(void);
  * The library maps the flattened N*T elements onto tiles of
  * 256*waves*rounds consecutive elements, one workgroup of 64*waves threads
  * (waves = 1, 2, 4 or 8 wave64s; 1 and 2 with one round only) per tile.
- * mapping RLSCAN_MAP_PACKED: every tile holds whole rows (the tile size is a
- * multiple of T, or there is a single tile), no inter-workgroup traffic.
+ * mapping RLSCAN_MAP_PACKED: every tile holds whole rows, no inter-workgroup
+ * traffic.  A tile holds floor(tile_elems / T) rows (fewer, if needed, to
+ * make their element count a multiple of 4: for odd T a multiple of 4
+ * rows), or all rows when they fit; where those rows do not fill the tile,
+ * its remaining lanes idle.  Chosen when the rows fill at least 3/4 of the
+ * tile (T = 100: 5 rows of a 512-element tile), so rollout lengths that
+ * divide no tile size pack too.  One round of work per lane (at most 2^20
+ * elements) allows tiles of up to 2048 elements (Retrace: 1024), so for
+ * example T = 702 (two rows, 69 % of 2048) or odd T = 171 (eight rows,
+ * 67 %) take the look-back.
  * mapping RLSCAN_MAP_LOOKBACK: rows span tiles; carries travel between
- * workgroups through the single-pass decoupled look-back. */
+ * workgroups through the single-pass decoupled look-back (rows longer than
+ * the largest tile, or rows that would fill less than 3/4 of one). */
 enum { RLSCAN_MAP_AUTO = 0, RLSCAN_MAP_PACKED = 1, RLSCAN_MAP_LOOKBACK = 2 };
 
 enum {
@@ -452,16 +480,22 @@ enum {
 typedef struct {
     int32_t mapping;     /* RLSCAN_MAP_PACKED or RLSCAN_MAP_LOOKBACK         */
     int32_t rounds;      /* 4-element chunks per lane per tile (1, 2 or 4)   */
-    int64_t tile_elems;  /* elements per tile = 4 * rounds * threads         */
-    int64_t tiles;       /* number of tiles = ceil(N*T / tile_elems)         */
+    int64_t tile_elems;  /* capacity of a tile = 4 * rounds * threads        */
+    int64_t tiles;       /* number of tiles: ceil(N*T / tile_span) for the
+                            look-back, ceil(N / rows per tile) for packed    */
     int64_t grid;        /* workgroups launched                              */
     int32_t threads;     /* threads per workgroup: 64, 128, 256 or 512       */
-    int32_t reserved;
+    int32_t tile_span;   /* elements of memory per tile: tile_elems, or for
+                            the packed mapping the whole rows a tile holds
+                            (a multiple of 4, at least 3/4 of tile_elems
+                            unless the mapping is forced)                     */
 } rlscan_plan_info;
 
 /* Fills *info with the launch the library would make for this estimator and
- * shape under the current override.  Returns RLSCAN_ERR_SHAPE for invalid
- * sizes, RLSCAN_ERR_PARAM for an unknown estimator id. */
+ * shape under the current override (V-trace: its float32 form; a call whose
+ * gamma*lambda*c_bar exceeds 1 runs at most two rounds per tile).  Returns
+ * RLSCAN_ERR_SHAPE for invalid sizes, RLSCAN_ERR_PARAM for an unknown
+ * estimator id. */
 int rlscan_plan(int estimator, int64_t N, int64_t T, int64_t A, rlscan_plan_info* info);
 
 enum {

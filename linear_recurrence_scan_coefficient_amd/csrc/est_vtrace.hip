@@ -40,8 +40,18 @@ int vtrace(const float* rewards, const float* values, const float* bootstrap_val
                                   pg_advantages}) &&
                      flags_aligned(terminated) && flags_aligned(truncated);
     const bool carry = carry_in != nullptr || carry_out != nullptr;
-    return run(RLSCAN_EST_VTRACE, N, T, vec, carry, stream,
+    // Trace coefficients gamma*c_t can exceed 1 only if gamma*lambda*c_bar
+    // does (c_bar = +inf with gamma*lambda = 0 gives NaN here: no growth).
+    // Such calls run the float64 form: the trace products then grow along an
+    // episode, and a float32 rounding anywhere on the way would grow with
+    // them.
+    const bool wide =
+        static_cast<double>(gamma) * static_cast<double>(lambda) * static_cast<double>(c_bar) > 1.0;
+    return run(wide ? kEstVtraceWide : RLSCAN_EST_VTRACE, N, T, vec, carry, stream,
                [&](const Geometry& g, const LookbackArgs& lb, const Plan& pl) {
+                   if (wide)
+                       return launch_vtrace_wide<F>(p, g, lb, pl, vec, carry, truncated != nullptr,
+                                                    stream);
                    return truncated
                               ? launch_kernel<Vtrace<true, F>>(p, g, lb, pl, vec, carry, stream)
                               : launch_kernel<Vtrace<false, F>>(p, g, lb, pl, vec, carry, stream);

@@ -53,14 +53,19 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "scan_core.hpp"
 
 namespace rlscan {
 
 struct Geometry {
     int64_t N, T, NT;       // rows, row length, N*T
-    int64_t num_tiles;      // tiles of tile_elems consecutive elements
+    int64_t num_tiles;      // tiles of tile_span consecutive elements
     int64_t grid;           // workgroups launched
+    int64_t tile_span;      // elements of memory per tile: the tile's capacity, or
+                            // (packed mapping) the whole rows it holds, a multiple
+                            // of 4 that can fall short of the capacity
     double inv_T;           // 1.0 / T, for the row/time split of an index
 };
 
@@ -250,6 +255,15 @@ __device__ __forceinline__ void fold_carry(StepF& e, float carry) {
     e.b = fmaf(e.a, carry, e.b);
     e.a = 0.0f;
 }
+__device__ __forceinline__ void fold_carry(StepW& e, double carry) {
+    e.b = fma(e.a, carry, e.b);
+    e.a = 0.0;
+}
+
+__device__ __forceinline__ float fma_of(float a, float b, float c) { return fmaf(a, b, c); }
+__device__ __forceinline__ double fma_of(double a, double b, double c) { return fma(a, b, c); }
+__device__ __forceinline__ float fmin_of(float a, float b) { return fminf(a, b); }
+__device__ __forceinline__ double fmin_of(double a, double b) { return fmin(a, b); }
 
 // ------------------------------------------------------------------ GAE
 // README, Kernels table, compute_gae row (backward scan of TD errors with
@@ -455,6 +469,9 @@ struct Discounted {
 // and the epilogue forms vs_t = V_t + u_t and
 //   pg_t = rho'_t*td_t + (cut ? 0 : gamma*rho'_t*u_{t+1})
 // which equals rho'_t*(r_t + gamma*(cut ? Vhat_{t+1} : vs_{t+1}) - V_t).
+// kWide: the float64 form (StepW) for calls whose trace coefficients can
+// exceed 1 (gamma*lambda*c_bar > 1): the ratio, rho, c, the TD error, the
+// scan and the epilogue are float64, and only vs and pg are rounded.
 template <class F>
 struct VtraceParams {
     const float *rewards, *values, *bootstrap_value, *log_rhos;
@@ -464,10 +481,10 @@ struct VtraceParams {
     float gamma, lambda, rho_bar, c_bar, rho_bar_pg;
 };
 
-template <bool kTrunc, class F = float>
+template <bool kTrunc, class F = float, bool kWide = false>
 struct Vtrace {
-    using S = StepF;
-    using V = float;
+    using S = typename std::conditional<kWide, StepW, StepF>::type;
+    using V = typename std::conditional<kWide, double, float>::type;
     static constexpr bool kReverse = true;
     using Params = VtraceParams<F>;
     struct Chunk {
@@ -478,8 +495,8 @@ struct Vtrace {
     };
     struct Epi {
         float v[4];
-        float pg_base[4];    // rho'_t * td_t
-        float gamma_rho[4];  // gamma * rho'_t, 0 at a cut
+        V pg_base[4];    // rho'_t * td_t
+        V gamma_rho[4];  // gamma * rho'_t, 0 at a cut
     };
     static constexpr int kStageFloats = 0;
     static constexpr int kOutStageFloats = 0;
@@ -505,35 +522,42 @@ struct Vtrace {
             const float v_next = j < kChunk - 1 ? c.v[j + 1] : c.v_halo;
             const float vh = successor_value(c.ep, j, row_end, j < q.valid,
                                              p.bootstrap_value, n, q.n0, v_next, continues, cut);
-            const float ratio = expf(c.lr[j]);
-            const float rho = fminf(p.rho_bar, ratio);
-            const float cc = p.lambda * fminf(p.c_bar, ratio);
-            const float rho_pg = fminf(p.rho_bar_pg, ratio);
-            const float td = fmaf(p.gamma, vh, c.ep.r[j]) - c.v[j];
+            V ratio;
+            if constexpr (kWide)
+                ratio = exp(static_cast<double>(c.lr[j]));
+            else
+                ratio = expf(c.lr[j]);
+            const V gamma = p.gamma;
+            const V rho = fmin_of(static_cast<V>(p.rho_bar), ratio);
+            const V cc = static_cast<V>(p.lambda) * fmin_of(static_cast<V>(p.c_bar), ratio);
+            const V rho_pg = fmin_of(static_cast<V>(p.rho_bar_pg), ratio);
+            const V td = fma_of(gamma, static_cast<V>(vh), static_cast<V>(c.ep.r[j])) -
+                         static_cast<V>(c.v[j]);
             epi.v[j] = c.v[j];
             epi.pg_base[j] = rho_pg * td;
-            epi.gamma_rho[j] = cut ? 0.0f : p.gamma * rho_pg;
-            e[j].a = cut ? 0.0f : p.gamma * cc;
+            epi.gamma_rho[j] = cut ? V(0) : gamma * rho_pg;
+            e[j].a = cut ? V(0) : gamma * cc;
             e[j].b = rho * td;
             if (row_end && continues && !cut && j < q.valid) {
                 // u at t = T is vs_T - V_T; the state before this element is
                 // not in the scan, so pg takes it here
-                const float u_T = row_carry(c.ep, p.carry_in, n, q.n0) - vh;
+                const V u_T = static_cast<V>(row_carry(c.ep, p.carry_in, n, q.n0)) -
+                              static_cast<V>(vh);
                 fold_carry(e[j], u_T);
-                epi.pg_base[j] = fmaf(epi.gamma_rho[j], u_T, epi.pg_base[j]);
-                epi.gamma_rho[j] = 0.0f;
+                epi.pg_base[j] = fma_of(epi.gamma_rho[j], u_T, epi.pg_base[j]);
+                epi.gamma_rho[j] = V(0);
             }
             next_position(n, t, geo.T);
         }
     }
     // carry_out of V-trace is vs, like its carry_in
     __device__ __forceinline__ static V edge_value(const Epi& c, const V x[4], int j) {
-        return c.v[j] + x[j];
+        return static_cast<V>(c.v[j]) + x[j];
     }
     // pg_t reads u_{t+1} unless t is a cut, also where c_t = 0 makes a_t = 0
     // (lambda = 0, or lambda * c underflowing)
     __device__ __forceinline__ static bool reads_before(const Epi& c, int j) {
-        return c.gamma_rho[j] != 0.0f;
+        return c.gamma_rho[j] != V(0);
     }
     template <bool VEC, bool FULL>
     __device__ __forceinline__ static void store(const Params& p, const ChunkPos& q, const Epi& c,
@@ -541,8 +565,8 @@ struct Vtrace {
         float vs[4], pg[4];
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
-            vs[j] = c.v[j] + x[j];
-            pg[j] = fmaf(c.gamma_rho[j], before[j], c.pg_base[j]);
+            vs[j] = static_cast<float>(static_cast<V>(c.v[j]) + x[j]);
+            pg[j] = static_cast<float>(fma_of(c.gamma_rho[j], before[j], c.pg_base[j]));
         }
         store4<VEC, FULL>(p.vs, q, vs);
         store4<VEC, FULL>(p.pg, q, pg);

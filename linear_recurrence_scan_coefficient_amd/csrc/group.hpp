@@ -25,8 +25,8 @@
 // either order.  Runs of 4 to 256 consecutive tiles per turn were no faster.
 //
 // Calls join a group when their own plan is packed, every pointer takes the
-// vector path, no carry is given, and their tile at the group's wave count
-// still holds whole rows.  Estimator instantiations that can be grouped are
+// vector path, no carry is given, and a tile at the group's wave count still
+// holds at least one whole row (packed_layout).  Estimator instantiations that can be grouped are
 // listed in GroupKinds; the kernel dispatches on the call's index in it.
 #pragma once
 
@@ -59,7 +59,9 @@ using GroupKinds =
              Vtrace<false, uint8_t>, Vtrace<true, uint8_t>, Retrace<4, float, false>,
              Retrace<6, float, false>, Retrace<8, float, false>, Retrace<4, uint8_t, false>,
              Retrace<6, uint8_t, false>, Retrace<8, uint8_t, false>, Eligibility<float>,
-             Eligibility<uint8_t>, PrefixSum<float>, PrefixSum<uint8_t>>;
+             Eligibility<uint8_t>, PrefixSum<float>, PrefixSum<uint8_t>,
+             Vtrace<false, float, true>, Vtrace<true, float, true>, Vtrace<false, uint8_t, true>,
+             Vtrace<true, uint8_t, true>>;
 
 // The form an estimator call takes inside a group (same Params layout).
 template <class E>
@@ -72,12 +74,15 @@ struct GroupForm<Retrace<kA, F, true>> {
 };
 
 // Kinds that hold many values per lane in registers (Retrace with 8 actions:
-// 64 action values per lane) run in a second build of the kernel, so that
-// groups without them keep the register count, and occupancy, of the rest.
+// 64 action values per lane; V-trace's float64 form) run in a second build
+// of the kernel, so that groups without them keep the register count, and
+// occupancy, of the rest.
 template <class E>
 struct GroupWide : std::false_type {};
 template <class F>
 struct GroupWide<Retrace<8, F, false>> : std::true_type {};
+template <bool kTrunc, class F>
+struct GroupWide<Vtrace<kTrunc, F, true>> : std::true_type {};
 
 template <class E, class L>
 struct KindOf;
@@ -244,16 +249,18 @@ struct GroupCollector {
         if constexpr (kind < 0) {
             reject = true;
         } else {
+            int64_t span = 0, tiles = 0;
             if (!vec || carry || mapping != RLSCAN_MAP_PACKED ||
-                !(geo.NT <= tile || tile % geo.T == 0)) {
+                !packed_layout(geo.N, geo.T, tile, span, tiles)) {
                 reject = true;
                 return;
             }
             GroupEntry e{};
             e.kind = kind;
             e.geo = geo;
-            e.geo.num_tiles = (geo.NT + tile - 1) / tile;
-            e.geo.grid = e.geo.num_tiles;
+            e.geo.num_tiles = tiles;
+            e.geo.grid = tiles;
+            e.geo.tile_span = span;
             std::memcpy(e.params, &p, sizeof(p));
             const size_t need = group_lds_bytes<G>(waves);
             lds = need > lds ? need : lds;

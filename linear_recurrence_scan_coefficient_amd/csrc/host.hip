@@ -129,7 +129,7 @@ int ensure_capacity(Scratch* sc, hipStream_t stream, int64_t tiles) {
 int auto_rounds(int est, int64_t NT) {
     if (est == RLSCAN_EST_RETRACE) return 1;
     if (NT <= (int64_t(1) << 20)) return 1;
-    if (NT < (int64_t(1) << 22)) return 2;
+    if (NT < (int64_t(1) << 22) || est == kEstVtraceWide) return 2;
     return 4;
 }
 
@@ -151,13 +151,29 @@ int auto_rounds(int est, int64_t NT) {
 //  - Two rounds: eight waves.  Measured against four: 32 x 65536 (look-back)
 //    10-18 % faster; 4096 x 512 and 16384 x 128 (packed) up to 12 % for GAE
 //    and V-trace, the same within 4 % for the others.
-int auto_waves(int est, int rounds, int64_t T) {
+//    Where T divides no such tile, the smallest tile whose whole rows fill
+//    at least 7/8 of it (100-step rows: 500 of 512 elements), else the
+//    best-filled one if its rows fill at least 3/4.
+int auto_waves(int est, int rounds, int64_t N, int64_t T) {
     if (rounds == 4) return 4;
     if (rounds == 1) {
-        const int first = (est == RLSCAN_EST_GAE || est == RLSCAN_EST_VTRACE) ? 2 : 1;
-        for (int w = first; w <= 8; w *= 2)
+        const int first =
+            (est == RLSCAN_EST_GAE || est == RLSCAN_EST_VTRACE || est == kEstVtraceWide) ? 2 : 1;
+        const int last = est == RLSCAN_EST_RETRACE ? 4 : 8;
+        for (int w = first; w <= last; w *= 2)
             if ((int64_t(kWave) * w * kChunk) % T == 0) return w;
-        return est == RLSCAN_EST_RETRACE ? 4 : 8;
+        int best = 0;
+        int64_t best_fill = 0;  // in 1/1024 of the tile
+        for (int w = first; w <= last; w *= 2) {
+            const int64_t cap = int64_t(kWave) * w * kChunk;
+            int64_t span = 0, tiles = 0;
+            if (!packed_layout(N, T, cap, span, tiles)) continue;
+            const int64_t fill = span * 1024 / cap;
+            if (fill >= 896) return w;
+            if (fill > best_fill) best = w, best_fill = fill;
+        }
+        if (best_fill >= 768) return best;
+        return last;
     }
     return 8;  // two rounds
 }
@@ -168,8 +184,9 @@ Plan make_plan(int est, int64_t N, int64_t T, bool vec, bool carry) {
     const int ro = g_override.rounds.load();
     pl.rounds = ro > 0 ? ro : auto_rounds(est, NT);
     if (!vec || est == RLSCAN_EST_RETRACE) pl.rounds = 1;
+    if (est == kEstVtraceWide && pl.rounds > 2) pl.rounds = 2;
     const int wo = g_override.waves.load();
-    pl.waves = wo > 0 ? wo : auto_waves(est, pl.rounds, T);
+    pl.waves = wo > 0 ? wo : auto_waves(est, pl.rounds, N, T);
     // kernels exist for 1 and 2 waves with one round only, for 8 waves not
     // for Retrace, for the unaligned path with 4 waves only and for the
     // carry path with 4 or 8
@@ -177,10 +194,17 @@ Plan make_plan(int est, int64_t N, int64_t T, bool vec, bool carry) {
     if (pl.waves == 8 && est == RLSCAN_EST_RETRACE) pl.waves = 4;
     if (!vec || (carry && pl.waves != 8)) pl.waves = 4;
     pl.tile_elems = int64_t(kWave) * pl.waves * kChunk * pl.rounds;
-    pl.tiles = (NT + pl.tile_elems - 1) / pl.tile_elems;
-    const bool packed_ok = pl.tiles <= 1 || pl.tile_elems % T == 0;
+    // Packed when every tile can hold whole rows and (unless forced) they
+    // fill at least 3/4 of it: the lanes past the rows idle, but no tile
+    // waits on another.
+    int64_t span = 0, tiles = 0;
+    const bool can_pack = packed_layout(N, T, pl.tile_elems, span, tiles);
+    const bool filled = can_pack && (tiles == 1 || 4 * span >= 3 * pl.tile_elems);
     const int mo = g_override.mapping.load();
-    pl.mapping = (packed_ok && mo != RLSCAN_MAP_LOOKBACK) ? RLSCAN_MAP_PACKED : RLSCAN_MAP_LOOKBACK;
+    const bool packed = mo == RLSCAN_MAP_PACKED ? can_pack : (mo == RLSCAN_MAP_AUTO && filled);
+    pl.mapping = packed ? RLSCAN_MAP_PACKED : RLSCAN_MAP_LOOKBACK;
+    pl.tile_span = packed ? span : pl.tile_elems;
+    pl.tiles = packed ? tiles : (NT + pl.tile_elems - 1) / pl.tile_elems;
     const int64_t cap = g_override.grid_cap.load();
     int64_t grid = pl.tiles;
     if (cap > 0 && grid > cap) grid = cap;
@@ -281,6 +305,7 @@ int rlscan_plan(int estimator, int64_t N, int64_t T, int64_t A, rlscan_plan_info
     info->mapping = pl.mapping;
     info->rounds = pl.rounds;
     info->tile_elems = pl.tile_elems;
+    info->tile_span = pl.tile_span;
     info->tiles = pl.tiles;
     info->grid = pl.grid;
     return RLSCAN_OK;

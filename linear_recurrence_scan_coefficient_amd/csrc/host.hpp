@@ -93,15 +93,29 @@ LaunchOrder* launch_order(int device);
 // Called with sc->m held.  Makes room for `tiles` status entries.
 int ensure_capacity(Scratch* sc, hipStream_t stream, int64_t tiles);
 
+// Planning id of V-trace's float64 form (not a public estimator id): at most
+// two rounds per tile (four spill its float64 registers), two status
+// entries per look-back tile.
+constexpr int kEstVtraceWide = RLSCAN_EST_PREFIX_SUM + 1;
+
 struct Plan {
     int mapping;
     int rounds;
     int waves;
-    int64_t tile_elems, tiles, grid;
+    int64_t tile_elems;  // capacity of a tile
+    int64_t tile_span;   // elements of memory per tile (packed: its whole rows)
+    int64_t tiles, grid;
 };
 
 // `vec`: every pointer is 16-byte aligned; `carry`: a carry argument is given.
 Plan make_plan(int est, int64_t N, int64_t T, bool vec, bool carry = false);
+
+// V-trace launches in the float64 form (est_vtrace_wide.hip: a translation
+// unit of their own, compiled in parallel with the float32 form's).
+template <class F>
+hipError_t launch_vtrace_wide(const VtraceParams<F>& p, const Geometry& geo,
+                              const LookbackArgs& lb, const Plan& pl, bool vec, bool carry,
+                              bool trunc, hipStream_t stream);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -157,13 +171,24 @@ hipError_t launch_r(const typename E::Params& p, const Geometry& geo, const Look
     return hipGetLastError();
 }
 
+// Most rounds per tile an estimator's kernels are built for (the planner
+// never asks for more).
+template <class E> struct MaxRounds { static constexpr int value = 4; };
+template <bool kTrunc, class F> struct MaxRounds<Vtrace<kTrunc, F, true>> {
+    static constexpr int value = 2;
+};
+
 template <class E, int W, bool CARRY>
 hipError_t launch_w(const typename E::Params& p, const Geometry& geo, const LookbackArgs& lb,
                     const Plan& pl, hipStream_t stream) {
     switch (pl.rounds) {
         case 1: return launch_r<E, 1, W, true, CARRY>(p, geo, lb, pl, stream);
         case 2: return launch_r<E, 2, W, true, CARRY>(p, geo, lb, pl, stream);
-        default: return launch_r<E, 4, W, true, CARRY>(p, geo, lb, pl, stream);
+        default:
+            if constexpr (MaxRounds<E>::value >= 4)
+                return launch_r<E, 4, W, true, CARRY>(p, geo, lb, pl, stream);
+            else
+                return hipErrorInvalidValue;
     }
 }
 
@@ -217,11 +242,13 @@ template <class Fn>
 int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream, Fn&& fn,
         const ScratchSource* src = nullptr) {
     const Plan pl = make_plan(est, N, T, vec, carry);
+    // status entries per tile: two for float64 steps (StatusEntries)
+    const int entries = est == kEstVtraceWide ? StatusEntries<StepW>::value : 1;
     if (pl.rounds != 1 && pl.rounds != 2 && pl.rounds != 4) return RLSCAN_ERR_PARAM;
     if (pl.waves != 1 && pl.waves != 2 && pl.waves != 4 && pl.waves != 8)
         return RLSCAN_ERR_PARAM;
     if (src != nullptr && t_group == nullptr && pl.mapping == RLSCAN_MAP_LOOKBACK &&
-        pl.tiles > src->max_tiles)
+        pl.tiles > src->max_tiles / entries)
         return RLSCAN_ERR_SCRATCH;
     Geometry geo;
     geo.N = N;
@@ -229,6 +256,7 @@ int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream,
     geo.NT = N * T;
     geo.num_tiles = pl.tiles;
     geo.grid = pl.grid;
+    geo.tile_span = pl.tile_span;
     geo.inv_T = 1.0 / static_cast<double>(T);
     LookbackArgs lb{};
     if (t_group != nullptr) {  // collecting for a grouped launch: no side effects
@@ -250,7 +278,7 @@ int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream,
     Scratch* sc = src != nullptr ? src->get(device) : scratch_for(device, stream);
     if (sc == nullptr) return src != nullptr ? RLSCAN_ERR_HIP : RLSCAN_ERR_ALLOC;
     std::lock_guard<std::mutex> g(sc->m);
-    const int rc = ensure_capacity(sc, stream, pl.tiles);
+    const int rc = ensure_capacity(sc, stream, pl.tiles * entries);
     if (rc != RLSCAN_OK) return rc;
     // tile = blockIdx needs every tile to have its own workgroup
     const bool tickets = pl.grid < pl.tiles || (g_override.flags.load() & RLSCAN_FLAG_TICKETS);

@@ -47,6 +47,17 @@ struct TileStatus {
     uint64_t w[4];  // float: agg a, agg b, incl x, -; int: agg b lo/hi, incl x lo/hi
 };
 
+// Status entries per tile: one, or two for float64 steps, whose aggregate
+// (a, b) and inclusive value take six 32-bit payloads: entry 0 holds a lo/hi
+// and b lo/hi, entry 1 the inclusive value lo/hi.
+template <class A> struct StatusEntries { static constexpr int value = 1; };
+template <> struct StatusEntries<StepW> { static constexpr int value = 2; };
+
+template <class A>
+__device__ __forceinline__ TileStatus* status_of(TileStatus* base, int64_t tile) {
+    return base + StatusEntries<A>::value * tile;
+}
+
 struct LookbackArgs {
     TileStatus* status;       // >= number of tiles entries
     unsigned long long* ticket_counter;
@@ -79,6 +90,7 @@ constexpr uint32_t kMaxPolls = 1u << 22;
 constexpr int kNarrow = 4;
 
 __device__ __forceinline__ float poisoned(float) { return __builtin_nanf(""); }
+__device__ __forceinline__ double poisoned(double) { return __builtin_nan(""); }
 __device__ __forceinline__ int64_t poisoned(int64_t) { return INT64_MIN; }
 
 __device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t payload) {
@@ -137,6 +149,25 @@ __device__ __forceinline__ void publish_inclusive(TileStatus* st, int64_t x, uin
     publish_int(&st->w[2], x, tag);
 }
 
+// Float64 values: each 32-bit half is a word of its own, validated by its
+// own tag (each is written once per call, so two current halves are the
+// value).
+__device__ __forceinline__ void publish_f64(uint64_t* w, double v, uint32_t tag) {
+    const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+    store_word(w, tagged(tag, static_cast<uint32_t>(u)));
+    store_word(w + 1, tagged(tag, static_cast<uint32_t>(u >> 32)));
+}
+__device__ __forceinline__ double f64_value(uint64_t lo, uint64_t hi) {
+    return __longlong_as_double(static_cast<long long>(long_value(lo, hi)));
+}
+__device__ __forceinline__ void publish_aggregate(TileStatus* st, StepW s, uint32_t tag) {
+    publish_f64(&st[0].w[0], s.a, tag);
+    publish_f64(&st[0].w[2], s.b, tag);
+}
+__device__ __forceinline__ void publish_inclusive(TileStatus* st, double x, uint32_t tag) {
+    publish_f64(&st[1].w[0], x, tag);
+}
+
 // ---------------------------------------------------------------- read
 // Returns 0 (not ready), 1 (aggregate) or 2 (inclusive state, given as the
 // step (0, x)), and the step in `s`.
@@ -179,6 +210,24 @@ __device__ __forceinline__ int read_status(TileStatus* st, uint32_t tag, StepI& 
     return 0;
 }
 
+__device__ __forceinline__ int read_status(TileStatus* st, uint32_t tag, StepW& s) {
+    const uint64_t xl = load_word(&st[1].w[0]);
+    const uint64_t xh = load_word(&st[1].w[1]);
+    if (has_tag(xl, tag) && has_tag(xh, tag)) {
+        s = {0.0, f64_value(xl, xh)};
+        return 2;
+    }
+    const uint64_t al = load_word(&st[0].w[0]);
+    const uint64_t ah = load_word(&st[0].w[1]);
+    const uint64_t bl = load_word(&st[0].w[2]);
+    const uint64_t bh = load_word(&st[0].w[3]);
+    if (has_tag(al, tag) && has_tag(ah, tag) && has_tag(bl, tag) && has_tag(bh, tag)) {
+        s = {f64_value(al, ah), f64_value(bl, bh)};
+        return 1;
+    }
+    return 0;
+}
+
 __device__ __forceinline__ uint64_t take_ticket(const LookbackArgs& lb) {
     const unsigned long long t = __hip_atomic_fetch_add(lb.ticket_counter, 1ull, __ATOMIC_RELAXED,
                                                         __HIP_MEMORY_SCOPE_AGENT);
@@ -209,7 +258,7 @@ __device__ V look_back(const LookbackArgs& lb, uint64_t tile, int lane) {
         for (uint32_t polls = 0;; ++polls) {
             const bool in_window = kWave - 1 - lane < width;
             int kind = q < 0 ? 3 : 0;
-            if (q >= 0 && in_window) kind = read_status(lb.status + q, lb.read_tag, s);
+            if (q >= 0 && in_window) kind = read_status(status_of<A>(lb.status, q), lb.read_tag, s);
             const bool terminal = kind == 2 || (kind == 1 && cuts_chain(s));
             const uint64_t term_mask = __ballot(terminal);
             const uint64_t ready_mask = __ballot(kind != 0);

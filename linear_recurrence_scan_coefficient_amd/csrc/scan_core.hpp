@@ -46,17 +46,30 @@ struct StepI {
     int64_t b;
 };
 
+// Float64 step, for recurrences whose coefficients can exceed 1 (V-trace
+// with gamma*lambda*c_bar > 1).  There the trace products grow along an
+// episode, and so does the weight of every earlier rounding: a relative
+// error of 1e-8 in one coefficient (one float32 rounding of exp or of a
+// TD error) can move a result by 1e-4 of its size.  Coefficients, state and
+// epilogue are then all float64, and only the outputs are rounded.
+struct StepW {
+    double a, b;
+};
+
 // Type that holds compositions of a given element step type.
 template <class S> struct AggOf;
 template <> struct AggOf<StepF> { using type = StepD; };
 template <> struct AggOf<StepI> { using type = StepI; };
+template <> struct AggOf<StepW> { using type = StepW; };
 
 __device__ __forceinline__ StepD identity_step(StepD) { return {1.0, 0.0f}; }
 __device__ __forceinline__ StepI identity_step(StepI) { return {1u, 0}; }
 __device__ __forceinline__ StepF identity_step(StepF) { return {1.0f, 0.0f}; }
+__device__ __forceinline__ StepW identity_step(StepW) { return {1.0, 0.0}; }
 
 __device__ __forceinline__ StepD promote(StepF s) { return {static_cast<double>(s.a), s.b}; }
 __device__ __forceinline__ StepI promote(StepI s) { return s; }
+__device__ __forceinline__ StepW promote(StepW s) { return s; }
 
 // later o earlier
 __device__ __forceinline__ StepD compose(StepD later, StepD earlier) {
@@ -65,16 +78,21 @@ __device__ __forceinline__ StepD compose(StepD later, StepD earlier) {
 __device__ __forceinline__ StepI compose(StepI later, StepI earlier) {
     return {later.a & earlier.a, later.a ? later.b + earlier.b : later.b};
 }
+__device__ __forceinline__ StepW compose(StepW later, StepW earlier) {
+    return {later.a * earlier.a, fma(later.a, earlier.b, later.b)};
+}
 
 __device__ __forceinline__ float apply(StepF s, float x) { return fmaf(s.a, x, s.b); }
 __device__ __forceinline__ float apply(StepD s, float x) {
     return fmaf(static_cast<float>(s.a), x, s.b);
 }
 __device__ __forceinline__ int64_t apply(StepI s, int64_t x) { return s.a ? x + s.b : s.b; }
+__device__ __forceinline__ double apply(StepW s, double x) { return fma(s.a, x, s.b); }
 
 __device__ __forceinline__ bool cuts_chain(StepF s) { return s.a == 0.0f; }
 __device__ __forceinline__ bool cuts_chain(StepD s) { return s.a == 0.0; }
 __device__ __forceinline__ bool cuts_chain(StepI s) { return s.a == 0u; }
+__device__ __forceinline__ bool cuts_chain(StepW s) { return s.a == 0.0; }
 
 // ---------------------------------------------------------------- DPP moves
 // DPP control words of the GFX9 family (gfx950 included):
@@ -108,6 +126,26 @@ __device__ __forceinline__ StepD dpp_step(StepD s) {
     StepD r;
     r.a = __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
     r.b = __uint_as_float(dpp_move<kCtrl, kRowMask>(0u, __float_as_uint(s.b)));
+    return r;
+}
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint64_t dpp_move64(uint64_t old, uint64_t src) {
+    const uint32_t lo = dpp_move<kCtrl, kRowMask>(static_cast<uint32_t>(old),
+                                                  static_cast<uint32_t>(src));
+    const uint32_t hi = dpp_move<kCtrl, kRowMask>(static_cast<uint32_t>(old >> 32),
+                                                  static_cast<uint32_t>(src >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ StepW dpp_step(StepW s) {
+    const uint64_t one = static_cast<uint64_t>(__double_as_longlong(1.0));
+    StepW r;
+    r.a = __longlong_as_double(static_cast<long long>(
+        dpp_move64<kCtrl, kRowMask>(one, static_cast<uint64_t>(__double_as_longlong(s.a)))));
+    r.b = __longlong_as_double(static_cast<long long>(
+        dpp_move64<kCtrl, kRowMask>(0u, static_cast<uint64_t>(__double_as_longlong(s.b)))));
     return r;
 }
 
@@ -152,6 +190,9 @@ __device__ __forceinline__ double read_lane(double v, int lane) {
 __device__ __forceinline__ StepD read_lane(StepD s, int lane) {
     return {read_lane(s.a, lane), read_lane(s.b, lane)};
 }
+__device__ __forceinline__ StepW read_lane(StepW s, int lane) {
+    return {read_lane(s.a, lane), read_lane(s.b, lane)};
+}
 __device__ __forceinline__ StepI read_lane(StepI s, int lane) {
     return {static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(s.a), lane)),
             read_lane(s.b, lane)};
@@ -172,6 +213,12 @@ __device__ __forceinline__ int64_t lane_before(int64_t v, int lane, int64_t firs
     const uint32_t hi = lane_before_u32(static_cast<uint32_t>(u >> 32), lane,
                                         static_cast<uint32_t>(f >> 32));
     return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ double lane_before(double v, int lane, double first) {
+    return __longlong_as_double(static_cast<long long>(
+        lane_before(static_cast<int64_t>(__double_as_longlong(v)), lane,
+                    static_cast<int64_t>(__double_as_longlong(first)))));
 }
 
 }  // namespace rlscan

@@ -49,26 +49,62 @@ constexpr int64_t tile_elems() {
     return static_cast<int64_t>(kWave) * W * kChunk * R;
 }
 
-// Memory position of lane `lane`'s chunk in round r of wave `wave`.
+// The packed mapping at a tile capacity of `cap` elements: every tile holds
+// whole rows, `span` elements of them, a multiple of 4 (so that no 4-element
+// chunk straddles two tiles); `tiles` tiles in all.  One tile holds all rows
+// when they fit.  False if no tile can hold a row that way.
+inline bool packed_layout(int64_t N, int64_t T, int64_t cap, int64_t& span, int64_t& tiles) {
+    if (N * T <= cap) {
+        span = cap;
+        tiles = 1;
+        return true;
+    }
+    int64_t rows = cap / T;
+    while (rows > 0 && (rows * T) % kChunk != 0) --rows;
+    if (rows == 0) return false;
+    span = rows * T;
+    tiles = (N + rows - 1) / rows;
+    return true;
+}
+
+// Memory position of lane `lane`'s chunk in round r of wave `wave`, and
+// whether the chunk lies in the tile's span.  A tile spans tile_span
+// elements from mem_tile * tile_span; its chunks run from the span's high
+// end downwards for reverse estimators.  When the span falls short of the
+// tile's capacity (whole rows that do not fill it), the chunks past it hold
+// no elements: they are placed at the span's first element, so that every
+// value an estimator preloads for a chunk (bootstrap value, halo, carry)
+// stays in bounds, and take the identity step.
 template <class E, int R, int W>
 __device__ __forceinline__ int64_t chunk_base(const Geometry& geo, uint64_t tile, int wave, int r,
-                                              int lane) {
-    constexpr int64_t kTile = tile_elems<R, W>();
+                                              int lane, bool& inside) {
     const int64_t mem_tile = E::kReverse ? geo.num_tiles - 1 - static_cast<int64_t>(tile)
                                          : static_cast<int64_t>(tile);
     const int c = (wave * R + r) * kWave + lane;  // chunk index in scan order
-    const int64_t off = E::kReverse ? kTile - static_cast<int64_t>(kChunk) * (c + 1)
+    const int64_t off = E::kReverse ? geo.tile_span - static_cast<int64_t>(kChunk) * (c + 1)
                                     : static_cast<int64_t>(kChunk) * c;
-    return mem_tile * kTile + off;
+    inside = off >= 0 && off < geo.tile_span;
+    return mem_tile * geo.tile_span + (inside ? off : 0);
 }
 
-// Whether every element of the tile lies below N*T.
+// Lane `lane`'s chunk in round r of wave `wave`: elements that lie in the
+// tile's span and below N*T are valid.
+template <class E, int R, int W>
+__device__ __forceinline__ ChunkPos chunk_at(const Geometry& geo, uint64_t tile, int wave, int r,
+                                             int lane) {
+    bool inside;
+    ChunkPos q = chunk_pos(chunk_base<E, R, W>(geo, tile, wave, r, lane, inside), geo);
+    if (!inside) q.valid = 0;
+    return q;
+}
+
+// Whether every element of the tile lies in its span and below N*T.
 template <class E, int R, int W>
 __device__ __forceinline__ bool tile_is_full(const Geometry& geo, uint64_t tile) {
     constexpr int64_t kTile = tile_elems<R, W>();
     const int64_t mem_tile = E::kReverse ? geo.num_tiles - 1 - static_cast<int64_t>(tile)
                                          : static_cast<int64_t>(tile);
-    return (mem_tile + 1) * kTile <= geo.NT;
+    return geo.tile_span == kTile && (mem_tile + 1) * kTile <= geo.NT;
 }
 
 // 1. loads, all rounds first so every load of the tile is in flight
@@ -80,7 +116,7 @@ __device__ __forceinline__ void load_tile(const typename E::Params& p, const Geo
     const int wave = threadIdx.x / kWave;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        pos[r] = chunk_pos(chunk_base<E, R, W>(geo, tile, wave, r, lane), geo);
+        pos[r] = chunk_at<E, R, W>(geo, tile, wave, r, lane);
         E::template load<VEC, FULL, CARRY>(p, geo, pos[r], ch[r],
                                     stage + (wave * R + r) * E::kStageFloats);
     }
@@ -139,7 +175,7 @@ __device__ __forceinline__ void tile_carry(const LookbackArgs& lb, uint64_t tile
             A agg = identity_step(A{});
 #pragma unroll
             for (int w = 0; w < W; ++w) agg = compose(sm_wave[w], agg);
-            TileStatus* st = lb.status + tile;
+            TileStatus* st = status_of<A>(lb.status, static_cast<int64_t>(tile));
             const bool known = tile == 0 || cuts_chain(agg);
             if (lane == 0) {
                 if (known)
@@ -186,9 +222,10 @@ __device__ __forceinline__ void replay_store(const typename E::Params& p, const 
             out[j] = x;
         }
         ChunkPos q;
-        q.g0 = chunk_base<E, R, W>(geo, tile, wave, r, lane);
+        bool inside;
+        q.g0 = chunk_base<E, R, W>(geo, tile, wave, r, lane, inside);
         const int64_t rem = geo.NT - q.g0;
-        q.valid = rem <= 0 ? 0 : (rem >= kChunk ? kChunk : static_cast<int>(rem));
+        q.valid = (!inside || rem <= 0) ? 0 : (rem >= kChunk ? kChunk : static_cast<int>(rem));
         E::template store<VEC, FULL>(p, q, epi[r], out, before,
                                      ostage + wave * E::kOutStageFloats);
         if (CARRY && p.carry_out != nullptr) {

@@ -85,7 +85,7 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("mapping", ctypes.c_int32), ("rounds", ctypes.c_int32),
                 ("tile_elems", ctypes.c_int64), ("tiles", ctypes.c_int64),
                 ("grid", ctypes.c_int64), ("threads", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("tile_span", ctypes.c_int32)]
 
 
 _lib = None
@@ -552,7 +552,7 @@ def rlscan_plan(estimator, N, T, A=1) -> dict:
     info = PlanInfo()
     est = ESTIMATOR_IDS[estimator] if isinstance(estimator, str) else int(estimator)
     _check(library().rlscan_plan(est, N, T, A, ctypes.byref(info)))
-    return {f[0]: getattr(info, f[0]) for f in PlanInfo._fields_ if f[0] != "reserved"}
+    return {f[0]: getattr(info, f[0]) for f in PlanInfo._fields_}
 
 
 def rlscan_set_launch_override(mapping=MAP_AUTO, rounds=0, waves=0, grid_cap=0, flags=0):

@@ -138,11 +138,29 @@ def test_plan_mapping_choice(lib):
     assert rlscan.rlscan_plan("gae", 1024, 1024)["threads"] == 256
     p = rlscan.rlscan_plan("discounted_returns", 256, 2048)
     assert p["threads"] == 512 and p["mapping"] == rlscan.MAP_PACKED
-    # rows longer than a tile, or rows that do not divide it: look-back,
+    assert p["tile_span"] == p["tile_elems"]
+    # rows that divide no tile: the smallest tile whose whole rows fill at
+    # least 7/8 of it (a span that is a multiple of 4), else the best-filled
+    # one if at least 3/4 full; the remaining lanes idle
+    for est, N, T, threads, span, tiles in (
+            ("gae", 4096, 100, 128, 500, 820), ("episodic_prefix_sum", 4096, 100, 128, 500, 820),
+            ("gae", 4096, 200, 256, 1000, 820), ("discounted_returns", 1024, 96, 128, 480, 205),
+            ("retrace", 4096, 20, 64, 240, 342), ("gae", 5, 1000, 256, 1000, 5),
+            ("eligibility_traces", 11, 7, 64, 256, 1)):
+        p = rlscan.rlscan_plan(est, N, T, 6)
+        assert p["mapping"] == rlscan.MAP_PACKED, (est, N, T)
+        assert (p["threads"], p["tile_span"], p["tiles"]) == (threads, span, tiles), (est, N, T, p)
+    p = rlscan.rlscan_plan("gae", 1000, 7)  # 73 rows of 7 would be 511 elements: 72 rows
+    assert p["mapping"] == rlscan.MAP_PACKED and p["tile_span"] == 504 and p["tiles"] == 14
+    p = rlscan.rlscan_plan("gae", 2048, 1000)  # two rounds of eight waves: 4 rows of 4096
+    assert p["rounds"] == 2 and p["tile_span"] == 4000 and p["tiles"] == 512
+    # rows longer than a tile, or filling less than 3/4 of one: look-back,
     # with eight waves (one round)
     p = rlscan.rlscan_plan("gae", 64, 8192)
     assert p["mapping"] == rlscan.MAP_LOOKBACK and p["threads"] == 512 and p["rounds"] == 1
-    assert rlscan.rlscan_plan("gae", 5, 1000)["mapping"] == rlscan.MAP_LOOKBACK
+    assert p["tile_span"] == p["tile_elems"]
+    p = rlscan.rlscan_plan("gae", 1024, 3000)  # one row of 3000 in a tile of 4096
+    assert p["mapping"] == rlscan.MAP_LOOKBACK and p["tiles"] == (1024 * 3000 + 4095) // 4096
     # long rows: four rounds of four waves
     for est, waves in (("discounted_returns", 4), ("episodic_prefix_sum", 4),
                        ("eligibility_traces", 4), ("gae", 4), ("vtrace", 4),
@@ -165,6 +183,11 @@ def test_plan_mapping_choice(lib):
     rlscan.rlscan_set_launch_override(rlscan.MAP_LOOKBACK, 2, grid_cap=7)
     p = rlscan.rlscan_plan("gae", 4096, 128)
     assert p["mapping"] == rlscan.MAP_LOOKBACK and p["rounds"] == 2 and p["grid"] == 7
+    # a forced packed mapping is honoured wherever a tile holds a whole row
+    rlscan.rlscan_set_launch_override(rlscan.MAP_PACKED, 2, 8)
+    p = rlscan.rlscan_plan("gae", 1024, 3000)
+    assert p["mapping"] == rlscan.MAP_PACKED and p["tile_span"] == 3000 and p["tiles"] == 1024
+    assert rlscan.rlscan_plan("gae", 4, 5000)["mapping"] == rlscan.MAP_LOOKBACK
     rlscan.rlscan_set_launch_override(waves=8)
     p = rlscan.rlscan_plan("gae", 4096, 128)
     assert p["threads"] == 512 and p["tile_elems"] == 2048 and p["tiles"] == 256

@@ -206,6 +206,125 @@ def test_degenerate_parameters(estimator, params, shape):
     check(estimator, w, inputs, f"degenerate {params}")
 
 
+# V-trace whose trace coefficients gamma*c_t can exceed 1 (gamma*lambda*c_bar
+# > 1, here c_bar = 2 or +inf): the recurrence expands along an episode.
+# With terminated ~ Bernoulli(0.01) (episodes of about 100 steps) the trace
+# products reach 10^3 and beyond, and float32 evaluation misses the bar; the
+# library runs these calls in its float64 form.  Every mapping and round
+# count, one-byte flags, and a long look-back row.
+INF = float("inf")
+EXPANDING = [dict(c_bar=INF, rho_bar=1.0), dict(c_bar=2.0, rho_bar=1.0),
+             dict(c_bar=INF, rho_bar=INF)]
+EXPANDING_SHAPES = [((4096, 128), None), ((40, 1000), None), ((3, 5000), None),
+                    ((2, 20000), (1, 1)), ((2, 20000), (1, 8)), ((2, 20000), (2, 4)),
+                    ((2, 20000), (4, 8)), ((8, 1 << 18), None)]
+
+
+@pytest.mark.parametrize("params", EXPANDING, ids=["cinf", "c2", "cinf-rhoinf"])
+@pytest.mark.parametrize("shape,rw", EXPANDING_SHAPES,
+                         ids=[f"{n}x{t}" + (f"-R{rw[0]}W{rw[1]}" if rw else "")
+                              for (n, t), rw in EXPANDING_SHAPES])
+@pytest.mark.parametrize("byte_flags", [False, True], ids=["f32flags", "u8flags"])
+def test_vtrace_expanding_traces(params, shape, rw, byte_flags):
+    N, T = shape
+    w, inputs = case("vtrace", N, T, seed=T + N, gamma=0.99, term_p=0.01, trunc_p=0.002,
+                     **params)
+    if rw is not None:
+        rlscan.rlscan_set_launch_override(rlscan.MAP_AUTO, *rw)
+    print(f"[parity] vtrace expanding {N}x{T} {params} rw={rw} u8={byte_flags}", flush=True)
+    d = device.upload(inputs)
+    if byte_flags:
+        for k in ("terminated", "truncated"):
+            d[k] = (d[k] != 0).to(torch.uint8)
+    out = device.alloc_outputs("vtrace", N, T)
+    device.call("vtrace", d, out, w)
+    torch.cuda.synchronize()
+    assert_parity({k: v.cpu().numpy() for k, v in out.items()},
+                  oracle_outputs("vtrace", inputs, w), f"vtrace expanding {N}x{T} {params}")
+
+
+def test_vtrace_expanding_traces_options_carry_and_group():
+    """The float64 form through rlscan_vtrace_ex (lambda = 0.9: gamma*lambda
+    *c_bar still above 1), chained carry calls, and a grouped launch beside
+    a float32-form call."""
+    import oracle
+    w, inputs = case("vtrace", 24, 3000, seed=77, gamma=0.995, term_p=0.01, c_bar=INF,
+                     rho_bar=1.5)
+    lam, rho_bar_pg = 0.9, 0.8
+    d = device.upload(inputs)
+    vs = torch.empty((w.N, w.T), device="cuda")
+    pg = torch.empty((w.N, w.T), device="cuda")
+    rlscan.rlscan_vtrace_ex(d["rewards"], d["values"], d["bootstrap_value"], d["log_rhos"],
+                            d["terminated"], d["truncated"], d["bootstrap_values"], vs, pg,
+                            w.gamma, lam, w.rho_bar, w.c_bar, rho_bar_pg)
+    # the same rollout in three chunks, later chunks first, chained through
+    # carry_in / carry_out (vs at the chunk edges)
+    cuts = (0, 1100, 2048, w.T)
+    cvs = torch.empty((w.N, w.T), device="cuda")
+    cpg = torch.empty((w.N, w.T), device="cuda")
+    carry = None
+    for a, b in reversed(list(zip(cuts[:-1], cuts[1:]))):
+        part = {k: (None if v is None else v[:, a:b].contiguous() if v.dim() == 2 else v)
+                for k, v in d.items()}
+        if b < w.T:  # V at the chunk's end is V_b, the next chunk's first value
+            part["bootstrap_value"] = d["values"][:, b].contiguous()
+        pvs = torch.empty((w.N, b - a), device="cuda")
+        ppg = torch.empty((w.N, b - a), device="cuda")
+        co = torch.empty(w.N, device="cuda")
+        rlscan.rlscan_vtrace_ex(part["rewards"], part["values"], part["bootstrap_value"],
+                                part["log_rhos"], part["terminated"], part["truncated"],
+                                part["bootstrap_values"], pvs, ppg, w.gamma, lam, w.rho_bar,
+                                w.c_bar, rho_bar_pg, carry_in=carry, carry_out=co)
+        cvs[:, a:b] = pvs
+        cpg[:, a:b] = ppg
+        carry = co
+    torch.cuda.synchronize()
+    want_vs, want_pg = oracle.vtrace(
+        inputs["rewards"], inputs["values"], inputs["log_rhos"], inputs["terminated"],
+        gamma=w.gamma, rho_bar=w.rho_bar, c_bar=w.c_bar,
+        bootstrap_value=inputs["bootstrap_value"], truncated=inputs["truncated"],
+        bootstrap_values=inputs["bootstrap_values"], lam=lam, rho_bar_pg=rho_bar_pg)
+    want = {"vs": want_vs, "pg_advantages": want_pg}
+    assert_parity({"vs": vs.cpu().numpy(), "pg_advantages": pg.cpu().numpy()}, want,
+                  "vtrace_ex expanding")
+    # The carry crosses the interface in float32 (vs at the chunk edge), and
+    # an expanding recurrence amplifies that rounding like any other: the
+    # reference for the chained calls is the oracle chained the same way, its
+    # own carry_out rounded to float32 before the chunk below reads it.
+    ovs, opg = np.empty((w.N, w.T)), np.empty((w.N, w.T))
+    ocarry = None
+    for a, b in reversed(list(zip(cuts[:-1], cuts[1:]))):
+        part = {k: (None if v is None else v[:, a:b] if v.ndim == 2 else v)
+                for k, v in inputs.items()}
+        if b < w.T:
+            part["bootstrap_value"] = inputs["values"][:, b].copy()
+        pv, pp, co = oracle.vtrace(
+            part["rewards"], part["values"], part["log_rhos"], part["terminated"],
+            gamma=w.gamma, rho_bar=w.rho_bar, c_bar=w.c_bar,
+            bootstrap_value=part["bootstrap_value"], truncated=part["truncated"],
+            bootstrap_values=part["bootstrap_values"], lam=lam, rho_bar_pg=rho_bar_pg,
+            carry_in=ocarry, return_carry=True)
+        ovs[:, a:b], opg[:, a:b] = pv, pp
+        ocarry = co.astype(np.float32)
+    assert_parity({"vs": cvs.cpu().numpy(), "pg_advantages": cpg.cpu().numpy()},
+                  {"vs": ovs, "pg_advantages": opg}, "vtrace_ex expanding, chained carry calls")
+    # grouped: an expanding call beside a float32-form call
+    wg, ig = case("vtrace", 512, 128, seed=78, gamma=0.99, term_p=0.01, c_bar=INF)
+    wf, jf = case("vtrace", 256, 128, seed=79, gamma=0.99, term_p=0.01, c_bar=1.0)
+    dg, df = device.upload(ig), device.upload(jf)
+    og, of = device.alloc_outputs("vtrace", 512, 128), device.alloc_outputs("vtrace", 256, 128)
+    calls = [rlscan.GroupCall("vtrace", tuple(x.get(k) for k in device.INPUT_ORDER["vtrace"]),
+                              (o["vs"], o["pg_advantages"]), gamma=ww.gamma, lam=1.0,
+                              rho_bar=ww.rho_bar, c_bar=ww.c_bar)
+             for x, o, ww in ((dg, og, wg), (df, of, wf))]
+    rlscan.rlscan_group(calls)
+    torch.cuda.synchronize()
+    assert_parity({k: v.cpu().numpy() for k, v in og.items()}, oracle_outputs("vtrace", ig, wg),
+                  "grouped expanding vtrace")
+    assert_parity({k: v.cpu().numpy() for k, v in of.items()}, oracle_outputs("vtrace", jf, wf),
+                  "grouped float32-form vtrace")
+
+
 @pytest.mark.parametrize("estimator", ESTIMATORS)
 def test_empty_inputs(estimator):
     for N, T in ((0, 5), (5, 0), (0, 0)):
@@ -313,6 +432,91 @@ def test_graph_capture_of_packed_calls():
         # eager work between replays
         device.call("gae", dev["gae"], eager["gae"], w)
         torch.cuda.synchronize()
+
+
+# Rollout lengths that divide no tile size: tiles of whole rows whose span
+# falls short of the tile (the remaining lanes idle), a multiple of 4
+# elements; ragged last tiles (fewer rows); odd T.
+PARTIAL = [(4096, 100), (4096, 200), (1024, 96), (2048, 1000), (4096, 20), (1000, 7),
+           (333, 25), (77, 37), (130, 124), (9, 300)]
+
+
+@pytest.mark.parametrize("estimator", ESTIMATORS)
+@pytest.mark.parametrize("shape", PARTIAL, ids=[f"{n}x{t}" for n, t in PARTIAL])
+def test_packed_rows_that_do_not_divide_the_tile(estimator, shape):
+    N, T = shape
+    w, inputs = case(estimator, N, T, seed=N + 3 * T)
+    plan = rlscan.rlscan_plan(estimator, N, T, w.A)
+    assert plan["mapping"] == rlscan.MAP_PACKED, plan
+    assert plan["tile_span"] % 4 == 0 and plan["tile_span"] % T == 0 or plan["tiles"] == 1
+    print(f"[parity] {estimator} {N}x{T} packed span {plan['tile_span']} of "
+          f"{plan['tile_elems']}", flush=True)
+    d = device.upload(inputs)
+    outs = [device.alloc_outputs(estimator, N, T) for _ in range(2)]
+    for out in outs:
+        device.call(estimator, d, out, w)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in outs[0].items()}
+    assert_parity(got, oracle_outputs(estimator, inputs, w), f"{estimator} {N}x{T} packed")
+    for k, v in outs[1].items():  # no look-back: deterministic
+        assert torch.equal(v, outs[0][k]), k
+
+
+@pytest.mark.parametrize("estimator", ESTIMATORS)
+def test_forced_packed_mapping_with_a_sparse_tile(estimator):
+    """A packed mapping forced where the rows fill less than 3/4 of a tile
+    (one row of 3000 in 4096), two rounds of eight waves."""
+    w, inputs = case(estimator, 6, 3000, seed=5)
+    rlscan.rlscan_set_launch_override(rlscan.MAP_PACKED, 2, 8)
+    plan = rlscan.rlscan_plan(estimator, 6, 3000, w.A)
+    want = rlscan.MAP_PACKED if estimator != "retrace" else plan["mapping"]
+    assert plan["mapping"] == want
+    check(estimator, w, inputs, f"forced packed {plan}")
+
+
+def test_graph_capture_and_group_of_rows_that_do_not_divide_the_tile():
+    """Calls of 4096 x 100 (packed with partly filled tiles) capture into a
+    HIP graph, replaying to the eager results bit for bit, and join one
+    grouped launch."""
+    w = workloads.custom(4096, 100, gamma=0.99, lam=0.95, term_p=1 / 200, done_p=0.01)
+    host = {e: workloads.inputs_for(e, w, 3) for e in ESTIMATORS}
+    dev = {e: device.upload(host[e]) for e in ESTIMATORS}
+    eager = {}
+    for e in ESTIMATORS:
+        eager[e] = device.alloc_outputs(e, w.N, w.T)
+        device.call(e, dev[e], eager[e], w)
+    torch.cuda.synchronize()
+    for e in ESTIMATORS:
+        assert_parity({k: v.cpu().numpy() for k, v in eager[e].items()},
+                      oracle_outputs(e, host[e], w), f"{e} 4096x100")
+    outs = {e: device.alloc_outputs(e, w.N, w.T) for e in ESTIMATORS}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for e in ESTIMATORS:
+            device.call(e, dev[e], outs[e], w)
+    for rep in range(3):
+        for o in outs.values():
+            for v in o.values():
+                v.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"[parity] 4096x100 graph replay {rep}", flush=True)
+        for e in ESTIMATORS:
+            for k in eager[e]:
+                assert torch.equal(outs[e][k], eager[e][k]), (rep, e, k)
+        device.call("gae", dev["gae"], outs["gae"], w)  # eager work between replays
+        torch.cuda.synchronize()
+    grouped = {e: device.alloc_outputs(e, w.N, w.T) for e in ESTIMATORS}
+    calls = [rlscan.GroupCall(e, tuple(dev[e].get(k) for k in device.INPUT_ORDER[e]),
+                              tuple(grouped[e].values()), gamma=w.gamma,
+                              lam=1.0 if e == "vtrace" else w.lam)
+             for e in ESTIMATORS]
+    rlscan.rlscan_group(calls)
+    torch.cuda.synchronize()
+    for e in ESTIMATORS:
+        assert_parity({k: v.cpu().numpy() for k, v in grouped[e].items()},
+                      oracle_outputs(e, host[e], w), f"grouped {e} 4096x100")
 
 
 # the refused call enqueues nothing, so the captured graph is empty by design
@@ -425,14 +629,13 @@ def random_case(seed):
         if est == "retrace" and opts["trunc_mode"] == "none":
             opts["trunc_mode"] = "independent"
     if est == "vtrace":
-        # traces stay clipped at c_bar <= 1: above 1 the recurrence expands
-        # (a = gamma*c > 1 where the ratio exceeds 1) and float32 rounding
-        # grows with the trace product along an episode, beyond the parity
-        # bar for any float32 evaluation (a sequential float32 loop misses it
-        # too); test_degenerate_parameters covers c_bar = +inf on short
-        # episodes
         opts["rho_bar"] = float(rng.choice([1.0, 0.5, 2.0, np.inf]))
-        opts["c_bar"] = float(rng.choice([1.0, 0.9, 1e-3]))
+        opts["c_bar"] = float(rng.choice([1.0, 0.9, 1e-3, 2.0, np.inf]))
+        if opts["c_bar"] > 1.0:
+            # expanding traces (the float64 form when gamma*c_bar > 1):
+            # episodes of at most about 100 steps on average, so that trace
+            # products stay within float32's range
+            opts["term_p"] = float(rng.choice([0.01, 0.02, 0.3]))
     rounds, waves = SHAPES_RW[rng.integers(len(SHAPES_RW))]
     mapping = int(rng.choice([rlscan.MAP_AUTO, rlscan.MAP_LOOKBACK]))
     grid_cap = int(rng.choice([0, 0, 0, 7, 64]))
