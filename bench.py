@@ -504,8 +504,13 @@ FLAG_KEYS = ("terminated", "truncated", "dones")
 def algorithmic_bytes(inputs: dict, outputs: dict) -> int:
     """Bytes the method must move: every input read once, every output
     written once."""
-    return int(sum(v.nbytes for v in inputs.values() if v is not None) +
-               sum(o.numel() * o.element_size() for o in outputs.values()))
+    return sum(read_write_bytes(inputs, outputs))
+
+
+def read_write_bytes(inputs: dict, outputs: dict):
+    """(bytes read, bytes written): every input once, every output once."""
+    return (int(sum(v.nbytes for v in inputs.values() if v is not None)),
+            int(sum(o.numel() * o.element_size() for o in outputs.values())))
 
 
 class CallSet:
@@ -517,6 +522,7 @@ class CallSet:
         from linear_recurrence_scan_coefficient_amd import device, workloads
         self.calls = []
         self.bytes = {}
+        self.rw = {}  # (bytes read, bytes written) per estimator
         self.keep = []
         for est in estimators:
             host = workloads.inputs_for(est, w, seed)
@@ -529,6 +535,7 @@ class CallSet:
             name, args = make(est, d, out, w, stream_handle)
             self.calls.append((est, getattr(lib, name), args))
             self.bytes[est] = algorithmic_bytes(host, out)
+            self.rw[est] = read_write_bytes(host, out)
             self.keep.append((d, out))
         self.w = w
 
@@ -538,7 +545,7 @@ class CallSet:
         host-side input generation."""
         from linear_recurrence_scan_coefficient_amd import device
         c = CallSet.__new__(CallSet)
-        c.calls, c.bytes, c.keep, c.w = [], dict(self.bytes), [], self.w
+        c.calls, c.bytes, c.rw, c.keep, c.w = [], dict(self.bytes), dict(self.rw), [], self.w
         for (est, fn, _), (d, out) in zip(self.calls, self.keep):
             d2 = {k: (None if v is None else v.clone()) for k, v in d.items()}
             out2 = device.alloc_outputs(est, self.w.N, self.w.T)
@@ -640,21 +647,21 @@ def eager_workload(torch, w, sh, lib, reps, nsets=3, byte_flags=False):
     reps = max(reps, len(sets))
     per = time_batched_calls(torch, sets, reps)
     iso = time_eager_calls(torch, sets, max(reps, 50))
-    nbytes = dict(sets[0].bytes)
+    nbytes, rw = dict(sets[0].bytes), dict(sets[0].rw)
     del sets
     torch.cuda.empty_cache()
     res = {}
     for e in w.estimators:
         b, us = nbytes[e], per[e]
         gbs = b / (us * 1e-6) / 1e9
-        copy_us, copy_gbs = copy_ceiling(torch, sh, lib, b)
+        ceil = mix_ceiling(torch, sh, lib, *rw[e])
         res[e] = {"us_per_call": round(us, 2), "elements_per_s": w.N * w.T / (us * 1e-6),
-                  "bytes": b, "GB_per_s": round(gbs, 1),
+                  "bytes": b, "bytes_read": rw[e][0], "bytes_written": rw[e][1],
+                  "GB_per_s": round(gbs, 1),
                   "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                   "us_per_isolated_call": round(sum(iso[e]) / len(iso[e]), 2),
                   "isolated_call_us": spread(iso[e]),
-                  "copy_same_bytes_GB_per_s": round(copy_gbs, 1),
-                  "frac_of_copy": round(gbs / copy_gbs, 4)}
+                  "stream_ceiling": ceil, "frac_of_ceiling": round(gbs / ceil["GB_per_s"], 4)}
     return res
 
 
@@ -737,16 +744,25 @@ def time_launches(torch, graph, launches, reps):
 def per_kernel(torch, est, w, sh, lib, reps=10, byte_flags=False):
     """Average launch duration of one estimator over M buffer sets in distinct
     memory (6 seeds, then device-side clones; M * bytes >= COLD_BYTES, so
-    every launch reads cold inputs)."""
+    every launch reads cold inputs): microseconds, algorithmic bytes, M, and
+    (bytes read, bytes written).  Packed calls are timed as replays of a
+    graph of the M launches; look-back calls, which cannot be captured, as
+    back-to-back launches between one event pair."""
+    from linear_recurrence_scan_coefficient_amd import rlscan
     probe = CallSet([est], w, 0, sh, lib, byte_flags)
-    b = probe.bytes[est]
+    b, rw = probe.bytes[est], probe.rw[est]
     sets = [probe] + [CallSet([est], w, seed, sh, lib, byte_flags) for seed in range(1, 6)]
     sets = cold_rotation(sets, b, sh, lib)
     m = len(sets)
-    g = capture_graph(torch, [s.calls[0] for s in sets])
-    us = time_launches(torch, g, m, reps)
-    del g, sets
-    return us, b, m
+    if rlscan.rlscan_plan(est, w.N, w.T, w.A)["mapping"] == rlscan.MAP_PACKED:
+        g = capture_graph(torch, [s.calls[0] for s in sets])
+        us = time_launches(torch, g, m, reps)
+        del g
+    else:
+        us = time_batched_calls(torch, sets, max(reps * m, 200))[est]
+    del sets
+    torch.cuda.empty_cache()
+    return us, b, m, rw
 
 
 def copy_ceiling(torch, sh, lib, nbytes, min_bytes=COLD_BYTES, reps=10):
@@ -765,6 +781,176 @@ def copy_ceiling(torch, sh, lib, nbytes, min_bytes=COLD_BYTES, reps=10):
     us = time_launches(torch, g, m, reps)
     del g, pairs
     return us, 2 * half / (us * 1e-6) / 1e9
+
+
+def mix_candidates(read_bytes, write_bytes):
+    """(reads, writes) words per thread for the stream ceiling: the call's
+    read:write ratio at 1, 2 and 4 written words per thread (more words per
+    thread: more bytes in flight, fewer workgroups)."""
+    ratio = read_bytes / max(1, write_bytes)
+    out = []
+    for wr in (1, 2, 4):
+        rd = max(1, min(16, int(round(ratio * wr))))
+        if (rd, wr) not in out:
+            out.append((rd, wr))
+    return out
+
+
+def mix_ceiling(torch, sh, lib, read_bytes, write_bytes, min_bytes=COLD_BYTES, reps=6):
+    """Achievable bandwidth for a launch that reads `read_bytes` and writes
+    `write_bytes`: the fastest of the library's streaming kernel
+    (rlscan_stream_mix) over mix_candidates, each timed over M distinct
+    buffer pairs (M * bytes >= min_bytes, so every launch reads cold data),
+    as `per_kernel` times the scans.  Returns a dict: microseconds per launch,
+    GB/s counting read and written bytes, and the (reads, writes) taken."""
+    rb, wb = read_bytes // 16 * 16, write_bytes // 16 * 16
+    m = max(6, min(512, -(-min_bytes // max(1, rb + wb))))
+    pairs = [(torch.ones(rb, dtype=torch.uint8, device="cuda"),
+              torch.empty(wb, dtype=torch.uint8, device="cuda")) for _ in range(m)]
+    best = None
+    for rd, wr in mix_candidates(rb, wb):
+        calls = [("mix", lib.rlscan_stream_mix,
+                  (dst.data_ptr(), wb, src.data_ptr(), rb, rd, wr, sh)) for src, dst in pairs]
+        g = capture_graph(torch, calls)
+        us = time_launches(torch, g, m, reps)
+        del g
+        if best is None or us < best[0]:
+            best = (us, rd, wr)
+    del pairs
+    torch.cuda.empty_cache()
+    us, rd, wr = best
+    return {"us": round(us, 3), "GB_per_s": round((rb + wb) / (us * 1e-6) / 1e9, 1),
+            "reads_per_thread": rd, "writes_per_thread": wr}
+
+
+def call_figures(torch, est, w, sh, lib, byte_flags=False):
+    """One estimator call of workload `w`: average launch duration over a
+    cold rotation (per_kernel), GB/s and fraction of the 8 TB/s peak, the
+    plan, the launch floor of its own grid and workgroup size, and the
+    stream ceiling for its read:write bytes."""
+    from linear_recurrence_scan_coefficient_amd import rlscan
+    us, b, m, rw = per_kernel(torch, est, w, sh, lib, byte_flags=byte_flags)
+    gbs = b / (us * 1e-6) / 1e9
+    p = rlscan.rlscan_plan(est, w.N, w.T, w.A)
+    ceil = mix_ceiling(torch, sh, lib, *rw)
+    return {"us_per_call": round(us, 3), "elements_per_s": w.N * w.T / (us * 1e-6),
+            "bytes": b, "bytes_read": rw[0], "bytes_written": rw[1],
+            "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "buffer_sets": m,
+            "mapping": "packed" if p["mapping"] == rlscan.MAP_PACKED else "lookback",
+            "tiles": p["tiles"], "threads": p["threads"], "tile_span": p["tile_span"],
+            "launch_floor_us": round(launch_floor_us(torch, p["grid"], p["threads"]), 3),
+            "stream_ceiling": ceil, "frac_of_ceiling": round(gbs / ceil["GB_per_s"], 4)}
+
+
+def time_configs(torch, sh, lib, steps, warmup):
+    """The other named configurations as timed lines: GAE at 64 x 512, the
+    truncation path at 4096 x 128 (five estimators, each call alone and the
+    five as one grouped launch), the 2^19-element shape sweep (GAE, V-trace,
+    discounted returns at six shapes from 16384 x 32 to 16 x 32768), and a
+    rollout length that divides no tile (4096 x 100, packed with 500 of each
+    512-element tile) beside 4096 x 128."""
+    from linear_recurrence_scan_coefficient_amd import workloads
+    res = {}
+    w0 = workloads.get("gae_64x512")
+    res[w0.name] = {"gae": call_figures(torch, "gae", w0, sh, lib)}
+    wt = workloads.get("truncation_4096x128")
+    res[wt.name] = {e: call_figures(torch, e, wt, sh, lib) for e in wt.estimators}
+    sets = [CallSet(wt.estimators, wt, seed, sh, lib) for seed in range(6)]
+    step_bytes = sum(sets[0].bytes.values())
+    sets = cold_rotation(sets, step_bytes, sh, lib)
+    groups = [s.group_array() for s in sets]
+    wall, dev_ms = time_group_steps(torch, lib, groups, sh, steps, warmup)
+    launch_us = dev_ms * 1000.0 / steps
+    rd = sum(v[0] for v in sets[0].rw.values())
+    wr = sum(v[1] for v in sets[0].rw.values())
+    del sets, groups
+    torch.cuda.empty_cache()
+    gbs = step_bytes / (launch_us * 1e-6) / 1e9
+    ceil = mix_ceiling(torch, sh, lib, rd, wr)
+    res[wt.name]["grouped"] = {
+        "avg_launch_us": round(launch_us, 3), "ms_per_step": wall * 1000.0 / steps,
+        "elements_per_s": len(wt.estimators) * wt.N * wt.T / (launch_us * 1e-6),
+        "bytes": step_bytes, "GB_per_s": round(gbs, 1),
+        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "stream_ceiling": ceil,
+        "frac_of_ceiling": round(gbs / ceil["GB_per_s"], 4),
+        "note": "the five truncation-path calls as one rlscan_group launch per step"}
+    sweep = {}
+    for n, t in workloads.SWEEP_SHAPES:
+        ws = workloads.get(f"sweep_{n}x{t}")
+        sweep[ws.name] = {e: call_figures(torch, e, ws, sh, lib) for e in ws.estimators}
+    res["sweep_2p19"] = sweep
+    wp = workloads.custom(4096, 100, name="production_4096x100")
+    res[wp.name] = {e: call_figures(torch, e, wp, sh, lib) for e in wp.estimators}
+    res[wp.name]["note"] = ("supplementary: rows that divide no tile size, packed with partly "
+                            "filled tiles; distributions as production_4096x128")
+    return res
+
+
+API_ARGS = {
+    # estimator: (positional input keys, keyword input keys) of its compute_* call
+    "gae": (("rewards", "values", "terminated"), ("bootstrap_value",)),
+    "lambda_returns": (("rewards", "values", "terminated"), ("bootstrap_value",)),
+    "discounted_returns": (("rewards", "terminated"), ("bootstrap_value",)),
+    "vtrace": (("rewards", "values", "log_rhos", "terminated"), ("bootstrap_value",)),
+    "retrace": (("rewards", "next_q_values_all", "next_target_probs", "actions",
+                 "behaviour_probs", "terminated", "truncated"), ()),
+    "eligibility_traces": (("x", "dones"), ()),
+    "episodic_prefix_sum": (("x", "dones"), ()),
+}
+
+
+def time_full_calls(torch, w, ests, reps=200, nsets=6):
+    """The pages' unit, the full call: each estimator's compute_* call (the
+    Python entry point: argument checks, output allocation, the C call and
+    its launch) at 4096 x 128.  `reps` back-to-back calls over a cold
+    rotation of device inputs, one synchronisation at the end (per call:
+    wall time / reps); and one call at a time, each followed by a
+    synchronisation (median of the wall time per call)."""
+    from linear_recurrence_scan_coefficient_amd import api, device, workloads
+    fns = {"gae": api.compute_gae, "lambda_returns": api.compute_lambda_returns,
+           "discounted_returns": api.compute_discounted_returns, "vtrace": api.compute_vtrace,
+           "retrace": api.compute_retrace, "eligibility_traces": api.compute_eligibility_traces,
+           "episodic_prefix_sum": api.compute_episodic_prefix_sum}
+    res = {}
+    for e in ests:
+        seeded = [device.upload(workloads.inputs_for(e, w, seed)) for seed in range(nsets)]
+        set_bytes = sum(v.numel() * v.element_size() for v in seeded[0].values()
+                        if v is not None)
+        n = max(nsets, min(256, -(-COLD_BYTES // set_bytes)))
+        sets = seeded + [{k: (None if v is None else v.clone()) for k, v in
+                          seeded[i % nsets].items()} for i in range(n - nsets)]
+        pos, kw = API_ARGS[e]
+        kwargs = {"gamma": w.gamma}
+        if e in ("gae", "lambda_returns", "retrace", "eligibility_traces"):
+            kwargs["lambda_"] = w.lam
+        if e == "vtrace":
+            kwargs.update(rho_bar=w.rho_bar, c_bar=w.c_bar)
+        if e == "episodic_prefix_sum":
+            kwargs = {}
+        calls = [((tuple(d[k] for k in pos)), {**kwargs, **{k: d[k] for k in kw}})
+                 for d in sets]
+        for a, k in calls[:4]:
+            fns[e](*a, **k)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(reps):
+            a, k = calls[i % len(calls)]
+            fns[e](*a, **k)
+        torch.cuda.synchronize()
+        back_to_back = (time.perf_counter() - t0) / reps * 1e6
+        alone = []
+        for i in range(50):
+            a, k = calls[i % len(calls)]
+            t0 = time.perf_counter()
+            fns[e](*a, **k)
+            torch.cuda.synchronize()
+            alone.append((time.perf_counter() - t0) * 1e6)
+        res[e] = {"full_call_us": round(back_to_back, 3), "full_call_synchronised_us":
+                  spread(alone)}
+        del sets, seeded, calls
+        torch.cuda.empty_cache()
+    return res
 
 
 def launch_floor_us(torch, grid, threads, launches=64, reps=10):
@@ -796,26 +982,59 @@ def read_traffic(kernel_label: str):
         return None
 
 
+def host_threads() -> int:
+    """Threads for the all-cores oracle leg: the host's CPUs, capped by the
+    OMP_NUM_THREADS share the environment gives this process."""
+    n = os.cpu_count() or 1
+    try:
+        n = min(n, int(os.environ.get("OMP_NUM_THREADS", n)))
+    except ValueError:
+        pass
+    return max(1, n)
+
+
 def cpu_baseline(w, estimators, seconds):
-    """The float64 oracle, single-threaded, on host copies of the same
-    workload, repeated for about `seconds`."""
+    """The float64 oracle, unchanged, on host copies of the same workload,
+    each leg repeated for about `seconds`: one thread, and the rows split
+    over min(N, host threads) threads calling the same oracle on their own
+    rows (rows are independent; the oracle's C loops run outside the
+    interpreter lock).  The all-cores leg is the reported value."""
+    import concurrent.futures
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from reference import oracle_outputs
     from linear_recurrence_scan_coefficient_amd import workloads
     host = {e: workloads.inputs_for(e, w, 0) for e in estimators}
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        for e in estimators:
-            oracle_outputs(e, host[e], w)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    elems = reps * len(estimators) * w.N * w.T
-    return {"value": elems / el, "unit": "elements/s", "cores": 1, "kind": "oracle",
-            "sample": (f"all {len(estimators)} estimators on {w.name} ({w.N}x{w.T}), "
-                       f"{reps} repetitions in {el:.1f} s, float64 C loops, one thread"),
-            "cpu": cpu_model(), "host_cpus": os.cpu_count()}
+
+    def rows(e, a, b):
+        sl = {k: (None if v is None else v[a:b]) for k, v in host[e].items()}
+        oracle_outputs(e, sl, workloads.custom(b - a, w.T, gamma=w.gamma, lam=w.lam,
+                                               rho_bar=w.rho_bar, c_bar=w.c_bar))
+
+    def leg(threads):
+        bounds = [(w.N * i // threads, w.N * (i + 1) // threads) for i in range(threads)]
+        reps, t0 = 0, time.perf_counter()
+        with concurrent.futures.ThreadPoolExecutor(threads) as pool:
+            while True:
+                for e in estimators:
+                    list(pool.map(lambda ab: rows(e, *ab), bounds))
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= seconds:
+                    break
+        return reps, el
+
+    threads = min(w.N, host_threads())
+    reps1, el1 = leg(1)
+    repsn, eln = leg(threads)
+    per_rep = len(estimators) * w.N * w.T
+    one = {"value": reps1 * per_rep / el1, "unit": "elements/s", "cores": 1,
+           "sample": f"{reps1} repetitions in {el1:.1f} s"}
+    return {"value": repsn * per_rep / eln, "unit": "elements/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"all {len(estimators)} estimators on {w.name} ({w.N}x{w.T}), rows split "
+                       f"over {threads} threads, {repsn} repetitions in {eln:.1f} s, float64 C "
+                       "loops"),
+            "one_core": one, "cpu": cpu_model(), "host_cpus": os.cpu_count()}
 
 
 def cpu_model() -> str:
@@ -853,7 +1072,7 @@ def time_variants(torch, w, ests, sh, lib, args):
     torch.cuda.empty_cache()
     per = {}
     for e in ests:
-        us, b, _ = per_kernel(torch, e, w, sh, lib, byte_flags=True)
+        us, b, _, _ = per_kernel(torch, e, w, sh, lib, byte_flags=True)
         per[e] = {"us_per_call": round(us, 3), "bytes": b,
                   "GB_per_s": round(b / (us * 1e-6) / 1e9, 1)}
     res["production_u8_flags"] = {
@@ -1029,24 +1248,23 @@ def main():
         del rev_groups
 
     print("[bench] timing each estimator's launches", file=sys.stderr, flush=True)
-    per_est = {}
-    for e in ests:
-        us, b, m = per_kernel(torch, e, w, sh, lib)
-        gbs = b / (us * 1e-6) / 1e9
-        per_est[e] = {"us_per_call": round(us, 3), "elements_per_s": w.N * w.T / (us * 1e-6),
-                      "bytes": b, "GB_per_s": round(gbs, 1),
-                      "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "buffer_sets": m}
+    per_est = {e: call_figures(torch, e, w, sh, lib) for e in ests}
     # each call alone: an event pair around every call of 100 steps made one
     # call at a time over the cold rotation
     iso = time_eager_calls(torch, sets, 100)
     for e in ests:
         per_est[e]["isolated_call_us"] = spread(iso[e])
-        p = rlscan.rlscan_plan(e, w.N, w.T, w.A)
-        per_est[e]["launch_floor_us"] = round(launch_floor_us(torch, p["grid"], p["threads"]), 3)
+    if not args.no_variants:
+        print("[bench] timing the full compute_* calls", file=sys.stderr, flush=True)
+        full = time_full_calls(torch, w, ests)
+        for e in ests:
+            per_est[e].update(full[e])
     dom = max(ests, key=lambda e: per_est[e]["us_per_call"])
     d = per_est[dom]
+    step_read = sum(v[0] for v in sets[0].rw.values())
+    step_written = sum(v[1] for v in sets[0].rw.values())
+    step_ceiling = mix_ceiling(torch, sh, lib, step_read, step_written)
     copy_us, copy_gbs = copy_ceiling(torch, sh, lib, set_bytes)
-    dom_copy_us, dom_copy_gbs = copy_ceiling(torch, sh, lib, d["bytes"])
     plan = rlscan.rlscan_plan(dom, w.N, w.T, w.A)
     floor = per_est[dom]["launch_floor_us"]
     # the grouped launch's grid: every call's tiles at the group's two waves
@@ -1070,7 +1288,10 @@ def main():
                      "traffic": read_traffic(f"group_{w.name}"),
                      "kernel": "group_kernel (the seven calls of a step)",
                      "algorithmic_bytes_per_launch": set_bytes,
+                     "bytes_read": step_read, "bytes_written": step_written,
                      "avg_launch_us": round(launch_us, 3),
+                     "stream_ceiling": step_ceiling,
+                     "frac_of_ceiling": round(group_gbs / step_ceiling["GB_per_s"], 4),
                      "copy_same_bytes": {"us": round(copy_us, 3),
                                          "GB_per_s": round(copy_gbs, 1)}},
         "per_estimator": per_est,
@@ -1086,8 +1307,8 @@ def main():
                                 "traffic": read_traffic(f"{dom}_{w.name}"),
                                 "algorithmic_bytes_per_launch": d["bytes"],
                                 "avg_launch_us": d["us_per_call"],
-                                "copy_same_bytes": {"us": round(dom_copy_us, 3),
-                                                    "GB_per_s": round(dom_copy_gbs, 1)}},
+                                "stream_ceiling": d["stream_ceiling"],
+                                "frac_of_ceiling": d["frac_of_ceiling"]},
             "note": "the seven C calls one after another on one stream"},
         "small_rotation": small_rotation,
         "group_waves": waves_sweep,
@@ -1120,6 +1341,8 @@ def main():
             "supplementary shape, not one of the named configurations")
 
     if not args.no_variants:
+        print("[bench] timing the other configurations", file=sys.stderr, flush=True)
+        result["configs"] = time_configs(torch, sh, lib, args.steps, args.warmup)
         print("[bench] timing the variants", file=sys.stderr, flush=True)
         result["variants"] = time_variants(torch, w, ests, sh, lib, args)
 

@@ -529,6 +529,19 @@ enum {
  * workgroups loop.  Returns RLSCAN_ERR_PARAM for other values. */
 int rlscan_set_launch_override(int mapping, int rounds, int waves, int64_t grid_cap, int flags);
 
+/* Overrides the order in which the workgroups of packed and grouped
+ * launches take their tiles, for every later call in the process (tests and
+ * benchmarks).  Workgroup b runs on XCD b % 8 of the MI355X; with run > 0
+ * the tiles are cut into groups of 8*run and in each group XCD x takes the
+ * x-th run of `run` consecutive tiles (a group cut short by the end of the
+ * grid keeps tile = b).  run = 0: tile = b; run = -1: the library's own
+ * choice (the default: runs of 16 for packed launches whose tile span is
+ * not a multiple of 32 elements, where neighbouring tiles share a cache
+ * line; tile = b otherwise and for grouped launches).  Look-back launches
+ * always take tile = b.  Results do not depend on the order.  Returns
+ * RLSCAN_ERR_PARAM for run < -1 or above 2^20. */
+int rlscan_set_xcd_run(int64_t run);
+
 /* Diagnostics: enqueues an empty kernel of `grid` workgroups of `threads`
  * threads on `stream` -- the launch-bound floor of a scan launch with that
  * grid and workgroup size (rlscan_plan gives both).  Returns
@@ -544,6 +557,22 @@ int rlscan_launch_floor(int64_t grid, int32_t threads, hipStream_t stream);
  * RLSCAN_ERR_NULL, RLSCAN_ERR_PARAM for a misaligned pointer, and
  * RLSCAN_ERR_ALIAS for overlapping ranges. */
 int rlscan_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
+
+/* Diagnostics: enqueues a streaming kernel with a read:write mix -- the
+ * achievable-bandwidth reference for a scan call that reads read_bytes and
+ * writes write_bytes.  Each thread reads `reads` (1..16) 16-byte words of
+ * `src`, then writes `writes` (1..4) words of `dst`, each the sum of the
+ * words it read (every read is used before any write, as in a scan);
+ * workgroups of 256 threads take consecutive spans of both buffers, with the
+ * same non-temporal 16-byte accesses as the scans.  With reads = writes = 1
+ * and equal sizes it is a copy.  A bandwidth reference is the fastest over
+ * a few (reads, writes) choices of the call's read:write ratio (more words
+ * per thread: more bytes in flight, fewer workgroups).  Buffers are device
+ * pointers, 16-byte aligned, not overlapping; sizes multiples of 16.
+ * Returns RLSCAN_ERR_SHAPE for bad sizes, RLSCAN_ERR_PARAM for counts out of
+ * range or misaligned pointers, RLSCAN_ERR_NULL, RLSCAN_ERR_ALIAS. */
+int rlscan_stream_mix(void* dst, int64_t write_bytes, const void* src, int64_t read_bytes,
+                      int32_t reads, int32_t writes, hipStream_t stream);
 
 /* Diagnostics: waits in the look-back are bounded (a few seconds per
  * predecessor); a wait that reaches the bound is counted, its tile takes NaN

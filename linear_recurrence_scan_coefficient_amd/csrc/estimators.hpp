@@ -66,6 +66,8 @@ struct Geometry {
     int64_t tile_span;      // elements of memory per tile: the tile's capacity, or
                             // (packed mapping) the whole rows it holds, a multiple
                             // of 4 that can fall short of the capacity
+    int64_t xcd_run;        // packed, one tile per workgroup: runs of this many
+                            // consecutive tiles per XCD (xcd_tile); 0: tile = blockIdx
     double inv_T;           // 1.0 / T, for the row/time split of an index
 };
 
@@ -190,6 +192,21 @@ __device__ __forceinline__ T load_halo(const T* __restrict__ p, const ChunkPos& 
     return p[i < NT ? i : NT - 1];
 }
 
+// The value just above a reverse estimator's chunk (V_{t+1} of its top
+// element) is the first value of the chunk above it, which the previous
+// lane holds: chunks run downwards from lane 0.  Only lane 0 reads it from
+// memory, at load time (halo_load); the others take it from that lane once
+// every round's loads are in flight (halo_exchange, called from `steps`: an
+// exchange at load time would wait for the round's data before the next
+// round's loads are issued).  One load per wave instead of one per lane.
+__device__ __forceinline__ float halo_load(const float* __restrict__ p, const ChunkPos& q,
+                                           int64_t NT) {
+    return (threadIdx.x & (kWave - 1)) == 0 ? load_halo(p, q, NT) : 0.0f;
+}
+__device__ __forceinline__ float halo_exchange(float first, float lane0_value) {
+    return lane_before(first, threadIdx.x & (kWave - 1), lane0_value);
+}
+
 struct NoEpi {};
 
 // Shared episode logic of the reverse estimators: the flags of one chunk and
@@ -207,10 +224,13 @@ __device__ __forceinline__ void load_episode(const float* rewards, const F* term
                                              const float* bootstrap_value,
                                              const float* carry_in, const Geometry& geo,
                                              const ChunkPos& q, EpisodeChunk& c) {
-    // loaded with the chunk so that the row-end case costs no dependent load
+    // loaded with the chunk so that the row-end case costs no dependent load,
+    // and only by lanes whose chunk holds the end of its first row (the
+    // others issue no request)
     const int64_t nr = q.n0 < geo.N ? q.n0 : geo.N - 1;
-    c.boot = bootstrap_value != nullptr ? bootstrap_value[nr] : 0.0f;
-    c.carry = (CARRY && carry_in != nullptr) ? carry_in[nr] : 0.0f;
+    const bool first_row_ends = q.t0 >= geo.T - kChunk;
+    c.boot = (bootstrap_value != nullptr && first_row_ends) ? bootstrap_value[nr] : 0.0f;
+    c.carry = (CARRY && carry_in != nullptr && first_row_ends) ? carry_in[nr] : 0.0f;
     load4<VEC, FULL>(rewards, q, c.r);
     load4<VEC, FULL>(terminated, q, c.term);
     if constexpr (TRUNC) {
@@ -299,18 +319,19 @@ struct Gae {
                                         p.bootstrap_values, p.bootstrap_value, p.carry_in, geo,
                                         q, c.ep);
         load4<VEC, FULL>(p.values, q, c.v);
-        c.v_halo = load_halo(p.values, q, geo.NT);
+        c.v_halo = halo_load(p.values, q, geo.NT);
     }
     template <bool CARRY>
     __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
                                  const Chunk& c, S e[4], Epi&) {
         int64_t n = q.n0, t = q.t0;
         const bool continues = CARRY && p.carry_in != nullptr;
+        const float v_halo = halo_exchange(c.v[0], c.v_halo);
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             bool cut;
             const bool row_end = t == geo.T - 1;
-            const float v_next = j < kChunk - 1 ? c.v[j + 1] : c.v_halo;
+            const float v_next = j < kChunk - 1 ? c.v[j + 1] : v_halo;
             const float vh = successor_value(c.ep, j, row_end, j < q.valid,
                                              p.bootstrap_value, n, q.n0, v_next, continues, cut);
             e[j].a = cut ? 0.0f : p.gamma_lambda;
@@ -361,18 +382,19 @@ struct LambdaReturns {
                                         p.bootstrap_values, p.bootstrap_value, p.carry_in, geo,
                                         q, c.ep);
         load4<VEC, FULL>(p.values, q, c.v);
-        c.v_halo = load_halo(p.values, q, geo.NT);
+        c.v_halo = halo_load(p.values, q, geo.NT);
     }
     template <bool CARRY>
     __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
                                  const Chunk& c, S e[4], Epi&) {
         int64_t n = q.n0, t = q.t0;
         const bool continues = CARRY && p.carry_in != nullptr;
+        const float v_halo = halo_exchange(c.v[0], c.v_halo);
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             bool cut;
             const bool row_end = t == geo.T - 1;
-            const float v_next = j < kChunk - 1 ? c.v[j + 1] : c.v_halo;
+            const float v_next = j < kChunk - 1 ? c.v[j + 1] : v_halo;
             // vh is V_{t+1} on a step that is not a cut (V at t = T at a
             // continued row end)
             const float vh = successor_value(c.ep, j, row_end, j < q.valid,
@@ -508,18 +530,19 @@ struct Vtrace {
                                         q, c.ep);
         load4<VEC, FULL>(p.values, q, c.v);
         load4<VEC, FULL>(p.log_rhos, q, c.lr);
-        c.v_halo = load_halo(p.values, q, geo.NT);
+        c.v_halo = halo_load(p.values, q, geo.NT);
     }
     template <bool CARRY>
     __device__ __forceinline__ static void steps(const Params& p, const Geometry& geo, const ChunkPos& q,
                                  const Chunk& c, S e[4], Epi& epi) {
         int64_t n = q.n0, t = q.t0;
         const bool continues = CARRY && p.carry_in != nullptr;
+        const float v_halo = halo_exchange(c.v[0], c.v_halo);
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             bool cut;
             const bool row_end = t == geo.T - 1;
-            const float v_next = j < kChunk - 1 ? c.v[j + 1] : c.v_halo;
+            const float v_next = j < kChunk - 1 ? c.v[j + 1] : v_halo;
             const float vh = successor_value(c.ep, j, row_end, j < q.valid,
                                              p.bootstrap_value, n, q.n0, v_next, continues, cut);
             V ratio;
@@ -638,17 +661,16 @@ struct Retrace {
         load4<VEC, FULL>(p.actions, q, c.act);
         load4<VEC, FULL>(p.behaviour_probs, q, c.mu);
         // a_{t+1} and mu_{t+1} of the chunk's top element: element 0 of the
-        // next chunk up, held by the previous lane (lane 0 reads memory)
+        // next chunk up, held by the previous lane; lane 0 reads memory here,
+        // the exchange follows in `steps` (after the action-value loads are
+        // issued)
         const int lane = threadIdx.x & (kWave - 1);
-        int32_t act_up = 0;
-        float mu_up = 1.0f;
+        c.act_halo = 0;
+        c.mu_halo = 1.0f;
         if (lane == 0) {
-            act_up = load_halo(p.actions, q, geo.NT);
-            mu_up = load_halo(p.behaviour_probs, q, geo.NT);
+            c.act_halo = load_halo(p.actions, q, geo.NT);
+            c.mu_halo = load_halo(p.behaviour_probs, q, geo.NT);
         }
-        c.act_halo = static_cast<int32_t>(lane_before_u32(static_cast<uint32_t>(c.act[0]), lane,
-                                                          static_cast<uint32_t>(act_up)));
-        c.mu_halo = lane_before(c.mu[0], lane, mu_up);
         c.lds = stage;
         c.staged = false;
         if constexpr (kA > 0 && VEC && FULL && kStageFloats > 0) {
@@ -723,6 +745,10 @@ struct Retrace {
             }
         }
         const bool continues = CARRY && p.carry_in != nullptr;
+        const int lane = threadIdx.x & (kWave - 1);
+        const int32_t act_halo = static_cast<int32_t>(lane_before_u32(
+            static_cast<uint32_t>(c.act[0]), lane, static_cast<uint32_t>(c.act_halo)));
+        const float mu_halo = lane_before(c.mu[0], lane, c.mu_halo);
         int64_t n = q.n0, t = q.t0;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
@@ -730,8 +756,8 @@ struct Retrace {
             const bool row_end = t == geo.T - 1;
             const bool cut = term || c.ep.trunc[j] != 0.0f || (row_end && !continues);
             const bool edge = row_end && continues && !cut && j < q.valid;
-            int32_t a_next = j < kChunk - 1 ? c.act[j + 1] : c.act_halo;
-            float mu_next = j < kChunk - 1 ? c.mu[j + 1] : c.mu_halo;
+            int32_t a_next = j < kChunk - 1 ? c.act[j + 1] : act_halo;
+            float mu_next = j < kChunk - 1 ? c.mu[j + 1] : mu_halo;
             if (edge) {  // the next step lies in the chunk that follows
                 a_next = p.next_actions[n];
                 mu_next = p.next_mu[n];

@@ -187,6 +187,7 @@ int group(const rlscan_call* calls, int32_t count, hipStream_t stream) {
         a.count = k;
         for (int32_t j = k; j <= kGroupMax; ++j) a.first_block[j] = blocks;
         a.interleaved = (g_override.flags.load() & RLSCAN_FLAG_GROUP_INTERLEAVED) ? 1 : 0;
+        a.xcd_run = static_cast<int32_t>(group_xcd_run());
         // interleaved schedule: calls by ascending tile count; segment s runs
         // the calls order[s..k-1] for the tiles the shorter ones do not have
         for (int32_t j = 0; j < k; ++j) a.order[j] = j;

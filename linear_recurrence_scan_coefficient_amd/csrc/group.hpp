@@ -116,7 +116,7 @@ struct GroupArgs {
     int32_t seg_first[kGroupMax + 1];
     int32_t seg_tile0[kGroupMax];
     int32_t order[kGroupMax];  // call indices by ascending tile count
-    int32_t pad2;
+    int32_t xcd_run;           // > 0: workgroups take grid slots in XCD runs (xcd_tile)
     GroupEntry e[kGroupMax];
 };
 
@@ -172,12 +172,12 @@ __device__ __forceinline__ void group_tile(kernarg_u32* entry, uint64_t tile, ch
     lds_float* stage = (lds_float*)(lds + group_lds_offset_stage<E>(W));
     lds_float* ostage = (lds_float*)(lds + group_lds_offset_ostage<E>(W));
     const LookbackArgs lb{};
-    if (tile_is_full<E, 1, W>(geo, tile))
-        scan_tile<E, 1, W, false, true, true, false>(p, geo, lb, tile, sm_wave, sm_carry, stage,
-                                                     ostage);
+    if (tile_is_full<E, 1, W, true>(geo, tile))
+        scan_tile<E, 1, W, false, true, true, false, true>(p, geo, lb, tile, sm_wave, sm_carry,
+                                                           stage, ostage);
     else
-        scan_tile<E, 1, W, false, true, false, false>(p, geo, lb, tile, sm_wave, sm_carry, stage,
-                                                      ostage);
+        scan_tile<E, 1, W, false, true, false, false, true>(p, geo, lb, tile, sm_wave, sm_carry,
+                                                            stage, ostage);
 }
 
 template <class E, int W, bool kWide>
@@ -200,7 +200,12 @@ template <int W, bool kWide>
 __global__ __launch_bounds__(kWave * W) void group_kernel(const GroupArgs args) {
     extern __shared__ __attribute__((aligned(16))) char group_lds[];
     kernarg_u32* base = (kernarg_u32*)__builtin_amdgcn_kernarg_segment_ptr();
-    const int64_t b = static_cast<int64_t>(blockIdx.x);
+    const int64_t b =
+        args.xcd_run > 0
+            ? static_cast<int64_t>(xcd_tile(blockIdx.x,
+                                            static_cast<uint64_t>(args.first_block[kGroupMax]),
+                                            static_cast<uint64_t>(args.xcd_run)))
+            : static_cast<int64_t>(blockIdx.x);
     int i = 0;
     uint64_t tile = 0;
     if (args.interleaved) {

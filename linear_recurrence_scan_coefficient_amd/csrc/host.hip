@@ -213,6 +213,25 @@ Plan make_plan(int est, int64_t N, int64_t T, bool vec, bool carry) {
     return pl;
 }
 
+// The library's choice of XCD runs (xcd_tile): runs of 16 tiles when a
+// tile's span is not a multiple of 128 bytes (32 elements), so that most
+// lines shared by neighbouring tiles stay in one L2; else tile = blockIdx.
+// Measured on MI355X (cold inputs): runs of 16 made such calls 1-5 % faster
+// (4200 x 125: prefix sum 4.34 -> 4.14 us; 4096 x 100: Retrace 8.78 -> 8.43
+// us), one contiguous run per XCD 5-9 % on another box; on aligned calls
+// (4096 x 128) runs cost up to 5 %, and one contiguous run per XCD made the
+// 2^20 x 32 calls 13 % and the grouped production step 50 % slower.
+int64_t xcd_run(int64_t tiles, int64_t span) {
+    const int64_t o = g_override.xcd_run.load();
+    if (o >= 0) return o;
+    return (span % 32 != 0 && tiles > 1) ? 16 : 0;
+}
+
+int64_t group_xcd_run() {
+    const int64_t o = g_override.xcd_run.load();
+    return o >= 0 ? o : 0;
+}
+
 // An empty kernel: the launch floor that a scan launch of the same grid and
 // workgroup size cannot go below.
 __global__ __launch_bounds__(1024) void empty_kernel() {}
@@ -235,6 +254,37 @@ __global__ __launch_bounds__(kCopyThreads) void copy_kernel(const f32x4* __restr
     for (int u = 0; u < kCopyUnroll; ++u) {
         const int64_t i = base + static_cast<int64_t>(u) * kCopyThreads;
         if (i < n) __builtin_nontemporal_store(v[u], dst + i);
+    }
+}
+
+// A streaming kernel with a read:write mix: each thread reads `reads`
+// 16-byte words of `src` (at most kMixMaxReads) and then writes `writes`
+// words of `dst` (at most kMixMaxWrites), every written word the sum of the
+// thread's read words -- all reads are used before any write, as in a scan
+// kernel.  Workgroup b reads the contiguous words [b*256*reads, ...) and
+// writes [b*256*writes, ...); accesses are 16-byte and non-temporal.
+constexpr int kMixThreads = 256;
+constexpr int kMixMaxReads = 16;
+constexpr int kMixMaxWrites = 4;
+__global__ __launch_bounds__(kMixThreads) void mix_kernel(const f32x4* __restrict__ src,
+                                                          int64_t nr, f32x4* __restrict__ dst,
+                                                          int64_t nw, int reads, int writes) {
+    const int64_t rb = static_cast<int64_t>(blockIdx.x) * kMixThreads * reads + threadIdx.x;
+    f32x4 v[kMixMaxReads];
+#pragma unroll
+    for (int u = 0; u < kMixMaxReads; ++u) {
+        const int64_t i = rb + static_cast<int64_t>(u) * kMixThreads;
+        v[u] = 0.0f;
+        if (u < reads && i < nr) v[u] = __builtin_nontemporal_load(src + i);
+    }
+    f32x4 acc = v[0];
+#pragma unroll
+    for (int u = 1; u < kMixMaxReads; ++u) acc += v[u];
+    const int64_t wb = static_cast<int64_t>(blockIdx.x) * kMixThreads * writes + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < kMixMaxWrites; ++u) {
+        const int64_t i = wb + static_cast<int64_t>(u) * kMixThreads;
+        if (u < writes && i < nw) __builtin_nontemporal_store(acc, dst + i);
     }
 }
 
@@ -338,6 +388,38 @@ int rlscan_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t st
 
 // Waits for each device that holds look-back scratch (not for the streams
 // the scratch was keyed by: the caller may have destroyed them since).
+int rlscan_stream_mix(void* dst, int64_t write_bytes, const void* src, int64_t read_bytes,
+                      int32_t reads, int32_t writes, hipStream_t stream) {
+    if (read_bytes < 0 || write_bytes < 0 || (read_bytes & 15) != 0 || (write_bytes & 15) != 0)
+        return RLSCAN_ERR_SHAPE;
+    if (reads < 1 || reads > kMixMaxReads || writes < 1 || writes > kMixMaxWrites)
+        return RLSCAN_ERR_PARAM;
+    if (read_bytes == 0 && write_bytes == 0) return RLSCAN_OK;
+    if ((read_bytes > 0 && src == nullptr) || (write_bytes > 0 && dst == nullptr))
+        return RLSCAN_ERR_NULL;
+    if ((src != nullptr && !aligned16(src)) || (dst != nullptr && !aligned16(dst)))
+        return RLSCAN_ERR_PARAM;
+    const uintptr_t d = reinterpret_cast<uintptr_t>(dst), s = reinterpret_cast<uintptr_t>(src);
+    if (read_bytes > 0 && write_bytes > 0 && d < s + static_cast<uintptr_t>(read_bytes) &&
+        s < d + static_cast<uintptr_t>(write_bytes))
+        return RLSCAN_ERR_ALIAS;
+    const int64_t nr = read_bytes / 16, nw = write_bytes / 16;
+    const int64_t gr = (nr + int64_t(kMixThreads) * reads - 1) / (int64_t(kMixThreads) * reads);
+    const int64_t gw = (nw + int64_t(kMixThreads) * writes - 1) / (int64_t(kMixThreads) * writes);
+    const int64_t grid = gr > gw ? gr : gw;
+    if (grid > kMaxGrid) return RLSCAN_ERR_SHAPE;
+    hipLaunchKernelGGL(mix_kernel, dim3(static_cast<unsigned>(grid)), dim3(kMixThreads), 0,
+                       stream, static_cast<const f32x4*>(src), nr, static_cast<f32x4*>(dst), nw,
+                       reads, writes);
+    return hipGetLastError() == hipSuccess ? RLSCAN_OK : RLSCAN_ERR_HIP;
+}
+
+int rlscan_set_xcd_run(int64_t run) {
+    if (run < -1 || run > (int64_t(1) << 20)) return RLSCAN_ERR_PARAM;
+    g_override.xcd_run.store(run);
+    return RLSCAN_OK;
+}
+
 int rlscan_lookback_timeouts(uint64_t* count) {
     if (count == nullptr) return RLSCAN_ERR_NULL;
     *count = 0;

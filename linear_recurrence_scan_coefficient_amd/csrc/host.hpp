@@ -28,8 +28,15 @@ struct LaunchOverride {
     std::atomic<int> waves{0};
     std::atomic<int64_t> grid_cap{0};
     std::atomic<int> flags{0};  // RLSCAN_FLAG_* bits
+    std::atomic<int64_t> xcd_run{-1};  // -1: the library's choice
 };
 extern LaunchOverride g_override;
+
+// Run length of the XCD tile order (xcd_tile) of packed launches with
+// `tiles` tiles whose span is `span` elements, and of grouped launches
+// (0: tile = blockIdx).
+int64_t xcd_run(int64_t tiles, int64_t span);
+int64_t group_xcd_run();
 
 struct Scratch {
     std::mutex m;
@@ -157,17 +164,21 @@ inline bool flags_aligned(const F* p) {
     return (reinterpret_cast<uintptr_t>(p) % (sizeof(F) * 4)) == 0;  // NULL is aligned
 }
 
+// Three builds per shape: look-back; packed with tiles that span their
+// whole capacity; packed with tiles of whole rows that fall short of it.
 template <class E, int R, int W, bool VEC, bool CARRY>
 hipError_t launch_r(const typename E::Params& p, const Geometry& geo, const LookbackArgs& lb,
                     const Plan& pl, hipStream_t stream) {
-    const bool lookback = pl.mapping == RLSCAN_MAP_LOOKBACK;
     const dim3 grid(static_cast<unsigned>(geo.grid)), block(kWave * W);
-    if (lookback)
-        hipLaunchKernelGGL((scan_kernel<E, R, W, true, VEC, CARRY>), grid, block, 0, stream, p,
-                           geo, lb);
+    if (pl.mapping == RLSCAN_MAP_LOOKBACK)
+        hipLaunchKernelGGL((scan_kernel<E, R, W, true, VEC, CARRY, false>), grid, block, 0, stream,
+                           p, geo, lb);
+    else if (pl.tile_span != pl.tile_elems)
+        hipLaunchKernelGGL((scan_kernel<E, R, W, false, VEC, CARRY, true>), grid, block, 0, stream,
+                           p, geo, lb);
     else
-        hipLaunchKernelGGL((scan_kernel<E, R, W, false, VEC, CARRY>), grid, block, 0, stream, p,
-                           geo, lb);
+        hipLaunchKernelGGL((scan_kernel<E, R, W, false, VEC, CARRY, false>), grid, block, 0,
+                           stream, p, geo, lb);
     return hipGetLastError();
 }
 
@@ -257,6 +268,7 @@ int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream,
     geo.num_tiles = pl.tiles;
     geo.grid = pl.grid;
     geo.tile_span = pl.tile_span;
+    geo.xcd_run = pl.mapping == RLSCAN_MAP_PACKED ? xcd_run(pl.tiles, pl.tile_span) : 0;
     geo.inv_T = 1.0 / static_cast<double>(T);
     LookbackArgs lb{};
     if (t_group != nullptr) {  // collecting for a grouped launch: no side effects

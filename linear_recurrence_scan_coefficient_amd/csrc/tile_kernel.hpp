@@ -75,40 +75,73 @@ inline bool packed_layout(int64_t N, int64_t T, int64_t cap, int64_t& span, int6
 // no elements: they are placed at the span's first element, so that every
 // value an estimator preloads for a chunk (bootstrap value, halo, carry)
 // stays in bounds, and take the identity step.
-template <class E, int R, int W>
+// kFixed: the tile spans its whole capacity -- FULL tiles (tile_is_full) and
+// every tile of the look-back mapping -- so positions use the compile-time
+// tile size.  With a runtime span the compiler kept more of the addresses
+// live across the scan: the prefix sum's four-round look-back kernel went
+// from 94 to 119 VGPRs and lost a wave per SIMD.
+template <class E, int R, int W, bool kFixed>
 __device__ __forceinline__ int64_t chunk_base(const Geometry& geo, uint64_t tile, int wave, int r,
                                               int lane, bool& inside) {
     const int64_t mem_tile = E::kReverse ? geo.num_tiles - 1 - static_cast<int64_t>(tile)
                                          : static_cast<int64_t>(tile);
     const int c = (wave * R + r) * kWave + lane;  // chunk index in scan order
-    const int64_t off = E::kReverse ? geo.tile_span - static_cast<int64_t>(kChunk) * (c + 1)
-                                    : static_cast<int64_t>(kChunk) * c;
-    inside = off >= 0 && off < geo.tile_span;
-    return mem_tile * geo.tile_span + (inside ? off : 0);
+    if constexpr (kFixed) {
+        constexpr int64_t kTile = tile_elems<R, W>();
+        inside = true;
+        const int64_t off = E::kReverse ? kTile - static_cast<int64_t>(kChunk) * (c + 1)
+                                        : static_cast<int64_t>(kChunk) * c;
+        return mem_tile * kTile + off;
+    } else {
+        const int64_t off = E::kReverse ? geo.tile_span - static_cast<int64_t>(kChunk) * (c + 1)
+                                        : static_cast<int64_t>(kChunk) * c;
+        inside = off >= 0 && off < geo.tile_span;
+        return mem_tile * geo.tile_span + (inside ? off : 0);
+    }
 }
 
 // Lane `lane`'s chunk in round r of wave `wave`: elements that lie in the
 // tile's span and below N*T are valid.
-template <class E, int R, int W>
+template <class E, int R, int W, bool kFixed>
 __device__ __forceinline__ ChunkPos chunk_at(const Geometry& geo, uint64_t tile, int wave, int r,
                                              int lane) {
     bool inside;
-    ChunkPos q = chunk_pos(chunk_base<E, R, W>(geo, tile, wave, r, lane, inside), geo);
-    if (!inside) q.valid = 0;
+    ChunkPos q = chunk_pos(chunk_base<E, R, W, kFixed>(geo, tile, wave, r, lane, inside), geo);
+    if (!kFixed && !inside) q.valid = 0;
     return q;
 }
 
-// Whether every element of the tile lies in its span and below N*T.
-template <class E, int R, int W>
+// Whether every element of the tile lies in its span and below N*T
+// (SPAN: the span may fall short of the tile's capacity).
+template <class E, int R, int W, bool SPAN>
 __device__ __forceinline__ bool tile_is_full(const Geometry& geo, uint64_t tile) {
     constexpr int64_t kTile = tile_elems<R, W>();
     const int64_t mem_tile = E::kReverse ? geo.num_tiles - 1 - static_cast<int64_t>(tile)
                                          : static_cast<int64_t>(tile);
-    return geo.tile_span == kTile && (mem_tile + 1) * kTile <= geo.NT;
+    return (!SPAN || geo.tile_span == kTile) && (mem_tile + 1) * kTile <= geo.NT;
+}
+
+// The dispatcher hands workgroups to the XCDs round-robin: workgroup b runs
+// on XCD b % kXcds (each with its own L2).  For launches whose tiles are
+// independent (packed, one tile per workgroup) the order below gives each
+// XCD runs of `run` consecutive tiles instead of every kXcds-th tile: the
+// tiles are cut into groups of kXcds*run, and in each group XCD x takes the
+// x-th run.  A cache line shared by two neighbouring tiles (whole rows
+// whose span is not a multiple of 128 bytes) is then mostly fetched and
+// written back through one L2.  A group cut short by the end of the grid
+// keeps tile = b, so the order is a permutation of [0, tiles).
+constexpr uint64_t kXcds = 8;
+
+__device__ __forceinline__ uint64_t xcd_tile(uint64_t b, uint64_t tiles, uint64_t run) {
+    const uint64_t group = kXcds * run;
+    if (b >= tiles / group * group) return b;
+    const uint64_t x = b % kXcds, i = b / kXcds;
+    return (i / run) * group + x * run + i % run;
 }
 
 // 1. loads, all rounds first so every load of the tile is in flight
-template <class E, int R, int W, bool VEC, bool FULL, bool CARRY>
+// (kFixed: the tile spans its whole capacity, see chunk_base)
+template <class E, int R, int W, bool VEC, bool FULL, bool CARRY, bool kFixed>
 __device__ __forceinline__ void load_tile(const typename E::Params& p, const Geometry& geo,
                                           uint64_t tile, typename E::Chunk (&ch)[R],
                                           ChunkPos (&pos)[R], lds_float* stage) {
@@ -116,7 +149,7 @@ __device__ __forceinline__ void load_tile(const typename E::Params& p, const Geo
     const int wave = threadIdx.x / kWave;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        pos[r] = chunk_at<E, R, W>(geo, tile, wave, r, lane);
+        pos[r] = chunk_at<E, R, W, kFixed>(geo, tile, wave, r, lane);
         E::template load<VEC, FULL, CARRY>(p, geo, pos[r], ch[r],
                                     stage + (wave * R + r) * E::kStageFloats);
     }
@@ -197,7 +230,7 @@ __device__ __forceinline__ void tile_carry(const LookbackArgs& lb, uint64_t tile
 }
 
 // 6. replay each lane's steps from its entering state and store
-template <class E, int R, int W, bool VEC, bool FULL, bool CARRY, class A>
+template <class E, int R, int W, bool VEC, bool FULL, bool CARRY, bool kFixed, class A>
 __device__ __forceinline__ void replay_store(const typename E::Params& p, const Geometry& geo,
                                              uint64_t tile,
                                              const typename E::S (&e)[R][kChunk],
@@ -223,9 +256,13 @@ __device__ __forceinline__ void replay_store(const typename E::Params& p, const 
         }
         ChunkPos q;
         bool inside;
-        q.g0 = chunk_base<E, R, W>(geo, tile, wave, r, lane, inside);
+        q.g0 = chunk_base<E, R, W, kFixed>(geo, tile, wave, r, lane, inside);
         const int64_t rem = geo.NT - q.g0;
-        q.valid = (!inside || rem <= 0) ? 0 : (rem >= kChunk ? kChunk : static_cast<int>(rem));
+        // (the compile-time kFixed test keeps the compiler from carrying
+        // `inside` where it is always true: 8 more VGPRs in the prefix sum's
+        // four-round look-back kernel otherwise)
+        const bool outside = !kFixed && !inside;
+        q.valid = (outside || rem <= 0) ? 0 : (rem >= kChunk ? kChunk : static_cast<int>(rem));
         E::template store<VEC, FULL>(p, q, epi[r], out, before,
                                      ostage + wave * E::kOutStageFloats);
         if (CARRY && p.carry_out != nullptr) {
@@ -243,7 +280,10 @@ __device__ __forceinline__ void replay_store(const typename E::Params& p, const 
     }
 }
 
-template <class E, int R, int W, bool LOOKBACK, bool VEC, bool FULL, bool CARRY>
+// SPAN: the tile's span may fall short of its capacity (a packed mapping of
+// whole rows that do not fill the tile); kernels built without it compute
+// chunk positions from the compile-time tile size throughout.
+template <class E, int R, int W, bool LOOKBACK, bool VEC, bool FULL, bool CARRY, bool SPAN>
 __device__ __forceinline__ void scan_tile(const typename E::Params& p, const Geometry& geo,
                                           const LookbackArgs& lb, uint64_t tile,
                                           typename AggOf<typename E::S>::type* sm_wave,
@@ -253,9 +293,10 @@ __device__ __forceinline__ void scan_tile(const typename E::Params& p, const Geo
     using A = typename AggOf<S>::type;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
+    constexpr bool kFixed = FULL || !SPAN;
     typename E::Chunk ch[R];
     ChunkPos pos[R];
-    load_tile<E, R, W, VEC, FULL, CARRY>(p, geo, tile, ch, pos, stage);
+    load_tile<E, R, W, VEC, FULL, CARRY, kFixed>(p, geo, tile, ch, pos, stage);
     S e[R][kChunk];
     typename E::Epi epi[R];
     build_steps<E, R, FULL, CARRY>(p, geo, ch, pos, e, epi);
@@ -273,15 +314,17 @@ __device__ __forceinline__ void scan_tile(const typename E::Params& p, const Geo
         cuts_chain(e[0][0]) && !E::reads_before(epi[0], E::kReverse ? kChunk - 1 : 0);
     tile_carry<E, W, LOOKBACK>(lb, tile, sm_wave, first_free, sm_carry);
     __syncthreads();
-    replay_store<E, R, W, VEC, FULL, CARRY>(p, geo, tile, e, epi, incl, wpre, *sm_carry,
-                                             ostage);
+    replay_store<E, R, W, VEC, FULL, CARRY, kFixed>(p, geo, tile, e, epi, incl, wpre, *sm_carry,
+                                                     ostage);
 }
 
-// One tile per workgroup (or, grid-capped, a loop over tiles).
-template <class E, int R, int W, bool LOOKBACK, bool VEC, bool CARRY>
+// One tile per workgroup (or, grid-capped, a loop over tiles).  SPAN (packed
+// only): tiles of whole rows that may fall short of the tile's capacity.
+template <class E, int R, int W, bool LOOKBACK, bool VEC, bool CARRY, bool SPAN>
 __global__ __launch_bounds__(kWave * W) void scan_kernel(const typename E::Params p,
                                                         const Geometry geo,
                                                         const LookbackArgs lb) {
+    static_assert(!(SPAN && LOOKBACK), "look-back tiles span their whole capacity");
     using A = typename AggOf<typename E::S>::type;
     using V = typename E::V;
     __shared__ A sm_wave[W];
@@ -297,6 +340,9 @@ __global__ __launch_bounds__(kWave * W) void scan_kernel(const typename E::Param
     lds_float* ostage = (lds_float*)sm_out;
     const bool one_tile_per_group = geo.grid >= geo.num_tiles;
     uint64_t tile = blockIdx.x;
+    if (!LOOKBACK && one_tile_per_group && geo.xcd_run > 0)
+        tile = xcd_tile(blockIdx.x, static_cast<uint64_t>(geo.num_tiles),
+                        static_cast<uint64_t>(geo.xcd_run));
     for (;;) {
         if constexpr (LOOKBACK) {
             if (lb.use_tickets) {
@@ -307,12 +353,12 @@ __global__ __launch_bounds__(kWave * W) void scan_kernel(const typename E::Param
         }
         if (tile >= static_cast<uint64_t>(geo.num_tiles)) break;
         // only the tile holding the end of the data needs bounds checks
-        if (tile_is_full<E, R, W>(geo, tile))
-            scan_tile<E, R, W, LOOKBACK, VEC, true, CARRY>(p, geo, lb, tile, sm_wave, &sm_carry,
-                                                           stage, ostage);
+        if (tile_is_full<E, R, W, SPAN>(geo, tile))
+            scan_tile<E, R, W, LOOKBACK, VEC, true, CARRY, SPAN>(p, geo, lb, tile, sm_wave,
+                                                                 &sm_carry, stage, ostage);
         else
-            scan_tile<E, R, W, LOOKBACK, VEC, false, CARRY>(p, geo, lb, tile, sm_wave, &sm_carry,
-                                                            stage, ostage);
+            scan_tile<E, R, W, LOOKBACK, VEC, false, CARRY, SPAN>(p, geo, lb, tile, sm_wave,
+                                                                  &sm_carry, stage, ostage);
         if (one_tile_per_group) break;
         if (!LOOKBACK || !lb.use_tickets) tile += gridDim.x;
         __syncthreads();  // LDS is reused by the next tile

@@ -54,7 +54,8 @@ EXPORTED = (
     "rlscan_vtrace_ex", "rlscan_episodic_prefix_sum_f32",
     "rlscan_gae_u8", "rlscan_lambda_returns_u8", "rlscan_discounted_returns_u8",
     "rlscan_vtrace_u8", "rlscan_retrace_u8", "rlscan_eligibility_traces_u8",
-    "rlscan_episodic_prefix_sum_u8", "rlscan_group", "rlscan_gae_noalloc",
+    "rlscan_episodic_prefix_sum_u8", "rlscan_group", "rlscan_gae_noalloc", "rlscan_stream_mix",
+    "rlscan_set_xcd_run",
 )
 
 
@@ -149,6 +150,10 @@ def _declare(lib):
     lib.rlscan_launch_floor.restype = ctypes.c_int
     lib.rlscan_stream_copy.argtypes = [_vp, _vp, _i64, _vp]
     lib.rlscan_stream_copy.restype = ctypes.c_int
+    lib.rlscan_set_xcd_run.argtypes = [_i64]
+    lib.rlscan_set_xcd_run.restype = ctypes.c_int
+    lib.rlscan_stream_mix.argtypes = [_vp, _i64, _vp, _i64, ctypes.c_int32, ctypes.c_int32, _vp]
+    lib.rlscan_stream_mix.restype = ctypes.c_int
 
 
 def library(path: str = LIB_PATH):
@@ -560,6 +565,12 @@ def rlscan_set_launch_override(mapping=MAP_AUTO, rounds=0, waves=0, grid_cap=0, 
                                                 int(flags)))
 
 
+def rlscan_set_xcd_run(run=-1):
+    """Tiles per XCD run of packed and grouped launches (-1: the library's
+    choice, 0: tile = workgroup index)."""
+    _check(library().rlscan_set_xcd_run(int(run)))
+
+
 def rlscan_lookback_timeouts() -> int:
     n = ctypes.c_uint64()
     _check(library().rlscan_lookback_timeouts(ctypes.byref(n)))
@@ -579,3 +590,20 @@ def rlscan_stream_copy(dst, src, nbytes=None, stream=None):
         raise RlscanError(RLSCAN_ERR_SHAPE, "rlscan_stream_copy: nbytes exceeds a tensor")
     _check(library().rlscan_stream_copy(dst.data_ptr(), src.data_ptr(), int(nbytes),
                                         _stream(stream)))
+
+
+def rlscan_stream_mix(dst, src, write_bytes=None, read_bytes=None, reads=1, writes=1,
+                      stream=None):
+    """Streaming kernel reading `read_bytes` of `src` and writing
+    `write_bytes` of `dst` (defaults: whole tensors), `reads` and `writes`
+    16-byte words per thread."""
+    if read_bytes is None:
+        read_bytes = src.numel() * src.element_size()
+    if write_bytes is None:
+        write_bytes = dst.numel() * dst.element_size()
+    if read_bytes > src.numel() * src.element_size() or \
+            write_bytes > dst.numel() * dst.element_size():
+        raise RlscanError(RLSCAN_ERR_SHAPE, "rlscan_stream_mix: a size exceeds its tensor")
+    _check(library().rlscan_stream_mix(dst.data_ptr(), int(write_bytes), src.data_ptr(),
+                                       int(read_bytes), int(reads), int(writes),
+                                       _stream(stream)))

@@ -222,6 +222,27 @@ def test_stream_copy_argument_checks(lib):
     assert f(P[0], P[0] + 32, 64, None) == ALIAS
 
 
+def test_xcd_run_override_checks(lib):
+    f = lib.rlscan_set_xcd_run
+    assert f(-2) == PARAM and f((1 << 20) + 1) == PARAM
+    assert f(0) == OK and f(16) == OK and f(1 << 20) == OK and f(-1) == OK
+
+
+def test_stream_mix_argument_checks(lib):
+    f = lib.rlscan_stream_mix
+    assert f(P[1], 0, P[0], 0, 1, 1, None) == OK          # nothing to move
+    assert f(P[1], 16, P[0], 15, 1, 1, None) == SHAPE     # not a multiple of 16
+    assert f(P[1], -16, P[0], 16, 1, 1, None) == SHAPE
+    assert f(P[1], 64, P[0], 64, 0, 1, None) == PARAM     # word counts out of range
+    assert f(P[1], 64, P[0], 64, 17, 1, None) == PARAM
+    assert f(P[1], 64, P[0], 64, 1, 5, None) == PARAM
+    assert f(None, 64, P[0], 64, 1, 1, None) == NULL
+    assert f(P[1], 64, None, 64, 1, 1, None) == NULL
+    assert f(P[1] + 4, 64, P[0], 64, 1, 1, None) == PARAM  # misaligned
+    assert f(P[0] + 32, 64, P[0], 64, 1, 1, None) == ALIAS  # overlapping ranges
+    assert f(P[1], 1 << 44, P[0], 16, 1, 1, None) == SHAPE  # grid beyond 2^23 workgroups
+
+
 def test_launch_floor_argument_checks(lib):
     """Refused on the host before any launch: a grid outside [1, 2^23) or a
     workgroup size that is not a multiple of 64 from 64 to 1024."""

@@ -28,8 +28,10 @@ REVERSE_WITH_TRUNC = ("gae", "lambda_returns", "discounted_returns", "vtrace")
 @pytest.fixture(autouse=True)
 def _reset_override():
     rlscan.rlscan_set_launch_override()
+    rlscan.rlscan_set_xcd_run(-1)
     yield
     rlscan.rlscan_set_launch_override()
+    rlscan.rlscan_set_xcd_run(-1)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -325,6 +327,26 @@ def test_vtrace_expanding_traces_options_carry_and_group():
                   "grouped float32-form vtrace")
 
 
+@pytest.mark.parametrize("reads,writes", [(1, 1), (3, 1), (12, 4), (16, 1), (2, 3)])
+def test_stream_mix_kernel(reads, writes):
+    """The bandwidth-reference kernel: thread t of workgroup b writes the sum
+    of its read words (b*256*reads + u*256 + t) to its write words.  Small
+    integer values, so every float32 sum is exact in any order; a ragged
+    tail on both sides."""
+    g = 37  # workgroups
+    nr, nw = g * 256 * reads - 5, g * 256 * writes - 3  # 16-byte words
+    src = torch.randint(-8, 9, (g * 256 * reads, 4), device="cuda").float()
+    src[nr:] = 0  # past read_bytes: read as zero by the kernel
+    dst = torch.full((g * 256 * writes, 4), -1.0, device="cuda")
+    rlscan.rlscan_stream_mix(dst, src, write_bytes=nw * 16, read_bytes=nr * 16, reads=reads,
+                             writes=writes)
+    torch.cuda.synchronize()
+    acc = src.view(g, reads, 256, 4).sum(1)  # [g, 256, 4]
+    want = acc[:, None].expand(g, writes, 256, 4).reshape(-1, 4).clone()
+    want[nw:] = -1.0
+    assert torch.equal(dst, want)
+
+
 @pytest.mark.parametrize("estimator", ESTIMATORS)
 def test_empty_inputs(estimator):
     for N, T in ((0, 5), (5, 0), (0, 0)):
@@ -460,6 +482,34 @@ def test_packed_rows_that_do_not_divide_the_tile(estimator, shape):
     assert_parity(got, oracle_outputs(estimator, inputs, w), f"{estimator} {N}x{T} packed")
     for k, v in outs[1].items():  # no look-back: deterministic
         assert torch.equal(v, outs[0][k]), k
+
+
+@pytest.mark.parametrize("run", [0, 1, 3, 16, 1 << 20])
+@pytest.mark.parametrize("shape", [(4096, 100), (333, 128), (64, 8192)],
+                         ids=["4096x100", "333x128", "64x8192"])
+def test_xcd_tile_order(run, shape):
+    """Packed and grouped launches with workgroups taking tiles in runs per
+    XCD (a permutation of the tiles; the last, short group of runs keeps
+    tile = workgroup index); look-back launches ignore the order."""
+    N, T = shape
+    rlscan.rlscan_set_xcd_run(run)
+    for est in ("gae", "episodic_prefix_sum", "retrace"):
+        w, inputs = case(est, N, T, seed=run % 97 + N)
+        check(est, w, inputs, f"xcd run {run}")
+    if T <= 128:
+        w = workloads.custom(N, T, gamma=0.99, lam=0.95, term_p=0.01, done_p=0.02)
+        host = {e: workloads.inputs_for(e, w, 5) for e in ESTIMATORS}
+        dev = {e: device.upload(host[e]) for e in ESTIMATORS}
+        outs = {e: device.alloc_outputs(e, N, T) for e in ESTIMATORS}
+        rlscan.rlscan_group([rlscan.GroupCall(e, tuple(dev[e].get(k) for k in
+                                                       device.INPUT_ORDER[e]),
+                                              tuple(outs[e].values()), gamma=w.gamma,
+                                              lam=1.0 if e == "vtrace" else w.lam)
+                             for e in ESTIMATORS])
+        torch.cuda.synchronize()
+        for e in ESTIMATORS:
+            assert_parity({k: v.cpu().numpy() for k, v in outs[e].items()},
+                          oracle_outputs(e, host[e], w), f"grouped {e} xcd run {run}")
 
 
 @pytest.mark.parametrize("estimator", ESTIMATORS)
