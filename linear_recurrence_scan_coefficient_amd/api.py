@@ -135,53 +135,92 @@ def _submit(estimator, ins, outs, params, alone, stream, carry, extra=()):
         _on_stream(alone, stream, (*ins, *outs, *extra))
 
 
-def _device_tensor(t, name, dtype=torch.float32, flag=False):
-    if t is None:
-        return None
+# ------------------------------------------------------------------ marshalling
+# One pass over each tensor: device, dtype, shape, contiguity; then the C
+# entry point is called with raw pointers.  (The binding module rlscan.py
+# checks the same things again; these calls skip that second pass: it cost
+# about as much as the kernel of a 4096 x 128 call.)
+_F32 = torch.float32
+_I32 = torch.int32
+_BYTE = (torch.bool, torch.uint8)
+_clib = None
+
+
+def _lib():
+    global _clib
+    if _clib is None:
+        _clib = rlscan.library()
+    return _clib
+
+
+def _check(rc):
+    if rc != rlscan.RLSCAN_OK:
+        raise rlscan.RlscanError(rc, rlscan.status_string(rc))
+
+
+def _gpu(t, name):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU (got device {t.device}); rlscan has no "
                          "CPU path")
-    if t.dtype != dtype:
-        if not flag:
-            raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
-        t = t.to(dtype)  # a flag: any dtype, set iff nonzero
-    return t.contiguous()
+    return t
 
 
-_BYTE = (torch.bool, torch.uint8)
+def _tensor(t, name, shape, dtype=_F32):
+    """A device tensor of `dtype` and `shape`, made contiguous; None stays
+    None."""
+    if t is None:
+        return None
+    _gpu(t, name)
+    if t.dtype is not dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.shape != shape:
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t if t.is_contiguous() else t.contiguous()
 
 
-def _flags(**flags):
-    """The call's flag tensors, all float32 or all one-byte (bool / uint8)."""
-    given = {k: t for k, t in flags.items() if t is not None}
-    for k, t in given.items():
-        if not isinstance(t, torch.Tensor):
-            raise TypeError(f"{k} must be a torch.Tensor")
-        if t.device.type != "cuda":
-            raise ValueError(f"{k} must be on the GPU (got device {t.device}); rlscan has no "
-                             "CPU path")
-    def kind(t):
-        return "float32" if t.dtype == torch.float32 else ("byte" if t.dtype in _BYTE else "other")
-
-    kinds = {kind(t) for t in given.values()}
-    if kinds in ({"float32"}, {"byte"}):
-        out = {k: t.contiguous() for k, t in given.items()}
-    else:  # any other dtype, or a mix: one byte per flag
-        out = {k: (t if t.dtype in _BYTE else t != 0).contiguous() for k, t in given.items()}
-    return [out.get(k) for k in flags]
-
-
-def _carry_out(wanted, N, device, dtype=torch.float32):
-    return torch.empty((N,), dtype=dtype, device=device) if wanted else None
-
-
-def _check_2d(t, name):
+def _rows(t, name, dtype=_F32):
+    """The first [num_envs, seq_len] tensor of a call: its shape sets N, T."""
+    _gpu(t, name)
     if t.dim() != 2:
         raise ValueError(f"{name} must be a [num_envs, seq_len] tensor, got shape "
                          f"{tuple(t.shape)}")
-    return t.shape
+    return _tensor(t, name, t.shape, dtype)
+
+
+def _flags(shape, *named):
+    """The call's flag tensors (name, tensor pairs), all float32 or all one
+    byte (bool / uint8): as given when they already are, else each turned
+    into bool (set iff != 0).  Returns (tensors, one_byte)."""
+    given = [(n, t) for n, t in named if t is not None]
+    for n, t in given:
+        _gpu(t, n)
+        if t.shape != shape:
+            raise ValueError(f"{n} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if all(t.dtype is _F32 for _, t in given):
+        byte = False
+    elif all(t.dtype in _BYTE for _, t in given):
+        byte = True
+    else:  # any other dtype, or a mix: one byte per flag
+        given = [(n, t if t.dtype in _BYTE else t != 0) for n, t in given]
+        byte = True
+    out = dict((n, t if t.is_contiguous() else t.contiguous()) for n, t in given)
+    return [out.get(n) for n, _ in named], byte
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def _raw_stream(stream, t):
+    """The HIP stream handle of `stream` (None: the current stream of t's
+    device)."""
+    if stream is None:
+        return torch._C._cuda_getCurrentRawStream(t.get_device())
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
 
 
 def compute_gae(rewards, values, terminateds, gamma=0.99, lambda_=0.95, *,
@@ -191,18 +230,26 @@ def compute_gae(rewards, values, terminateds, gamma=0.99, lambda_=0.95, *,
     (README, Kernels: compute_gae).  bootstrap_value [N] is V at t = T
     (None: 0); truncateds [N, T] with bootstrap_values [N, T] handle
     time-limit truncation."""
-    r = _device_tensor(rewards, "rewards")
-    N, T = _check_2d(r, "rewards")
-    out = torch.empty((N, T), dtype=torch.float32, device=r.device)
-    co = _carry_out(return_carry, N, r.device)
-    term, trunc = _flags(terminateds=terminateds, truncateds=truncateds)
-    ins = (r, _device_tensor(values, "values"), _device_tensor(bootstrap_value, "bootstrap_value"),
-           term, trunc, _device_tensor(bootstrap_values, "bootstrap_values"))
-    ci = _device_tensor(carry_in, "carry_in")
-    _submit("gae", ins, (out,), dict(gamma=float(gamma), lam=float(lambda_)),
-            lambda st: rlscan.rlscan_gae(*ins, out, float(gamma), float(lambda_), st,
-                                         carry_in=ci, carry_out=co),
-            stream, ci is not None or co is not None, (ci, co))
+    r = _rows(rewards, "rewards")
+    N, T = r.shape
+    (term, trunc), byte = _flags(r.shape, ("terminateds", terminateds), ("truncateds", truncateds))
+    ins = (r, _tensor(values, "values", r.shape), _tensor(bootstrap_value, "bootstrap_value", (N,)),
+           term, trunc, _tensor(bootstrap_values, "bootstrap_values", r.shape))
+    ci = _tensor(carry_in, "carry_in", (N,))
+    out = torch.empty_like(r)
+    co = r.new_empty((N,)) if return_carry else None
+    g, lam = float(gamma), float(lambda_)
+
+    def alone(st):
+        lib, P, h = _lib(), [_p(t) for t in ins], _raw_stream(st, r)
+        if byte:
+            _check(lib.rlscan_gae_u8(*P, _p(ci), out.data_ptr(), _p(co), N, T, g, lam, h))
+        elif ci is not None or co is not None:
+            _check(lib.rlscan_gae_carry(*P, _p(ci), out.data_ptr(), _p(co), N, T, g, lam, h))
+        else:
+            _check(lib.rlscan_gae(*P, out.data_ptr(), N, T, g, lam, h))
+    _submit("gae", ins, (out,), dict(gamma=g, lam=lam), alone, stream,
+            ci is not None or co is not None, (ci, co))
     return (out, co) if return_carry else out
 
 
@@ -210,18 +257,28 @@ def compute_lambda_returns(rewards, values, terminateds, gamma=0.99, lambda_=0.9
                            bootstrap_value=None, truncateds=None, bootstrap_values=None,
                            carry_in=None, return_carry=False, stream=None):
     """TD(lambda) returns [N, T] (README, Kernels: compute_lambda_returns)."""
-    r = _device_tensor(rewards, "rewards")
-    N, T = _check_2d(r, "rewards")
-    out = torch.empty((N, T), dtype=torch.float32, device=r.device)
-    co = _carry_out(return_carry, N, r.device)
-    term, trunc = _flags(terminateds=terminateds, truncateds=truncateds)
-    ins = (r, _device_tensor(values, "values"), _device_tensor(bootstrap_value, "bootstrap_value"),
-           term, trunc, _device_tensor(bootstrap_values, "bootstrap_values"))
-    ci = _device_tensor(carry_in, "carry_in")
-    _submit("lambda_returns", ins, (out,), dict(gamma=float(gamma), lam=float(lambda_)),
-            lambda st: rlscan.rlscan_lambda_returns(*ins, out, float(gamma), float(lambda_), st,
-                                                    carry_in=ci, carry_out=co),
-            stream, ci is not None or co is not None, (ci, co))
+    r = _rows(rewards, "rewards")
+    N, T = r.shape
+    (term, trunc), byte = _flags(r.shape, ("terminateds", terminateds), ("truncateds", truncateds))
+    ins = (r, _tensor(values, "values", r.shape), _tensor(bootstrap_value, "bootstrap_value", (N,)),
+           term, trunc, _tensor(bootstrap_values, "bootstrap_values", r.shape))
+    ci = _tensor(carry_in, "carry_in", (N,))
+    out = torch.empty_like(r)
+    co = r.new_empty((N,)) if return_carry else None
+    g, lam = float(gamma), float(lambda_)
+
+    def alone(st):
+        lib, P, h = _lib(), [_p(t) for t in ins], _raw_stream(st, r)
+        if byte:
+            _check(lib.rlscan_lambda_returns_u8(*P, _p(ci), out.data_ptr(), _p(co), N, T, g, lam,
+                                                h))
+        elif ci is not None or co is not None:
+            _check(lib.rlscan_lambda_returns_carry(*P, _p(ci), out.data_ptr(), _p(co), N, T, g,
+                                                   lam, h))
+        else:
+            _check(lib.rlscan_lambda_returns(*P, out.data_ptr(), N, T, g, lam, h))
+    _submit("lambda_returns", ins, (out,), dict(gamma=g, lam=lam), alone, stream,
+            ci is not None or co is not None, (ci, co))
     return (out, co) if return_carry else out
 
 
@@ -230,18 +287,28 @@ def compute_discounted_returns(rewards, terminateds, gamma=0.99, *, bootstrap_va
                                return_carry=False, stream=None):
     """Discounted reward-to-go [N, T] (README, Kernels:
     compute_discounted_returns)."""
-    r = _device_tensor(rewards, "rewards")
-    N, T = _check_2d(r, "rewards")
-    out = torch.empty((N, T), dtype=torch.float32, device=r.device)
-    co = _carry_out(return_carry, N, r.device)
-    term, trunc = _flags(terminateds=terminateds, truncateds=truncateds)
-    ins = (r, _device_tensor(bootstrap_value, "bootstrap_value"), term, trunc,
-           _device_tensor(bootstrap_values, "bootstrap_values"))
-    ci = _device_tensor(carry_in, "carry_in")
-    _submit("discounted_returns", ins, (out,), dict(gamma=float(gamma)),
-            lambda st: rlscan.rlscan_discounted_returns(*ins, out, float(gamma), st, carry_in=ci,
-                                                        carry_out=co),
-            stream, ci is not None or co is not None, (ci, co))
+    r = _rows(rewards, "rewards")
+    N, T = r.shape
+    (term, trunc), byte = _flags(r.shape, ("terminateds", terminateds), ("truncateds", truncateds))
+    ins = (r, _tensor(bootstrap_value, "bootstrap_value", (N,)), term, trunc,
+           _tensor(bootstrap_values, "bootstrap_values", r.shape))
+    ci = _tensor(carry_in, "carry_in", (N,))
+    out = torch.empty_like(r)
+    co = r.new_empty((N,)) if return_carry else None
+    g = float(gamma)
+
+    def alone(st):
+        lib, P, h = _lib(), [_p(t) for t in ins], _raw_stream(st, r)
+        if byte:
+            _check(lib.rlscan_discounted_returns_u8(*P, _p(ci), out.data_ptr(), _p(co), N, T, g,
+                                                    h))
+        elif ci is not None or co is not None:
+            _check(lib.rlscan_discounted_returns_carry(*P, _p(ci), out.data_ptr(), _p(co), N, T,
+                                                       g, h))
+        else:
+            _check(lib.rlscan_discounted_returns(*P, out.data_ptr(), N, T, g, h))
+    _submit("discounted_returns", ins, (out,), dict(gamma=g), alone, stream,
+            ci is not None or co is not None, (ci, co))
     return (out, co) if return_carry else out
 
 
@@ -254,26 +321,45 @@ def compute_vtrace(rewards, values, log_rhos, terminateds, gamma=0.99, rho_bar=1
     carry_in / carry_out are vs values.  IMPALA's options: lambda_ scales
     every trace coefficient c_t (None: 1) and rho_bar_pg truncates the
     policy-gradient weight (None: rho_bar)."""
-    r = _device_tensor(rewards, "rewards")
-    N, T = _check_2d(r, "rewards")
-    vs = torch.empty((N, T), dtype=torch.float32, device=r.device)
-    pg = torch.empty((N, T), dtype=torch.float32, device=r.device)
-    co = _carry_out(return_carry, N, r.device)
-    term, trunc = _flags(terminateds=terminateds, truncateds=truncateds)
-    ins = (r, _device_tensor(values, "values"), _device_tensor(bootstrap_value, "bootstrap_value"),
-           _device_tensor(log_rhos, "log_rhos"), term, trunc,
-           _device_tensor(bootstrap_values, "bootstrap_values"))
-    ci = _device_tensor(carry_in, "carry_in")
-    lam = None if lambda_ is None else float(lambda_)
-    pgc = None if rho_bar_pg is None else float(rho_bar_pg)
+    r = _rows(rewards, "rewards")
+    N, T = r.shape
+    (term, trunc), byte = _flags(r.shape, ("terminateds", terminateds), ("truncateds", truncateds))
+    ins = (r, _tensor(values, "values", r.shape), _tensor(bootstrap_value, "bootstrap_value", (N,)),
+           _tensor(log_rhos, "log_rhos", r.shape), term, trunc,
+           _tensor(bootstrap_values, "bootstrap_values", r.shape))
+    ci = _tensor(carry_in, "carry_in", (N,))
+    vs, pg = torch.empty_like(r), torch.empty_like(r)
+    co = r.new_empty((N,)) if return_carry else None
+    g, rb, cb = float(gamma), float(rho_bar), float(c_bar)
+    ex = lambda_ is not None or rho_bar_pg is not None
+    lam = 1.0 if lambda_ is None else float(lambda_)
+    rbpg = rb if rho_bar_pg is None else float(rho_bar_pg)
+
+    def alone(st):
+        lib, P, h = _lib(), [_p(t) for t in ins], _raw_stream(st, r)
+        o = (vs.data_ptr(), pg.data_ptr())
+        if byte:
+            _check(lib.rlscan_vtrace_u8(*P, _p(ci), *o, _p(co), N, T, g, lam, rb, cb, rbpg, h))
+        elif ex:
+            _check(lib.rlscan_vtrace_ex(*P, _p(ci), *o, _p(co), N, T, g, lam, rb, cb, rbpg, h))
+        elif ci is not None or co is not None:
+            _check(lib.rlscan_vtrace_carry(*P, _p(ci), *o, _p(co), N, T, g, rb, cb, h))
+        else:
+            _check(lib.rlscan_vtrace(*P, *o, N, T, g, rb, cb, h))
     _submit("vtrace", ins, (vs, pg),
-            dict(gamma=float(gamma), lam=1.0 if lam is None else lam, rho_bar=float(rho_bar),
-                 c_bar=float(c_bar), rho_bar_pg=pgc),
-            lambda st: rlscan.rlscan_vtrace(*ins, vs, pg, float(gamma), float(rho_bar),
-                                            float(c_bar), st, carry_in=ci, carry_out=co,
-                                            lam=lam, rho_bar_pg=pgc),
-            stream, ci is not None or co is not None, (ci, co))
+            dict(gamma=g, lam=lam, rho_bar=rb, c_bar=cb, rho_bar_pg=rbpg), alone, stream,
+            ci is not None or co is not None, (ci, co))
     return (vs, pg, co) if return_carry else (vs, pg)
+
+
+def _int32(t, name, shape):
+    """Integer indices as int32 (any integer dtype, narrowed or widened)."""
+    if t is None:
+        return None
+    _gpu(t, name)
+    if t.dtype is not _I32 and not t.dtype.is_floating_point:
+        t = t.to(_I32)
+    return _tensor(t, name, shape, _I32)
 
 
 def compute_retrace(rewards, next_q_values_all, next_target_probs, actions, behaviour_probs,
@@ -285,31 +371,36 @@ def compute_retrace(rewards, next_q_values_all, next_target_probs, actions, beha
     successor state; actions [N, T] are the taken actions (int32, or any
     integer dtype, converted); behaviour_probs [N, T] is mu of the taken
     action.  Both flags are required (README, Performance)."""
-    r = _device_tensor(rewards, "rewards")
-    N, T = _check_2d(r, "rewards")
+    r = _rows(rewards, "rewards")
+    N, T = r.shape
     if truncateds is None:
         raise ValueError("compute_retrace takes terminateds and truncateds, both required")
-    a = actions
-    if isinstance(a, torch.Tensor) and a.dtype != torch.int32 and not a.dtype.is_floating_point:
-        a = a.to(torch.int32)
-    na = next_actions
-    if isinstance(na, torch.Tensor) and na.dtype != torch.int32 and not na.dtype.is_floating_point:
-        na = na.to(torch.int32)
-    out = torch.empty((N, T), dtype=torch.float32, device=r.device)
-    co = _carry_out(return_carry, N, r.device)
-    term, trunc = _flags(terminateds=terminateds, truncateds=truncateds)
-    ins = (r, _device_tensor(next_q_values_all, "next_q_values_all"),
-           _device_tensor(next_target_probs, "next_target_probs"),
-           _device_tensor(a, "actions", torch.int32),
-           _device_tensor(behaviour_probs, "behaviour_probs"), term, trunc)
-    ci = _device_tensor(carry_in, "carry_in")
-    nat = _device_tensor(na, "next_actions", torch.int32)
-    nbp = _device_tensor(next_behaviour_probs, "next_behaviour_probs")
-    _submit("retrace", ins, (out,), dict(gamma=float(gamma), lam=float(lambda_)),
-            lambda st: rlscan.rlscan_retrace(*ins, out, float(gamma), float(lambda_), st,
-                                             carry_in=ci, carry_out=co, next_actions=nat,
-                                             next_behaviour_probs=nbp),
-            stream, ci is not None or co is not None, (ci, co, nat, nbp))
+    q = _gpu(next_q_values_all, "next_q_values_all")
+    if q.dim() != 3 or q.shape[:2] != r.shape:
+        raise ValueError(f"next_q_values_all must be a [N, T, A] tensor, got shape "
+                         f"{tuple(q.shape)}")
+    A = q.shape[2]
+    (term, trunc), byte = _flags(r.shape, ("terminateds", terminateds), ("truncateds", truncateds))
+    ins = (r, _tensor(q, "next_q_values_all", q.shape),
+           _tensor(next_target_probs, "next_target_probs", q.shape),
+           _int32(actions, "actions", r.shape), _tensor(behaviour_probs, "behaviour_probs", r.shape),
+           term, trunc)
+    ci = _tensor(carry_in, "carry_in", (N,))
+    nat = _int32(next_actions, "next_actions", (N,))
+    nbp = _tensor(next_behaviour_probs, "next_behaviour_probs", (N,))
+    out = torch.empty_like(r)
+    co = r.new_empty((N,)) if return_carry else None
+    g, lam = float(gamma), float(lambda_)
+
+    def alone(st):
+        lib, P, h = _lib(), [_p(t) for t in ins], _raw_stream(st, r)
+        if byte or ci is not None or co is not None:
+            fn = lib.rlscan_retrace_u8 if byte else lib.rlscan_retrace_carry
+            _check(fn(*P, _p(ci), _p(nat), _p(nbp), out.data_ptr(), _p(co), N, T, A, g, lam, h))
+        else:
+            _check(lib.rlscan_retrace(*P, out.data_ptr(), N, T, A, g, lam, h))
+    _submit("retrace", ins, (out,), dict(gamma=g, lam=lam), alone, stream,
+            ci is not None or co is not None, (ci, co, nat, nbp))
     return (out, co) if return_carry else out
 
 
@@ -317,16 +408,27 @@ def compute_eligibility_traces(x, dones, gamma=0.99, lambda_=0.95, *, carry_in=N
                                return_carry=False, stream=None):
     """Forward traces e_t = x_t + gamma*lambda*(1 - d_t)*e_{t-1} [N, T]
     (README, Kernels: compute_eligibility_traces)."""
-    xx = _device_tensor(x, "x")
-    N, T = _check_2d(xx, "x")
-    out = torch.empty((N, T), dtype=torch.float32, device=xx.device)
-    co = _carry_out(return_carry, N, xx.device)
-    ins = (xx, _flags(dones=dones)[0])
-    ci = _device_tensor(carry_in, "carry_in")
-    _submit("eligibility_traces", ins, (out,), dict(gamma=float(gamma), lam=float(lambda_)),
-            lambda st: rlscan.rlscan_eligibility_traces(*ins, out, float(gamma), float(lambda_),
-                                                        st, carry_in=ci, carry_out=co),
-            stream, ci is not None or co is not None, (ci, co))
+    xx = _rows(x, "x")
+    N, T = xx.shape
+    (d,), byte = _flags(xx.shape, ("dones", dones))
+    ins = (xx, d)
+    ci = _tensor(carry_in, "carry_in", (N,))
+    out = torch.empty_like(xx)
+    co = xx.new_empty((N,)) if return_carry else None
+    g, lam = float(gamma), float(lambda_)
+
+    def alone(st):
+        lib, P, h = _lib(), [_p(t) for t in ins], _raw_stream(st, xx)
+        if byte:
+            _check(lib.rlscan_eligibility_traces_u8(*P, _p(ci), out.data_ptr(), _p(co), N, T, g,
+                                                    lam, h))
+        elif ci is not None or co is not None:
+            _check(lib.rlscan_eligibility_traces_carry(*P, _p(ci), out.data_ptr(), _p(co), N, T,
+                                                       g, lam, h))
+        else:
+            _check(lib.rlscan_eligibility_traces(*P, out.data_ptr(), N, T, g, lam, h))
+    _submit("eligibility_traces", ins, (out,), dict(gamma=g, lam=lam), alone, stream,
+            ci is not None or co is not None, (ci, co))
     return (out, co) if return_carry else out
 
 
@@ -336,29 +438,42 @@ def compute_episodic_prefix_sum(x, dones, *, carry_in=None, return_carry=False, 
     int32, narrower integer dtypes are widened, int64 is refused (it would
     not fit).  float32 x: float32 output, summed in float32 in the scan's
     order (float dones only)."""
-    if isinstance(x, torch.Tensor) and x.dtype == torch.float32:
-        xx = _device_tensor(x, "x")
-        N, T = _check_2d(xx, "x")
-        out = torch.empty((N, T), dtype=torch.float32, device=xx.device)
-        co = _carry_out(return_carry, N, xx.device)
-        d = _device_tensor(dones, "dones", torch.float32, flag=True)
-        ci = _device_tensor(carry_in, "carry_in")
-        _on_stream(lambda st: rlscan.rlscan_episodic_prefix_sum_f32(xx, d, out, st, carry_in=ci,
-                                                                     carry_out=co),
-                   stream, (xx, d, out, ci, co))
+    if isinstance(x, torch.Tensor) and x.dtype is _F32:
+        xx = _rows(x, "x")
+        N, T = xx.shape
+        d = _gpu(dones, "dones")
+        d = _tensor(d if d.dtype is _F32 else (d != 0).to(_F32), "dones", xx.shape)
+        ci = _tensor(carry_in, "carry_in", (N,))
+        out = torch.empty_like(xx)
+        co = xx.new_empty((N,)) if return_carry else None
+
+        def alone_f32(st):
+            _check(_lib().rlscan_episodic_prefix_sum_f32(
+                xx.data_ptr(), d.data_ptr(), _p(ci), out.data_ptr(), _p(co), N, T,
+                _raw_stream(st, xx)))
+        _on_stream(alone_f32, stream, (xx, d, out, ci, co))
         return (out, co) if return_carry else out
     xx = x
     if isinstance(xx, torch.Tensor) and xx.dtype in (torch.bool, torch.uint8, torch.int8,
                                                      torch.int16):
-        xx = xx.to(torch.int32)
-    xx = _device_tensor(xx, "x", torch.int32)
-    N, T = _check_2d(xx, "x")
+        xx = _gpu(xx, "x").to(_I32)
+    xx = _rows(xx, "x", _I32)
+    N, T = xx.shape
+    (d,), byte = _flags(xx.shape, ("dones", dones))
+    ins = (xx, d)
+    ci = _tensor(carry_in, "carry_in", (N,), torch.int64)
     out = torch.empty((N, T), dtype=torch.int64, device=xx.device)
-    co = _carry_out(return_carry, N, xx.device, torch.int64)
-    ins = (xx, _flags(dones=dones)[0])
-    ci = _device_tensor(carry_in, "carry_in", torch.int64)
-    _submit("episodic_prefix_sum", ins, (out,), {},
-            lambda st: rlscan.rlscan_episodic_prefix_sum(*ins, out, st, carry_in=ci,
-                                                         carry_out=co),
-            stream, ci is not None or co is not None, (ci, co))
+    co = torch.empty((N,), dtype=torch.int64, device=xx.device) if return_carry else None
+
+    def alone(st):
+        lib, P, h = _lib(), [_p(t) for t in ins], _raw_stream(st, xx)
+        if byte:
+            _check(lib.rlscan_episodic_prefix_sum_u8(*P, _p(ci), out.data_ptr(), _p(co), N, T, h))
+        elif ci is not None or co is not None:
+            _check(lib.rlscan_episodic_prefix_sum_carry(*P, _p(ci), out.data_ptr(), _p(co), N, T,
+                                                        h))
+        else:
+            _check(lib.rlscan_episodic_prefix_sum(*P, out.data_ptr(), N, T, h))
+    _submit("episodic_prefix_sum", ins, (out,), {}, alone, stream,
+            ci is not None or co is not None, (ci, co))
     return (out, co) if return_carry else out
