@@ -54,7 +54,7 @@ template <class A> struct StatusEntries { static constexpr int value = 1; };
 template <> struct StatusEntries<StepW> { static constexpr int value = 2; };
 
 template <class A>
-__device__ __forceinline__ TileStatus* status_of(TileStatus* base, int64_t tile) {
+__host__ __device__ __forceinline__ TileStatus* status_of(TileStatus* base, int64_t tile) {
     return base + StatusEntries<A>::value * tile;
 }
 
@@ -93,16 +93,16 @@ __device__ __forceinline__ float poisoned(float) { return __builtin_nanf(""); }
 __device__ __forceinline__ double poisoned(double) { return __builtin_nan(""); }
 __device__ __forceinline__ int64_t poisoned(int64_t) { return INT64_MIN; }
 
-__device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t payload) {
+__host__ __device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t payload) {
     return (static_cast<uint64_t>(tag) << 32) | payload;
 }
-__device__ __forceinline__ void store_word(uint64_t* p, uint64_t v) {
+__host__ __device__ __forceinline__ void store_word(uint64_t* p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint64_t load_word(uint64_t* p) {
+__host__ __device__ __forceinline__ uint64_t load_word(uint64_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ bool has_tag(uint64_t w, uint32_t tag) {
+__host__ __device__ __forceinline__ bool has_tag(uint64_t w, uint32_t tag) {
     return static_cast<uint32_t>(w >> 32) == tag;
 }
 
@@ -110,28 +110,28 @@ __device__ __forceinline__ bool has_tag(uint64_t w, uint32_t tag) {
 // 32-bit payload).
 constexpr uint32_t kShortForm = 0x80000000u;
 
-__device__ __forceinline__ bool fits_short(int64_t v) {
+__host__ __device__ __forceinline__ bool fits_short(int64_t v) {
     return v == static_cast<int64_t>(static_cast<int32_t>(v));
 }
-__device__ __forceinline__ int64_t short_value(uint64_t w) {
+__host__ __device__ __forceinline__ int64_t short_value(uint64_t w) {
     return static_cast<int64_t>(static_cast<int32_t>(static_cast<uint32_t>(w)));
 }
-__device__ __forceinline__ int64_t long_value(uint64_t lo, uint64_t hi) {
+__host__ __device__ __forceinline__ int64_t long_value(uint64_t lo, uint64_t hi) {
     return static_cast<int64_t>(((hi & 0xffffffffull) << 32) | (lo & 0xffffffffull));
 }
 
 // ---------------------------------------------------------------- publish
 // The float aggregate's a is published rounded once to float32: a single
 // rounding, unlike the many that motivated the float64 a in StepD.
-__device__ __forceinline__ void publish_aggregate(TileStatus* st, StepD s, uint32_t tag) {
-    store_word(&st->w[0], tagged(tag, __float_as_uint(static_cast<float>(s.a))));
-    store_word(&st->w[1], tagged(tag, __float_as_uint(s.b)));
+__host__ __device__ __forceinline__ void publish_aggregate(TileStatus* st, StepD s, uint32_t tag) {
+    store_word(&st->w[0], tagged(tag, __builtin_bit_cast(uint32_t, static_cast<float>(s.a))));
+    store_word(&st->w[1], tagged(tag, __builtin_bit_cast(uint32_t, s.b)));
 }
-__device__ __forceinline__ void publish_inclusive(TileStatus* st, float x, uint32_t tag) {
-    store_word(&st->w[2], tagged(tag, __float_as_uint(x)));
+__host__ __device__ __forceinline__ void publish_inclusive(TileStatus* st, float x, uint32_t tag) {
+    store_word(&st->w[2], tagged(tag, __builtin_bit_cast(uint32_t, x)));
 }
 // Integer value v into words w[k] (and w[k+1] if it needs 64 bits).
-__device__ __forceinline__ void publish_int(uint64_t* w, int64_t v, uint32_t tag) {
+__host__ __device__ __forceinline__ void publish_int(uint64_t* w, int64_t v, uint32_t tag) {
     const uint64_t u = static_cast<uint64_t>(v);
     if (fits_short(v)) {
         store_word(w, tagged(tag | kShortForm, static_cast<uint32_t>(u)));
@@ -142,53 +142,53 @@ __device__ __forceinline__ void publish_int(uint64_t* w, int64_t v, uint32_t tag
 }
 // An integer aggregate published as AGG never cuts the chain (a cut aggregate
 // is published as INCL), so its a is 1 and only b is stored.
-__device__ __forceinline__ void publish_aggregate(TileStatus* st, StepI s, uint32_t tag) {
+__host__ __device__ __forceinline__ void publish_aggregate(TileStatus* st, StepI s, uint32_t tag) {
     publish_int(&st->w[0], s.b, tag);
 }
-__device__ __forceinline__ void publish_inclusive(TileStatus* st, int64_t x, uint32_t tag) {
+__host__ __device__ __forceinline__ void publish_inclusive(TileStatus* st, int64_t x, uint32_t tag) {
     publish_int(&st->w[2], x, tag);
 }
 
 // Float64 values: each 32-bit half is a word of its own, validated by its
 // own tag (each is written once per call, so two current halves are the
 // value).
-__device__ __forceinline__ void publish_f64(uint64_t* w, double v, uint32_t tag) {
-    const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+__host__ __device__ __forceinline__ void publish_f64(uint64_t* w, double v, uint32_t tag) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
     store_word(w, tagged(tag, static_cast<uint32_t>(u)));
     store_word(w + 1, tagged(tag, static_cast<uint32_t>(u >> 32)));
 }
-__device__ __forceinline__ double f64_value(uint64_t lo, uint64_t hi) {
-    return __longlong_as_double(static_cast<long long>(long_value(lo, hi)));
+__host__ __device__ __forceinline__ double f64_value(uint64_t lo, uint64_t hi) {
+    return __builtin_bit_cast(double, static_cast<uint64_t>(long_value(lo, hi)));
 }
-__device__ __forceinline__ void publish_aggregate(TileStatus* st, StepW s, uint32_t tag) {
+__host__ __device__ __forceinline__ void publish_aggregate(TileStatus* st, StepW s, uint32_t tag) {
     publish_f64(&st[0].w[0], s.a, tag);
     publish_f64(&st[0].w[2], s.b, tag);
 }
-__device__ __forceinline__ void publish_inclusive(TileStatus* st, double x, uint32_t tag) {
+__host__ __device__ __forceinline__ void publish_inclusive(TileStatus* st, double x, uint32_t tag) {
     publish_f64(&st[1].w[0], x, tag);
 }
 
 // ---------------------------------------------------------------- read
 // Returns 0 (not ready), 1 (aggregate) or 2 (inclusive state, given as the
 // step (0, x)), and the step in `s`.
-__device__ __forceinline__ int read_status(TileStatus* st, uint32_t tag, StepD& s) {
+__host__ __device__ __forceinline__ int read_status(TileStatus* st, uint32_t tag, StepD& s) {
     const uint64_t x = load_word(&st->w[2]);
     const uint64_t a = load_word(&st->w[0]);
     const uint64_t b = load_word(&st->w[1]);
     if (has_tag(x, tag)) {
-        s = {0.0, __uint_as_float(static_cast<uint32_t>(x))};
+        s = {0.0, __builtin_bit_cast(float, static_cast<uint32_t>(x))};
         return 2;
     }
     if (has_tag(a, tag) && has_tag(b, tag)) {
-        s = {static_cast<double>(__uint_as_float(static_cast<uint32_t>(a))),
-             __uint_as_float(static_cast<uint32_t>(b))};
+        s = {static_cast<double>(__builtin_bit_cast(float, static_cast<uint32_t>(a))),
+             __builtin_bit_cast(float, static_cast<uint32_t>(b))};
         return 1;
     }
     return 0;
 }
 // The high word of a two-word value is read only once its low word is seen
 // (one dependent read, the inclusive value's if its low word is there).
-__device__ __forceinline__ int read_status(TileStatus* st, uint32_t tag, StepI& s) {
+__host__ __device__ __forceinline__ int read_status(TileStatus* st, uint32_t tag, StepI& s) {
     const uint64_t x = load_word(&st->w[2]);
     const uint64_t b = load_word(&st->w[0]);
     if (has_tag(x, tag | kShortForm)) {
@@ -210,7 +210,7 @@ __device__ __forceinline__ int read_status(TileStatus* st, uint32_t tag, StepI& 
     return 0;
 }
 
-__device__ __forceinline__ int read_status(TileStatus* st, uint32_t tag, StepW& s) {
+__host__ __device__ __forceinline__ int read_status(TileStatus* st, uint32_t tag, StepW& s) {
     const uint64_t xl = load_word(&st[1].w[0]);
     const uint64_t xh = load_word(&st[1].w[1]);
     if (has_tag(xl, tag) && has_tag(xh, tag)) {
@@ -226,6 +226,29 @@ __device__ __forceinline__ int read_status(TileStatus* st, uint32_t tag, StepW& 
         return 1;
     }
     return 0;
+}
+
+// One poll of a look-back window, decided from two lane masks of the window
+// (lane 63 the nearest predecessor): `term_mask` marks the entries that end
+// the walk (an inclusive value, or an aggregate that cuts the chain),
+// `ready_mask` the entries read with the call's tag (lanes before tile 0
+// count as ready).  The walk needs every entry from the nearest terminal one
+// up to lane 63, or the whole window if none is terminal; a narrow poll
+// (width < 64) that finds its lanes ready and none terminal widens.
+struct PollStep {
+    int stop;    // nearest terminal lane, -1 if none
+    bool done;   // every entry the walk needs is ready
+    bool widen;  // read the whole window next
+};
+__host__ __device__ __forceinline__ PollStep poll_step(uint64_t term_mask, uint64_t ready_mask,
+                                                       int width) {
+    PollStep r;
+    r.stop = term_mask ? 63 - __builtin_clzll(term_mask) : -1;
+    const uint64_t need = r.stop >= 0 ? (~0ull << r.stop) : ~0ull;
+    r.done = (ready_mask & need) == need;
+    const uint64_t narrow = ~0ull << (kWave - kNarrow);
+    r.widen = !r.done && r.stop < 0 && width < kWave && (ready_mask & narrow) == narrow;
+    return r;
 }
 
 __device__ __forceinline__ uint64_t take_ticket(const LookbackArgs& lb) {
@@ -260,13 +283,10 @@ __device__ V look_back(const LookbackArgs& lb, uint64_t tile, int lane) {
             int kind = q < 0 ? 3 : 0;
             if (q >= 0 && in_window) kind = read_status(status_of<A>(lb.status, q), lb.read_tag, s);
             const bool terminal = kind == 2 || (kind == 1 && cuts_chain(s));
-            const uint64_t term_mask = __ballot(terminal);
-            const uint64_t ready_mask = __ballot(kind != 0);
-            stop = term_mask ? 63 - __clzll(term_mask) : -1;  // nearest terminal lane
-            const uint64_t need = stop >= 0 ? (~0ull << stop) : ~0ull;
-            if ((ready_mask & need) == need) break;
-            const uint64_t narrow = ~0ull << (kWave - kNarrow);
-            if (stop < 0 && width < kWave && (ready_mask & narrow) == narrow) {
+            const PollStep step = poll_step(__ballot(terminal), __ballot(kind != 0), width);
+            stop = step.stop;
+            if (step.done) break;
+            if (step.widen) {
                 width = kWave;  // no terminal entry near: read the whole window now
                 continue;
             }

@@ -56,43 +56,46 @@ struct StepW {
     double a, b;
 };
 
+// The step operations below are host-and-device functions: the CPU model of
+// the look-back protocol (tests) composes steps with them too.
+
 // Type that holds compositions of a given element step type.
 template <class S> struct AggOf;
 template <> struct AggOf<StepF> { using type = StepD; };
 template <> struct AggOf<StepI> { using type = StepI; };
 template <> struct AggOf<StepW> { using type = StepW; };
 
-__device__ __forceinline__ StepD identity_step(StepD) { return {1.0, 0.0f}; }
-__device__ __forceinline__ StepI identity_step(StepI) { return {1u, 0}; }
-__device__ __forceinline__ StepF identity_step(StepF) { return {1.0f, 0.0f}; }
-__device__ __forceinline__ StepW identity_step(StepW) { return {1.0, 0.0}; }
+__host__ __device__ __forceinline__ StepD identity_step(StepD) { return {1.0, 0.0f}; }
+__host__ __device__ __forceinline__ StepI identity_step(StepI) { return {1u, 0}; }
+__host__ __device__ __forceinline__ StepF identity_step(StepF) { return {1.0f, 0.0f}; }
+__host__ __device__ __forceinline__ StepW identity_step(StepW) { return {1.0, 0.0}; }
 
-__device__ __forceinline__ StepD promote(StepF s) { return {static_cast<double>(s.a), s.b}; }
-__device__ __forceinline__ StepI promote(StepI s) { return s; }
-__device__ __forceinline__ StepW promote(StepW s) { return s; }
+__host__ __device__ __forceinline__ StepD promote(StepF s) { return {static_cast<double>(s.a), s.b}; }
+__host__ __device__ __forceinline__ StepI promote(StepI s) { return s; }
+__host__ __device__ __forceinline__ StepW promote(StepW s) { return s; }
 
 // later o earlier
-__device__ __forceinline__ StepD compose(StepD later, StepD earlier) {
+__host__ __device__ __forceinline__ StepD compose(StepD later, StepD earlier) {
     return {later.a * earlier.a, fmaf(static_cast<float>(later.a), earlier.b, later.b)};
 }
-__device__ __forceinline__ StepI compose(StepI later, StepI earlier) {
+__host__ __device__ __forceinline__ StepI compose(StepI later, StepI earlier) {
     return {later.a & earlier.a, later.a ? later.b + earlier.b : later.b};
 }
-__device__ __forceinline__ StepW compose(StepW later, StepW earlier) {
+__host__ __device__ __forceinline__ StepW compose(StepW later, StepW earlier) {
     return {later.a * earlier.a, fma(later.a, earlier.b, later.b)};
 }
 
-__device__ __forceinline__ float apply(StepF s, float x) { return fmaf(s.a, x, s.b); }
-__device__ __forceinline__ float apply(StepD s, float x) {
+__host__ __device__ __forceinline__ float apply(StepF s, float x) { return fmaf(s.a, x, s.b); }
+__host__ __device__ __forceinline__ float apply(StepD s, float x) {
     return fmaf(static_cast<float>(s.a), x, s.b);
 }
-__device__ __forceinline__ int64_t apply(StepI s, int64_t x) { return s.a ? x + s.b : s.b; }
-__device__ __forceinline__ double apply(StepW s, double x) { return fma(s.a, x, s.b); }
+__host__ __device__ __forceinline__ int64_t apply(StepI s, int64_t x) { return s.a ? x + s.b : s.b; }
+__host__ __device__ __forceinline__ double apply(StepW s, double x) { return fma(s.a, x, s.b); }
 
-__device__ __forceinline__ bool cuts_chain(StepF s) { return s.a == 0.0f; }
-__device__ __forceinline__ bool cuts_chain(StepD s) { return s.a == 0.0; }
-__device__ __forceinline__ bool cuts_chain(StepI s) { return s.a == 0u; }
-__device__ __forceinline__ bool cuts_chain(StepW s) { return s.a == 0.0; }
+__host__ __device__ __forceinline__ bool cuts_chain(StepF s) { return s.a == 0.0f; }
+__host__ __device__ __forceinline__ bool cuts_chain(StepD s) { return s.a == 0.0; }
+__host__ __device__ __forceinline__ bool cuts_chain(StepI s) { return s.a == 0u; }
+__host__ __device__ __forceinline__ bool cuts_chain(StepW s) { return s.a == 0.0; }
 
 // ---------------------------------------------------------------- DPP moves
 // DPP control words of the GFX9 family (gfx950 included):
