@@ -574,6 +574,28 @@ int rlscan_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t st
 int rlscan_stream_mix(void* dst, int64_t write_bytes, const void* src, int64_t read_bytes,
                       int32_t reads, int32_t writes, hipStream_t stream);
 
+/* Diagnostics: the streaming reference in a scan's own access pattern.
+ * `src` holds `arrays_in` (1..16) consecutive arrays of read_bytes/arrays_in
+ * bytes, `dst` `arrays_out` (1..4) arrays of write_bytes/arrays_out bytes;
+ * word i of every output array becomes the sum of word i of every input
+ * array (16-byte words, non-temporal accesses).  Each thread handles `words`
+ * (1..4) indices, laid out as the scans lay out their chunks (each wave64 a
+ * run of 64*words consecutive indices, a workgroup of 256 threads four
+ * such runs); arrays_in * words is at most 16.  workgroups_per_cu (0, or
+ * 2..8) caps the workgroups resident on a CU by giving each a share of the
+ * CU's LDS (0: as many as registers allow): fewer waves in flight can suit
+ * the DRAM better, as a scan kernel's register use does.  A scan call reads
+ * each input at the index it writes, so this layout, beside
+ * rlscan_stream_mix's spans, is a candidate for the call's achievable
+ * bandwidth.  Buffers are device pointers, 16-byte aligned, not
+ * overlapping.  Returns RLSCAN_ERR_SHAPE for sizes that are negative or do
+ * not split into whole words per array, RLSCAN_ERR_PARAM for counts out of
+ * range (or a cap the device's LDS cannot express) or misaligned pointers,
+ * RLSCAN_ERR_NULL, RLSCAN_ERR_ALIAS. */
+int rlscan_stream_mix_arrays(void* dst, int64_t write_bytes, const void* src, int64_t read_bytes,
+                             int32_t arrays_in, int32_t arrays_out, int32_t words,
+                             int32_t workgroups_per_cu, hipStream_t stream);
+
 /* Diagnostics: waits in the look-back are bounded (a few seconds per
  * predecessor); a wait that reaches the bound is counted, its tile takes NaN
  * as its entering state, so every float result of the tile is NaN (the

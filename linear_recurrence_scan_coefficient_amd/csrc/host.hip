@@ -288,6 +288,43 @@ __global__ __launch_bounds__(kMixThreads) void mix_kernel(const f32x4* __restric
     }
 }
 
+// The same reference in a scan's access pattern: `ain` input arrays and
+// `aout` output arrays of n_in and n_out 16-byte words.  Indices are laid
+// out as the scan lays out its chunks: lane l of wave w in workgroup b takes
+// indices b*256*words + (w*words + u)*64 + l (u < words), so each wave
+// covers `words` consecutive KiB of every array.  It reads that word of
+// every input array and writes their sum to that word of every output
+// array.  Indices past an array's end read as zero / are not written.
+constexpr int kMixMaxWords = 4;
+template <int WORDS>
+__global__ __launch_bounds__(kMixThreads) void mix_arrays_kernel(
+    const f32x4* __restrict__ src, int64_t n_in, f32x4* __restrict__ dst, int64_t n_out, int ain,
+    int aout) {
+    constexpr int kArrays = kMixMaxReads / WORDS;  // most input arrays at this width
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kMixThreads * WORDS +
+                         static_cast<int64_t>(wave) * WORDS * kWave + lane;
+    f32x4 v[kArrays][WORDS];
+#pragma unroll
+    for (int a = 0; a < kArrays; ++a)
+#pragma unroll
+        for (int u = 0; u < WORDS; ++u) {
+            const int64_t i = base + static_cast<int64_t>(u) * kWave;
+            v[a][u] = 0.0f;
+            if (a < ain && i < n_in) v[a][u] = __builtin_nontemporal_load(src + a * n_in + i);
+        }
+#pragma unroll
+    for (int u = 0; u < WORDS; ++u) {
+        f32x4 acc = v[0][u];
+#pragma unroll
+        for (int a = 1; a < kArrays; ++a) acc += v[a][u];
+        const int64_t i = base + static_cast<int64_t>(u) * kWave;
+#pragma unroll
+        for (int o = 0; o < kMixMaxWrites; ++o)
+            if (o < aout && i < n_out) __builtin_nontemporal_store(acc, dst + o * n_out + i);
+    }
+}
+
 }  // namespace rlscan
 
 using namespace rlscan;
@@ -411,6 +448,71 @@ int rlscan_stream_mix(void* dst, int64_t write_bytes, const void* src, int64_t r
     hipLaunchKernelGGL(mix_kernel, dim3(static_cast<unsigned>(grid)), dim3(kMixThreads), 0,
                        stream, static_cast<const f32x4*>(src), nr, static_cast<f32x4*>(dst), nw,
                        reads, writes);
+    return hipGetLastError() == hipSuccess ? RLSCAN_OK : RLSCAN_ERR_HIP;
+}
+
+int rlscan_stream_mix_arrays(void* dst, int64_t write_bytes, const void* src, int64_t read_bytes,
+                             int32_t arrays_in, int32_t arrays_out, int32_t words,
+                             int32_t workgroups_per_cu, hipStream_t stream) {
+    if (read_bytes < 0 || write_bytes < 0) return RLSCAN_ERR_SHAPE;
+    if (arrays_in < 1 || arrays_in > kMixMaxReads || arrays_out < 1 ||
+        arrays_out > kMixMaxWrites || words < 1 || words > kMixMaxWords ||
+        arrays_in * words > kMixMaxReads || workgroups_per_cu < 0 || workgroups_per_cu == 1 ||
+        workgroups_per_cu > 8)
+        return RLSCAN_ERR_PARAM;
+    if (read_bytes % (16 * int64_t(arrays_in)) != 0 || write_bytes % (16 * int64_t(arrays_out)) != 0)
+        return RLSCAN_ERR_SHAPE;
+    if (read_bytes == 0 && write_bytes == 0) return RLSCAN_OK;
+    if ((read_bytes > 0 && src == nullptr) || (write_bytes > 0 && dst == nullptr))
+        return RLSCAN_ERR_NULL;
+    if ((src != nullptr && !aligned16(src)) || (dst != nullptr && !aligned16(dst)))
+        return RLSCAN_ERR_PARAM;
+    const uintptr_t d = reinterpret_cast<uintptr_t>(dst), s = reinterpret_cast<uintptr_t>(src);
+    if (read_bytes > 0 && write_bytes > 0 && d < s + static_cast<uintptr_t>(read_bytes) &&
+        s < d + static_cast<uintptr_t>(write_bytes))
+        return RLSCAN_ERR_ALIAS;
+    const int64_t n_in = read_bytes / 16 / arrays_in, n_out = write_bytes / 16 / arrays_out;
+    const int64_t n = n_in > n_out ? n_in : n_out;
+    const int64_t per_group = int64_t(kMixThreads) * words;
+    const int64_t grid = (n + per_group - 1) / per_group;
+    if (grid > kMaxGrid) return RLSCAN_ERR_SHAPE;
+    // the residency cap: an unused share of the CU's LDS per workgroup, just
+    // over 1/(cap+1) of it, so that at most `cap` fit
+    size_t lds = 0;
+    if (workgroups_per_cu > 0) {
+        int dev = 0, per_cu = 0, per_block = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                                  dev) != hipSuccess ||
+            hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+                hipSuccess)
+            return RLSCAN_ERR_HIP;
+        lds = static_cast<size_t>(per_cu) / (workgroups_per_cu + 1) + 1024;
+        if (lds > static_cast<size_t>(per_block) ||
+            lds * workgroups_per_cu > static_cast<size_t>(per_cu))
+            return RLSCAN_ERR_PARAM;
+    }
+    const dim3 g(static_cast<unsigned>(grid)), b(kMixThreads);
+    const f32x4* in = static_cast<const f32x4*>(src);
+    f32x4* out = static_cast<f32x4*>(dst);
+    switch (words) {
+        case 1:
+            hipLaunchKernelGGL(mix_arrays_kernel<1>, g, b, lds, stream, in, n_in, out, n_out,
+                               arrays_in, arrays_out);
+            break;
+        case 2:
+            hipLaunchKernelGGL(mix_arrays_kernel<2>, g, b, lds, stream, in, n_in, out, n_out,
+                               arrays_in, arrays_out);
+            break;
+        case 3:
+            hipLaunchKernelGGL(mix_arrays_kernel<3>, g, b, lds, stream, in, n_in, out, n_out,
+                               arrays_in, arrays_out);
+            break;
+        default:
+            hipLaunchKernelGGL(mix_arrays_kernel<4>, g, b, lds, stream, in, n_in, out, n_out,
+                               arrays_in, arrays_out);
+            break;
+    }
     return hipGetLastError() == hipSuccess ? RLSCAN_OK : RLSCAN_ERR_HIP;
 }
 

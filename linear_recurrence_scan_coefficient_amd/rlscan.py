@@ -55,6 +55,7 @@ EXPORTED = (
     "rlscan_gae_u8", "rlscan_lambda_returns_u8", "rlscan_discounted_returns_u8",
     "rlscan_vtrace_u8", "rlscan_retrace_u8", "rlscan_eligibility_traces_u8",
     "rlscan_episodic_prefix_sum_u8", "rlscan_group", "rlscan_gae_noalloc", "rlscan_stream_mix",
+    "rlscan_stream_mix_arrays",
     "rlscan_set_xcd_run",
 )
 
@@ -154,6 +155,9 @@ def _declare(lib):
     lib.rlscan_set_xcd_run.restype = ctypes.c_int
     lib.rlscan_stream_mix.argtypes = [_vp, _i64, _vp, _i64, ctypes.c_int32, ctypes.c_int32, _vp]
     lib.rlscan_stream_mix.restype = ctypes.c_int
+    lib.rlscan_stream_mix_arrays.argtypes = [_vp, _i64, _vp, _i64, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_int32, _vp]
+    lib.rlscan_stream_mix_arrays.restype = ctypes.c_int
 
 
 def library(path: str = LIB_PATH):
@@ -590,6 +594,25 @@ def rlscan_stream_copy(dst, src, nbytes=None, stream=None):
         raise RlscanError(RLSCAN_ERR_SHAPE, "rlscan_stream_copy: nbytes exceeds a tensor")
     _check(library().rlscan_stream_copy(dst.data_ptr(), src.data_ptr(), int(nbytes),
                                         _stream(stream)))
+
+
+def rlscan_stream_mix_arrays(dst, src, write_bytes=None, read_bytes=None, arrays_in=1,
+                             arrays_out=1, words=1, workgroups_per_cu=0, stream=None):
+    """Streaming kernel in a scan's access pattern: `src` as `arrays_in`
+    arrays, `dst` as `arrays_out` arrays; word i of every output array gets
+    the sum of word i of every input array; `words` indices per thread; at
+    most `workgroups_per_cu` resident workgroups per CU (0: no cap)."""
+    if read_bytes is None:
+        read_bytes = src.numel() * src.element_size()
+    if write_bytes is None:
+        write_bytes = dst.numel() * dst.element_size()
+    if read_bytes > src.numel() * src.element_size() or \
+            write_bytes > dst.numel() * dst.element_size():
+        raise RlscanError(RLSCAN_ERR_SHAPE, "rlscan_stream_mix_arrays: a size exceeds its tensor")
+    _check(library().rlscan_stream_mix_arrays(dst.data_ptr(), int(write_bytes), src.data_ptr(),
+                                              int(read_bytes), int(arrays_in), int(arrays_out),
+                                              int(words), int(workgroups_per_cu),
+                                              _stream(stream)))
 
 
 def rlscan_stream_mix(dst, src, write_bytes=None, read_bytes=None, reads=1, writes=1,

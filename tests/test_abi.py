@@ -243,6 +243,25 @@ def test_stream_mix_argument_checks(lib):
     assert f(P[1], 1 << 44, P[0], 16, 1, 1, None) == SHAPE  # grid beyond 2^23 workgroups
 
 
+def test_stream_mix_arrays_argument_checks(lib):
+    f = lib.rlscan_stream_mix_arrays
+    assert f(P[1], 0, P[0], 0, 1, 1, 1, 0, None) == OK           # nothing to move
+    assert f(P[1], 64, P[0], 48, 2, 1, 1, 0, None) == SHAPE      # 3 words do not split in 2 arrays
+    assert f(P[1], 48, P[0], 64, 1, 2, 1, 0, None) == SHAPE
+    assert f(P[1], -16, P[0], 16, 1, 1, 1, 0, None) == SHAPE
+    assert f(P[1], 64, P[0], 64, 0, 1, 1, 0, None) == PARAM      # counts out of range
+    assert f(P[1], 64, P[0], 64 * 17, 17, 1, 1, 0, None) == PARAM
+    assert f(P[1], 64, P[0], 64, 1, 5, 1, 0, None) == PARAM
+    assert f(P[1], 64, P[0], 64, 1, 1, 5, 0, None) == PARAM
+    assert f(P[1], 64, P[0], 64 * 5, 5, 1, 4, 0, None) == PARAM  # 5 arrays x 4 words > 16
+    assert f(None, 64, P[0], 64, 1, 1, 1, 0, None) == NULL
+    assert f(P[1], 64, None, 64, 1, 1, 1, 0, None) == NULL
+    assert f(P[1] + 4, 64, P[0], 64, 1, 1, 1, 0, None) == PARAM  # misaligned
+    assert f(P[0] + 32, 64, P[0], 64, 1, 1, 1, 0, None) == ALIAS  # overlapping ranges
+    for cap in (-1, 1, 9):                                       # residency cap out of range
+        assert f(P[1], 64, P[0], 64, 1, 1, 1, cap, None) == PARAM
+
+
 def test_launch_floor_argument_checks(lib):
     """Refused on the host before any launch: a grid outside [1, 2^23) or a
     workgroup size that is not a multiple of 64 from 64 to 1024."""

@@ -103,6 +103,21 @@ def test_grid_capped_loops(estimator, mapping, waves):
         check(estimator, w, inputs, f"{mapping} W={waves} grid_cap=13")
 
 
+def test_ticket_bases_across_mixed_lookback_launches():
+    """Grid-capped (ticketed), ticket-ordered and one-tile-per-workgroup
+    look-back calls in turn on one scratch: every ticketed call's tickets
+    must start where the last ticketed call's ended."""
+    forms = [(0, 0), (5, 0), (0, rlscan.FLAG_TICKETS), (9, rlscan.FLAG_TICKETS), (2, 0),
+             (64, 0), (1, 0)]
+    for i, (cap, flags) in enumerate(forms * 2):
+        N, T = [(3, 5000), (2, 70000), (11, 999)][i % 3]
+        est = ["gae", "episodic_prefix_sum", "vtrace"][i % 3]
+        rlscan.rlscan_set_launch_override(rlscan.MAP_LOOKBACK, 1, 4, cap, flags)
+        w, inputs = case(est, N, T, seed=i)
+        check(est, w, inputs, f"mixed look-back launches, call {i} cap={cap} flags={flags}")
+    assert rlscan.rlscan_lookback_timeouts() == 0
+
+
 @pytest.mark.parametrize("estimator", ESTIMATORS)
 def test_flag_patterns(estimator):
     N, T = 6, 700
@@ -345,6 +360,23 @@ def test_stream_mix_kernel(reads, writes):
     want = acc[:, None].expand(g, writes, 256, 4).reshape(-1, 4).clone()
     want[nw:] = -1.0
     assert torch.equal(dst, want)
+
+
+@pytest.mark.parametrize("ain,aout,words,cap", [(1, 1, 1, 0), (5, 1, 2, 0), (3, 2, 4, 2),
+                                                 (16, 1, 1, 3), (2, 4, 3, 8)])
+def test_stream_mix_arrays_kernel(ain, aout, words, cap):
+    """The reference kernel in a scan's pattern: word i of every output array
+    is the sum of word i of every input array.  Small integers (exact float32
+    sums); arrays whose length is not a multiple of a workgroup's span."""
+    n_in, n_out = 37 * 256 * words - 5, 37 * 256 * words - 3  # 16-byte words per array
+    src = torch.randint(-8, 9, (ain, n_in, 4), device="cuda").float()
+    dst = torch.full((aout, n_out, 4), -1.0, device="cuda")
+    rlscan.rlscan_stream_mix_arrays(dst, src, arrays_in=ain, arrays_out=aout, words=words,
+                                    workgroups_per_cu=cap)
+    torch.cuda.synchronize()
+    acc = torch.zeros(max(n_in, n_out), 4, device="cuda")
+    acc[:n_in] = src.sum(0)
+    assert torch.equal(dst, acc[None, :n_out].expand(aout, n_out, 4))
 
 
 @pytest.mark.parametrize("estimator", ESTIMATORS)
