@@ -153,7 +153,12 @@ int auto_rounds(int est, int64_t NT) {
 //    and V-trace, the same within 4 % for the others.
 //    Where T divides no such tile, the smallest tile whose whole rows fill
 //    at least 7/8 of it (100-step rows: 500 of 512 elements), else the
-//    best-filled one if its rows fill at least 3/4.
+//    best-filled one if its rows fill at least 3/4.  Retrace and the prefix
+//    sum take the smallest tile filled to 3/4: measured at 2^19 elements,
+//    one wave beat two for Retrace at T = 96, 100 and 200 (9.20 / 9.56 /
+//    9.56 us against 9.91 / 10.15 / 9.84) and for the prefix sum at T = 96
+//    and 100 (3.64 / 3.92 against 3.84 / 4.06); for the others the two were
+//    within a few per cent, either way between runs.
 int auto_waves(int est, int rounds, int64_t N, int64_t T) {
     if (rounds == 4) return 4;
     if (rounds == 1) {
@@ -162,14 +167,16 @@ int auto_waves(int est, int rounds, int64_t N, int64_t T) {
         const int last = est == RLSCAN_EST_RETRACE ? 4 : 8;
         for (int w = first; w <= last; w *= 2)
             if ((int64_t(kWave) * w * kChunk) % T == 0) return w;
+        const int64_t enough =  // fill (in 1/1024 of the tile) taken at once
+            (est == RLSCAN_EST_RETRACE || est == RLSCAN_EST_PREFIX_SUM) ? 768 : 896;
         int best = 0;
-        int64_t best_fill = 0;  // in 1/1024 of the tile
+        int64_t best_fill = 0;
         for (int w = first; w <= last; w *= 2) {
             const int64_t cap = int64_t(kWave) * w * kChunk;
             int64_t span = 0, tiles = 0;
             if (!packed_layout(N, T, cap, span, tiles)) continue;
             const int64_t fill = span * 1024 / cap;
-            if (fill >= 896) return w;
+            if (fill >= enough) return w;
             if (fill > best_fill) best = w, best_fill = fill;
         }
         if (best_fill >= 768) return best;

@@ -140,10 +140,13 @@ def test_plan_mapping_choice(lib):
     assert p["threads"] == 512 and p["mapping"] == rlscan.MAP_PACKED
     assert p["tile_span"] == p["tile_elems"]
     # rows that divide no tile: the smallest tile whose whole rows fill at
-    # least 7/8 of it (a span that is a multiple of 4), else the best-filled
-    # one if at least 3/4 full; the remaining lanes idle
+    # least 7/8 of it (3/4 for Retrace and the prefix sum; a span that is a
+    # multiple of 4), else the best-filled one if at least 3/4 full; the
+    # remaining lanes idle
     for est, N, T, threads, span, tiles in (
-            ("gae", 4096, 100, 128, 500, 820), ("episodic_prefix_sum", 4096, 100, 128, 500, 820),
+            ("gae", 4096, 100, 128, 500, 820), ("episodic_prefix_sum", 4096, 100, 64, 200, 2048),
+            ("discounted_returns", 4096, 100, 128, 500, 820),
+            ("retrace", 4096, 96, 64, 192, 2048), ("retrace", 4096, 200, 64, 200, 4096),
             ("gae", 4096, 200, 256, 1000, 820), ("discounted_returns", 1024, 96, 128, 480, 205),
             ("retrace", 4096, 20, 64, 240, 342), ("gae", 5, 1000, 256, 1000, 5),
             ("eligibility_traces", 11, 7, 64, 256, 1)):
