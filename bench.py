@@ -20,14 +20,20 @@ Beside it: the same seven calls made one by one on one stream (eager, as one
 HIP graph replay per step, and on one warm buffer set), the grouped step at
 each wave count, and each estimator's own average launch duration, measured
 with HIP events around replays of a graph of M back-to-back launches over M
-buffer sets in distinct memory (M * bytes >= COLD_BYTES).  The
+buffer sets in distinct memory (M * bytes >= COLD_BYTES), beside the
+launch floor of its grid (an empty kernel) and the full call from Python.
+Every other workload is timed too: GAE on 64 x 512, the truncation path,
+the six-shape 2^19-element sweep and rows of 100 steps (`configs`); the
 long-sequence workload (8 x 2^20 steps, four estimators, decoupled
 look-back; timed over back-to-back calls, and with events around each
 call), the same rollout streamed through the carry calls, a supplementary
-large-batch workload (2^20 x 32, packed), the estimator variants (one-byte
-flags, V-trace options, float prefix sum), the bandwidth of a plain
-streaming copy moving the same bytes, and the float64 oracle timed on one
-host core are reported as well.
+large-batch workload (2^20 x 32, packed) and the estimator variants
+(one-byte flags, V-trace options, float prefix sum).  Each call's figures
+carry its stream ceiling: the fastest of the library's streaming kernels
+(spans, or the scans' own array pattern with a cap on resident workgroups)
+moving the same bytes in the same read:write mix.  The float64 oracle is
+timed on the host, on one core and with the rows split over forked
+processes.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
