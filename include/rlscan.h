@@ -45,8 +45,10 @@
  *             step t-1; every row starts from 0.
  * Parameters  gamma, lambda in [0, 1] and finite; rho_bar, c_bar, rho_bar_pg
  *             > 0 (+inf allowed, NaN rejected).
- * Streams     Work is enqueued on `stream` (NULL = the device's null stream)
- *             and the call returns without synchronising.  Results are valid
+ * Streams     Work is enqueued on `stream` (NULL = the device's null stream),
+ *             which must belong to the current HIP device (the library's
+ *             own scratch is taken on the current device), and the call
+ *             returns without synchronising.  Results are valid
  *             once the stream has completed.  Faults inside kernels surface at
  *             the caller's next synchronisation, as for any HIP kernel.
  * Empty       N == 0 or T == 0 is a successful no-op (pointers may be NULL).

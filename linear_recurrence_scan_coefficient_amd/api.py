@@ -84,6 +84,8 @@ class grouped:
         if not calls:
             return
         tensors = [t for g, _ in calls for part in g.keep for t in part]
+        index = next(t for t in tensors if isinstance(t, torch.Tensor)).get_device()
+        _one_device(index, [t for t in tensors if isinstance(t, torch.Tensor)])
 
         def run(stream):
             try:
@@ -94,7 +96,8 @@ class grouped:
                 for _, alone in calls:  # not groupable: the same calls one by one
                     alone(stream)
 
-        _on_stream(run, self.stream, tensors)
+        with _on_device(index):
+            _on_stream(run, self.stream, tensors)
 
 
 def _as_stream(stream):
@@ -124,15 +127,47 @@ def _on_stream(fn, stream, tensors):
             t.record_stream(s)
 
 
+def _one_device(index, tensors):
+    """Every tensor of a call on the GPU of index `index`."""
+    for t in tensors:
+        if t is not None and t.get_device() != index:
+            raise ValueError(f"every tensor of a call must be on cuda:{index}, got one on "
+                             f"{t.device}")
+
+
+class _on_device:
+    """Makes GPU `index` current for the block (the library launches on, and
+    takes its scratch from, the current device)."""
+
+    def __init__(self, index):
+        self.index, self.prev = index, None
+
+    def __enter__(self):
+        cur = torch.cuda.current_device()
+        if cur != self.index:
+            self.prev = cur
+            torch.cuda.set_device(self.index)
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            torch.cuda.set_device(self.prev)
+        return False
+
+
 def _submit(estimator, ins, outs, params, alone, stream, carry, extra=()):
     """Runs `alone(stream)` now, or defers the call to the innermost active
     `grouped` block (plain calls on the current stream only).  `extra`: the
     call's other tensors (carries, Retrace's next-chunk arrays)."""
+    index = outs[0].get_device()
+    _one_device(index, (*ins, *extra))
+    if isinstance(stream, torch.cuda.Stream) and stream.device.index != index:
+        raise ValueError(f"stream is on {stream.device}, the tensors on cuda:{index}")
     stack = getattr(_local, "groups", None)
     if stack and not carry and stream is None:
         stack[-1].calls.append((rlscan.GroupCall(estimator, ins, outs, **params), alone))
     else:
-        _on_stream(alone, stream, (*ins, *outs, *extra))
+        with _on_device(index):
+            _on_stream(alone, stream, (*ins, *outs, *extra))
 
 
 # ------------------------------------------------------------------ marshalling

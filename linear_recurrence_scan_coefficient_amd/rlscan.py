@@ -198,6 +198,9 @@ def _ptr(t, dtype=torch.float32, shape=None, name="tensor"):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.numel() > 0 and t.device.type != "cuda":
         raise ValueError(f"{name} must live on the GPU")
+    if t.numel() > 0 and t.get_device() != torch.cuda.current_device():
+        raise ValueError(f"{name} must live on the current device (cuda:"
+                         f"{torch.cuda.current_device()}), got {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
