@@ -84,8 +84,10 @@ class grouped:
         if not calls:
             return
         tensors = [t for g, _ in calls for part in g.keep for t in part]
-        index = next(t for t in tensors if isinstance(t, torch.Tensor)).get_device()
-        _one_device(index, [t for t in tensors if isinstance(t, torch.Tensor)])
+        index = torch.cuda.current_device()
+        if _several_gpus():
+            index = next(t for t in tensors if isinstance(t, torch.Tensor)).get_device()
+            _one_device(index, [t for t in tensors if isinstance(t, torch.Tensor)])
 
         def run(stream):
             try:
@@ -127,6 +129,18 @@ def _on_stream(fn, stream, tensors):
             t.record_stream(s)
 
 
+_gpus = None
+
+
+def _several_gpus():
+    """Whether more than one GPU is visible (with one, every device tensor
+    is on the current device and the checks below have nothing to find)."""
+    global _gpus
+    if _gpus is None:
+        _gpus = torch.cuda.device_count()
+    return _gpus > 1
+
+
 def _one_device(index, tensors):
     """Every tensor of a call on the GPU of index `index`."""
     for t in tensors:
@@ -158,16 +172,20 @@ def _submit(estimator, ins, outs, params, alone, stream, carry, extra=()):
     """Runs `alone(stream)` now, or defers the call to the innermost active
     `grouped` block (plain calls on the current stream only).  `extra`: the
     call's other tensors (carries, Retrace's next-chunk arrays)."""
-    index = outs[0].get_device()
-    _one_device(index, (*ins, *extra))
-    if isinstance(stream, torch.cuda.Stream) and stream.device.index != index:
-        raise ValueError(f"stream is on {stream.device}, the tensors on cuda:{index}")
+    several = _several_gpus()
+    if several:
+        index = outs[0].get_device()
+        _one_device(index, (*ins, *extra))
+        if isinstance(stream, torch.cuda.Stream) and stream.device.index != index:
+            raise ValueError(f"stream is on {stream.device}, the tensors on cuda:{index}")
     stack = getattr(_local, "groups", None)
     if stack and not carry and stream is None:
         stack[-1].calls.append((rlscan.GroupCall(estimator, ins, outs, **params), alone))
-    else:
+    elif several:
         with _on_device(index):
             _on_stream(alone, stream, (*ins, *outs, *extra))
+    else:
+        _on_stream(alone, stream, (*ins, *outs, *extra))
 
 
 # ------------------------------------------------------------------ marshalling

@@ -189,6 +189,18 @@ def _check(status: int):
 
 
 # ------------------------------------------------------------------ marshalling
+_gpus = None
+
+
+def _several_gpus():
+    """Whether more than one GPU is visible (with one, every device tensor is
+    on the current device)."""
+    global _gpus
+    if _gpus is None:
+        _gpus = torch.cuda.device_count()
+    return _gpus > 1
+
+
 def _ptr(t, dtype=torch.float32, shape=None, name="tensor"):
     if t is None:
         return None
@@ -198,7 +210,7 @@ def _ptr(t, dtype=torch.float32, shape=None, name="tensor"):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.numel() > 0 and t.device.type != "cuda":
         raise ValueError(f"{name} must live on the GPU")
-    if t.numel() > 0 and t.get_device() != torch.cuda.current_device():
+    if t.numel() > 0 and _several_gpus() and t.get_device() != torch.cuda.current_device():
         raise ValueError(f"{name} must live on the current device (cuda:"
                          f"{torch.cuda.current_device()}), got {t.device}")
     if not t.is_contiguous():
