@@ -296,3 +296,39 @@ def test_calls_on_a_stream_that_is_not_current():
                   "retrace on another stream")
     assert_parity({"advantages": adv.cpu().numpy()}, oracle_outputs("gae", inputs_g, wg),
                   "grouped gae on another stream")
+
+
+@pytest.fixture
+def several_gpus_path():
+    """Takes the calls' several-GPU path (one device check per tensor, the
+    tensors' device made current) on a box with one GPU."""
+    from linear_recurrence_scan_coefficient_amd import rlscan
+    saved = (api._gpus, rlscan._gpus)
+    api._gpus = rlscan._gpus = 2
+    yield
+    api._gpus, rlscan._gpus = saved
+
+
+@pytest.mark.parametrize("estimator", ESTIMATORS)
+def test_several_gpu_checks_leave_results_unchanged(estimator, several_gpus_path):
+    w, inputs = case(estimator)
+    d = {k: dev(v) for k, v in inputs.items()}
+    assert_parity(host(call(estimator, d, w)), oracle_outputs(estimator, inputs, w),
+                  f"several-GPU path {estimator}")
+    with api.grouped():
+        pending = call(estimator, d, w)
+    torch.cuda.synchronize()
+    assert_parity(host(pending), oracle_outputs(estimator, inputs, w),
+                  f"several-GPU path, grouped {estimator}")
+    s = torch.cuda.Stream()
+    out = call(estimator, d, w) if estimator != "gae" else {"advantages": api.compute_gae(
+        d["rewards"], d["values"], d["terminated"], gamma=w.gamma, lambda_=w.lam,
+        bootstrap_value=d.get("bootstrap_value"), truncateds=d.get("truncated"),
+        bootstrap_values=d.get("bootstrap_values"), stream=s)}
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert_parity(host(out), oracle_outputs(estimator, inputs, w), f"several-GPU path, stream")
+    # the thin binding's own per-pointer check on the same path
+    from linear_recurrence_scan_coefficient_amd import device
+    assert_parity(device.run(estimator, inputs, w), oracle_outputs(estimator, inputs, w),
+                  f"several-GPU path, binding {estimator}")
