@@ -90,8 +90,9 @@
  *             or 1000) launch one kernel and nothing else, and may be
  *             captured into a HIP graph.  A call that needs the
  *             look-back (rlscan_plan: RLSCAN_MAP_LOOKBACK) returns
- *             RLSCAN_ERR_CAPTURE on a capturing stream, since its replay
- *             would reuse a stale ticket base.
+ *             RLSCAN_ERR_CAPTURE on a capturing stream: a replay would
+ *             reuse the call's tag and scratch (rlscan_gae_noalloc, whose
+ *             scratch never moves, is the exception; see there).
  * Thread      All entry points may be called concurrently from several host
  * safety      threads.
  */
@@ -113,7 +114,8 @@ typedef enum {
     RLSCAN_ERR_ALIAS = -4, /* an output pointer equals an input or other output */
     RLSCAN_ERR_HIP = -5,   /* a HIP runtime call or kernel launch failed        */
     RLSCAN_ERR_ALLOC = -6, /* the library could not allocate its scratch        */
-    RLSCAN_ERR_CAPTURE = -7, /* a look-back launch on a stream under graph capture */
+    RLSCAN_ERR_CAPTURE = -7, /* a look-back launch on a stream under graph capture
+                               (rlscan_gae_noalloc: one that would need tickets) */
     RLSCAN_ERR_SCRATCH = -8  /* rlscan_gae_noalloc: more look-back tiles than its
                                 fixed array holds                                */
 } rlscan_status;
@@ -380,8 +382,15 @@ int rlscan_episodic_prefix_sum_u8(const int32_t* x, const uint8_t* dones,
  *            GPU race on it: issue them on one stream, and do not let them
  *            overlap with the library's other look-back launches on that GPU
  *            (unlike those, they are not ordered across streams).
- *   Graphs   As for rlscan_gae: a look-back call returns RLSCAN_ERR_CAPTURE on
- *            a capturing stream; packed calls may be captured. */
+ *   Graphs   Every call may be captured into a HIP graph.  A captured
+ *            look-back call records a clear of its status words before its
+ *            scan and takes a call tag reserved for captured calls (eager
+ *            calls never use it), so each replay starts from cleared words
+ *            and reads no other call's.  Replays share the array as calls
+ *            do: keep them from overlapping each other and other look-back
+ *            work of the GPU.  (Under a launch override that makes
+ *            workgroups loop over tiles, a capturing stream gets
+ *            RLSCAN_ERR_CAPTURE: tickets cannot be replayed.) */
 int rlscan_gae_noalloc(const float* rewards, const float* values, const float* bootstrap_value,
                        const float* terminated, const float* truncated,
                        const float* bootstrap_values, const float* carry_in, float* advantages,

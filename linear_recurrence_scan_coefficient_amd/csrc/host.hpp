@@ -68,6 +68,10 @@ struct ScratchSource {
 // words and counters are cleared this way, never by a memset node).
 hipError_t clear_words(uint64_t* p, int64_t words, hipStream_t stream);
 
+// The call tag of look-back calls captured into a graph (fixed scratch
+// only); eager calls take the tags below it.
+constexpr uint32_t kCaptureTag = kLastTag;
+
 // rlscan_gae_carry with its look-back scratch taken from `src`.
 int gae_with_scratch(const float* rewards, const float* values, const float* bootstrap_value,
                      const float* terminated, const float* truncated,
@@ -281,10 +285,18 @@ int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream,
     if (pl.mapping == RLSCAN_MAP_PACKED) {
         return fn(geo, lb, pl) == hipSuccess ? RLSCAN_OK : RLSCAN_ERR_HIP;
     }
-    // a captured look-back launch would replay with a stale ticket base
+    // tile = blockIdx needs every tile to have its own workgroup
+    const bool tickets = pl.grid < pl.tiles || (g_override.flags.load() & RLSCAN_FLAG_TICKETS);
+    // Under graph capture a replay would reuse the call's tag (reading the
+    // last replay's status words as its own), its ticket base, and a
+    // scratch buffer that later calls may move.  Only the fixed array,
+    // whose address never changes, serves captured look-back calls, with
+    // one tile per workgroup: each records a clear of its status words
+    // before the scan and takes the tag reserved for captured calls.
     hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &capture) != hipSuccess) return RLSCAN_ERR_HIP;
-    if (capture != hipStreamCaptureStatusNone) return RLSCAN_ERR_CAPTURE;
+    const bool captured = capture != hipStreamCaptureStatusNone;
+    if (captured && (src == nullptr || tickets)) return RLSCAN_ERR_CAPTURE;
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return RLSCAN_ERR_HIP;
     Scratch* sc = src != nullptr ? src->get(device) : scratch_for(device, stream);
@@ -292,23 +304,31 @@ int run(int est, int64_t N, int64_t T, bool vec, bool carry, hipStream_t stream,
     std::lock_guard<std::mutex> g(sc->m);
     const int rc = ensure_capacity(sc, stream, pl.tiles * entries);
     if (rc != RLSCAN_OK) return rc;
-    // tile = blockIdx needs every tile to have its own workgroup
-    const bool tickets = pl.grid < pl.tiles || (g_override.flags.load() & RLSCAN_FLAG_TICKETS);
     lb.use_tickets = tickets ? 1u : 0u;
     lb.status = sc->status;
     lb.ticket_counter = sc->counter;
     lb.timeouts = reinterpret_cast<unsigned int*>(sc->counter + 1);
     lb.ticket_base = sc->next_ticket;
-    if (sc->epoch >= kLastTag) {
-        // the call tags (at most kLastTag: their top bit marks a one-word
-        // integer value) are about to repeat: clear the status words
+    if (captured) {
+        // cleared words carry tag 0, which no call uses
         if (clear_words(reinterpret_cast<uint64_t*>(sc->status),
-                        static_cast<int64_t>(sizeof(TileStatus) / 8) * sc->capacity,
+                        static_cast<int64_t>(sizeof(TileStatus) / 8) * pl.tiles * entries,
                         stream) != hipSuccess)
             return RLSCAN_ERR_HIP;
-        sc->epoch = 0;
+        lb.tag = kCaptureTag;
+    } else {
+        if (sc->epoch >= kCaptureTag - 1) {
+            // the eager call tags (below kCaptureTag; at most kLastTag in
+            // all, as a one-word integer value's top bit marks its form)
+            // are about to repeat: clear the status words
+            if (clear_words(reinterpret_cast<uint64_t*>(sc->status),
+                            static_cast<int64_t>(sizeof(TileStatus) / 8) * sc->capacity,
+                            stream) != hipSuccess)
+                return RLSCAN_ERR_HIP;
+            sc->epoch = 0;
+        }
+        lb.tag = static_cast<uint32_t>(++sc->epoch);
     }
-    lb.tag = static_cast<uint32_t>(++sc->epoch);
     const bool give_up = (g_override.flags.load() & RLSCAN_FLAG_LOOKBACK_GIVE_UP) != 0;
     lb.read_tag = give_up ? kNeverTag : lb.tag;
     lb.max_polls = give_up ? 8u : kMaxPolls;

@@ -78,3 +78,61 @@ def test_noalloc_packed_and_plain_match_oracle():
         torch.cuda.synchronize()
         assert_parity({"advantages": adv.cpu().numpy()}, oracle_outputs("gae", inputs, w),
                       f"noalloc {N}x{T}")
+
+
+def test_noalloc_lookback_calls_captured_into_a_graph():
+    """Look-back calls of rlscan_gae_noalloc captured into a HIP graph (each
+    records a clear of its status words before its scan): three replays,
+    with eager calls of the library on the same array between them, each
+    matching the eager rlscan_gae_carry results; a capture that would need
+    tickets is refused."""
+    from linear_recurrence_scan_coefficient_amd import rlscan
+    rlscan.rlscan_set_launch_override()
+    before = rlscan.rlscan_lookback_timeouts()
+    cases = []
+    for i, (N, T) in enumerate(((8, 1 << 17), (3, 5003))):
+        assert rlscan.rlscan_plan("gae", N, T)["mapping"] == rlscan.MAP_LOOKBACK
+        w, inputs, d, carry = _gae_inputs(N, T, seed=60 + i)
+        want = _both(d, carry, N, T)["carry"]
+        adv = torch.empty((N, T), dtype=torch.float32, device="cuda")
+        co = torch.empty((N,), dtype=torch.float32, device="cuda")
+        cases.append((N, T, d, carry, adv, co, want))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for N, T, d, carry, adv, co, _ in cases:
+            rlscan.rlscan_gae_noalloc(d["rewards"], d["values"], d["bootstrap_value"],
+                                      d["terminated"], d["truncated"], d["bootstrap_values"], adv,
+                                      0.99, 0.95, carry_in=carry, carry_out=co)
+    _, _, d_other, carry_other = _gae_inputs(5, 7001, seed=70)
+    for replay in range(3):
+        for *_, adv, co, _ in cases:
+            adv.fill_(float("nan"))
+            co.fill_(float("nan"))
+        torch.cuda.synchronize()
+        print(f"noalloc graph replay {replay}", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        for N, T, _, _, adv, co, want in cases:
+            _close(adv.cpu().numpy(), want[0], f"replay {replay} {N}x{T} advantages")
+            _close(co.cpu().numpy(), want[1], f"replay {replay} {N}x{T} carry_out")
+        # eager look-back work on the same array (and the allocating path)
+        # between the replays
+        got = _both(d_other, carry_other, 5, 7001)
+        _close(got["noalloc"][0], got["carry"][0], f"eager call after replay {replay}")
+    del g
+    # workgroups looping over tiles (tickets) cannot be replayed: refused
+    N, T, d, carry, adv, co, _ = cases[1]
+    rlscan.rlscan_set_launch_override(grid_cap=2)
+    g2 = torch.cuda.CUDAGraph()
+    try:
+        with pytest.raises(rlscan.RlscanError) as err:
+            with torch.cuda.graph(g2):
+                rlscan.rlscan_gae_noalloc(d["rewards"], d["values"], d["bootstrap_value"],
+                                          d["terminated"], d["truncated"],
+                                          d["bootstrap_values"], adv, 0.99, 0.95)
+        assert err.value.status == rlscan.RLSCAN_ERR_CAPTURE
+    finally:
+        rlscan.rlscan_set_launch_override()
+    torch.cuda.synchronize()
+    assert rlscan.rlscan_lookback_timeouts() == before
