@@ -43,6 +43,8 @@ than 4, 6 or 8), they run one by one instead.
 """
 from __future__ import annotations
 
+import ctypes
+import struct
 import threading
 
 import torch
@@ -83,23 +85,59 @@ class grouped:
         calls, self.calls = self.calls, []
         if not calls:
             return
-        tensors = [t for g, _ in calls for part in g.keep for t in part]
-        index = torch.cuda.current_device()
-        if _several_gpus():
-            index = next(t for t in tensors if isinstance(t, torch.Tensor)).get_device()
-            _one_device(index, [t for t in tensors if isinstance(t, torch.Tensor)])
+        # the rlscan_call array, packed straight from the calls' tensors
+        # (already checked by their compute_* call)
+        buf = bytearray(_CALL_SIZE * len(calls))
+        for k, c in enumerate(calls):
+            ins = [0 if t is None else t.data_ptr() for t in c.ins]
+            outs = [0 if t is None else t.data_ptr() for t in c.outs]
+            struct.pack_into(_CALL_FMT, buf, k * _CALL_SIZE, c.est, c.flags, c.N, c.T, c.A,
+                             *c.params, 0.0, *ins, *([0] * (8 - len(ins))), *outs,
+                             *([0] * (2 - len(outs))))
+        arr = (rlscan.Call * len(calls)).from_buffer(buf)
+        first = calls[0].outs[0]
 
         def run(stream):
-            try:
-                rlscan.rlscan_group([g for g, _ in calls], stream)
-            except rlscan.RlscanError as e:
-                if e.status != rlscan.RLSCAN_ERR_PARAM:
-                    raise
-                for _, alone in calls:  # not groupable: the same calls one by one
-                    alone(stream)
+            rc = _lib().rlscan_group(arr, len(calls), _raw_stream(stream, first))
+            if rc == rlscan.RLSCAN_ERR_PARAM:
+                for c in calls:  # not groupable: the same calls one by one
+                    c.alone(stream)
+            else:
+                _check(rc)
 
+        several = _several_gpus()
+        if self.stream is None and not several:
+            run(None)
+            return
+        tensors = [t for c in calls for t in (*c.ins, *c.outs) if t is not None]
+        index = first.get_device()
+        if several:
+            _one_device(index, tensors)
         with _on_device(index):
             _on_stream(run, self.stream, tensors)
+
+
+# The layout of rlscan_call (include/rlscan.h): estimator, flags, N, T, A,
+# gamma, lam, rho_bar, c_bar, rho_bar_pg, reserved, inp[8], out[2].
+_CALL_FMT = "@iiqqqffffff8P2P"
+_CALL_SIZE = struct.calcsize(_CALL_FMT)
+assert _CALL_SIZE == ctypes.sizeof(rlscan.Call)
+
+
+class _Deferred:
+    """A compute_* call held by a `grouped` block until it ends."""
+    __slots__ = ("est", "flags", "N", "T", "A", "params", "ins", "outs", "alone")
+
+    def __init__(self, estimator, ins, outs, params, alone, byte):
+        self.est = rlscan.ESTIMATOR_IDS[estimator]
+        self.flags = rlscan.CALL_BYTE_FLAGS if byte else 0
+        self.N, self.T = ins[0].shape
+        self.A = ins[1].shape[2] if estimator == "retrace" else 1
+        rho_bar = params.get("rho_bar", 1.0)
+        rbpg = params.get("rho_bar_pg")
+        self.params = (params.get("gamma", 0.99), params.get("lam", 0.95), rho_bar,
+                       params.get("c_bar", 1.0), rho_bar if rbpg is None else rbpg)
+        self.ins, self.outs, self.alone = ins, outs, alone
 
 
 def _as_stream(stream):
@@ -168,10 +206,11 @@ class _on_device:
         return False
 
 
-def _submit(estimator, ins, outs, params, alone, stream, carry, extra=()):
+def _submit(estimator, ins, outs, params, alone, stream, carry, extra=(), byte=False):
     """Runs `alone(stream)` now, or defers the call to the innermost active
     `grouped` block (plain calls on the current stream only).  `extra`: the
-    call's other tensors (carries, Retrace's next-chunk arrays)."""
+    call's other tensors (carries, Retrace's next-chunk arrays); `byte`: its
+    flags are one byte each."""
     several = _several_gpus()
     if several:
         index = outs[0].get_device()
@@ -180,7 +219,9 @@ def _submit(estimator, ins, outs, params, alone, stream, carry, extra=()):
             raise ValueError(f"stream is on {stream.device}, the tensors on cuda:{index}")
     stack = getattr(_local, "groups", None)
     if stack and not carry and stream is None:
-        stack[-1].calls.append((rlscan.GroupCall(estimator, ins, outs, **params), alone))
+        stack[-1].calls.append(_Deferred(estimator, ins, outs, params, alone, byte))
+    elif stream is None and not several:
+        alone(None)
     elif several:
         with _on_device(index):
             _on_stream(alone, stream, (*ins, *outs, *extra))
@@ -225,10 +266,10 @@ def _tensor(t, name, shape, dtype=_F32):
     None."""
     if t is None:
         return None
-    _gpu(t, name)
-    if t.dtype is not dtype:
-        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
-    if t.shape != shape:
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype is dtype and t.shape == shape):
+        _gpu(t, name)  # raises for a non-tensor or a host tensor
+        if t.dtype is not dtype:
+            raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     return t if t.is_contiguous() else t.contiguous()
 
@@ -246,6 +287,18 @@ def _flags(shape, *named):
     """The call's flag tensors (name, tensor pairs), all float32 or all one
     byte (bool / uint8): as given when they already are, else each turned
     into bool (set iff != 0).  Returns (tensors, one_byte)."""
+    # the common case: contiguous float32 device flags of the right shape
+    fast = []
+    for n, t in named:
+        if t is None:
+            fast.append(None)
+        elif (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype is _F32 and
+              t.shape == shape and t.is_contiguous()):
+            fast.append(t)
+        else:
+            break
+    else:
+        return fast, False
     given = [(n, t) for n, t in named if t is not None]
     for n, t in given:
         _gpu(t, n)
@@ -302,7 +355,7 @@ def compute_gae(rewards, values, terminateds, gamma=0.99, lambda_=0.95, *,
         else:
             _check(lib.rlscan_gae(*P, out.data_ptr(), N, T, g, lam, h))
     _submit("gae", ins, (out,), dict(gamma=g, lam=lam), alone, stream,
-            ci is not None or co is not None, (ci, co))
+            ci is not None or co is not None, (ci, co), byte)
     return (out, co) if return_carry else out
 
 
@@ -331,7 +384,7 @@ def compute_lambda_returns(rewards, values, terminateds, gamma=0.99, lambda_=0.9
         else:
             _check(lib.rlscan_lambda_returns(*P, out.data_ptr(), N, T, g, lam, h))
     _submit("lambda_returns", ins, (out,), dict(gamma=g, lam=lam), alone, stream,
-            ci is not None or co is not None, (ci, co))
+            ci is not None or co is not None, (ci, co), byte)
     return (out, co) if return_carry else out
 
 
@@ -361,7 +414,7 @@ def compute_discounted_returns(rewards, terminateds, gamma=0.99, *, bootstrap_va
         else:
             _check(lib.rlscan_discounted_returns(*P, out.data_ptr(), N, T, g, h))
     _submit("discounted_returns", ins, (out,), dict(gamma=g), alone, stream,
-            ci is not None or co is not None, (ci, co))
+            ci is not None or co is not None, (ci, co), byte)
     return (out, co) if return_carry else out
 
 
@@ -401,7 +454,7 @@ def compute_vtrace(rewards, values, log_rhos, terminateds, gamma=0.99, rho_bar=1
             _check(lib.rlscan_vtrace(*P, *o, N, T, g, rb, cb, h))
     _submit("vtrace", ins, (vs, pg),
             dict(gamma=g, lam=lam, rho_bar=rb, c_bar=cb, rho_bar_pg=rbpg), alone, stream,
-            ci is not None or co is not None, (ci, co))
+            ci is not None or co is not None, (ci, co), byte)
     return (vs, pg, co) if return_carry else (vs, pg)
 
 
@@ -453,7 +506,7 @@ def compute_retrace(rewards, next_q_values_all, next_target_probs, actions, beha
         else:
             _check(lib.rlscan_retrace(*P, out.data_ptr(), N, T, A, g, lam, h))
     _submit("retrace", ins, (out,), dict(gamma=g, lam=lam), alone, stream,
-            ci is not None or co is not None, (ci, co, nat, nbp))
+            ci is not None or co is not None, (ci, co, nat, nbp), byte)
     return (out, co) if return_carry else out
 
 
@@ -481,7 +534,7 @@ def compute_eligibility_traces(x, dones, gamma=0.99, lambda_=0.95, *, carry_in=N
         else:
             _check(lib.rlscan_eligibility_traces(*P, out.data_ptr(), N, T, g, lam, h))
     _submit("eligibility_traces", ins, (out,), dict(gamma=g, lam=lam), alone, stream,
-            ci is not None or co is not None, (ci, co))
+            ci is not None or co is not None, (ci, co), byte)
     return (out, co) if return_carry else out
 
 
@@ -528,5 +581,5 @@ def compute_episodic_prefix_sum(x, dones, *, carry_in=None, return_carry=False, 
         else:
             _check(lib.rlscan_episodic_prefix_sum(*P, out.data_ptr(), N, T, h))
     _submit("episodic_prefix_sum", ins, (out,), {}, alone, stream,
-            ci is not None or co is not None, (ci, co))
+            ci is not None or co is not None, (ci, co), byte)
     return (out, co) if return_carry else out
