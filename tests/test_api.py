@@ -332,3 +332,36 @@ def test_several_gpu_checks_leave_results_unchanged(estimator, several_gpus_path
     from linear_recurrence_scan_coefficient_amd import device
     assert_parity(device.run(estimator, inputs, w), oracle_outputs(estimator, inputs, w),
                   f"several-GPU path, binding {estimator}")
+
+
+def test_grouped_block_captured_into_a_torch_graph():
+    """The seven production calls in a `with api.grouped():` block captured
+    into a torch CUDA graph (packed calls launch one kernel and nothing
+    else): replays with new inputs copied into the captured tensors, eager
+    calls between the replays, each replay equal to eager calls on the same
+    inputs."""
+    w = workloads.get("production_4096x128")
+    static = {e: {k: dev(v) for k, v in workloads.inputs_for(e, w, 31).items()}
+              for e in ESTIMATORS}
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        with api.grouped():
+            outs = _all_seven(static, w)
+    for replay, seed in enumerate((32, 33, 34)):
+        fresh = {e: workloads.inputs_for(e, w, seed) for e in ESTIMATORS}
+        for e in ESTIMATORS:
+            for k, v in fresh[e].items():
+                if v is not None:
+                    static[e][k].copy_(torch.from_numpy(np.ascontiguousarray(v)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eager = _all_seven({e: {k: dev(v) for k, v in fresh[e].items()} for e in ESTIMATORS}, w)
+        torch.cuda.synchronize()
+        for e in ESTIMATORS:
+            got, want = host(outs[e]), host(eager[e])
+            for k in want:
+                ref = want[k].astype(np.float64)
+                err = np.abs(got[k].astype(np.float64) - ref) / (1 + np.abs(ref))
+                assert err.max() <= 1e-6, (replay, e, k, float(err.max()))
