@@ -17,7 +17,8 @@
 // Each call: K tiles over one status buffer shared by every call, as the
 // library's scratch is; one thread per tile: publish the aggregate (or the
 // inclusive value when already known), walk back, publish the inclusive
-// value.  The buffer starts each call holding words of other tags, of both
+// value (some tiles after a long delay, so that walks fold aggregates over
+// several windows).  The buffer starts each call holding words of other tags, of both
 // integer forms (stale words of earlier calls, or of no call).  Every
 // tile's entering value must equal the sequential fold of the aggregates
 // before it, exactly: values are integers and a is 0 or 1 (float32 steps)
@@ -69,12 +70,16 @@ template <> struct Value<StepW> { using type = double; };
 
 // The look-back walk of one tile, lane by lane (lane 63: the nearest
 // predecessor).
+// Walks that folded more than one window (every entry of a 64-tile window
+// an aggregate, none cutting the chain), over all trials.
+std::atomic<long> g_deep_walks{0};
+
 template <class A>
 typename Value<A>::type walk(TileStatus* base, uint32_t tag, int64_t tile, bool& gave_up) {
     using V = typename Value<A>::type;
     A acc = identity_step(A{});
     int64_t top = tile - 1;
-    for (;;) {
+    for (int windows = 1;; ++windows) {
         A s[kWave];
         int width = kNarrow;
         PollStep step{};
@@ -107,7 +112,10 @@ typename Value<A>::type walk(TileStatus* base, uint32_t tag, int64_t tile, bool&
         for (int lane = step.stop >= 0 ? step.stop : 0; lane < kWave; ++lane)
             total = compose(s[lane], total);
         acc = compose(acc, total);
-        if (step.stop >= 0) return acc.b;
+        if (step.stop >= 0) {
+            if (windows > 1) g_deep_walks.fetch_add(1, std::memory_order_relaxed);
+            return acc.b;
+        }
         top -= kWave;
     }
 }
@@ -176,8 +184,12 @@ bool run_call(TileStatus* status, int64_t capacity, uint32_t tag, int K, double 
     }
     std::vector<V> got(K, V(0));
     std::vector<char> gave_up(K, 0);
-    std::vector<uint64_t> delay(K);
+    // yields before a tile starts, and before it publishes its inclusive
+    // value: late inclusive values make successors fold aggregates further
+    // back, over several windows when K > 64 and no aggregate cuts
+    std::vector<uint64_t> delay(K), late(K);
     for (auto& d : delay) d = rng() % 64;
+    for (auto& d : late) d = rng() % 4 == 0 ? rng() % 2048 : 0;
     std::atomic<int> start{0};
     std::vector<std::thread> threads;
     threads.reserve(K);
@@ -194,6 +206,7 @@ bool run_call(TileStatus* status, int64_t capacity, uint32_t tag, int K, double 
             V carry = V(0);
             bool gu = false;
             if (k > 0) carry = walk<A>(status, tag, k, gu);
+            for (uint64_t i = 0; i < late[k]; ++i) std::this_thread::yield();
             if (!known) publish_inclusive(st, apply(agg[k], carry), tag);
             got[k] = carry;
             gave_up[k] = gu;
@@ -331,6 +344,7 @@ int main(int argc, char** argv) {
         std::printf("FAILED: %d failure(s)\n", g_failures);
         return 1;
     }
-    std::printf("ok: %d trials, %d calls, %d tag wraps\n", trials, calls, wraps);
+    std::printf("ok: %d trials, %d calls, %d tag wraps, %ld walks over several windows\n",
+                trials, calls, wraps, g_deep_walks.load());
     return 0;
 }

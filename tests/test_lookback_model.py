@@ -53,5 +53,7 @@ def test_lookback_protocol_under_tsan(model, seed):
     assert "ThreadSanitizer" not in out, out[-4000:]
     assert r.returncode == 0, out[-4000:]
     assert r.stdout.startswith("ok"), out[-4000:]
-    # the trials must have crossed the tag wrap at least once
+    # the trials must have crossed the tag wrap at least once, and some
+    # walks must have folded aggregates over more than one window
     assert " 0 tag wraps" not in r.stdout, r.stdout
+    assert " 0 walks over several windows" not in r.stdout, r.stdout
