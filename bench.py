@@ -1148,8 +1148,30 @@ def time_variants(torch, w, ests, sh, lib, args):
         res["long_8x1048576_u8_flags"] = eager_workload(torch, wl, sh, lib, args.long_calls,
                                                         byte_flags=True)
     res["vtrace_lambda_pg_clip"] = time_vtrace_ex(torch, w, sh, lib)
+    res["vtrace_expanding_traces"] = time_vtrace_wide(torch, w, sh, lib, args)
     if not args.no_long:
         res["prefix_sum_f32_long_8x1048576"] = time_prefix_f32(torch, sh, lib, args.long_calls)
+    return res
+
+
+def time_vtrace_wide(torch, w, sh, lib, args):
+    """V-trace with c_bar = 2, where gamma * c_t can exceed 1 and the calls
+    run the kernels' float64 form: microseconds per call (cold, timed as the
+    per-estimator figures) on the production shape and, unless --no-long, on
+    the long rows."""
+    from dataclasses import replace
+    from linear_recurrence_scan_coefficient_amd import workloads
+    res = {}
+    shapes = [("production_4096x128", w)]
+    if not args.no_long:
+        shapes.append(("long_8x1048576", workloads.get("long_8x1048576")))
+    for name, base in shapes:
+        ww = replace(base, estimators=("vtrace",), c_bar=2.0)
+        us, b, _, _ = per_kernel(torch, "vtrace", ww, sh, lib)
+        gbs = b / (us * 1e-6) / 1e9
+        res[name] = {"us_per_call": round(us, 3), "bytes": b, "GB_per_s": round(gbs, 1),
+                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    res["note"] = "c_bar = 2: the float64 form of the V-trace kernels"
     return res
 
 

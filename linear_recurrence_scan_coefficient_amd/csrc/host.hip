@@ -151,6 +151,10 @@ int auto_rounds(int est, int64_t NT) {
 //  - Two rounds: eight waves.  Measured against four: 32 x 65536 (look-back)
 //    10-18 % faster; 4096 x 512 and 16384 x 128 (packed) up to 12 % for GAE
 //    and V-trace, the same within 4 % for the others.
+//    V-trace's float64 form takes four: at two rounds of eight waves it
+//    needs 178 VGPRs (one workgroup per CU), at four waves 162 (three);
+//    measured with c_bar = 2: 8 x 2^20 75.6 -> 58.2 us, 32 x 65536
+//    21.1 -> 19.8 us.
 //    Where T divides no such tile, the smallest tile whose whole rows fill
 //    at least 7/8 of it (100-step rows: 500 of 512 elements), else the
 //    best-filled one if its rows fill at least 3/4.  Retrace and the prefix
@@ -182,7 +186,7 @@ int auto_waves(int est, int rounds, int64_t N, int64_t T) {
         if (best_fill >= 768) return best;
         return last;
     }
-    return 8;  // two rounds
+    return est == kEstVtraceWide ? 4 : 8;  // two rounds
 }
 
 Plan make_plan(int est, int64_t N, int64_t T, bool vec, bool carry) {
